@@ -1,0 +1,157 @@
+"""CPU oracle for paged decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library never calls it, and
+it shares no code with the GPU path: ``pa_oracle.c`` re-implements the cache
+layout from its written contract and does all arithmetic in IEEE double.
+
+Contents
+  * ``pa_oracle.c`` (built to ``liboracle.so`` with gcc, no fast-math): fp64
+    table-walk decode, contiguous brute force, the slot-mapped KV append and
+    whole-block copies.  Passages followed are cited in that file.
+  * ``pool_model.py``: an independent pure-Python model of the refcounted
+    block pool (allocation, fork, append with copy-on-write, free).
+
+Data convention for the wrappers: cache-typed arrays are numpy arrays of
+``np.float32`` (fp32), ``np.float16`` (fp16) or ``np.uint16`` holding raw
+bfloat16 bits (bf16); ``dtype`` names the type: "f32", "f16" or "bf16".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+from .pool_model import PoolModel, PoolError, OutOfBlocks  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+_NP = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_k_offset.restype = _I64
+        lib.oracle_k_offset.argtypes = [_I64, _I, _I, _I, _I, _I, _I]
+        lib.oracle_v_offset.restype = _I64
+        lib.oracle_v_offset.argtypes = [_I64, _I, _I, _I, _I, _I, _I]
+        lib.oracle_reshape_and_cache.restype = _I
+        lib.oracle_reshape_and_cache.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I64, _I]
+        lib.oracle_copy_blocks.restype = None
+        lib.oracle_copy_blocks.argtypes = [_P, _P, _P, _I, _I, _I, _I]
+        lib.oracle_decode.restype = _I
+        lib.oracle_decode.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                      ctypes.c_float, _I, _I]
+        lib.oracle_bruteforce_contiguous.restype = None
+        lib.oracle_bruteforce_contiguous.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                                     ctypes.c_float, _I]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(a: np.ndarray, dtype: str):
+    if a.dtype != _NP[dtype]:
+        raise TypeError(f"expected {np.dtype(_NP[dtype])} for {dtype}, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def np_type(dtype: str):
+    return _NP[dtype]
+
+
+def k_offset(block, head, tok, dim, num_kv_heads, head_dim, dtype):
+    return _load().oracle_k_offset(block, head, tok, dim, num_kv_heads, head_dim, _DTYPES[dtype])
+
+
+def v_offset(block, head, tok, dim, num_kv_heads, head_dim, dtype):
+    return _load().oracle_v_offset(block, head, tok, dim, num_kv_heads, head_dim, _DTYPES[dtype])
+
+
+def empty_cache(num_blocks, num_kv_heads, head_dim, dtype):
+    """A pool whose every element is NaN (unused slots stay poisoned)."""
+    n = num_blocks * num_kv_heads * 16 * head_dim
+    if dtype == "bf16":
+        return np.full(n, 0x7FC0, dtype=np.uint16)
+    return np.full(n, np.nan, dtype=_NP[dtype])
+
+
+def reshape_and_cache(k_new, v_new, k_cache, v_cache, slot_mapping, num_kv_heads, head_dim,
+                      num_blocks, dtype):
+    """Scatter [T][Hkv][D] rows into the caches in place; returns #out-of-range slots."""
+    k_new = _check(k_new, dtype)
+    v_new = _check(v_new, dtype)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    assert k_cache.flags["C_CONTIGUOUS"] and v_cache.flags["C_CONTIGUOUS"]
+    return _load().oracle_reshape_and_cache(_ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                            _ptr(v_cache), _ptr(slots), len(slots),
+                                            num_kv_heads, head_dim, num_blocks, _DTYPES[dtype])
+
+
+def copy_blocks(k_cache, v_cache, pairs, num_kv_heads, head_dim, dtype):
+    pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    _load().oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), len(pairs),
+                               num_kv_heads, head_dim, _DTYPES[dtype])
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads, scale, dtype,
+           nthreads=0, return_threads=False):
+    """fp64 paged decode; q is [S][Hq][D] in the cache type.  Returns float64 [S][Hq][D]."""
+    q = _check(q, dtype)
+    S, Hq, D = q.shape
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    out = np.empty((S, Hq, D), dtype=np.float64)
+    used = _load().oracle_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(tables),
+                                 _ptr(lens), S, Hq, num_kv_heads, D, tables.shape[1],
+                                 float(scale), _DTYPES[dtype], nthreads)
+    return (out, used) if return_threads else out
+
+
+def bruteforce_contiguous(q, k_seq, v_seq, context_lens, scale, dtype):
+    """fp64 attention over contiguous [S][Lmax][Hkv][D] arrays (no table)."""
+    q = _check(q, dtype)
+    k_seq = _check(k_seq, dtype)
+    v_seq = _check(v_seq, dtype)
+    S, Hq, D = q.shape
+    _, Lmax, Hkv, _ = k_seq.shape
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    out = np.empty((S, Hq, D), dtype=np.float64)
+    _load().oracle_bruteforce_contiguous(_ptr(out), _ptr(q), _ptr(k_seq), _ptr(v_seq),
+                                         _ptr(lens), S, Hq, Hkv, D, Lmax, float(scale),
+                                         _DTYPES[dtype])
+    return out
+
+
+def to_float64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Widen cache-typed values to float64 exactly (bf16 bits are the top half of fp32)."""
+    if dtype == "bf16":
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)

@@ -1,0 +1,307 @@
+/*
+ * pa_oracle.c -- plain, slow, obviously correct CPU oracle for paged decode
+ * attention, the KV append through a slot mapping, and whole-block copies.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  It shares no code, header, table or
+ * helper with the GPU library; the cache layout it addresses is re-implemented
+ * here from the written layout contract.
+ *
+ * Arithmetic is IEEE double throughout.  Every cache element, whatever its
+ * stored type (fp32, fp16, bf16), is widened exactly to double before use.
+ *
+ * What is computed, and where it is stated on the pages:
+ *  - out = softmax(q . K^T / sqrt(d)) . V for one new query per (sequence,
+ *    head): "KV Cache Explained Like You're an LLM Engineer", section
+ *    "Transformer Attention: A Quick Refresher" (the attention formula), and
+ *    "What Happens Inside an LLM During Inference", section on self-attention
+ *    (the division by sqrt(d_k)).
+ *  - the decode query attends over every cached position including the one
+ *    just appended: "LLM Inference Optimization: KV-Cache, PagedAttention, and
+ *    GPU Memory Efficiency", section "The Attention Bottleneck in Decode-Phase
+ *    Inference" (the decode snippet that slices the cache up to and including
+ *    the current step).
+ *  - a logical position maps to (table[pos / block_size], pos % block_size):
+ *    same page, section "PagedAttention: OS Concepts Meet GPU Memory" (the
+ *    block-table lookup); the kernel walks the table block by block and
+ *    accumulates with an online softmax.  The online rescaling reaches the
+ *    same real number as the two-pass max / exp-sum form used here, so the
+ *    oracle writes the plain definition out.
+ *  - several query heads share one KV head (grouped-query attention): "What
+ *    Happens Inside an LLM During Inference" (GQA paragraph) and "Inference
+ *    serving: the KV-cache machine", section "The KV cache: attention's memory
+ *    bill, derived".  Reading taken: contiguous groups, kv head = h / G.
+ *  - appending a new token's K/V and copying a shared block on write:
+ *    "KV Cache Explained ...", section "What KV Cache Stores" (append, then
+ *    attend) and "Modern AI Infrastructure and Agentic System Design", section
+ *    9.1, the shared-prefix diagram (a write to a shared block is copied into a
+ *    fresh block).
+ *
+ * Summation order is fixed: dot products ascend in d, the exponential sum and
+ * the weighted V sum ascend in logical position i.  The table walk and the
+ * contiguous brute force therefore produce bit-identical doubles.
+ *
+ * Parity pins (tests marked "not gpu"): contiguous brute force (bitwise),
+ * numpy float64 softmax attention, closed forms (length 1, uniform weights,
+ * constant V, hard-max limit), block-permutation / shared-prefix / GQA-vs-MHA
+ * invariants, the pages' worked block table, and hand-computed layout offsets.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Element types, numbered for this file only. */
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+
+static int elem_bytes(int dtype) { return dtype == ORC_F32 ? 4 : 2; }
+
+/* IEEE binary16 -> double, from the format definition
+ * (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits). */
+static double f16_bits_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int m = h & 0x3ff;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-14 * 2^-10 */
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+  return sign ? -v : v;
+}
+
+/* bfloat16 -> double: bf16 is the upper half of an IEEE binary32. */
+static double bf16_bits_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double load_elem(const void *base, int64_t idx, int dtype) {
+  if (dtype == ORC_F32) {
+    float f;
+    memcpy(&f, (const char *)base + idx * 4, 4);
+    return (double)f;
+  }
+  uint16_t bits;
+  memcpy(&bits, (const char *)base + idx * 2, 2);
+  return dtype == ORC_F16 ? f16_bits_to_double(bits) : bf16_bits_to_double(bits);
+}
+
+/* ---------------------------------------------------------------------------
+ * Cache layout contract (element offsets).  Both caches hold num_blocks
+ * physical blocks; a block holds, per KV head, one tile of 16 tokens x D dims.
+ * X = 16 / element bytes is the number of elements in one 16-byte vector.
+ *
+ *   K tile: [D/X][16][X]    element (t, d) at (d / X)*16*X + t*X + d % X
+ *   V tile: slabs of 4X dims; inside a slab, 64 vectors indexed by
+ *           (t/4)*16 + (d % 4X) % 16, each vector holding (X/4) dims x 4
+ *           tokens, dim-major:
+ *           element (t, d) at (d/(4X))*64*X + ((t/4)*16 + (d%(4X))%16)*X
+ *                              + ((d%(4X))/16)*4 + t%4
+ *   tile (b, g) starts at (b*Hkv + g) * 16 * D elements.
+ * ------------------------------------------------------------------------ */
+#define ORC_BS 16
+
+int64_t oracle_k_offset(int64_t block, int head, int tok, int dim, int num_kv_heads,
+                        int head_dim, int dtype) {
+  int X = 16 / elem_bytes(dtype);
+  int64_t tile = (block * num_kv_heads + head) * (int64_t)ORC_BS * head_dim;
+  return tile + (int64_t)(dim / X) * ORC_BS * X + (int64_t)tok * X + dim % X;
+}
+
+int64_t oracle_v_offset(int64_t block, int head, int tok, int dim, int num_kv_heads,
+                        int head_dim, int dtype) {
+  int X = 16 / elem_bytes(dtype);
+  int slab_dims = 4 * X;
+  int slab = dim / slab_dims;
+  int e = dim % slab_dims;
+  int64_t tile = (block * num_kv_heads + head) * (int64_t)ORC_BS * head_dim;
+  int64_t vec = (int64_t)(tok / 4) * 16 + e % 16;
+  return tile + (int64_t)slab * 64 * X + vec * X + (e / 16) * 4 + tok % 4;
+}
+
+/* ---------------------------------------------------------------------------
+ * KV append through a slot mapping.  Token n's K/V row for every KV head is
+ * written at slot s = slot_mapping[n]: block s / 16, in-block position s % 16.
+ * Negative slots are skipped.  k_new, v_new: [T][Hkv][D] in the cache type.
+ * Returns the number of out-of-range slots (nothing is written for them).
+ * ------------------------------------------------------------------------ */
+int oracle_reshape_and_cache(const void *k_new, const void *v_new, void *k_cache,
+                             void *v_cache, const int64_t *slot_mapping, int num_tokens,
+                             int num_kv_heads, int head_dim, int64_t num_blocks, int dtype) {
+  int eb = elem_bytes(dtype);
+  int bad = 0;
+  for (int n = 0; n < num_tokens; ++n) {
+    int64_t s = slot_mapping[n];
+    if (s < 0) continue;
+    if (s >= num_blocks * ORC_BS) { ++bad; continue; }
+    int64_t blk = s / ORC_BS;
+    int t = (int)(s % ORC_BS);
+    for (int g = 0; g < num_kv_heads; ++g)
+      for (int d = 0; d < head_dim; ++d) {
+        int64_t src = ((int64_t)n * num_kv_heads + g) * head_dim + d;
+        memcpy((char *)k_cache + oracle_k_offset(blk, g, t, d, num_kv_heads, head_dim, dtype) * eb,
+               (const char *)k_new + src * eb, eb);
+        memcpy((char *)v_cache + oracle_v_offset(blk, g, t, d, num_kv_heads, head_dim, dtype) * eb,
+               (const char *)v_new + src * eb, eb);
+      }
+  }
+  return bad;
+}
+
+/* Whole-block copy (all heads, K and V) for each (src, dst) pair, in order. */
+void oracle_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int num_pairs,
+                        int num_kv_heads, int head_dim, int dtype) {
+  size_t block_bytes = (size_t)num_kv_heads * ORC_BS * head_dim * elem_bytes(dtype);
+  for (int p = 0; p < num_pairs; ++p) {
+    size_t src = (size_t)pairs[2 * p] * block_bytes, dst = (size_t)pairs[2 * p + 1] * block_bytes;
+    memmove((char *)k_cache + dst, (const char *)k_cache + src, block_bytes);
+    memmove((char *)v_cache + dst, (const char *)v_cache + src, block_bytes);
+  }
+}
+
+/* ---------------------------------------------------------------------------
+ * Attention of one query row over L keys/values given by accessor callbacks.
+ * sigma_i = scale * sum_d q[d]*k_i[d];  M = max_i sigma_i;
+ * w_i = exp(sigma_i - M);  Z = sum_i w_i;  out[d] = (sum_i w_i * v_i[d]) / Z.
+ * L == 0 gives a zero row (softmax over an empty set is left undefined by the
+ * pages; the reading taken is a defined, finite zero output).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  /* paged source */
+  const void *k_cache, *v_cache;
+  const int32_t *table; /* this sequence's row */
+  int num_kv_heads, head_dim, dtype, kv_head;
+  /* contiguous source ([Lmax][Hkv][D]); used when table == NULL */
+  const void *k_seq, *v_seq;
+} orc_src;
+
+static double key_at(const orc_src *s, int i, int d) {
+  if (s->table) {
+    int64_t blk = s->table[i / ORC_BS];
+    return load_elem(s->k_cache,
+                     oracle_k_offset(blk, s->kv_head, i % ORC_BS, d, s->num_kv_heads,
+                                     s->head_dim, s->dtype),
+                     s->dtype);
+  }
+  return load_elem(s->k_seq, ((int64_t)i * s->num_kv_heads + s->kv_head) * s->head_dim + d,
+                   s->dtype);
+}
+
+static double value_at(const orc_src *s, int i, int d) {
+  if (s->table) {
+    int64_t blk = s->table[i / ORC_BS];
+    return load_elem(s->v_cache,
+                     oracle_v_offset(blk, s->kv_head, i % ORC_BS, d, s->num_kv_heads,
+                                     s->head_dim, s->dtype),
+                     s->dtype);
+  }
+  return load_elem(s->v_seq, ((int64_t)i * s->num_kv_heads + s->kv_head) * s->head_dim + d,
+                   s->dtype);
+}
+
+static void attend_one(double *out, const double *q, const orc_src *src, int L, double scale,
+                       double *sigma /* scratch, >= L */) {
+  int D = src->head_dim;
+  if (L <= 0) {
+    for (int d = 0; d < D; ++d) out[d] = 0.0;
+    return;
+  }
+  double M = -INFINITY;
+  for (int i = 0; i < L; ++i) {
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += q[d] * key_at(src, i, d);
+    sigma[i] = scale * dot;
+    if (sigma[i] > M) M = sigma[i];
+  }
+  double Z = 0.0;
+  for (int i = 0; i < L; ++i) {
+    sigma[i] = exp(sigma[i] - M); /* sigma now holds the weights w_i */
+    Z += sigma[i];
+  }
+  for (int d = 0; d < D; ++d) {
+    double acc = 0.0;
+    for (int i = 0; i < L; ++i) acc += sigma[i] * value_at(src, i, d);
+    out[d] = acc / Z;
+  }
+}
+
+/* ---------------------------------------------------------------------------
+ * Paged decode attention by walking each sequence's block table.
+ *   out:    [S][Hq][D] doubles
+ *   q:      [S][Hq][D] in the cache type
+ *   tables: [S][max_blocks] int32;  lens: [S] int32
+ *   scale:  taken as the fp32 value the caller passes, widened to double
+ *   nthreads: OpenMP threads for the (s, h) loop; <= 0 means the default
+ * Returns the number of threads used.
+ * ------------------------------------------------------------------------ */
+int oracle_decode(double *out, const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *tables, const int32_t *lens, int num_seqs, int num_q_heads,
+                  int num_kv_heads, int head_dim, int max_blocks, float scale, int dtype,
+                  int nthreads) {
+  int G = num_q_heads / num_kv_heads;
+  int Lmax = 0;
+  for (int s = 0; s < num_seqs; ++s)
+    if (lens[s] > Lmax) Lmax = lens[s];
+  int used = 1;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+  {
+#pragma omp single
+    used = omp_get_num_threads();
+#endif
+    double *sigma = (double *)malloc(sizeof(double) * (Lmax > 0 ? Lmax : 1));
+    double *qd = (double *)malloc(sizeof(double) * head_dim);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+    for (int sh = 0; sh < num_seqs * num_q_heads; ++sh) {
+      int s = sh / num_q_heads, h = sh % num_q_heads;
+      for (int d = 0; d < head_dim; ++d)
+        qd[d] = load_elem(q, (int64_t)sh * head_dim + d, dtype);
+      orc_src src = {k_cache, v_cache, tables + (int64_t)s * max_blocks, num_kv_heads,
+                     head_dim, dtype, h / G, NULL, NULL};
+      attend_one(out + (int64_t)sh * head_dim, qd, &src, lens[s], (double)scale, sigma);
+    }
+    free(sigma);
+    free(qd);
+#ifdef _OPENMP
+  }
+#endif
+  (void)nthreads;
+  return used;
+}
+
+/* ---------------------------------------------------------------------------
+ * Brute force over contiguous per-sequence arrays k_seq, v_seq:
+ * [S][Lmax][Hkv][D] in the cache type.  Never touches a table.
+ * ------------------------------------------------------------------------ */
+void oracle_bruteforce_contiguous(double *out, const void *q, const void *k_seq,
+                                  const void *v_seq, const int32_t *lens, int num_seqs,
+                                  int num_q_heads, int num_kv_heads, int head_dim, int Lmax,
+                                  float scale, int dtype) {
+  int G = num_q_heads / num_kv_heads;
+  int eb = elem_bytes(dtype);
+  double *sigma = (double *)malloc(sizeof(double) * (Lmax > 0 ? Lmax : 1));
+  double *qd = (double *)malloc(sizeof(double) * head_dim);
+  size_t seq_elems = (size_t)Lmax * num_kv_heads * head_dim;
+  for (int s = 0; s < num_seqs; ++s)
+    for (int h = 0; h < num_q_heads; ++h) {
+      int64_t sh = (int64_t)s * num_q_heads + h;
+      for (int d = 0; d < head_dim; ++d) qd[d] = load_elem(q, sh * head_dim + d, dtype);
+      orc_src src = {NULL, NULL, NULL, num_kv_heads, head_dim, dtype, h / G,
+                     (const char *)k_seq + s * seq_elems * eb,
+                     (const char *)v_seq + s * seq_elems * eb};
+      attend_one(out + sh * head_dim, qd, &src, lens[s], (double)scale, sigma);
+    }
+  free(sigma);
+  free(qd);
+}

@@ -1,0 +1,59 @@
+"""Byte and FLOP accounting for paged decode attention (host-side arithmetic).
+
+KV bytes per token = 2 (K and V) x layers x KV heads x head_dim x element bytes
+-- the closed form stated on several pages: "Modern AI Infrastructure and
+Agentic System Design", section 9.1 "The key and value cache"; "Inference
+serving: the KV-cache machine", section "The KV cache: attention's memory bill,
+derived"; "KV Cache Explained Like You're an LLM Engineer", section "Why
+Recomputing Attention is Inefficient".  All kernels here work on one layer.
+
+Algorithmic bytes of one decode launch are the bytes the method must move:
+every cached K/V row read once per (sequence, KV head) -- a physical block
+shared by several sequences counts once -- plus q, the output, the used block
+table entries and the context lengths.  Split-K workspace traffic is not
+algorithmic and is reported apart.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK_SIZE = 16
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    return 2 * num_layers * num_kv_heads * head_dim * elem_bytes
+
+
+def decode_algorithmic_bytes(context_lens, num_q_heads, num_kv_heads, head_dim, dtype,
+                             out_dtype, shared_tokens: int = 0) -> dict:
+    """Bytes one paged decode launch must move.
+
+    shared_tokens: tokens of a prefix whose blocks every sequence maps (counted
+    once in 'kv_unique' and once per sequence in 'kv_logical').
+    """
+    lens = np.asarray(context_lens, dtype=np.int64)
+    eb = ELEM_BYTES[dtype]
+    S = len(lens)
+    per_tok = kv_bytes_per_token(1, num_kv_heads, head_dim, eb)
+    kv_logical = int(lens.sum()) * per_tok
+    kv_unique = kv_logical - max(S - 1, 0) * shared_tokens * per_tok if shared_tokens else kv_logical
+    q = S * num_q_heads * head_dim * eb
+    out = S * num_q_heads * head_dim * ELEM_BYTES[out_dtype]
+    tables = 4 * int((-(-lens // BLOCK_SIZE)).sum())
+    ctx = 4 * S
+    small = q + out + tables + ctx
+    return {"kv_unique": kv_unique, "kv_logical": kv_logical, "q": q, "out": out,
+            "tables": tables, "context_lens": ctx,
+            "total": kv_unique + small, "total_logical": kv_logical + small}
+
+
+def decode_flops(context_lens, num_q_heads, head_dim) -> int:
+    """q.k and p.v multiply-adds: 4*D flops per (query head, context token)."""
+    return 4 * head_dim * num_q_heads * int(np.asarray(context_lens, dtype=np.int64).sum())
+
+
+def append_bytes(num_tokens, num_kv_heads, head_dim, dtype) -> int:
+    """Read new K/V rows + write them into the cache + the int64 slot mapping."""
+    row = 2 * num_kv_heads * head_dim * ELEM_BYTES[dtype]
+    return num_tokens * (2 * row + 8)

@@ -1,0 +1,329 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test checks the oracle against something other than itself: hand-computed
+layout offsets, the pages' worked block table, a contiguous brute force that
+never touches a table, numpy float64 softmax attention, closed forms, and
+invariants the method fixes.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_65_amd import workloads
+from tests import oracle_side
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built(oracle_lib):
+    return oracle_lib
+
+
+def _contig(wl, which):
+    """[S][Lmax][Hkv][D] prompt rows, NaN-padded beyond each length."""
+    spec = wl.spec
+    Lmax = int(wl.prompt_lens.max()) if len(wl.prompt_lens) else 0
+    fill = 0x7FC0 if spec.dtype == "bf16" else np.nan
+    a = np.full((spec.num_seqs, max(Lmax, 1), spec.num_kv_heads, spec.head_dim), fill,
+                dtype=workloads.np_cache_type(spec.dtype))
+    for s in range(spec.num_seqs):
+        rows = wl.seq_rows(s, which)
+        a[s, :len(rows)] = rows
+    return a
+
+
+def _numpy_attention(q64, k64, v64, lens, G, scale):
+    """Textbook softmax attention in float64 numpy: one query row per head."""
+    S, Hq, D = q64.shape
+    out = np.zeros((S, Hq, D))
+    for s in range(S):
+        L = lens[s]
+        if L == 0:
+            continue
+        for h in range(Hq):
+            k = k64[s, :L, h // G]
+            v = v64[s, :L, h // G]
+            sc = (k @ q64[s, h]) * scale
+            w = np.exp(sc - sc.max())
+            out[s, h] = (w / w.sum()) @ v
+    return out
+
+
+# ---------------------------------------------------------------- layout / slots
+def test_layout_offsets_match_hand_computed_golden():
+    n = 0
+    with open(os.path.join(GOLDEN, "layout_offsets.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            which, dt, hkv, d, blk, head, tok, dim, expect = line.split()
+            fn = oracle.k_offset if which == "K" else oracle.v_offset
+            got = fn(int(blk), int(head), int(tok), int(dim), int(hkv), int(d), dt)
+            assert got == int(expect), line
+            n += 1
+    assert n >= 15
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64), ("f32", 64), ("f32", 128)])
+def test_layout_is_a_bijection_per_tile(dtype, D):
+    for fn in (oracle.k_offset, oracle.v_offset):
+        offs = sorted(fn(1, 1, t, d, 2, D, dtype) for t in range(16) for d in range(D))
+        base = (1 * 2 + 1) * 16 * D
+        assert offs == list(range(base, base + 16 * D))
+
+
+def test_worked_block_table_slots():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "worked_block_table.txt"))
+            if l.strip() and not l.startswith("#")]
+    table = [int(x) for x in rows[0][1:]]
+    pairs = [(int(a), int(b)) for a, b in rows[1:]]
+    # the pool hands out blocks 7, 2, 15, 3 in that order (stack top = last)
+    order = [b for b in range(16) if b not in table] + table[::-1]
+    pool = oracle.PoolModel(16, 16, order)
+    sid = pool.seq_create()
+    slots, cow = pool.seq_append(sid, 64)
+    assert cow is None and pool.seq_table(sid) == table
+    for pos, slot in pairs:
+        assert slots[pos] == slot
+
+
+# ---------------------------------------------------------------- decode pins
+SWEEP = [
+    dict(dtype="f32", head_dim=64, num_q_heads=4, num_kv_heads=4, lens=(1, 17, 33, 100)),
+    dict(dtype="f16", head_dim=128, num_q_heads=4, num_kv_heads=2, lens=(16, 15, 0, 47)),
+    dict(dtype="bf16", head_dim=128, num_q_heads=8, num_kv_heads=1, lens=(70, 1, 33)),
+    dict(dtype="bf16", head_dim=64, num_q_heads=16, num_kv_heads=2, lens=(5, 64, 129)),
+]
+
+
+@pytest.mark.parametrize("cfg", SWEEP)
+def test_table_walk_equals_contiguous_bruteforce_bitwise(cfg):
+    wl = workloads.generate(workloads.custom(seed=11, **cfg))
+    st = oracle_side.build(wl)
+    mb = oracle_side.max_blocks_for(wl)
+    got = oracle_side.decode(wl, st, mb)
+    ref = oracle.bruteforce_contiguous(wl.q, _contig(wl, "k"), _contig(wl, "v"), wl.prompt_lens,
+                                       wl.spec.fp32_scale(), wl.spec.dtype)
+    assert np.array_equal(got, ref)
+    assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("cfg", SWEEP)
+def test_matches_numpy_float64_attention(cfg):
+    wl = workloads.generate(workloads.custom(seed=12, **cfg))
+    st = oracle_side.build(wl)
+    got = oracle_side.decode(wl, st, oracle_side.max_blocks_for(wl))
+    dt = wl.spec.dtype
+    ref = _numpy_attention(oracle.to_float64(wl.q, dt), oracle.to_float64(_contig(wl, "k"), dt),
+                           oracle.to_float64(_contig(wl, "v"), dt), wl.prompt_lens,
+                           wl.spec.group, float(np.float32(wl.spec.fp32_scale())))
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def _single(dtype, q, k, v, scale):
+    """One sequence in a fresh oracle pool; q [Hq][D], k/v [L][Hkv][D] (cache type)."""
+    L, Hkv, D = k.shape
+    nb = L // 16 + 3
+    pool = oracle.PoolModel(nb, 16, np.random.default_rng(5).permutation(nb))
+    sid = pool.seq_create()
+    slots, _ = pool.seq_append(sid, L)
+    kc = oracle.empty_cache(nb, Hkv, D, dtype)
+    vc = oracle.empty_cache(nb, Hkv, D, dtype)
+    oracle.reshape_and_cache(k, v, kc, vc, slots, Hkv, D, nb, dtype)
+    t, l = pool.export([sid], nb)
+    return oracle.decode(q[None], kc, vc, np.array(t, np.int32), np.array(l, np.int32), Hkv,
+                         scale, dtype)[0]
+
+
+def test_length_one_returns_v_exactly():
+    rng = np.random.default_rng(3)
+    for dt in ("f32", "f16", "bf16"):
+        q = workloads.round_to(rng.standard_normal((4, 64), dtype=np.float32) * 5, dt)
+        k = workloads.round_to(rng.standard_normal((1, 2, 64), dtype=np.float32) * 5, dt)
+        v = workloads.round_to(rng.standard_normal((1, 2, 64), dtype=np.float32), dt)
+        out = _single(dt, q, k, v, 0.125)
+        v64 = oracle.to_float64(v, dt)
+        for h in range(4):
+            assert np.array_equal(out[h], v64[0, h // 2])
+
+
+def test_zero_query_gives_mean_of_values():
+    rng = np.random.default_rng(4)
+    q = np.zeros((2, 128), np.float32)
+    k = rng.standard_normal((77, 1, 128), dtype=np.float32)
+    v = rng.standard_normal((77, 1, 128), dtype=np.float32)
+    out = _single("f32", q, k, v, 0.088)
+    mean = v.astype(np.float64).mean(axis=0)[0]
+    assert np.max(np.abs(out[0] - mean)) <= 1e-15 * 77
+    assert np.array_equal(out[0], out[1])
+
+
+def test_equal_keys_give_uniform_weights():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 64), dtype=np.float32)
+    k = np.repeat(rng.standard_normal((1, 1, 64), dtype=np.float32), 40, axis=0)
+    v = rng.standard_normal((40, 1, 64), dtype=np.float32)
+    out = _single("f32", q, k, v, 0.125)
+    assert np.max(np.abs(out[0] - v.astype(np.float64).mean(axis=0)[0])) <= 1e-14
+
+
+def test_constant_values_are_reproduced():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 64), dtype=np.float32) * 3
+    k = rng.standard_normal((50, 1, 64), dtype=np.float32)
+    c = rng.standard_normal(64).astype(np.float32)
+    v = np.broadcast_to(c, (50, 1, 64)).copy()
+    out = _single("f32", q, k, v, 0.125)
+    # sum_i w_i*c and c*sum_i w_i differ only by summation rounding: <= 2*L*eps
+    assert np.max(np.abs(out[0] - c.astype(np.float64)) / np.abs(c)) <= 2 * 50 * 2.0 ** -53
+
+
+def test_hard_max_limit_and_overflow_safety():
+    """One score exceeds every other by far more than 60: out = V of that token.
+    Scores of order 1e4 also check that the max is subtracted before exp."""
+    rng = np.random.default_rng(8)
+    L = 45
+    q = np.zeros((1, 64), np.float32)
+    q[0, 0] = 1000.0
+    k = np.zeros((L, 1, 64), np.float32)
+    k[:, 0, 0] = np.arange(L, dtype=np.float32) * 0.5
+    k[17, 0, 0] = 100.0
+    v = rng.standard_normal((L, 1, 64), dtype=np.float32)
+    out = _single("f32", q, k, v, 1.0)
+    assert np.all(np.isfinite(out))
+    assert np.max(np.abs(out[0] - v[17, 0].astype(np.float64))) <= 1e-12
+
+
+def test_empty_context_gives_zero_row():
+    wl = workloads.generate(workloads.custom(seed=9, dtype="f16", lens=(0, 3), num_q_heads=2,
+                                             num_kv_heads=1, head_dim=64))
+    st = oracle_side.build(wl)
+    out = oracle_side.decode(wl, st, 1)
+    assert np.array_equal(out[0], np.zeros_like(out[0]))
+    assert np.all(np.isfinite(out[1])) and np.any(out[1] != 0)
+
+
+# ---------------------------------------------------------------- invariants
+def test_block_permutation_invariance_bitwise():
+    wl = workloads.generate(workloads.custom(seed=21, dtype="bf16", lens=(40, 97, 16),
+                                             num_q_heads=8, num_kv_heads=2, head_dim=128))
+    st = oracle_side.build(wl)
+    mb = oracle_side.max_blocks_for(wl)
+    tab, lens = oracle_side.tables(st, mb)
+    ref = oracle.decode(wl.q, st.k_cache, st.v_cache, tab, lens, 2, wl.spec.fp32_scale(), "bf16")
+    # move every block to a new physical index, rewrite the tables
+    nb = wl.num_blocks
+    perm = np.random.default_rng(1).permutation(nb)
+    tile = 2 * 16 * 128
+    k2 = np.empty_like(st.k_cache)
+    v2 = np.empty_like(st.v_cache)
+    for b in range(nb):
+        k2[perm[b] * tile:(perm[b] + 1) * tile] = st.k_cache[b * tile:(b + 1) * tile]
+        v2[perm[b] * tile:(perm[b] + 1) * tile] = st.v_cache[b * tile:(b + 1) * tile]
+    tab2 = np.where(tab >= 0, perm[np.maximum(tab, 0)], -1).astype(np.int32)
+    got = oracle.decode(wl.q, k2, v2, tab2, lens, 2, wl.spec.fp32_scale(), "bf16")
+    assert np.array_equal(got, ref)
+
+
+def test_shared_prefix_equals_private_copies_bitwise():
+    spec = workloads.custom(seed=22, dtype="bf16", lens=(5, 33, 0, 16), num_q_heads=4,
+                            num_kv_heads=2, head_dim=64, prefix_len=48)
+    wl = workloads.generate(spec)
+    st = oracle_side.build(wl)
+    mb = oracle_side.max_blocks_for(wl)
+    tab, lens = oracle_side.tables(st, mb)
+    # the prefix blocks are shared: refcount = owner + 4 sequences
+    for b in st.pool.seq_table(st.owner):
+        assert st.pool.refcount[b] == 5
+    shared = oracle.decode(wl.q, st.k_cache, st.v_cache, tab, lens, 2, spec.fp32_scale(), "bf16")
+    # same rows, every sequence with private blocks (no prefix sharing)
+    private = workloads.Workload(
+        workloads.custom(seed=22, dtype="bf16", lens=tuple(int(x) for x in wl.prompt_lens),
+                         num_q_heads=4, num_kv_heads=2, head_dim=64),
+        wl.prompt_lens, np.arange(wl.num_blocks + 64, dtype=np.int32), wl.q,
+        wl.prefix_k[:0], wl.prefix_v[:0],
+        np.concatenate([wl.seq_rows(s, "k") for s in range(4)]),
+        np.concatenate([wl.seq_rows(s, "v") for s in range(4)]),
+        np.concatenate([[0], np.cumsum(wl.prompt_lens)]).astype(np.int64), wl.step_k, wl.step_v)
+    st2 = oracle_side.build(private)
+    tab2, lens2 = oracle_side.tables(st2, mb)
+    assert np.array_equal(lens2, lens)
+    got = oracle.decode(wl.q, st2.k_cache, st2.v_cache, tab2, lens2, 2, spec.fp32_scale(), "bf16")
+    assert np.array_equal(got, shared)
+
+
+def test_gqa_equals_mha_with_replicated_kv_heads_bitwise():
+    wl = workloads.generate(workloads.custom(seed=23, dtype="f16", lens=(29, 80), num_q_heads=8,
+                                             num_kv_heads=2, head_dim=128))
+    st = oracle_side.build(wl)
+    mb = oracle_side.max_blocks_for(wl)
+    tab, lens = oracle_side.tables(st, mb)
+    gqa = oracle.decode(wl.q, st.k_cache, st.v_cache, tab, lens, 2, wl.spec.fp32_scale(), "f16")
+    # MHA pool: kv head h holds group h // 4's rows
+    nb, D = wl.num_blocks, 128
+    kc = oracle.empty_cache(nb, 8, D, "f16")
+    vc = oracle.empty_cache(nb, 8, D, "f16")
+    for s in range(2):
+        rows_k, rows_v = wl.seq_rows(s, "k"), wl.seq_rows(s, "v")
+        rep_k = np.repeat(rows_k, 4, axis=1)
+        rep_v = np.repeat(rows_v, 4, axis=1)
+        L = len(rows_k)
+        slots = [tab[s][i // 16] * 16 + i % 16 for i in range(L)]
+        oracle.reshape_and_cache(rep_k, rep_v, kc, vc, slots, 8, D, nb, "f16")
+    mha = oracle.decode(wl.q, kc, vc, tab, lens, 8, wl.spec.fp32_scale(), "f16")
+    assert np.array_equal(mha, gqa)
+
+
+def test_nan_poisoned_unused_slots_do_not_leak():
+    wl = workloads.generate(workloads.custom(seed=24, dtype="bf16", lens=(3, 18),
+                                             num_q_heads=2, num_kv_heads=1, head_dim=64))
+    st = oracle_side.build(wl)
+    tab, lens = oracle_side.tables(st, 4)  # -1 entries beyond each table
+    assert (tab == -1).sum() > 0
+    out = oracle.decode(wl.q, st.k_cache, st.v_cache, tab, lens, 1, wl.spec.fp32_scale(), "bf16")
+    assert np.all(np.isfinite(out))
+
+
+# ---------------------------------------------------------------- append / copy
+def test_reshape_and_cache_writes_exactly_the_mapped_slots():
+    rng = np.random.default_rng(30)
+    nb, Hkv, D = 6, 2, 64
+    kc = oracle.empty_cache(nb, Hkv, D, "bf16")
+    vc = oracle.empty_cache(nb, Hkv, D, "bf16")
+    before_k, before_v = kc.copy(), vc.copy()
+    slots = np.array([5, -1, 17, 95, 16 * nb, 40], dtype=np.int64)
+    k = workloads.round_to(rng.standard_normal((6, Hkv, D), dtype=np.float32), "bf16")
+    v = workloads.round_to(rng.standard_normal((6, Hkv, D), dtype=np.float32), "bf16")
+    bad = oracle.reshape_and_cache(k, v, kc, vc, slots, Hkv, D, nb, "bf16")
+    assert bad == 1
+    written = set()
+    for n, s in enumerate(slots):
+        if s < 0 or s >= 16 * nb:
+            continue
+        for g in range(Hkv):
+            for d in range(D):
+                ko = oracle.k_offset(s // 16, g, s % 16, d, Hkv, D, "bf16")
+                vo = oracle.v_offset(s // 16, g, s % 16, d, Hkv, D, "bf16")
+                assert kc[ko] == k[n, g, d] and vc[vo] == v[n, g, d]
+                written.add(ko)
+    untouched = np.ones(kc.size, bool)
+    untouched[list(written)] = False
+    assert np.array_equal(kc[untouched], before_k[untouched])
+    assert len(written) == 4 * Hkv * D
+
+
+def test_copy_blocks_copies_whole_blocks_in_order():
+    rng = np.random.default_rng(31)
+    nb, Hkv, D = 5, 2, 64
+    kc = rng.integers(0, 2 ** 16, nb * Hkv * 16 * D, dtype=np.uint16)
+    vc = rng.integers(0, 2 ** 16, nb * Hkv * 16 * D, dtype=np.uint16)
+    k0, v0 = kc.copy(), vc.copy()
+    oracle.copy_blocks(kc, vc, [[1, 3], [3, 4]], Hkv, D, "bf16")
+    blk = Hkv * 16 * D
+    assert np.array_equal(kc[3 * blk:4 * blk], k0[1 * blk:2 * blk])
+    assert np.array_equal(kc[4 * blk:5 * blk], k0[1 * blk:2 * blk])  # chained in order
+    assert np.array_equal(vc[4 * blk:5 * blk], v0[1 * blk:2 * blk])
+    assert np.array_equal(kc[:3 * blk], k0[:3 * blk])
