@@ -1,0 +1,236 @@
+/*
+ * pa.h -- C ABI of libpa: paged decode attention on AMD MI355X (gfx950).
+ *
+ * The library exports three groups of calls:
+ *   1. pa_decode            paged decode attention (one new query per sequence)
+ *   2. pa_reshape_and_cache append new tokens' K/V into the block pool through
+ *      pa_copy_blocks       a slot mapping; whole-block copies for copy-on-write
+ *   3. pa_block_pool_* /    a host-side refcounted block pool that owns block
+ *      pa_seq_*             tables, hands out slots and decides copy-on-write
+ *
+ * Conventions (all calls):
+ *   - Every call returns pa_status; nothing throws or aborts across the ABI.
+ *     On any error no kernel is launched and no pool state changes;
+ *     pa_last_error() returns a thread-local message for the last failure.
+ *   - Device calls take raw device pointers owned by the caller and a HIP
+ *     stream (hipStream_t passed as void*, NULL = the default stream).  They
+ *     enqueue work asynchronously and never synchronize.  The library
+ *     allocates no device memory: the decode workspace is caller-provided.
+ *   - Every device pointer must be 16-byte aligned.
+ *   - Block size is fixed at PA_BLOCK_SIZE = 16 tokens.
+ *
+ * Cache layout (one layer).  k_cache and v_cache each hold num_blocks physical
+ * blocks; block b holds, for every KV head g, one tile of 16 tokens x head_dim
+ * dims starting at element (b * num_kv_heads + g) * 16 * head_dim.  With
+ * X = 16 / sizeof(element) (8 for fp16/bf16, 4 for fp32):
+ *   K tile, [head_dim/X][16][X]:  (t, d) -> (d / X)*16*X + t*X + d % X
+ *   V tile, slabs of 4X dims, 64 16-byte vectors per slab, each vector holding
+ *   X/4 dims x 4 consecutive tokens (dim-major):
+ *     (t, d) -> (d / (4X))*64*X + ((t / 4)*16 + (d % (4X)) % 16)*X
+ *               + ((d % (4X)) / 16)*4 + t % 4
+ * Both tiles are layouts of this library's own choosing (the pages leave the
+ * in-block order open): one 16-byte load per lane then hands each lane of a
+ * 64-wide wavefront exactly the operand fragment the matrix-core tiles use.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,  /* a null pointer, a size or an id out of range */
+  PA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement */
+  PA_ERR_WORKSPACE = 3,    /* the decode workspace is missing or too small */
+  PA_ERR_OOM = 4,          /* the block pool has too few free blocks */
+  PA_ERR_HIP = 5           /* a HIP runtime call failed (e.g. launch error) */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Which decode kernel runs.  AUTO picks the matrix-core kernel for fp16/bf16
+ * caches and the vector-ALU kernel for fp32. */
+typedef enum pa_kernel { PA_KERNEL_AUTO = 0, PA_KERNEL_VALU = 1, PA_KERNEL_MFMA = 2 } pa_kernel;
+
+/* Library version string. */
+const char *pa_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *pa_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Paged decode attention.
+ *
+ * For every sequence s < num_seqs and query head h < num_q_heads, with
+ * G = num_q_heads / num_kv_heads, kv head g = h / G (contiguous groups of
+ * query heads share one KV head) and L = context_lens[s]:
+ *   score_i = scale * sum_d q[s][h][d] * K(s, i, g, d),   i < L
+ *   out[s][h][:] = sum_i softmax(score)_i * V(s, i, g, :)
+ * where K(s, i, g, d) is element (i % 16, d) of tile (block_tables[s][i / 16],
+ * g) in k_cache, and V likewise.  This is softmax(q.K^T / sqrt(d)).V for one
+ * new query ("KV Cache Explained Like You're an LLM Engineer", section
+ * "Transformer Attention: A Quick Refresher"), gathered block by block through
+ * a per-sequence table ("LLM Inference Optimization: KV-Cache, PagedAttention,
+ * and GPU Memory Efficiency", section "PagedAttention: OS Concepts Meet GPU
+ * Memory"), with grouped-query head sharing ("Inference serving: the KV-cache
+ * machine", section "The KV cache: attention's memory bill, derived").  The
+ * context counts the token appended this step.  L = 0 yields a zero row.
+ *
+ * Long contexts are split into partitions of partition_tokens tokens, each
+ * reduced with an online softmax into (max, sum, weighted V) partials that a
+ * second kernel merges by log-sum-exp rescaling.  The result does not depend
+ * on the partition size beyond float32 rounding.
+ *
+ * Arguments (all pointers are device memory):
+ *   out           [num_seqs][num_q_heads][head_dim], out_dtype (F32 or kv_dtype;
+ *                 a 16-bit output is the float32 result rounded to nearest even)
+ *   q             [num_seqs][num_q_heads][head_dim], kv_dtype
+ *   k_cache, v_cache  [num_blocks] blocks in the layout above, kv_dtype
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; only the first
+ *                 ceil(L/16) entries of a row are read
+ *   context_lens  int32 [num_seqs]
+ *   max_context_len  host-known upper bound on every context_lens[s]; it sizes
+ *                 the launch grid
+ *   scale         usually 1/sqrt(head_dim)
+ *   partition_tokens  0 = automatic, else a positive multiple of 16
+ * Supported: head_dim in {64, 128}; num_q_heads % num_kv_heads == 0;
+ *   G <= 16; fp16/bf16 with any kernel, fp32 with the VALU kernel.
+ * Contract violations found on the device (a table entry outside
+ * [0, num_blocks), or L outside [0, min(max_context_len,
+ * 16*max_blocks_per_seq)]) are never dereferenced: that sequence's output row
+ * is set to NaN.
+ * Workspace: pa_decode_workspace_bytes() bytes of device memory (may be 0);
+ * it is scratch for this call only and may be reused once the stream passes
+ * the call.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_decode_params {
+  void *out;
+  const void *q;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  int32_t max_context_len;
+  float scale;
+  pa_dtype kv_dtype;
+  pa_dtype out_dtype;
+  int32_t partition_tokens;
+  pa_kernel kernel;
+} pa_decode_params;
+
+/* Partition size (tokens) pa_decode will use for these parameters, or a
+ * negative pa_status value if the parameters are invalid. */
+int32_t pa_decode_partition_tokens(const pa_decode_params *p);
+
+/* Workspace bytes pa_decode needs for these parameters (0 if the whole context
+ * fits one partition).  Returns 0 for invalid parameters as well; pa_decode
+ * reports those. */
+size_t pa_decode_workspace_bytes(const pa_decode_params *p);
+
+pa_status pa_decode(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* ------------------------------------------------------------------------
+ * KV append through a slot mapping.
+ * For each new token n < num_tokens with slot s = slot_mapping[n] >= 0, and
+ * every kv head g: K row k_new[n][g][:] becomes element (s % 16, :) of tile
+ * (s / 16, g) in k_cache; likewise v_new into v_cache.  Negative slots are
+ * skipped; slots >= 16*num_blocks are skipped too (contract violation).
+ * Appending the new token's K/V before attending is the decode step of "KV
+ * Cache Explained Like You're an LLM Engineer", section "What KV Cache
+ * Stores".  Bytes are copied unchanged (bit-exact).
+ *   k_new, v_new  [num_tokens][num_kv_heads][head_dim], dtype
+ *   slot_mapping  int64 [num_tokens] (device)
+ * Two tokens mapped to one slot leave either row there (no ordering).
+ * ------------------------------------------------------------------------ */
+pa_status pa_reshape_and_cache(const void *k_new, const void *v_new, void *k_cache,
+                               void *v_cache, const int64_t *slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                               pa_dtype dtype, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Whole-block copies for copy-on-write: for each pair i, block
+ * src_dst_pairs[2i] (all heads, K and V) is copied to block src_dst_pairs[2i+1]
+ * ("Modern AI Infrastructure and Agentic System Design", section 9.1: a write
+ * to a shared block is copied into a fresh block first).  Pairs are applied in
+ * parallel: a block may not be both a source and a destination in one call.
+ * Pairs with an id outside [0, num_blocks) are skipped.
+ *   src_dst_pairs int32 [num_pairs][2] (device)
+ * ------------------------------------------------------------------------ */
+pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst_pairs,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t num_blocks, pa_dtype dtype, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Host-side block pool.  Blocks are allocated on demand and returned when
+ * their refcount reaches zero ("PagedAttention vs Traditional KV Cache",
+ * section 4 "PagedAttention: How It Works"; "Inference serving: the KV-cache
+ * machine", section "Paged KV: virtual memory for tokens").
+ *   - Free blocks form a stack: allocation pops the top; a block whose
+ *     refcount reaches zero is pushed.  initial_free_order (host, nullable)
+ *     seeds the stack bottom-to-top; NULL means 0..num_blocks-1 (so block
+ *     num_blocks-1 is handed out first).
+ *   - A sequence owns a block table and a token count.  pa_seq_fork copies
+ *     the parent's table and increments every block (the prefix is shared).
+ *   - Appending a token when the last block is full (or there is none) takes a
+ *     fresh block.  Appending into a partly filled last block whose refcount
+ *     is > 1 first takes a fresh block, reports (src, dst) for a whole-block
+ *     copy (pa_copy_blocks), decrements src and replaces the table entry.
+ *   - Freeing a sequence decrements its blocks in table order.
+ *   - Sequence ids are the lowest ids not in use.
+ *   - Running out of blocks returns PA_ERR_OOM with the pool unchanged.
+ * The pool is not thread-safe (one scheduler thread owns it).  All pointers
+ * here are host memory.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_block_pool pa_block_pool;
+
+pa_status pa_block_pool_create(int32_t num_blocks, int32_t block_size,
+                               const int32_t *initial_free_order, pa_block_pool **out);
+void pa_block_pool_destroy(pa_block_pool *pool);
+int32_t pa_block_pool_num_blocks(const pa_block_pool *pool);
+int32_t pa_block_pool_num_free(const pa_block_pool *pool);
+/* Refcount of a block, or -1 for an invalid id. */
+int32_t pa_block_pool_refcount(const pa_block_pool *pool, int32_t block);
+/* Copies the free stack bottom-to-top into out[capacity]; returns its size. */
+int32_t pa_block_pool_free_list(const pa_block_pool *pool, int32_t *out, int32_t capacity);
+pa_status pa_block_pool_alloc(pa_block_pool *pool, int32_t *block); /* refcount := 1 */
+pa_status pa_block_pool_incref(pa_block_pool *pool, int32_t block);
+pa_status pa_block_pool_decref(pa_block_pool *pool, int32_t block); /* frees at 0 */
+
+pa_status pa_seq_create(pa_block_pool *pool, int32_t *seq_id);
+pa_status pa_seq_fork(pa_block_pool *pool, int32_t parent, int32_t *child);
+/* Append n_tokens >= 0 tokens to one sequence.  slots[n_tokens] receives the
+ * flat slot table[i/16]*16 + i%16 of each new position i.  *cow_src and *cow_dst
+ * receive the copy-on-write pair, or -1/-1 if none. */
+pa_status pa_seq_append(pa_block_pool *pool, int32_t seq, int32_t n_tokens, int64_t *slots,
+                        int32_t *cow_src, int32_t *cow_dst);
+/* One token for each of n distinct sequences (a decode step), all or nothing.
+ * slots[n]; cow_pairs[2*n] receives the copy pairs in sequence order and
+ * *num_cow their count. */
+pa_status pa_seq_append_batch(pa_block_pool *pool, const int32_t *seq_ids, int32_t n,
+                              int64_t *slots, int32_t *cow_pairs, int32_t *num_cow);
+pa_status pa_seq_free(pa_block_pool *pool, int32_t seq);
+/* Token count of a sequence, or -1 for an invalid id. */
+int32_t pa_seq_num_tokens(const pa_block_pool *pool, int32_t seq);
+/* Tables [n][max_blocks] padded with -1, and context lengths [n]. */
+pa_status pa_seq_export(const pa_block_pool *pool, const int32_t *seq_ids, int32_t n,
+                        int32_t max_blocks, int32_t *tables_out, int32_t *context_lens_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

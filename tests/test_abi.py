@@ -1,0 +1,96 @@
+"""The C-ABI library loads and exports every declared entry point (no GPU).
+
+Only host-side paths run here: symbol lookup, argument validation that returns
+before any launch, and the workspace / partition arithmetic.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_65_amd import binding as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(pa.LIB_PATH)
+    names = _declared()
+    assert len(names) >= 20
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in pa.pa_version()
+
+
+def _params(**over):
+    p = pa.pa_decode_params(
+        ctypes.c_void_p(16), ctypes.c_void_p(32), ctypes.c_void_p(48), ctypes.c_void_p(64),
+        ctypes.c_void_p(80), ctypes.c_void_p(96), 64, 64, 8, 128, 256, 20000, 4096, 0.088,
+        pa.PA_BF16, pa.PA_BF16, 0, pa.PA_KERNEL_AUTO)
+    for k, v in over.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_workspace_and_partition_arithmetic():
+    p = _params()
+    assert pa.pa_decode_partition_tokens(p) == 512
+    # m and l plus a D-wide accumulator per (seq, q head, partition), float32
+    assert pa.pa_decode_workspace_bytes(p) == 64 * 64 * 8 * (128 + 2) * 4
+    p.max_context_len = 300
+    assert pa.pa_decode_partition_tokens(p) == 304
+    assert pa.pa_decode_workspace_bytes(p) == 0
+    p.partition_tokens = 64
+    assert pa.pa_decode_workspace_bytes(p) == 64 * 64 * 5 * 130 * 4
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 96, pa.PA_ERR_UNSUPPORTED),
+    ("num_kv_heads", 7, pa.PA_ERR_INVALID_ARG),
+    ("num_q_heads", 256, pa.PA_ERR_UNSUPPORTED),
+    ("partition_tokens", 24, pa.PA_ERR_INVALID_ARG),
+    ("out_dtype", pa.PA_F16, pa.PA_ERR_UNSUPPORTED),
+    ("q", ctypes.c_void_p(33), pa.PA_ERR_INVALID_ARG),
+    ("k_cache", None, pa.PA_ERR_INVALID_ARG),
+    ("kernel", 9, pa.PA_ERR_INVALID_ARG),
+])
+def test_decode_rejects_bad_parameters_before_launch(field, value, status):
+    p = _params(**{field: value})
+    assert pa.lib().pa_decode(ctypes.byref(p), None, 0, None) == status
+    assert pa.lib().pa_last_error().decode().startswith("pa_decode")
+
+
+def test_decode_requires_the_workspace():
+    p = _params()
+    assert pa.lib().pa_decode(ctypes.byref(p), None, 0, None) == pa.PA_ERR_WORKSPACE
+
+
+def test_mfma_kernel_rejects_fp32():
+    p = _params(kv_dtype=pa.PA_F32, out_dtype=pa.PA_F32, kernel=pa.PA_KERNEL_MFMA)
+    assert pa.lib().pa_decode(ctypes.byref(p), None, 0, None) == pa.PA_ERR_UNSUPPORTED
+
+
+def test_append_and_copy_reject_bad_sizes():
+    L = pa.lib()
+    assert L.pa_reshape_and_cache(None, None, None, None, None, 4, 8, 96, 10, pa.PA_BF16, None) \
+        == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_reshape_and_cache(None, None, None, None, None, 4, 8, 128, 10, pa.PA_BF16, None) \
+        == pa.PA_ERR_INVALID_ARG
+    assert L.pa_reshape_and_cache(None, None, None, None, None, 0, 8, 128, 10, pa.PA_BF16, None) \
+        == pa.PA_OK
+    assert L.pa_copy_blocks(None, None, None, -1, 8, 128, 10, pa.PA_BF16, None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_copy_blocks(None, None, None, 0, 8, 128, 10, pa.PA_BF16, None) == pa.PA_OK
