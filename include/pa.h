@@ -143,6 +143,24 @@ size_t pa_decode_workspace_bytes(const pa_decode_params *p);
 pa_status pa_decode(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* pa_decode in its two launches, for callers that time, overlap or combine
+ * them.  pa_decode_partitions runs the partition kernel: it writes the final
+ * rows of sequences whose context fits one partition, and for the others one
+ * partial per (sequence, query head, partition) into the workspace:
+ *   float32 [num_seqs][num_q_heads][P][2]  (m, l): m = max score in log2
+ *           units (score * log2(e)), l = sum of 2^(score*log2(e) - m)
+ *   float32 [num_seqs][num_q_heads][P][head_dim]  sum of 2^(...) * V rows
+ * (the second array follows the first; P = ceil(max_context_len /
+ * partition_tokens)).  pa_decode_merge folds those partials into the output
+ * rows: M = max_p m_p, out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+ * Partials of one sequence computed elsewhere (e.g. other devices holding
+ * other context ranges) can be merged the same way.  Both calls take the same
+ * parameters and workspace as pa_decode. */
+pa_status pa_decode_partitions(const pa_decode_params *p, void *workspace,
+                               size_t workspace_bytes, void *stream);
+pa_status pa_decode_merge(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
 /* ------------------------------------------------------------------------
  * KV append through a slot mapping.
  * For each new token n < num_tokens with slot s = slot_mapping[n] >= 0, and

@@ -61,6 +61,8 @@ def lib():
             "pa_decode_partition_tokens": (_I32, [ctypes.POINTER(pa_decode_params)]),
             "pa_decode_workspace_bytes": (_SZ, [ctypes.POINTER(pa_decode_params)]),
             "pa_decode": (ctypes.c_int, [ctypes.POINTER(pa_decode_params), _P, _SZ, _P]),
+            "pa_decode_partitions": (ctypes.c_int, [ctypes.POINTER(pa_decode_params), _P, _SZ, _P]),
+            "pa_decode_merge": (ctypes.c_int, [ctypes.POINTER(pa_decode_params), _P, _SZ, _P]),
             "pa_reshape_and_cache": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                                     ctypes.c_int, _P]),
             "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, ctypes.c_int, _P]),
@@ -162,6 +164,24 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().pa_decode(ctypes.byref(params), ws_ptr, ws_bytes, _stream(stream)))
     return out
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _dev(workspace), workspace.numel() * workspace.element_size()
+
+
+def pa_decode_partitions(params: pa_decode_params, workspace=None, stream=None):
+    """Partition kernel only, on prebuilt parameters (see include/pa.h)."""
+    ptr, n = _ws(workspace)
+    _check(lib().pa_decode_partitions(ctypes.byref(params), ptr, n, _stream(stream)))
+
+
+def pa_decode_merge(params: pa_decode_params, workspace=None, stream=None):
+    """Merge kernel only, on prebuilt parameters (see include/pa.h)."""
+    ptr, n = _ws(workspace)
+    _check(lib().pa_decode_merge(ctypes.byref(params), ptr, n, _stream(stream)))
 
 
 def pa_reshape_and_cache(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):

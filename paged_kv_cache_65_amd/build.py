@@ -21,6 +21,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     # packed fp32 instructions stay off: plain float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in VGPRs: the softmax rescale then works on them in place
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

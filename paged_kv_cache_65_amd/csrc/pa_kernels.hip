@@ -43,6 +43,7 @@ constexpr int kWaves = 4;      // waves per partition workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kGMax = 16;      // query heads per KV head (MFMA column tile)
 constexpr int kDMax = 128;
+constexpr float kLazyLog2 = 8.0f;  // MFMA path: softmax weights stay below 2^8
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -88,6 +89,47 @@ __device__ inline void store_out(void *out, int64_t idx, float v, int out_dtype)
 
 __device__ inline float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Cross-lane combines that stay in the vector ALU (no LDS round trip).
+// permlane16_swap / permlane32_swap of a value with itself leave, in the two
+// results, the lane's own value and the value of the lane 16 (resp. 32)
+// apart; DPP quad permutes and row mirrors pair lanes inside a 16-lane row.
+__device__ inline float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Reductions over the 16 lanes of a row: quad_perm [1,0,3,2], [2,3,0,1],
+// then row_half_mirror and row_mirror.
+__device__ inline float row_max16(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  return fmaxf(x, dpp<0x140>(x));
+}
+__device__ inline float row_sum16(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  return x + dpp<0x140>(x);
+}
+// 2^x for x <= 0 (one v_exp_f32; results below 2^-126 flush to zero).
+__device__ inline float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---------------------------------------------------------------- arguments
 struct DecodeArgs {
   void *out;
@@ -98,7 +140,7 @@ struct DecodeArgs {
   const int32_t *context_lens;
   float *ws_ml;   // [S][Hq][max_parts][2]  (m in log2 units, l)
   float *ws_acc;  // [S][Hq][max_parts][D]  unnormalised weighted V sums
-  int32_t num_q_heads, num_kv_heads, group, max_blocks, num_blocks, max_ctx, max_parts,
+  int32_t num_seqs, num_q_heads, num_kv_heads, group, max_blocks, num_blocks, max_ctx, max_parts,
       part_tokens, out_dtype;
   float scale_log2;
 };
@@ -138,6 +180,10 @@ struct MfmaWave {
   static constexpr int NC = D / 32;  // 16-byte fragments per tile
   static constexpr int NT = D / 16;  // output tiles
   static constexpr int TILE = kBS * D * 2;
+#ifndef PA_MFMA_RING
+#define PA_MFMA_RING 3
+#endif
+  static constexpr int kRing = PA_MFMA_RING;  // blocks held in registers per wave
   using v8 = typename std::conditional<DT == PA_BF16, bf16x8_t, f16x8_t>::type;
 
   struct Frag {
@@ -176,9 +222,9 @@ struct MfmaWave {
     const u32x4_t *kp = reinterpret_cast<const u32x4_t *>(ktile);
     const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(vtile);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) f.k[c] = kp[c * 64 + lane];
+    for (int c = 0; c < NC; ++c) f.k[c] = __builtin_nontemporal_load(&kp[c * 64 + lane]);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) f.v[c] = vp[c * 64 + lane];
+    for (int c = 0; c < NC; ++c) f.v[c] = __builtin_nontemporal_load(&vp[c * 64 + lane]);
   }
 
   __device__ static f32x4_t mma_qk(const v8 &a, const v8 &b, f32x4_t c) {
@@ -238,17 +284,23 @@ struct MfmaWave {
       for (int v = 0; v < 4; ++v) s[v] = (4 * tq + v < valid) ? s[v] : -INFINITY;
     }
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = exp2f(m - m_new);
+    mx = max_xor32(max_xor16(mx));
+    // Lazy reference max: the state is rescaled only when a head's block max
+    // exceeds its reference by more than kLazyLog2, so weights stay below
+    // 2^kLazyLog2 and most blocks skip the rescale (a wave-uniform branch).
+    const bool bump = mx > m + kLazyLog2;
+    if (__builtin_amdgcn_ballot_w64(bump)) {
+      const float m_new = bump ? mx : m;
+      const float alpha = exp2_neg(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+      m = m_new;
+    }
     float p[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) p[v] = exp2f(s[v] - m_new);
-    l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    m = m_new;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+    for (int v = 0; v < 4; ++v) p[v] = __builtin_amdgcn_exp2f(s[v] - m);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
     u32x2_t ph, pl;
     split(p, ph, pl);
 #pragma unroll
@@ -265,8 +317,7 @@ struct MfmaWave {
   // Publishes this wave's state for the group's heads into LDS.
   __device__ void finish(Smem &sm, int w, int lane, int G) {
     const int r = lane % 16, tq = lane / 16;
-    float lt = l + shfl_xor(l, 16);
-    lt += shfl_xor(lt, 32);
+    const float lt = sum_xor32(sum_xor16(l));
     if (r < G) {
 #pragma unroll
       for (int n = 0; n < NT; ++n)
@@ -296,6 +347,7 @@ struct ValuWave {
   static constexpr int NCF = D * EB / 64;  // 16-byte fragments per lane per tile
   static constexpr int VD = D / 16;        // V dims per lane
   static constexpr int TILE = kBS * D * EB;
+  static constexpr int kRing = 2;
   using Smem = SmemValu;
 
   struct Frag {
@@ -334,9 +386,9 @@ struct ValuWave {
     const u32x4_t *kp = reinterpret_cast<const u32x4_t *>(ktile);
     const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(vtile);
 #pragma unroll
-    for (int c = 0; c < NCF; ++c) f.k[c] = kp[c * 64 + lane];
+    for (int c = 0; c < NCF; ++c) f.k[c] = __builtin_nontemporal_load(&kp[c * 64 + lane]);
 #pragma unroll
-    for (int c = 0; c < NCF; ++c) f.v[c] = vp[c * 64 + lane];
+    for (int c = 0; c < NCF; ++c) f.v[c] = __builtin_nontemporal_load(&vp[c * 64 + lane]);
   }
 
   // element e (0..X-1) of a 16-byte fragment as float
@@ -367,17 +419,12 @@ struct ValuWave {
 #pragma unroll
           for (int e = 0; e < X; ++e) part = fmaf(qv[e], kf[c * X + e], part);
         }
-        part += shfl_xor(part, 16);
-        part += shfl_xor(part, 32);
+        part = sum_xor32(sum_xor16(part));
         const float sv = (r < valid) ? part * scale_log2 : -INFINITY;
-        float mx = sv;
-        mx = fmaxf(mx, shfl_xor(mx, 1));
-        mx = fmaxf(mx, shfl_xor(mx, 2));
-        mx = fmaxf(mx, shfl_xor(mx, 4));
-        mx = fmaxf(mx, shfl_xor(mx, 8));
+        const float mx = row_max16(sv);
         const float m_new = fmaxf(m[h], mx);
-        const float alpha = exp2f(m[h] - m_new);
-        const float pv = exp2f(sv - m_new);
+        const float alpha = exp2_neg(m[h] - m_new);
+        const float pv = exp2_neg(sv - m_new);
         l[h] = l[h] * alpha + pv;
         m[h] = m_new;
         if (tq == 0) sm.ps[w][h][r] = pv;
@@ -415,16 +462,10 @@ struct ValuWave {
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
       if (h < G) {
-        float lt = l[h];
-        lt += shfl_xor(lt, 1);
-        lt += shfl_xor(lt, 2);
-        lt += shfl_xor(lt, 4);
-        lt += shfl_xor(lt, 8);
+        const float lt = row_sum16(l[h]);
 #pragma unroll
         for (int k = 0; k < VD; ++k) {
-          float a = acc[h][k];
-          a += shfl_xor(a, 16);
-          a += shfl_xor(a, 32);
+          const float a = sum_xor32(sum_xor16(acc[h][k]));
           const int dim = (k / (X / 4)) * 4 * X + (k % (X / 4)) * 16 + r;
           if (tq == 0) sm.acc[w][h][dim] = a;
         }
@@ -459,7 +500,13 @@ __device__ void write_partial_nan(const DecodeArgs &a, int s, int h0, int G, int
 template <class W, int D, bool kMfma>
 __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeArgs a) {
   __shared__ typename W::Smem sm;
-  const int p = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  // 1-D grid, KV head fastest, then sequence, then partition.  Workgroups are
+  // dealt round-robin to the 8 XCDs by linear id, so this order spreads every
+  // sequence's (unequal) partitions evenly over the XCDs; with the partition
+  // index fastest, partition p of every sequence would land on the same XCD.
+  const int g = blockIdx.x % a.num_kv_heads;
+  const int s = (blockIdx.x / a.num_kv_heads) % a.num_seqs;
+  const int p = blockIdx.x / (a.num_kv_heads * a.num_seqs);
   const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
   const int G = a.group;
   const int h0 = g * G;
@@ -483,41 +530,68 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeArgs a) {
 
   W wave;
   wave.stage(a, sm, s, g, tid);
-  int bad = 0;
-  for (int j = tid; j < nblk; j += kThreads) bad |= (uint32_t)trow[j] >= (uint32_t)a.num_blocks;
-  bad = __syncthreads_or(bad);
-  if (bad) {
+  wave.init(a, sm, s, g, lane);
+  if constexpr (!kMfma) __syncthreads();  // q staged in LDS
+  int bad = 0;  // a block id outside the pool was seen (never dereferenced)
+
+  const int64_t head_off = (int64_t)g * W::TILE;
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * W::TILE;
+  // Each wave streams its blocks (w, w+4, w+8, ...) through a ring of NB
+  // register fragments: block i is computed while blocks i+1 .. i+NB-1 are in
+  // flight, so every wave keeps (NB-1) x 2 tiles of loads outstanding.
+  constexpr int NB = W::kRing;
+  typename W::Frag fr[NB];
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int nmine = nblk > wu ? (nblk - wu + kWaves - 1) / kWaves : 0;
+  // Each wave streams its blocks (wu, wu+4, wu+8, ...) through a ring of NB
+  // register fragments: block i is computed while blocks i+1 .. i+NB-1 are in
+  // flight.  Block ids come 64 at a time, one per lane, and are read into
+  // scalar registers.  Every ring slot is refilled unconditionally (past the
+  // end a wave re-reads its last block, a valid address that hits in cache),
+  // so the number of loads in flight is the same on every path and the
+  // compiler's wait counts never drain the ring early.
+  for (int c0 = 0; c0 < nmine; c0 += 64) {
+    const int nc = min(64, nmine - c0);
+    int ids = lane < nc ? trow[wu + (c0 + lane) * kWaves] : 0;
+    const bool id_ok = (uint32_t)ids < (uint32_t)a.num_blocks;
+    if (__builtin_amdgcn_ballot_w64(!id_ok)) bad = 1;
+    ids = id_ok ? ids : 0;
+    // Past the end of the chunk a ring slot is refilled with a dummy load of
+    // the same shape in which every lane reads the pool's first 16 bytes.
+    auto refill = [&](typename W::Frag &f, int i) {
+      const bool real = i < nc;
+      const int64_t off = real ? (int64_t)__builtin_amdgcn_readlane(ids, min(i, nc - 1)) * blk_stride + head_off : 0;
+      W::load(f, a.k_cache + off, a.v_cache + off, real ? lane : 0);
+    };
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b) {
+      refill(fr[b], b);
+      __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
+    }
+    for (int i0 = 0; i0 < nc; i0 += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int i = i0 + b;
+        refill(fr[(b + NB - 1) % NB], i + NB - 1);
+        if (i < nc) {
+          const int j = wu + (c0 + i) * kWaves;
+          const int valid = (j == nblk - 1) ? last_valid : kBS;
+          if constexpr (kMfma)
+            wave.compute(fr[b], valid, a.scale_log2, lane);
+          else
+            wave.compute(fr[b], valid, a.scale_log2, lane, sm, w, G);
+        }
+      }
+    }
+  }
+  wave.finish(sm, w, lane, G);
+  if (__syncthreads_or(bad)) {
     if (nparts == 1)
       write_rows<D>(a, s, h0, G, NAN);
     else
       write_partial_nan<D>(a, s, h0, G, p);
     return;
   }
-  wave.init(a, sm, s, g, lane);
-
-  const int64_t head_off = (int64_t)g * W::TILE;
-  const int64_t blk_stride = (int64_t)a.num_kv_heads * W::TILE;
-  typename W::Frag cur, nxt;
-  int j = w;
-  if (j < nblk) {
-    const int64_t off = (int64_t)trow[j] * blk_stride + head_off;
-    W::load(cur, a.k_cache + off, a.v_cache + off, lane);
-  }
-  for (; j < nblk; j += kWaves) {
-    const int jn = j + kWaves;
-    if (jn < nblk) {
-      const int64_t off = (int64_t)trow[jn] * blk_stride + head_off;
-      W::load(nxt, a.k_cache + off, a.v_cache + off, lane);
-    }
-    const int valid = (j == nblk - 1) ? last_valid : kBS;
-    if constexpr (kMfma)
-      wave.compute(cur, valid, a.scale_log2, lane);
-    else
-      wave.compute(cur, valid, a.scale_log2, lane, sm, w, G);
-    cur = nxt;
-  }
-  wave.finish(sm, w, lane, G);
-  __syncthreads();
 
   // Fold the four wave states: M = max m_w, out = sum 2^(m_w-M) acc_w / sum 2^(m_w-M) l_w.
   for (int i = tid; i < G * D; i += kThreads) {
@@ -547,33 +621,61 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- merge kernel
-// One 64-lane workgroup per (query head, sequence) with more than one
-// partition: M = max_p m_p, out = sum_p 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p.
-// A NaN partial (bad table entry) makes the row NaN.
+// One wave per (sequence, query head) row with more than one partition:
+//   M = max_p m_p,  out = sum_p 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p.
+// Lanes read the (m, l) pairs in parallel; each lane then owns D/64 output
+// dims and sums the partitions' accumulators.  A NaN partial (bad table
+// entry) makes the row NaN.
+constexpr int kMergeWaves = 4;
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, shfl_xor(v, o));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += shfl_xor(v, o);
+  return v;
+}
+
 template <int D>
-__global__ __launch_bounds__(64) void pa_merge_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+__global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_kernel(DecodeArgs a, int32_t num_rows) {
+  constexpr int PER = D / 64;  // output dims per lane
+  const int lane = threadIdx.x % 64;
+  const int64_t row = (int64_t)blockIdx.x * kMergeWaves + threadIdx.x / 64;
+  if (row >= num_rows) return;
+  const int s = (int)(row / a.num_q_heads);
   const int L = a.context_lens[s];
   if (!ctx_valid(L, a)) return;
   const int np = (L + a.part_tokens - 1) / a.part_tokens;
   if (np <= 1) return;
-  const int64_t row = (int64_t)s * a.num_q_heads + h;
   const float *ml = a.ws_ml + row * a.max_parts * 2;
   const float *acc = a.ws_acc + row * a.max_parts * D;
-  float M = -INFINITY;
-  bool nan = false;
-  for (int q = 0; q < np; ++q) {
+  float M = -INFINITY, nan = 0.f;
+  for (int q = lane; q < np; q += 64) {
     const float mq = ml[2 * q];
-    nan |= mq != mq;
+    nan += (mq != mq) ? 1.f : 0.f;
     M = fmaxf(M, mq);
   }
+  M = wave_max(M);
+  nan = wave_sum(nan);
   float den = 0.f;
-  for (int q = 0; q < np; ++q) den += exp2f(ml[2 * q] - M) * ml[2 * q + 1];
-  for (int d = lane; d < D; d += 64) {
-    float num = 0.f;
-    for (int q = 0; q < np; ++q) num += exp2f(ml[2 * q] - M) * acc[(int64_t)q * D + d];
-    store_out(a.out, row * D + d, nan ? NAN : num / den, a.out_dtype);
+  for (int q = lane; q < np; q += 64) den += exp2f(ml[2 * q] - M) * ml[2 * q + 1];
+  den = wave_sum(den);
+  float num[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) num[e] = 0.f;
+#pragma unroll 4
+  for (int q = 0; q < np; ++q) {
+    const float wq = exp2f(ml[2 * q] - M);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) num[e] += wq * acc[(int64_t)q * D + lane * PER + e];
   }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    store_out(a.out, row * D + lane * PER + e, nan > 0.f ? NAN : num[e] * inv, a.out_dtype);
 }
 
 // ---------------------------------------------------------------- KV append
@@ -739,18 +841,23 @@ size_t pa_decode_workspace_bytes(const pa_decode_params *p) {
   return (size_t)p->num_seqs * p->num_q_heads * np * (p->head_dim + 2) * sizeof(float);
 }
 
-pa_status pa_decode(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
-                    void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates, checks the workspace and fills the kernel arguments.
+pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
+                  const char *who, DecodeArgs &a) {
   pa_status st = validate(p);
   if (st != PA_OK) return st;
   const int32_t pt = resolve_partition(p);
   const int32_t np = num_partitions(p, pt);
+  if ((int64_t)np * p->num_kv_heads * p->num_seqs > INT32_MAX)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: more than 2^31-1 workgroups (raise partition_tokens)", who);
   const size_t need = pa_decode_workspace_bytes(p);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-    return pa::fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes (16-byte aligned) required, got %zu",
-                    need, workspace ? workspace_bytes : (size_t)0);
-  if (p->num_seqs == 0) return PA_OK;
-  DecodeArgs a;
+    return pa::fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu",
+                    who, need, workspace ? workspace_bytes : (size_t)0);
   a.out = p->out;
   a.q = p->q;
   a.k_cache = static_cast<const uint8_t *>(p->k_cache);
@@ -760,6 +867,7 @@ pa_status pa_decode(const pa_decode_params *p, void *workspace, size_t workspace
   const size_t rows = (size_t)p->num_seqs * p->num_q_heads * np;
   a.ws_ml = need ? static_cast<float *>(workspace) : nullptr;
   a.ws_acc = need ? static_cast<float *>(workspace) + rows * 2 : nullptr;
+  a.num_seqs = p->num_seqs;
   a.num_q_heads = p->num_q_heads;
   a.num_kv_heads = p->num_kv_heads;
   a.group = p->num_q_heads / p->num_kv_heads;
@@ -770,23 +878,58 @@ pa_status pa_decode(const pa_decode_params *p, void *workspace, size_t workspace
   a.part_tokens = pt;
   a.out_dtype = p->out_dtype;
   a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  return PA_OK;
+}
+
+pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipStream_t hs) {
   const bool mfma = p->kernel == PA_KERNEL_MFMA || (p->kernel == PA_KERNEL_AUTO && p->kv_dtype != PA_F32);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  const dim3 grid(np, p->num_kv_heads, p->num_seqs);
+  const dim3 grid((unsigned)((int64_t)a.max_parts * p->num_kv_heads * p->num_seqs));
   if (p->head_dim == 128)
     launch_partition<128>(p->kv_dtype, mfma, a.group, grid, hs, a);
   else
     launch_partition<64>(p->kv_dtype, mfma, a.group, grid, hs, a);
-  if ((st = hip_check(hipGetLastError(), "pa_decode partition launch")) != PA_OK) return st;
-  if (np > 1) {
-    const dim3 mgrid(p->num_q_heads, p->num_seqs);
-    if (p->head_dim == 128)
-      hipLaunchKernelGGL(pa_merge_kernel<128>, mgrid, dim3(64), 0, hs, a);
-    else
-      hipLaunchKernelGGL(pa_merge_kernel<64>, mgrid, dim3(64), 0, hs, a);
-    if ((st = hip_check(hipGetLastError(), "pa_decode merge launch")) != PA_OK) return st;
-  }
-  return PA_OK;
+  return hip_check(hipGetLastError(), "pa_decode partition launch");
+}
+
+pa_status launch_merge(const pa_decode_params *p, const DecodeArgs &a, hipStream_t hs) {
+  if (a.max_parts <= 1) return PA_OK;
+  const int32_t rows = p->num_seqs * p->num_q_heads;
+  const dim3 mgrid((rows + kMergeWaves - 1) / kMergeWaves);
+  if (p->head_dim == 128)
+    hipLaunchKernelGGL(pa_merge_kernel<128>, mgrid, dim3(kMergeWaves * 64), 0, hs, a, rows);
+  else
+    hipLaunchKernelGGL(pa_merge_kernel<64>, mgrid, dim3(kMergeWaves * 64), 0, hs, a, rows);
+  return hip_check(hipGetLastError(), "pa_decode merge launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  DecodeArgs a;
+  pa_status st = prepare(p, workspace, workspace_bytes, "pa_decode", a);
+  if (st != PA_OK || p->num_seqs == 0) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = launch_partitions(p, a, hs)) != PA_OK) return st;
+  return launch_merge(p, a, hs);
+}
+
+pa_status pa_decode_partitions(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  DecodeArgs a;
+  pa_status st = prepare(p, workspace, workspace_bytes, "pa_decode_partitions", a);
+  if (st != PA_OK || p->num_seqs == 0) return st;
+  return launch_partitions(p, a, static_cast<hipStream_t>(stream));
+}
+
+pa_status pa_decode_merge(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  DecodeArgs a;
+  pa_status st = prepare(p, workspace, workspace_bytes, "pa_decode_merge", a);
+  if (st != PA_OK || p->num_seqs == 0) return st;
+  return launch_merge(p, a, static_cast<hipStream_t>(stream));
 }
 
 pa_status pa_reshape_and_cache(const void *k_new, const void *v_new, void *k_cache, void *v_cache,

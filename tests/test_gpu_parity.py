@@ -319,3 +319,21 @@ def test_workload_5_long_context_loop_sampled_steps():
             assert err <= 2e-3
     torch.cuda.synchronize()
     _assert_caches_equal(gst, ost, "bf16")
+
+
+def test_split_launches_equal_pa_decode_bitwise():
+    spec = workloads.custom(seed=65, dtype="bf16", lens=(1500, 20, 700), num_q_heads=16,
+                            num_kv_heads=2, head_dim=128)
+    wl = workloads.generate(spec)
+    gst = gpu_side.build(wl)
+    mb = oracle_side.max_blocks_for(wl)
+    whole = gpu_side.decode(wl, gst, mb, out_dtype="f32", partition_tokens=256)
+    tab_d, lens_d, _, l = gpu_side.tables(gst, mb)
+    q = gpu_side.to_device(wl.q, "bf16")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    params = pa.make_decode_params(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, 2,
+                                   int(l.max()), spec.fp32_scale(), partition_tokens=256)
+    ws = torch.empty(pa.pa_decode_workspace_bytes(params), dtype=torch.uint8, device="cuda")
+    pa.pa_decode_partitions(params, ws)
+    pa.pa_decode_merge(params, ws)
+    assert torch.equal(out, whole)
