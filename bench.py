@@ -4,8 +4,8 @@
 One step is one pass of the whole hot path over the batch:
   1. host block pool: append one token to every sequence (a new block at each
      16-token boundary; copy-on-write pairs if a shared block is written),
-  2. the step's slots, block tables and context lengths go to the device on a
-     copy stream (pinned staging, overlapped with the previous step's kernels),
+  2. the step's slots, block tables and context lengths go to the device
+     (pinned staging, one copy on the compute stream),
   3. pa_copy_blocks (only when the pool asked for a copy),
   4. pa_reshape_and_cache writes the new tokens' K/V through the slots,
   5. pa_decode_partitions + pa_decode_merge (paged decode attention).
@@ -135,7 +135,6 @@ class Replica:
     out: object
     max_ctx: int
     copied: object
-    last_use: object
     lens_host: np.ndarray
 
 
@@ -178,8 +177,7 @@ def build_replica(pa, torch, wl, order, k_rows_d, v_rows_d, MB, S, dev):
     stage = torch.empty(words, dtype=torch.int32, pin_memory=True)
     desc = torch.empty(words, dtype=torch.int32, device=dev)
     tab, lens = pool.seq_export(ids, MB)
-    return Replica(pool, ids, kc, vc, stage, desc, None, None, int(lens.max()), None, None,
-                   lens.copy())
+    return Replica(pool, ids, kc, vc, stage, desc, None, None, int(lens.max()), None, lens.copy())
 
 
 def run_gpu(args, wl):
@@ -229,13 +227,15 @@ def run_gpu(args, wl):
     part_tokens = pa.pa_decode_partition_tokens(reps[0].params)
 
     hip = Hip()
+    # One stream: the small host-to-device copy of the step inputs is ordered
+    # behind the previous step's kernels on the same queue.  (On a second
+    # stream, a copy that waits on a compute-stream event blocked the host for
+    # most of a step.)  The host only waits before it reuses a replica's
+    # pinned staging buffer, i.e. R steps behind.
     compute = hip.stream()
-    copy = hip.stream()
     for rep in reps:
         rep.copied = hip.event()
-        rep.last_use = hip.event()
-        hip.record(rep.copied, copy)       # both start "done"
-        hip.record(rep.last_use, compute)
+        hip.record(rep.copied, compute)    # starts "done"
     cs = ctypes.c_void_p(compute)
     ids_ptr = [rep.seq_ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) for rep in reps]
     ncow = ctypes.c_int32()
@@ -268,7 +268,7 @@ def run_gpu(args, wl):
         r = i % R
         rep, pp = reps[r], ptrs[r]
         w0 = time.perf_counter()
-        hip.sync_event(rep.copied)                     # staging buffer free again
+        hip.sync_event(rep.copied)                     # its last copy has run: staging free
         waited[0] += time.perf_counter() - w0
         st = L.pa_seq_append_batch(pool_h[r], ids_ptr[r], S, pp["slots"], pp["cow"], ctypes.byref(ncow))
         if st:
@@ -278,10 +278,8 @@ def run_gpu(args, wl):
             pa._check(st)
         rep.max_ctx += 1
         rep.params.max_context_len = rep.max_ctx
-        hip.wait(copy, rep.last_use)                   # previous kernels on this replica done
-        hip.h2d(pp["desc"], pp["stage"], stage_bytes, copy)
-        hip.record(rep.copied, copy)
-        hip.wait(compute, rep.copied)
+        hip.h2d(pp["desc"], pp["stage"], stage_bytes, compute)
+        hip.record(rep.copied, compute)
         if ncow.value:
             pa._check(L.pa_copy_blocks(pp["kc"], pp["vc"], pp["cows_d"], ncow.value, Hkv, D,
                                        nb_rep, dt_code, cs))
@@ -294,7 +292,6 @@ def run_gpu(args, wl):
         if timed_idx >= 0:
             hip.record(ev_b[timed_idx], compute)
         pa._check(L.pa_decode_merge(ctypes.byref(rep.params), ws_ptr, ws_bytes, cs))
-        hip.record(rep.last_use, compute)
         if timed_idx >= 0:
             lens_log.append(pp["lens_np"].copy())
 
@@ -450,7 +447,7 @@ def main():
             "mean_context": round(mean_kv_tokens / spec.num_seqs, 1),
             "partition_tokens": g["part_tokens"], "replicas": args.replicas,
             "kernel": args.kernel, "seed": spec.seed,
-            "step": "pool append + H2D tables + reshape_and_cache + decode partitions + merge",
+            "step": "pool append + H2D slots/tables/lens + reshape_and_cache + decode partitions + merge",
             "device": g["device"],
         },
         "roofline": {
