@@ -5,10 +5,13 @@ One step is one pass of the whole hot path over the batch:
   1. host block pool: append one token to every sequence (a new block at each
      16-token boundary; copy-on-write pairs if a shared block is written),
   2. the step's slots, block tables and context lengths go to the device
-     (pinned staging, one copy on the compute stream),
+     (pinned staging; copied on a second stream while the previous step's
+     kernels run),
   3. pa_copy_blocks (only when the pool asked for a copy),
-  4. pa_reshape_and_cache writes the new tokens' K/V through the slots,
-  5. pa_decode_partitions + pa_decode_merge (paged decode attention).
+  4. pa_decode_partitions: one launch that appends the new tokens' K/V
+     through the slots and attends (with --append separate,
+     pa_reshape_and_cache runs first instead),
+  5. pa_decode_merge: log-sum-exp merge of split contexts.
 Steps rotate over --replicas independent pools (own caches, tables, block
 placement) so the working set is several times the 256 MB Infinity Cache.
 
@@ -136,6 +139,7 @@ class Replica:
     max_ctx: int
     copied: object
     lens_host: np.ndarray
+    done: object = None
 
 
 def stage_layout(S, MB):
@@ -222,23 +226,34 @@ def run_gpu(args, wl):
         ws_need = max(ws_need, pa.pa_decode_workspace_bytes(rep.params))
         rep.params.max_context_len = rep.max_ctx
         rep.slots_v = slots_v
+        if args.append == "fused":
+            rep.params.k_new = step_k_d.data_ptr()
+            rep.params.v_new = step_v_d.data_ptr()
+            rep.params.slot_mapping = slots_v.data_ptr()
     ws = torch.empty(max(ws_need, 16), dtype=torch.uint8, device=dev)
     ws_ptr, ws_bytes = ctypes.c_void_p(ws.data_ptr()), ws.numel()
     part_tokens = pa.pa_decode_partition_tokens(reps[0].params)
 
     hip = Hip()
-    # One stream: the small host-to-device copy of the step inputs is ordered
-    # behind the previous step's kernels on the same queue.  (On a second
-    # stream, a copy that waits on a compute-stream event blocked the host for
-    # most of a step.)  The host only waits before it reuses a replica's
-    # pinned staging buffer, i.e. R steps behind.
+    # Two streams of default priority.  Step i+1's inputs are prepared on the
+    # host and copied on the copy stream while step i's kernels run; the host
+    # then waits for that copy (an event that is normally already complete)
+    # before launching step i+1, so the compute queue holds only kernels and
+    # never waits on the copy engine.  No GPU-side cross-stream waits are used:
+    # a copy that waited on a compute-stream event blocked the host for most
+    # of a step.  A replica's staging and device buffers are reused R steps
+    # later, after the host has seen that replica's previous kernels finish.
     compute = hip.stream()
+    copy = hip.stream()
     for rep in reps:
         rep.copied = hip.event()
-        hip.record(rep.copied, compute)    # starts "done"
+        rep.done = hip.event()
+        hip.record(rep.copied, copy)       # start "complete"
+        hip.record(rep.done, compute)
     cs = ctypes.c_void_p(compute)
     ids_ptr = [rep.seq_ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) for rep in reps]
-    ncow = ctypes.c_int32()
+    ncow = [0] * R
+    ncow_c = ctypes.c_int32()
     row_bytes = S * Hkv * D * step_k_d.element_size()
     nb_rep = wl.num_blocks
     ev_a = [hip.event(timing=True) for _ in range(K)]
@@ -261,42 +276,61 @@ def run_gpu(args, wl):
             lens_np=np.ctypeslib.as_array(ctypes.cast(base + 4 * lay["lens"], ctypes.POINTER(ctypes.c_int32)),
                                           shape=(S,))))
     pool_h = [rep.pool._h for rep in reps]
+    fused = args.append == "fused"
     k0, v0 = step_k_d.data_ptr(), step_v_d.data_ptr()
     torch.cuda.synchronize()
 
-    def step(i, timed_idx):
+    def prepare(i):
+        """Host pool append for step i and the copy of its inputs (copy stream)."""
         r = i % R
         rep, pp = reps[r], ptrs[r]
         w0 = time.perf_counter()
-        hip.sync_event(rep.copied)                     # its last copy has run: staging free
+        hip.sync_event(rep.done)                       # replica's previous step finished
         waited[0] += time.perf_counter() - w0
-        st = L.pa_seq_append_batch(pool_h[r], ids_ptr[r], S, pp["slots"], pp["cow"], ctypes.byref(ncow))
+        st = L.pa_seq_append_batch(pool_h[r], ids_ptr[r], S, pp["slots"], pp["cow"], ctypes.byref(ncow_c))
         if st:
             pa._check(st)
+        ncow[r] = ncow_c.value
         st = L.pa_seq_export(pool_h[r], ids_ptr[r], S, MB, pp["tab"], pp["lens"])
         if st:
             pa._check(st)
         rep.max_ctx += 1
         rep.params.max_context_len = rep.max_ctx
-        hip.h2d(pp["desc"], pp["stage"], stage_bytes, compute)
-        hip.record(rep.copied, compute)
-        if ncow.value:
-            pa._check(L.pa_copy_blocks(pp["kc"], pp["vc"], pp["cows_d"], ncow.value, Hkv, D,
+        hip.h2d(pp["desc"], pp["stage"], stage_bytes, copy)
+        hip.record(rep.copied, copy)
+
+    def launch(i, timed_idx):
+        """Step i's kernels (compute stream), once its inputs are on the device."""
+        r = i % R
+        rep, pp = reps[r], ptrs[r]
+        w0 = time.perf_counter()
+        hip.sync_event(rep.copied)
+        waited[0] += time.perf_counter() - w0
+        if ncow[r]:
+            pa._check(L.pa_copy_blocks(pp["kc"], pp["vc"], pp["cows_d"], ncow[r], Hkv, D,
                                        nb_rep, dt_code, cs))
-        pa._check(L.pa_reshape_and_cache(ctypes.c_void_p(k0 + i * row_bytes),
-                                         ctypes.c_void_p(v0 + i * row_bytes), pp["kc"], pp["vc"],
-                                         pp["slots_d"], S, Hkv, D, nb_rep, dt_code, cs))
+        if fused:
+            rep.params.k_new = k0 + i * row_bytes
+            rep.params.v_new = v0 + i * row_bytes
+        else:
+            pa._check(L.pa_reshape_and_cache(ctypes.c_void_p(k0 + i * row_bytes),
+                                             ctypes.c_void_p(v0 + i * row_bytes), pp["kc"], pp["vc"],
+                                             pp["slots_d"], S, Hkv, D, nb_rep, dt_code, cs))
         if timed_idx >= 0:
             hip.record(ev_a[timed_idx], compute)
         pa._check(L.pa_decode_partitions(ctypes.byref(rep.params), ws_ptr, ws_bytes, cs))
         if timed_idx >= 0:
             hip.record(ev_b[timed_idx], compute)
         pa._check(L.pa_decode_merge(ctypes.byref(rep.params), ws_ptr, ws_bytes, cs))
+        hip.record(rep.done, compute)
         if timed_idx >= 0:
             lens_log.append(pp["lens_np"].copy())
 
+    total = W + K
+    prepare(0)
     for i in range(W):
-        step(i, -1)
+        launch(i, -1)
+        prepare(i + 1)
     hip.sync_device()
     log(f"warmup done ({W} steps); timing {K} steps")
     waited[0] = 0.0
@@ -304,7 +338,9 @@ def run_gpu(args, wl):
     host = 0.0
     for k in range(K):
         h0 = time.perf_counter()
-        step(W + k, k)
+        launch(W + k, k)
+        if W + k + 1 < total:
+            prepare(W + k + 1)
         host += time.perf_counter() - h0
     hip.sync_device()
     t1 = time.perf_counter()
@@ -389,6 +425,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--append", default="fused", choices=["fused", "separate"],
+                    help="append the step's K/V inside the decode launch, or with pa_reshape_and_cache")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -447,7 +485,9 @@ def main():
             "mean_context": round(mean_kv_tokens / spec.num_seqs, 1),
             "partition_tokens": g["part_tokens"], "replicas": args.replicas,
             "kernel": args.kernel, "seed": spec.seed,
-            "step": "pool append + H2D slots/tables/lens + reshape_and_cache + decode partitions + merge",
+            "step": ("pool append + H2D slots/tables/lens + decode partitions (fused K/V append) + merge"
+                     if args.append == "fused" else
+                     "pool append + H2D slots/tables/lens + reshape_and_cache + decode partitions + merge"),
             "device": g["device"],
         },
         "roofline": {

@@ -99,16 +99,18 @@ const char *pa_last_error(void);
  *   max_context_len  host-known upper bound on every context_lens[s]; it sizes
  *                 the launch grid
  *   scale         usually 1/sqrt(head_dim)
- *   partition_tokens  0 = automatic, else a positive multiple of 16
+ *   partition_tokens  0 = automatic (1024, 512 or 256 tokens: the largest
+ *                 that gives >= 8 workgroups per compute unit), else a
+ *                 positive multiple of 16
  * Supported: head_dim in {64, 128}; num_q_heads % num_kv_heads == 0;
  *   G <= 16; fp16/bf16 with any kernel, fp32 with the VALU kernel.
  * Contract violations found on the device (a table entry outside
  * [0, num_blocks), or L outside [0, min(max_context_len,
  * 16*max_blocks_per_seq)]) are never dereferenced: that sequence's output row
  * is set to NaN.
- * Workspace: pa_decode_workspace_bytes() bytes of device memory (may be 0);
- * it is scratch for this call only and may be reused once the stream passes
- * the call.
+ * Workspace: pa_decode_workspace_bytes() bytes of device memory (0 when no
+ * context is split); scratch for this call only (no initialization needed),
+ * reusable by any later call once the stream has passed this one.
  * ------------------------------------------------------------------------ */
 typedef struct pa_decode_params {
   void *out;
@@ -129,6 +131,19 @@ typedef struct pa_decode_params {
   pa_dtype out_dtype;
   int32_t partition_tokens;
   pa_kernel kernel;
+  /* Optional fused append (all three set, or all NULL).  Equivalent to
+   * pa_reshape_and_cache(k_new, v_new, ..., slot_mapping, num_seqs) followed
+   * by the decode, for a decode step that appends one token per sequence:
+   *   k_new, v_new  [num_seqs][num_kv_heads][head_dim], kv_dtype
+   *   slot_mapping  int64 [num_seqs]: the slot of position context_lens[s]-1,
+   *                 i.e. block_tables[s][(L-1)/16]*16 + (L-1)%16, or negative
+   *                 for no append.  Any other slot writes nothing and makes
+   *                 that sequence's row NaN.
+   * A block written this way must be private to its sequence (copy-on-write
+   * copies done beforehand with pa_copy_blocks). */
+  const void *k_new;
+  const void *v_new;
+  const int64_t *slot_mapping;
 } pa_decode_params;
 
 /* Partition size (tokens) pa_decode will use for these parameters, or a
@@ -153,6 +168,7 @@ pa_status pa_decode(const pa_decode_params *p, void *workspace, size_t workspace
  * (the second array follows the first; P = ceil(max_context_len /
  * partition_tokens)).  pa_decode_merge folds those partials into the output
  * rows: M = max_p m_p, out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+
  * Partials of one sequence computed elsewhere (e.g. other devices holding
  * other context ranges) can be merged the same way.  Both calls take the same
  * parameters and workspace as pa_decode. */

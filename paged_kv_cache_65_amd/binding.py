@@ -42,7 +42,8 @@ class pa_decode_params(ctypes.Structure):
                 ("num_seqs", _I32), ("num_q_heads", _I32), ("num_kv_heads", _I32),
                 ("head_dim", _I32), ("max_blocks_per_seq", _I32), ("num_blocks", _I32),
                 ("max_context_len", _I32), ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int),
-                ("out_dtype", ctypes.c_int), ("partition_tokens", _I32), ("kernel", ctypes.c_int)]
+                ("out_dtype", ctypes.c_int), ("partition_tokens", _I32), ("kernel", ctypes.c_int),
+                ("k_new", _P), ("v_new", _P), ("slot_mapping", _P)]
 
 
 _lib = None
@@ -128,14 +129,15 @@ def _stream(stream):
 
 
 def make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
-                       max_context_len, scale, partition_tokens=0, kernel="auto"):
+                       max_context_len, scale, partition_tokens=0, kernel="auto", k_new=None,
+                       v_new=None, slot_mapping=None):
     S, Hq, D = q.shape
     nb = k_cache.numel() // (num_kv_heads * BLOCK_SIZE * D)
     return pa_decode_params(
         _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), _dev(context_lens),
         S, Hq, num_kv_heads, D, block_tables.shape[1] if block_tables.dim() == 2 else 0, nb,
         int(max_context_len), float(scale), _dtype_code(k_cache), _dtype_code(out),
-        int(partition_tokens), KERNELS[kernel])
+        int(partition_tokens), KERNELS[kernel], _dev(k_new), _dev(v_new), _dev(slot_mapping))
 
 
 def pa_decode_workspace_bytes(params: pa_decode_params) -> int:
@@ -151,12 +153,14 @@ def pa_decode_partition_tokens(params: pa_decode_params) -> int:
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
               max_context_len, scale, partition_tokens=0, kernel="auto", workspace=None,
-              stream=None):
-    """out <- paged decode attention.  workspace: a uint8 device tensor, or None to
-    allocate one of pa_decode_workspace_bytes() bytes with torch."""
+              stream=None, k_new=None, v_new=None, slot_mapping=None):
+    """out <- paged decode attention (optionally appending k_new/v_new first).
+    workspace: a uint8 device tensor of at least pa_decode_workspace_bytes()
+    bytes (no initialization needed), or None to allocate one."""
     import torch
     params = make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens,
-                                num_kv_heads, max_context_len, scale, partition_tokens, kernel)
+                                num_kv_heads, max_context_len, scale, partition_tokens, kernel,
+                                k_new, v_new, slot_mapping)
     need = pa_decode_workspace_bytes(params)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

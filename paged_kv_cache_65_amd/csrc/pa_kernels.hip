@@ -140,6 +140,9 @@ struct DecodeArgs {
   const int32_t *context_lens;
   float *ws_ml;   // [S][Hq][max_parts][2]  (m in log2 units, l)
   float *ws_acc;  // [S][Hq][max_parts][D]  unnormalised weighted V sums
+  const uint8_t *k_new;          // fused append: [S][Hkv][D] rows of the step's token, or null
+  const uint8_t *v_new;
+  const int64_t *slot_mapping;   // fused append: [S] slot of position L-1 (negative = no append)
   int32_t num_seqs, num_q_heads, num_kv_heads, group, max_blocks, num_blocks, max_ctx, max_parts,
       part_tokens, out_dtype;
   float scale_log2;
@@ -154,11 +157,75 @@ struct __align__(16) SmemBase {
   float acc[kWaves][kGMax][kDMax];
   float m[kWaves][kGMax];
   float l[kWaves][kGMax];
+  uint32_t knew[kDMax];  // fused append: the new token's K and V rows (raw bits, up to 512 B)
+  uint32_t vnew[kDMax];
 };
 struct __align__(16) SmemValu : SmemBase {
   float qs[kGMax][kDMax];        // q of the group in float32
   float ps[kWaves][kGMax][kBS];  // softmax weights of the current block
 };
+
+// ---------------------------------------------------------------- fused append
+// Fragment layouts shared by both wave policies (X = 16 / element bytes):
+//   K fragment c of lane l: token l % 16, dims X*(4c + l/16) .. +X-1;
+//   V fragment c of lane l: element sub*4 + i = (token 4*(l/16) + i,
+//     dim c*4X + sub*16 + l % 16), sub < X/4.
+// Replaces token t's elements in a tile's fragments with the staged new row,
+// so the step's own token is attended from registers even while its store to
+// the cache is still in flight.
+template <int EB, int NCF>
+__device__ inline void patch_new_token(u32x4_t (&fk)[NCF], u32x4_t (&fv)[NCF], int t, int lane,
+                                       const uint32_t *knew, const uint32_t *vnew) {
+  constexpr int X = 16 / EB;
+  const int r = lane % 16, tq = lane / 16;
+  // Every register index below is a compile-time constant (runtime indices
+  // into the fragments would send the whole ring to scratch memory).
+#pragma unroll
+  for (int c = 0; c < NCF; ++c) {
+    const u32x4_t kx = *reinterpret_cast<const u32x4_t *>(knew + (X * (4 * c + tq)) * EB / 4);
+    fk[c] = (r == t) ? kx : fk[c];
+  }
+  const bool in_quad = tq == t / 4;
+  const int i = t % 4;
+#pragma unroll
+  for (int c = 0; c < NCF; ++c) {
+#pragma unroll
+    for (int e = 0; e < X; ++e) {  // element e = (token 4*tq + e%4, dim c*4X + (e/4)*16 + r)
+      const bool hit = in_quad && (e % 4 == i);
+      const int d = c * 4 * X + (e / 4) * 16 + r;
+      if constexpr (EB == 4) {
+        fv[c][e] = hit ? vnew[d] : fv[c][e];
+      } else {
+        const uint32_t val = (vnew[d / 2] >> ((d & 1) * 16)) & 0xFFFFu;
+        const uint32_t old = fv[c][e / 2];
+        const uint32_t upd = (e & 1) ? ((old & 0x0000FFFFu) | (val << 16)) : ((old & 0xFFFF0000u) | val);
+        fv[c][e / 2] = hit ? upd : old;
+      }
+    }
+  }
+}
+
+// Writes one token's K and V rows of one KV head into its slot (tile layouts
+// as in pa_reshape_and_cache).  Threads 0 .. D-1 of the workgroup take part.
+template <int EB, int D>
+__device__ inline void write_token_row(uint8_t *k_cache, uint8_t *v_cache, int64_t blk, int t, int g,
+                                       int num_kv_heads, const uint32_t *knew, const uint32_t *vnew,
+                                       int tid) {
+  constexpr int X = 16 / EB;
+  const int64_t tile = (blk * num_kv_heads + g) * kBS * D;
+  if (tid < D / X) {
+    const u32x4_t kx = *reinterpret_cast<const u32x4_t *>(knew + tid * 4);
+    reinterpret_cast<u32x4_t *>(k_cache + (tile + (int64_t)tid * kBS * X + t * X) * EB)[0] = kx;
+  }
+  if (tid < D) {
+    const int d = tid, slab = d / (4 * X), de = d % (4 * X);
+    const int64_t off = tile + (int64_t)slab * 64 * X + ((t / 4) * 16 + de % 16) * X + (de / 16) * 4 + t % 4;
+    if constexpr (EB == 4)
+      reinterpret_cast<uint32_t *>(v_cache)[off] = vnew[d];
+    else
+      reinterpret_cast<uint16_t *>(v_cache)[off] = (uint16_t)((vnew[d / 2] >> ((d & 1) * 16)) & 0xFFFFu);
+  }
+}
 
 // ============================================================================
 // MFMA wave: fp16 / bf16 caches.
@@ -262,9 +329,12 @@ struct MfmaWave {
     lo = u32x2_t{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
   }
 
-  // One block; `valid` = tokens of this block inside the context (1..16).
-  __device__ void compute(Frag &f, int valid, float scale_log2, int lane) {
+  // One block; `valid` = tokens of this block inside the context (1..16);
+  // new_tok >= 0: that token's K/V come from the staged new row.
+  __device__ void compute(Frag &f, int valid, float scale_log2, int lane, int new_tok,
+                          const Smem &sm) {
     const int tq = lane / 16;
+    if (new_tok >= 0) patch_new_token<2, NC>(f.k, f.v, new_tok, lane, sm.knew, sm.vnew);
     if (valid < kBS) {
       // Slots past the context may hold anything (NaN included): zero the V
       // elements so 0 * V stays 0; scores are masked below.
@@ -401,9 +471,10 @@ struct ValuWave {
     }
   }
 
-  __device__ void compute(Frag &f, int valid, float scale_log2, int lane, Smem &sm, int w,
-                          int G) {
+  __device__ void compute(Frag &f, int valid, float scale_log2, int lane, int new_tok, Smem &sm,
+                          int w, int G) {
     const int r = lane % 16, tq = lane / 16;
+    if (new_tok >= 0) patch_new_token<EB, NCF>(f.k, f.v, new_tok, lane, sm.knew, sm.vnew);
     float kf[NCF * X];
 #pragma unroll
     for (int c = 0; c < NCF; ++c)
@@ -531,8 +602,39 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeArgs a) {
   W wave;
   wave.stage(a, sm, s, g, tid);
   wave.init(a, sm, s, g, lane);
-  if constexpr (!kMfma) __syncthreads();  // q staged in LDS
   int bad = 0;  // a block id outside the pool was seen (never dereferenced)
+  // Fused append (one new token per sequence, at position L-1, which lies in
+  // the last block of the last partition): that partition's workgroup stages
+  // the token's K/V rows for head g in LDS, stores them into the slot, and its
+  // waves take the token from LDS.  A slot that is not position L-1's slot in
+  // the table marks the sequence bad: nothing is written, the row is NaN.
+  int new_tok = -1;
+  if (a.k_new != nullptr && p == nparts - 1) {
+    const int64_t slot = a.slot_mapping[s];
+    if (slot >= 0) {
+      const int pos = L - 1;
+      const int32_t blk = trow[pos / kBS - blk0];
+      if ((uint32_t)blk >= (uint32_t)a.num_blocks || slot != (int64_t)blk * kBS + pos % kBS) {
+        bad = 1;
+      } else {
+        constexpr int EB = W::TILE / (kBS * D);
+        const int64_t row = ((int64_t)s * a.num_kv_heads + g) * D * EB;  // bytes
+        if (tid < D * EB / 4) {
+          sm.knew[tid] = reinterpret_cast<const uint32_t *>(a.k_new + row)[tid];
+          sm.vnew[tid] = reinterpret_cast<const uint32_t *>(a.v_new + row)[tid];
+        }
+        new_tok = pos % kBS;
+      }
+    }
+  }
+  // q staged in LDS (VALU) / the new row staged (fused append)
+  if (!kMfma || a.k_new != nullptr) __syncthreads();
+  if (new_tok >= 0) {
+    constexpr int EB = W::TILE / (kBS * D);
+    write_token_row<EB, D>(const_cast<uint8_t *>(a.k_cache), const_cast<uint8_t *>(a.v_cache),
+                           trow[(L - 1) / kBS - blk0], new_tok, g, a.num_kv_heads, sm.knew,
+                           sm.vnew, tid);
+  }
 
   const int64_t head_off = (int64_t)g * W::TILE;
   const int64_t blk_stride = (int64_t)a.num_kv_heads * W::TILE;
@@ -576,45 +678,46 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeArgs a) {
         if (i < nc) {
           const int j = wu + (c0 + i) * kWaves;
           const int valid = (j == nblk - 1) ? last_valid : kBS;
+          const int nt = (j == nblk - 1) ? new_tok : -1;
           if constexpr (kMfma)
-            wave.compute(fr[b], valid, a.scale_log2, lane);
+            wave.compute(fr[b], valid, a.scale_log2, lane, nt, sm);
           else
-            wave.compute(fr[b], valid, a.scale_log2, lane, sm, w, G);
+            wave.compute(fr[b], valid, a.scale_log2, lane, nt, sm, w, G);
         }
       }
     }
   }
   wave.finish(sm, w, lane, G);
   if (__syncthreads_or(bad)) {
-    if (nparts == 1)
-      write_rows<D>(a, s, h0, G, NAN);
-    else
-      write_partial_nan<D>(a, s, h0, G, p);
-    return;
-  }
-
-  // Fold the four wave states: M = max m_w, out = sum 2^(m_w-M) acc_w / sum 2^(m_w-M) l_w.
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int h = i / D, d = i % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][h]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = exp2f(sm.m[ww][h] - M);  // 0 for a wave that saw no block
-      num += f * sm.acc[ww][h][d];
-      den += f * sm.l[ww][h];
-    }
-    const int64_t row = (int64_t)s * a.num_q_heads + h0 + h;
     if (nparts == 1) {
-      store_out(a.out, row * D + d, num / den, a.out_dtype);
-    } else {
-      const int64_t prow = row * a.max_parts + p;
-      a.ws_acc[prow * D + d] = num;
-      if (d == 0) {
-        a.ws_ml[prow * 2] = M;
-        a.ws_ml[prow * 2 + 1] = den;
+      write_rows<D>(a, s, h0, G, NAN);
+      return;
+    }
+    write_partial_nan<D>(a, s, h0, G, p);
+  } else {
+    // Fold the four wave states: M = max m_w, out = sum 2^(m_w-M) acc_w / sum 2^(m_w-M) l_w.
+    for (int i = tid; i < G * D; i += kThreads) {
+      const int h = i / D, d = i % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][h]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float f = exp2f(sm.m[ww][h] - M);  // 0 for a wave that saw no block
+        num += f * sm.acc[ww][h][d];
+        den += f * sm.l[ww][h];
+      }
+      const int64_t row = (int64_t)s * a.num_q_heads + h0 + h;
+      if (nparts == 1) {
+        store_out(a.out, row * D + d, num / den, a.out_dtype);
+      } else {
+        const int64_t prow = row * a.max_parts + p;
+        a.ws_acc[prow * D + d] = num;
+        if (d == 0) {
+          a.ws_ml[prow * 2] = M;
+          a.ws_ml[prow * 2 + 1] = den;
+        }
       }
     }
   }
@@ -623,21 +726,9 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------- merge kernel
 // One wave per (sequence, query head) row with more than one partition:
 //   M = max_p m_p,  out = sum_p 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p.
-// Lanes read the (m, l) pairs in parallel; each lane then owns D/64 output
-// dims and sums the partitions' accumulators.  A NaN partial (bad table
-// entry) makes the row NaN.
+// Each lane owns D/64 output dims and sums the partitions in order.  A NaN
+// partial (bad table entry) makes the row NaN.
 constexpr int kMergeWaves = 4;
-
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, shfl_xor(v, o));
-  return v;
-}
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += shfl_xor(v, o);
-  return v;
-}
 
 template <int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_kernel(DecodeArgs a, int32_t num_rows) {
@@ -652,30 +743,29 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_kernel(DecodeArgs a
   if (np <= 1) return;
   const float *ml = a.ws_ml + row * a.max_parts * 2;
   const float *acc = a.ws_acc + row * a.max_parts * D;
-  float M = -INFINITY, nan = 0.f;
-  for (int q = lane; q < np; q += 64) {
+  // Same arithmetic, in the same order, as the merge inside pa_decode's
+  // launch, so both paths give bit-identical rows.
+  float M = -INFINITY;
+  bool nan = false;
+  for (int q = 0; q < np; ++q) {
     const float mq = ml[2 * q];
-    nan += (mq != mq) ? 1.f : 0.f;
+    nan |= mq != mq;
     M = fmaxf(M, mq);
   }
-  M = wave_max(M);
-  nan = wave_sum(nan);
   float den = 0.f;
-  for (int q = lane; q < np; q += 64) den += exp2f(ml[2 * q] - M) * ml[2 * q + 1];
-  den = wave_sum(den);
   float num[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) num[e] = 0.f;
 #pragma unroll 4
   for (int q = 0; q < np; ++q) {
-    const float wq = exp2f(ml[2 * q] - M);
+    const float f = exp2f(ml[2 * q] - M);
+    den += f * ml[2 * q + 1];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] += wq * acc[(int64_t)q * D + lane * PER + e];
+    for (int e = 0; e < PER; ++e) num[e] += f * acc[(int64_t)q * D + lane * PER + e];
   }
-  const float inv = 1.f / den;
 #pragma unroll
   for (int e = 0; e < PER; ++e)
-    store_out(a.out, row * D + lane * PER + e, nan > 0.f ? NAN : num[e] * inv, a.out_dtype);
+    store_out(a.out, row * D + lane * PER + e, nan ? NAN : num[e] / den, a.out_dtype);
 }
 
 // ---------------------------------------------------------------- KV append
@@ -777,16 +867,50 @@ pa_status validate(const pa_decode_params *p) {
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: unknown kernel");
   if (p->kernel == PA_KERNEL_MFMA && p->kv_dtype == PA_F32)
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: the MFMA kernel needs an fp16 or bf16 cache");
+  if ((p->k_new != nullptr) != (p->v_new != nullptr) || (p->k_new != nullptr) != (p->slot_mapping != nullptr))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: k_new, v_new and slot_mapping go together");
+  if (p->k_new && (!aligned16(p->k_new) || !aligned16(p->v_new) || !aligned16(p->slot_mapping)))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: device pointers must be 16-byte aligned");
   if (!(std::isfinite(p->scale)))
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: scale must be finite");
   return PA_OK;
 }
 
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Automatic partition size: the largest of 1024 / 512 / 256 tokens whose grid
+// still has >= 8 workgroups per CU (shorter partitions balance better but add
+// merge work); a context that fits one such partition is not split.
 int32_t resolve_partition(const pa_decode_params *p) {
   if (p->partition_tokens > 0) return p->partition_tokens;
   const int32_t ctx = ((std::max(p->max_context_len, 1) + kBS - 1) / kBS) * kBS;
-  return ctx <= 512 ? ctx : 512;
+  const int64_t pairs = (int64_t)p->num_seqs * p->num_kv_heads;
+  const int64_t target = 8LL * cu_count();
+  int32_t pt = 256;
+  for (int32_t cand : {1024, 512}) {
+    if (pairs * ((ctx + cand - 1) / cand) >= target) {
+      pt = cand;
+      break;
+    }
+  }
+  return ctx <= pt ? ctx : pt;
 }
+
+size_t partial_bytes(const pa_decode_params *p, int32_t np) {
+  return (size_t)p->num_seqs * p->num_q_heads * np * (p->head_dim + 2) * sizeof(float);
+}
+
 
 int32_t num_partitions(const pa_decode_params *p, int32_t pt) {
   return std::max(1, (std::max(p->max_context_len, 1) + pt - 1) / pt);
@@ -838,7 +962,7 @@ size_t pa_decode_workspace_bytes(const pa_decode_params *p) {
   const int32_t pt = resolve_partition(p);
   const int32_t np = num_partitions(p, pt);
   if (np <= 1) return 0;
-  return (size_t)p->num_seqs * p->num_q_heads * np * (p->head_dim + 2) * sizeof(float);
+  return partial_bytes(p, np);
 }
 
 }  // extern "C"
@@ -864,9 +988,13 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
   a.v_cache = static_cast<const uint8_t *>(p->v_cache);
   a.block_tables = p->block_tables;
   a.context_lens = p->context_lens;
+  a.k_new = static_cast<const uint8_t *>(p->k_new);
+  a.v_new = static_cast<const uint8_t *>(p->v_new);
+  a.slot_mapping = p->slot_mapping;
   const size_t rows = (size_t)p->num_seqs * p->num_q_heads * np;
   a.ws_ml = need ? static_cast<float *>(workspace) : nullptr;
   a.ws_acc = need ? static_cast<float *>(workspace) + rows * 2 : nullptr;
+
   a.num_seqs = p->num_seqs;
   a.num_q_heads = p->num_q_heads;
   a.num_kv_heads = p->num_kv_heads;

@@ -47,15 +47,27 @@ def _params(**over):
 
 
 def test_workspace_and_partition_arithmetic():
+    # no GPU here: the library assumes 256 compute units, i.e. a target of 2048
+    # workgroups; 64 sequences x 8 KV heads x ceil(4096/1024) reach it
     p = _params()
-    assert pa.pa_decode_partition_tokens(p) == 512
+    assert pa.pa_decode_partition_tokens(p) == 1024
     # m and l plus a D-wide accumulator per (seq, q head, partition), float32
-    assert pa.pa_decode_workspace_bytes(p) == 64 * 64 * 8 * (128 + 2) * 4
-    p.max_context_len = 300
+    counters = 0
+    assert pa.pa_decode_workspace_bytes(p) == 64 * 64 * 4 * (128 + 2) * 4 + counters
+    p.num_seqs = 8                      # 8 x 8 x ceil(4096/256) < 2048: smallest partitions
+    assert pa.pa_decode_partition_tokens(p) == 256
+    p.num_seqs = 64
+    p.max_context_len = 300             # 512 pairs x 1 partition < 2048: split at 256
+    assert pa.pa_decode_partition_tokens(p) == 256
+    assert pa.pa_decode_workspace_bytes(p) == 64 * 64 * 2 * 130 * 4 + counters
+    p.num_seqs = 4096                   # a large batch of short contexts is not split
     assert pa.pa_decode_partition_tokens(p) == 304
     assert pa.pa_decode_workspace_bytes(p) == 0
+    p.num_seqs = 64
     p.partition_tokens = 64
-    assert pa.pa_decode_workspace_bytes(p) == 64 * 64 * 5 * 130 * 4
+    assert pa.pa_decode_workspace_bytes(p) == 64 * 64 * 5 * 130 * 4 + counters
+    p.num_seqs, p.num_kv_heads, p.num_q_heads = 3, 1, 2
+    assert pa.pa_decode_workspace_bytes(p) == 3 * 2 * 5 * 130 * 4
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -77,6 +89,11 @@ def test_decode_rejects_bad_parameters_before_launch(field, value, status):
 def test_decode_requires_the_workspace():
     p = _params()
     assert pa.lib().pa_decode(ctypes.byref(p), None, 0, None) == pa.PA_ERR_WORKSPACE
+
+
+def test_fused_append_fields_go_together():
+    p = _params(k_new=ctypes.c_void_p(16))
+    assert pa.lib().pa_decode(ctypes.byref(p), None, 0, None) == pa.PA_ERR_INVALID_ARG
 
 
 def test_mfma_kernel_rejects_fp32():

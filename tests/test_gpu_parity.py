@@ -5,6 +5,7 @@ byte the append / copy kernels write; max-abs error <= 1e-5 for fp32 caches
 and <= 2e-3 for fp16/bf16 caches (float32 accumulation) on decode outputs.
 A 16-bit output must equal the float32 output rounded to nearest even.
 """
+import ctypes
 import sys
 
 import numpy as np
@@ -333,7 +334,102 @@ def test_split_launches_equal_pa_decode_bitwise():
     out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     params = pa.make_decode_params(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, 2,
                                    int(l.max()), spec.fp32_scale(), partition_tokens=256)
-    ws = torch.empty(pa.pa_decode_workspace_bytes(params), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(pa.pa_decode_workspace_bytes(params), dtype=torch.uint8, device="cuda")
     pa.pa_decode_partitions(params, ws)
     pa.pa_decode_merge(params, ws)
     assert torch.equal(out, whole)
+
+
+# ------------------------------------------------------------------ fused append
+@pytest.mark.parametrize("dtype,D,kern,pt", [("bf16", 128, "mfma", 0), ("bf16", 128, "mfma", 16),
+                                             ("f16", 64, "mfma", 64), ("bf16", 128, "valu", 0),
+                                             ("f32", 64, "valu", 32)])
+def test_fused_append_equals_append_then_decode(dtype, D, kern, pt):
+    spec = workloads.custom(seed=70, dtype=dtype, lens=(5, 40, 16, 300, 33), num_q_heads=8,
+                            num_kv_heads=2, head_dim=D, prefix_len=20, decode_steps=18)
+    wl, gst, ost = _both(spec, steps=0)
+    # a child of sequence 0 (not decoded) shares its partly filled last block,
+    # so the first step's append into sequence 0 must copy that block
+    assert gst.pool.seq_fork(gst.seq_ids[0]) == ost.pool.seq_fork(ost.seq_ids[0])
+    mb = oracle_side.max_blocks_for(wl)
+    q = gpu_side.to_device(wl.q, dtype)
+    saw_cow = False
+    for step in range(spec.decode_steps):
+        slots, cows = gst.pool.seq_append_batch(gst.seq_ids)
+        if len(cows):
+            saw_cow = True
+            pa.pa_copy_blocks(gst.k_cache, gst.v_cache, torch.from_numpy(cows.copy()).cuda(),
+                              spec.num_kv_heads, D)
+        oracle_side.advance(wl, ost, step)
+        assert slots.tolist() == ost.step_slots[-1]
+        tab_d, lens_d, _, lh = gpu_side.tables(gst, mb)
+        out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        pa.pa_decode(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, spec.num_kv_heads,
+                     int(lh.max()), spec.fp32_scale(), partition_tokens=pt, kernel=kern,
+                     k_new=gpu_side.to_device(wl.step_k[step], dtype),
+                     v_new=gpu_side.to_device(wl.step_v[step], dtype),
+                     slot_mapping=torch.from_numpy(slots.copy()).cuda())
+        ref = oracle_side.decode(wl, ost, mb)
+        err = np.max(np.abs(_f32(out) - ref))
+        assert err <= TOL[dtype], (step, err)
+    assert saw_cow
+    torch.cuda.synchronize()
+    _assert_caches_equal(gst, ost, dtype)
+
+
+def test_fused_append_rejects_a_foreign_slot():
+    spec = workloads.custom(seed=71, dtype="bf16", lens=(40, 70), num_q_heads=4, num_kv_heads=2,
+                            head_dim=128, decode_steps=1)
+    wl = workloads.generate(spec)
+    gst = gpu_side.build(wl)
+    slots, _ = gst.pool.seq_append_batch(gst.seq_ids)
+    mb = oracle_side.max_blocks_for(wl)
+    tab_d, lens_d, _, lh = gpu_side.tables(gst, mb)
+    before_k = _cache_bits(gst.k_cache).copy()
+    bad = slots.copy()
+    bad[1] = bad[0]                      # sequence 1 pointed at sequence 0's slot
+    q = gpu_side.to_device(wl.q, "bf16")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    pa.pa_decode(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, 2, int(lh.max()),
+                 spec.fp32_scale(), k_new=gpu_side.to_device(wl.step_k[0], "bf16"),
+                 v_new=gpu_side.to_device(wl.step_v[0], "bf16"),
+                 slot_mapping=torch.from_numpy(bad).cuda())
+    o = out.cpu().numpy()
+    assert np.all(np.isfinite(o[0])) and np.all(np.isnan(o[1]))
+    after_k = _cache_bits(gst.k_cache)
+    changed = np.nonzero(after_k != before_k)[0]
+    # only sequence 0's new token was written (both heads x D dims)
+    assert len(changed) == 2 * 128
+
+
+def test_one_workspace_serves_calls_of_any_shape():
+    """The decode workspace is per-call scratch: one buffer full of garbage
+    serves many calls of different shapes, and pa_decode always equals its
+    two launches run separately, bit for bit."""
+    ws = torch.randint(0, 256, (64 << 20,), dtype=torch.uint8, device="cuda")
+    cases = [(("bf16", 128, 16, 2), (900, 20, 700, 1, 1500)), (("f16", 64, 8, 8), (300, 513, 64)),
+             (("bf16", 128, 8, 1), (4000, 3000))]
+    for (dt, D, Hq, Hkv), lens in cases:
+        spec = workloads.custom(seed=80 + D + Hq, dtype=dt, lens=lens, num_q_heads=Hq,
+                                num_kv_heads=Hkv, head_dim=D)
+        wl = workloads.generate(spec)
+        gst = gpu_side.build(wl)
+        mb = oracle_side.max_blocks_for(wl)
+        tab_d, lens_d, _, lh = gpu_side.tables(gst, mb)
+        q = gpu_side.to_device(wl.q, dt)
+        for kern in ("mfma", "valu"):
+            for pt in (16, 64, 256):
+                whole = torch.full(q.shape, -7.0, dtype=torch.float32, device="cuda")
+                split = torch.full(q.shape, -7.0, dtype=torch.float32, device="cuda")
+                prm = pa.make_decode_params(whole, q, gst.k_cache, gst.v_cache, tab_d, lens_d,
+                                            Hkv, int(lh.max()), spec.fp32_scale(), pt, kern)
+                need = pa.pa_decode_workspace_bytes(prm)
+                assert 0 < need <= ws.numel()
+                pa._check(pa.lib().pa_decode(ctypes.byref(prm), ctypes.c_void_p(ws.data_ptr()),
+                                             need, pa._stream(None)))
+                prm2 = pa.make_decode_params(split, q, gst.k_cache, gst.v_cache, tab_d, lens_d,
+                                             Hkv, int(lh.max()), spec.fp32_scale(), pt, kern)
+                ws2 = torch.empty(need, dtype=torch.uint8, device="cuda")
+                pa.pa_decode_partitions(prm2, ws2)
+                pa.pa_decode_merge(prm2, ws2)
+                assert torch.equal(whole, split), (dt, D, Hq, Hkv, kern, pt)
