@@ -206,19 +206,19 @@ __device__ inline void patch_new_token(u32x4_t (&fk)[NCF], u32x4_t (&fv)[NCF], i
 }
 
 // Writes one token's K and V rows of one KV head into its slot (tile layouts
-// as in pa_reshape_and_cache).  Threads 0 .. D-1 of the workgroup take part.
+// as in pa_reshape_and_cache), by the 64 lanes of one wave.
 template <int EB, int D>
 __device__ inline void write_token_row(uint8_t *k_cache, uint8_t *v_cache, int64_t blk, int t, int g,
                                        int num_kv_heads, const uint32_t *knew, const uint32_t *vnew,
-                                       int tid) {
+                                       int lane) {
   constexpr int X = 16 / EB;
   const int64_t tile = (blk * num_kv_heads + g) * kBS * D;
-  if (tid < D / X) {
-    const u32x4_t kx = *reinterpret_cast<const u32x4_t *>(knew + tid * 4);
-    reinterpret_cast<u32x4_t *>(k_cache + (tile + (int64_t)tid * kBS * X + t * X) * EB)[0] = kx;
+  if (lane < D / X) {
+    const u32x4_t kx = *reinterpret_cast<const u32x4_t *>(knew + lane * 4);
+    reinterpret_cast<u32x4_t *>(k_cache + (tile + (int64_t)lane * kBS * X + t * X) * EB)[0] = kx;
   }
-  if (tid < D) {
-    const int d = tid, slab = d / (4 * X), de = d % (4 * X);
+  for (int d = lane; d < D; d += 64) {
+    const int slab = d / (4 * X), de = d % (4 * X);
     const int64_t off = tile + (int64_t)slab * 64 * X + ((t / 4) * 16 + de % 16) * X + (de / 16) * 4 + t % 4;
     if constexpr (EB == 4)
       reinterpret_cast<uint32_t *>(v_cache)[off] = vnew[d];
@@ -568,8 +568,9 @@ __device__ void write_partial_nan(const DecodeArgs &a, int s, int h0, int G, int
   }
 }
 
+// MFMA path: three 4-wave workgroups per CU (3 waves per SIMD, <= 168 VGPRs).
 template <class W, int D, bool kMfma>
-__global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(DecodeArgs a) {
   __shared__ typename W::Smem sm;
   // 1-D grid, KV head fastest, then sequence, then partition.  Workgroups are
   // dealt round-robin to the 8 XCDs by linear id, so this order spreads every
@@ -581,7 +582,16 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
   const int G = a.group;
   const int h0 = g * G;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  // Loads that do not depend on the context length go out together with it:
+  // the q fragments, and this wave's first 64 block ids (speculative: only
+  // bounded by the table row; validated once the length is known).
   const int L = a.context_lens[s];
+  const int blk0 = (int)((int64_t)p * a.part_tokens / kBS);
+  const int32_t *trow = a.block_tables + (int64_t)s * a.max_blocks + blk0;
+  const int ids_first = (int64_t)blk0 + wu + lane * kWaves < a.max_blocks ? trow[wu + lane * kWaves] : 0;
+  W wave;
+  wave.init(a, sm, s, g, lane);
   if (!ctx_valid(L, a)) {
     if (p == 0) write_rows<D>(a, s, h0, G, NAN);
     return;
@@ -594,56 +604,44 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeArgs a) {
   if (p >= nparts) return;
   const int tok0 = p * a.part_tokens;
   const int tok1 = min(L, tok0 + a.part_tokens);
-  const int blk0 = tok0 / kBS;
   const int nblk = (tok1 - tok0 + kBS - 1) / kBS;
   const int last_valid = tok1 - (blk0 + nblk - 1) * kBS;
-  const int32_t *trow = a.block_tables + (int64_t)s * a.max_blocks + blk0;
 
-  W wave;
   wave.stage(a, sm, s, g, tid);
-  wave.init(a, sm, s, g, lane);
+  if constexpr (!kMfma) __syncthreads();  // q staged in LDS
   int bad = 0;  // a block id outside the pool was seen (never dereferenced)
-  // Fused append (one new token per sequence, at position L-1, which lies in
-  // the last block of the last partition): that partition's workgroup stages
-  // the token's K/V rows for head g in LDS, stores them into the slot, and its
-  // waves take the token from LDS.  A slot that is not position L-1's slot in
-  // the table marks the sequence bad: nothing is written, the row is NaN.
+  // Fused append (one new token per sequence, at position L-1, in the last
+  // block of the last partition): the wave that computes that block checks
+  // the slot against the table, stages the token's K/V rows for head g in
+  // LDS, stores them into the slot, and later takes the token from LDS.  A
+  // slot that is not position L-1's slot marks the sequence bad: nothing is
+  // written and the row is NaN.  Only that wave is involved (no barrier).
   int new_tok = -1;
-  if (a.k_new != nullptr && p == nparts - 1) {
+  if (a.k_new != nullptr && p == nparts - 1 && wu == (nblk - 1) % kWaves) {
     const int64_t slot = a.slot_mapping[s];
     if (slot >= 0) {
       const int pos = L - 1;
-      const int32_t blk = trow[pos / kBS - blk0];
+      const int32_t blk = trow[nblk - 1];
       if ((uint32_t)blk >= (uint32_t)a.num_blocks || slot != (int64_t)blk * kBS + pos % kBS) {
         bad = 1;
       } else {
         constexpr int EB = W::TILE / (kBS * D);
         const int64_t row = ((int64_t)s * a.num_kv_heads + g) * D * EB;  // bytes
-        if (tid < D * EB / 4) {
-          sm.knew[tid] = reinterpret_cast<const uint32_t *>(a.k_new + row)[tid];
-          sm.vnew[tid] = reinterpret_cast<const uint32_t *>(a.v_new + row)[tid];
+        for (int i = lane; i < D * EB / 4; i += 64) {
+          sm.knew[i] = reinterpret_cast<const uint32_t *>(a.k_new + row)[i];
+          sm.vnew[i] = reinterpret_cast<const uint32_t *>(a.v_new + row)[i];
         }
         new_tok = pos % kBS;
+        write_token_row<EB, D>(const_cast<uint8_t *>(a.k_cache), const_cast<uint8_t *>(a.v_cache),
+                               blk, new_tok, g, a.num_kv_heads, sm.knew, sm.vnew, lane);
       }
     }
-  }
-  // q staged in LDS (VALU) / the new row staged (fused append)
-  if (!kMfma || a.k_new != nullptr) __syncthreads();
-  if (new_tok >= 0) {
-    constexpr int EB = W::TILE / (kBS * D);
-    write_token_row<EB, D>(const_cast<uint8_t *>(a.k_cache), const_cast<uint8_t *>(a.v_cache),
-                           trow[(L - 1) / kBS - blk0], new_tok, g, a.num_kv_heads, sm.knew,
-                           sm.vnew, tid);
   }
 
   const int64_t head_off = (int64_t)g * W::TILE;
   const int64_t blk_stride = (int64_t)a.num_kv_heads * W::TILE;
-  // Each wave streams its blocks (w, w+4, w+8, ...) through a ring of NB
-  // register fragments: block i is computed while blocks i+1 .. i+NB-1 are in
-  // flight, so every wave keeps (NB-1) x 2 tiles of loads outstanding.
   constexpr int NB = W::kRing;
   typename W::Frag fr[NB];
-  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int nmine = nblk > wu ? (nblk - wu + kWaves - 1) / kWaves : 0;
   // Each wave streams its blocks (wu, wu+4, wu+8, ...) through a ring of NB
   // register fragments: block i is computed while blocks i+1 .. i+NB-1 are in
@@ -654,7 +652,8 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeArgs a) {
   // compiler's wait counts never drain the ring early.
   for (int c0 = 0; c0 < nmine; c0 += 64) {
     const int nc = min(64, nmine - c0);
-    int ids = lane < nc ? trow[wu + (c0 + lane) * kWaves] : 0;
+    int ids = c0 == 0 ? ids_first : trow[wu + (c0 + lane) * kWaves];
+    ids = lane < nc ? ids : 0;
     const bool id_ok = (uint32_t)ids < (uint32_t)a.num_blocks;
     if (__builtin_amdgcn_ballot_w64(!id_ok)) bad = 1;
     ids = id_ok ? ids : 0;
