@@ -17,7 +17,8 @@ placement) so the working set is several times the 256 MB Infinity Cache.
 
 Prints one JSON line.  value = decode tokens/s (one token per sequence per
 step) over the timed steps, wall clock between device synchronizations.
-roofline = the partition kernel: algorithmic bytes per launch / its mean
+roofline = the attention kernel (balanced split, or partitions when
+  --partition-tokens is set): algorithmic bytes per launch / its mean
 duration from HIP events recorded around it on its stream.
 cpu_baseline = the fp64 CPU oracle on whole-batch passes of the same workload.
 """
@@ -41,7 +42,7 @@ from paged_kv_cache_65_amd import accounting, workloads  # noqa: E402
 
 METRIC = "paged decode-attention tokens/s + achieved HBM GB/s (% of 8 TB/s peak)"
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pa_partition_kernel_llama70b_gqa8.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_65_amd", "csrc", "pa_kernels.hip")
 
 
@@ -53,13 +54,14 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per partition launch from committed rocprofv3 counter runs, or None
-    when the kernel source changed since they were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs, or
+    None when the kernel source changed since they were taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_llama70b_gqa8.txt")
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         parts = line.split()
         if len(parts) == 2 and not line.startswith("#"):
             kv[parts[0]] = parts[1]
@@ -457,7 +459,8 @@ def main():
     achieved = mean_alg / part_s / 1e9
     step_bytes = mean_alg + g["append_bytes"]
     step_gbps = step_bytes * K / g["elapsed"] / 1e9
-    traffic = read_traffic()
+    kernel_name = "pa_balanced_kernel" if g["part_tokens"] == 0 else "pa_partition_kernel"
+    traffic = read_traffic(kernel_name)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle")
@@ -491,7 +494,7 @@ def main():
             "device": g["device"],
         },
         "roofline": {
-            "kernel": "pa_partition_kernel",
+            "kernel": kernel_name,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

@@ -83,10 +83,18 @@ const char *pa_last_error(void);
  * machine", section "The KV cache: attention's memory bill, derived").  The
  * context counts the token appended this step.  L = 0 yields a zero row.
  *
- * Long contexts are split into partitions of partition_tokens tokens, each
- * reduced with an online softmax into (max, sum, weighted V) partials that a
- * second kernel merges by log-sum-exp rescaling.  The result does not depend
- * on the partition size beyond float32 rounding.
+ * The work is split into pieces, each reduced with an online softmax into a
+ * (max, sum, weighted V) partial, which a second kernel merges by
+ * log-sum-exp rescaling.  Two splits exist:
+ *   - partitions: every context is cut into partition_tokens-token pieces,
+ *     one workgroup per (piece, KV head, sequence);
+ *   - balanced (automatic partitioning on the matrix-core path, at most 1024
+ *     sequences and 2^15 (sequence, KV head) pairs): all (sequence, KV head,
+ *     16-token block) units are cut into equal contiguous shares, one per
+ *     wave of a grid that fills every CU once, whatever the length mix.
+ * The result does not depend on the split beyond float32 rounding; it is
+ * deterministic for a given device (the balanced shares depend on its CU
+ * count).
  *
  * Arguments (all pointers are device memory):
  *   out           [num_seqs][num_q_heads][head_dim], out_dtype (F32 or kv_dtype;
@@ -99,9 +107,10 @@ const char *pa_last_error(void);
  *   max_context_len  host-known upper bound on every context_lens[s]; it sizes
  *                 the launch grid
  *   scale         usually 1/sqrt(head_dim)
- *   partition_tokens  0 = automatic (1024, 512 or 256 tokens: the largest
+ *   partition_tokens  0 = automatic (the balanced split where it applies,
+ *                 else partitions of 1024, 512 or 256 tokens: the largest
  *                 that gives >= 8 workgroups per compute unit), else a
- *                 positive multiple of 16
+ *                 positive multiple of 16 (partitions)
  * Supported: head_dim in {64, 128}; num_q_heads % num_kv_heads == 0;
  *   G <= 16; fp16/bf16 with any kernel, fp32 with the VALU kernel.
  * Contract violations found on the device (a table entry outside
@@ -110,7 +119,9 @@ const char *pa_last_error(void);
  * is set to NaN.
  * Workspace: pa_decode_workspace_bytes() bytes of device memory (0 when no
  * context is split); scratch for this call only (no initialization needed),
- * reusable by any later call once the stream has passed this one.
+ * reusable by any later call once the stream has passed this one.  Under the
+ * balanced split its size depends on the current device's CU count: query it
+ * with that device current.
  * ------------------------------------------------------------------------ */
 typedef struct pa_decode_params {
   void *out;
@@ -146,8 +157,9 @@ typedef struct pa_decode_params {
   const int64_t *slot_mapping;
 } pa_decode_params;
 
-/* Partition size (tokens) pa_decode will use for these parameters, or a
- * negative pa_status value if the parameters are invalid. */
+/* Partition size (tokens) pa_decode will use for these parameters, 0 for the
+ * balanced split, or a negative pa_status value if the parameters are
+ * invalid. */
 int32_t pa_decode_partition_tokens(const pa_decode_params *p);
 
 /* Workspace bytes pa_decode needs for these parameters (0 if the whole context
@@ -159,7 +171,10 @@ pa_status pa_decode(const pa_decode_params *p, void *workspace, size_t workspace
                     void *stream);
 
 /* pa_decode in its two launches, for callers that time, overlap or combine
- * them.  pa_decode_partitions runs the partition kernel: it writes the final
+ * them; together they write every output row, and they give the same bits
+ * as pa_decode.  Under the balanced split the workspace holds partials in an
+ * internal layout and pa_decode_merge must follow pa_decode_partitions on
+ * the same workspace.  With partitions, pa_decode_partitions writes the final
  * rows of sequences whose context fits one partition, and for the others one
  * partial per (sequence, query head, partition) into the workspace:
  *   float32 [num_seqs][num_q_heads][P][2]  (m, l): m = max score in log2
@@ -168,7 +183,7 @@ pa_status pa_decode(const pa_decode_params *p, void *workspace, size_t workspace
  * (the second array follows the first; P = ceil(max_context_len /
  * partition_tokens)).  pa_decode_merge folds those partials into the output
  * rows: M = max_p m_p, out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
-
+ *
  * Partials of one sequence computed elsewhere (e.g. other devices holding
  * other context ranges) can be merged the same way.  Both calls take the same
  * parameters and workspace as pa_decode. */

@@ -4,14 +4,17 @@
 // Decode ("LLM Inference Optimization: KV-Cache, PagedAttention, and GPU
 // Memory Efficiency", section "PagedAttention: OS Concepts Meet GPU Memory":
 // walk the sequence's block table, load K and V of each physical block, score
-// it and fold it in with an online softmax).  One workgroup of four waves
-// takes one (context partition, KV head, sequence).  The waves split the
-// partition's 16-token blocks round-robin; each wave keeps an online-softmax
-// state (running max m, running sum l, weighted V sum) for all query heads of
-// the KV head's group, so every K/V tile is read from HBM once and reused by
-// the whole group.  The four wave states meet in LDS at the end; a partition
-// either writes the final row (single-partition sequences) or an (m, l, acc)
-// partial that the merge kernel folds with log-sum-exp rescaling.
+// it and fold it in with an online softmax).  Every wave keeps an
+// online-softmax state (running max m, running sum l, weighted V sum) for all
+// query heads of a KV head's group, so every K/V tile is read from HBM once
+// and reused by the whole group.  Two ways to split the work:
+//   * partitions: one workgroup of four waves takes one (context partition,
+//     KV head, sequence); the waves split the partition's 16-token blocks
+//     round-robin and their states meet in LDS at the end;
+//   * balanced: a persistent grid whose waves each stream an equal share of
+//     all (sequence, KV head, block) units (see pa_balanced_kernel).
+// A piece of work either writes its final rows or an (m, l, acc) partial that
+// the merge kernel folds with log-sum-exp rescaling.
 //
 // Two per-wave math policies share that skeleton:
 //   * MfmaWave (fp16/bf16): q.K^T for the whole group is one 16x16x32 matrix
@@ -87,6 +90,18 @@ __device__ inline void store_out(void *out, int64_t idx, float v, int out_dtype)
     static_cast<uint16_t *>(out)[idx] = f32_to_bf16_bits(v);
 }
 
+// Four consecutive elements (idx a multiple of 4).
+__device__ inline void store_out4(void *out, int64_t idx, f32x4_t v, int out_dtype) {
+  if (out_dtype == PA_F32) {
+    *reinterpret_cast<f32x4_t *>(static_cast<float *>(out) + idx) = v;
+  } else {
+    uint32_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = out_dtype == PA_F16 ? f32_to_f16_bits(v[e]) : f32_to_bf16_bits(v[e]);
+    *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(out) + idx) = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  }
+}
+
 __device__ inline float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
 // Cross-lane combines that stay in the vector ALU (no LDS round trip).
@@ -143,8 +158,9 @@ struct DecodeArgs {
   const uint8_t *k_new;          // fused append: [S][Hkv][D] rows of the step's token, or null
   const uint8_t *v_new;
   const int64_t *slot_mapping;   // fused append: [S] slot of position L-1 (negative = no append)
+  int32_t *ws_pre;               // balanced split: [S+1] blocks of the sequences before s
   int32_t num_seqs, num_q_heads, num_kv_heads, group, max_blocks, num_blocks, max_ctx, max_parts,
-      part_tokens, out_dtype;
+      part_tokens, out_dtype, num_workers;
   float scale_log2;
 };
 
@@ -266,23 +282,31 @@ struct MfmaWave {
 
   __device__ void stage(const DecodeArgs &, Smem &, int, int, int) {}
 
-  __device__ void init(const DecodeArgs &a, const Smem &, int s, int g, int lane) {
+  __device__ void reset() {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    l = 0.f;
+  }
+
+  // q fragments from the group's G rows of D 16-bit values (rows >= G are 0).
+  // The pointer may be global or LDS memory; the load instructions follow it.
+  template <class P>
+  __device__ void load_q(const P *rows, int G, int lane) {
     const int r = lane % 16, tq = lane / 16;
-    const int G = a.group;
-    const int h = g * G + r;
-    const u32x4_t *qrow =
-        reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
-                                          ((int64_t)s * a.num_q_heads + (r < G ? h : 0)) * D * 2);
+    const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(rows) + (r < G ? r : 0) * (D / 8);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       u32x4_t x = qrow[4 * c + tq];
       if (r >= G) x = u32x4_t{0, 0, 0, 0};
       qB[c] = __builtin_bit_cast(v8, x);
     }
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m = -INFINITY;
-    l = 0.f;
+  }
+
+  __device__ void init(const DecodeArgs &a, const Smem &, int s, int g, int lane) {
+    const int G = a.group;
+    load_q(static_cast<const uint8_t *>(a.q) + ((int64_t)s * a.num_q_heads + g * G) * D * 2, G, lane);
+    reset();
   }
 
   __device__ static void load(Frag &f, const uint8_t *ktile, const uint8_t *vtile, int lane) {
@@ -332,9 +356,9 @@ struct MfmaWave {
   // One block; `valid` = tokens of this block inside the context (1..16);
   // new_tok >= 0: that token's K/V come from the staged new row.
   __device__ void compute(Frag &f, int valid, float scale_log2, int lane, int new_tok,
-                          const Smem &sm) {
+                          const uint32_t *knew, const uint32_t *vnew) {
     const int tq = lane / 16;
-    if (new_tok >= 0) patch_new_token<2, NC>(f.k, f.v, new_tok, lane, sm.knew, sm.vnew);
+    if (new_tok >= 0) patch_new_token<2, NC>(f.k, f.v, new_tok, lane, knew, vnew);
     if (valid < kBS) {
       // Slots past the context may hold anything (NaN included): zero the V
       // elements so 0 * V stays 0; scores are masked below.
@@ -398,7 +422,74 @@ struct MfmaWave {
       }
     }
   }
+
+  // Balanced split: writes this wave's state for one (sequence, KV head)
+  // pair whose query rows start at row0: the normalised output rows when the
+  // wave saw the whole pair, else an (m, l, acc) partial at partial row
+  // prow0.  `bad` turns them into NaN.
+  __device__ void store_segment(const DecodeArgs &a, int64_t row0, int64_t prow0, bool whole, bool bad,
+                                int lane, int G) const {
+    const int r = lane % 16, tq = lane / 16;
+    const float lt = sum_xor32(sum_xor16(l));
+    if (r >= G) return;
+    const f32x4_t nan4 = {NAN, NAN, NAN, NAN};
+    if (whole) {
+      const int64_t o = (row0 + r) * D + 4 * tq;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        f32x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[n][e] / lt;
+        store_out4(a.out, o + 16 * n, bad ? nan4 : v, a.out_dtype);
+      }
+    } else {
+      float *pacc = a.ws_acc + (prow0 + r) * D + 4 * tq;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4_t *>(pacc + 16 * n) = bad ? nan4 : acc[n];
+      if (tq == 0) {
+        a.ws_ml[(prow0 + r) * 2] = bad ? NAN : m;
+        a.ws_ml[(prow0 + r) * 2 + 1] = lt;
+      }
+    }
+  }
+
+  // Balanced split: parks the state in LDS instead (acc rows [G][D], then
+  // m[G], l[G]); flush_parked() writes it out later.
+  __device__ void park_segment(float *st, int lane, int G) const {
+    const int r = lane % 16, tq = lane / 16;
+    const float lt = sum_xor32(sum_xor16(l));
+    if (r >= G) return;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4_t *>(st + r * D + 16 * n + 4 * tq) = acc[n];
+    if (tq == 0) {
+      st[G * D + r] = m;
+      st[G * D + G + r] = lt;
+    }
+  }
 };
+
+// Writes a state parked by park_segment exactly as store_segment would have.
+template <int D>
+__device__ void flush_parked(const DecodeArgs &a, const float *st, int64_t row0, int64_t prow0, bool whole,
+                             bool bad, int lane, int G) {
+  const f32x4_t nan4 = {NAN, NAN, NAN, NAN};
+  for (int e = lane * 4; e < G * D; e += 256) {
+    const int r = e / D;
+    f32x4_t v = *reinterpret_cast<const f32x4_t *>(st + e);
+    if (whole) {
+      const float lt = st[G * D + G + r];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = v[k] / lt;
+      store_out4(a.out, (row0 + r) * D + e % D, bad ? nan4 : v, a.out_dtype);
+    } else {
+      *reinterpret_cast<f32x4_t *>(a.ws_acc + prow0 * D + e) = bad ? nan4 : v;
+    }
+  }
+  if (!whole && lane < G) {
+    a.ws_ml[(prow0 + lane) * 2] = bad ? NAN : st[G * D + lane];
+    a.ws_ml[(prow0 + lane) * 2 + 1] = st[G * D + G + lane];
+  }
+}
 
 // ============================================================================
 // Vector-ALU wave: any cache type, GM = compile-time bound on the group size.
@@ -679,7 +770,7 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
           const int valid = (j == nblk - 1) ? last_valid : kBS;
           const int nt = (j == nblk - 1) ? new_tok : -1;
           if constexpr (kMfma)
-            wave.compute(fr[b], valid, a.scale_log2, lane, nt, sm);
+            wave.compute(fr[b], valid, a.scale_log2, lane, nt, sm.knew, sm.vnew);
           else
             wave.compute(fr[b], valid, a.scale_log2, lane, nt, sm, w, G);
         }
@@ -722,6 +813,311 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
   }
 }
 
+// ---------------------------------------------------------------- balanced split
+// Matrix-core path with automatic partitioning.  The work is the list of
+// units (sequence s, KV head g, block j), ordered by s, then g, then j, with
+// ceil(L_s / 16) blocks per (s, g) pair.  A persistent grid (every wave slot
+// of the GPU once, NW waves) cuts the list into NW equal contiguous shares
+// of C = ceil(U / NW) units, so every wave streams the same number of K/V
+// tiles whatever the mix of context lengths, and no workgroup is spent on
+// an empty partition.  A share covers pieces ("segments") of one or more
+// pairs; each segment keeps one online-softmax state.  A segment that is a
+// whole pair writes its output rows itself; any other writes an (m, l, acc)
+// partial into slot w + pair.  Walking along the unit list, every new
+// segment starts a new wave share or a new pair (or both), so w + pair grows
+// strictly from segment to segment: no two segments share a slot, and the
+// NW + S*Hkv - 1 slots cover every case.  The merge kernel folds the
+// partials of each pair that was split.
+// One 4-wave workgroup per CU (one wave per SIMD), each wave with a ring of
+// four blocks (32 KiB) in flight: fewer, longer wave shares mean fewer
+// segments, hence fewer partial stores and a cheaper merge, and 128 KiB in
+// flight per CU still saturates HBM.
+#ifndef PA_BALANCED_WG_PER_CU
+#define PA_BALANCED_WG_PER_CU 1
+#endif
+#ifndef PA_BALANCED_RING
+#define PA_BALANCED_RING 4
+#endif
+constexpr int kSeqMax = 1024;    // sequences per launch on this path
+constexpr int kQLds = 16384;     // bytes of q staged per workgroup
+constexpr int kAppendMax = 4;    // fused-append rows staged per wave and chunk
+
+struct __align__(16) SmemBalanced {
+  uint32_t q[kQLds / 4];                        // q rows of pairs qbase .. qbase+nq-1
+  uint32_t knew[kWaves][kAppendMax][kDMax / 2];  // fused append: new K / V rows (16-bit)
+  uint32_t vnew[kWaves][kAppendMax][kDMax / 2];
+  int32_t pre[kSeqMax + 1];                      // blocks of the sequences before s
+  int32_t len[kSeqMax];                          // context length (0 when invalid)
+};
+
+// Floats of one wave's parking area: G rows of D, then m and l per row
+// (rounded to 16 bytes).
+__host__ __device__ constexpr int park_floats(int G, int D) { return (G * (D + 2) + 3) / 4 * 4; }
+
+// Per-unit flags, one unit per lane.
+constexpr uint32_t kUValid = 0x1Fu;         // tokens of the block inside the context (1..16)
+constexpr uint32_t kUFirst = 1u << 5;       // first unit of a segment
+constexpr uint32_t kULast = 1u << 6;        // last unit of a segment
+constexpr uint32_t kUPairStart = 1u << 7;   // block 0 of its pair
+constexpr uint32_t kUPairEnd = 1u << 8;     // last block of its pair
+constexpr uint32_t kUBad = 1u << 9;         // block id outside the pool, or a foreign slot
+constexpr uint32_t kUNew = 1u << 10;        // holds the fused-append token
+constexpr int kUNewTokShift = 11;           // its position in the block (4 bits)
+constexpr int kUNewIdxShift = 15;           // its staging row (2 bits)
+constexpr int kUPairShift = 17;             // (s, g) pair index s*Hkv + g (15 bits)
+constexpr int kPairMax = 1 << 15;
+
+// Instruction-issue priority of this wave (0..3).  The sequencer favours
+// older waves; a wave of the balanced split lowers its priority as it works
+// through its share, so waves that started later (or were starved) catch up
+// and all shares end together.
+__device__ inline void set_wave_priority(int level) {
+  switch (level) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
+// Sequence that holds block b of the concatenated block list: the last s with pre[s] <= b.
+__device__ inline int seq_of_block(const SmemBalanced &sm, int b, int S) {
+  int lo = 0, hi = S;  // pre[lo] <= b < pre[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (sm.pre[mid] <= b) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ inline int pair_of_unit(const SmemBalanced &sm, int u, int Hkv, int S) {
+  const int s = seq_of_block(sm, u / Hkv, S);
+  const int nb = sm.pre[s + 1] - sm.pre[s];
+  return s * Hkv + (u - Hkv * sm.pre[s]) / nb;
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads, PA_BALANCED_WG_PER_CU) void pa_balanced_kernel(DecodeArgs a) {
+  using W = MfmaWave<DT, D>;
+  __shared__ SmemBalanced sm;
+  extern __shared__ __align__(16) float park_lds[];  // kWaves x park_floats(G, D)
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wu = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int S = a.num_seqs, Hkv = a.num_kv_heads, G = a.group;
+
+  // Context lengths, then block offsets by an exclusive scan (wave 0: each
+  // lane sums a run of ceil(S/64) sequences, then a scan across lanes).
+  for (int s = tid; s < S; s += kThreads) {
+    const int L = a.context_lens[s];
+    sm.len[s] = ctx_valid(L, a) ? L : 0;
+  }
+  __syncthreads();
+  if (wu == 0) {
+    const int per = (S + 63) / 64;
+    const int s0 = min(S, lane * per), s1 = min(S, s0 + per);
+    int sum = 0;
+    for (int s = s0; s < s1; ++s) sum += (sm.len[s] + kBS - 1) / kBS;
+    int inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    int run = inc - sum;
+    for (int s = s0; s < s1; ++s) {
+      sm.pre[s] = run;
+      run += (sm.len[s] + kBS - 1) / kBS;
+    }
+    if (lane == 63) sm.pre[S] = inc;
+  }
+  __syncthreads();
+  const int U = Hkv * sm.pre[S];
+  const int NW = a.num_workers;
+  const int C = (U + NW - 1) / NW;
+  if (blockIdx.x == 0)
+    for (int s = tid; s <= S; s += kThreads) a.ws_pre[s] = sm.pre[s];
+  const int wg0 = blockIdx.x * kWaves * C;
+  if (wg0 >= U) return;  // the whole workgroup is idle
+  const int wg1 = min(U, wg0 + kWaves * C);
+
+  // q rows of the pairs this workgroup touches (as many as fit), contiguous in q.
+  const int pair_bytes = G * D * 2;
+  const int qbase = pair_of_unit(sm, wg0, Hkv, S);
+  const int nq = min(pair_of_unit(sm, wg1 - 1, Hkv, S) - qbase + 1, kQLds / pair_bytes);
+  {
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
+                                                           (int64_t)qbase * pair_bytes);
+    for (int i = tid; i < nq * pair_bytes / 16; i += kThreads) reinterpret_cast<u32x4_t *>(sm.q)[i] = src[i];
+  }
+  __syncthreads();
+
+  const int w = blockIdx.x * kWaves + wu;
+  const int u0 = w * C, u1 = min(U, u0 + C);
+  if (u0 >= u1) return;
+
+  W wave;
+  constexpr int NB = PA_BALANCED_RING;  // blocks held in registers per wave
+  typename W::Frag fr[NB];
+  bool bad = false, whole = false;
+  constexpr int EB = 2;
+  // A segment that ends before the wave's share does is parked in LDS and
+  // written when the share is done: stores count in the same counter as the
+  // ring's loads, so a store in mid-stream would make the next block wait
+  // for its acknowledgement.
+  float *park = park_lds + wu * park_floats(G, D);
+  bool parked = false, p_whole = false, p_bad = false;
+  int64_t p_row0 = 0, p_prow0 = 0;
+  for (int c0 = u0; c0 < u1;) {
+    // ---- this chunk's units, one per lane
+    int nc = min(64, u1 - c0);
+    const int u = min(c0 + lane, u1 - 1);
+    const int s = seq_of_block(sm, u / Hkv, S);
+    const int nb = sm.pre[s + 1] - sm.pre[s];
+    const int off = u - Hkv * sm.pre[s];
+    const int g = off / nb, j = off - g * nb;
+    const int L = sm.len[s];
+    const bool pend = j == nb - 1;
+    // Fused append: the unit holding position L-1 of a pair takes the new
+    // token.  At most kAppendMax such units per chunk (the chunk ends early).
+    uint64_t amask = 0;
+    if (a.k_new != nullptr) {
+      amask = __builtin_amdgcn_ballot_w64(lane < nc && pend);
+      uint64_t rest = amask;
+#pragma unroll
+      for (int k = 0; k < kAppendMax; ++k) rest &= rest - 1;
+      if (rest) {
+        nc = __builtin_ctzll(rest);
+        amask &= (1ull << nc) - 1;
+      }
+    }
+    int id = lane < nc ? a.block_tables[(int64_t)s * a.max_blocks + j] : 0;
+    uint32_t meta = (uint32_t)(pend ? L - (nb - 1) * kBS : kBS) | (j == 0 ? kUPairStart : 0u) |
+                    (pend ? kUPairEnd : 0u) | (u == u0 || j == 0 ? kUFirst : 0u) |
+                    (u == u1 - 1 || pend ? kULast : 0u);
+    // Cache rows of this chunk's appended tokens, written after its stream
+    // (the blocks' fragments take the token from LDS, so the store may come
+    // later; stores issued before the ring's loads would make its first wait
+    // cover their acknowledgement too).
+    int n_app = 0;
+    int app_blk[kAppendMax], app_tg[kAppendMax];
+    if (amask) {
+      const int64_t slot_l = ((amask >> lane) & 1) ? a.slot_mapping[s] : -1;
+      uint32_t kr[kAppendMax], vr[kAppendMax];
+      int pos[kAppendMax];
+      uint64_t mm = amask;
+#pragma unroll
+      for (int k = 0; k < kAppendMax; ++k) {
+        pos[k] = mm ? __builtin_ctzll(mm) : -1;
+        mm &= mm - 1;
+        kr[k] = vr[k] = 0;
+        if (pos[k] >= 0 && lane < D * EB / 4) {
+          const int sk = __builtin_amdgcn_readlane(s, pos[k]), gk = __builtin_amdgcn_readlane(g, pos[k]);
+          const int64_t row = ((int64_t)sk * Hkv + gk) * D * EB / 4;
+          kr[k] = reinterpret_cast<const uint32_t *>(a.k_new)[row + lane];
+          vr[k] = reinterpret_cast<const uint32_t *>(a.v_new)[row + lane];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kAppendMax; ++k) {
+        if (pos[k] < 0) break;
+        const int p = pos[k];
+        const uint32_t slo = __builtin_amdgcn_readlane((uint32_t)slot_l, p);
+        const uint32_t shi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)slot_l >> 32), p);
+        const int64_t slot = (int64_t)(((uint64_t)shi << 32) | slo);
+        if (slot < 0) continue;
+        const int blk = __builtin_amdgcn_readlane(id, p);
+        const int t = (__builtin_amdgcn_readlane(L, p) - 1) % kBS;
+        if ((uint32_t)blk >= (uint32_t)a.num_blocks || slot != (int64_t)blk * kBS + t) {
+          if (lane == p) meta |= kUBad;
+          continue;
+        }
+        if (lane < D * EB / 4) {
+          sm.knew[wu][k][lane] = kr[k];
+          sm.vnew[wu][k][lane] = vr[k];
+        }
+        app_blk[n_app] = blk;
+        app_tg[n_app] = (k << 24) | (t << 16) | __builtin_amdgcn_readlane(g, p);
+        ++n_app;
+        if (lane == p) meta |= kUNew | ((uint32_t)t << kUNewTokShift) | ((uint32_t)k << kUNewIdxShift);
+      }
+    }
+    if ((uint32_t)id >= (uint32_t)a.num_blocks) {
+      meta |= kUBad;
+      id = 0;
+    }
+    // Per unit only two registers stay live through the ring: the K/V tile
+    // index (block * Hkv + g) and the flags with the pair index.
+    const uint32_t tile = (uint32_t)id * (uint32_t)Hkv + (uint32_t)g;
+    meta |= (uint32_t)(s * Hkv + g) << kUPairShift;
+
+    // ---- stream the chunk through the register ring as the partition kernel
+    // does; the online-softmax state carries over from chunk to chunk.
+    auto refill = [&](typename W::Frag &f, int i) {
+      const bool real = i < nc;
+      const int64_t off = real ? (int64_t)__builtin_amdgcn_readlane(tile, min(i, nc - 1)) * W::TILE : 0;
+      W::load(f, a.k_cache + off, a.v_cache + off, real ? lane : 0);
+    };
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b) {
+      refill(fr[b], b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int i0 = 0; i0 < nc; i0 += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int i = i0 + b;
+        refill(fr[(b + NB - 1) % NB], i + NB - 1);
+        if (i < nc) {
+#ifndef PA_NO_PRIO
+          set_wave_priority((u1 - c0 - i) * 4 / (C + 1));
+#endif
+          const uint32_t mt = __builtin_amdgcn_readlane(meta, i);
+          const int pq = (int)(mt >> kUPairShift);
+          if (mt & kUFirst) {
+            wave.reset();
+            if (pq - qbase < nq) {
+              wave.load_q(sm.q + (pq - qbase) * (pair_bytes / 4), G, lane);
+            } else {
+              wave.load_q(static_cast<const uint8_t *>(a.q) + (int64_t)pq * pair_bytes, G, lane);
+              __builtin_amdgcn_s_waitcnt(0);  // keep the ring's wait counts static
+            }
+            bad = false;
+            whole = (mt & kUPairStart) != 0;
+          }
+          bad |= (mt & kUBad) != 0;
+          const int nt = (mt & kUNew) ? (int)((mt >> kUNewTokShift) & 15) : -1;
+          const int k = (mt >> kUNewIdxShift) & 3;
+          wave.compute(fr[b], (int)(mt & kUValid), a.scale_log2, lane, nt, sm.knew[wu][k], sm.vnew[wu][k]);
+          if (mt & kULast) {  // (a segment may go on into the next chunk)
+            const bool wh = whole && (mt & kUPairEnd);
+            if (c0 + i == u1 - 1 || parked) {  // (one parking place: a third segment stores)
+              wave.store_segment(a, (int64_t)pq * G, (int64_t)(w + pq) * G, wh, bad, lane, G);
+            } else {
+              wave.park_segment(park, lane, G);
+              parked = true;
+              p_whole = wh;
+              p_bad = bad;
+              p_row0 = (int64_t)pq * G;
+              p_prow0 = (int64_t)(w + pq) * G;
+            }
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int x = 0; x < kAppendMax; ++x) {
+      if (x < n_app) {
+        const int k = app_tg[x] >> 24, t = (app_tg[x] >> 16) & 0xFF, gx = app_tg[x] & 0xFFFF;
+        write_token_row<EB, D>(const_cast<uint8_t *>(a.k_cache), const_cast<uint8_t *>(a.v_cache), app_blk[x],
+                               t, gx, Hkv, sm.knew[wu][k], sm.vnew[wu][k], lane);
+      }
+    }
+    c0 += nc;
+  }
+  if (parked) flush_parked<D>(a, park, p_row0, p_prow0, p_whole, p_bad, lane, G);
+}
+
 // ---------------------------------------------------------------- merge kernel
 // One wave per (sequence, query head) row with more than one partition:
 //   M = max_p m_p,  out = sum_p 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p.
@@ -729,25 +1125,57 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
 // partial (bad table entry) makes the row NaN.
 constexpr int kMergeWaves = 4;
 
+// Folds np partials (m, l at ml + q*ml_stride, acc at acc + q*acc_stride)
+// into one output row.
 template <int D>
-__global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_kernel(DecodeArgs a, int32_t num_rows) {
+__device__ void merge_row(const DecodeArgs &a, int64_t row, const float *ml, int64_t ml_stride,
+                          const float *acc, int64_t acc_stride, int np, int lane) {
   constexpr int PER = D / 64;  // output dims per lane
-  const int lane = threadIdx.x % 64;
-  const int64_t row = (int64_t)blockIdx.x * kMergeWaves + threadIdx.x / 64;
-  if (row >= num_rows) return;
-  const int s = (int)(row / a.num_q_heads);
-  const int L = a.context_lens[s];
-  if (!ctx_valid(L, a)) return;
-  const int np = (L + a.part_tokens - 1) / a.part_tokens;
-  if (np <= 1) return;
-  const float *ml = a.ws_ml + row * a.max_parts * 2;
-  const float *acc = a.ws_acc + row * a.max_parts * D;
-  // Same arithmetic, in the same order, as the merge inside pa_decode's
-  // launch, so both paths give bit-identical rows.
+  constexpr int kFew = 8;
+  if (np <= kFew) {
+    // Every load first (one memory round trip), then the same arithmetic in
+    // the same order as the general loop below.
+    float mv[kFew], lv[kFew], av[kFew][PER];
+#pragma unroll
+    for (int q = 0; q < kFew; ++q) {
+      if (q < np) {
+        mv[q] = ml[q * ml_stride];
+        lv[q] = ml[q * ml_stride + 1];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) av[q][e] = acc[q * acc_stride + lane * PER + e];
+      }
+    }
+    float M = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int q = 0; q < kFew; ++q) {
+      if (q < np) {
+        nan |= mv[q] != mv[q];
+        M = fmaxf(M, mv[q]);
+      }
+    }
+    float den = 0.f;
+    float num[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) num[e] = 0.f;
+#pragma unroll
+    for (int q = 0; q < kFew; ++q) {
+      if (q < np) {
+        const float f = exp2f(mv[q] - M);
+        den += f * lv[q];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) num[e] += f * av[q][e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      store_out(a.out, row * D + lane * PER + e, nan ? NAN : num[e] / den, a.out_dtype);
+    return;
+  }
   float M = -INFINITY;
   bool nan = false;
   for (int q = 0; q < np; ++q) {
-    const float mq = ml[2 * q];
+    const float mq = ml[q * ml_stride];
     nan |= mq != mq;
     M = fmaxf(M, mq);
   }
@@ -757,14 +1185,56 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_kernel(DecodeArgs a
   for (int e = 0; e < PER; ++e) num[e] = 0.f;
 #pragma unroll 4
   for (int q = 0; q < np; ++q) {
-    const float f = exp2f(ml[2 * q] - M);
-    den += f * ml[2 * q + 1];
+    const float f = exp2f(ml[q * ml_stride] - M);
+    den += f * ml[q * ml_stride + 1];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] += f * acc[(int64_t)q * D + lane * PER + e];
+    for (int e = 0; e < PER; ++e) num[e] += f * acc[q * acc_stride + lane * PER + e];
   }
 #pragma unroll
   for (int e = 0; e < PER; ++e)
     store_out(a.out, row * D + lane * PER + e, nan ? NAN : num[e] / den, a.out_dtype);
+}
+
+template <int D>
+__global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_kernel(DecodeArgs a, int32_t num_rows) {
+  const int lane = threadIdx.x % 64;
+  const int64_t row = (int64_t)blockIdx.x * kMergeWaves + threadIdx.x / 64;
+  if (row >= num_rows) return;
+  const int s = (int)(row / a.num_q_heads);
+  const int L = a.context_lens[s];
+  if (!ctx_valid(L, a)) return;
+  const int np = (L + a.part_tokens - 1) / a.part_tokens;
+  if (np <= 1) return;
+  merge_row<D>(a, row, a.ws_ml + row * a.max_parts * 2, 2, a.ws_acc + row * a.max_parts * D, D, np, lane);
+}
+
+// Balanced split: the row of (s, head g*G + r) gathers the partials of its
+// pair from slots w + pair, w = first .. last wave share that overlaps the
+// pair's units.  A pair inside one share was written by its wave; rows of
+// empty (L = 0) and invalid contexts are written here (zeros / NaN).
+template <int D>
+__global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_balanced_kernel(DecodeArgs a, int32_t num_rows) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x % 64;
+  const int64_t row = (int64_t)blockIdx.x * kMergeWaves + threadIdx.x / 64;
+  if (row >= num_rows) return;
+  const int s = (int)(row / a.num_q_heads), h = (int)(row % a.num_q_heads);
+  const int G = a.group, g = h / G, r = h % G, Hkv = a.num_kv_heads;
+  const int L = a.context_lens[s];
+  const int pre_s = a.ws_pre[s], pre_s1 = a.ws_pre[s + 1], pre_end = a.ws_pre[a.num_seqs];
+  if (!ctx_valid(L, a) || L == 0) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) store_out(a.out, row * D + lane * PER + e, L == 0 ? 0.f : NAN, a.out_dtype);
+    return;
+  }
+  const int nb = pre_s1 - pre_s;
+  const int U = Hkv * pre_end;
+  const int C = (U + a.num_workers - 1) / a.num_workers;
+  const int us = Hkv * pre_s + g * nb;
+  const int w0 = us / C, w1 = (us + nb - 1) / C;
+  if (w0 == w1) return;
+  const int64_t prow = (int64_t)(w0 + s * Hkv + g) * G + r;
+  merge_row<D>(a, row, a.ws_ml + prow * 2, (int64_t)G * 2, a.ws_acc + prow * D, (int64_t)G * D, w1 - w0 + 1, lane);
 }
 
 // ---------------------------------------------------------------- KV append
@@ -906,6 +1376,63 @@ int32_t resolve_partition(const pa_decode_params *p) {
   return ctx <= pt ? ctx : pt;
 }
 
+bool use_mfma(const pa_decode_params *p) {
+  return p->kernel == PA_KERNEL_MFMA || (p->kernel == PA_KERNEL_AUTO && p->kv_dtype != PA_F32);
+}
+
+// Workgroups of the balanced grid: PA_BALANCED_WG_PER_CU per CU (checked
+// against the kernel's occupancy with its parking LDS for G query heads per
+// KV head where a device answers).
+size_t park_bytes(int G, int D) { return (size_t)kWaves * park_floats(G, D) * sizeof(float); }
+
+int balanced_workgroups(pa_dtype dt, int D, int G) {
+  static int cached[64][4][kGMax + 1] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PA_BALANCED_WG_PER_CU * cu_count();
+  const int k = (dt == PA_BF16 ? 0 : 2) + (D == 128 ? 0 : 1);
+  if (!cached[dev][k][G]) {
+    const void *fn = k == 0   ? reinterpret_cast<const void *>(&pa_balanced_kernel<PA_BF16, 128>)
+                     : k == 1 ? reinterpret_cast<const void *>(&pa_balanced_kernel<PA_BF16, 64>)
+                     : k == 2 ? reinterpret_cast<const void *>(&pa_balanced_kernel<PA_F16, 128>)
+                              : reinterpret_cast<const void *>(&pa_balanced_kernel<PA_F16, 64>);
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, park_bytes(G, D)) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = PA_BALANCED_WG_PER_CU;
+    cached[dev][k][G] = std::min(per_cu, PA_BALANCED_WG_PER_CU) * cu_count();
+  }
+  return cached[dev][k][G];
+}
+
+int balanced_workgroups(const pa_decode_params *p) {
+  return balanced_workgroups(p->kv_dtype, p->head_dim, p->num_q_heads / p->num_kv_heads);
+}
+
+// Automatic partitioning on the matrix-core path uses the balanced split
+// when the batch fits its LDS tables and its unit counts fit 32 bits.
+bool use_balanced(const pa_decode_params *p) {
+  if (p->partition_tokens != 0 || !use_mfma(p) || p->num_seqs < 1 || p->num_seqs > kSeqMax) return false;
+  if ((int64_t)p->num_seqs * p->num_kv_heads > kPairMax) return false;
+  if ((int64_t)p->num_blocks * p->num_kv_heads > UINT32_MAX) return false;
+  const int64_t units = (int64_t)p->num_kv_heads * p->num_seqs * ((std::max(p->max_context_len, 0) + kBS - 1) / kBS);
+  return units + (int64_t)kWaves * balanced_workgroups(p) < INT32_MAX;
+}
+
+size_t round16(size_t x) { return (x + 15) / 16 * 16; }
+
+// Balanced-split workspace: [S+1] int32 block offsets, then per slot
+// (NW + S*Hkv - 1 of them) G rows of (m, l) and G rows of D accumulators.
+size_t balanced_bytes(const pa_decode_params *p, size_t *ml_off, size_t *acc_off) {
+  const int64_t nw = (int64_t)kWaves * balanced_workgroups(p);
+  const int64_t slots = nw + (int64_t)p->num_seqs * p->num_kv_heads - 1;
+  const int64_t G = p->num_q_heads / p->num_kv_heads;
+  const size_t pre = round16(((size_t)p->num_seqs + 1) * 4);
+  const size_t ml = round16((size_t)slots * G * 2 * 4);
+  if (ml_off) *ml_off = pre;
+  if (acc_off) *acc_off = pre + ml;
+  return pre + ml + (size_t)slots * G * p->head_dim * 4;
+}
+
 size_t partial_bytes(const pa_decode_params *p, int32_t np) {
   return (size_t)p->num_seqs * p->num_q_heads * np * (p->head_dim + 2) * sizeof(float);
 }
@@ -953,11 +1480,13 @@ extern "C" {
 int32_t pa_decode_partition_tokens(const pa_decode_params *p) {
   pa_status st = validate(p);
   if (st != PA_OK) return -(int32_t)st;
+  if (use_balanced(p)) return 0;
   return resolve_partition(p);
 }
 
 size_t pa_decode_workspace_bytes(const pa_decode_params *p) {
   if (validate(p) != PA_OK) return 0;
+  if (use_balanced(p)) return balanced_bytes(p, nullptr, nullptr);
   const int32_t pt = resolve_partition(p);
   const int32_t np = num_partitions(p, pt);
   if (np <= 1) return 0;
@@ -973,8 +1502,9 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
                   const char *who, DecodeArgs &a) {
   pa_status st = validate(p);
   if (st != PA_OK) return st;
-  const int32_t pt = resolve_partition(p);
-  const int32_t np = num_partitions(p, pt);
+  const bool bal = use_balanced(p);
+  const int32_t pt = bal ? 0 : resolve_partition(p);
+  const int32_t np = bal ? 1 : num_partitions(p, pt);
   if ((int64_t)np * p->num_kv_heads * p->num_seqs > INT32_MAX)
     return pa::fail(PA_ERR_UNSUPPORTED, "%s: more than 2^31-1 workgroups (raise partition_tokens)", who);
   const size_t need = pa_decode_workspace_bytes(p);
@@ -993,6 +1523,16 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
   const size_t rows = (size_t)p->num_seqs * p->num_q_heads * np;
   a.ws_ml = need ? static_cast<float *>(workspace) : nullptr;
   a.ws_acc = need ? static_cast<float *>(workspace) + rows * 2 : nullptr;
+  a.ws_pre = nullptr;
+  a.num_workers = 0;
+  if (bal) {
+    size_t ml_off = 0, acc_off = 0;
+    balanced_bytes(p, &ml_off, &acc_off);
+    a.ws_pre = static_cast<int32_t *>(workspace);
+    a.ws_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + ml_off);
+    a.ws_acc = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + acc_off);
+    a.num_workers = kWaves * balanced_workgroups(p);
+  }
 
   a.num_seqs = p->num_seqs;
   a.num_q_heads = p->num_q_heads;
@@ -1009,7 +1549,20 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
 }
 
 pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipStream_t hs) {
-  const bool mfma = p->kernel == PA_KERNEL_MFMA || (p->kernel == PA_KERNEL_AUTO && p->kv_dtype != PA_F32);
+  const bool mfma = use_mfma(p);
+  if (use_balanced(p)) {
+    const dim3 grid((unsigned)(a.num_workers / kWaves));
+    const size_t lds = park_bytes(a.group, p->head_dim);
+    if (p->kv_dtype == PA_BF16 && p->head_dim == 128)
+      hipLaunchKernelGGL((pa_balanced_kernel<PA_BF16, 128>), grid, dim3(kThreads), lds, hs, a);
+    else if (p->kv_dtype == PA_BF16)
+      hipLaunchKernelGGL((pa_balanced_kernel<PA_BF16, 64>), grid, dim3(kThreads), lds, hs, a);
+    else if (p->head_dim == 128)
+      hipLaunchKernelGGL((pa_balanced_kernel<PA_F16, 128>), grid, dim3(kThreads), lds, hs, a);
+    else
+      hipLaunchKernelGGL((pa_balanced_kernel<PA_F16, 64>), grid, dim3(kThreads), lds, hs, a);
+    return hip_check(hipGetLastError(), "pa_decode balanced launch");
+  }
   const dim3 grid((unsigned)((int64_t)a.max_parts * p->num_kv_heads * p->num_seqs));
   if (p->head_dim == 128)
     launch_partition<128>(p->kv_dtype, mfma, a.group, grid, hs, a);
@@ -1019,9 +1572,16 @@ pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipS
 }
 
 pa_status launch_merge(const pa_decode_params *p, const DecodeArgs &a, hipStream_t hs) {
-  if (a.max_parts <= 1) return PA_OK;
   const int32_t rows = p->num_seqs * p->num_q_heads;
   const dim3 mgrid((rows + kMergeWaves - 1) / kMergeWaves);
+  if (use_balanced(p)) {
+    if (p->head_dim == 128)
+      hipLaunchKernelGGL(pa_merge_balanced_kernel<128>, mgrid, dim3(kMergeWaves * 64), 0, hs, a, rows);
+    else
+      hipLaunchKernelGGL(pa_merge_balanced_kernel<64>, mgrid, dim3(kMergeWaves * 64), 0, hs, a, rows);
+    return hip_check(hipGetLastError(), "pa_decode merge launch");
+  }
+  if (a.max_parts <= 1) return PA_OK;
   if (p->head_dim == 128)
     hipLaunchKernelGGL(pa_merge_kernel<128>, mgrid, dim3(kMergeWaves * 64), 0, hs, a, rows);
   else

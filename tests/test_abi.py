@@ -47,27 +47,52 @@ def _params(**over):
 
 
 def test_workspace_and_partition_arithmetic():
-    # no GPU here: the library assumes 256 compute units, i.e. a target of 2048
-    # workgroups; 64 sequences x 8 KV heads x ceil(4096/1024) reach it
-    p = _params()
+    # the partition rule of the vector-ALU path (and of the matrix-core path
+    # when a batch is too large for the balanced split).  No GPU here: the
+    # library assumes 256 compute units, i.e. a target of 2048 workgroups;
+    # 64 sequences x 8 KV heads x ceil(4096/1024) reach it
+    p = _params(kernel=pa.PA_KERNEL_VALU)
     assert pa.pa_decode_partition_tokens(p) == 1024
     # m and l plus a D-wide accumulator per (seq, q head, partition), float32
-    counters = 0
-    assert pa.pa_decode_workspace_bytes(p) == 64 * 64 * 4 * (128 + 2) * 4 + counters
+    assert pa.pa_decode_workspace_bytes(p) == 64 * 64 * 4 * (128 + 2) * 4
     p.num_seqs = 8                      # 8 x 8 x ceil(4096/256) < 2048: smallest partitions
     assert pa.pa_decode_partition_tokens(p) == 256
     p.num_seqs = 64
     p.max_context_len = 300             # 512 pairs x 1 partition < 2048: split at 256
     assert pa.pa_decode_partition_tokens(p) == 256
-    assert pa.pa_decode_workspace_bytes(p) == 64 * 64 * 2 * 130 * 4 + counters
+    assert pa.pa_decode_workspace_bytes(p) == 64 * 64 * 2 * 130 * 4
     p.num_seqs = 4096                   # a large batch of short contexts is not split
     assert pa.pa_decode_partition_tokens(p) == 304
     assert pa.pa_decode_workspace_bytes(p) == 0
     p.num_seqs = 64
     p.partition_tokens = 64
-    assert pa.pa_decode_workspace_bytes(p) == 64 * 64 * 5 * 130 * 4 + counters
+    assert pa.pa_decode_workspace_bytes(p) == 64 * 64 * 5 * 130 * 4
     p.num_seqs, p.num_kv_heads, p.num_q_heads = 3, 1, 2
     assert pa.pa_decode_workspace_bytes(p) == 3 * 2 * 5 * 130 * 4
+
+
+def _r16(x):
+    return (x + 15) // 16 * 16
+
+
+def test_balanced_split_selection_and_workspace():
+    # automatic partitioning on the matrix-core path: balanced split, reported
+    # as partition size 0.  Without a GPU: one workgroup of 4 waves per CU, 256 CUs.
+    nw = 256 * 4
+    p = _params()
+    assert pa.pa_decode_partition_tokens(p) == 0
+    slots = nw + 64 * 8 - 1             # one slot per segment: NW + pairs - 1
+    G, D = 8, 128
+    assert pa.pa_decode_workspace_bytes(p) == _r16(65 * 4) + _r16(slots * G * 2 * 4) + slots * G * D * 4
+    # explicit partitions, more than 1024 sequences, or more than 2^15 (s, g)
+    # pairs go back to the partition path
+    assert pa.pa_decode_partition_tokens(_params(partition_tokens=512)) == 512
+    assert pa.pa_decode_partition_tokens(_params(num_seqs=1025)) == 1024
+    assert pa.pa_decode_partition_tokens(_params(num_seqs=1024)) == 0
+    assert pa.pa_decode_partition_tokens(_params(num_seqs=1024, num_q_heads=64, num_kv_heads=32)) == 0
+    assert pa.pa_decode_partition_tokens(_params(num_seqs=1024, num_q_heads=64, num_kv_heads=64)) > 0
+    # fp32 caches never take the matrix-core path
+    assert pa.pa_decode_partition_tokens(_params(kv_dtype=pa.PA_F32, out_dtype=pa.PA_F32)) > 0
 
 
 @pytest.mark.parametrize("field,value,status", [

@@ -328,16 +328,64 @@ def test_split_launches_equal_pa_decode_bitwise():
     wl = workloads.generate(spec)
     gst = gpu_side.build(wl)
     mb = oracle_side.max_blocks_for(wl)
-    whole = gpu_side.decode(wl, gst, mb, out_dtype="f32", partition_tokens=256)
-    tab_d, lens_d, _, l = gpu_side.tables(gst, mb)
-    q = gpu_side.to_device(wl.q, "bf16")
-    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-    params = pa.make_decode_params(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, 2,
-                                   int(l.max()), spec.fp32_scale(), partition_tokens=256)
-    ws = torch.zeros(pa.pa_decode_workspace_bytes(params), dtype=torch.uint8, device="cuda")
-    pa.pa_decode_partitions(params, ws)
-    pa.pa_decode_merge(params, ws)
-    assert torch.equal(out, whole)
+    for pt in (256, 0):
+        whole = gpu_side.decode(wl, gst, mb, out_dtype="f32", partition_tokens=pt)
+        tab_d, lens_d, _, l = gpu_side.tables(gst, mb)
+        q = gpu_side.to_device(wl.q, "bf16")
+        out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        params = pa.make_decode_params(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, 2,
+                                       int(l.max()), spec.fp32_scale(), partition_tokens=pt)
+        ws = torch.zeros(pa.pa_decode_workspace_bytes(params), dtype=torch.uint8, device="cuda")
+        pa.pa_decode_partitions(params, ws)
+        pa.pa_decode_merge(params, ws)
+        assert torch.equal(out, whole), pt
+
+
+# ------------------------------------------------------------------ balanced split
+BALANCED_CASES = ["tiny_pairs", "one_long_context", "fewer_units_than_waves",
+                  "two_chunks_per_wave", "largest_batch"]
+
+
+@pytest.mark.parametrize("case", BALANCED_CASES)
+def test_balanced_split_length_mixes(case):
+    """Automatic partitioning on the matrix-core path: wave shares of equal
+    unit counts, crossing (sequence, KV head) pairs in every way."""
+    rng = np.random.default_rng(90)
+    sample = None
+    if case == "tiny_pairs":              # a wave's share spans several whole pairs
+        lens = rng.integers(1, 65, 1000)
+        spec = workloads.custom(seed=90, dtype="bf16", lens=tuple(int(x) for x in lens),
+                                num_q_heads=16, num_kv_heads=8, head_dim=64)
+    elif case == "one_long_context":      # one pair cut into more than a thousand partials
+        spec = workloads.custom(seed=91, dtype="f16", lens=(40000,), num_q_heads=8,
+                                num_kv_heads=1, head_dim=128)
+    elif case == "fewer_units_than_waves":
+        spec = workloads.custom(seed=92, dtype="bf16", lens=(3, 17, 40), num_q_heads=4,
+                                num_kv_heads=2, head_dim=128)
+    elif case == "two_chunks_per_wave":   # > 64 units per wave: shares go by 64-unit chunks
+        spec = workloads.custom(seed=93, dtype="bf16", lens=(8192,) * 12 + (8000,),
+                                num_q_heads=32, num_kv_heads=32, head_dim=64)
+        sample = [0, 5, 12]
+    else:                                 # 1024 sequences (the path's limit), some empty
+        lens = rng.integers(0, 300, 1024)
+        lens[::37] = 0
+        spec = workloads.custom(seed=94, dtype="bf16", lens=tuple(int(x) for x in lens),
+                                num_q_heads=8, num_kv_heads=2, head_dim=128)
+    wl, gst, ost = _both(spec)
+    mb = oracle_side.max_blocks_for(wl)
+    ref = oracle_side.decode(wl, ost, mb, seq_subset=sample)
+    tab_d, lens_d, _, lh = gpu_side.tables(gst, mb)
+    q = gpu_side.to_device(wl.q, spec.dtype)
+    prm = pa.make_decode_params(torch.empty(1, device="cuda"), q, gst.k_cache, gst.v_cache, tab_d,
+                                lens_d, spec.num_kv_heads, int(lh.max()), spec.fp32_scale(), 0, "mfma")
+    assert pa.pa_decode_partition_tokens(prm) == 0          # the balanced split runs
+    out = gpu_side.decode(wl, gst, mb, out_dtype="f32", kernel="mfma", partition_tokens=0)
+    got = _f32(out) if sample is None else _f32(out)[sample]
+    err = np.max(np.abs(got - ref))
+    _say(f"  {case}: max_abs_err={err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= TOL[spec.dtype], err
+    if sample is None:
+        assert np.all(got[np.asarray(wl.prompt_lens) == 0] == 0)
 
 
 # ------------------------------------------------------------------ fused append
@@ -351,6 +399,26 @@ def test_fused_append_equals_append_then_decode(dtype, D, kern, pt):
     # a child of sequence 0 (not decoded) shares its partly filled last block,
     # so the first step's append into sequence 0 must copy that block
     assert gst.pool.seq_fork(gst.seq_ids[0]) == ost.pool.seq_fork(ost.seq_ids[0])
+    assert _fused_steps(wl, gst, ost, kern, pt)
+
+
+def test_balanced_fused_append_with_more_pair_ends_than_one_chunk_stages():
+    # one-block contexts: every unit ends its (sequence, KV head) pair, so a
+    # wave's share holds more appended tokens than one chunk stages and the
+    # chunk is cut short
+    lens = tuple(int(x) for x in np.random.default_rng(95).integers(1, 15, 1000))
+    spec = workloads.custom(seed=95, dtype="bf16", lens=lens, num_q_heads=16, num_kv_heads=16,
+                            head_dim=64, decode_steps=2)
+    wl, gst, ost = _both(spec, steps=0)
+    _fused_steps(wl, gst, ost, "mfma", 0)
+
+
+def _fused_steps(wl, gst, ost, kern, pt):
+    """Runs the spec's decode steps with the append fused into pa_decode and
+    checks every step's rows against the oracle and the caches bit for bit;
+    returns whether any step needed a copy-on-write."""
+    spec = wl.spec
+    dtype, D = spec.dtype, spec.head_dim
     mb = oracle_side.max_blocks_for(wl)
     q = gpu_side.to_device(wl.q, dtype)
     saw_cow = False
@@ -371,10 +439,11 @@ def test_fused_append_equals_append_then_decode(dtype, D, kern, pt):
                      slot_mapping=torch.from_numpy(slots.copy()).cuda())
         ref = oracle_side.decode(wl, ost, mb)
         err = np.max(np.abs(_f32(out) - ref))
+        _say(f"  step {step} kernel={kern} partition_tokens={pt} max_abs_err={err:.3e}")
         assert err <= TOL[dtype], (step, err)
-    assert saw_cow
     torch.cuda.synchronize()
     _assert_caches_equal(gst, ost, dtype)
+    return saw_cow
 
 
 def test_fused_append_rejects_a_foreign_slot():
@@ -418,7 +487,7 @@ def test_one_workspace_serves_calls_of_any_shape():
         tab_d, lens_d, _, lh = gpu_side.tables(gst, mb)
         q = gpu_side.to_device(wl.q, dt)
         for kern in ("mfma", "valu"):
-            for pt in (16, 64, 256):
+            for pt in (0, 16, 64, 256):
                 whole = torch.full(q.shape, -7.0, dtype=torch.float32, device="cuda")
                 split = torch.full(q.shape, -7.0, dtype=torch.float32, device="cuda")
                 prm = pa.make_decode_params(whole, q, gst.k_cache, gst.v_cache, tab_d, lens_d,
