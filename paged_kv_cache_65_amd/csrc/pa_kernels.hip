@@ -838,14 +838,19 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
 #ifndef PA_BALANCED_RING
 #define PA_BALANCED_RING 4
 #endif
+#ifndef PA_BALANCED_WAVES
+#define PA_BALANCED_WAVES 4
+#endif
+constexpr int kBWaves = PA_BALANCED_WAVES;  // waves per balanced workgroup
+constexpr int kBThreads = kBWaves * 64;
 constexpr int kSeqMax = 1024;    // sequences per launch on this path
 constexpr int kQLds = 16384;     // bytes of q staged per workgroup
 constexpr int kAppendMax = 4;    // fused-append rows staged per wave and chunk
 
 struct __align__(16) SmemBalanced {
   uint32_t q[kQLds / 4];                        // q rows of pairs qbase .. qbase+nq-1
-  uint32_t knew[kWaves][kAppendMax][kDMax / 2];  // fused append: new K / V rows (16-bit)
-  uint32_t vnew[kWaves][kAppendMax][kDMax / 2];
+  uint32_t knew[kBWaves][kAppendMax][kDMax / 2];  // fused append: new K / V rows (16-bit)
+  uint32_t vnew[kBWaves][kAppendMax][kDMax / 2];
   int32_t pre[kSeqMax + 1];                      // blocks of the sequences before s
   int32_t len[kSeqMax];                          // context length (0 when invalid)
 };
@@ -897,19 +902,19 @@ __device__ inline int pair_of_unit(const SmemBalanced &sm, int u, int Hkv, int S
 }
 
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads, PA_BALANCED_WG_PER_CU) void pa_balanced_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kBThreads, PA_BALANCED_WG_PER_CU) void pa_balanced_kernel(DecodeArgs a) {
   using W = MfmaWave<DT, D>;
   __shared__ SmemBalanced sm;
-  extern __shared__ __align__(16) float park_lds[];  // kWaves x park_floats(G, D)
+  extern __shared__ __align__(16) float park_lds[];  // kBWaves x park_floats(G, D)
   const int tid = threadIdx.x, lane = tid % 64;
   const int wu = __builtin_amdgcn_readfirstlane(tid / 64);
   const int S = a.num_seqs, Hkv = a.num_kv_heads, G = a.group;
 
   // Context lengths, then block offsets by an exclusive scan (wave 0: each
   // lane sums a run of ceil(S/64) sequences, then a scan across lanes).
-  for (int s = tid; s < S; s += kThreads) {
+  for (int s = tid; s < S; s += kBThreads) {
     const int L = a.context_lens[s];
-    sm.len[s] = ctx_valid(L, a) ? L : 0;
+    sm.len[s] = ctx_valid(L, a) ? L : -1;  // -1: invalid (no blocks, NaN rows)
   }
   __syncthreads();
   if (wu == 0) {
@@ -935,10 +940,30 @@ __global__ __launch_bounds__(kThreads, PA_BALANCED_WG_PER_CU) void pa_balanced_k
   const int NW = a.num_workers;
   const int C = (U + NW - 1) / NW;
   if (blockIdx.x == 0)
-    for (int s = tid; s <= S; s += kThreads) a.ws_pre[s] = sm.pre[s];
-  const int wg0 = blockIdx.x * kWaves * C;
+    for (int s = tid; s <= S; s += kBThreads) a.ws_pre[s] = sm.pre[s];
+  // Rows of empty (L = 0: zeros) and invalid (NaN) contexts, spread over the grid.
+  for (int s = blockIdx.x; s < S; s += gridDim.x) {
+    const int L = sm.len[s];
+    if (L <= 0) {
+      const f32x4_t v = L == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : f32x4_t{NAN, NAN, NAN, NAN};
+      for (int e = tid * 4; e < a.num_q_heads * D; e += kBThreads * 4)
+        store_out4(a.out, (int64_t)s * a.num_q_heads * D + e, v, a.out_dtype);
+    }
+  }
+  const int wg0 = blockIdx.x * kBWaves * C;
   if (wg0 >= U) return;  // the whole workgroup is idle
-  const int wg1 = min(U, wg0 + kWaves * C);
+  const int wg1 = min(U, wg0 + kBWaves * C);
+  const int w = blockIdx.x * kBWaves + wu;
+  const int u0 = w * C, u1 = min(U, u0 + C);
+  // The first chunk's block ids go out before the q staging below.
+  int id_first = 0;
+  if (u0 < u1 && lane < u1 - u0) {
+    const int u = u0 + lane;
+    const int s = seq_of_block(sm, u / Hkv, S);
+    const int nb = sm.pre[s + 1] - sm.pre[s];
+    const int off = u - Hkv * sm.pre[s];
+    id_first = a.block_tables[(int64_t)s * a.max_blocks + off % nb];
+  }
 
   // q rows of the pairs this workgroup touches (as many as fit), contiguous in q.
   const int pair_bytes = G * D * 2;
@@ -947,12 +972,9 @@ __global__ __launch_bounds__(kThreads, PA_BALANCED_WG_PER_CU) void pa_balanced_k
   {
     const u32x4_t *src = reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
                                                            (int64_t)qbase * pair_bytes);
-    for (int i = tid; i < nq * pair_bytes / 16; i += kThreads) reinterpret_cast<u32x4_t *>(sm.q)[i] = src[i];
+    for (int i = tid; i < nq * pair_bytes / 16; i += kBThreads) reinterpret_cast<u32x4_t *>(sm.q)[i] = src[i];
   }
   __syncthreads();
-
-  const int w = blockIdx.x * kWaves + wu;
-  const int u0 = w * C, u1 = min(U, u0 + C);
   if (u0 >= u1) return;
 
   W wave;
@@ -990,7 +1012,8 @@ __global__ __launch_bounds__(kThreads, PA_BALANCED_WG_PER_CU) void pa_balanced_k
         amask &= (1ull << nc) - 1;
       }
     }
-    int id = lane < nc ? a.block_tables[(int64_t)s * a.max_blocks + j] : 0;
+    int id = c0 == u0 ? id_first : a.block_tables[(int64_t)s * a.max_blocks + j];
+    id = lane < nc ? id : 0;
     uint32_t meta = (uint32_t)(pend ? L - (nb - 1) * kBS : kBS) | (j == 0 ? kUPairStart : 0u) |
                     (pend ? kUPairEnd : 0u) | (u == u0 || j == 0 ? kUFirst : 0u) |
                     (u == u1 - 1 || pend ? kULast : 0u);
@@ -1210,24 +1233,18 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_kernel(DecodeArgs a
 
 // Balanced split: the row of (s, head g*G + r) gathers the partials of its
 // pair from slots w + pair, w = first .. last wave share that overlaps the
-// pair's units.  A pair inside one share was written by its wave; rows of
-// empty (L = 0) and invalid contexts are written here (zeros / NaN).
+// pair's units.  A pair inside one share, and the rows of empty (L = 0) and
+// invalid contexts, were written by the attention launch.
 template <int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_balanced_kernel(DecodeArgs a, int32_t num_rows) {
-  constexpr int PER = D / 64;
   const int lane = threadIdx.x % 64;
   const int64_t row = (int64_t)blockIdx.x * kMergeWaves + threadIdx.x / 64;
   if (row >= num_rows) return;
   const int s = (int)(row / a.num_q_heads), h = (int)(row % a.num_q_heads);
   const int G = a.group, g = h / G, r = h % G, Hkv = a.num_kv_heads;
-  const int L = a.context_lens[s];
   const int pre_s = a.ws_pre[s], pre_s1 = a.ws_pre[s + 1], pre_end = a.ws_pre[a.num_seqs];
-  if (!ctx_valid(L, a) || L == 0) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) store_out(a.out, row * D + lane * PER + e, L == 0 ? 0.f : NAN, a.out_dtype);
-    return;
-  }
   const int nb = pre_s1 - pre_s;
+  if (nb == 0) return;  // empty or invalid context: its rows come from the attention launch
   const int U = Hkv * pre_end;
   const int C = (U + a.num_workers - 1) / a.num_workers;
   const int us = Hkv * pre_s + g * nb;
@@ -1383,7 +1400,7 @@ bool use_mfma(const pa_decode_params *p) {
 // Workgroups of the balanced grid: PA_BALANCED_WG_PER_CU per CU (checked
 // against the kernel's occupancy with its parking LDS for G query heads per
 // KV head where a device answers).
-size_t park_bytes(int G, int D) { return (size_t)kWaves * park_floats(G, D) * sizeof(float); }
+size_t park_bytes(int G, int D) { return (size_t)kBWaves * park_floats(G, D) * sizeof(float); }
 
 int balanced_workgroups(pa_dtype dt, int D, int G) {
   static int cached[64][4][kGMax + 1] = {};
@@ -1396,7 +1413,7 @@ int balanced_workgroups(pa_dtype dt, int D, int G) {
                      : k == 2 ? reinterpret_cast<const void *>(&pa_balanced_kernel<PA_F16, 128>)
                               : reinterpret_cast<const void *>(&pa_balanced_kernel<PA_F16, 64>);
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, park_bytes(G, D)) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBThreads, park_bytes(G, D)) != hipSuccess ||
         per_cu <= 0)
       per_cu = PA_BALANCED_WG_PER_CU;
     cached[dev][k][G] = std::min(per_cu, PA_BALANCED_WG_PER_CU) * cu_count();
@@ -1415,7 +1432,7 @@ bool use_balanced(const pa_decode_params *p) {
   if ((int64_t)p->num_seqs * p->num_kv_heads > kPairMax) return false;
   if ((int64_t)p->num_blocks * p->num_kv_heads > UINT32_MAX) return false;
   const int64_t units = (int64_t)p->num_kv_heads * p->num_seqs * ((std::max(p->max_context_len, 0) + kBS - 1) / kBS);
-  return units + (int64_t)kWaves * balanced_workgroups(p) < INT32_MAX;
+  return units + (int64_t)kBWaves * balanced_workgroups(p) < INT32_MAX;
 }
 
 size_t round16(size_t x) { return (x + 15) / 16 * 16; }
@@ -1423,7 +1440,7 @@ size_t round16(size_t x) { return (x + 15) / 16 * 16; }
 // Balanced-split workspace: [S+1] int32 block offsets, then per slot
 // (NW + S*Hkv - 1 of them) G rows of (m, l) and G rows of D accumulators.
 size_t balanced_bytes(const pa_decode_params *p, size_t *ml_off, size_t *acc_off) {
-  const int64_t nw = (int64_t)kWaves * balanced_workgroups(p);
+  const int64_t nw = (int64_t)kBWaves * balanced_workgroups(p);
   const int64_t slots = nw + (int64_t)p->num_seqs * p->num_kv_heads - 1;
   const int64_t G = p->num_q_heads / p->num_kv_heads;
   const size_t pre = round16(((size_t)p->num_seqs + 1) * 4);
@@ -1531,7 +1548,7 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
     a.ws_pre = static_cast<int32_t *>(workspace);
     a.ws_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + ml_off);
     a.ws_acc = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + acc_off);
-    a.num_workers = kWaves * balanced_workgroups(p);
+    a.num_workers = kBWaves * balanced_workgroups(p);
   }
 
   a.num_seqs = p->num_seqs;
@@ -1551,16 +1568,16 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
 pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipStream_t hs) {
   const bool mfma = use_mfma(p);
   if (use_balanced(p)) {
-    const dim3 grid((unsigned)(a.num_workers / kWaves));
+    const dim3 grid((unsigned)(a.num_workers / kBWaves));
     const size_t lds = park_bytes(a.group, p->head_dim);
     if (p->kv_dtype == PA_BF16 && p->head_dim == 128)
-      hipLaunchKernelGGL((pa_balanced_kernel<PA_BF16, 128>), grid, dim3(kThreads), lds, hs, a);
+      hipLaunchKernelGGL((pa_balanced_kernel<PA_BF16, 128>), grid, dim3(kBThreads), lds, hs, a);
     else if (p->kv_dtype == PA_BF16)
-      hipLaunchKernelGGL((pa_balanced_kernel<PA_BF16, 64>), grid, dim3(kThreads), lds, hs, a);
+      hipLaunchKernelGGL((pa_balanced_kernel<PA_BF16, 64>), grid, dim3(kBThreads), lds, hs, a);
     else if (p->head_dim == 128)
-      hipLaunchKernelGGL((pa_balanced_kernel<PA_F16, 128>), grid, dim3(kThreads), lds, hs, a);
+      hipLaunchKernelGGL((pa_balanced_kernel<PA_F16, 128>), grid, dim3(kBThreads), lds, hs, a);
     else
-      hipLaunchKernelGGL((pa_balanced_kernel<PA_F16, 64>), grid, dim3(kThreads), lds, hs, a);
+      hipLaunchKernelGGL((pa_balanced_kernel<PA_F16, 64>), grid, dim3(kBThreads), lds, hs, a);
     return hip_check(hipGetLastError(), "pa_decode balanced launch");
   }
   const dim3 grid((unsigned)((int64_t)a.max_parts * p->num_kv_heads * p->num_seqs));
