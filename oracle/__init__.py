@@ -11,6 +11,9 @@ Contents
     whole-block copies.  Passages followed are cited in that file.
   * ``pool_model.py``: an independent pure-Python model of the refcounted
     block pool (allocation, fork, append with copy-on-write, free).
+  * INT8 caches: codes (``np.int8``) in their own tile layout plus one fp32
+    scale per (token, KV head) row; quantized on append, attended over the
+    dequantized rows (``*_i8`` functions).
 
 Data convention for the wrappers: cache-typed arrays are numpy arrays of
 ``np.float32`` (fp32), ``np.float16`` (fp16) or ``np.uint16`` holding raw
@@ -65,6 +68,20 @@ def _load():
         lib.oracle_decode.restype = _I
         lib.oracle_decode.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                       ctypes.c_float, _I, _I]
+        lib.oracle_k_offset_i8.restype = _I64
+        lib.oracle_k_offset_i8.argtypes = [_I64, _I, _I, _I, _I, _I]
+        lib.oracle_v_offset_i8.restype = _I64
+        lib.oracle_v_offset_i8.argtypes = [_I64, _I, _I, _I, _I, _I]
+        lib.oracle_quantize_row_i8.restype = ctypes.c_float
+        lib.oracle_quantize_row_i8.argtypes = [_P, _I64, _I, _I, _P]
+        lib.oracle_reshape_and_cache_i8.restype = _I
+        lib.oracle_reshape_and_cache_i8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
+                                                    _I64, _I]
+        lib.oracle_copy_blocks_i8.restype = None
+        lib.oracle_copy_blocks_i8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I]
+        lib.oracle_decode_i8.restype = _I
+        lib.oracle_decode_i8.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                         _I, ctypes.c_float, _I]
         lib.oracle_bruteforce_contiguous.restype = None
         lib.oracle_bruteforce_contiguous.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                                      ctypes.c_float, _I]
@@ -155,3 +172,60 @@ def to_float64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return a.astype(np.float64)
+
+
+# ---------------------------------------------------------------- INT8 caches
+def k_offset_i8(block, head, tok, dim, num_kv_heads, head_dim):
+    return _load().oracle_k_offset_i8(block, head, tok, dim, num_kv_heads, head_dim)
+
+
+def v_offset_i8(block, head, tok, dim, num_kv_heads, head_dim):
+    return _load().oracle_v_offset_i8(block, head, tok, dim, num_kv_heads, head_dim)
+
+
+def quantize_row_i8(row: np.ndarray, dtype: str):
+    """(codes int8 [n], scale float32) of one row in the given type."""
+    row = _check(np.asarray(row), dtype)
+    codes = np.empty(row.size, dtype=np.int8)
+    sc = _load().oracle_quantize_row_i8(_ptr(row), 0, row.size, _DTYPES[dtype], _ptr(codes))
+    return codes, np.float32(sc)
+
+
+def empty_cache_i8(num_blocks, num_kv_heads, head_dim):
+    """(codes, scales) of an unwritten int8 pool: codes 0x7F, scales NaN."""
+    codes = np.full(num_blocks * num_kv_heads * 16 * head_dim, 127, dtype=np.int8)
+    scales = np.full(num_blocks * num_kv_heads * 16, np.nan, dtype=np.float32)
+    return codes, scales
+
+
+def reshape_and_cache_i8(k_new, v_new, k_cache, v_cache, k_scales, v_scales, slot_mapping,
+                         num_kv_heads, head_dim, num_blocks, src_dtype):
+    """Quantize [T][Hkv][D] rows into the int8 caches in place; returns #out-of-range slots."""
+    k_new = _check(k_new, src_dtype)
+    v_new = _check(v_new, src_dtype)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    for a, t in ((k_cache, np.int8), (v_cache, np.int8), (k_scales, np.float32), (v_scales, np.float32)):
+        assert a.dtype == t and a.flags["C_CONTIGUOUS"]
+    return _load().oracle_reshape_and_cache_i8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                               _ptr(k_scales), _ptr(v_scales), _ptr(slots), len(slots),
+                                               num_kv_heads, head_dim, num_blocks, _DTYPES[src_dtype])
+
+
+def copy_blocks_i8(k_cache, v_cache, k_scales, v_scales, pairs, num_kv_heads, head_dim):
+    pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    _load().oracle_copy_blocks_i8(_ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+                                  _ptr(pairs), len(pairs), num_kv_heads, head_dim)
+
+
+def decode_i8(q, q_dtype, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens,
+              num_kv_heads, scale, nthreads=0, return_threads=False):
+    """fp64 paged decode over an int8 cache; q is [S][Hq][D] in q_dtype."""
+    q = _check(q, q_dtype)
+    S, Hq, D = q.shape
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    out = np.empty((S, Hq, D), dtype=np.float64)
+    used = _load().oracle_decode_i8(_ptr(out), _ptr(q), _DTYPES[q_dtype], _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(k_scales), _ptr(v_scales), _ptr(tables), _ptr(lens), S, Hq,
+                                    num_kv_heads, D, tables.shape[1], float(scale), nthreads)
+    return (out, used) if return_threads else out

@@ -41,6 +41,9 @@
  * the weighted V sum ascend in logical position i.  The table walk and the
  * contiguous brute force therefore produce bit-identical doubles.
  *
+ * The INT8 cache variant (quantize on append, attend over the dequantized
+ * rows) is at the end of this file.
+ *
  * Parity pins (tests marked "not gpu"): contiguous brute force (bitwise),
  * numpy float64 softmax attention, closed forms (length 1, uniform weights,
  * constant V, hard-max limit), block-permutation / shared-prefix / GQA-vs-MHA
@@ -304,4 +307,184 @@ void oracle_bruteforce_contiguous(double *out, const void *q, const void *k_seq,
     }
   free(sigma);
   free(qd);
+}
+
+/* ===========================================================================
+ * INT8 KV cache with one scale per (token, KV head) row.
+ *
+ * Quantization follows "LLM Inference Optimization: KV-Cache, PagedAttention,
+ * and GPU Memory Efficiency", section "Future Optimizations" (KV cache
+ * quantization): scale = max |x| over the row's last dimension / 127,
+ * code = (x / scale) converted to int8, dequantized value = code * scale.
+ * Readings: the arithmetic is float32 (the row's 16-bit values are widened
+ * exactly; the division is IEEE single precision, correctly rounded); the
+ * conversion to int8 truncates toward zero, as a float-to-integer cast does;
+ * an all-zero row has scale 0 and codes 0.  "Inference serving: the KV-cache
+ * machine" ("What insiders know") names per-head / per-channel scales as what
+ * keeps outlier heads accurate; here every (token, head) row has its own.
+ *
+ * Layout contract (byte offsets inside a tile of 16 tokens x D dims; tile
+ * (b, g) starts at byte (b*Hkv + g)*16*D; scales at float index
+ * (b*Hkv + g)*16 + t in separate k_scales / v_scales arrays):
+ *   K: element (t, d): c = d/64, w = d%64, h = w/32, q = (w%32)/8, e = w%8
+ *      -> byte (c*64 + q*16 + t)*16 + h*8 + e
+ *   V: element (t, d): m = d/64, k = (d%64)/16, r = d%16
+ *      -> byte (m*64 + (t/4)*16 + r)*16 + k*4 + t%4
+ * ------------------------------------------------------------------------ */
+int64_t oracle_k_offset_i8(int64_t block, int head, int tok, int dim, int num_kv_heads,
+                           int head_dim) {
+  int64_t tile = (block * num_kv_heads + head) * (int64_t)ORC_BS * head_dim;
+  int c = dim / 64, w = dim % 64, h = w / 32, q = (w % 32) / 8, e = w % 8;
+  return tile + (int64_t)(c * 64 + q * 16 + tok) * 16 + h * 8 + e;
+}
+
+int64_t oracle_v_offset_i8(int64_t block, int head, int tok, int dim, int num_kv_heads,
+                           int head_dim) {
+  int64_t tile = (block * num_kv_heads + head) * (int64_t)ORC_BS * head_dim;
+  int m = dim / 64, k = (dim % 64) / 16, r = dim % 16;
+  return tile + (int64_t)(m * 64 + (tok / 4) * 16 + r) * 16 + k * 4 + tok % 4;
+}
+
+/* Quantizes n elements of a row (src_dtype F16/BF16/F32) into int8 codes and
+ * returns the row's scale. */
+float oracle_quantize_row_i8(const void *x, int64_t first, int n, int src_dtype, int8_t *codes) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float a = (float)fabs(load_elem(x, first + i, src_dtype));
+    if (a > amax) amax = a;
+  }
+  float scale = amax / 127.0f;
+  for (int i = 0; i < n; ++i) {
+    if (scale == 0.0f) {
+      codes[i] = 0;
+      continue;
+    }
+    float v = (float)load_elem(x, first + i, src_dtype) / scale;
+    codes[i] = (v == v) ? (int8_t)(int)v : 0; /* C conversion truncates toward zero */
+  }
+  return scale;
+}
+
+/* Append with quantization: like oracle_reshape_and_cache, into int8 tiles
+ * plus per-row scales.  Returns the number of out-of-range slots. */
+int oracle_reshape_and_cache_i8(const void *k_new, const void *v_new, int8_t *k_cache,
+                                int8_t *v_cache, float *k_scales, float *v_scales,
+                                const int64_t *slot_mapping, int num_tokens, int num_kv_heads,
+                                int head_dim, int64_t num_blocks, int src_dtype) {
+  int bad = 0;
+  int8_t *codes = (int8_t *)malloc((size_t)head_dim);
+  for (int n = 0; n < num_tokens; ++n) {
+    int64_t s = slot_mapping[n];
+    if (s < 0) continue;
+    if (s >= num_blocks * ORC_BS) { ++bad; continue; }
+    int64_t blk = s / ORC_BS;
+    int t = (int)(s % ORC_BS);
+    for (int g = 0; g < num_kv_heads; ++g) {
+      int64_t row = ((int64_t)n * num_kv_heads + g) * head_dim;
+      int64_t sidx = (blk * num_kv_heads + g) * ORC_BS + t;
+      k_scales[sidx] = oracle_quantize_row_i8(k_new, row, head_dim, src_dtype, codes);
+      for (int d = 0; d < head_dim; ++d)
+        k_cache[oracle_k_offset_i8(blk, g, t, d, num_kv_heads, head_dim)] = codes[d];
+      v_scales[sidx] = oracle_quantize_row_i8(v_new, row, head_dim, src_dtype, codes);
+      for (int d = 0; d < head_dim; ++d)
+        v_cache[oracle_v_offset_i8(blk, g, t, d, num_kv_heads, head_dim)] = codes[d];
+    }
+  }
+  free(codes);
+  return bad;
+}
+
+/* Whole-block copy of an int8 cache: codes and scales of every head. */
+void oracle_copy_blocks_i8(int8_t *k_cache, int8_t *v_cache, float *k_scales, float *v_scales,
+                           const int32_t *pairs, int num_pairs, int num_kv_heads, int head_dim) {
+  size_t code_bytes = (size_t)num_kv_heads * ORC_BS * head_dim;
+  size_t scale_count = (size_t)num_kv_heads * ORC_BS;
+  for (int p = 0; p < num_pairs; ++p) {
+    size_t src = (size_t)pairs[2 * p], dst = (size_t)pairs[2 * p + 1];
+    memmove(k_cache + dst * code_bytes, k_cache + src * code_bytes, code_bytes);
+    memmove(v_cache + dst * code_bytes, v_cache + src * code_bytes, code_bytes);
+    memmove(k_scales + dst * scale_count, k_scales + src * scale_count, scale_count * sizeof(float));
+    memmove(v_scales + dst * scale_count, v_scales + src * scale_count, scale_count * sizeof(float));
+  }
+}
+
+/* Decode over an int8 cache: the keys and values attended are the
+ * dequantized rows code * scale (exact in double); q is F16 or BF16. */
+typedef struct {
+  const int8_t *k_cache, *v_cache;
+  const float *k_scales, *v_scales;
+  const int32_t *table;
+  int num_kv_heads, head_dim, kv_head;
+} orc_src_i8;
+
+static void attend_one_i8(double *out, const double *q, const orc_src_i8 *s, int L, double scale,
+                          double *sigma) {
+  int D = s->head_dim;
+  if (L <= 0) {
+    for (int d = 0; d < D; ++d) out[d] = 0.0;
+    return;
+  }
+  double M = -INFINITY;
+  for (int i = 0; i < L; ++i) {
+    int64_t blk = s->table[i / ORC_BS];
+    int t = i % ORC_BS;
+    double ks = (double)s->k_scales[(blk * s->num_kv_heads + s->kv_head) * ORC_BS + t];
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d)
+      dot += q[d] * ((double)s->k_cache[oracle_k_offset_i8(blk, s->kv_head, t, d, s->num_kv_heads, D)] * ks);
+    sigma[i] = scale * dot;
+    if (sigma[i] > M) M = sigma[i];
+  }
+  double Z = 0.0;
+  for (int i = 0; i < L; ++i) {
+    sigma[i] = exp(sigma[i] - M);
+    Z += sigma[i];
+  }
+  for (int d = 0; d < D; ++d) {
+    double acc = 0.0;
+    for (int i = 0; i < L; ++i) {
+      int64_t blk = s->table[i / ORC_BS];
+      int t = i % ORC_BS;
+      double vs = (double)s->v_scales[(blk * s->num_kv_heads + s->kv_head) * ORC_BS + t];
+      acc += sigma[i] * ((double)s->v_cache[oracle_v_offset_i8(blk, s->kv_head, t, d, s->num_kv_heads, D)] * vs);
+    }
+    out[d] = acc / Z;
+  }
+}
+
+int oracle_decode_i8(double *out, const void *q, int q_dtype, const int8_t *k_cache,
+                     const int8_t *v_cache, const float *k_scales, const float *v_scales,
+                     const int32_t *tables, const int32_t *lens, int num_seqs, int num_q_heads,
+                     int num_kv_heads, int head_dim, int max_blocks, float scale, int nthreads) {
+  int G = num_q_heads / num_kv_heads;
+  int Lmax = 0;
+  for (int s = 0; s < num_seqs; ++s)
+    if (lens[s] > Lmax) Lmax = lens[s];
+  int used = 1;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+  {
+#pragma omp single
+    used = omp_get_num_threads();
+#endif
+    double *sigma = (double *)malloc(sizeof(double) * (Lmax > 0 ? Lmax : 1));
+    double *qd = (double *)malloc(sizeof(double) * head_dim);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+    for (int sh = 0; sh < num_seqs * num_q_heads; ++sh) {
+      int s = sh / num_q_heads, h = sh % num_q_heads;
+      for (int d = 0; d < head_dim; ++d) qd[d] = load_elem(q, (int64_t)sh * head_dim + d, q_dtype);
+      orc_src_i8 src = {k_cache, v_cache, k_scales, v_scales, tables + (int64_t)s * max_blocks,
+                        num_kv_heads, head_dim, h / G};
+      attend_one_i8(out + (int64_t)sh * head_dim, qd, &src, lens[s], (double)scale, sigma);
+    }
+    free(sigma);
+    free(qd);
+#ifdef _OPENMP
+  }
+#endif
+  (void)nthreads;
+  return used;
 }
