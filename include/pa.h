@@ -31,6 +31,19 @@
  * Both tiles are layouts of this library's own choosing (the pages leave the
  * in-block order open): one 16-byte load per lane then hands each lane of a
  * 64-wide wavefront exactly the operand fragment the matrix-core tiles use.
+ *
+ * INT8 caches.  Row (token t, KV head g) of K (and of V) is stored as
+ * head_dim int8 codes c and one float32 scale sc, standing for the values
+ * c * sc.  Quantization ("LLM Inference Optimization: KV-Cache,
+ * PagedAttention, and GPU Memory Efficiency", section "Future
+ * Optimizations"): sc = max_d |x_d| / 127 and c_d = x_d / sc truncated
+ * toward zero, both in float32 (an all-zero row has sc = 0, codes 0).  Code
+ * tiles are 16*head_dim bytes at byte (b*num_kv_heads + g)*16*head_dim:
+ *   K: (t, d) -> (c*64 + q*16 + t)*16 + h*8 + e,  with c = d/64, w = d%64,
+ *               h = w/32, q = (w%32)/8, e = w%8
+ *   V: (t, d) -> (m*64 + (t/4)*16 + d%16)*16 + ((d%64)/16)*4 + t%4,  m = d/64
+ * (again one 16-byte lane load per operand fragment); scales are float32
+ * arrays k_scales, v_scales [num_blocks][num_kv_heads][16].
  */
 #ifndef PA_H
 #define PA_H
@@ -53,7 +66,9 @@ typedef enum pa_status {
   PA_ERR_HIP = 5           /* a HIP runtime call failed (e.g. launch error) */
 } pa_status;
 
-typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* PA_I8: a cache of int8 codes with one float32 scale per (token, KV head)
+ * row (see "INT8 caches" below); never a q or output type. */
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_I8 = 3 } pa_dtype;
 
 /* Which decode kernel runs.  AUTO picks the matrix-core kernel for fp16/bf16
  * caches and the vector-ALU kernel for fp32. */
@@ -155,6 +170,15 @@ typedef struct pa_decode_params {
   const void *k_new;
   const void *v_new;
   const int64_t *slot_mapping;
+  /* INT8 caches (kv_dtype = PA_I8) only, else ignored: the type of q (F16 or
+   * BF16; out_dtype is F32 or q_dtype) and the float32 scale arrays
+   * [num_blocks][num_kv_heads][16].  Decoding an INT8 cache needs the
+   * matrix-core kernel and automatic partitioning (the balanced split); the
+   * fused append is not available for it (append with
+   * pa_reshape_and_cache_int8 first). */
+  pa_dtype q_dtype;
+  const float *k_scales;
+  const float *v_scales;
 } pa_decode_params;
 
 /* Partition size (tokens) pa_decode will use for these parameters, 0 for the
@@ -210,6 +234,16 @@ pa_status pa_reshape_and_cache(const void *k_new, const void *v_new, void *k_cac
                                int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                                pa_dtype dtype, void *stream);
 
+/* pa_reshape_and_cache into an INT8 cache: each (token, KV head) row of
+ * k_new / v_new (src_dtype F16 or BF16) is quantized as described under
+ * "INT8 caches" and stored with its scale.  Codes and scales are bit-exact
+ * with that definition (float32 division, correctly rounded). */
+pa_status pa_reshape_and_cache_int8(const void *k_new, const void *v_new, int8_t *k_cache,
+                                    int8_t *v_cache, float *k_scales, float *v_scales,
+                                    const int64_t *slot_mapping, int32_t num_tokens,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                    pa_dtype src_dtype, void *stream);
+
 /* ------------------------------------------------------------------------
  * Whole-block copies for copy-on-write: for each pair i, block
  * src_dst_pairs[2i] (all heads, K and V) is copied to block src_dst_pairs[2i+1]
@@ -222,6 +256,11 @@ pa_status pa_reshape_and_cache(const void *k_new, const void *v_new, void *k_cac
 pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst_pairs,
                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                          int32_t num_blocks, pa_dtype dtype, void *stream);
+
+/* pa_copy_blocks for an INT8 cache: codes and scales of every head. */
+pa_status pa_copy_blocks_int8(int8_t *k_cache, int8_t *v_cache, float *k_scales, float *v_scales,
+                              const int32_t *src_dst_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t num_blocks, void *stream);
 
 /* ------------------------------------------------------------------------
  * Host-side block pool.  Blocks are allocated on demand and returned when

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_OOM, PA_ERR_HIP = range(6)
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_I8 = 0, 1, 2, 3
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
 KERNELS = {"auto": PA_KERNEL_AUTO, "valu": PA_KERNEL_VALU, "mfma": PA_KERNEL_MFMA}
 BLOCK_SIZE = 16
@@ -43,7 +43,8 @@ class pa_decode_params(ctypes.Structure):
                 ("head_dim", _I32), ("max_blocks_per_seq", _I32), ("num_blocks", _I32),
                 ("max_context_len", _I32), ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int),
                 ("out_dtype", ctypes.c_int), ("partition_tokens", _I32), ("kernel", ctypes.c_int),
-                ("k_new", _P), ("v_new", _P), ("slot_mapping", _P)]
+                ("k_new", _P), ("v_new", _P), ("slot_mapping", _P),
+                ("q_dtype", ctypes.c_int), ("k_scales", _P), ("v_scales", _P)]
 
 
 _lib = None
@@ -67,6 +68,9 @@ def lib():
             "pa_reshape_and_cache": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                                     ctypes.c_int, _P]),
             "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, ctypes.c_int, _P]),
+            "pa_reshape_and_cache_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                                         _I32, ctypes.c_int, _P]),
+            "pa_copy_blocks_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P]),
             "pa_block_pool_create": (ctypes.c_int, [_I32, _I32, _PI32, ctypes.POINTER(_P)]),
             "pa_block_pool_destroy": (None, [_P]),
             "pa_block_pool_num_blocks": (_I32, [_P]),
@@ -105,7 +109,7 @@ def pa_version() -> str:
 # ---------------------------------------------------------------- device calls
 def _dtype_code(t) -> int:
     import torch
-    codes = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+    codes = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
     if t.dtype not in codes:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return codes[t.dtype]
@@ -130,14 +134,16 @@ def _stream(stream):
 
 def make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
                        max_context_len, scale, partition_tokens=0, kernel="auto", k_new=None,
-                       v_new=None, slot_mapping=None):
+                       v_new=None, slot_mapping=None, k_scales=None, v_scales=None):
+    """k_scales / v_scales: the float32 scale arrays of an int8 cache (else None)."""
     S, Hq, D = q.shape
     nb = k_cache.numel() // (num_kv_heads * BLOCK_SIZE * D)
     return pa_decode_params(
         _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), _dev(context_lens),
         S, Hq, num_kv_heads, D, block_tables.shape[1] if block_tables.dim() == 2 else 0, nb,
         int(max_context_len), float(scale), _dtype_code(k_cache), _dtype_code(out),
-        int(partition_tokens), KERNELS[kernel], _dev(k_new), _dev(v_new), _dev(slot_mapping))
+        int(partition_tokens), KERNELS[kernel], _dev(k_new), _dev(v_new), _dev(slot_mapping),
+        _dtype_code(q), _dev(k_scales), _dev(v_scales))
 
 
 def pa_decode_workspace_bytes(params: pa_decode_params) -> int:
@@ -153,14 +159,16 @@ def pa_decode_partition_tokens(params: pa_decode_params) -> int:
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
               max_context_len, scale, partition_tokens=0, kernel="auto", workspace=None,
-              stream=None, k_new=None, v_new=None, slot_mapping=None):
+              stream=None, k_new=None, v_new=None, slot_mapping=None, k_scales=None,
+              v_scales=None):
     """out <- paged decode attention (optionally appending k_new/v_new first).
     workspace: a uint8 device tensor of at least pa_decode_workspace_bytes()
-    bytes (no initialization needed), or None to allocate one."""
+    bytes (no initialization needed), or None to allocate one.  For an int8
+    cache pass its k_scales / v_scales."""
     import torch
     params = make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens,
                                 num_kv_heads, max_context_len, scale, partition_tokens, kernel,
-                                k_new, v_new, slot_mapping)
+                                k_new, v_new, slot_mapping, k_scales, v_scales)
     need = pa_decode_workspace_bytes(params)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -194,6 +202,25 @@ def pa_reshape_and_cache(k_new, v_new, k_cache, v_cache, slot_mapping, stream=No
     _check(lib().pa_reshape_and_cache(_dev(k_new), _dev(v_new), _dev(k_cache), _dev(v_cache),
                                       _dev(slot_mapping), T, Hkv, D, nb, _dtype_code(k_cache),
                                       _stream(stream)))
+
+
+def pa_reshape_and_cache_int8(k_new, v_new, k_cache, v_cache, k_scales, v_scales, slot_mapping,
+                              stream=None):
+    """Quantize [T][Hkv][D] fp16/bf16 rows into an int8 cache and its scales."""
+    T, Hkv, D = k_new.shape
+    nb = k_cache.numel() // (Hkv * BLOCK_SIZE * D)
+    _check(lib().pa_reshape_and_cache_int8(_dev(k_new), _dev(v_new), _dev(k_cache), _dev(v_cache),
+                                           _dev(k_scales), _dev(v_scales), _dev(slot_mapping), T,
+                                           Hkv, D, nb, _dtype_code(k_new), _stream(stream)))
+
+
+def pa_copy_blocks_int8(k_cache, v_cache, k_scales, v_scales, src_dst_pairs, num_kv_heads,
+                        head_dim, stream=None):
+    n = src_dst_pairs.numel() // 2
+    nb = k_cache.numel() // (num_kv_heads * BLOCK_SIZE * head_dim)
+    _check(lib().pa_copy_blocks_int8(_dev(k_cache), _dev(v_cache), _dev(k_scales), _dev(v_scales),
+                                     _dev(src_dst_pairs), n, num_kv_heads, head_dim, nb,
+                                     _stream(stream)))
 
 
 def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, num_kv_heads, head_dim, stream=None):

@@ -155,6 +155,8 @@ struct DecodeArgs {
   const int32_t *context_lens;
   float *ws_ml;   // [S][Hq][max_parts][2]  (m in log2 units, l)
   float *ws_acc;  // [S][Hq][max_parts][D]  unnormalised weighted V sums
+  const float *k_scales;         // INT8 caches: [NB][Hkv][16] per-row scales
+  const float *v_scales;
   const uint8_t *k_new;          // fused append: [S][Hkv][D] rows of the step's token, or null
   const uint8_t *v_new;
   const int64_t *slot_mapping;   // fused append: [S] slot of position L-1 (negative = no append)
@@ -316,6 +318,12 @@ struct MfmaWave {
     for (int c = 0; c < NC; ++c) f.k[c] = __builtin_nontemporal_load(&kp[c * 64 + lane]);
 #pragma unroll
     for (int c = 0; c < NC; ++c) f.v[c] = __builtin_nontemporal_load(&vp[c * 64 + lane]);
+  }
+
+  static constexpr bool kAppend = true;  // supports the fused append
+  // Tile index = block * Hkv + head.
+  __device__ static void load_tile(Frag &f, const DecodeArgs &a, int64_t tile, int lane) {
+    load(f, a.k_cache + tile * TILE, a.v_cache + tile * TILE, lane);
   }
 
   __device__ static f32x4_t mma_qk(const v8 &a, const v8 &b, f32x4_t c) {
@@ -490,6 +498,107 @@ __device__ void flush_parked(const DecodeArgs &a, const float *st, int64_t row0,
     a.ws_ml[(prow0 + lane) * 2 + 1] = st[G * D + G + lane];
   }
 }
+
+// ============================================================================
+// MFMA wave over an INT8 cache (q in QDT = fp16 / bf16).
+//
+// Codes are small integers, exact in fp16 and bf16, so the matrix cores take
+// them unscaled: the K scale multiplies the token's score after q.K^T, and
+// the V scale joins the token's softmax weight before P.V (the running sum l
+// keeps the unscaled weights).  With c = lane / 16 and r = lane % 16:
+//   K code vector x (x < D/64) of lane l: token r; bytes 0-7 dims
+//     64x + 8c .. +7 (q.K^T chunk 2x), bytes 8-15 dims 64x + 32 + 8c .. +7
+//     (chunk 2x + 1);
+//   V code vector x: tokens 4c .. 4c+3 of dims 64x + 16k + r, bytes 4k .. 4k+3
+//     -> A operand of the P.V tile n = 4x + k;
+//   scales: the four tokens 4c .. 4c+3 of the lane's score rows.
+// ============================================================================
+template <int QDT, int D>
+struct MfmaWaveI8 : MfmaWave<QDT, D> {
+  using Base = MfmaWave<QDT, D>;
+  using typename Base::v8;
+  using Base::NC;
+  using Base::NT;
+  static constexpr int NV = D / 64;        // 16-byte code vectors per lane and tile
+  static constexpr int TILE = kBS * D;     // code bytes per (block, head) tile
+  static constexpr bool kAppend = false;   // append with pa_reshape_and_cache_int8 first
+
+  struct Frag {
+    u32x4_t k[NV];
+    u32x4_t v[NV];
+    f32x4_t ks, vs;
+  };
+
+  __device__ static void load_tile(Frag &f, const DecodeArgs &a, int64_t tile, int lane) {
+    const u32x4_t *kp = reinterpret_cast<const u32x4_t *>(a.k_cache + tile * TILE);
+    const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(a.v_cache + tile * TILE);
+#pragma unroll
+    for (int x = 0; x < NV; ++x) f.k[x] = __builtin_nontemporal_load(&kp[x * 64 + lane]);
+#pragma unroll
+    for (int x = 0; x < NV; ++x) f.v[x] = __builtin_nontemporal_load(&vp[x * 64 + lane]);
+    const f32x4_t *ksp = reinterpret_cast<const f32x4_t *>(a.k_scales + tile * kBS);
+    const f32x4_t *vsp = reinterpret_cast<const f32x4_t *>(a.v_scales + tile * kBS);
+    f.ks = __builtin_nontemporal_load(&ksp[lane / 16]);
+    f.vs = __builtin_nontemporal_load(&vsp[lane / 16]);
+  }
+
+  // Two sign-extended codes of w (bytes i, i+1) as a packed pair of 16-bit values.
+  __device__ static uint32_t pair16(uint32_t w, int i) {
+    const float lo = (float)(int8_t)(w >> (8 * i));
+    const float hi = (float)(int8_t)(w >> (8 * i + 8));
+    if constexpr (QDT == PA_BF16)
+      return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+    else
+      return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+  }
+
+  __device__ void compute(Frag &f, int valid, float scale_log2, int lane, int /*new_tok*/,
+                          const uint32_t *, const uint32_t *) {
+    const int tq = lane / 16;
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint32_t w0 = f.k[c / 2][(c % 2) * 2], w1 = f.k[c / 2][(c % 2) * 2 + 1];
+      const u32x4_t ab = {pair16(w0, 0), pair16(w0, 2), pair16(w1, 0), pair16(w1, 2)};
+      sc = Base::mma_qk(__builtin_bit_cast(v8, ab), this->qB[c], sc);
+    }
+    float s[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s[v] = sc[v] * f.ks[v] * scale_log2;
+    // tokens past the context: scores masked (their scales may be anything)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s[v] = (4 * tq + v < valid) ? s[v] : -INFINITY;
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = max_xor32(max_xor16(mx));
+    const bool bump = mx > this->m + kLazyLog2;
+    if (__builtin_amdgcn_ballot_w64(bump)) {
+      const float m_new = bump ? mx : this->m;
+      const float alpha = exp2_neg(this->m - m_new);
+      this->l *= alpha;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) this->acc[n] *= alpha;
+      this->m = m_new;
+    }
+    float p[4], pw[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      p[v] = __builtin_amdgcn_exp2f(s[v] - this->m);
+      pw[v] = (4 * tq + v < valid) ? p[v] * f.vs[v] : 0.f;
+    }
+    this->l += (p[0] + p[1]) + (p[2] + p[3]);
+    u32x2_t ph, pl;
+    Base::split(pw, ph, pl);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const uint32_t w = f.v[n / 4][n % 4];
+      const u32x2_t av = {pair16(w, 0), pair16(w, 2)};
+      this->acc[n] = Base::mma_pv(av, ph, this->acc[n]);
+      this->acc[n] = Base::mma_pv(av, pl, this->acc[n]);
+    }
+  }
+};
 
 // ============================================================================
 // Vector-ALU wave: any cache type, GM = compile-time bound on the group size.
@@ -901,9 +1010,8 @@ __device__ inline int pair_of_unit(const SmemBalanced &sm, int u, int Hkv, int S
   return s * Hkv + (u - Hkv * sm.pre[s]) / nb;
 }
 
-template <int DT, int D>
+template <class W, int D>
 __global__ __launch_bounds__(kBThreads, PA_BALANCED_WG_PER_CU) void pa_balanced_kernel(DecodeArgs a) {
-  using W = MfmaWave<DT, D>;
   __shared__ SmemBalanced sm;
   extern __shared__ __align__(16) float park_lds[];  // kBWaves x park_floats(G, D)
   const int tid = threadIdx.x, lane = tid % 64;
@@ -1002,7 +1110,7 @@ __global__ __launch_bounds__(kBThreads, PA_BALANCED_WG_PER_CU) void pa_balanced_
     // Fused append: the unit holding position L-1 of a pair takes the new
     // token.  At most kAppendMax such units per chunk (the chunk ends early).
     uint64_t amask = 0;
-    if (a.k_new != nullptr) {
+    if (W::kAppend && a.k_new != nullptr) {
       amask = __builtin_amdgcn_ballot_w64(lane < nc && pend);
       uint64_t rest = amask;
 #pragma unroll
@@ -1077,8 +1185,7 @@ __global__ __launch_bounds__(kBThreads, PA_BALANCED_WG_PER_CU) void pa_balanced_
     // does; the online-softmax state carries over from chunk to chunk.
     auto refill = [&](typename W::Frag &f, int i) {
       const bool real = i < nc;
-      const int64_t off = real ? (int64_t)__builtin_amdgcn_readlane(tile, min(i, nc - 1)) * W::TILE : 0;
-      W::load(f, a.k_cache + off, a.v_cache + off, real ? lane : 0);
+      W::load_tile(f, a, real ? (int64_t)__builtin_amdgcn_readlane(tile, min(i, nc - 1)) : 0, real ? lane : 0);
     };
 #pragma unroll
     for (int b = 0; b < NB - 1; ++b) {
@@ -1294,6 +1401,61 @@ __global__ __launch_bounds__(256) void pa_reshape_and_cache_kernel(
   }
 }
 
+// ---------------------------------------------------------------- INT8 append
+// One wave per (token, KV head) row: max |x| over the row by a wave
+// reduction, scale = max / 127 and codes = x / scale truncated toward zero
+// (float32, correctly rounded division), codes scattered into the int8 tile
+// layout, the scale stored beside it.
+template <int SDT, int D>
+__device__ void quantize_row_i8(const uint16_t *x, int8_t *tile_codes, float *scale_out, int t, bool is_v,
+                                int lane) {
+  constexpr int PER = D / 64;
+  float v[PER];
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const uint32_t bits = x[lane * PER + e];
+    v[e] = SDT == PA_BF16 ? __uint_as_float(bits << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+    amax = fmaxf(amax, fabsf(v[e]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  const float scale = amax / 127.0f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int d = lane * PER + e;
+    const float qv = scale == 0.f ? 0.f : v[e] / scale;
+    const int code = qv == qv ? (int)qv : 0;  // conversion truncates toward zero
+    int off;
+    if (!is_v) {
+      const int c = d / 64, w = d % 64;
+      off = (c * 64 + ((w % 32) / 8) * 16 + t) * 16 + (w / 32) * 8 + w % 8;
+    } else {
+      off = ((d / 64) * 64 + (t / 4) * 16 + d % 16) * 16 + ((d % 64) / 16) * 4 + t % 4;
+    }
+    tile_codes[off] = (int8_t)code;
+  }
+  if (lane == 0) *scale_out = scale;
+}
+
+template <int SDT, int D>
+__global__ __launch_bounds__(256) void pa_reshape_and_cache_i8_kernel(
+    const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new, int8_t *k_cache, int8_t *v_cache,
+    float *k_scales, float *v_scales, const int64_t *__restrict__ slots, int32_t num_tokens,
+    int32_t num_kv_heads, int64_t num_slots) {
+  const int lane = threadIdx.x % 64;
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // token * Hkv + head
+  if (row >= (int64_t)num_tokens * num_kv_heads) return;
+  const int g = (int)(row % num_kv_heads);
+  const int64_t n = row / num_kv_heads;
+  const int64_t slot = slots[n];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t tile = (slot / kBS) * num_kv_heads + g;
+  const int t = (int)(slot % kBS);
+  quantize_row_i8<SDT, D>(k_new + row * D, k_cache + tile * kBS * D, k_scales + tile * kBS + t, t, false, lane);
+  quantize_row_i8<SDT, D>(v_new + row * D, v_cache + tile * kBS * D, v_scales + tile * kBS + t, t, true, lane);
+}
+
 // ---------------------------------------------------------------- block copy
 // grid.x = pair; each thread moves 16-byte vectors of the whole block (K and V).
 __global__ __launch_bounds__(256) void pa_copy_blocks_kernel(uint8_t *k_cache, uint8_t *v_cache,
@@ -1343,10 +1505,22 @@ pa_status validate(const pa_decode_params *p) {
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim must be 64 or 128");
   if (p->max_blocks_per_seq <= 0 || p->num_blocks <= 0 || p->max_context_len < 0)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: sizes must be positive");
-  if (!valid_dtype(p->kv_dtype) || !valid_dtype(p->out_dtype))
+  if (!(valid_dtype(p->kv_dtype) || p->kv_dtype == PA_I8) || !valid_dtype(p->out_dtype))
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: unknown dtype");
-  if (p->out_dtype != PA_F32 && p->out_dtype != p->kv_dtype)
+  if (p->kv_dtype == PA_I8) {
+    if (p->q_dtype != PA_F16 && p->q_dtype != PA_BF16)
+      return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: an INT8 cache needs q_dtype F16 or BF16");
+    if (p->out_dtype != PA_F32 && p->out_dtype != p->q_dtype)
+      return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype must be F32 or q_dtype");
+    if (!p->k_scales || !p->v_scales || !aligned16(p->k_scales) || !aligned16(p->v_scales))
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: an INT8 cache needs 16-byte aligned scale arrays");
+    if (p->kernel == PA_KERNEL_VALU || p->partition_tokens != 0 || p->k_new != nullptr)
+      return pa::fail(PA_ERR_UNSUPPORTED,
+                      "pa_decode: an INT8 cache is decoded by the matrix-core kernel with automatic "
+                      "partitioning and no fused append");
+  } else if (p->out_dtype != PA_F32 && p->out_dtype != p->kv_dtype) {
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype must be F32 or the cache type");
+  }
   if (p->partition_tokens < 0 || p->partition_tokens % kBS)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: partition_tokens must be 0 or a positive multiple of 16");
   if (p->kernel != PA_KERNEL_AUTO && p->kernel != PA_KERNEL_VALU && p->kernel != PA_KERNEL_MFMA)
@@ -1359,6 +1533,19 @@ pa_status validate(const pa_decode_params *p) {
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: device pointers must be 16-byte aligned");
   if (!(std::isfinite(p->scale)))
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: scale must be finite");
+  return PA_OK;
+}
+
+bool use_balanced(const pa_decode_params *p);
+
+// validate() plus the checks that depend on the chosen split.
+pa_status validate_all(const pa_decode_params *p) {
+  pa_status st = validate(p);
+  if (st != PA_OK) return st;
+  if (p->kv_dtype == PA_I8 && !use_balanced(p))
+    return pa::fail(PA_ERR_UNSUPPORTED,
+                    "pa_decode: an INT8 cache needs the balanced split (<= 1024 sequences, <= 32768 "
+                    "(sequence, KV head) pairs)");
   return PA_OK;
 }
 
@@ -1402,18 +1589,28 @@ bool use_mfma(const pa_decode_params *p) {
 // KV head where a device answers).
 size_t park_bytes(int G, int D) { return (size_t)kBWaves * park_floats(G, D) * sizeof(float); }
 
-int balanced_workgroups(pa_dtype dt, int D, int G) {
-  static int cached[64][4][kGMax + 1] = {};
+// The balanced kernel for a cache type, q type and head size.
+template <class W, int D>
+const void *kfn() { return reinterpret_cast<const void *>(&pa_balanced_kernel<W, D>); }
+
+const void *balanced_kernel(pa_dtype kv, pa_dtype qt, int D) {
+  if (kv == PA_I8) {
+    if (qt == PA_BF16) return D == 128 ? kfn<MfmaWaveI8<PA_BF16, 128>, 128>() : kfn<MfmaWaveI8<PA_BF16, 64>, 64>();
+    return D == 128 ? kfn<MfmaWaveI8<PA_F16, 128>, 128>() : kfn<MfmaWaveI8<PA_F16, 64>, 64>();
+  }
+  if (kv == PA_BF16) return D == 128 ? kfn<MfmaWave<PA_BF16, 128>, 128>() : kfn<MfmaWave<PA_BF16, 64>, 64>();
+  return D == 128 ? kfn<MfmaWave<PA_F16, 128>, 128>() : kfn<MfmaWave<PA_F16, 64>, 64>();
+}
+
+int balanced_workgroups(pa_dtype kv, pa_dtype qt, int D, int G) {
+  static int cached[64][8][kGMax + 1] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PA_BALANCED_WG_PER_CU * cu_count();
-  const int k = (dt == PA_BF16 ? 0 : 2) + (D == 128 ? 0 : 1);
+  const int k = (kv == PA_I8 ? 4 : 0) + ((kv == PA_I8 ? qt : kv) == PA_BF16 ? 0 : 2) + (D == 128 ? 0 : 1);
   if (!cached[dev][k][G]) {
-    const void *fn = k == 0   ? reinterpret_cast<const void *>(&pa_balanced_kernel<PA_BF16, 128>)
-                     : k == 1 ? reinterpret_cast<const void *>(&pa_balanced_kernel<PA_BF16, 64>)
-                     : k == 2 ? reinterpret_cast<const void *>(&pa_balanced_kernel<PA_F16, 128>)
-                              : reinterpret_cast<const void *>(&pa_balanced_kernel<PA_F16, 64>);
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBThreads, park_bytes(G, D)) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, balanced_kernel(kv, qt, D), kBThreads,
+                                                     park_bytes(G, D)) != hipSuccess ||
         per_cu <= 0)
       per_cu = PA_BALANCED_WG_PER_CU;
     cached[dev][k][G] = std::min(per_cu, PA_BALANCED_WG_PER_CU) * cu_count();
@@ -1422,7 +1619,7 @@ int balanced_workgroups(pa_dtype dt, int D, int G) {
 }
 
 int balanced_workgroups(const pa_decode_params *p) {
-  return balanced_workgroups(p->kv_dtype, p->head_dim, p->num_q_heads / p->num_kv_heads);
+  return balanced_workgroups(p->kv_dtype, p->q_dtype, p->head_dim, p->num_q_heads / p->num_kv_heads);
 }
 
 // Automatic partitioning on the matrix-core path uses the balanced split
@@ -1495,14 +1692,14 @@ void launch_partition(pa_dtype dt, bool mfma, int G, dim3 grid, hipStream_t st, 
 extern "C" {
 
 int32_t pa_decode_partition_tokens(const pa_decode_params *p) {
-  pa_status st = validate(p);
+  pa_status st = validate_all(p);
   if (st != PA_OK) return -(int32_t)st;
   if (use_balanced(p)) return 0;
   return resolve_partition(p);
 }
 
 size_t pa_decode_workspace_bytes(const pa_decode_params *p) {
-  if (validate(p) != PA_OK) return 0;
+  if (validate_all(p) != PA_OK) return 0;
   if (use_balanced(p)) return balanced_bytes(p, nullptr, nullptr);
   const int32_t pt = resolve_partition(p);
   const int32_t np = num_partitions(p, pt);
@@ -1517,7 +1714,7 @@ namespace {
 // Validates, checks the workspace and fills the kernel arguments.
 pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
                   const char *who, DecodeArgs &a) {
-  pa_status st = validate(p);
+  pa_status st = validate_all(p);
   if (st != PA_OK) return st;
   const bool bal = use_balanced(p);
   const int32_t pt = bal ? 0 : resolve_partition(p);
@@ -1534,6 +1731,8 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
   a.v_cache = static_cast<const uint8_t *>(p->v_cache);
   a.block_tables = p->block_tables;
   a.context_lens = p->context_lens;
+  a.k_scales = p->kv_dtype == PA_I8 ? p->k_scales : nullptr;
+  a.v_scales = p->kv_dtype == PA_I8 ? p->v_scales : nullptr;
   a.k_new = static_cast<const uint8_t *>(p->k_new);
   a.v_new = static_cast<const uint8_t *>(p->v_new);
   a.slot_mapping = p->slot_mapping;
@@ -1570,14 +1769,10 @@ pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipS
   if (use_balanced(p)) {
     const dim3 grid((unsigned)(a.num_workers / kBWaves));
     const size_t lds = park_bytes(a.group, p->head_dim);
-    if (p->kv_dtype == PA_BF16 && p->head_dim == 128)
-      hipLaunchKernelGGL((pa_balanced_kernel<PA_BF16, 128>), grid, dim3(kBThreads), lds, hs, a);
-    else if (p->kv_dtype == PA_BF16)
-      hipLaunchKernelGGL((pa_balanced_kernel<PA_BF16, 64>), grid, dim3(kBThreads), lds, hs, a);
-    else if (p->head_dim == 128)
-      hipLaunchKernelGGL((pa_balanced_kernel<PA_F16, 128>), grid, dim3(kBThreads), lds, hs, a);
-    else
-      hipLaunchKernelGGL((pa_balanced_kernel<PA_F16, 64>), grid, dim3(kBThreads), lds, hs, a);
+    void *args[] = {const_cast<DecodeArgs *>(&a)};
+    hipError_t e = hipLaunchKernel(balanced_kernel(p->kv_dtype, p->q_dtype, p->head_dim), grid,
+                                   dim3(kBThreads), args, lds, hs);
+    if (e != hipSuccess) return hip_check(e, "pa_decode balanced launch");
     return hip_check(hipGetLastError(), "pa_decode balanced launch");
   }
   const dim3 grid((unsigned)((int64_t)a.max_parts * p->num_kv_heads * p->num_seqs));
@@ -1668,6 +1863,62 @@ pa_status pa_reshape_and_cache(const void *k_new, const void *v_new, void *k_cac
   else
     hipLaunchKernelGGL((pa_reshape_and_cache_kernel<2, 64>), grid, dim3(256), 0, hs, kn, vn, kc, vc, slot_mapping, num_tokens, num_kv_heads, nslots);
   return hip_check(hipGetLastError(), "pa_reshape_and_cache launch");
+}
+
+pa_status pa_reshape_and_cache_int8(const void *k_new, const void *v_new, int8_t *k_cache, int8_t *v_cache,
+                                    float *k_scales, float *v_scales, const int64_t *slot_mapping,
+                                    int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t num_blocks, pa_dtype src_dtype, void *stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_reshape_and_cache_int8: bad sizes");
+  if (head_dim != 64 && head_dim != 128)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache_int8: head_dim must be 64 or 128");
+  if (src_dtype != PA_F16 && src_dtype != PA_BF16)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache_int8: rows must be F16 or BF16");
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !k_scales || !v_scales || !slot_mapping)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_reshape_and_cache_int8: NULL device pointer");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(k_scales) || !aligned16(v_scales) || !aligned16(slot_mapping))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_reshape_and_cache_int8: device pointers must be 16-byte aligned");
+  const int64_t rows = (int64_t)num_tokens * num_kv_heads;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const auto *kn = static_cast<const uint16_t *>(k_new);
+  const auto *vn = static_cast<const uint16_t *>(v_new);
+  const int64_t nslots = (int64_t)num_blocks * kBS;
+  if (src_dtype == PA_BF16 && head_dim == 128)
+    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_BF16, 128>), grid, dim3(256), 0, hs, kn, vn, k_cache, v_cache, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
+  else if (src_dtype == PA_BF16)
+    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_BF16, 64>), grid, dim3(256), 0, hs, kn, vn, k_cache, v_cache, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_F16, 128>), grid, dim3(256), 0, hs, kn, vn, k_cache, v_cache, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
+  else
+    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_F16, 64>), grid, dim3(256), 0, hs, kn, vn, k_cache, v_cache, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
+  return hip_check(hipGetLastError(), "pa_reshape_and_cache_int8 launch");
+}
+
+pa_status pa_copy_blocks_int8(int8_t *k_cache, int8_t *v_cache, float *k_scales, float *v_scales,
+                              const int32_t *src_dst_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t num_blocks, void *stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_copy_blocks_int8: bad sizes");
+  if (head_dim != 64 && head_dim != 128)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks_int8: head_dim must be 64 or 128");
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !k_scales || !v_scales || !src_dst_pairs)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_copy_blocks_int8: NULL device pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_scales) || !aligned16(v_scales))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_copy_blocks_int8: caches must be 16-byte aligned");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // codes, then scales: each a [num_blocks] array of equal-size blocks
+  hipLaunchKernelGGL(pa_copy_blocks_kernel, dim3(num_pairs), dim3(256), 0, hs, reinterpret_cast<uint8_t *>(k_cache),
+                     reinterpret_cast<uint8_t *>(v_cache), src_dst_pairs, (int64_t)num_kv_heads * kBS * head_dim,
+                     num_blocks);
+  hipLaunchKernelGGL(pa_copy_blocks_kernel, dim3(num_pairs), dim3(256), 0, hs, reinterpret_cast<uint8_t *>(k_scales),
+                     reinterpret_cast<uint8_t *>(v_scales), src_dst_pairs,
+                     (int64_t)num_kv_heads * kBS * (int64_t)sizeof(float), num_blocks);
+  return hip_check(hipGetLastError(), "pa_copy_blocks_int8 launch");
 }
 
 pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst_pairs, int32_t num_pairs,

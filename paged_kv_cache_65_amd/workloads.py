@@ -52,6 +52,8 @@ class Spec:
     decode_steps: int = 0                # tokens appended per sequence after the prompt
     partition_tokens: int = 0            # 0 = library default
     scale: Optional[float] = None        # None = 1/sqrt(head_dim) rounded to fp32
+    cache: str = ""                      # cache type when it differs from dtype: "i8"
+                                         # (int8 codes + per-row scales; q, rows, out in dtype)
 
     @property
     def group(self) -> int:
@@ -63,7 +65,7 @@ class Spec:
 
 
 def named(n: int) -> Spec:
-    """The five measured workloads (1-based)."""
+    """The measured workloads (1-based; 6 is workload 3 over an INT8 cache)."""
     if n == 1:
         return Spec("tiny-fp32-mha-d64", 1, "f32", "f32", 4, 4, 4, 64, 64,
                     lens=[1, 17, 33, 100], scale=1.0 / 8.0)
@@ -79,6 +81,9 @@ def named(n: int) -> Spec:
     if n == 5:
         return Spec("long-ctx-gqa4-bf16-b4-l32768-128steps", 5, "bf16", "bf16", 4, 32, 8, 128,
                     8192 + 64, lens=[32768] * 4, decode_steps=128, partition_tokens=512)
+    if n == 6:  # workload 3 with an INT8 cache (rows quantized on append)
+        return Spec("llama70b-gqa8-int8kv-b64-l128to4096", 3, "bf16", "bf16", 64, 64, 8, 128,
+                    20000, len_range=(128, 4096), cache="i8")
     raise ValueError(f"no workload {n}")
 
 
@@ -169,11 +174,12 @@ def generate(spec: Spec) -> Workload:
 
 def custom(name="custom", seed=0, dtype="bf16", out_dtype=None, lens=(1, 17), num_q_heads=8,
            num_kv_heads=2, head_dim=128, num_blocks=0, prefix_len=0, decode_steps=0,
-           partition_tokens=0, scale=None) -> Spec:
+           partition_tokens=0, scale=None, cache="") -> Spec:
     """A small spec for parity sweeps; num_blocks=0 sizes the pool to fit plus slack."""
     if num_blocks == 0:
         need = sum(-(-(l + decode_steps) // BLOCK_SIZE) + 1 for l in lens)
         num_blocks = prefix_len // BLOCK_SIZE + need + 16
     return Spec(name, seed, dtype, out_dtype or dtype, len(lens), num_q_heads, num_kv_heads,
                 head_dim, num_blocks, lens=list(lens), prefix_len=prefix_len,
-                decode_steps=decode_steps, partition_tokens=partition_tokens, scale=scale)
+                decode_steps=decode_steps, partition_tokens=partition_tokens, scale=scale,
+                cache=cache)

@@ -49,25 +49,47 @@ class GpuState:
     prefix_slots: list
     step_slots: list
     cow_log: list
+    k_scales: torch.Tensor = None   # int8 caches: per-row scales
+    v_scales: torch.Tensor = None
 
 
 def _append_rows(st, k_rows, v_rows, slots, spec, cow_pairs):
     dev = st.k_cache.device
+    i8 = spec.cache == "i8"
     if len(cow_pairs):
         pairs = torch.from_numpy(np.ascontiguousarray(cow_pairs, dtype=np.int32)).to(dev)
-        pa.pa_copy_blocks(st.k_cache, st.v_cache, pairs, spec.num_kv_heads, spec.head_dim)
+        if i8:
+            pa.pa_copy_blocks_int8(st.k_cache, st.v_cache, st.k_scales, st.v_scales, pairs,
+                                   spec.num_kv_heads, spec.head_dim)
+        else:
+            pa.pa_copy_blocks(st.k_cache, st.v_cache, pairs, spec.num_kv_heads, spec.head_dim)
     if len(slots):
         s = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).to(dev)
-        pa.pa_reshape_and_cache(to_device(k_rows, spec.dtype, dev), to_device(v_rows, spec.dtype, dev),
-                                st.k_cache, st.v_cache, s)
+        kd, vd = to_device(k_rows, spec.dtype, dev), to_device(v_rows, spec.dtype, dev)
+        if i8:
+            pa.pa_reshape_and_cache_int8(kd, vd, st.k_cache, st.v_cache, st.k_scales, st.v_scales, s)
+        else:
+            pa.pa_reshape_and_cache(kd, vd, st.k_cache, st.v_cache, s)
+
+
+def i8_cache(num_blocks, num_kv_heads, head_dim, device="cuda"):
+    """(codes, scales) of an unwritten int8 pool: codes 0x7F, scales NaN."""
+    codes = torch.full((num_blocks * num_kv_heads * BS * head_dim,), 127, dtype=torch.int8, device=device)
+    scales = torch.full((num_blocks * num_kv_heads * BS,), float("nan"), dtype=torch.float32, device=device)
+    return codes, scales
 
 
 def build(wl, steps: int = 0, device="cuda") -> GpuState:
     spec = wl.spec
     pool = pa.BlockPool(wl.num_blocks, BS, wl.free_order)
-    kc = nan_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, spec.dtype, device)
-    vc = nan_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, spec.dtype, device)
-    st = GpuState(pool, [], -1, kc, vc, [], [], [], [])
+    if spec.cache == "i8":
+        kc, ks = i8_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, device)
+        vc, vs = i8_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, device)
+    else:
+        kc = nan_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, spec.dtype, device)
+        vc = nan_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, spec.dtype, device)
+        ks = vs = None
+    st = GpuState(pool, [], -1, kc, vc, [], [], [], [], ks, vs)
     if spec.prefix_len:
         st.owner = pool.seq_create()
         slots, cow = pool.seq_append(st.owner, spec.prefix_len)
@@ -113,5 +135,6 @@ def decode(wl, st: GpuState, max_blocks: int, out_dtype=None, kernel="auto", par
     pt = spec.partition_tokens if partition_tokens is None else partition_tokens
     max_ctx = int(lens_h.max()) if len(lens_h) else 0
     pa.pa_decode(out, qd, st.k_cache, st.v_cache, tab_d, lens_d, spec.num_kv_heads, max_ctx,
-                 spec.fp32_scale(), partition_tokens=pt, kernel=kernel)
+                 spec.fp32_scale(), partition_tokens=pt, kernel=kernel, k_scales=st.k_scales,
+                 v_scales=st.v_scales)
     return out

@@ -30,6 +30,8 @@ class OracleState:
     prefix_slots: list
     step_slots: list            # per step, slots in sequence order
     cow_log: list               # (phase, src, dst)
+    k_scales: np.ndarray = None  # int8 caches: per-row scales
+    v_scales: np.ndarray = None
 
 
 def max_blocks_for(wl, steps=None) -> int:
@@ -41,8 +43,26 @@ def build(wl, steps: int = 0) -> OracleState:
     spec = wl.spec
     Hkv, D, dt = spec.num_kv_heads, spec.head_dim, spec.dtype
     pool = PoolModel(wl.num_blocks, BS, wl.free_order)
-    kc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
-    vc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
+    i8 = spec.cache == "i8"
+    if i8:
+        kc, ks = oracle.empty_cache_i8(wl.num_blocks, Hkv, D)
+        vc, vs = oracle.empty_cache_i8(wl.num_blocks, Hkv, D)
+    else:
+        kc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
+        vc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
+        ks = vs = None
+
+    def put(k, v, slots):
+        if i8:
+            oracle.reshape_and_cache_i8(k, v, kc, vc, ks, vs, slots, Hkv, D, wl.num_blocks, dt)
+        else:
+            oracle.reshape_and_cache(k, v, kc, vc, slots, Hkv, D, wl.num_blocks, dt)
+
+    def copy(pairs):
+        if i8:
+            oracle.copy_blocks_i8(kc, vc, ks, vs, pairs, Hkv, D)
+        else:
+            oracle.copy_blocks(kc, vc, pairs, Hkv, D, dt)
     cow_log = []
     owner = -1
     prefix_slots = []
@@ -50,8 +70,7 @@ def build(wl, steps: int = 0) -> OracleState:
         owner = pool.seq_create()
         prefix_slots, cow = pool.seq_append(owner, spec.prefix_len)
         assert cow is None
-        oracle.reshape_and_cache(wl.prefix_k, wl.prefix_v, kc, vc, prefix_slots, Hkv, D,
-                                 wl.num_blocks, dt)
+        put(wl.prefix_k, wl.prefix_v, prefix_slots)
     seq_ids, prompt_slots = [], []
     for s in range(spec.num_seqs):
         sid = pool.seq_fork(owner) if spec.prefix_len else pool.seq_create()
@@ -59,12 +78,11 @@ def build(wl, steps: int = 0) -> OracleState:
         lo, hi = wl.token_offsets[s], wl.token_offsets[s + 1]
         slots, cow = pool.seq_append(sid, int(hi - lo))
         if cow is not None:
-            oracle.copy_blocks(kc, vc, np.array([cow]), Hkv, D, dt)
+            copy(np.array([cow]))
             cow_log.append(("prompt", *cow))
-        oracle.reshape_and_cache(wl.k_tokens[lo:hi], wl.v_tokens[lo:hi], kc, vc, slots, Hkv, D,
-                                 wl.num_blocks, dt)
+        put(wl.k_tokens[lo:hi], wl.v_tokens[lo:hi], slots)
         prompt_slots.append(slots)
-    st = OracleState(pool, seq_ids, owner, kc, vc, prompt_slots, prefix_slots, [], cow_log)
+    st = OracleState(pool, seq_ids, owner, kc, vc, prompt_slots, prefix_slots, [], cow_log, ks, vs)
     for step in range(steps):
         advance(wl, st, step)
     return st
@@ -73,12 +91,22 @@ def build(wl, steps: int = 0) -> OracleState:
 def advance(wl, st: OracleState, step: int):
     spec = wl.spec
     slots, cows = st.pool.seq_append_batch(st.seq_ids)
+    i8 = spec.cache == "i8"
     if cows:
-        oracle.copy_blocks(st.k_cache, st.v_cache, np.array(cows), spec.num_kv_heads,
-                           spec.head_dim, spec.dtype)
+        if i8:
+            oracle.copy_blocks_i8(st.k_cache, st.v_cache, st.k_scales, st.v_scales, np.array(cows),
+                                  spec.num_kv_heads, spec.head_dim)
+        else:
+            oracle.copy_blocks(st.k_cache, st.v_cache, np.array(cows), spec.num_kv_heads,
+                               spec.head_dim, spec.dtype)
         st.cow_log.extend(("step", *c) for c in cows)
-    oracle.reshape_and_cache(wl.step_k[step], wl.step_v[step], st.k_cache, st.v_cache, slots,
-                             spec.num_kv_heads, spec.head_dim, wl.num_blocks, spec.dtype)
+    if i8:
+        oracle.reshape_and_cache_i8(wl.step_k[step], wl.step_v[step], st.k_cache, st.v_cache,
+                                    st.k_scales, st.v_scales, slots, spec.num_kv_heads,
+                                    spec.head_dim, wl.num_blocks, spec.dtype)
+    else:
+        oracle.reshape_and_cache(wl.step_k[step], wl.step_v[step], st.k_cache, st.v_cache, slots,
+                                 spec.num_kv_heads, spec.head_dim, wl.num_blocks, spec.dtype)
     st.step_slots.append(slots)
 
 
@@ -93,5 +121,8 @@ def decode(wl, st: OracleState, max_blocks: int, nthreads: int = 0, seq_subset=N
     q = wl.q
     if seq_subset is not None:
         tab, lens, q = tab[seq_subset], lens[seq_subset], np.ascontiguousarray(q[seq_subset])
+    if spec.cache == "i8":
+        return oracle.decode_i8(q, spec.dtype, st.k_cache, st.v_cache, st.k_scales, st.v_scales,
+                                tab, lens, spec.num_kv_heads, spec.fp32_scale(), nthreads=nthreads)
     return oracle.decode(q, st.k_cache, st.v_cache, tab, lens, spec.num_kv_heads,
                          spec.fp32_scale(), spec.dtype, nthreads=nthreads)

@@ -136,3 +136,43 @@ def test_append_and_copy_reject_bad_sizes():
         == pa.PA_OK
     assert L.pa_copy_blocks(None, None, None, -1, 8, 128, 10, pa.PA_BF16, None) == pa.PA_ERR_INVALID_ARG
     assert L.pa_copy_blocks(None, None, None, 0, 8, 128, 10, pa.PA_BF16, None) == pa.PA_OK
+
+
+def _i8(**over):
+    base = dict(kv_dtype=pa.PA_I8, q_dtype=pa.PA_BF16, out_dtype=pa.PA_F32,
+                k_scales=ctypes.c_void_p(112), v_scales=ctypes.c_void_p(128))
+    base.update(over)
+    return _params(**base)
+
+
+def test_int8_cache_takes_the_balanced_split():
+    assert pa.pa_decode_partition_tokens(_i8()) == 0
+    assert pa.pa_decode_partition_tokens(_i8(out_dtype=pa.PA_BF16)) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q_dtype=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),
+    (dict(out_dtype=pa.PA_F16), pa.PA_ERR_UNSUPPORTED),
+    (dict(k_scales=None), pa.PA_ERR_INVALID_ARG),
+    (dict(v_scales=ctypes.c_void_p(129)), pa.PA_ERR_INVALID_ARG),
+    (dict(partition_tokens=256), pa.PA_ERR_UNSUPPORTED),
+    (dict(kernel=pa.PA_KERNEL_VALU), pa.PA_ERR_UNSUPPORTED),
+    (dict(num_seqs=1025), pa.PA_ERR_UNSUPPORTED),
+    (dict(k_new=ctypes.c_void_p(16), v_new=ctypes.c_void_p(16), slot_mapping=ctypes.c_void_p(16)),
+     pa.PA_ERR_UNSUPPORTED),
+])
+def test_int8_decode_rejects_unsupported_requests(over, status):
+    p = _i8(**over)
+    assert pa.lib().pa_decode(ctypes.byref(p), None, 0, None) == status
+    assert pa.pa_decode_workspace_bytes(p) == 0
+
+
+def test_int8_append_and_copy_reject_bad_arguments():
+    L = pa.lib()
+    args = (None, None, None, None, None, None, None)
+    assert L.pa_reshape_and_cache_int8(*args, 4, 8, 128, 10, pa.PA_F32, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_reshape_and_cache_int8(*args, 4, 8, 96, 10, pa.PA_BF16, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_reshape_and_cache_int8(*args, 4, 8, 128, 10, pa.PA_BF16, None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_reshape_and_cache_int8(*args, 0, 8, 128, 10, pa.PA_BF16, None) == pa.PA_OK
+    assert L.pa_copy_blocks_int8(None, None, None, None, None, 0, 8, 128, 10, None) == pa.PA_OK
+    assert L.pa_copy_blocks_int8(None, None, None, None, None, 2, 8, 128, 10, None) == pa.PA_ERR_INVALID_ARG
