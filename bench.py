@@ -54,10 +54,10 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs, or
-    None when the kernel source changed since they were taken."""
-    path = os.path.join(PROFILES, f"traffic_{kernel}_llama70b_gqa8.txt")
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from committed rocprofv3
+    counter runs, or None when the kernel source changed since they were taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -174,16 +174,26 @@ def build_replica(pa, torch, wl, order, k_rows_d, v_rows_d, MB, S, dev):
         slots_all.append(s_)
     slots = torch.from_numpy(np.concatenate(slots_all)).to(dev)
     n_elems = wl.num_blocks * spec.num_kv_heads * 16 * spec.head_dim
-    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[spec.dtype]
-    kc = torch.full((n_elems,), float("nan"), dtype=dt, device=dev)
-    vc = torch.full((n_elems,), float("nan"), dtype=dt, device=dev)
-    pa.pa_reshape_and_cache(k_rows_d, v_rows_d, kc, vc, slots)
+    ks = vs = None
+    if spec.cache == "i8":
+        kc = torch.full((n_elems,), 127, dtype=torch.int8, device=dev)
+        vc = torch.full((n_elems,), 127, dtype=torch.int8, device=dev)
+        ks = torch.full((n_elems // spec.head_dim,), float("nan"), dtype=torch.float32, device=dev)
+        vs = torch.full((n_elems // spec.head_dim,), float("nan"), dtype=torch.float32, device=dev)
+        pa.pa_reshape_and_cache_int8(k_rows_d, v_rows_d, kc, vc, ks, vs, slots)
+    else:
+        dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[spec.dtype]
+        kc = torch.full((n_elems,), float("nan"), dtype=dt, device=dev)
+        vc = torch.full((n_elems,), float("nan"), dtype=dt, device=dev)
+        pa.pa_reshape_and_cache(k_rows_d, v_rows_d, kc, vc, slots)
     ids = np.array(ids, dtype=np.int32)
     words = stage_layout(S, MB)["words"]
     stage = torch.empty(words, dtype=torch.int32, pin_memory=True)
     desc = torch.empty(words, dtype=torch.int32, device=dev)
     tab, lens = pool.seq_export(ids, MB)
-    return Replica(pool, ids, kc, vc, stage, desc, None, None, int(lens.max()), None, lens.copy())
+    rep = Replica(pool, ids, kc, vc, stage, desc, None, None, int(lens.max()), None, lens.copy())
+    rep.k_scales, rep.v_scales = ks, vs
+    return rep
 
 
 def run_gpu(args, wl):
@@ -224,11 +234,12 @@ def run_gpu(args, wl):
         rep.out = torch.empty((S, Hq, D), dtype=out_dt, device=dev)
         rep.params = pa.make_decode_params(rep.out, q_d, rep.k_cache, rep.v_cache, tab_v, lens_v,
                                            Hkv, rep.max_ctx + W + K, spec.fp32_scale(),
-                                           args.partition_tokens, args.kernel)
+                                           args.partition_tokens, args.kernel,
+                                           k_scales=rep.k_scales, v_scales=rep.v_scales)
         ws_need = max(ws_need, pa.pa_decode_workspace_bytes(rep.params))
         rep.params.max_context_len = rep.max_ctx
         rep.slots_v = slots_v
-        if args.append == "fused":
+        if args.append == "fused" and spec.cache != "i8":
             rep.params.k_new = step_k_d.data_ptr()
             rep.params.v_new = step_v_d.data_ptr()
             rep.params.slot_mapping = slots_v.data_ptr()
@@ -273,12 +284,15 @@ def run_gpu(args, wl):
             cow=ctypes.cast(base + 4 * lay["cows"], ctypes.POINTER(ctypes.c_int32)),
             stage=ctypes.c_void_p(base), desc=ctypes.c_void_p(rep.desc.data_ptr()),
             kc=ctypes.c_void_p(rep.k_cache.data_ptr()), vc=ctypes.c_void_p(rep.v_cache.data_ptr()),
+            ks=ctypes.c_void_p(rep.k_scales.data_ptr()) if rep.k_scales is not None else None,
+            vs=ctypes.c_void_p(rep.v_scales.data_ptr()) if rep.v_scales is not None else None,
             slots_d=ctypes.c_void_p(rep.slots_v.data_ptr()),
             cows_d=ctypes.c_void_p(rep.desc.data_ptr() + 4 * lay["cows"]),
             lens_np=np.ctypeslib.as_array(ctypes.cast(base + 4 * lay["lens"], ctypes.POINTER(ctypes.c_int32)),
                                           shape=(S,))))
     pool_h = [rep.pool._h for rep in reps]
-    fused = args.append == "fused"
+    i8 = spec.cache == "i8"
+    fused = args.append == "fused" and not i8   # an INT8 cache appends with its own kernel
     k0, v0 = step_k_d.data_ptr(), step_v_d.data_ptr()
     torch.cuda.synchronize()
 
@@ -309,11 +323,20 @@ def run_gpu(args, wl):
         hip.sync_event(rep.copied)
         waited[0] += time.perf_counter() - w0
         if ncow[r]:
-            pa._check(L.pa_copy_blocks(pp["kc"], pp["vc"], pp["cows_d"], ncow[r], Hkv, D,
-                                       nb_rep, dt_code, cs))
+            if i8:
+                pa._check(L.pa_copy_blocks_int8(pp["kc"], pp["vc"], pp["ks"], pp["vs"], pp["cows_d"],
+                                                ncow[r], Hkv, D, nb_rep, cs))
+            else:
+                pa._check(L.pa_copy_blocks(pp["kc"], pp["vc"], pp["cows_d"], ncow[r], Hkv, D,
+                                           nb_rep, dt_code, cs))
         if fused:
             rep.params.k_new = k0 + i * row_bytes
             rep.params.v_new = v0 + i * row_bytes
+        elif i8:
+            pa._check(L.pa_reshape_and_cache_int8(ctypes.c_void_p(k0 + i * row_bytes),
+                                                  ctypes.c_void_p(v0 + i * row_bytes), pp["kc"], pp["vc"],
+                                                  pp["ks"], pp["vs"], pp["slots_d"], S, Hkv, D, nb_rep,
+                                                  dt_code, cs))
         else:
             pa._check(L.pa_reshape_and_cache(ctypes.c_void_p(k0 + i * row_bytes),
                                              ctypes.c_void_p(v0 + i * row_bytes), pp["kc"], pp["vc"],
@@ -350,13 +373,13 @@ def run_gpu(args, wl):
         f"{waited[0] / K * 1e6:.1f} us blocked on the device")
     elapsed = t1 - t0
     part_ms = np.array([hip.elapsed_ms(ev_a[k], ev_b[k]) for k in range(K)])
-    alg_bytes = [accounting.decode_algorithmic_bytes(l, Hq, Hkv, D, spec.dtype, spec.out_dtype,
+    alg_bytes = [accounting.decode_algorithmic_bytes(l, Hq, Hkv, D, spec.dtype, spec.out_dtype, cache=spec.cache,
                                                      shared_tokens=spec.prefix_len) for l in lens_log]
     log(f"timed {K} steps in {elapsed * 1e3:.2f} ms; partition kernel mean {part_ms.mean() * 1e3:.1f} us")
     return {
         "elapsed": elapsed, "part_ms": part_ms, "alg": alg_bytes, "part_tokens": part_tokens,
         "max_blocks": MB, "S": S,
-        "append_bytes": accounting.append_bytes(S, Hkv, D, spec.dtype),
+        "append_bytes": accounting.append_bytes(S, Hkv, D, spec.dtype, spec.cache),
         "device": torch.cuda.get_device_name(0),
     }
 
@@ -369,29 +392,43 @@ def run_cpu_baseline(wl, seconds):
     spec = wl.spec
     Hkv, D, dt = spec.num_kv_heads, spec.head_dim, spec.dtype
     pool = PoolModel(wl.num_blocks, 16, wl.free_order)
-    kc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
-    vc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
+    i8 = spec.cache == "i8"
+    if i8:
+        kc, ks = oracle.empty_cache_i8(wl.num_blocks, Hkv, D)
+        vc, vs = oracle.empty_cache_i8(wl.num_blocks, Hkv, D)
+    else:
+        kc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
+        vc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
+
+    def put(k, v, sl):
+        if i8:
+            oracle.reshape_and_cache_i8(k, v, kc, vc, ks, vs, sl, Hkv, D, wl.num_blocks, dt)
+        else:
+            oracle.reshape_and_cache(k, v, kc, vc, sl, Hkv, D, wl.num_blocks, dt)
     owner = -1
     if spec.prefix_len:
         owner = pool.seq_create()
         sl, _ = pool.seq_append(owner, spec.prefix_len)
-        oracle.reshape_and_cache(wl.prefix_k, wl.prefix_v, kc, vc, sl, Hkv, D, wl.num_blocks, dt)
+        put(wl.prefix_k, wl.prefix_v, sl)
     ids = []
     for s in range(spec.num_seqs):
         sid = pool.seq_fork(owner) if spec.prefix_len else pool.seq_create()
         ids.append(sid)
         lo, hi = wl.token_offsets[s], wl.token_offsets[s + 1]
         sl, _ = pool.seq_append(sid, int(hi - lo))
-        oracle.reshape_and_cache(wl.k_tokens[lo:hi], wl.v_tokens[lo:hi], kc, vc, sl, Hkv, D,
-                                 wl.num_blocks, dt)
+        put(wl.k_tokens[lo:hi], wl.v_tokens[lo:hi], sl)
     mb = int(-(-int(wl.prompt_lens.max()) // 16))
     tab, lens = pool.export(ids, mb)
     tab, lens = np.array(tab, np.int32), np.array(lens, np.int32)
     passes, used = 0, 0
     t0 = time.perf_counter()
     while True:
-        _, used = oracle.decode(wl.q, kc, vc, tab, lens, Hkv, spec.fp32_scale(), dt,
-                                nthreads=0, return_threads=True)
+        if i8:
+            _, used = oracle.decode_i8(wl.q, dt, kc, vc, ks, vs, tab, lens, Hkv, spec.fp32_scale(),
+                                       nthreads=0, return_threads=True)
+        else:
+            _, used = oracle.decode(wl.q, kc, vc, tab, lens, Hkv, spec.fp32_scale(), dt,
+                                    nthreads=0, return_threads=True)
         passes += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -423,7 +460,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
@@ -453,14 +490,15 @@ def main():
     K = args.steps
     tok_s = spec.num_seqs * K / g["elapsed"]
     mean_alg = float(np.mean([a["total"] for a in g["alg"]]))
-    mean_kv_tokens = float(np.mean([a["kv_logical"] for a in g["alg"]])) / (
-        2 * spec.num_kv_heads * spec.head_dim * accounting.ELEM_BYTES[spec.dtype])
+    row_bytes = (spec.head_dim + accounting.I8_SCALE_BYTES) if spec.cache == "i8" else \
+        spec.head_dim * accounting.ELEM_BYTES[spec.dtype]
+    mean_kv_tokens = float(np.mean([a["kv_logical"] for a in g["alg"]])) / (2 * spec.num_kv_heads * row_bytes)
     part_s = float(g["part_ms"].mean()) / 1e3
     achieved = mean_alg / part_s / 1e9
     step_bytes = mean_alg + g["append_bytes"]
     step_gbps = step_bytes * K / g["elapsed"] / 1e9
     kernel_name = "pa_balanced_kernel" if g["part_tokens"] == 0 else "pa_partition_kernel"
-    traffic = read_traffic(kernel_name)
+    traffic = read_traffic(kernel_name, spec.name)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle")
@@ -484,12 +522,15 @@ def main():
         "config": {
             "workload": spec.name, "num_seqs": spec.num_seqs, "num_q_heads": spec.num_q_heads,
             "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim, "block_size": 16,
-            "kv_dtype": spec.dtype, "pool_blocks": int(wl.num_blocks),
+            "kv_dtype": "int8 + f32 row scales" if spec.cache == "i8" else spec.dtype,
+            "pool_blocks": int(wl.num_blocks),
             "mean_context": round(mean_kv_tokens / spec.num_seqs, 1),
             "partition_tokens": g["part_tokens"], "replicas": args.replicas,
             "kernel": args.kernel, "seed": spec.seed,
             "step": ("pool append + H2D slots/tables/lens + decode partitions (fused K/V append) + merge"
-                     if args.append == "fused" else
+                     if args.append == "fused" and spec.cache != "i8" else
+                     "pool append + H2D slots/tables/lens + reshape_and_cache_int8 + decode partitions + merge"
+                     if spec.cache == "i8" else
                      "pool append + H2D slots/tables/lens + reshape_and_cache + decode partitions + merge"),
             "device": g["device"],
         },

@@ -19,6 +19,8 @@ import numpy as np
 
 BLOCK_SIZE = 16
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+# An INT8 cache row is head_dim one-byte codes plus one float32 scale.
+I8_SCALE_BYTES = 4
 
 
 def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
@@ -26,16 +28,21 @@ def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, elem_b
 
 
 def decode_algorithmic_bytes(context_lens, num_q_heads, num_kv_heads, head_dim, dtype,
-                             out_dtype, shared_tokens: int = 0) -> dict:
+                             out_dtype, shared_tokens: int = 0, cache: str = "") -> dict:
     """Bytes one paged decode launch must move.
 
     shared_tokens: tokens of a prefix whose blocks every sequence maps (counted
     once in 'kv_unique' and once per sequence in 'kv_logical').
+    cache: "i8" for an INT8 cache (codes + per-row scales); q and out stay in
+    dtype / out_dtype.
     """
     lens = np.asarray(context_lens, dtype=np.int64)
     eb = ELEM_BYTES[dtype]
     S = len(lens)
-    per_tok = kv_bytes_per_token(1, num_kv_heads, head_dim, eb)
+    if cache == "i8":
+        per_tok = 2 * num_kv_heads * (head_dim + I8_SCALE_BYTES)
+    else:
+        per_tok = kv_bytes_per_token(1, num_kv_heads, head_dim, eb)
     kv_logical = int(lens.sum()) * per_tok
     kv_unique = kv_logical - max(S - 1, 0) * shared_tokens * per_tok if shared_tokens else kv_logical
     q = S * num_q_heads * head_dim * eb
@@ -53,7 +60,8 @@ def decode_flops(context_lens, num_q_heads, head_dim) -> int:
     return 4 * head_dim * num_q_heads * int(np.asarray(context_lens, dtype=np.int64).sum())
 
 
-def append_bytes(num_tokens, num_kv_heads, head_dim, dtype) -> int:
+def append_bytes(num_tokens, num_kv_heads, head_dim, dtype, cache: str = "") -> int:
     """Read new K/V rows + write them into the cache + the int64 slot mapping."""
     row = 2 * num_kv_heads * head_dim * ELEM_BYTES[dtype]
-    return num_tokens * (2 * row + 8)
+    written = 2 * num_kv_heads * (head_dim + I8_SCALE_BYTES) if cache == "i8" else row
+    return num_tokens * (row + written + 8)

@@ -245,6 +245,26 @@ __device__ inline void write_token_row(uint8_t *k_cache, uint8_t *v_cache, int64
   }
 }
 
+// One 4-wave workgroup per CU (one wave per SIMD), each wave with a ring of
+// four blocks (32 KiB) in flight: fewer, longer wave shares mean fewer
+// segments, hence fewer partial stores and a cheaper merge, and 128 KiB in
+// flight per CU still saturates HBM.
+#ifndef PA_BALANCED_WG_PER_CU
+#define PA_BALANCED_WG_PER_CU 1
+#endif
+#ifndef PA_BALANCED_RING
+#define PA_BALANCED_RING 4
+#endif
+#ifndef PA_BALANCED_WAVES
+#define PA_BALANCED_WAVES 4
+#endif
+#ifndef PA_I8_RING
+#define PA_I8_RING 2
+#endif
+#ifndef PA_I8_WG_PER_CU
+#define PA_I8_WG_PER_CU 2
+#endif
+
 // ============================================================================
 // MFMA wave: fp16 / bf16 caches.
 //
@@ -321,6 +341,8 @@ struct MfmaWave {
   }
 
   static constexpr bool kAppend = true;  // supports the fused append
+  static constexpr int kBalRing = PA_BALANCED_RING;          // balanced kernel: blocks in flight per wave
+  static constexpr int kBalWgPerCu = PA_BALANCED_WG_PER_CU;  // balanced kernel: workgroups per CU
   // Tile index = block * Hkv + head.
   __device__ static void load_tile(Frag &f, const DecodeArgs &a, int64_t tile, int lane) {
     load(f, a.k_cache + tile * TILE, a.v_cache + tile * TILE, lane);
@@ -522,6 +544,10 @@ struct MfmaWaveI8 : MfmaWave<QDT, D> {
   static constexpr int NV = D / 64;        // 16-byte code vectors per lane and tile
   static constexpr int TILE = kBS * D;     // code bytes per (block, head) tile
   static constexpr bool kAppend = false;   // append with pa_reshape_and_cache_int8 first
+  // The code conversions add ~250 VALU instructions per block: more waves per
+  // SIMD hide their latency, a shallower ring keeps them in registers.
+  static constexpr int kBalRing = PA_I8_RING;
+  static constexpr int kBalWgPerCu = PA_I8_WG_PER_CU;
 
   struct Frag {
     u32x4_t k[NV];
@@ -937,19 +963,6 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
 // strictly from segment to segment: no two segments share a slot, and the
 // NW + S*Hkv - 1 slots cover every case.  The merge kernel folds the
 // partials of each pair that was split.
-// One 4-wave workgroup per CU (one wave per SIMD), each wave with a ring of
-// four blocks (32 KiB) in flight: fewer, longer wave shares mean fewer
-// segments, hence fewer partial stores and a cheaper merge, and 128 KiB in
-// flight per CU still saturates HBM.
-#ifndef PA_BALANCED_WG_PER_CU
-#define PA_BALANCED_WG_PER_CU 1
-#endif
-#ifndef PA_BALANCED_RING
-#define PA_BALANCED_RING 4
-#endif
-#ifndef PA_BALANCED_WAVES
-#define PA_BALANCED_WAVES 4
-#endif
 constexpr int kBWaves = PA_BALANCED_WAVES;  // waves per balanced workgroup
 constexpr int kBThreads = kBWaves * 64;
 constexpr int kSeqMax = 1024;    // sequences per launch on this path
@@ -1011,7 +1024,7 @@ __device__ inline int pair_of_unit(const SmemBalanced &sm, int u, int Hkv, int S
 }
 
 template <class W, int D>
-__global__ __launch_bounds__(kBThreads, PA_BALANCED_WG_PER_CU) void pa_balanced_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(DecodeArgs a) {
   __shared__ SmemBalanced sm;
   extern __shared__ __align__(16) float park_lds[];  // kBWaves x park_floats(G, D)
   const int tid = threadIdx.x, lane = tid % 64;
@@ -1086,7 +1099,7 @@ __global__ __launch_bounds__(kBThreads, PA_BALANCED_WG_PER_CU) void pa_balanced_
   if (u0 >= u1) return;
 
   W wave;
-  constexpr int NB = PA_BALANCED_RING;  // blocks held in registers per wave
+  constexpr int NB = W::kBalRing;  // blocks held in registers per wave
   typename W::Frag fr[NB];
   bool bad = false, whole = false;
   constexpr int EB = 2;
@@ -1605,15 +1618,17 @@ const void *balanced_kernel(pa_dtype kv, pa_dtype qt, int D) {
 int balanced_workgroups(pa_dtype kv, pa_dtype qt, int D, int G) {
   static int cached[64][8][kGMax + 1] = {};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PA_BALANCED_WG_PER_CU * cu_count();
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return (kv == PA_I8 ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU) * cu_count();
   const int k = (kv == PA_I8 ? 4 : 0) + ((kv == PA_I8 ? qt : kv) == PA_BF16 ? 0 : 2) + (D == 128 ? 0 : 1);
   if (!cached[dev][k][G]) {
+    const int want = kv == PA_I8 ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, balanced_kernel(kv, qt, D), kBThreads,
                                                      park_bytes(G, D)) != hipSuccess ||
         per_cu <= 0)
-      per_cu = PA_BALANCED_WG_PER_CU;
-    cached[dev][k][G] = std::min(per_cu, PA_BALANCED_WG_PER_CU) * cu_count();
+      per_cu = want;
+    cached[dev][k][G] = std::min(per_cu, want) * cu_count();
   }
   return cached[dev][k][G];
 }
