@@ -134,14 +134,18 @@ class Replica:
     seq_ids: np.ndarray
     k_cache: object
     v_cache: object
-    stage: object          # pinned int32 staging: slots(int64) | lens | tables | cows
-    desc: object           # device copy of the staging buffer
     params: object
     out: object
     max_ctx: int
-    copied: object
     lens_host: np.ndarray
-    done: object = None
+
+
+@dataclasses.dataclass
+class Slot:
+    """One step descriptor in flight: pinned host staging and its device copy."""
+    stage: object          # pinned int32 staging: slots(int64) | lens | tables | cows
+    desc: object           # device copy of the staging buffer
+    copied: object = None  # copy-stream event: desc holds this slot's step
 
 
 def stage_layout(S, MB):
@@ -157,7 +161,8 @@ def stage_layout(S, MB):
 
 def build_replica(pa, torch, wl, order, k_rows_d, v_rows_d, MB, S, dev):
     spec = wl.spec
-    pool = pa.BlockPool(wl.num_blocks, 16, order)
+    nb = len(order)
+    pool = pa.BlockPool(nb, 16, order)
     slots_all = []
     owner = -1
     if spec.prefix_len:
@@ -173,7 +178,7 @@ def build_replica(pa, torch, wl, order, k_rows_d, v_rows_d, MB, S, dev):
         assert cow is None  # prefixes are block-aligned in the named workloads
         slots_all.append(s_)
     slots = torch.from_numpy(np.concatenate(slots_all)).to(dev)
-    n_elems = wl.num_blocks * spec.num_kv_heads * 16 * spec.head_dim
+    n_elems = nb * spec.num_kv_heads * 16 * spec.head_dim
     ks = vs = None
     if spec.cache == "i8":
         kc = torch.full((n_elems,), 127, dtype=torch.int8, device=dev)
@@ -187,11 +192,8 @@ def build_replica(pa, torch, wl, order, k_rows_d, v_rows_d, MB, S, dev):
         vc = torch.full((n_elems,), float("nan"), dtype=dt, device=dev)
         pa.pa_reshape_and_cache(k_rows_d, v_rows_d, kc, vc, slots)
     ids = np.array(ids, dtype=np.int32)
-    words = stage_layout(S, MB)["words"]
-    stage = torch.empty(words, dtype=torch.int32, pin_memory=True)
-    desc = torch.empty(words, dtype=torch.int32, device=dev)
     tab, lens = pool.seq_export(ids, MB)
-    rep = Replica(pool, ids, kc, vc, stage, desc, None, None, int(lens.max()), None, lens.copy())
+    rep = Replica(pool, ids, kc, vc, None, None, int(lens.max()), lens.copy())
     rep.k_scales, rep.v_scales = ks, vs
     return rep
 
@@ -218,19 +220,36 @@ def run_gpu(args, wl):
     step_k_d, step_v_d = to_dev(wl.step_k), to_dev(wl.step_v)
     q_d = to_dev(wl.q)
     reps = []
+    # A pool sized exactly for the prompts (the 7B MHA workload) gets slack blocks
+    # for the timed decode steps, at the bottom of the free stack so the
+    # workload's own placement is used first.
+    grow = int(np.sum(-(-(wl.prompt_lens + W + K) // 16) - (-(-wl.prompt_lens // 16))))
+    slack = max(0, grow - (wl.num_blocks - int(np.sum(-(-(wl.prompt_lens - spec.prefix_len) // 16)))
+                           - spec.prefix_len // 16))
+    nb_pool = wl.num_blocks + slack
     for r in range(R):
         order = wl.free_order if r == 0 else \
             np.random.default_rng(spec.seed * 1000 + r).permutation(wl.num_blocks).astype(np.int32)
+        order = np.concatenate([np.arange(wl.num_blocks, nb_pool, dtype=np.int32), order])
         reps.append(build_replica(pa, torch, wl, order, k_rows_d, v_rows_d, MB, S, dev))
-        log(f"replica {r} built: {wl.num_blocks} blocks, max context {reps[-1].max_ctx}")
+        log(f"replica {r} built: {nb_pool} blocks, max context {reps[-1].max_ctx}")
     del k_rows_d, v_rows_d
     out_dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[spec.out_dtype]
     ws_need = 0
     lay = stage_layout(S, MB)
+    # Step descriptors travel through a ring of NS staging slots (pinned host
+    # buffer + device copy), independent of the R replicas, so the host needs a
+    # completion event only every DONE_EVERY steps.
+    NS, DONE_EVERY = 32, 16
+    slots = [Slot(torch.empty(lay["words"], dtype=torch.int32, pin_memory=True),
+                  torch.empty(lay["words"], dtype=torch.int32, device=dev)) for _ in range(NS)]
+
+    def views(slot):
+        return (slot.desc[0:2 * S].view(torch.int64), slot.desc[lay["lens"]:lay["lens"] + S],
+                slot.desc[lay["tables"]:lay["tables"] + S * MB].view(S, MB))
+
     for rep in reps:
-        slots_v = rep.desc[0:2 * S].view(torch.int64)
-        lens_v = rep.desc[lay["lens"]:lay["lens"] + S]
-        tab_v = rep.desc[lay["tables"]:lay["tables"] + S * MB].view(S, MB)
+        slots_v, lens_v, tab_v = views(slots[0])
         rep.out = torch.empty((S, Hq, D), dtype=out_dt, device=dev)
         rep.params = pa.make_decode_params(rep.out, q_d, rep.k_cache, rep.v_cache, tab_v, lens_v,
                                            Hkv, rep.max_ctx + W + K, spec.fp32_scale(),
@@ -238,7 +257,6 @@ def run_gpu(args, wl):
                                            k_scales=rep.k_scales, v_scales=rep.v_scales)
         ws_need = max(ws_need, pa.pa_decode_workspace_bytes(rep.params))
         rep.params.max_context_len = rep.max_ctx
-        rep.slots_v = slots_v
         if args.append == "fused" and spec.cache != "i8":
             rep.params.k_new = step_k_d.data_ptr()
             rep.params.v_new = step_v_d.data_ptr()
@@ -254,42 +272,50 @@ def run_gpu(args, wl):
     # before launching step i+1, so the compute queue holds only kernels and
     # never waits on the copy engine.  No GPU-side cross-stream waits are used:
     # a copy that waited on a compute-stream event blocked the host for most
-    # of a step.  A replica's staging and device buffers are reused R steps
-    # later, after the host has seen that replica's previous kernels finish.
+    # of a step.  Events on the compute stream ride on the kernel dispatches
+    # (no marker packets) and are attached to few steps: each one makes that
+    # dispatch's completion visible to the host, which costs stream time.
     compute = hip.stream()
     copy = hip.stream()
-    for rep in reps:
-        rep.copied = hip.event()
-        rep.done = hip.event()
-        hip.record(rep.copied, copy)       # start "complete"
-        hip.record(rep.done, compute)
+    for sl in slots:
+        sl.copied = hip.event()
+        hip.record(sl.copied, copy)        # start "complete"
+    done_events = {}                       # step -> event attached to its merge
+    done_pool = [hip.event(timing=True) for _ in range(NS // DONE_EVERY + 3)]
     cs = ctypes.c_void_p(compute)
     ids_ptr = [rep.seq_ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) for rep in reps]
-    ncow = [0] * R
+    ncow = [0] * NS
     ncow_c = ctypes.c_int32()
     row_bytes = S * Hkv * D * step_k_d.element_size()
-    nb_rep = wl.num_blocks
-    ev_a = [hip.event(timing=True) for _ in range(K)]
-    ev_b = [hip.event(timing=True) for _ in range(K)]
+    nb_rep = nb_pool
+    every = max(1, args.time_every)
+    markers = args.event_markers
+    n_timed = (K + every - 1) // every
+    ev_a = [hip.event(timing=True) for _ in range(n_timed)]
+    ev_b = [hip.event(timing=True) for _ in range(n_timed)]
     lens_log = []
     waited = [0.0]
-    stage_bytes = reps[0].stage.numel() * 4
+    stage_bytes = lay["words"] * 4
     ptrs = []
-    for rep in reps:
-        base = rep.stage.data_ptr()
+    for sl in slots:
+        base = sl.stage.data_ptr()
+        slots_v, lens_v, tab_v = views(sl)
         ptrs.append(dict(
             slots=ctypes.cast(base, ctypes.POINTER(ctypes.c_int64)),
             lens=ctypes.cast(base + 4 * lay["lens"], ctypes.POINTER(ctypes.c_int32)),
             tab=ctypes.cast(base + 4 * lay["tables"], ctypes.POINTER(ctypes.c_int32)),
             cow=ctypes.cast(base + 4 * lay["cows"], ctypes.POINTER(ctypes.c_int32)),
-            stage=ctypes.c_void_p(base), desc=ctypes.c_void_p(rep.desc.data_ptr()),
-            kc=ctypes.c_void_p(rep.k_cache.data_ptr()), vc=ctypes.c_void_p(rep.v_cache.data_ptr()),
-            ks=ctypes.c_void_p(rep.k_scales.data_ptr()) if rep.k_scales is not None else None,
-            vs=ctypes.c_void_p(rep.v_scales.data_ptr()) if rep.v_scales is not None else None,
-            slots_d=ctypes.c_void_p(rep.slots_v.data_ptr()),
-            cows_d=ctypes.c_void_p(rep.desc.data_ptr() + 4 * lay["cows"]),
+            stage=ctypes.c_void_p(base), desc=ctypes.c_void_p(sl.desc.data_ptr()),
+            slots_d=slots_v.data_ptr(), lens_d=lens_v.data_ptr(), tab_d=tab_v.data_ptr(),
+            cows_d=ctypes.c_void_p(sl.desc.data_ptr() + 4 * lay["cows"]),
             lens_np=np.ctypeslib.as_array(ctypes.cast(base + 4 * lay["lens"], ctypes.POINTER(ctypes.c_int32)),
                                           shape=(S,))))
+    rp = []
+    for rep in reps:
+        rp.append(dict(
+            kc=ctypes.c_void_p(rep.k_cache.data_ptr()), vc=ctypes.c_void_p(rep.v_cache.data_ptr()),
+            ks=ctypes.c_void_p(rep.k_scales.data_ptr()) if rep.k_scales is not None else None,
+            vs=ctypes.c_void_p(rep.v_scales.data_ptr()) if rep.v_scales is not None else None))
     pool_h = [rep.pool._h for rep in reps]
     i8 = spec.cache == "i8"
     fused = args.append == "fused" and not i8   # an INT8 cache appends with its own kernel
@@ -298,56 +324,76 @@ def run_gpu(args, wl):
 
     def prepare(i):
         """Host pool append for step i and the copy of its inputs (copy stream)."""
-        r = i % R
-        rep, pp = reps[r], ptrs[r]
-        w0 = time.perf_counter()
-        hip.sync_event(rep.done)                       # replica's previous step finished
-        waited[0] += time.perf_counter() - w0
+        r, j = i % R, i % NS
+        rep, pp = reps[r], ptrs[j]
+        if i >= NS:                                    # slot j was last used by step i - NS
+            w0 = time.perf_counter()
+            s_done = min(s for s in done_events if s >= i - NS)
+            hip.sync_event(done_events[s_done])
+            waited[0] += time.perf_counter() - w0
+            for s in [s for s in done_events if s < s_done]:
+                done_pool.append(done_events.pop(s))
         st = L.pa_seq_append_batch(pool_h[r], ids_ptr[r], S, pp["slots"], pp["cow"], ctypes.byref(ncow_c))
         if st:
             pa._check(st)
-        ncow[r] = ncow_c.value
+        ncow[j] = ncow_c.value
         st = L.pa_seq_export(pool_h[r], ids_ptr[r], S, MB, pp["tab"], pp["lens"])
         if st:
             pa._check(st)
         rep.max_ctx += 1
-        rep.params.max_context_len = rep.max_ctx
         hip.h2d(pp["desc"], pp["stage"], stage_bytes, copy)
-        hip.record(rep.copied, copy)
+        hip.record(slots[j].copied, copy)
 
     def launch(i, timed_idx):
         """Step i's kernels (compute stream), once its inputs are on the device."""
-        r = i % R
-        rep, pp = reps[r], ptrs[r]
+        r, j = i % R, i % NS
+        rep, pp, q = reps[r], ptrs[j], rp[r]
         w0 = time.perf_counter()
-        hip.sync_event(rep.copied)
+        hip.sync_event(slots[j].copied)
         waited[0] += time.perf_counter() - w0
-        if ncow[r]:
+        prm = rep.params
+        prm.block_tables, prm.context_lens = pp["tab_d"], pp["lens_d"]
+        prm.max_context_len = rep.max_ctx
+        if ncow[j]:
             if i8:
-                pa._check(L.pa_copy_blocks_int8(pp["kc"], pp["vc"], pp["ks"], pp["vs"], pp["cows_d"],
-                                                ncow[r], Hkv, D, nb_rep, cs))
+                pa._check(L.pa_copy_blocks_int8(q["kc"], q["vc"], q["ks"], q["vs"], pp["cows_d"],
+                                                ncow[j], Hkv, D, nb_rep, cs))
             else:
-                pa._check(L.pa_copy_blocks(pp["kc"], pp["vc"], pp["cows_d"], ncow[r], Hkv, D,
+                pa._check(L.pa_copy_blocks(q["kc"], q["vc"], pp["cows_d"], ncow[j], Hkv, D,
                                            nb_rep, dt_code, cs))
         if fused:
-            rep.params.k_new = k0 + i * row_bytes
-            rep.params.v_new = v0 + i * row_bytes
+            prm.k_new = k0 + i * row_bytes
+            prm.v_new = v0 + i * row_bytes
+            prm.slot_mapping = pp["slots_d"]
         elif i8:
             pa._check(L.pa_reshape_and_cache_int8(ctypes.c_void_p(k0 + i * row_bytes),
-                                                  ctypes.c_void_p(v0 + i * row_bytes), pp["kc"], pp["vc"],
-                                                  pp["ks"], pp["vs"], pp["slots_d"], S, Hkv, D, nb_rep,
-                                                  dt_code, cs))
+                                                  ctypes.c_void_p(v0 + i * row_bytes), q["kc"], q["vc"],
+                                                  q["ks"], q["vs"], ctypes.c_void_p(pp["slots_d"]), S, Hkv,
+                                                  D, nb_rep, dt_code, cs))
         else:
             pa._check(L.pa_reshape_and_cache(ctypes.c_void_p(k0 + i * row_bytes),
-                                             ctypes.c_void_p(v0 + i * row_bytes), pp["kc"], pp["vc"],
-                                             pp["slots_d"], S, Hkv, D, nb_rep, dt_code, cs))
-        if timed_idx >= 0:
-            hip.record(ev_a[timed_idx], compute)
-        pa._check(L.pa_decode_partitions(ctypes.byref(rep.params), ws_ptr, ws_bytes, cs))
-        if timed_idx >= 0:
-            hip.record(ev_b[timed_idx], compute)
-        pa._check(L.pa_decode_merge(ctypes.byref(rep.params), ws_ptr, ws_bytes, cs))
-        hip.record(rep.done, compute)
+                                             ctypes.c_void_p(v0 + i * row_bytes), q["kc"], q["vc"],
+                                             ctypes.c_void_p(pp["slots_d"]), S, Hkv, D, nb_rep, dt_code, cs))
+        done = None
+        if i % DONE_EVERY == DONE_EVERY - 1 or i == total - 1:
+            done = done_pool.pop()
+            done_events[i] = done
+        if markers:
+            if timed_idx >= 0:
+                hip.record(ev_a[timed_idx], compute)
+            pa._check(L.pa_decode_partitions(ctypes.byref(prm), ws_ptr, ws_bytes, cs))
+            if timed_idx >= 0:
+                hip.record(ev_b[timed_idx], compute)
+            pa._check(L.pa_decode_merge(ctypes.byref(prm), ws_ptr, ws_bytes, cs))
+            if done is not None:
+                hip.record(done, compute)
+        else:
+            prm.start_event = ev_a[timed_idx] if timed_idx >= 0 else None
+            prm.stop_event = ev_b[timed_idx] if timed_idx >= 0 else None
+            pa._check(L.pa_decode_partitions(ctypes.byref(prm), ws_ptr, ws_bytes, cs))
+            prm.start_event = None
+            prm.stop_event = done
+            pa._check(L.pa_decode_merge(ctypes.byref(prm), ws_ptr, ws_bytes, cs))
         if timed_idx >= 0:
             lens_log.append(pp["lens_np"].copy())
 
@@ -363,7 +409,7 @@ def run_gpu(args, wl):
     host = 0.0
     for k in range(K):
         h0 = time.perf_counter()
-        launch(W + k, k)
+        launch(W + k, k // every if k % every == 0 else -1)
         if W + k + 1 < total:
             prepare(W + k + 1)
         host += time.perf_counter() - h0
@@ -372,7 +418,7 @@ def run_gpu(args, wl):
     log(f"host time inside the step loop: {host / K * 1e6:.1f} us per step, of which "
         f"{waited[0] / K * 1e6:.1f} us blocked on the device")
     elapsed = t1 - t0
-    part_ms = np.array([hip.elapsed_ms(ev_a[k], ev_b[k]) for k in range(K)])
+    part_ms = np.array([hip.elapsed_ms(ev_a[k], ev_b[k]) for k in range(n_timed)])
     alg_bytes = [accounting.decode_algorithmic_bytes(l, Hq, Hkv, D, spec.dtype, spec.out_dtype, cache=spec.cache,
                                                      shared_tokens=spec.prefix_len) for l in lens_log]
     log(f"timed {K} steps in {elapsed * 1e3:.2f} ms; partition kernel mean {part_ms.mean() * 1e3:.1f} us")
@@ -458,7 +504,7 @@ def run_copy_calibration(nbytes):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--replicas", type=int, default=3)
@@ -466,6 +512,12 @@ def main():
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--append", default="fused", choices=["fused", "separate"],
                     help="append the step's K/V inside the decode launch, or with pa_reshape_and_cache")
+    ap.add_argument("--time-every", type=int, default=10, metavar="N",
+                    help="bracket every N-th attention launch with timing events (the event markers "
+                         "themselves cost stream time)")
+    ap.add_argument("--event-markers", action="store_true",
+                    help="record the timing and completion events as separate stream markers "
+                         "(hipEventRecord) instead of on the kernel dispatches")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",

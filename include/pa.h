@@ -179,6 +179,18 @@ typedef struct pa_decode_params {
   pa_dtype q_dtype;
   const float *k_scales;
   const float *v_scales;
+  /* Optional hipEvent_t handles (NULL = none), created by the caller.  They
+   * are recorded from the kernel dispatches' own start and end times
+   * (hipExtLaunchKernel), so timing a launch adds no marker to the stream:
+   *   pa_decode_partitions  start and end of the attention kernel;
+   *   pa_decode_merge       start and end of the merge kernel;
+   *   pa_decode             start of the attention kernel, end of the last
+   *                         kernel of the call.
+   * A call that launches nothing (no sequences, or no merge needed) records
+   * the given events on the stream instead, so they always complete after
+   * the call's work.  The events are not read back by the library. */
+  void *start_event;
+  void *stop_event;
 } pa_decode_params;
 
 /* Partition size (tokens) pa_decode will use for these parameters, 0 for the

@@ -44,7 +44,8 @@ class pa_decode_params(ctypes.Structure):
                 ("max_context_len", _I32), ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int),
                 ("out_dtype", ctypes.c_int), ("partition_tokens", _I32), ("kernel", ctypes.c_int),
                 ("k_new", _P), ("v_new", _P), ("slot_mapping", _P),
-                ("q_dtype", ctypes.c_int), ("k_scales", _P), ("v_scales", _P)]
+                ("q_dtype", ctypes.c_int), ("k_scales", _P), ("v_scales", _P),
+                ("start_event", _P), ("stop_event", _P)]
 
 
 _lib = None
@@ -134,8 +135,10 @@ def _stream(stream):
 
 def make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
                        max_context_len, scale, partition_tokens=0, kernel="auto", k_new=None,
-                       v_new=None, slot_mapping=None, k_scales=None, v_scales=None):
-    """k_scales / v_scales: the float32 scale arrays of an int8 cache (else None)."""
+                       v_new=None, slot_mapping=None, k_scales=None, v_scales=None,
+                       start_event=None, stop_event=None):
+    """k_scales / v_scales: the float32 scale arrays of an int8 cache (else None).
+    start_event / stop_event: raw hipEvent_t handles (ints) or None."""
     S, Hq, D = q.shape
     nb = k_cache.numel() // (num_kv_heads * BLOCK_SIZE * D)
     return pa_decode_params(
@@ -143,7 +146,13 @@ def make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens, num
         S, Hq, num_kv_heads, D, block_tables.shape[1] if block_tables.dim() == 2 else 0, nb,
         int(max_context_len), float(scale), _dtype_code(k_cache), _dtype_code(out),
         int(partition_tokens), KERNELS[kernel], _dev(k_new), _dev(v_new), _dev(slot_mapping),
-        _dtype_code(q), _dev(k_scales), _dev(v_scales))
+        _dtype_code(q), _dev(k_scales), _dev(v_scales), _event(start_event), _event(stop_event))
+
+
+def _event(ev):
+    if ev is None:
+        return None
+    return int(ev.value if isinstance(ev, ctypes.c_void_p) else ev)
 
 
 def pa_decode_workspace_bytes(params: pa_decode_params) -> int:

@@ -29,6 +29,7 @@
 //     LDS, cross-lane reductions by shuffles.
 // Scores are kept in the log2 domain (scale * log2(e) folded into one
 // multiply) so the exponentials are single v_exp_f32 instructions.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -1671,35 +1672,49 @@ int32_t num_partitions(const pa_decode_params *p, int32_t pt) {
   return std::max(1, (std::max(p->max_context_len, 1) + pt - 1) / pt);
 }
 
+// Optional start/stop events of a launch, taken from the dispatch itself.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// One kernel launch: through hipExtLaunchKernel when events are attached, so
+// they carry the dispatch's own timestamps and add no stream marker.
+hipError_t launch_kernel(const void *fn, dim3 grid, dim3 block, void **args, size_t lds, hipStream_t hs,
+                         const LaunchEvents &ev) {
+  if (ev.start || ev.stop) return hipExtLaunchKernel(fn, grid, block, args, lds, hs, ev.start, ev.stop, 0);
+  return hipLaunchKernel(fn, grid, block, args, lds, hs);
+}
+
+// Records the events of a call that launches no kernel.
+pa_status record_events(const LaunchEvents &ev, hipStream_t hs, const char *who) {
+  if (ev.start) {
+    const hipError_t e = hipEventRecord(ev.start, hs);
+    if (e != hipSuccess) return hip_check(e, who);
+  }
+  if (ev.stop) {
+    const hipError_t e = hipEventRecord(ev.stop, hs);
+    if (e != hipSuccess) return hip_check(e, who);
+  }
+  return PA_OK;
+}
+
 template <int DT, int D>
-void launch_valu(int G, dim3 grid, hipStream_t st, const DecodeArgs &a) {
-  if (G <= 1)
-    hipLaunchKernelGGL((pa_partition_kernel<ValuWave<DT, D, 1>, D, false>), grid, dim3(kThreads), 0, st, a);
-  else if (G <= 2)
-    hipLaunchKernelGGL((pa_partition_kernel<ValuWave<DT, D, 2>, D, false>), grid, dim3(kThreads), 0, st, a);
-  else if (G <= 4)
-    hipLaunchKernelGGL((pa_partition_kernel<ValuWave<DT, D, 4>, D, false>), grid, dim3(kThreads), 0, st, a);
-  else if (G <= 8)
-    hipLaunchKernelGGL((pa_partition_kernel<ValuWave<DT, D, 8>, D, false>), grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((pa_partition_kernel<ValuWave<DT, D, 16>, D, false>), grid, dim3(kThreads), 0, st, a);
+const void *valu_kernel(int G) {
+  if (G <= 1) return reinterpret_cast<const void *>(&pa_partition_kernel<ValuWave<DT, D, 1>, D, false>);
+  if (G <= 2) return reinterpret_cast<const void *>(&pa_partition_kernel<ValuWave<DT, D, 2>, D, false>);
+  if (G <= 4) return reinterpret_cast<const void *>(&pa_partition_kernel<ValuWave<DT, D, 4>, D, false>);
+  if (G <= 8) return reinterpret_cast<const void *>(&pa_partition_kernel<ValuWave<DT, D, 8>, D, false>);
+  return reinterpret_cast<const void *>(&pa_partition_kernel<ValuWave<DT, D, 16>, D, false>);
 }
 
 template <int D>
-void launch_partition(pa_dtype dt, bool mfma, int G, dim3 grid, hipStream_t st, const DecodeArgs &a) {
-  if (mfma) {
-    if (dt == PA_BF16)
-      hipLaunchKernelGGL((pa_partition_kernel<MfmaWave<PA_BF16, D>, D, true>), grid, dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL((pa_partition_kernel<MfmaWave<PA_F16, D>, D, true>), grid, dim3(kThreads), 0, st, a);
-  } else {
-    if (dt == PA_BF16)
-      launch_valu<PA_BF16, D>(G, grid, st, a);
-    else if (dt == PA_F16)
-      launch_valu<PA_F16, D>(G, grid, st, a);
-    else
-      launch_valu<PA_F32, D>(G, grid, st, a);
-  }
+const void *partition_kernel(pa_dtype dt, bool mfma, int G) {
+  if (mfma)
+    return dt == PA_BF16 ? reinterpret_cast<const void *>(&pa_partition_kernel<MfmaWave<PA_BF16, D>, D, true>)
+                         : reinterpret_cast<const void *>(&pa_partition_kernel<MfmaWave<PA_F16, D>, D, true>);
+  if (dt == PA_BF16) return valu_kernel<PA_BF16, D>(G);
+  if (dt == PA_F16) return valu_kernel<PA_F16, D>(G);
+  return valu_kernel<PA_F32, D>(G);
 }
 
 }  // namespace
@@ -1779,41 +1794,54 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
   return PA_OK;
 }
 
-pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipStream_t hs) {
-  const bool mfma = use_mfma(p);
+pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipStream_t hs,
+                            const LaunchEvents &ev) {
+  void *args[] = {const_cast<DecodeArgs *>(&a)};
   if (use_balanced(p)) {
     const dim3 grid((unsigned)(a.num_workers / kBWaves));
     const size_t lds = park_bytes(a.group, p->head_dim);
-    void *args[] = {const_cast<DecodeArgs *>(&a)};
-    hipError_t e = hipLaunchKernel(balanced_kernel(p->kv_dtype, p->q_dtype, p->head_dim), grid,
-                                   dim3(kBThreads), args, lds, hs);
+    hipError_t e = launch_kernel(balanced_kernel(p->kv_dtype, p->q_dtype, p->head_dim), grid,
+                                 dim3(kBThreads), args, lds, hs, ev);
     if (e != hipSuccess) return hip_check(e, "pa_decode balanced launch");
     return hip_check(hipGetLastError(), "pa_decode balanced launch");
   }
+  const bool mfma = use_mfma(p);
   const dim3 grid((unsigned)((int64_t)a.max_parts * p->num_kv_heads * p->num_seqs));
-  if (p->head_dim == 128)
-    launch_partition<128>(p->kv_dtype, mfma, a.group, grid, hs, a);
-  else
-    launch_partition<64>(p->kv_dtype, mfma, a.group, grid, hs, a);
+  const void *fn = p->head_dim == 128 ? partition_kernel<128>(p->kv_dtype, mfma, a.group)
+                                      : partition_kernel<64>(p->kv_dtype, mfma, a.group);
+  hipError_t e = launch_kernel(fn, grid, dim3(kThreads), args, 0, hs, ev);
+  if (e != hipSuccess) return hip_check(e, "pa_decode partition launch");
   return hip_check(hipGetLastError(), "pa_decode partition launch");
 }
 
-pa_status launch_merge(const pa_decode_params *p, const DecodeArgs &a, hipStream_t hs) {
-  const int32_t rows = p->num_seqs * p->num_q_heads;
+// True when the call's merge step launches a kernel.
+bool has_merge(const pa_decode_params *p, const DecodeArgs &a) {
+  return use_balanced(p) || a.max_parts > 1;
+}
+
+pa_status launch_merge(const pa_decode_params *p, const DecodeArgs &a, hipStream_t hs,
+                       const LaunchEvents &ev) {
+  if (!has_merge(p, a)) return record_events(ev, hs, "pa_decode merge events");
+  int32_t rows = p->num_seqs * p->num_q_heads;
   const dim3 mgrid((rows + kMergeWaves - 1) / kMergeWaves);
-  if (use_balanced(p)) {
-    if (p->head_dim == 128)
-      hipLaunchKernelGGL(pa_merge_balanced_kernel<128>, mgrid, dim3(kMergeWaves * 64), 0, hs, a, rows);
-    else
-      hipLaunchKernelGGL(pa_merge_balanced_kernel<64>, mgrid, dim3(kMergeWaves * 64), 0, hs, a, rows);
-    return hip_check(hipGetLastError(), "pa_decode merge launch");
-  }
-  if (a.max_parts <= 1) return PA_OK;
-  if (p->head_dim == 128)
-    hipLaunchKernelGGL(pa_merge_kernel<128>, mgrid, dim3(kMergeWaves * 64), 0, hs, a, rows);
+  void *args[] = {const_cast<DecodeArgs *>(&a), &rows};
+  const void *fn;
+  if (use_balanced(p))
+    fn = p->head_dim == 128 ? reinterpret_cast<const void *>(&pa_merge_balanced_kernel<128>)
+                            : reinterpret_cast<const void *>(&pa_merge_balanced_kernel<64>);
   else
-    hipLaunchKernelGGL(pa_merge_kernel<64>, mgrid, dim3(kMergeWaves * 64), 0, hs, a, rows);
+    fn = p->head_dim == 128 ? reinterpret_cast<const void *>(&pa_merge_kernel<128>)
+                            : reinterpret_cast<const void *>(&pa_merge_kernel<64>);
+  hipError_t e = launch_kernel(fn, mgrid, dim3(kMergeWaves * 64), args, 0, hs, ev);
+  if (e != hipSuccess) return hip_check(e, "pa_decode merge launch");
   return hip_check(hipGetLastError(), "pa_decode merge launch");
+}
+
+LaunchEvents events_of(const pa_decode_params *p) {
+  LaunchEvents ev;
+  ev.start = static_cast<hipEvent_t>(p->start_event);
+  ev.stop = static_cast<hipEvent_t>(p->stop_event);
+  return ev;
 }
 
 }  // namespace
@@ -1824,26 +1852,36 @@ pa_status pa_decode(const pa_decode_params *p, void *workspace, size_t workspace
                     void *stream) {
   DecodeArgs a;
   pa_status st = prepare(p, workspace, workspace_bytes, "pa_decode", a);
-  if (st != PA_OK || p->num_seqs == 0) return st;
+  if (st != PA_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if ((st = launch_partitions(p, a, hs)) != PA_OK) return st;
-  return launch_merge(p, a, hs);
+  const LaunchEvents ev = events_of(p);
+  if (p->num_seqs == 0) return record_events(ev, hs, "pa_decode events");
+  const bool merge = has_merge(p, a);
+  LaunchEvents first, second;
+  first.start = ev.start;
+  (merge ? second : first).stop = ev.stop;
+  if ((st = launch_partitions(p, a, hs, first)) != PA_OK) return st;
+  return merge ? launch_merge(p, a, hs, second) : PA_OK;
 }
 
 pa_status pa_decode_partitions(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
                                void *stream) {
   DecodeArgs a;
   pa_status st = prepare(p, workspace, workspace_bytes, "pa_decode_partitions", a);
-  if (st != PA_OK || p->num_seqs == 0) return st;
-  return launch_partitions(p, a, static_cast<hipStream_t>(stream));
+  if (st != PA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (p->num_seqs == 0) return record_events(events_of(p), hs, "pa_decode_partitions events");
+  return launch_partitions(p, a, hs, events_of(p));
 }
 
 pa_status pa_decode_merge(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
                           void *stream) {
   DecodeArgs a;
   pa_status st = prepare(p, workspace, workspace_bytes, "pa_decode_merge", a);
-  if (st != PA_OK || p->num_seqs == 0) return st;
-  return launch_merge(p, a, static_cast<hipStream_t>(stream));
+  if (st != PA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (p->num_seqs == 0) return record_events(events_of(p), hs, "pa_decode_merge events");
+  return launch_merge(p, a, hs, events_of(p));
 }
 
 pa_status pa_reshape_and_cache(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
