@@ -67,7 +67,7 @@ def _load():
         lib.oracle_copy_blocks.argtypes = [_P, _P, _P, _I, _I, _I, _I]
         lib.oracle_decode.restype = _I
         lib.oracle_decode.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
-                                      ctypes.c_float, _I, _I]
+                                      ctypes.c_float, _I, _I, _I]
         lib.oracle_k_offset_i8.restype = _I64
         lib.oracle_k_offset_i8.argtypes = [_I64, _I, _I, _I, _I, _I]
         lib.oracle_v_offset_i8.restype = _I64
@@ -81,10 +81,10 @@ def _load():
         lib.oracle_copy_blocks_i8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I]
         lib.oracle_decode_i8.restype = _I
         lib.oracle_decode_i8.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
-                                         _I, ctypes.c_float, _I]
+                                         _I, ctypes.c_float, _I, _I]
         lib.oracle_bruteforce_contiguous.restype = None
         lib.oracle_bruteforce_contiguous.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
-                                                     ctypes.c_float, _I]
+                                                     ctypes.c_float, _I, _I]
         _lib = lib
     return _lib
 
@@ -139,8 +139,9 @@ def copy_blocks(k_cache, v_cache, pairs, num_kv_heads, head_dim, dtype):
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads, scale, dtype,
-           nthreads=0, return_threads=False):
-    """fp64 paged decode; q is [S][Hq][D] in the cache type.  Returns float64 [S][Hq][D]."""
+           nthreads=0, return_threads=False, window=0):
+    """fp64 paged decode; q is [S][Hq][D] in the cache type.  Returns float64 [S][Hq][D].
+    window: sliding window W (0 = none): the query at position L-1 sees L-1-W .. L-1."""
     q = _check(q, dtype)
     S, Hq, D = q.shape
     tables = np.ascontiguousarray(block_tables, dtype=np.int32)
@@ -148,11 +149,11 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads, scale,
     out = np.empty((S, Hq, D), dtype=np.float64)
     used = _load().oracle_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(tables),
                                  _ptr(lens), S, Hq, num_kv_heads, D, tables.shape[1],
-                                 float(scale), _DTYPES[dtype], nthreads)
+                                 float(scale), _DTYPES[dtype], int(window), nthreads)
     return (out, used) if return_threads else out
 
 
-def bruteforce_contiguous(q, k_seq, v_seq, context_lens, scale, dtype):
+def bruteforce_contiguous(q, k_seq, v_seq, context_lens, scale, dtype, window=0):
     """fp64 attention over contiguous [S][Lmax][Hkv][D] arrays (no table)."""
     q = _check(q, dtype)
     k_seq = _check(k_seq, dtype)
@@ -163,7 +164,7 @@ def bruteforce_contiguous(q, k_seq, v_seq, context_lens, scale, dtype):
     out = np.empty((S, Hq, D), dtype=np.float64)
     _load().oracle_bruteforce_contiguous(_ptr(out), _ptr(q), _ptr(k_seq), _ptr(v_seq),
                                          _ptr(lens), S, Hq, Hkv, D, Lmax, float(scale),
-                                         _DTYPES[dtype])
+                                         _DTYPES[dtype], int(window))
     return out
 
 
@@ -218,7 +219,7 @@ def copy_blocks_i8(k_cache, v_cache, k_scales, v_scales, pairs, num_kv_heads, he
 
 
 def decode_i8(q, q_dtype, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens,
-              num_kv_heads, scale, nthreads=0, return_threads=False):
+              num_kv_heads, scale, nthreads=0, return_threads=False, window=0):
     """fp64 paged decode over an int8 cache; q is [S][Hq][D] in q_dtype."""
     q = _check(q, q_dtype)
     S, Hq, D = q.shape
@@ -227,5 +228,6 @@ def decode_i8(q, q_dtype, k_cache, v_cache, k_scales, v_scales, block_tables, co
     out = np.empty((S, Hq, D), dtype=np.float64)
     used = _load().oracle_decode_i8(_ptr(out), _ptr(q), _DTYPES[q_dtype], _ptr(k_cache), _ptr(v_cache),
                                     _ptr(k_scales), _ptr(v_scales), _ptr(tables), _ptr(lens), S, Hq,
-                                    num_kv_heads, D, tables.shape[1], float(scale), nthreads)
+                                    num_kv_heads, D, tables.shape[1], float(scale), int(window),
+                                    nthreads)
     return (out, used) if return_threads else out

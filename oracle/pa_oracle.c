@@ -210,28 +210,40 @@ static double value_at(const orc_src *s, int i, int d) {
                    s->dtype);
 }
 
-static void attend_one(double *out, const double *q, const orc_src *src, int L, double scale,
-                       double *sigma /* scratch, >= L */) {
+/* First position a decode query attends to.  The query is the newest token,
+ * position i = L-1.  Without a window (window <= 0) it sees every position;
+ * with a sliding window W it sees positions i-W .. i (clipped at 0): the
+ * interval "[i-W, i]" of "LLM Inference Optimization: KV-Cache,
+ * PagedAttention, and GPU Memory Efficiency", section "Future Optimizations"
+ * (sliding window attention), read with both ends included. */
+static int first_attended(int L, int window) {
+  if (window <= 0 || L - 1 - window <= 0) return 0;
+  return L - 1 - window;
+}
+
+static void attend_one(double *out, const double *q, const orc_src *src, int L, int window,
+                       double scale, double *sigma /* scratch, >= L */) {
   int D = src->head_dim;
   if (L <= 0) {
     for (int d = 0; d < D; ++d) out[d] = 0.0;
     return;
   }
+  int i0 = first_attended(L, window);
   double M = -INFINITY;
-  for (int i = 0; i < L; ++i) {
+  for (int i = i0; i < L; ++i) {
     double dot = 0.0;
     for (int d = 0; d < D; ++d) dot += q[d] * key_at(src, i, d);
     sigma[i] = scale * dot;
     if (sigma[i] > M) M = sigma[i];
   }
   double Z = 0.0;
-  for (int i = 0; i < L; ++i) {
+  for (int i = i0; i < L; ++i) {
     sigma[i] = exp(sigma[i] - M); /* sigma now holds the weights w_i */
     Z += sigma[i];
   }
   for (int d = 0; d < D; ++d) {
     double acc = 0.0;
-    for (int i = 0; i < L; ++i) acc += sigma[i] * value_at(src, i, d);
+    for (int i = i0; i < L; ++i) acc += sigma[i] * value_at(src, i, d);
     out[d] = acc / Z;
   }
 }
@@ -242,13 +254,15 @@ static void attend_one(double *out, const double *q, const orc_src *src, int L, 
  *   q:      [S][Hq][D] in the cache type
  *   tables: [S][max_blocks] int32;  lens: [S] int32
  *   scale:  taken as the fp32 value the caller passes, widened to double
+ *   window: sliding window W (<= 0: none); positions before L-1-W are
+ *           never read, table entries included
  *   nthreads: OpenMP threads for the (s, h) loop; <= 0 means the default
  * Returns the number of threads used.
  * ------------------------------------------------------------------------ */
 int oracle_decode(double *out, const void *q, const void *k_cache, const void *v_cache,
                   const int32_t *tables, const int32_t *lens, int num_seqs, int num_q_heads,
                   int num_kv_heads, int head_dim, int max_blocks, float scale, int dtype,
-                  int nthreads) {
+                  int window, int nthreads) {
   int G = num_q_heads / num_kv_heads;
   int Lmax = 0;
   for (int s = 0; s < num_seqs; ++s)
@@ -272,7 +286,7 @@ int oracle_decode(double *out, const void *q, const void *k_cache, const void *v
         qd[d] = load_elem(q, (int64_t)sh * head_dim + d, dtype);
       orc_src src = {k_cache, v_cache, tables + (int64_t)s * max_blocks, num_kv_heads,
                      head_dim, dtype, h / G, NULL, NULL};
-      attend_one(out + (int64_t)sh * head_dim, qd, &src, lens[s], (double)scale, sigma);
+      attend_one(out + (int64_t)sh * head_dim, qd, &src, lens[s], window, (double)scale, sigma);
     }
     free(sigma);
     free(qd);
@@ -290,7 +304,7 @@ int oracle_decode(double *out, const void *q, const void *k_cache, const void *v
 void oracle_bruteforce_contiguous(double *out, const void *q, const void *k_seq,
                                   const void *v_seq, const int32_t *lens, int num_seqs,
                                   int num_q_heads, int num_kv_heads, int head_dim, int Lmax,
-                                  float scale, int dtype) {
+                                  float scale, int dtype, int window) {
   int G = num_q_heads / num_kv_heads;
   int eb = elem_bytes(dtype);
   double *sigma = (double *)malloc(sizeof(double) * (Lmax > 0 ? Lmax : 1));
@@ -303,7 +317,7 @@ void oracle_bruteforce_contiguous(double *out, const void *q, const void *k_seq,
       orc_src src = {NULL, NULL, NULL, num_kv_heads, head_dim, dtype, h / G,
                      (const char *)k_seq + s * seq_elems * eb,
                      (const char *)v_seq + s * seq_elems * eb};
-      attend_one(out + sh * head_dim, qd, &src, lens[s], (double)scale, sigma);
+      attend_one(out + sh * head_dim, qd, &src, lens[s], window, (double)scale, sigma);
     }
   free(sigma);
   free(qd);
@@ -417,15 +431,16 @@ typedef struct {
   int num_kv_heads, head_dim, kv_head;
 } orc_src_i8;
 
-static void attend_one_i8(double *out, const double *q, const orc_src_i8 *s, int L, double scale,
-                          double *sigma) {
+static void attend_one_i8(double *out, const double *q, const orc_src_i8 *s, int L, int window,
+                          double scale, double *sigma) {
   int D = s->head_dim;
   if (L <= 0) {
     for (int d = 0; d < D; ++d) out[d] = 0.0;
     return;
   }
+  int i0 = first_attended(L, window);
   double M = -INFINITY;
-  for (int i = 0; i < L; ++i) {
+  for (int i = i0; i < L; ++i) {
     int64_t blk = s->table[i / ORC_BS];
     int t = i % ORC_BS;
     double ks = (double)s->k_scales[(blk * s->num_kv_heads + s->kv_head) * ORC_BS + t];
@@ -436,13 +451,13 @@ static void attend_one_i8(double *out, const double *q, const orc_src_i8 *s, int
     if (sigma[i] > M) M = sigma[i];
   }
   double Z = 0.0;
-  for (int i = 0; i < L; ++i) {
+  for (int i = i0; i < L; ++i) {
     sigma[i] = exp(sigma[i] - M);
     Z += sigma[i];
   }
   for (int d = 0; d < D; ++d) {
     double acc = 0.0;
-    for (int i = 0; i < L; ++i) {
+    for (int i = i0; i < L; ++i) {
       int64_t blk = s->table[i / ORC_BS];
       int t = i % ORC_BS;
       double vs = (double)s->v_scales[(blk * s->num_kv_heads + s->kv_head) * ORC_BS + t];
@@ -455,7 +470,8 @@ static void attend_one_i8(double *out, const double *q, const orc_src_i8 *s, int
 int oracle_decode_i8(double *out, const void *q, int q_dtype, const int8_t *k_cache,
                      const int8_t *v_cache, const float *k_scales, const float *v_scales,
                      const int32_t *tables, const int32_t *lens, int num_seqs, int num_q_heads,
-                     int num_kv_heads, int head_dim, int max_blocks, float scale, int nthreads) {
+                     int num_kv_heads, int head_dim, int max_blocks, float scale, int window,
+                     int nthreads) {
   int G = num_q_heads / num_kv_heads;
   int Lmax = 0;
   for (int s = 0; s < num_seqs; ++s)
@@ -478,7 +494,7 @@ int oracle_decode_i8(double *out, const void *q, int q_dtype, const int8_t *k_ca
       for (int d = 0; d < head_dim; ++d) qd[d] = load_elem(q, (int64_t)sh * head_dim + d, q_dtype);
       orc_src_i8 src = {k_cache, v_cache, k_scales, v_scales, tables + (int64_t)s * max_blocks,
                         num_kv_heads, head_dim, h / G};
-      attend_one_i8(out + (int64_t)sh * head_dim, qd, &src, lens[s], (double)scale, sigma);
+      attend_one_i8(out + (int64_t)sh * head_dim, qd, &src, lens[s], window, (double)scale, sigma);
     }
     free(sigma);
     free(qd);

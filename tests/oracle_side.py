@@ -115,7 +115,7 @@ def tables(st: OracleState, max_blocks: int):
     return np.array(t, dtype=np.int32).reshape(len(st.seq_ids), max_blocks), np.array(l, dtype=np.int32)
 
 
-def decode(wl, st: OracleState, max_blocks: int, nthreads: int = 0, seq_subset=None):
+def decode(wl, st: OracleState, max_blocks: int, nthreads: int = 0, seq_subset=None, window: int = 0):
     spec = wl.spec
     tab, lens = tables(st, max_blocks)
     q = wl.q
@@ -123,6 +123,7 @@ def decode(wl, st: OracleState, max_blocks: int, nthreads: int = 0, seq_subset=N
         tab, lens, q = tab[seq_subset], lens[seq_subset], np.ascontiguousarray(q[seq_subset])
     if spec.cache == "i8":
         return oracle.decode_i8(q, spec.dtype, st.k_cache, st.v_cache, st.k_scales, st.v_scales,
-                                tab, lens, spec.num_kv_heads, spec.fp32_scale(), nthreads=nthreads)
+                                tab, lens, spec.num_kv_heads, spec.fp32_scale(), nthreads=nthreads,
+                                window=window)
     return oracle.decode(q, st.k_cache, st.v_cache, tab, lens, spec.num_kv_heads,
-                         spec.fp32_scale(), spec.dtype, nthreads=nthreads)
+                         spec.fp32_scale(), spec.dtype, nthreads=nthreads, window=window)
