@@ -254,7 +254,8 @@ def run_gpu(args, wl):
         rep.params = pa.make_decode_params(rep.out, q_d, rep.k_cache, rep.v_cache, tab_v, lens_v,
                                            Hkv, rep.max_ctx + W + K, spec.fp32_scale(),
                                            args.partition_tokens, args.kernel,
-                                           k_scales=rep.k_scales, v_scales=rep.v_scales)
+                                           k_scales=rep.k_scales, v_scales=rep.v_scales,
+                                           sliding_window=spec.window)
         ws_need = max(ws_need, pa.pa_decode_workspace_bytes(rep.params))
         rep.params.max_context_len = rep.max_ctx
         if args.append == "fused" and spec.cache != "i8":
@@ -420,7 +421,8 @@ def run_gpu(args, wl):
     elapsed = t1 - t0
     part_ms = np.array([hip.elapsed_ms(ev_a[k], ev_b[k]) for k in range(n_timed)])
     alg_bytes = [accounting.decode_algorithmic_bytes(l, Hq, Hkv, D, spec.dtype, spec.out_dtype, cache=spec.cache,
-                                                     shared_tokens=spec.prefix_len) for l in lens_log]
+                                                     shared_tokens=spec.prefix_len, window=spec.window)
+                 for l in lens_log]
     log(f"timed {K} steps in {elapsed * 1e3:.2f} ms; partition kernel mean {part_ms.mean() * 1e3:.1f} us")
     return {
         "elapsed": elapsed, "part_ms": part_ms, "alg": alg_bytes, "part_tokens": part_tokens,
@@ -471,10 +473,10 @@ def run_cpu_baseline(wl, seconds):
     while True:
         if i8:
             _, used = oracle.decode_i8(wl.q, dt, kc, vc, ks, vs, tab, lens, Hkv, spec.fp32_scale(),
-                                       nthreads=0, return_threads=True)
+                                       nthreads=0, return_threads=True, window=spec.window)
         else:
             _, used = oracle.decode(wl.q, kc, vc, tab, lens, Hkv, spec.fp32_scale(), dt,
-                                    nthreads=0, return_threads=True)
+                                    nthreads=0, return_threads=True, window=spec.window)
         passes += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -506,7 +508,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
@@ -576,6 +578,7 @@ def main():
             "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim, "block_size": 16,
             "kv_dtype": "int8 + f32 row scales" if spec.cache == "i8" else spec.dtype,
             "pool_blocks": int(wl.num_blocks),
+            "sliding_window": int(spec.window),
             "mean_context": round(mean_kv_tokens / spec.num_seqs, 1),
             "partition_tokens": g["part_tokens"], "replicas": args.replicas,
             "kernel": args.kernel, "seed": spec.seed,

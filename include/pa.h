@@ -191,6 +191,13 @@ typedef struct pa_decode_params {
    * the call's work.  The events are not read back by the library. */
   void *start_event;
   void *stop_event;
+  /* Sliding window ("LLM Inference Optimization: KV-Cache, PagedAttention,
+   * and GPU Memory Efficiency", Future Optimizations: token i attends to
+   * [i-W, i]).  0 = none.  W > 0: the query of sequence s, at position
+   * L-1, attends to positions max(0, L-1-W) .. L-1 (W+1 tokens, both ends
+   * included).  Table entries of blocks wholly before position L-1-W are
+   * never read (they may be -1 or stale); negative values are rejected. */
+  int32_t sliding_window;
 } pa_decode_params;
 
 /* Partition size (tokens) pa_decode will use for these parameters, 0 for the

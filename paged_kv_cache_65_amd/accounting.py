@@ -27,16 +27,30 @@ def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, elem_b
     return 2 * num_layers * num_kv_heads * head_dim * elem_bytes
 
 
+def attended(context_lens, window: int = 0):
+    """(tokens, blocks) a decode query reads per sequence: with a sliding window
+    W > 0 the positions L-1-W .. L-1 (clipped at 0) and the blocks holding them."""
+    lens = np.asarray(context_lens, dtype=np.int64)
+    blocks = -(-lens // BLOCK_SIZE)
+    if window <= 0:
+        return lens, blocks
+    first = np.maximum(lens - 1 - window, 0)
+    return np.where(lens > 0, lens - first, 0), np.where(lens > 0, blocks - first // BLOCK_SIZE, 0)
+
+
 def decode_algorithmic_bytes(context_lens, num_q_heads, num_kv_heads, head_dim, dtype,
-                             out_dtype, shared_tokens: int = 0, cache: str = "") -> dict:
+                             out_dtype, shared_tokens: int = 0, cache: str = "", window: int = 0) -> dict:
     """Bytes one paged decode launch must move.
 
     shared_tokens: tokens of a prefix whose blocks every sequence maps (counted
     once in 'kv_unique' and once per sequence in 'kv_logical').
     cache: "i8" for an INT8 cache (codes + per-row scales); q and out stay in
     dtype / out_dtype.
+    window: sliding window W (0 = none): only the attended rows and the table
+    entries of their blocks count.
     """
-    lens = np.asarray(context_lens, dtype=np.int64)
+    lens_all = np.asarray(context_lens, dtype=np.int64)
+    lens, blocks = attended(lens_all, window)
     eb = ELEM_BYTES[dtype]
     S = len(lens)
     if cache == "i8":
@@ -47,7 +61,7 @@ def decode_algorithmic_bytes(context_lens, num_q_heads, num_kv_heads, head_dim, 
     kv_unique = kv_logical - max(S - 1, 0) * shared_tokens * per_tok if shared_tokens else kv_logical
     q = S * num_q_heads * head_dim * eb
     out = S * num_q_heads * head_dim * ELEM_BYTES[out_dtype]
-    tables = 4 * int((-(-lens // BLOCK_SIZE)).sum())
+    tables = 4 * int(blocks.sum())
     ctx = 4 * S
     small = q + out + tables + ctx
     return {"kv_unique": kv_unique, "kv_logical": kv_logical, "q": q, "out": out,

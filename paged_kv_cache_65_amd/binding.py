@@ -45,7 +45,7 @@ class pa_decode_params(ctypes.Structure):
                 ("out_dtype", ctypes.c_int), ("partition_tokens", _I32), ("kernel", ctypes.c_int),
                 ("k_new", _P), ("v_new", _P), ("slot_mapping", _P),
                 ("q_dtype", ctypes.c_int), ("k_scales", _P), ("v_scales", _P),
-                ("start_event", _P), ("stop_event", _P)]
+                ("start_event", _P), ("stop_event", _P), ("sliding_window", _I32)]
 
 
 _lib = None
@@ -136,9 +136,10 @@ def _stream(stream):
 def make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
                        max_context_len, scale, partition_tokens=0, kernel="auto", k_new=None,
                        v_new=None, slot_mapping=None, k_scales=None, v_scales=None,
-                       start_event=None, stop_event=None):
+                       start_event=None, stop_event=None, sliding_window=0):
     """k_scales / v_scales: the float32 scale arrays of an int8 cache (else None).
-    start_event / stop_event: raw hipEvent_t handles (ints) or None."""
+    start_event / stop_event: raw hipEvent_t handles (ints) or None.
+    sliding_window: W > 0 attends positions L-1-W .. L-1 only; 0 = the whole context."""
     S, Hq, D = q.shape
     nb = k_cache.numel() // (num_kv_heads * BLOCK_SIZE * D)
     return pa_decode_params(
@@ -146,7 +147,8 @@ def make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens, num
         S, Hq, num_kv_heads, D, block_tables.shape[1] if block_tables.dim() == 2 else 0, nb,
         int(max_context_len), float(scale), _dtype_code(k_cache), _dtype_code(out),
         int(partition_tokens), KERNELS[kernel], _dev(k_new), _dev(v_new), _dev(slot_mapping),
-        _dtype_code(q), _dev(k_scales), _dev(v_scales), _event(start_event), _event(stop_event))
+        _dtype_code(q), _dev(k_scales), _dev(v_scales), _event(start_event), _event(stop_event),
+        int(sliding_window))
 
 
 def _event(ev):
@@ -169,7 +171,7 @@ def pa_decode_partition_tokens(params: pa_decode_params) -> int:
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
               max_context_len, scale, partition_tokens=0, kernel="auto", workspace=None,
               stream=None, k_new=None, v_new=None, slot_mapping=None, k_scales=None,
-              v_scales=None):
+              v_scales=None, sliding_window=0):
     """out <- paged decode attention (optionally appending k_new/v_new first).
     workspace: a uint8 device tensor of at least pa_decode_workspace_bytes()
     bytes (no initialization needed), or None to allocate one.  For an int8
@@ -177,7 +179,8 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads
     import torch
     params = make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens,
                                 num_kv_heads, max_context_len, scale, partition_tokens, kernel,
-                                k_new, v_new, slot_mapping, k_scales, v_scales)
+                                k_new, v_new, slot_mapping, k_scales, v_scales,
+                                sliding_window=sliding_window)
     need = pa_decode_workspace_bytes(params)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

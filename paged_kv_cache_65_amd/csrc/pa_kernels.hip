@@ -163,13 +163,24 @@ struct DecodeArgs {
   const int64_t *slot_mapping;   // fused append: [S] slot of position L-1 (negative = no append)
   int32_t *ws_pre;               // balanced split: [S+1] blocks of the sequences before s
   int32_t num_seqs, num_q_heads, num_kv_heads, group, max_blocks, num_blocks, max_ctx, max_parts,
-      part_tokens, out_dtype, num_workers;
+      part_tokens, out_dtype, num_workers, window;
   float scale_log2;
 };
 
 __device__ inline bool ctx_valid(int L, const DecodeArgs &a) {
   return L >= 0 && L <= a.max_ctx && (int64_t)L <= (int64_t)a.max_blocks * kBS;
 }
+
+// Sliding window ("LLM Inference Optimization: KV-Cache, PagedAttention, and
+// GPU Memory Efficiency", Future Optimizations): the query at position L-1
+// sees positions L-1-W .. L-1 (clipped at 0); W <= 0: no window.  Blocks
+// before the one holding the first such position are never touched.
+__device__ inline int window_first_token(int L, int W) { return (W > 0 && L - 1 - W > 0) ? L - 1 - W : 0; }
+
+constexpr uint32_t kAllTokens = 0xFFFFu;
+
+// Tokens lo .. hi-1 of a block (0 <= lo < hi <= 16) as a bit mask.
+__device__ inline uint32_t token_mask(int lo, int hi) { return ((1u << hi) - 1u) & ~((1u << lo) - 1u); }
 
 // Per-wave online-softmax states meet here at the end of a partition.
 struct __align__(16) SmemBase {
@@ -384,17 +395,19 @@ struct MfmaWave {
     lo = u32x2_t{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
   }
 
-  // One block; `valid` = tokens of this block inside the context (1..16);
-  // new_tok >= 0: that token's K/V come from the staged new row.
-  __device__ void compute(Frag &f, int valid, float scale_log2, int lane, int new_tok,
+  // One block; bit t of `vm` set = token t of the block is attended (inside
+  // the context and the window); new_tok >= 0: that token's K/V come from
+  // the staged new row.
+  __device__ void compute(Frag &f, uint32_t vm, float scale_log2, int lane, int new_tok,
                           const uint32_t *knew, const uint32_t *vnew) {
     const int tq = lane / 16;
     if (new_tok >= 0) patch_new_token<2, NC>(f.k, f.v, new_tok, lane, knew, vnew);
-    if (valid < kBS) {
-      // Slots past the context may hold anything (NaN included): zero the V
-      // elements so 0 * V stays 0; scores are masked below.
-      const uint32_t lo = (4 * tq + 0 < valid ? 0x0000FFFFu : 0u) | (4 * tq + 1 < valid ? 0xFFFF0000u : 0u);
-      const uint32_t hi = (4 * tq + 2 < valid ? 0x0000FFFFu : 0u) | (4 * tq + 3 < valid ? 0xFFFF0000u : 0u);
+    const uint32_t mine = vm >> (4 * tq);  // this lane's 4 tokens in the low bits
+    if (vm != kAllTokens) {
+      // Slots outside the attended range may hold anything (NaN included):
+      // zero the V elements so 0 * V stays 0; scores are masked below.
+      const uint32_t lo = ((mine & 1u) ? 0x0000FFFFu : 0u) | ((mine & 2u) ? 0xFFFF0000u : 0u);
+      const uint32_t hi = ((mine & 4u) ? 0x0000FFFFu : 0u) | ((mine & 8u) ? 0xFFFF0000u : 0u);
 #pragma unroll
       for (int c = 0; c < NC; ++c) f.v[c] &= u32x4_t{lo, hi, lo, hi};
     }
@@ -404,9 +417,9 @@ struct MfmaWave {
     float s[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) s[v] = sc[v] * scale_log2;
-    if (valid < kBS) {
+    if (vm != kAllTokens) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) s[v] = (4 * tq + v < valid) ? s[v] : -INFINITY;
+      for (int v = 0; v < 4; ++v) s[v] = ((mine >> v) & 1u) ? s[v] : -INFINITY;
     }
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mx = max_xor32(max_xor16(mx));
@@ -581,9 +594,10 @@ struct MfmaWaveI8 : MfmaWave<QDT, D> {
              ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
   }
 
-  __device__ void compute(Frag &f, int valid, float scale_log2, int lane, int /*new_tok*/,
+  __device__ void compute(Frag &f, uint32_t vm, float scale_log2, int lane, int /*new_tok*/,
                           const uint32_t *, const uint32_t *) {
     const int tq = lane / 16;
+    const uint32_t mine = vm >> (4 * tq);
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -594,9 +608,9 @@ struct MfmaWaveI8 : MfmaWave<QDT, D> {
     float s[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) s[v] = sc[v] * f.ks[v] * scale_log2;
-    // tokens past the context: scores masked (their scales may be anything)
+    // tokens outside the attended range: scores masked (their scales may be anything)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s[v] = (4 * tq + v < valid) ? s[v] : -INFINITY;
+    for (int v = 0; v < 4; ++v) s[v] = ((mine >> v) & 1u) ? s[v] : -INFINITY;
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mx = max_xor32(max_xor16(mx));
     const bool bump = mx > this->m + kLazyLog2;
@@ -612,7 +626,7 @@ struct MfmaWaveI8 : MfmaWave<QDT, D> {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       p[v] = __builtin_amdgcn_exp2f(s[v] - this->m);
-      pw[v] = (4 * tq + v < valid) ? p[v] * f.vs[v] : 0.f;
+      pw[v] = ((mine >> v) & 1u) ? p[v] * f.vs[v] : 0.f;
     }
     this->l += (p[0] + p[1]) + (p[2] + p[3]);
     u32x2_t ph, pl;
@@ -698,7 +712,7 @@ struct ValuWave {
     }
   }
 
-  __device__ void compute(Frag &f, int valid, float scale_log2, int lane, int new_tok, Smem &sm,
+  __device__ void compute(Frag &f, uint32_t vm, float scale_log2, int lane, int new_tok, Smem &sm,
                           int w, int G) {
     const int r = lane % 16, tq = lane / 16;
     if (new_tok >= 0) patch_new_token<EB, NCF>(f.k, f.v, new_tok, lane, sm.knew, sm.vnew);
@@ -718,7 +732,7 @@ struct ValuWave {
           for (int e = 0; e < X; ++e) part = fmaf(qv[e], kf[c * X + e], part);
         }
         part = sum_xor32(sum_xor16(part));
-        const float sv = (r < valid) ? part * scale_log2 : -INFINITY;
+        const float sv = ((vm >> r) & 1u) ? part * scale_log2 : -INFINITY;
         const float mx = row_max16(sv);
         const float m_new = fmaxf(m[h], mx);
         const float alpha = exp2_neg(m[h] - m_new);
@@ -739,7 +753,7 @@ struct ValuWave {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float x = elem(f.v[c], sub * 4 + i);
-          vf[c * (X / 4) + sub][i] = (4 * tq + i < valid) ? x : 0.f;
+          vf[c * (X / 4) + sub][i] = ((vm >> (4 * tq + i)) & 1u) ? x : 0.f;
         }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -813,10 +827,12 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
   // Loads that do not depend on the context length go out together with it:
   // the q fragments, and this wave's first 64 block ids (speculative: only
   // bounded by the table row; validated once the length is known).
+  // Partitions split the attended blocks: from the block holding the
+  // window's first position (block 0 without a window) to the last one.
   const int L = a.context_lens[s];
-  const int blk0 = (int)((int64_t)p * a.part_tokens / kBS);
+  int blk0 = (int)((int64_t)p * a.part_tokens / kBS);
   const int32_t *trow = a.block_tables + (int64_t)s * a.max_blocks + blk0;
-  const int ids_first = (int64_t)blk0 + wu + lane * kWaves < a.max_blocks ? trow[wu + lane * kWaves] : 0;
+  int ids_first = (int64_t)blk0 + wu + lane * kWaves < a.max_blocks ? trow[wu + lane * kWaves] : 0;
   W wave;
   wave.init(a, sm, s, g, lane);
   if (!ctx_valid(L, a)) {
@@ -827,12 +843,20 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
     if (p == 0) write_rows<D>(a, s, h0, G, 0.f);
     return;
   }
-  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+  const int first = window_first_token(L, a.window);
+  const int jb = first / kBS;
+  const int nparts = (L - jb * kBS + a.part_tokens - 1) / a.part_tokens;
   if (p >= nparts) return;
-  const int tok0 = p * a.part_tokens;
+  if (jb > 0) {  // the speculative id load above assumed no window
+    blk0 += jb;
+    trow += jb;
+    ids_first = (int64_t)blk0 + wu + lane * kWaves < a.max_blocks ? trow[wu + lane * kWaves] : 0;
+  }
+  const int tok0 = blk0 * kBS;
   const int tok1 = min(L, tok0 + a.part_tokens);
   const int nblk = (tok1 - tok0 + kBS - 1) / kBS;
   const int last_valid = tok1 - (blk0 + nblk - 1) * kBS;
+  const int first_lo = p == 0 ? first - jb * kBS : 0;  // masked tokens of the partition's block 0
 
   wave.stage(a, sm, s, g, tid);
   if constexpr (!kMfma) __syncthreads();  // q staged in LDS
@@ -903,12 +927,12 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
         refill(fr[(b + NB - 1) % NB], i + NB - 1);
         if (i < nc) {
           const int j = wu + (c0 + i) * kWaves;
-          const int valid = (j == nblk - 1) ? last_valid : kBS;
+          const uint32_t vm = token_mask(j == 0 ? first_lo : 0, (j == nblk - 1) ? last_valid : kBS);
           const int nt = (j == nblk - 1) ? new_tok : -1;
           if constexpr (kMfma)
-            wave.compute(fr[b], valid, a.scale_log2, lane, nt, sm.knew, sm.vnew);
+            wave.compute(fr[b], vm, a.scale_log2, lane, nt, sm.knew, sm.vnew);
           else
-            wave.compute(fr[b], valid, a.scale_log2, lane, nt, sm, w, G);
+            wave.compute(fr[b], vm, a.scale_log2, lane, nt, sm, w, G);
         }
       }
     }
@@ -974,9 +998,15 @@ struct __align__(16) SmemBalanced {
   uint32_t q[kQLds / 4];                        // q rows of pairs qbase .. qbase+nq-1
   uint32_t knew[kBWaves][kAppendMax][kDMax / 2];  // fused append: new K / V rows (16-bit)
   uint32_t vnew[kBWaves][kAppendMax][kDMax / 2];
-  int32_t pre[kSeqMax + 1];                      // blocks of the sequences before s
-  int32_t len[kSeqMax];                          // context length (0 when invalid)
+  int32_t pre[kSeqMax + 1];                      // attended blocks of the sequences before s
+  int32_t len[kSeqMax];                          // context length (-1 when invalid)
 };
+
+// Attended blocks of a context of L tokens (L = -1: invalid, none): from the
+// block holding the window's first position to the one holding position L-1.
+__device__ inline int attended_blocks(int L, int W) {
+  return L > 0 ? (L + kBS - 1) / kBS - window_first_token(L, W) / kBS : 0;
+}
 
 // Floats of one wave's parking area: G rows of D, then m and l per row
 // (rounded to 16 bytes).
@@ -1043,7 +1073,7 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
     const int per = (S + 63) / 64;
     const int s0 = min(S, lane * per), s1 = min(S, s0 + per);
     int sum = 0;
-    for (int s = s0; s < s1; ++s) sum += (sm.len[s] + kBS - 1) / kBS;
+    for (int s = s0; s < s1; ++s) sum += attended_blocks(sm.len[s], a.window);
     int inc = sum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -1053,7 +1083,7 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
     int run = inc - sum;
     for (int s = s0; s < s1; ++s) {
       sm.pre[s] = run;
-      run += (sm.len[s] + kBS - 1) / kBS;
+      run += attended_blocks(sm.len[s], a.window);
     }
     if (lane == 63) sm.pre[S] = inc;
   }
@@ -1084,7 +1114,8 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
     const int s = seq_of_block(sm, u / Hkv, S);
     const int nb = sm.pre[s + 1] - sm.pre[s];
     const int off = u - Hkv * sm.pre[s];
-    id_first = a.block_tables[(int64_t)s * a.max_blocks + off % nb];
+    const int jb = window_first_token(sm.len[s], a.window) / kBS;
+    id_first = a.block_tables[(int64_t)s * a.max_blocks + jb + off % nb];
   }
 
   // q rows of the pairs this workgroup touches (as many as fit), contiguous in q.
@@ -1120,6 +1151,7 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
     const int off = u - Hkv * sm.pre[s];
     const int g = off / nb, j = off - g * nb;
     const int L = sm.len[s];
+    const int jb = window_first_token(L, a.window) / kBS;  // attended block j is table entry jb + j
     const bool pend = j == nb - 1;
     // Fused append: the unit holding position L-1 of a pair takes the new
     // token.  At most kAppendMax such units per chunk (the chunk ends early).
@@ -1134,9 +1166,9 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
         amask &= (1ull << nc) - 1;
       }
     }
-    int id = c0 == u0 ? id_first : a.block_tables[(int64_t)s * a.max_blocks + j];
+    int id = c0 == u0 ? id_first : a.block_tables[(int64_t)s * a.max_blocks + jb + j];
     id = lane < nc ? id : 0;
-    uint32_t meta = (uint32_t)(pend ? L - (nb - 1) * kBS : kBS) | (j == 0 ? kUPairStart : 0u) |
+    uint32_t meta = (uint32_t)(pend ? L - (jb + nb - 1) * kBS : kBS) | (j == 0 ? kUPairStart : 0u) |
                     (pend ? kUPairEnd : 0u) | (u == u0 || j == 0 ? kUFirst : 0u) |
                     (u == u1 - 1 || pend ? kULast : 0u);
     // Cache rows of this chunk's appended tokens, written after its stream
@@ -1231,7 +1263,11 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
           bad |= (mt & kUBad) != 0;
           const int nt = (mt & kUNew) ? (int)((mt >> kUNewTokShift) & 15) : -1;
           const int k = (mt >> kUNewIdxShift) & 3;
-          wave.compute(fr[b], (int)(mt & kUValid), a.scale_log2, lane, nt, sm.knew[wu][k], sm.vnew[wu][k]);
+          // The window's first block masks the tokens before its first position.
+          const int lo = (a.window > 0 && (mt & kUPairStart))
+                             ? window_first_token(sm.len[pq / Hkv], a.window) % kBS : 0;
+          wave.compute(fr[b], token_mask(lo, (int)(mt & kUValid)), a.scale_log2, lane, nt, sm.knew[wu][k],
+                       sm.vnew[wu][k]);
           if (mt & kULast) {  // (a segment may go on into the next chunk)
             const bool wh = whole && (mt & kUPairEnd);
             if (c0 + i == u1 - 1 || parked) {  // (one parking place: a third segment stores)
@@ -1347,7 +1383,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_kernel(DecodeArgs a
   const int s = (int)(row / a.num_q_heads);
   const int L = a.context_lens[s];
   if (!ctx_valid(L, a)) return;
-  const int np = (L + a.part_tokens - 1) / a.part_tokens;
+  const int skip = window_first_token(L, a.window) / kBS * kBS;  // tokens of the unattended blocks
+  const int np = (L - skip + a.part_tokens - 1) / a.part_tokens;
   if (np <= 1) return;
   merge_row<D>(a, row, a.ws_ml + row * a.max_parts * 2, 2, a.ws_acc + row * a.max_parts * D, D, np, lane);
 }
@@ -1547,6 +1584,8 @@ pa_status validate(const pa_decode_params *p) {
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: device pointers must be 16-byte aligned");
   if (!(std::isfinite(p->scale)))
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: scale must be finite");
+  if (p->sliding_window < 0)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: sliding_window must be >= 0 (0 = none)");
   return PA_OK;
 }
 
@@ -1791,6 +1830,7 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
   a.part_tokens = pt;
   a.out_dtype = p->out_dtype;
   a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  a.window = p->sliding_window;
   return PA_OK;
 }
 

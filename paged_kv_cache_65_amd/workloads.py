@@ -54,6 +54,8 @@ class Spec:
     scale: Optional[float] = None        # None = 1/sqrt(head_dim) rounded to fp32
     cache: str = ""                      # cache type when it differs from dtype: "i8"
                                          # (int8 codes + per-row scales; q, rows, out in dtype)
+    window: int = 0                      # sliding window W (0 = none): the query at L-1
+                                         # attends to positions L-1-W .. L-1
 
     @property
     def group(self) -> int:
@@ -65,7 +67,8 @@ class Spec:
 
 
 def named(n: int) -> Spec:
-    """The measured workloads (1-based; 6 is workload 3 over an INT8 cache)."""
+    """The measured workloads (1-based; 6 is workload 3 over an INT8 cache; 7 is a
+    Mistral-7B-shaped batch under a 4096-token sliding window)."""
     if n == 1:
         return Spec("tiny-fp32-mha-d64", 1, "f32", "f32", 4, 4, 4, 64, 64,
                     lens=[1, 17, 33, 100], scale=1.0 / 8.0)
@@ -84,6 +87,9 @@ def named(n: int) -> Spec:
     if n == 6:  # workload 3 with an INT8 cache (rows quantized on append)
         return Spec("llama70b-gqa8-int8kv-b64-l128to4096", 3, "bf16", "bf16", 64, 64, 8, 128,
                     20000, len_range=(128, 4096), cache="i8")
+    if n == 7:  # GQA 32/8 heads, D = 128, contexts past the window
+        return Spec("mistral7b-gqa4-bf16-b32-l4kto16k-sw4096", 7, "bf16", "bf16", 32, 32, 8, 128,
+                    0, len_range=(4096, 16384), window=4096)
     raise ValueError(f"no workload {n}")
 
 
@@ -124,9 +130,21 @@ def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
         return x
     if dtype == "f16":
         return x.astype(np.float16)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    # bf16: add 0x7FFF plus the lowest kept bit, keep the high half.  In
+    # chunks, in uint32 (the only inputs that wrap are negative NaNs with
+    # large payloads, which wrap to 0 as the uint16 conversion would).
+    u = x.view(np.uint32).reshape(-1)
+    out = np.empty(u.shape, np.uint16)
+    step = 1 << 22
+    for i in range(0, u.size, step):
+        c = u[i:i + step]
+        t = c >> 16
+        t &= 1
+        t += 0x7FFF
+        t += c
+        t >>= 16
+        out[i:i + step] = t
+    return out.reshape(x.shape)
 
 
 def _normals(rng, shape, dtype):

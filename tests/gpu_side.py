@@ -125,10 +125,12 @@ def tables(st: GpuState, max_blocks: int, device="cuda"):
 
 
 def decode(wl, st: GpuState, max_blocks: int, out_dtype=None, kernel="auto", partition_tokens=None,
-           q=None, lens_host=None):
+           q=None, lens_host=None, window=0, tables_override=None):
     spec = wl.spec
     dev = st.k_cache.device
     tab_d, lens_d, _, lens_h = tables(st, max_blocks, dev)
+    if tables_override is not None:
+        tab_d = torch.from_numpy(tables_override).to(dev)
     qd = to_device(wl.q, spec.dtype, dev) if q is None else q
     od = out_dtype or spec.out_dtype
     out = torch.empty(qd.shape, dtype=TORCH[od], device=dev)
@@ -136,5 +138,5 @@ def decode(wl, st: GpuState, max_blocks: int, out_dtype=None, kernel="auto", par
     max_ctx = int(lens_h.max()) if len(lens_h) else 0
     pa.pa_decode(out, qd, st.k_cache, st.v_cache, tab_d, lens_d, spec.num_kv_heads, max_ctx,
                  spec.fp32_scale(), partition_tokens=pt, kernel=kernel, k_scales=st.k_scales,
-                 v_scales=st.v_scales)
+                 v_scales=st.v_scales, sliding_window=window)
     return out

@@ -36,3 +36,21 @@ def test_decode_bytes_single_layer_and_shared_prefix():
     assert sh["kv_logical"] == (522 + 532) * per_tok
     assert sh["kv_unique"] == (512 + 30) * per_tok
     assert acc.decode_flops([3, 5], 4, 64) == 4 * 64 * 4 * 8
+
+
+def test_windowed_tokens_and_blocks_hand_counted():
+    # L = 5, W = 2: positions 2..4 (3 tokens) in block 0.  L = 40, W = 20:
+    # positions 19..39 (21 tokens) in blocks 1, 2.  L = 17, W = 0: no window,
+    # 17 tokens in 2 blocks.  L = 0: nothing.  L = 33, W = 16: positions
+    # 16..32 (17 tokens) in blocks 1, 2.
+    toks, blks = acc.attended([5, 40, 17, 0, 33], window=0)
+    assert toks.tolist() == [5, 40, 17, 0, 33] and blks.tolist() == [1, 3, 2, 0, 3]
+    toks, blks = acc.attended([5, 40, 0, 33], window=2)  # L = 33: positions 30..32, blocks 1 and 2
+    assert toks.tolist() == [3, 3, 0, 3] and blks.tolist() == [1, 1, 0, 2]
+    toks, blks = acc.attended([40, 33], window=20)
+    assert toks.tolist() == [21, 21] and blks.tolist() == [2, 3]
+    toks, blks = acc.attended([33], window=16)
+    assert toks.tolist() == [17] and blks.tolist() == [2]
+    b = acc.decode_algorithmic_bytes([40, 33], 8, 2, 64, "bf16", "f32", window=20)
+    assert b["kv_unique"] == (21 + 21) * 2 * 2 * 64 * 2
+    assert b["tables"] == 4 * (2 + 3)

@@ -267,16 +267,16 @@ def _named_case(n, sample=None, steps=0, kernels=("auto",)):
     wl, gst, ost = _both(spec, steps)
     mb = oracle_side.max_blocks_for(wl, steps)
     subset = sample
-    ref = oracle_side.decode(wl, ost, mb, seq_subset=subset)
+    ref = oracle_side.decode(wl, ost, mb, seq_subset=subset, window=spec.window)
     for kern in kernels:
-        out = gpu_side.decode(wl, gst, mb, out_dtype="f32", kernel=kern)
+        out = gpu_side.decode(wl, gst, mb, out_dtype="f32", kernel=kern, window=spec.window)
         got = _f32(out)
         if subset is not None:
             got = got[subset]
         err = np.max(np.abs(got - ref))
         _say(f"  {spec.name} kernel={kern} max_abs_err={err:.3e}")
         assert err <= TOL[spec.dtype], (kern, err)
-        o16 = gpu_side.decode(wl, gst, mb, kernel=kern)
+        o16 = gpu_side.decode(wl, gst, mb, kernel=kern, window=spec.window)
         if spec.out_dtype != "f32":
             assert torch.equal(o16.cpu().view(torch.int16),
                                out.cpu().to(gpu_side.TORCH[spec.out_dtype]).view(torch.int16))
@@ -293,6 +293,11 @@ def test_workload_2_llama7b_mha_fp16():
 
 def test_workload_3_llama70b_gqa_bf16_sampled():
     _named_case(3, sample=[0, 7, 21, 40, 63], kernels=("auto", "valu"))
+
+
+def test_workload_7_sliding_window_sampled():
+    # Mistral-7B-shaped batch, contexts 4096..16384 under a 4096-token window
+    _named_case(7, sample=[0, 9, 17, 31], kernels=("auto", "valu"))
 
 
 def test_workload_4_shared_prefix_sampled():

@@ -1,0 +1,153 @@
+"""GPU parity of sliding-window decode (sliding_window = W > 0) against the oracle.
+
+The query at position L-1 attends to positions max(0, L-1-W) .. L-1; blocks
+wholly before that are never read.  Bars as for the full decode: max-abs
+<= 1e-5 (fp32 caches), <= 2e-3 (fp16/bf16 and INT8 with 16-bit q).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from paged_kv_cache_65_amd import binding as pa  # noqa: E402
+from paged_kv_cache_65_amd import workloads  # noqa: E402
+from tests import gpu_side, oracle_side  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+# lengths around block edges for the windows below: first attended position
+# at a block start, at a block end, inside; windows covering everything
+LENS = (1, 2, 16, 17, 18, 31, 32, 33, 47, 48, 49, 100, 129, 250, 600, 1024, 1500)
+WINDOWS = (1, 15, 16, 17, 31, 100, 511, 4096)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(oracle_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.lib()
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _f32(out):
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def _both(spec):
+    wl = workloads.generate(spec)
+    return wl, gpu_side.build(wl), oracle_side.build(wl)
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,kern,pt", [
+    ("bf16", 128, 16, 2, "auto", 0),      # balanced split
+    ("f16", 64, 8, 8, "auto", 0),         # balanced split, G = 1
+    ("bf16", 128, 8, 1, "mfma", 16),      # partitions of one block
+    ("bf16", 128, 8, 2, "mfma", 256),
+    ("f32", 64, 4, 2, "auto", 64),        # VALU kernel (fp32 cache)
+    ("bf16", 64, 12, 4, "valu", 0),
+])
+def test_window_matches_oracle(dtype, D, Hq, Hkv, kern, pt):
+    spec = workloads.custom(seed=80, dtype=dtype, lens=LENS, num_q_heads=Hq, num_kv_heads=Hkv,
+                            head_dim=D)
+    wl, gst, ost = _both(spec)
+    mb = oracle_side.max_blocks_for(wl)
+    for W in WINDOWS:
+        _say(f"[case] window W={W} {dtype} D={D} Hq={Hq} Hkv={Hkv} kernel={kern} pt={pt}")
+        out = gpu_side.decode(wl, gst, mb, out_dtype="f32", kernel=kern, partition_tokens=pt, window=W)
+        ref = oracle_side.decode(wl, ost, mb, window=W)
+        err = np.max(np.abs(_f32(out) - ref))
+        assert err <= TOL[dtype], (W, err)
+
+
+def test_window_covering_every_context_is_the_full_decode_bitwise():
+    spec = workloads.custom(seed=81, dtype="bf16", lens=LENS, num_q_heads=16, num_kv_heads=2,
+                            head_dim=128)
+    wl, gst, ost = _both(spec)
+    mb = oracle_side.max_blocks_for(wl)
+    for pt in (0, 64):
+        full = gpu_side.decode(wl, gst, mb, out_dtype="f32", partition_tokens=pt)
+        for W in (max(LENS) - 1, 10 ** 6):
+            assert torch.equal(gpu_side.decode(wl, gst, mb, out_dtype="f32", partition_tokens=pt, window=W),
+                               full), (pt, W)
+
+
+@pytest.mark.parametrize("pt", [0, 16, 128])
+def test_table_entries_before_the_window_are_never_read(pt):
+    # entries of blocks wholly before the window set to -1 or outside the pool:
+    # a read would make the row NaN (bad id); the output must not change
+    spec = workloads.custom(seed=82, dtype="bf16", lens=LENS, num_q_heads=8, num_kv_heads=2,
+                            head_dim=128)
+    wl, gst, ost = _both(spec)
+    mb = oracle_side.max_blocks_for(wl)
+    W = 40
+    ref = gpu_side.decode(wl, gst, mb, out_dtype="f32", partition_tokens=pt, window=W)
+    _, _, tab, lens = gpu_side.tables(gst, mb)
+    bad = tab.copy()
+    for s, L in enumerate(lens):
+        first = max(0, int(L) - 1 - W)
+        bad[s, :first // 16] = -1 if s % 2 else 10 ** 9
+    got = gpu_side.decode(wl, gst, mb, out_dtype="f32", partition_tokens=pt, window=W, tables_override=bad)
+    assert torch.equal(got, ref)
+    assert torch.isfinite(got).all()
+
+
+def test_int8_cache_window_matches_oracle():
+    spec = workloads.custom(seed=83, dtype="bf16", lens=LENS, num_q_heads=16, num_kv_heads=2,
+                            head_dim=128)
+    spec = type(spec)(**{**spec.__dict__, "cache": "i8"})
+    wl, gst, ost = _both(spec)
+    mb = oracle_side.max_blocks_for(wl)
+    for W in (1, 16, 17, 100, 4096):
+        _say(f"[case] int8 window W={W}")
+        out = gpu_side.decode(wl, gst, mb, out_dtype="f32", window=W)
+        ref = oracle_side.decode(wl, ost, mb, window=W)
+        assert np.max(np.abs(_f32(out) - ref)) <= 2e-3, W
+
+
+@pytest.mark.parametrize("pt", [0, 32])
+def test_window_with_fused_append(pt):
+    spec = workloads.custom(seed=84, dtype="bf16", lens=(5, 40, 16, 300, 33, 64), num_q_heads=8,
+                            num_kv_heads=2, head_dim=128, decode_steps=20)
+    wl, gst, ost = _both(spec)
+    mb = oracle_side.max_blocks_for(wl)
+    q = gpu_side.to_device(wl.q, "bf16")
+    W = 17
+    for step in range(spec.decode_steps):
+        slots, cows = gst.pool.seq_append_batch(gst.seq_ids)
+        assert not len(cows)
+        oracle_side.advance(wl, ost, step)
+        tab_d, lens_d, _, lh = gpu_side.tables(gst, mb)
+        out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        pa.pa_decode(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, 2, int(lh.max()), spec.fp32_scale(),
+                     partition_tokens=pt, k_new=gpu_side.to_device(wl.step_k[step], "bf16"),
+                     v_new=gpu_side.to_device(wl.step_v[step], "bf16"),
+                     slot_mapping=torch.from_numpy(slots.copy()).cuda(), sliding_window=W)
+        ref = oracle_side.decode(wl, ost, mb, window=W)
+        err = np.max(np.abs(_f32(out) - ref))
+        assert err <= 2e-3, (step, err)
+
+
+def test_balanced_window_over_a_long_mixed_batch():
+    lens = tuple(int(x) for x in np.random.default_rng(85).integers(1, 3000, 96))
+    spec = workloads.custom(seed=85, dtype="bf16", lens=lens, num_q_heads=32, num_kv_heads=4,
+                            head_dim=128)
+    wl, gst, ost = _both(spec)
+    mb = oracle_side.max_blocks_for(wl)
+    for W in (255, 1000):
+        _say(f"[case] balanced mixed batch window W={W}")
+        out = gpu_side.decode(wl, gst, mb, out_dtype="f32", window=W)
+        ref = oracle_side.decode(wl, ost, mb, window=W)
+        assert np.max(np.abs(_f32(out) - ref)) <= 2e-3, W
+
+
+def test_negative_window_is_rejected():
+    spec = workloads.custom(seed=86, dtype="bf16", lens=(10,), num_q_heads=2, num_kv_heads=1, head_dim=64)
+    wl, gst, ost = _both(spec)
+    with pytest.raises(pa.PaError):
+        gpu_side.decode(wl, gst, oracle_side.max_blocks_for(wl), window=-1)
