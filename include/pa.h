@@ -276,6 +276,36 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst_pa
                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                          int32_t num_blocks, pa_dtype dtype, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Swap copies: whole blocks (all heads, K and V) between two pools of the
+ * same tile layout, for preemption by swapping ("Inference serving: the
+ * KV-cache machine", section "Paged KV": a block table lets a sequence's
+ * private blocks be swapped out and reloaded anywhere; the Lab B loop swaps a
+ * victim to CPU DRAM and back into new blocks).  Either pool may be device
+ * memory or pinned host memory the GPU can address (hipHostMalloc, or a
+ * PyTorch tensor made with pin_memory=True).  For each pair i, block
+ * src_dst_pairs[2i] of the source pool is copied to block src_dst_pairs[2i+1]
+ * of the destination pool; pairs outside [0, src_num_blocks) or
+ * [0, dst_num_blocks) are skipped.
+ *   src_dst_pairs int32 [num_pairs][2], device or pinned host memory;
+ *                 num_pairs <= 65535 per call.
+ * Asynchronous like every device call: a host-side pool is complete after
+ * the stream passes the call, and must not be changed before then.  Swap a
+ * sequence out with pa_seq_swap_out, then copy its released blocks before
+ * anything on the stream writes into them again (stream order suffices).
+ * ------------------------------------------------------------------------ */
+pa_status pa_swap_blocks(const void *src_k, const void *src_v, int32_t src_num_blocks, void *dst_k,
+                         void *dst_v, int32_t dst_num_blocks, const int32_t *src_dst_pairs,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                         void *stream);
+
+/* pa_swap_blocks for INT8 caches: codes and the per-row scales of every head. */
+pa_status pa_swap_blocks_int8(const int8_t *src_k, const int8_t *src_v, const float *src_k_scales,
+                              const float *src_v_scales, int32_t src_num_blocks, int8_t *dst_k,
+                              int8_t *dst_v, float *dst_k_scales, float *dst_v_scales,
+                              int32_t dst_num_blocks, const int32_t *src_dst_pairs, int32_t num_pairs,
+                              int32_t num_kv_heads, int32_t head_dim, void *stream);
+
 /* pa_copy_blocks for an INT8 cache: codes and scales of every head. */
 pa_status pa_copy_blocks_int8(int8_t *k_cache, int8_t *v_cache, float *k_scales, float *v_scales,
                               const int32_t *src_dst_pairs, int32_t num_pairs, int32_t num_kv_heads,
@@ -330,6 +360,24 @@ pa_status pa_seq_append(pa_block_pool *pool, int32_t seq, int32_t n_tokens, int6
 pa_status pa_seq_append_batch(pa_block_pool *pool, const int32_t *seq_ids, int32_t n,
                               int64_t *slots, int32_t *cow_pairs, int32_t *num_cow);
 pa_status pa_seq_free(pa_block_pool *pool, int32_t seq);
+/* Preemption by swapping ("Inference serving: the KV-cache machine",
+ * section "Paged KV" and Lab B).  pa_seq_swap_out releases the sequence's
+ * private blocks -- the longest suffix of its table whose blocks it holds
+ * alone (refcount 1) -- front to back, writes their ids in table order to
+ * blocks_out[capacity] and their count to *n_out, and keeps the shared
+ * blocks and the token count.  ceil(num_tokens / 16) is always enough
+ * capacity.  Copy the blocks out (pa_swap_blocks) before they are written
+ * again.  A swapped-out sequence cannot be appended to, forked or exported;
+ * pa_seq_free releases its resident blocks.  pa_seq_swap_in takes that many
+ * fresh blocks from the free stack, appends them to the table and writes
+ * their ids to blocks_out (all or nothing: PA_ERR_OOM leaves the pool as it
+ * was); copy the contents back into them.  pa_seq_swapped_blocks: the count
+ * held outside for a swapped-out sequence, else -1. */
+pa_status pa_seq_swap_out(pa_block_pool *pool, int32_t seq, int32_t *blocks_out, int32_t capacity,
+                          int32_t *n_out);
+pa_status pa_seq_swap_in(pa_block_pool *pool, int32_t seq, int32_t *blocks_out, int32_t capacity,
+                         int32_t *n_out);
+int32_t pa_seq_swapped_blocks(const pa_block_pool *pool, int32_t seq);
 /* Token count of a sequence, or -1 for an invalid id. */
 int32_t pa_seq_num_tokens(const pa_block_pool *pool, int32_t seq);
 /* Tables [n][max_blocks] padded with -1, and context lengths [n]. */

@@ -138,6 +138,19 @@ def copy_blocks(k_cache, v_cache, pairs, num_kv_heads, head_dim, dtype):
                                num_kv_heads, head_dim, _DTYPES[dtype])
 
 
+def swap_blocks(src, dst, pairs, per_block):
+    """Whole-block copies between two pools of one array each (a K or V cache,
+    or a scale array): block p of src -> block q of dst for each (p, q), with
+    per_block elements per block; pairs outside either pool are skipped.  The
+    swap copies of preemption ("Inference serving: the KV-cache machine",
+    section "Paged KV")."""
+    s = src.reshape(-1, per_block)
+    d = dst.reshape(-1, per_block)
+    for p, q in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        if 0 <= p < len(s) and 0 <= q < len(d):
+            d[q] = s[p]
+
+
 def decode(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads, scale, dtype,
            nthreads=0, return_threads=False, window=0):
     """fp64 paged decode; q is [S][Hq][D] in the cache type.  Returns float64 [S][Hq][D].

@@ -29,6 +29,16 @@ What the pages fix, and the readings taken where they leave a choice:
     unchanged.
   * Freeing a sequence decrements its blocks in table order (front to back).
   * Sequence ids: the lowest id not currently in use.
+  * Preemption by swapping ("Inference serving ...", section "Paged KV" -- a
+    block table lets the private blocks be swapped out and reloaded anywhere --
+    and the Lab B loop): swap-out returns the victim's private blocks to the
+    pool, front to back, and keeps the shared ones; swap-in takes that many
+    fresh blocks from the free stack and appends them to the table.  Readings
+    taken: the private blocks are the longest suffix of the table whose
+    blocks have refcount 1 (blocks are shared only through forks, which share
+    a prefix); swap-in is all-or-nothing; a swapped-out sequence keeps its
+    token count and cannot be appended to, forked or exported until swapped
+    back in; freeing it releases its resident blocks.
 """
 from __future__ import annotations
 
@@ -56,7 +66,7 @@ class PoolModel:
         self.block_size = block_size
         self.free = order                  # top of the stack = last element
         self.refcount = [0] * num_blocks
-        self.seqs = {}                     # id -> [table(list), num_tokens]
+        self.seqs = {}                     # id -> [table(list), num_tokens, swapped blocks or None]
 
     # ---- blocks -----------------------------------------------------------
     def num_free(self) -> int:
@@ -95,21 +105,27 @@ class PoolModel:
             raise PoolError(f"no sequence {sid}")
         return self.seqs[sid]
 
+    def _resident(self, sid: int):
+        s = self._seq(sid)
+        if s[2] is not None:
+            raise PoolError(f"sequence {sid} is swapped out")
+        return s
+
     def seq_create(self) -> int:
         sid = self._new_id()
-        self.seqs[sid] = [[], 0]
+        self.seqs[sid] = [[], 0, None]
         return sid
 
     def seq_fork(self, parent: int) -> int:
-        table, ntok = self._seq(parent)
+        table, ntok, _ = self._resident(parent)
         sid = self._new_id()
         for b in table:
             self.refcount[b] += 1
-        self.seqs[sid] = [list(table), ntok]
+        self.seqs[sid] = [list(table), ntok, None]
         return sid
 
     def _blocks_needed(self, sid: int, n: int) -> int:
-        table, ntok = self.seqs[sid]
+        table, ntok, _ = self.seqs[sid]
         if n == 0:
             return 0
         need = 0
@@ -125,10 +141,10 @@ class PoolModel:
         """Append n tokens.  Returns (slots, cow) with cow = (src, dst) or None."""
         if n < 0:
             raise PoolError("negative token count")
-        self._seq(sid)
+        self._resident(sid)
         if self._blocks_needed(sid, n) > len(self.free):
             raise OutOfBlocks("pool exhausted")
-        table, ntok = self.seqs[sid]
+        table, ntok, _ = self.seqs[sid]
         cow = None
         slots = []
         for _ in range(n):
@@ -152,7 +168,7 @@ class PoolModel:
             raise PoolError("duplicate sequence in batch")
         need = 0
         for sid in sids:
-            self._seq(sid)
+            self._resident(sid)
             need += self._blocks_needed(sid, 1)
         if need > len(self.free):
             raise OutOfBlocks("pool exhausted")
@@ -165,10 +181,42 @@ class PoolModel:
         return slots, cows
 
     def seq_free(self, sid: int):
-        table, _ = self._seq(sid)
+        table = self._seq(sid)[0]
         for b in table:
             self.decref(b)
         del self.seqs[sid]
+
+    def seq_swap_out(self, sid: int):
+        """Releases the private blocks (table order) and returns their ids; the
+        caller copies their contents out before the pool hands them again."""
+        table = self._resident(sid)[0]
+        k = 0
+        while k < len(table) and self.refcount[table[len(table) - 1 - k]] == 1:
+            k += 1
+        out = table[len(table) - k:]
+        for b in out:
+            self.decref(b)
+        del table[len(table) - k:]
+        self.seqs[sid][2] = k
+        return out
+
+    def seq_swap_in(self, sid: int):
+        """Appends fresh blocks for the swapped-out ones and returns their ids
+        (table order); the caller copies the contents back into them."""
+        s = self._seq(sid)
+        if s[2] is None:
+            raise PoolError(f"sequence {sid} is not swapped out")
+        if s[2] > len(self.free):
+            raise OutOfBlocks("pool exhausted")
+        new = [self.alloc() for _ in range(s[2])]
+        s[0].extend(new)
+        s[2] = None
+        return new
+
+    def seq_swapped_blocks(self, sid: int) -> int:
+        """Blocks held on the host for a swapped-out sequence, else -1."""
+        s = self._seq(sid)
+        return -1 if s[2] is None else s[2]
 
     def seq_num_tokens(self, sid: int) -> int:
         return self._seq(sid)[1]
@@ -180,7 +228,7 @@ class PoolModel:
         """Tables padded with -1 to max_blocks, and context lengths."""
         tables, lens = [], []
         for sid in sids:
-            table, ntok = self._seq(sid)
+            table, ntok, _ = self._resident(sid)
             if len(table) > max_blocks:
                 raise PoolError("table longer than max_blocks")
             tables.append(list(table) + [-1] * (max_blocks - len(table)))

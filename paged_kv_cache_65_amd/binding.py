@@ -72,6 +72,13 @@ def lib():
             "pa_reshape_and_cache_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                                          _I32, ctypes.c_int, _P]),
             "pa_copy_blocks_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P]),
+            "pa_swap_blocks": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I32, _P, _I32, _I32, _I32,
+                                              ctypes.c_int, _P]),
+            "pa_swap_blocks_int8": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _P, _P, _I32, _P,
+                                                   _I32, _I32, _I32, _P]),
+            "pa_seq_swap_out": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32]),
+            "pa_seq_swap_in": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32]),
+            "pa_seq_swapped_blocks": (_I32, [_P, _I32]),
             "pa_block_pool_create": (ctypes.c_int, [_I32, _I32, _PI32, ctypes.POINTER(_P)]),
             "pa_block_pool_destroy": (None, [_P]),
             "pa_block_pool_num_blocks": (_I32, [_P]),
@@ -121,6 +128,15 @@ def _dev(t):
         return None
     if not t.is_cuda:
         raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _gpu_addressable(t):
+    """A device tensor, or a pinned host tensor (the GPU addresses it directly)."""
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError("expected a device tensor or a pinned host tensor")
     if not t.is_contiguous():
         raise ValueError("expected a contiguous tensor")
     return ctypes.c_void_p(t.data_ptr())
@@ -235,6 +251,27 @@ def pa_copy_blocks_int8(k_cache, v_cache, k_scales, v_scales, src_dst_pairs, num
                                      _stream(stream)))
 
 
+def pa_swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs, num_kv_heads, head_dim, stream=None):
+    """Block copies between two pools (device or pinned host tensors of the cache
+    layout); src_dst_pairs int32 [n][2] on the device or pinned."""
+    n = src_dst_pairs.numel() // 2
+    per = num_kv_heads * BLOCK_SIZE * head_dim
+    _check(lib().pa_swap_blocks(_gpu_addressable(src_k), _gpu_addressable(src_v), src_k.numel() // per,
+                                _gpu_addressable(dst_k), _gpu_addressable(dst_v), dst_k.numel() // per,
+                                _gpu_addressable(src_dst_pairs), n, num_kv_heads, head_dim,
+                                _dtype_code(src_k), _stream(stream)))
+
+
+def pa_swap_blocks_int8(src_k, src_v, src_ks, src_vs, dst_k, dst_v, dst_ks, dst_vs, src_dst_pairs,
+                        num_kv_heads, head_dim, stream=None):
+    n = src_dst_pairs.numel() // 2
+    per = num_kv_heads * BLOCK_SIZE * head_dim
+    g = _gpu_addressable
+    _check(lib().pa_swap_blocks_int8(g(src_k), g(src_v), g(src_ks), g(src_vs), src_k.numel() // per,
+                                     g(dst_k), g(dst_v), g(dst_ks), g(dst_vs), dst_k.numel() // per,
+                                     g(src_dst_pairs), n, num_kv_heads, head_dim, _stream(stream)))
+
+
 def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, num_kv_heads, head_dim, stream=None):
     n = src_dst_pairs.numel() // 2
     nb = k_cache.numel() // (num_kv_heads * BLOCK_SIZE * head_dim)
@@ -327,6 +364,25 @@ class BlockPool:
 
     def seq_num_tokens(self, seq: int) -> int:
         return lib().pa_seq_num_tokens(self._h, seq)
+
+    def seq_swap_out(self, seq: int) -> np.ndarray:
+        """Releases the private blocks; returns their ids (table order)."""
+        cap = max(1, -(-self.seq_num_tokens(seq) // BLOCK_SIZE))
+        buf = np.empty(cap, dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(lib().pa_seq_swap_out(self._h, seq, buf.ctypes.data_as(_PI32), cap, ctypes.byref(n)))
+        return buf[:n.value].copy()
+
+    def seq_swap_in(self, seq: int) -> np.ndarray:
+        """Appends fresh blocks for the swapped-out ones; returns their ids."""
+        cap = max(1, self.seq_swapped_blocks(seq))
+        buf = np.empty(cap, dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(lib().pa_seq_swap_in(self._h, seq, buf.ctypes.data_as(_PI32), cap, ctypes.byref(n)))
+        return buf[:n.value].copy()
+
+    def seq_swapped_blocks(self, seq: int) -> int:
+        return lib().pa_seq_swapped_blocks(self._h, seq)
 
     def seq_export(self, seq_ids, max_blocks: int, tables_out=None, lens_out=None):
         ids = np.ascontiguousarray(seq_ids, dtype=np.int32)

@@ -1525,6 +1525,43 @@ __global__ __launch_bounds__(256) void pa_copy_blocks_kernel(uint8_t *k_cache, u
   }
 }
 
+// ---------------------------------------------------------------- swap copies
+// Block copies between two pools of the same tile layout, either of which
+// may be pinned host memory (preemption by swapping: "Inference serving: the
+// KV-cache machine", section "Paged KV").  Grid: (pair, chunk); a chunk is
+// kSwapVecs 16-byte vectors of the pair's K tile followed by its V tile, and
+// every thread has kSwapUnroll loads in flight before it stores (host memory
+// is far away).
+constexpr int kSwapThreads = 256;
+constexpr int kSwapUnroll = 4;
+constexpr int kSwapVecs = kSwapThreads * kSwapUnroll;
+
+__global__ __launch_bounds__(kSwapThreads) void pa_swap_blocks_kernel(
+    const uint8_t *src_k, const uint8_t *src_v, int32_t src_nb, uint8_t *dst_k, uint8_t *dst_v,
+    int32_t dst_nb, const int32_t *__restrict__ pairs, int64_t block_bytes) {
+  const int32_t src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= src_nb || dst < 0 || dst >= dst_nb) return;
+  const int64_t nvec = block_bytes / 16;  // per tile (K or V)
+  const int64_t v0 = (int64_t)blockIdx.y * kSwapVecs + threadIdx.x;
+  u32x4_t x[kSwapUnroll];
+#pragma unroll
+  for (int k = 0; k < kSwapUnroll; ++k) {
+    const int64_t v = v0 + k * kSwapThreads;
+    if (v < 2 * nvec) {
+      const uint8_t *base = v < nvec ? src_k : src_v;
+      x[k] = reinterpret_cast<const u32x4_t *>(base + src * block_bytes)[v < nvec ? v : v - nvec];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kSwapUnroll; ++k) {
+    const int64_t v = v0 + k * kSwapThreads;
+    if (v < 2 * nvec) {
+      uint8_t *base = v < nvec ? dst_k : dst_v;
+      reinterpret_cast<u32x4_t *>(base + dst * block_bytes)[v < nvec ? v : v - nvec] = x[k];
+    }
+  }
+}
+
 // ============================================================================
 // Host side
 // ============================================================================
@@ -2012,6 +2049,100 @@ pa_status pa_copy_blocks_int8(int8_t *k_cache, int8_t *v_cache, float *k_scales,
                      reinterpret_cast<uint8_t *>(v_scales), src_dst_pairs,
                      (int64_t)num_kv_heads * kBS * (int64_t)sizeof(float), num_blocks);
   return hip_check(hipGetLastError(), "pa_copy_blocks_int8 launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+pa_status launch_swap(const void *src_k, const void *src_v, int32_t src_nb, void *dst_k, void *dst_v,
+                      int32_t dst_nb, const int32_t *pairs, int32_t num_pairs, int64_t block_bytes,
+                      hipStream_t hs, const char *who) {
+  const int64_t chunks = (2 * block_bytes / 16 + kSwapVecs - 1) / kSwapVecs;
+  hipLaunchKernelGGL(pa_swap_blocks_kernel, dim3(num_pairs, (unsigned)chunks), dim3(kSwapThreads), 0, hs,
+                     static_cast<const uint8_t *>(src_k), static_cast<const uint8_t *>(src_v), src_nb,
+                     static_cast<uint8_t *>(dst_k), static_cast<uint8_t *>(dst_v), dst_nb, pairs, block_bytes);
+  return hip_check(hipGetLastError(), who);
+}
+
+// The address the GPU uses for p: device memory as it is, pinned host memory
+// through its device mapping.  Anything else (pageable host memory, unknown
+// pointers) is an error here rather than a memory fault in the kernel.
+pa_status gpu_address(const void *p, const void **out, const char *who) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: %p is neither device memory nor pinned host memory", who, p);
+  }
+  if (attr.type == hipMemoryTypeDevice) {
+    *out = p;
+    return PA_OK;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer && attr.hostPointer) {
+    const char *hp = static_cast<const char *>(attr.hostPointer);
+    *out = static_cast<const char *>(attr.devicePointer) + (static_cast<const char *>(p) - hp);
+    return PA_OK;
+  }
+  return pa::fail(PA_ERR_INVALID_ARG, "%s: %p is neither device memory nor pinned host memory", who, p);
+}
+
+// Checks sizes and pointers; ptrs[] are replaced by their GPU addresses.
+pa_status check_swap_args(int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t src_nb,
+                          int32_t dst_nb, const void **ptrs, int nptr, const int32_t **pairs,
+                          const char *who) {
+  if (num_pairs < 0 || num_pairs > 65535 || num_kv_heads <= 0 || src_nb <= 0 || dst_nb <= 0)
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: bad sizes (num_pairs must be in [0, 65535])", who);
+  if (head_dim != 64 && head_dim != 128)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128", who);
+  if (num_pairs == 0) return PA_OK;
+  if (!*pairs) return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pairs", who);
+  const void *pp = nullptr;
+  pa_status st = gpu_address(*pairs, &pp, who);
+  if (st != PA_OK) return st;
+  *pairs = static_cast<const int32_t *>(pp);
+  for (int i = 0; i < nptr; ++i) {
+    if (!ptrs[i]) return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL pool pointer", who);
+    if (!aligned16(ptrs[i])) return pa::fail(PA_ERR_INVALID_ARG, "%s: pools must be 16-byte aligned", who);
+    if ((st = gpu_address(ptrs[i], &ptrs[i], who)) != PA_OK) return st;
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_swap_blocks(const void *src_k, const void *src_v, int32_t src_num_blocks, void *dst_k,
+                         void *dst_v, int32_t dst_num_blocks, const int32_t *src_dst_pairs, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype, void *stream) {
+  if (!valid_dtype(dtype)) return pa::fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: unknown dtype");
+  const void *ptrs[] = {src_k, src_v, dst_k, dst_v};
+  const int32_t *pairs = src_dst_pairs;
+  pa_status st = check_swap_args(num_pairs, num_kv_heads, head_dim, src_num_blocks, dst_num_blocks, ptrs, 4,
+                                 &pairs, "pa_swap_blocks");
+  if (st != PA_OK || num_pairs == 0) return st;
+  return launch_swap(ptrs[0], ptrs[1], src_num_blocks, const_cast<void *>(ptrs[2]), const_cast<void *>(ptrs[3]),
+                     dst_num_blocks, pairs, num_pairs, (int64_t)num_kv_heads * kBS * head_dim * elem_bytes(dtype),
+                     static_cast<hipStream_t>(stream), "pa_swap_blocks launch");
+}
+
+pa_status pa_swap_blocks_int8(const int8_t *src_k, const int8_t *src_v, const float *src_k_scales,
+                              const float *src_v_scales, int32_t src_num_blocks, int8_t *dst_k, int8_t *dst_v,
+                              float *dst_k_scales, float *dst_v_scales, int32_t dst_num_blocks,
+                              const int32_t *src_dst_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                              int32_t head_dim, void *stream) {
+  const void *ptrs[] = {src_k, src_v, src_k_scales, src_v_scales, dst_k, dst_v, dst_k_scales, dst_v_scales};
+  const int32_t *pairs = src_dst_pairs;
+  pa_status st = check_swap_args(num_pairs, num_kv_heads, head_dim, src_num_blocks, dst_num_blocks, ptrs, 8,
+                                 &pairs, "pa_swap_blocks_int8");
+  if (st != PA_OK || num_pairs == 0) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  auto w = [&](int i) { return const_cast<void *>(ptrs[i]); };
+  st = launch_swap(ptrs[0], ptrs[1], src_num_blocks, w(4), w(5), dst_num_blocks, pairs, num_pairs,
+                   (int64_t)num_kv_heads * kBS * head_dim, hs, "pa_swap_blocks_int8 launch");
+  if (st != PA_OK) return st;
+  return launch_swap(ptrs[2], ptrs[3], src_num_blocks, w(6), w(7), dst_num_blocks, pairs, num_pairs,
+                     (int64_t)num_kv_heads * kBS * (int64_t)sizeof(float), hs, "pa_swap_blocks_int8 launch");
 }
 
 pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst_pairs, int32_t num_pairs,

@@ -7,7 +7,10 @@
 // parent's blocks, and the first write into a shared, partly filled block is
 // redirected to a fresh copy ("Modern AI Infrastructure and Agentic System
 // Design", section 9.1).  Every operation checks first and mutates second, so
-// a failure leaves the pool exactly as it was.
+// a failure leaves the pool exactly as it was.  Preemption by swapping
+// ("Inference serving: the KV-cache machine", section "Paged KV": the private
+// blocks of a block table can be swapped out and reloaded anywhere) releases a
+// sequence's private suffix and later refills it with fresh blocks.
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -20,6 +23,7 @@ struct pa_block_pool {
     std::vector<int32_t> table;
     int64_t tokens = 0;
     bool live = false;
+    int32_t swapped = -1;  // blocks held elsewhere while swapped out, else -1
   };
   int32_t num_blocks = 0;
   std::vector<int32_t> free_stack;  // top = back()
@@ -30,6 +34,7 @@ struct pa_block_pool {
   bool valid_seq(int32_t s) const {
     return s >= 0 && s < (int32_t)seqs.size() && seqs[s].live;
   }
+  bool resident(int32_t s) const { return valid_seq(s) && seqs[s].swapped < 0; }
 
   int32_t pop() {
     int32_t b = free_stack.back();
@@ -169,6 +174,8 @@ pa_status pa_seq_fork(pa_block_pool *pool, int32_t parent, int32_t *child) {
   if (!pool || !child) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_fork: NULL argument");
   if (!pool->valid_seq(parent))
     return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_fork: no sequence %d", parent);
+  if (!pool->resident(parent))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_fork: sequence %d is swapped out", parent);
   int32_t id = pool->new_seq_id();  // may grow seqs: index, do not hold references
   pa_block_pool::Seq s;
   s.table = pool->seqs[parent].table;
@@ -186,6 +193,8 @@ pa_status pa_seq_append(pa_block_pool *pool, int32_t seq, int32_t n_tokens, int6
     return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append: NULL argument");
   if (n_tokens < 0) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append: negative n_tokens");
   if (!pool->valid_seq(seq)) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append: no sequence %d", seq);
+  if (!pool->resident(seq))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append: sequence %d is swapped out", seq);
   auto &s = pool->seqs[seq];
   if (s.tokens + n_tokens > (int64_t)INT32_MAX)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append: sequence would exceed 2^31-1 tokens");
@@ -206,6 +215,8 @@ pa_status pa_seq_append_batch(pa_block_pool *pool, const int32_t *seq_ids, int32
     int32_t sid = seq_ids[i];
     if (!pool->valid_seq(sid))
       return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append_batch: no sequence %d", sid);
+    if (!pool->resident(sid))
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append_batch: sequence %d is swapped out", sid);
     if (seen[sid]) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append_batch: duplicate sequence %d", sid);
     seen[sid] = 1;
     if (pool->seqs[sid].tokens >= (int64_t)INT32_MAX)
@@ -237,6 +248,54 @@ pa_status pa_seq_free(pa_block_pool *pool, int32_t seq) {
   return PA_OK;
 }
 
+pa_status pa_seq_swap_out(pa_block_pool *pool, int32_t seq, int32_t *blocks_out, int32_t capacity,
+                          int32_t *n_out) {
+  if (!pool || !n_out) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_swap_out: NULL argument");
+  if (!pool->valid_seq(seq)) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_swap_out: no sequence %d", seq);
+  if (!pool->resident(seq))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_swap_out: sequence %d is already swapped out", seq);
+  auto &s = pool->seqs[seq];
+  // the private blocks: the longest suffix of the table held by this sequence alone
+  int32_t k = 0;
+  const int32_t nb = (int32_t)s.table.size();
+  while (k < nb && pool->refcount[s.table[nb - 1 - k]] == 1) ++k;
+  if (k > 0 && (!blocks_out || capacity < k))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_swap_out: %d private blocks, capacity %d", k, capacity);
+  for (int32_t i = 0; i < k; ++i) {
+    const int32_t b = s.table[nb - k + i];
+    blocks_out[i] = b;
+    pool->release(b);  // front to back, as a finished sequence frees its blocks
+  }
+  s.table.resize(nb - k);
+  s.swapped = k;
+  *n_out = k;
+  return PA_OK;
+}
+
+pa_status pa_seq_swap_in(pa_block_pool *pool, int32_t seq, int32_t *blocks_out, int32_t capacity,
+                         int32_t *n_out) {
+  if (!pool || !n_out) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_swap_in: NULL argument");
+  if (!pool->valid_seq(seq)) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_swap_in: no sequence %d", seq);
+  auto &s = pool->seqs[seq];
+  if (s.swapped < 0) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_swap_in: sequence %d is not swapped out", seq);
+  const int32_t k = s.swapped;
+  if (k > 0 && (!blocks_out || capacity < k))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_swap_in: %d blocks to restore, capacity %d", k, capacity);
+  if ((size_t)k > pool->free_stack.size()) return pa::fail(PA_ERR_OOM, "pa_seq_swap_in: pool exhausted");
+  for (int32_t i = 0; i < k; ++i) {
+    blocks_out[i] = pool->pop();
+    s.table.push_back(blocks_out[i]);
+  }
+  s.swapped = -1;
+  *n_out = k;
+  return PA_OK;
+}
+
+int32_t pa_seq_swapped_blocks(const pa_block_pool *pool, int32_t seq) {
+  if (!pool || !pool->valid_seq(seq)) return -1;
+  return pool->seqs[seq].swapped;
+}
+
 int32_t pa_seq_num_tokens(const pa_block_pool *pool, int32_t seq) {
   if (!pool || !pool->valid_seq(seq)) return -1;
   return (int32_t)pool->seqs[seq].tokens;
@@ -250,6 +309,8 @@ pa_status pa_seq_export(const pa_block_pool *pool, const int32_t *seq_ids, int32
   for (int32_t i = 0; i < n; ++i) {
     if (!pool->valid_seq(seq_ids[i]))
       return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_export: no sequence %d", seq_ids[i]);
+    if (!pool->resident(seq_ids[i]))
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_export: sequence %d is swapped out", seq_ids[i]);
     if ((int64_t)pool->seqs[seq_ids[i]].table.size() > max_blocks)
       return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_export: sequence %d needs %zu > %d blocks",
                       seq_ids[i], pool->seqs[seq_ids[i]].table.size(), max_blocks);

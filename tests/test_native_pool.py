@@ -135,3 +135,72 @@ def test_random_scripts_match_the_model(seed):
                 model.decref(b)
                 pool.decref(b)
         _same(model, pool, live)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_scripts_with_swaps_match_the_model(seed):
+    rng = np.random.default_rng(200 + seed)
+    n = int(rng.integers(6, 80))
+    order = rng.permutation(n)
+    model, pool = PoolModel(n, 16, order), pa.BlockPool(n, 16, order)
+    live, swapped = [], []
+    for _ in range(400):
+        op = int(rng.integers(0, 7))
+        if op == 0 or not (live or swapped):
+            sid = model.seq_create()
+            assert pool.seq_create() == sid
+            live.append(sid)
+        elif op == 1 and live:
+            p = live[int(rng.integers(len(live)))]
+            sid = model.seq_fork(p)
+            assert pool.seq_fork(p) == sid
+            live.append(sid)
+        elif op == 2 and live:
+            sid = live[int(rng.integers(len(live)))]
+            k = int(rng.integers(0, 50))
+            try:
+                s1, c1 = model.seq_append(sid, k)
+            except OutOfBlocks:
+                with pytest.raises(pa.PaOutOfBlocks):
+                    pool.seq_append(sid, k)
+            else:
+                s2, c2 = pool.seq_append(sid, k)
+                assert s1 == s2.tolist() and c1 == c2
+        elif op == 3:
+            group = live if (live and (not swapped or rng.integers(2))) else swapped
+            sid = group.pop(int(rng.integers(len(group))))
+            model.seq_free(sid)
+            pool.seq_free(sid)
+        elif op == 4 and live:
+            sid = live.pop(int(rng.integers(len(live))))
+            out = model.seq_swap_out(sid)
+            assert pool.seq_swap_out(sid).tolist() == out
+            assert pool.seq_swapped_blocks(sid) == len(out)
+            swapped.append(sid)
+        elif op == 5 and swapped:
+            sid = swapped[int(rng.integers(len(swapped)))]
+            try:
+                new = model.seq_swap_in(sid)
+            except OutOfBlocks:
+                with pytest.raises(pa.PaOutOfBlocks):
+                    pool.seq_swap_in(sid)
+            else:
+                assert pool.seq_swap_in(sid).tolist() == new
+                swapped.remove(sid)
+                live.append(sid)
+        elif op == 6 and live:
+            k = int(rng.integers(1, len(live) + 1))
+            ids = [int(x) for x in rng.choice(live, size=k, replace=False)]
+            try:
+                s1, c1 = model.seq_append_batch(ids)
+            except OutOfBlocks:
+                with pytest.raises(pa.PaOutOfBlocks):
+                    pool.seq_append_batch(ids)
+            else:
+                s2, c2 = pool.seq_append_batch(ids)
+                assert s1 == s2.tolist() and [list(c) for c in c1] == c2.tolist()
+        for sid in swapped:
+            with pytest.raises(pa.PaError):
+                pool.seq_append(sid, 1)
+            assert pool.seq_num_tokens(sid) == model.seq_num_tokens(sid)
+        _same(model, pool, live)

@@ -327,3 +327,14 @@ def test_copy_blocks_copies_whole_blocks_in_order():
     assert np.array_equal(kc[4 * blk:5 * blk], k0[1 * blk:2 * blk])  # chained in order
     assert np.array_equal(vc[4 * blk:5 * blk], v0[1 * blk:2 * blk])
     assert np.array_equal(kc[:3 * blk], k0[:3 * blk])
+
+
+def test_swap_blocks_copies_whole_blocks_between_pools_and_skips_bad_pairs():
+    # block b of the source holds the value b everywhere; the destination starts at -1
+    per = 2 * 16 * 8
+    src = np.repeat(np.arange(6, dtype=np.float32), per)
+    dst = np.full(4 * per, -1.0, np.float32)
+    oracle.swap_blocks(src, dst, [[5, 0], [2, 3], [6, 1], [1, -1], [-2, 2]], per)
+    got = dst.reshape(4, per)
+    assert np.all(got[0] == 5) and np.all(got[3] == 2)
+    assert np.all(got[1] == -1) and np.all(got[2] == -1)   # out-of-range pairs skipped

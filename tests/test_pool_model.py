@@ -176,3 +176,61 @@ def test_randomized_scripts_keep_invariants():
         for s in live:
             pool.seq_free(s)
         assert pool.num_free() == n
+
+
+# ---------------------------------------------------------------- swap (preemption)
+def test_swap_out_releases_the_private_suffix_and_swap_in_refills_from_the_stack():
+    # Identity order: the stack top is block 9.  The owner of a 32-token shared
+    # prefix takes 9, 8; A forks it and grows by 40 tokens into 7, 6, 5.
+    # Swap-out pushes 7, 6, 5 (front to back) and keeps 9, 8; swap-in pops
+    # 5, 6, 7 back into the table: [9, 8, 5, 6, 7].
+    pool = PoolModel(10)
+    owner = pool.seq_create()
+    pool.seq_append(owner, 32)
+    a = pool.seq_fork(owner)
+    pool.seq_append(a, 40)
+    assert pool.seq_table(a) == [9, 8, 7, 6, 5] and pool.num_free() == 5
+    out = pool.seq_swap_out(a)
+    assert out == [7, 6, 5]
+    assert pool.seq_table(a) == [9, 8] and pool.seq_num_tokens(a) == 72
+    assert pool.free == [0, 1, 2, 3, 4, 7, 6, 5] and pool.seq_swapped_blocks(a) == 3
+    assert pool.refcount[9] == pool.refcount[8] == 2      # the prefix stays shared
+    new = pool.seq_swap_in(a)
+    assert new == [5, 6, 7] and pool.seq_table(a) == [9, 8, 5, 6, 7]
+    assert pool.seq_swapped_blocks(a) == -1 and pool.free == [0, 1, 2, 3, 4]
+
+
+def test_swapped_out_sequence_is_frozen_until_swapped_in():
+    pool = PoolModel(8)
+    a = pool.seq_create()
+    pool.seq_append(a, 20)
+    pool.seq_swap_out(a)
+    for call in (lambda: pool.seq_append(a, 1), lambda: pool.seq_append_batch([a]),
+                 lambda: pool.seq_fork(a), lambda: pool.export([a], 4), lambda: pool.seq_swap_out(a)):
+        with pytest.raises(PoolError):
+            call()
+    b = pool.seq_create()
+    with pytest.raises(PoolError):
+        pool.seq_swap_in(b)                                # resident
+    pool.seq_append(b, 16 * 7)                             # takes all 7 free blocks but one
+    before = (list(pool.free), list(pool.refcount), pool.seq_table(a))
+    with pytest.raises(OutOfBlocks):
+        pool.seq_swap_in(a)                                # needs 2, 1 free
+    assert (list(pool.free), list(pool.refcount), pool.seq_table(a)) == before
+    pool.seq_free(b)
+    assert pool.seq_swap_in(a) and pool.seq_num_tokens(a) == 20
+    pool.seq_swap_out(a)
+    pool.seq_free(a)                                       # frees what is resident
+    assert pool.num_free() == 8
+
+
+def test_swap_out_keeps_a_shared_last_block():
+    # a fork shares every block, including the partly filled last one: nothing
+    # is private, so swap-out releases nothing and swap-in takes nothing
+    pool = PoolModel(6)
+    a = pool.seq_create()
+    pool.seq_append(a, 20)
+    b = pool.seq_fork(a)
+    assert pool.seq_swap_out(a) == [] and pool.seq_swapped_blocks(a) == 0
+    assert pool.seq_table(a) == pool.seq_table(b) and pool.refcount[5] == 2
+    assert pool.seq_swap_in(a) == [] and pool.seq_swapped_blocks(a) == -1
