@@ -503,6 +503,58 @@ def run_copy_calibration(nbytes):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
+def run_swap_bench(blocks, reps):
+    """Swap-out (device -> pinned host) and swap-in (host -> device) of `blocks`
+    scattered blocks of the 70B-GQA cache shape (8 KV heads, D = 128, bf16:
+    64 KiB of K+V per block) through pa_swap_blocks, against plain DMA copies
+    of the same bytes between contiguous buffers.  One JSON line."""
+    import torch
+    from paged_kv_cache_65_amd import binding as pa
+    Hkv, D, NB = 8, 128, 20000
+    per = Hkv * 16 * D
+    g = torch.Generator(device="cuda").manual_seed(11)
+    kc = torch.randn(NB * per, dtype=torch.bfloat16, device="cuda", generator=g)
+    vc = torch.randn(NB * per, dtype=torch.bfloat16, device="cuda", generator=g)
+    ids = torch.from_numpy(np.random.default_rng(12).permutation(NB)[:2 * blocks].astype(np.int32))
+    hk = torch.empty(blocks * per, dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty(blocks * per, dtype=torch.bfloat16).pin_memory()
+    ar = torch.arange(blocks, dtype=torch.int32)
+    out_pairs = torch.stack([ids[:blocks], ar], 1).contiguous().cuda()
+    in_pairs = torch.stack([ar, ids[blocks:]], 1).contiguous().cuda()   # back into other blocks
+    nbytes = 2 * blocks * per * 2
+    dev_flat = torch.empty(2 * blocks * per, dtype=torch.bfloat16, device="cuda")
+    host_flat = torch.empty(2 * blocks * per, dtype=torch.bfloat16).pin_memory()
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / 1e3 / reps
+
+    t_out = timed(lambda: pa.pa_swap_blocks(kc, vc, hk, hv, out_pairs, Hkv, D))
+    t_in = timed(lambda: pa.pa_swap_blocks(hk, hv, kc, vc, in_pairs, Hkv, D))
+    t_d2h = timed(lambda: host_flat.copy_(dev_flat, non_blocking=True))
+    t_h2d = timed(lambda: dev_flat.copy_(host_flat, non_blocking=True))
+    # the round trip restores the blocks bit for bit
+    torch.cuda.synchronize()
+    same = bool(torch.equal(kc.view(NB, per)[ids[blocks:].long()], kc.view(NB, per)[ids[:blocks].long()]))
+    rec = {"metric": "KV swap bandwidth, device <-> pinned host (pa_swap_blocks)", "unit": "GB/s",
+           "blocks": blocks, "bytes_per_direction": nbytes, "reps": reps,
+           "swap_out_GBps": round(nbytes / t_out / 1e9, 2), "swap_in_GBps": round(nbytes / t_in / 1e9, 2),
+           "memcpy_d2h_GBps": round(nbytes / t_d2h / 1e9, 2), "memcpy_h2d_GBps": round(nbytes / t_h2d / 1e9, 2),
+           "swap_out_ms": round(t_out * 1e3, 3), "swap_in_ms": round(t_in * 1e3, 3),
+           "round_trip_bitwise": same,
+           "config": {"workload": "70B-GQA cache blocks (8 KV heads, D=128, bf16), scattered over 20000",
+                      "device": torch.cuda.get_device_name(0)}}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -524,6 +576,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--swap", type=int, default=0, metavar="BLOCKS",
+                    help="only measure swap-out / swap-in of BLOCKS scattered cache blocks")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -533,6 +587,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         run_copy_calibration(args.copy_calibration)
+        return
+    if args.swap:
+        run_swap_bench(args.swap, 10)
         return
     base = workloads.named(args.workload)
     spec = dataclasses.replace(base, decode_steps=args.warmup + args.steps)
