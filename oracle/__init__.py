@@ -82,6 +82,9 @@ def _load():
         lib.oracle_decode_i8.restype = _I
         lib.oracle_decode_i8.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                          _I, ctypes.c_float, _I, _I]
+        lib.oracle_extend.restype = _I
+        lib.oracle_extend.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                      ctypes.c_float, _I, _I]
         lib.oracle_bruteforce_contiguous.restype = None
         lib.oracle_bruteforce_contiguous.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                                      ctypes.c_float, _I, _I]
@@ -164,6 +167,24 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads, scale,
                                  _ptr(lens), S, Hq, num_kv_heads, D, tables.shape[1],
                                  float(scale), _DTYPES[dtype], int(window), nthreads)
     return (out, used) if return_threads else out
+
+
+def extend(q, k_cache, v_cache, block_tables, context_lens, query_start, num_kv_heads, scale, dtype,
+           nthreads=0):
+    """fp64 multi-query attention: q is [T][Hq][D] (rows of sequence s are
+    query_start[s] .. query_start[s+1]-1, at positions L-n .. L-1); row t at
+    position p attends to 0 .. p.  Returns float64 [T][Hq][D]."""
+    q = _check(q, dtype)
+    T, Hq, D = q.shape
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    assert qs[-1] == T and len(qs) == len(lens) + 1
+    out = np.empty((T, Hq, D), dtype=np.float64)
+    _load().oracle_extend(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(tables), _ptr(lens),
+                          _ptr(qs), len(lens), Hq, num_kv_heads, D, tables.shape[1], float(scale),
+                          _DTYPES[dtype], nthreads)
+    return out
 
 
 def bruteforce_contiguous(q, k_seq, v_seq, context_lens, scale, dtype, window=0):

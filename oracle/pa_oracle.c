@@ -298,6 +298,64 @@ int oracle_decode(double *out, const void *q, const void *k_cache, const void *v
 }
 
 /* ---------------------------------------------------------------------------
+ * Multi-query ("extend") attention: sequence s brings n_s = query_start[s+1] -
+ * query_start[s] new tokens, already in the cache, at positions L-n_s .. L-1
+ * (L = lens[s]).  Query row t = query_start[s] + i sits at p = L - n_s + i and
+ * attends to positions 0 .. p: causal within the new tokens, everything
+ * before them ("Inference serving: the KV-cache machine": chunked prefill
+ * interleaves prompt chunks with decode; speculative decoding verifies k
+ * drafted tokens in one pass).  A sequence with n_s > L has NaN rows.
+ *   out: [T][Hq][D] doubles, T = query_start[S];  q: [T][Hq][D] in dtype
+ * Returns the number of threads used.
+ * ------------------------------------------------------------------------ */
+int oracle_extend(double *out, const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *tables, const int32_t *lens, const int32_t *query_start,
+                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int max_blocks,
+                  float scale, int dtype, int nthreads) {
+  int G = num_q_heads / num_kv_heads;
+  int T = query_start[num_seqs];
+  int Lmax = 0;
+  for (int s = 0; s < num_seqs; ++s)
+    if (lens[s] > Lmax) Lmax = lens[s];
+  int used = 1;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+  {
+#pragma omp single
+    used = omp_get_num_threads();
+#endif
+    double *sigma = (double *)malloc(sizeof(double) * (Lmax > 0 ? Lmax : 1));
+    double *qd = (double *)malloc(sizeof(double) * head_dim);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+    for (int64_t th = 0; th < (int64_t)T * num_q_heads; ++th) {
+      int t = (int)(th / num_q_heads), h = (int)(th % num_q_heads);
+      int s = 0;
+      while (query_start[s + 1] <= t) ++s;
+      int n = query_start[s + 1] - query_start[s];
+      int p = lens[s] - n + (t - query_start[s]);
+      double *o = out + th * head_dim;
+      if (n > lens[s]) {
+        for (int d = 0; d < head_dim; ++d) o[d] = NAN;
+        continue;
+      }
+      for (int d = 0; d < head_dim; ++d) qd[d] = load_elem(q, th * head_dim + d, dtype);
+      orc_src src = {k_cache, v_cache, tables + (int64_t)s * max_blocks, num_kv_heads,
+                     head_dim, dtype, h / G, NULL, NULL};
+      attend_one(o, qd, &src, p + 1, 0, (double)scale, sigma);
+    }
+    free(sigma);
+    free(qd);
+#ifdef _OPENMP
+  }
+#endif
+  (void)nthreads;
+  return used;
+}
+
+/* ---------------------------------------------------------------------------
  * Brute force over contiguous per-sequence arrays k_seq, v_seq:
  * [S][Lmax][Hkv][D] in the cache type.  Never touches a table.
  * ------------------------------------------------------------------------ */
