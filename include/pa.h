@@ -277,6 +277,61 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst_pa
                          int32_t num_blocks, pa_dtype dtype, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Multi-query ("extend") attention: several new tokens per sequence, each
+ * attending causally ("Inference serving: the KV-cache machine": chunked
+ * prefill interleaves ~2k-token prompt chunks with decode; speculative
+ * decoding verifies k drafted tokens in one pass).  Sequence s brings
+ * n_s = query_start[s+1] - query_start[s] new tokens whose K/V are already in
+ * the cache (pa_reshape_and_cache) at positions L-n_s .. L-1, L =
+ * context_lens[s]; query row t = query_start[s] + i is the token at position
+ * p = L - n_s + i and attends to positions 0 .. p:
+ *   out[t][h] = softmax_j(scale * q[t][h] . K[j][g]) V[j][g], j = 0 .. p,
+ *   g = h / (num_q_heads / num_kv_heads).
+ *   q, out      [num_query_rows][num_q_heads][head_dim] (out F32 or kv_dtype,
+ *               16-bit outputs rounded to nearest even from float32)
+ *   query_start int32 [num_seqs + 1], ascending, query_start[0] = 0 and
+ *               query_start[num_seqs] = num_query_rows (device)
+ *   max_query_len >= every n_s, max_context_len >= every L (host bounds)
+ * fp16 / bf16 caches, head_dim 64 or 128, up to 16 query heads per KV head.
+ * A sequence with n_s > L, L outside [0, max_context_len] or beyond its
+ * table row, or n_s > max_query_len, or a table entry outside the pool, gets
+ * NaN rows (never dereferenced); a sequence whose rows fall outside
+ * [0, num_query_rows) is skipped (nothing read or written).  n_s = 1 for every
+ * sequence is the decode.
+ * Workspace: pa_extend_workspace_bytes() (0 without split contexts); events
+ * as for pa_decode (start of the attention kernel, end of the last kernel).
+ * ------------------------------------------------------------------------ */
+typedef struct pa_extend_params {
+  void *out;
+  const void *q;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  const int32_t *query_start;
+  int32_t num_seqs;
+  int32_t num_query_rows;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  int32_t max_context_len;
+  int32_t max_query_len;
+  float scale;
+  pa_dtype kv_dtype;
+  pa_dtype out_dtype;
+  int32_t partition_tokens; /* 0 = automatic; else a multiple of 16 */
+  void *start_event;
+  void *stop_event;
+} pa_extend_params;
+
+/* Partition size in tokens pa_extend will use, or a negative pa_status. */
+int32_t pa_extend_partition_tokens(const pa_extend_params *p);
+size_t pa_extend_workspace_bytes(const pa_extend_params *p);
+pa_status pa_extend(const pa_extend_params *p, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Swap copies: whole blocks (all heads, K and V) between two pools of the
  * same tile layout, for preemption by swapping ("Inference serving: the
  * KV-cache machine", section "Paged KV": a block table lets a sequence's

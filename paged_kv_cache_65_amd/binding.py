@@ -48,6 +48,16 @@ class pa_decode_params(ctypes.Structure):
                 ("start_event", _P), ("stop_event", _P), ("sliding_window", _I32)]
 
 
+class pa_extend_params(ctypes.Structure):
+    _fields_ = [("out", _P), ("q", _P), ("k_cache", _P), ("v_cache", _P),
+                ("block_tables", _P), ("context_lens", _P), ("query_start", _P),
+                ("num_seqs", _I32), ("num_query_rows", _I32), ("num_q_heads", _I32),
+                ("num_kv_heads", _I32), ("head_dim", _I32), ("max_blocks_per_seq", _I32),
+                ("num_blocks", _I32), ("max_context_len", _I32), ("max_query_len", _I32),
+                ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("partition_tokens", _I32), ("start_event", _P), ("stop_event", _P)]
+
+
 _lib = None
 
 
@@ -66,6 +76,9 @@ def lib():
             "pa_decode": (ctypes.c_int, [ctypes.POINTER(pa_decode_params), _P, _SZ, _P]),
             "pa_decode_partitions": (ctypes.c_int, [ctypes.POINTER(pa_decode_params), _P, _SZ, _P]),
             "pa_decode_merge": (ctypes.c_int, [ctypes.POINTER(pa_decode_params), _P, _SZ, _P]),
+            "pa_extend_partition_tokens": (_I32, [ctypes.POINTER(pa_extend_params)]),
+            "pa_extend_workspace_bytes": (_SZ, [ctypes.POINTER(pa_extend_params)]),
+            "pa_extend": (ctypes.c_int, [ctypes.POINTER(pa_extend_params), _P, _SZ, _P]),
             "pa_reshape_and_cache": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                                     ctypes.c_int, _P]),
             "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, ctypes.c_int, _P]),
@@ -203,6 +216,46 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads
     ws_ptr = _dev(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().pa_decode(ctypes.byref(params), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def make_extend_params(out, q, k_cache, v_cache, block_tables, context_lens, query_start, num_kv_heads,
+                       max_context_len, max_query_len, scale, partition_tokens=0, start_event=None,
+                       stop_event=None):
+    """q, out: [T][Hq][D]; query_start: int32 [S+1] device tensor (see include/pa.h)."""
+    T, Hq, D = q.shape
+    S = context_lens.numel()
+    nb = k_cache.numel() // (num_kv_heads * BLOCK_SIZE * D)
+    return pa_extend_params(
+        _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), _dev(context_lens),
+        _dev(query_start), S, T, Hq, num_kv_heads, D,
+        block_tables.shape[1] if block_tables.dim() == 2 else 0, nb, int(max_context_len),
+        int(max_query_len), float(scale), _dtype_code(k_cache), _dtype_code(out), int(partition_tokens),
+        _event(start_event), _event(stop_event))
+
+
+def pa_extend_workspace_bytes(params: pa_extend_params) -> int:
+    return lib().pa_extend_workspace_bytes(ctypes.byref(params))
+
+
+def pa_extend_partition_tokens(params: pa_extend_params) -> int:
+    v = lib().pa_extend_partition_tokens(ctypes.byref(params))
+    if v < 0:
+        _check(-v)
+    return v
+
+
+def pa_extend(out, q, k_cache, v_cache, block_tables, context_lens, query_start, num_kv_heads,
+              max_context_len, max_query_len, scale, partition_tokens=0, workspace=None, stream=None):
+    """out <- multi-query attention of the new tokens (rows of q) over the cache."""
+    import torch
+    params = make_extend_params(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                                num_kv_heads, max_context_len, max_query_len, scale, partition_tokens)
+    need = pa_extend_workspace_bytes(params)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ptr, n = _ws(workspace)
+    _check(lib().pa_extend(ctypes.byref(params), ptr, n, _stream(stream)))
     return out
 
 

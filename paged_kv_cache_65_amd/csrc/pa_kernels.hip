@@ -1308,7 +1308,7 @@ constexpr int kMergeWaves = 4;
 // Folds np partials (m, l at ml + q*ml_stride, acc at acc + q*acc_stride)
 // into one output row.
 template <int D>
-__device__ void merge_row(const DecodeArgs &a, int64_t row, const float *ml, int64_t ml_stride,
+__device__ void merge_row(void *out, int out_dtype, int64_t row, const float *ml, int64_t ml_stride,
                           const float *acc, int64_t acc_stride, int np, int lane) {
   constexpr int PER = D / 64;  // output dims per lane
   constexpr int kFew = 8;
@@ -1349,7 +1349,7 @@ __device__ void merge_row(const DecodeArgs &a, int64_t row, const float *ml, int
     }
 #pragma unroll
     for (int e = 0; e < PER; ++e)
-      store_out(a.out, row * D + lane * PER + e, nan ? NAN : num[e] / den, a.out_dtype);
+      store_out(out, row * D + lane * PER + e, nan ? NAN : num[e] / den, out_dtype);
     return;
   }
   float M = -INFINITY;
@@ -1372,7 +1372,7 @@ __device__ void merge_row(const DecodeArgs &a, int64_t row, const float *ml, int
   }
 #pragma unroll
   for (int e = 0; e < PER; ++e)
-    store_out(a.out, row * D + lane * PER + e, nan ? NAN : num[e] / den, a.out_dtype);
+    store_out(out, row * D + lane * PER + e, nan ? NAN : num[e] / den, out_dtype);
 }
 
 template <int D>
@@ -1386,7 +1386,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_kernel(DecodeArgs a
   const int skip = window_first_token(L, a.window) / kBS * kBS;  // tokens of the unattended blocks
   const int np = (L - skip + a.part_tokens - 1) / a.part_tokens;
   if (np <= 1) return;
-  merge_row<D>(a, row, a.ws_ml + row * a.max_parts * 2, 2, a.ws_acc + row * a.max_parts * D, D, np, lane);
+  merge_row<D>(a.out, a.out_dtype, row, a.ws_ml + row * a.max_parts * 2, 2, a.ws_acc + row * a.max_parts * D, D, np, lane);
 }
 
 // Balanced split: the row of (s, head g*G + r) gathers the partials of its
@@ -1409,7 +1409,296 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_balanced_kernel(Dec
   const int w0 = us / C, w1 = (us + nb - 1) / C;
   if (w0 == w1) return;
   const int64_t prow = (int64_t)(w0 + s * Hkv + g) * G + r;
-  merge_row<D>(a, row, a.ws_ml + prow * 2, (int64_t)G * 2, a.ws_acc + prow * D, (int64_t)G * D, w1 - w0 + 1, lane);
+  merge_row<D>(a.out, a.out_dtype, row, a.ws_ml + prow * 2, (int64_t)G * 2, a.ws_acc + prow * D, (int64_t)G * D, w1 - w0 + 1, lane);
+}
+
+// ---------------------------------------------------------------- extend (multi-query)
+// Sequence s brings n_s new tokens, already in the cache, at positions
+// L-n_s .. L-1; query row i of it attends to positions 0 .. L-n_s+i (chunked
+// prefill and speculative verification: "Inference serving: the KV-cache
+// machine").  The score tile's 16 columns are (query token, head) pairs,
+// token-major: a tile holds tpt = 16/G tokens of the group's G heads, a wave
+// holds NCT tiles (tpg = NCT*tpt tokens: a "query group"), each column with
+// its own online-softmax state and causal limit.  Workgroup = (KV head g,
+// sequence s, query group, partition of the blocks the group needs); its
+// four waves take every fourth block, their states meet in LDS, and the
+// group writes final rows or (m, l, acc) partials for the merge.
+struct ExtendArgs {
+  void *out;                      // [T][Hq][D]
+  const void *q;                  // [T][Hq][D]
+  const uint8_t *k_cache;
+  const uint8_t *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  const int32_t *query_start;     // [S+1]
+  float *ws_ml;                   // [T][Hq][max_parts][2]
+  float *ws_acc;                  // [T][Hq][max_parts][D]
+  int32_t num_seqs, num_q_heads, num_kv_heads, group, max_blocks, num_blocks, max_ctx, max_q,
+      num_rows, max_parts, part_tokens, out_dtype, qgroups, tpt, tpg;
+  float scale_log2;
+};
+
+constexpr int kExtNctMax = 2;
+
+template <int D, int NCT>
+struct __align__(16) SmemExtend {
+  float acc[kWaves][NCT * 16][D];
+  float m[kWaves][NCT * 16];
+  float l[kWaves][NCT * 16];
+};
+
+// Sequence whose query rows hold row t (query_start ascending).
+__device__ inline int seq_of_row(const int32_t *qs, int S, int t) {
+  int lo = 0, hi = S;  // qs[lo] <= t < qs[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (qs[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Rows q0 .. q0+n-1 inside [0, num_rows): otherwise nothing is read or written.
+__device__ inline bool extend_rows_valid(int q0, int n, const ExtendArgs &a) {
+  return q0 >= 0 && n >= 0 && (int64_t)q0 + n <= a.num_rows;
+}
+
+// Contract of one sequence; a violation makes its rows NaN.
+__device__ inline bool extend_seq_valid(int L, int n, const ExtendArgs &a) {
+  return L >= 0 && L <= a.max_ctx && (int64_t)L <= (int64_t)a.max_blocks * kBS && n <= L && n <= a.max_q;
+}
+
+template <int DT, int D, int NCT>
+__global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
+  using M = MfmaWave<DT, D>;
+  using v8 = typename M::v8;
+  constexpr int NC = D / 32, NT = D / 16;
+  constexpr int NB = 2;  // blocks in flight per wave
+  __shared__ SmemExtend<D, NCT> sm;
+  const int Hkv = a.num_kv_heads, G = a.group;
+  const int g = blockIdx.x % Hkv;
+  int rest = blockIdx.x / Hkv;
+  const int s = rest % a.num_seqs;
+  rest /= a.num_seqs;
+  const int qg = rest % a.qgroups;
+  const int p = rest / a.qgroups;
+  const int tid = threadIdx.x, lane = tid % 64, r = lane % 16, tq = lane / 16;
+  const int wu = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int L = a.context_lens[s];
+  const int q0 = a.query_start[s];
+  const int n = a.query_start[s + 1] - q0;
+  const int i0 = qg * a.tpg;
+  if (!extend_rows_valid(q0, n, a) || i0 >= n) return;  // no such query group
+  const int ni = min(a.tpg, n - i0);
+  const int Hq = a.num_q_heads;
+  // this lane's column in tile ct: token tk(ct), head r % G
+  auto col_token = [&](int ct) { return (r < a.tpt * G) ? ct * a.tpt + r / G : 1 << 30; };
+  const int hd = g * G + r % G;
+  if (!extend_seq_valid(L, n, a)) {
+    if (p == 0)
+      for (int i = tid; i < ni * G * D; i += kThreads) {
+        const int tk = i / (G * D), h = (i / D) % G, d = i % D;
+        store_out(a.out, ((int64_t)(q0 + i0 + tk) * Hq + g * G + h) * D + d, NAN, a.out_dtype);
+      }
+    return;
+  }
+  const int pf = L - n + i0;       // position of the group's first token
+  const int pl = pf + ni - 1;      // and of its last
+  const int tok_end = pl + 1;      // the group reads positions 0 .. pl
+  const int nparts = (tok_end + a.part_tokens - 1) / a.part_tokens;
+  if (p >= nparts) return;
+  const int blk0 = (int)((int64_t)p * a.part_tokens / kBS);
+  const int tok1 = min(tok_end, (blk0 * kBS) + a.part_tokens);
+  const int nblk = (tok1 - blk0 * kBS + kBS - 1) / kBS;
+  const int32_t *trow = a.block_tables + (int64_t)s * a.max_blocks + blk0;
+
+  // q fragments and causal limits of this lane's columns
+  v8 qB[NCT][NC];
+  int lim[NCT];
+  f32x4_t acc[NCT][NT];
+  float mm[NCT], ll[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int tk = col_token(ct);
+    const bool ok = tk < ni;
+    lim[ct] = ok ? pf + tk : -1;
+    const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
+                                                            ((int64_t)(q0 + i0 + (ok ? tk : 0)) * Hq + hd) * D * 2);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4_t x = qrow[4 * c + tq];
+      if (!ok) x = u32x4_t{0, 0, 0, 0};
+      qB[ct][c] = __builtin_bit_cast(v8, x);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[ct][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    mm[ct] = -INFINITY;
+    ll[ct] = 0.f;
+  }
+  // the first position any column of tile ct may not see (wave-uniform)
+  int tile_min[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) tile_min[ct] = pf + ct * a.tpt;
+
+  const int64_t head_off = (int64_t)g * M::TILE;
+  const int64_t blk_stride = (int64_t)Hkv * M::TILE;
+  typename M::Frag fr[NB];
+  int bad = 0;
+  const int nmine = nblk > wu ? (nblk - wu + kWaves - 1) / kWaves : 0;
+  for (int c0 = 0; c0 < nmine; c0 += 64) {
+    const int nc = min(64, nmine - c0);
+    int ids = lane < nc ? trow[wu + (c0 + lane) * kWaves] : 0;
+    const bool id_ok = (uint32_t)ids < (uint32_t)a.num_blocks;
+    if (__builtin_amdgcn_ballot_w64(!id_ok)) bad = 1;
+    ids = id_ok ? ids : 0;
+    auto refill = [&](typename M::Frag &f, int i) {
+      const bool real = i < nc;
+      const int64_t off = real ? (int64_t)__builtin_amdgcn_readlane(ids, min(i, nc - 1)) * blk_stride + head_off : 0;
+      M::load(f, a.k_cache + off, a.v_cache + off, real ? lane : 0);
+    };
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b) {
+      refill(fr[b], b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int j0 = 0; j0 < nc; j0 += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int i = j0 + b;
+        refill(fr[(b + NB - 1) % NB], i + NB - 1);
+        if (i < nc) {
+          typename M::Frag &f = fr[b];
+          const int b0 = (blk0 + wu + (c0 + i) * kWaves) * kBS;  // position of the block's token 0
+          if (b0 + kBS > L) {
+            // slots at and past L may hold anything: zero their V elements
+            const int lo_ok = L - b0;  // tokens 0 .. lo_ok-1 exist
+            const uint32_t mine = token_mask(0, max(0, min(kBS, lo_ok))) >> (4 * tq);
+            const uint32_t lo = ((mine & 1u) ? 0x0000FFFFu : 0u) | ((mine & 2u) ? 0xFFFF0000u : 0u);
+            const uint32_t hi = ((mine & 4u) ? 0x0000FFFFu : 0u) | ((mine & 8u) ? 0xFFFF0000u : 0u);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) f.v[c] &= u32x4_t{lo, hi, lo, hi};
+          }
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) sc = M::mma_qk(__builtin_bit_cast(v8, f.k[c]), qB[ct][c], sc);
+            float sv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sv[v] = sc[v] * a.scale_log2;
+            if (b0 + kBS - 1 > tile_min[ct]) {  // some column of the tile stops inside this block
+#pragma unroll
+              for (int v = 0; v < 4; ++v) sv[v] = (b0 + 4 * tq + v <= lim[ct]) ? sv[v] : -INFINITY;
+            }
+            float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            mx = max_xor32(max_xor16(mx));
+            const bool bump = mx > mm[ct] + kLazyLog2;
+            if (__builtin_amdgcn_ballot_w64(bump)) {
+              const float m_new = bump ? mx : mm[ct];
+              const float alpha = mm[ct] == -INFINITY ? 0.f : exp2_neg(mm[ct] - m_new);
+              ll[ct] *= alpha;
+#pragma unroll
+              for (int t = 0; t < NT; ++t) acc[ct][t] *= alpha;
+              mm[ct] = m_new;
+            }
+            float pw[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) pw[v] = sv[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[v] - mm[ct]);
+            ll[ct] += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+            u32x2_t ph, pl2;
+            M::split(pw, ph, pl2);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              const u32x2_t a0 = u32x2_t{f.v[c][0], f.v[c][1]};
+              const u32x2_t a1 = u32x2_t{f.v[c][2], f.v[c][3]};
+              acc[ct][2 * c] = M::mma_pv(a0, ph, acc[ct][2 * c]);
+              acc[ct][2 * c + 1] = M::mma_pv(a1, ph, acc[ct][2 * c + 1]);
+              acc[ct][2 * c] = M::mma_pv(a0, pl2, acc[ct][2 * c]);
+              acc[ct][2 * c + 1] = M::mma_pv(a1, pl2, acc[ct][2 * c + 1]);
+            }
+          }
+        }
+      }
+    }
+  }
+  // wave states -> LDS
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const float lt = sum_xor32(sum_xor16(ll[ct]));
+    const int col = ct * 16 + r;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t *>(&sm.acc[wu][col][16 * t + 4 * tq]) = acc[ct][t];
+    if (tq == 0) {
+      sm.m[wu][col] = mm[ct];
+      sm.l[wu][col] = lt;
+    }
+  }
+  if (__syncthreads_or(bad)) {
+    for (int i = tid; i < ni * G * D; i += kThreads) {
+      const int tk = i / (G * D), h = (i / D) % G, d = i % D;
+      const int64_t row = (int64_t)(q0 + i0 + tk) * Hq + g * G + h;
+      if (nparts == 1) {
+        store_out(a.out, row * D + d, NAN, a.out_dtype);
+      } else {
+        const int64_t prow = row * a.max_parts + p;
+        a.ws_acc[prow * D + d] = NAN;
+        if (d == 0) {
+          a.ws_ml[prow * 2] = NAN;
+          a.ws_ml[prow * 2 + 1] = NAN;
+        }
+      }
+    }
+    return;
+  }
+  // fold the four waves; a wave (or the whole group) that saw no position of
+  // a column leaves m = -inf, l = 0 for it
+  for (int i = tid; i < ni * G * D; i += kThreads) {
+    const int tk = i / (G * D), h = (i / D) % G, d = i % D;
+    const int col = (tk / a.tpt) * 16 + (tk % a.tpt) * G + h;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, sm.m[w][col]);
+    float num = 0.f, den = 0.f;
+    if (Mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = exp2f(sm.m[w][col] - Mx);  // 0 for m = -inf
+        num += f * sm.acc[w][col][d];
+        den += f * sm.l[w][col];
+      }
+    }
+    const int64_t row = (int64_t)(q0 + i0 + tk) * Hq + g * G + h;
+    if (nparts == 1) {
+      store_out(a.out, row * D + d, num / den, a.out_dtype);
+    } else {
+      const int64_t prow = row * a.max_parts + p;
+      a.ws_acc[prow * D + d] = num;
+      if (d == 0) {
+        a.ws_ml[prow * 2] = Mx;
+        a.ws_ml[prow * 2 + 1] = den;
+      }
+    }
+  }
+}
+
+// One wave per (query row, head) whose group was split: folds its partials.
+template <int D>
+__global__ __launch_bounds__(kMergeWaves * 64) void pa_extend_merge_kernel(ExtendArgs a) {
+  const int lane = threadIdx.x % 64;
+  const int64_t row = (int64_t)blockIdx.x * kMergeWaves + threadIdx.x / 64;
+  if (row >= (int64_t)a.num_rows * a.num_q_heads) return;
+  const int t = (int)(row / a.num_q_heads);
+  const int s = seq_of_row(a.query_start, a.num_seqs, t);
+  const int L = a.context_lens[s];
+  const int q0 = a.query_start[s], n = a.query_start[s + 1] - q0;
+  if (!extend_rows_valid(q0, n, a) || !extend_seq_valid(L, n, a)) return;
+  const int i = t - q0;
+  if (i < 0 || i >= n) return;
+  const int qg = i / a.tpg;
+  const int pl = L - n + min(n, (qg + 1) * a.tpg) - 1;
+  const int np = (pl + 1 + a.part_tokens - 1) / a.part_tokens;
+  if (np <= 1) return;
+  merge_row<D>(a.out, a.out_dtype, row, a.ws_ml + row * a.max_parts * 2, 2,
+               a.ws_acc + row * a.max_parts * D, D, np, lane);
 }
 
 // ---------------------------------------------------------------- KV append
@@ -2163,6 +2452,155 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst_pa
                      static_cast<uint8_t *>(k_cache), static_cast<uint8_t *>(v_cache), src_dst_pairs,
                      block_bytes, num_blocks);
   return hip_check(hipGetLastError(), "pa_copy_blocks launch");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- extend: host side
+namespace {
+
+struct ExtendShape {
+  int nct, tpt, tpg, qgroups, pt, np;
+};
+
+pa_status validate_extend(const pa_extend_params *p) {
+  if (!p) return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: params is NULL");
+  if (!p->out || !p->q || !p->k_cache || !p->v_cache || !p->block_tables || !p->context_lens || !p->query_start)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: NULL device pointer");
+  if (!aligned16(p->out) || !aligned16(p->q) || !aligned16(p->k_cache) || !aligned16(p->v_cache) ||
+      !aligned16(p->block_tables) || !aligned16(p->context_lens) || !aligned16(p->query_start))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: device pointers must be 16-byte aligned");
+  if (p->num_seqs < 0 || p->num_seqs > 65535 || p->num_query_rows < 0)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: num_seqs must be in [0, 65535], num_query_rows >= 0");
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads || p->num_kv_heads > 65535)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: num_q_heads must be a positive multiple of num_kv_heads");
+  if (p->num_q_heads / p->num_kv_heads > 16)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_extend: at most 16 query heads per KV head");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_extend: head_dim must be 64 or 128");
+  if (p->kv_dtype != PA_F16 && p->kv_dtype != PA_BF16)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_extend: the cache must be fp16 or bf16");
+  if (p->out_dtype != PA_F32 && p->out_dtype != p->kv_dtype)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_extend: out_dtype must be F32 or the cache type");
+  if (p->max_blocks_per_seq <= 0 || p->num_blocks <= 0 || p->max_context_len < 0 || p->max_query_len < 0)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: sizes must be positive");
+  if (p->partition_tokens < 0 || p->partition_tokens % kBS)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: partition_tokens must be 0 or a positive multiple of 16");
+  if (!std::isfinite(p->scale)) return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: scale must be finite");
+  return PA_OK;
+}
+
+ExtendShape extend_shape(const pa_extend_params *p) {
+  ExtendShape e;
+  const int G = p->num_q_heads / p->num_kv_heads;
+  const int mq = std::max(p->max_query_len, 1);
+  e.tpt = 16 / G;
+  e.nct = (int64_t)mq * G > 16 ? kExtNctMax : 1;
+  e.tpg = e.nct * e.tpt;
+  e.qgroups = (mq + e.tpg - 1) / e.tpg;
+  const int ctx = ((std::max(p->max_context_len, 1) + kBS - 1) / kBS) * kBS;
+  if (p->partition_tokens > 0) {
+    e.pt = p->partition_tokens;
+  } else {
+    // enough workgroups for about two per CU, partitions of at least 64 tokens
+    const int64_t base = (int64_t)std::max(p->num_seqs, 1) * p->num_kv_heads * e.qgroups;
+    const int64_t want = 2LL * cu_count();
+    const int64_t parts = base >= want ? 1 : (want + base - 1) / base;
+    int64_t pt = (ctx + parts - 1) / parts;
+    pt = std::max<int64_t>(64, (pt + kBS - 1) / kBS * kBS);
+    e.pt = (int)std::min<int64_t>(pt, ctx);
+  }
+  e.np = (ctx + e.pt - 1) / e.pt;
+  return e;
+}
+
+size_t extend_ws_bytes(const pa_extend_params *p, const ExtendShape &e) {
+  if (e.np <= 1) return 0;
+  return (size_t)p->num_query_rows * p->num_q_heads * e.np * (p->head_dim + 2) * sizeof(float);
+}
+
+template <int D>
+const void *extend_kernel(pa_dtype dt, int nct) {
+  if (dt == PA_BF16)
+    return nct == 1 ? reinterpret_cast<const void *>(&pa_extend_kernel<PA_BF16, D, 1>)
+                    : reinterpret_cast<const void *>(&pa_extend_kernel<PA_BF16, D, kExtNctMax>);
+  return nct == 1 ? reinterpret_cast<const void *>(&pa_extend_kernel<PA_F16, D, 1>)
+                  : reinterpret_cast<const void *>(&pa_extend_kernel<PA_F16, D, kExtNctMax>);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_extend_partition_tokens(const pa_extend_params *p) {
+  pa_status st = validate_extend(p);
+  if (st != PA_OK) return -(int32_t)st;
+  return extend_shape(p).pt;
+}
+
+size_t pa_extend_workspace_bytes(const pa_extend_params *p) {
+  if (validate_extend(p) != PA_OK) return 0;
+  return extend_ws_bytes(p, extend_shape(p));
+}
+
+pa_status pa_extend(const pa_extend_params *p, void *workspace, size_t workspace_bytes, void *stream) {
+  pa_status st = validate_extend(p);
+  if (st != PA_OK) return st;
+  const ExtendShape e = extend_shape(p);
+  const size_t need = extend_ws_bytes(p, e);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return pa::fail(PA_ERR_WORKSPACE, "pa_extend: workspace of %zu bytes (16-byte aligned) required, got %zu",
+                    need, workspace ? workspace_bytes : (size_t)0);
+  const int64_t grid = (int64_t)p->num_kv_heads * p->num_seqs * e.qgroups * e.np;
+  if (grid > INT32_MAX)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_extend: more than 2^31-1 workgroups (raise partition_tokens)");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  LaunchEvents ev;
+  ev.start = static_cast<hipEvent_t>(p->start_event);
+  ev.stop = static_cast<hipEvent_t>(p->stop_event);
+  if (p->num_seqs == 0 || p->num_query_rows == 0) return record_events(ev, hs, "pa_extend events");
+  ExtendArgs a;
+  a.out = p->out;
+  a.q = p->q;
+  a.k_cache = static_cast<const uint8_t *>(p->k_cache);
+  a.v_cache = static_cast<const uint8_t *>(p->v_cache);
+  a.block_tables = p->block_tables;
+  a.context_lens = p->context_lens;
+  a.query_start = p->query_start;
+  a.ws_ml = need ? static_cast<float *>(workspace) : nullptr;
+  a.ws_acc = need ? static_cast<float *>(workspace) + (size_t)p->num_query_rows * p->num_q_heads * e.np * 2 : nullptr;
+  a.num_seqs = p->num_seqs;
+  a.num_q_heads = p->num_q_heads;
+  a.num_kv_heads = p->num_kv_heads;
+  a.group = p->num_q_heads / p->num_kv_heads;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.num_blocks = p->num_blocks;
+  a.max_ctx = p->max_context_len;
+  a.max_q = p->max_query_len;
+  a.num_rows = p->num_query_rows;
+  a.max_parts = e.np;
+  a.part_tokens = e.pt;
+  a.out_dtype = p->out_dtype;
+  a.qgroups = e.qgroups;
+  a.tpt = e.tpt;
+  a.tpg = e.tpg;
+  a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  const bool merge = e.np > 1;
+  LaunchEvents first, second;
+  first.start = ev.start;
+  (merge ? second : first).stop = ev.stop;
+  void *args[] = {&a};
+  const void *fn = p->head_dim == 128 ? extend_kernel<128>(p->kv_dtype, e.nct) : extend_kernel<64>(p->kv_dtype, e.nct);
+  hipError_t err = launch_kernel(fn, dim3((unsigned)grid), dim3(kThreads), args, 0, hs, first);
+  if (err != hipSuccess) return hip_check(err, "pa_extend launch");
+  if ((st = hip_check(hipGetLastError(), "pa_extend launch")) != PA_OK || !merge) return st;
+  const int64_t rows = (int64_t)p->num_query_rows * p->num_q_heads;
+  const void *mfn = p->head_dim == 128 ? reinterpret_cast<const void *>(&pa_extend_merge_kernel<128>)
+                                       : reinterpret_cast<const void *>(&pa_extend_merge_kernel<64>);
+  err = launch_kernel(mfn, dim3((unsigned)((rows + kMergeWaves - 1) / kMergeWaves)), dim3(kMergeWaves * 64), args,
+                      0, hs, second);
+  if (err != hipSuccess) return hip_check(err, "pa_extend merge launch");
+  return hip_check(hipGetLastError(), "pa_extend merge launch");
 }
 
 }  // extern "C"
