@@ -503,6 +503,84 @@ def run_copy_calibration(nbytes):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
+def run_extend_bench(args, wl, k):
+    """Speculative verification on the workload: the last k cached tokens of every
+    sequence are the drafted ones, each attending causally (pa_extend), over R
+    replicas in rotation.  Events ride on the dispatches of the timed calls."""
+    import torch
+    from paged_kv_cache_65_amd import binding as pa
+    spec = wl.spec
+    dev = torch.device("cuda:0")
+    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    R, K, W = args.replicas, args.steps, args.warmup
+    MB = int(-(-int(wl.prompt_lens.max()) // 16))
+
+    def to_dev(a):
+        if spec.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    k_rows_d, v_rows_d = to_dev(wl.k_tokens), to_dev(wl.v_tokens)
+    reps = []
+    for r in range(R):
+        order = wl.free_order if r == 0 else \
+            np.random.default_rng(spec.seed * 1000 + r).permutation(wl.num_blocks).astype(np.int32)
+        reps.append(build_replica(pa, torch, wl, order, k_rows_d, v_rows_d, MB, S, dev))
+    del k_rows_d, v_rows_d
+    T = S * k
+    rng = np.random.default_rng(spec.seed + 77)
+    q = to_dev(workloads.round_to(rng.standard_normal((T, Hq, D), dtype=np.float32), spec.dtype))
+    qs = torch.arange(0, T + 1, k, dtype=torch.int32, device=dev)
+    hip = Hip()
+    params, outs, tabs = [], [], []
+    for rep in reps:
+        tab, lens = rep.pool.seq_export(rep.seq_ids, MB)
+        tab_d, lens_d = torch.from_numpy(tab).to(dev), torch.from_numpy(lens).to(dev)
+        out = torch.empty((T, Hq, D), dtype=q.dtype, device=dev)
+        prm = pa.make_extend_params(out, q, rep.k_cache, rep.v_cache, tab_d, lens_d, qs, Hkv, int(lens.max()), k,
+                                    spec.fp32_scale(), partition_tokens=args.partition_tokens)
+        params.append(prm)
+        outs.append(out)
+        tabs.append((tab_d, lens_d, lens))
+    need = max(pa.pa_extend_workspace_bytes(p_) for p_ in params)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = ctypes.c_void_p(ws.data_ptr()), ws.numel()
+    L = pa.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ev_a = [hip.event(timing=True) for _ in range(K)]
+    ev_b = [hip.event(timing=True) for _ in range(K)]
+    for i in range(W):
+        pa._check(L.pa_extend(ctypes.byref(params[i % R]), ws_ptr, ws_bytes, stream))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        prm = params[i % R]
+        prm.start_event, prm.stop_event = ev_a[i], ev_b[i]
+        pa._check(L.pa_extend(ctypes.byref(prm), ws_ptr, ws_bytes, stream))
+        prm.start_event = prm.stop_event = None
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    call_ms = np.array([hip.elapsed_ms(ev_a[i], ev_b[i]) for i in range(K)])
+    lens = tabs[0][2]
+    eb = accounting.ELEM_BYTES[spec.dtype]
+    kv = int(np.sum(lens)) * 2 * Hkv * D * eb
+    small = 2 * T * Hq * D * eb + 4 * int(np.sum(-(-lens // 16))) + 4 * S + 4 * (S + 1)
+    alg = kv + small
+    call_s = float(call_ms.mean()) / 1e3
+    rec = {"metric": "speculative-verify attention tokens/s (k drafted tokens per sequence, pa_extend)",
+           "value": round(T * K / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+           "ms_per_step": round(elapsed / K * 1e3, 5), "higher_is_better": True, "dtype": spec.dtype,
+           "data": "synthetic",
+           "config": {"workload": spec.name, "draft_tokens": k, "query_rows": T,
+                      "partition_tokens": pa.pa_extend_partition_tokens(params[0]), "replicas": R,
+                      "device": torch.cuda.get_device_name(0)},
+           "roofline": {"kernel": "pa_extend (attention + merge)", "bound": "hbm",
+                        "achieved": round(alg / call_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(alg / call_s / 1e9 / HBM_PEAK_GBPS, 4),
+                        "algorithmic_bytes_per_launch": alg, "mean_call_us": round(call_s * 1e6, 2)}}
+    print(json.dumps(rec), flush=True)
+
+
 def run_swap_bench(blocks, reps):
     """Swap-out (device -> pinned host) and swap-in (host -> device) of `blocks`
     scattered blocks of the 70B-GQA cache shape (8 KV heads, D = 128, bf16:
@@ -576,6 +654,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--extend", type=int, default=0, metavar="K",
+                    help="only measure multi-query attention with K new tokens per sequence of the workload")
     ap.add_argument("--swap", type=int, default=0, metavar="BLOCKS",
                     help="only measure swap-out / swap-in of BLOCKS scattered cache blocks")
     args = ap.parse_args()
@@ -597,6 +677,9 @@ def main():
     wl = workloads.generate(spec)
     log(f"workload {spec.name} generated in {time.perf_counter() - t:.1f} s "
         f"(sum of prompt lengths {int(wl.prompt_lens.sum())})")
+    if args.extend:
+        run_extend_bench(args, wl, args.extend)
+        return
     g = run_gpu(args, wl)
     K = args.steps
     tok_s = spec.num_seqs * K / g["elapsed"]
