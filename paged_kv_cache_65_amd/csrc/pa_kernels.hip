@@ -550,8 +550,11 @@ __device__ void flush_parked(const DecodeArgs &a, const float *st, int64_t row0,
 //   scales: the four tokens 4c .. 4c+3 of the lane's score rows.
 // ============================================================================
 template <int QDT, int D>
-struct MfmaWaveI8 : MfmaWave<QDT, D> {
-  using Base = MfmaWave<QDT, D>;
+struct MfmaWaveI8 : MfmaWave<PA_F16, D> {
+  // fp16 matrix ops: a code c becomes an fp16 value exactly in three
+  // instructions per pair (pair16), and q (QDT) is carried in fp16 with a
+  // power-of-two prescale per (sequence, KV head) pair (load_q).
+  using Base = MfmaWave<PA_F16, D>;
   using typename Base::v8;
   using Base::NC;
   using Base::NT;
@@ -582,16 +585,61 @@ struct MfmaWaveI8 : MfmaWave<QDT, D> {
     f.vs = __builtin_nontemporal_load(&vsp[lane / 16]);
   }
 
-  // Two sign-extended codes of w (bytes i, i+1) as a packed pair of 16-bit values.
+  // Codes i, i+1 of w as a packed pair of fp16 values, exactly: each byte b
+  // goes under a 0x64 high byte with its top bit flipped, which is the fp16
+  // value 1024 + (b ^ 0x80) = 1152 + int8(b); one packed subtraction of 1152
+  // leaves int8(b).
   __device__ static uint32_t pair16(uint32_t w, int i) {
-    const float lo = (float)(int8_t)(w >> (8 * i));
-    const float hi = (float)(int8_t)(w >> (8 * i + 8));
-    if constexpr (QDT == PA_BF16)
-      return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
-    else
-      return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+    using h2 = _Float16 __attribute__((ext_vector_type(2)));
+    const uint32_t biased = __builtin_amdgcn_perm(0u, w, i == 0 ? 0x0c010c00u : 0x0c030c02u) ^ 0x64806480u;
+    const h2 x = __builtin_bit_cast(h2, biased) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
+    return __builtin_bit_cast(uint32_t, x);
+  }
+
+  float qscale;  // 2^-e undoes the prescale of q in the scores
+
+  // q rows (QDT) -> fp16 fragments scaled by 2^e, e chosen per wave so the
+  // largest |q| of the G rows lands in [2^14, 2^15): a bf16 or fp16 value is
+  // then exact in fp16 unless it is below 2^-28 of that largest one.
+  template <class P>
+  __device__ void load_q(const P *rows, int G, int lane) {
+    const int r = lane % 16, tq = lane / 16;
+    const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(rows) + (r < G ? r : 0) * (D / 8);
+    float x[NC][8];
+    float mx = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const u32x4_t w = qrow[4 * c + tq];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t h = (w[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+        float v;
+        if constexpr (QDT == PA_BF16)
+          v = __uint_as_float(h << 16);
+        else
+          v = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+        x[c][e] = r < G ? v : 0.f;
+        mx = fmaxf(mx, fabsf(x[c][e]));
+      }
+    }
+    mx = max_xor32(max_xor16(row_max16(mx)));
+    int ex = 0;
+    if (mx > 0.f && mx == mx && mx != INFINITY) {
+      int k;
+      (void)frexpf(mx, &k);  // mx = f * 2^k, f in [0.5, 1)
+      ex = min(max(15 - k, -126), 126);  // 2^ex and 2^-ex stay finite
+    }
+    const float up = ldexpf(1.f, ex);
+    qscale = ldexpf(1.f, -ex);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        h[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(x[c][2 * e] * up)) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(x[c][2 * e + 1] * up)) << 16);
+      this->qB[c] = __builtin_bit_cast(v8, u32x4_t{h[0], h[1], h[2], h[3]});
+    }
   }
 
   __device__ void compute(Frag &f, uint32_t vm, float scale_log2, int lane, int /*new_tok*/,
@@ -606,8 +654,9 @@ struct MfmaWaveI8 : MfmaWave<QDT, D> {
       sc = Base::mma_qk(__builtin_bit_cast(v8, ab), this->qB[c], sc);
     }
     float s[4];
+    const float sl = scale_log2 * qscale;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s[v] = sc[v] * f.ks[v] * scale_log2;
+    for (int v = 0; v < 4; ++v) s[v] = sc[v] * f.ks[v] * sl;
     // tokens outside the attended range: scores masked (their scales may be anything)
 #pragma unroll
     for (int v = 0; v < 4; ++v) s[v] = ((mine >> v) & 1u) ? s[v] : -INFINITY;
