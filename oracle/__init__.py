@@ -79,9 +79,18 @@ def _load():
                                                     _I64, _I]
         lib.oracle_copy_blocks_i8.restype = None
         lib.oracle_copy_blocks_i8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I]
-        lib.oracle_decode_i8.restype = _I
-        lib.oracle_decode_i8.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
-                                         _I, ctypes.c_float, _I, _I]
+        lib.oracle_decode_codes.restype = _I
+        lib.oracle_decode_codes.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                            _I, ctypes.c_float, _I, _I, _I]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [_I]
+        lib.oracle_e4m3_encode.restype = _I
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.oracle_quantize_row_fp8.restype = ctypes.c_float
+        lib.oracle_quantize_row_fp8.argtypes = [_P, _I64, _I, _I, _P]
+        lib.oracle_reshape_and_cache_fp8.restype = _I
+        lib.oracle_reshape_and_cache_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
+                                                     _I64, _I]
         lib.oracle_extend.restype = _I
         lib.oracle_extend.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                       ctypes.c_float, _I, _I]
@@ -253,15 +262,53 @@ def copy_blocks_i8(k_cache, v_cache, k_scales, v_scales, pairs, num_kv_heads, he
 
 
 def decode_i8(q, q_dtype, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens,
-              num_kv_heads, scale, nthreads=0, return_threads=False, window=0):
-    """fp64 paged decode over an int8 cache; q is [S][Hq][D] in q_dtype."""
+              num_kv_heads, scale, nthreads=0, return_threads=False, window=0, fp8=False):
+    """fp64 paged decode over an int8 cache (an E4M3 one with fp8=True; codes as
+    uint8); q is [S][Hq][D] in q_dtype."""
     q = _check(q, q_dtype)
     S, Hq, D = q.shape
     tables = np.ascontiguousarray(block_tables, dtype=np.int32)
     lens = np.ascontiguousarray(context_lens, dtype=np.int32)
     out = np.empty((S, Hq, D), dtype=np.float64)
-    used = _load().oracle_decode_i8(_ptr(out), _ptr(q), _DTYPES[q_dtype], _ptr(k_cache), _ptr(v_cache),
-                                    _ptr(k_scales), _ptr(v_scales), _ptr(tables), _ptr(lens), S, Hq,
-                                    num_kv_heads, D, tables.shape[1], float(scale), int(window),
-                                    nthreads)
+    used = _load().oracle_decode_codes(_ptr(out), _ptr(q), _DTYPES[q_dtype], _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(k_scales), _ptr(v_scales), _ptr(tables), _ptr(lens), S, Hq,
+                                       num_kv_heads, D, tables.shape[1], float(scale), int(window),
+                                       int(fp8), nthreads)
     return (out, used) if return_threads else out
+
+
+# ---------------------------------------------------------------- FP8 (E4M3) caches
+def e4m3_value(code: int) -> float:
+    return _load().oracle_e4m3_value(int(code))
+
+
+def e4m3_encode(x: float) -> int:
+    return _load().oracle_e4m3_encode(float(x))
+
+
+def quantize_row_fp8(row: np.ndarray, dtype: str):
+    """(codes uint8 [n], scale float32) of one row in the given type."""
+    row = _check(np.asarray(row), dtype)
+    codes = np.empty(row.size, dtype=np.uint8)
+    sc = _load().oracle_quantize_row_fp8(_ptr(row), 0, row.size, _DTYPES[dtype], _ptr(codes))
+    return codes, np.float32(sc)
+
+
+def empty_cache_fp8(num_blocks, num_kv_heads, head_dim):
+    """(codes, scales) of an unwritten FP8 pool: NaN codes 0x7F, NaN scales."""
+    codes = np.full(num_blocks * num_kv_heads * 16 * head_dim, 0x7F, dtype=np.uint8)
+    scales = np.full(num_blocks * num_kv_heads * 16, np.nan, dtype=np.float32)
+    return codes, scales
+
+
+def reshape_and_cache_fp8(k_new, v_new, k_cache, v_cache, k_scales, v_scales, slot_mapping,
+                          num_kv_heads, head_dim, num_blocks, src_dtype):
+    """Quantize [T][Hkv][D] rows into the FP8 caches in place; returns #out-of-range slots."""
+    k_new = _check(k_new, src_dtype)
+    v_new = _check(v_new, src_dtype)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    for a, t in ((k_cache, np.uint8), (v_cache, np.uint8), (k_scales, np.float32), (v_scales, np.float32)):
+        assert a.dtype == t and a.flags["C_CONTIGUOUS"]
+    return _load().oracle_reshape_and_cache_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                                _ptr(k_scales), _ptr(v_scales), _ptr(slots), len(slots),
+                                                num_kv_heads, head_dim, num_blocks, _DTYPES[src_dtype])

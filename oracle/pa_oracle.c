@@ -437,6 +437,91 @@ float oracle_quantize_row_i8(const void *x, int64_t first, int n, int src_dtype,
   return scale;
 }
 
+/* ===========================================================================
+ * FP8 (OCP E4M3) codes, same tiles and per-row scales as the int8 cache.
+ * A code is s eeee mmm: exponent bias 7; e = 0 is subnormal (m * 2^-9);
+ * e = 15 with m = 7 is NaN (no infinities); largest finite 448 (0x7E).
+ * Quantization, read from the int8 recipe of "LLM Inference Optimization:
+ * KV-Cache, PagedAttention, and GPU Memory Efficiency" (Future
+ * Optimizations) with FP8's range ("Modern AI Infrastructure ..." names an
+ * fp8 KV cache): scale = max |x| / 448 in float32, code = the E4M3 value
+ * nearest to x / scale (float32 division), ties to the even code, values
+ * beyond 448 saturate to +-448, NaN -> 0x7F; an all-zero row has scale 0.
+ * ------------------------------------------------------------------------ */
+double oracle_e4m3_value(int code) {
+  int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Nearest finite E4M3 value by search over the 127 non-negative codes. */
+int oracle_e4m3_encode(float x) {
+  if (x != x) return 0x7F;
+  int sign = signbit(x) ? 0x80 : 0;
+  double a = fabs((double)x);
+  if (a >= 448.0) return sign | 0x7E;
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double d = fabs(oracle_e4m3_value(c) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return sign | best;
+}
+
+float oracle_quantize_row_fp8(const void *x, int64_t first, int n, int src_dtype, uint8_t *codes) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float a = (float)fabs(load_elem(x, first + i, src_dtype));
+    if (a > amax) amax = a;
+  }
+  float scale = amax / 448.0f;
+  for (int i = 0; i < n; ++i) {
+    if (scale == 0.0f) {
+      codes[i] = 0;
+      continue;
+    }
+    float v = (float)load_elem(x, first + i, src_dtype) / scale;
+    codes[i] = (uint8_t)oracle_e4m3_encode(v);
+  }
+  return scale;
+}
+
+int oracle_reshape_and_cache_fp8(const void *k_new, const void *v_new, uint8_t *k_cache,
+                                 uint8_t *v_cache, float *k_scales, float *v_scales,
+                                 const int64_t *slot_mapping, int num_tokens, int num_kv_heads,
+                                 int head_dim, int64_t num_blocks, int src_dtype) {
+  int bad = 0;
+  uint8_t *codes = (uint8_t *)malloc((size_t)head_dim);
+  for (int n = 0; n < num_tokens; ++n) {
+    int64_t s = slot_mapping[n];
+    if (s < 0) continue;
+    if (s >= num_blocks * ORC_BS) { ++bad; continue; }
+    int64_t blk = s / ORC_BS;
+    int t = (int)(s % ORC_BS);
+    for (int g = 0; g < num_kv_heads; ++g) {
+      int64_t row = ((int64_t)n * num_kv_heads + g) * head_dim;
+      int64_t sidx = (blk * num_kv_heads + g) * ORC_BS + t;
+      k_scales[sidx] = oracle_quantize_row_fp8(k_new, row, head_dim, src_dtype, codes);
+      for (int d = 0; d < head_dim; ++d)
+        k_cache[oracle_k_offset_i8(blk, g, t, d, num_kv_heads, head_dim)] = codes[d];
+      v_scales[sidx] = oracle_quantize_row_fp8(v_new, row, head_dim, src_dtype, codes);
+      for (int d = 0; d < head_dim; ++d)
+        v_cache[oracle_v_offset_i8(blk, g, t, d, num_kv_heads, head_dim)] = codes[d];
+    }
+  }
+  free(codes);
+  return bad;
+}
+
 /* Append with quantization: like oracle_reshape_and_cache, into int8 tiles
  * plus per-row scales.  Returns the number of out-of-range slots. */
 int oracle_reshape_and_cache_i8(const void *k_new, const void *v_new, int8_t *k_cache,
@@ -487,7 +572,12 @@ typedef struct {
   const float *k_scales, *v_scales;
   const int32_t *table;
   int num_kv_heads, head_dim, kv_head;
+  int fp8; /* codes are E4M3 (else int8) */
 } orc_src_i8;
+
+static double code_value(const orc_src_i8 *s, int8_t c) {
+  return s->fp8 ? oracle_e4m3_value((uint8_t)c) : (double)c;
+}
 
 static void attend_one_i8(double *out, const double *q, const orc_src_i8 *s, int L, int window,
                           double scale, double *sigma) {
@@ -504,7 +594,7 @@ static void attend_one_i8(double *out, const double *q, const orc_src_i8 *s, int
     double ks = (double)s->k_scales[(blk * s->num_kv_heads + s->kv_head) * ORC_BS + t];
     double dot = 0.0;
     for (int d = 0; d < D; ++d)
-      dot += q[d] * ((double)s->k_cache[oracle_k_offset_i8(blk, s->kv_head, t, d, s->num_kv_heads, D)] * ks);
+      dot += q[d] * (code_value(s, s->k_cache[oracle_k_offset_i8(blk, s->kv_head, t, d, s->num_kv_heads, D)]) * ks);
     sigma[i] = scale * dot;
     if (sigma[i] > M) M = sigma[i];
   }
@@ -519,17 +609,18 @@ static void attend_one_i8(double *out, const double *q, const orc_src_i8 *s, int
       int64_t blk = s->table[i / ORC_BS];
       int t = i % ORC_BS;
       double vs = (double)s->v_scales[(blk * s->num_kv_heads + s->kv_head) * ORC_BS + t];
-      acc += sigma[i] * ((double)s->v_cache[oracle_v_offset_i8(blk, s->kv_head, t, d, s->num_kv_heads, D)] * vs);
+      acc += sigma[i] * (code_value(s, s->v_cache[oracle_v_offset_i8(blk, s->kv_head, t, d, s->num_kv_heads, D)]) * vs);
     }
     out[d] = acc / Z;
   }
 }
 
-int oracle_decode_i8(double *out, const void *q, int q_dtype, const int8_t *k_cache,
-                     const int8_t *v_cache, const float *k_scales, const float *v_scales,
-                     const int32_t *tables, const int32_t *lens, int num_seqs, int num_q_heads,
-                     int num_kv_heads, int head_dim, int max_blocks, float scale, int window,
-                     int nthreads) {
+/* Decode over an int8 (fp8 = 0) or E4M3 (fp8 = 1) cache. */
+int oracle_decode_codes(double *out, const void *q, int q_dtype, const int8_t *k_cache,
+                        const int8_t *v_cache, const float *k_scales, const float *v_scales,
+                        const int32_t *tables, const int32_t *lens, int num_seqs, int num_q_heads,
+                        int num_kv_heads, int head_dim, int max_blocks, float scale, int window,
+                        int fp8, int nthreads) {
   int G = num_q_heads / num_kv_heads;
   int Lmax = 0;
   for (int s = 0; s < num_seqs; ++s)
@@ -551,7 +642,7 @@ int oracle_decode_i8(double *out, const void *q, int q_dtype, const int8_t *k_ca
       int s = sh / num_q_heads, h = sh % num_q_heads;
       for (int d = 0; d < head_dim; ++d) qd[d] = load_elem(q, (int64_t)sh * head_dim + d, q_dtype);
       orc_src_i8 src = {k_cache, v_cache, k_scales, v_scales, tables + (int64_t)s * max_blocks,
-                        num_kv_heads, head_dim, h / G};
+                        num_kv_heads, head_dim, h / G, fp8};
       attend_one_i8(out + (int64_t)sh * head_dim, qd, &src, lens[s], window, (double)scale, sigma);
     }
     free(sigma);

@@ -52,8 +52,8 @@ class Spec:
     decode_steps: int = 0                # tokens appended per sequence after the prompt
     partition_tokens: int = 0            # 0 = library default
     scale: Optional[float] = None        # None = 1/sqrt(head_dim) rounded to fp32
-    cache: str = ""                      # cache type when it differs from dtype: "i8"
-                                         # (int8 codes + per-row scales; q, rows, out in dtype)
+    cache: str = ""                      # cache type when it differs from dtype: "i8", "fp8"
+                                         # (int8 or E4M3 codes + per-row scales; q, rows, out in dtype)
     window: int = 0                      # sliding window W (0 = none): the query at L-1
                                          # attends to positions L-1-W .. L-1
 

@@ -43,17 +43,21 @@ def build(wl, steps: int = 0) -> OracleState:
     spec = wl.spec
     Hkv, D, dt = spec.num_kv_heads, spec.head_dim, spec.dtype
     pool = PoolModel(wl.num_blocks, BS, wl.free_order)
-    i8 = spec.cache == "i8"
+    i8 = spec.cache in ("i8", "fp8")
+    fp8 = spec.cache == "fp8"
     if i8:
-        kc, ks = oracle.empty_cache_i8(wl.num_blocks, Hkv, D)
-        vc, vs = oracle.empty_cache_i8(wl.num_blocks, Hkv, D)
+        empty = oracle.empty_cache_fp8 if fp8 else oracle.empty_cache_i8
+        kc, ks = empty(wl.num_blocks, Hkv, D)
+        vc, vs = empty(wl.num_blocks, Hkv, D)
     else:
         kc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
         vc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
         ks = vs = None
 
     def put(k, v, slots):
-        if i8:
+        if fp8:
+            oracle.reshape_and_cache_fp8(k, v, kc, vc, ks, vs, slots, Hkv, D, wl.num_blocks, dt)
+        elif i8:
             oracle.reshape_and_cache_i8(k, v, kc, vc, ks, vs, slots, Hkv, D, wl.num_blocks, dt)
         else:
             oracle.reshape_and_cache(k, v, kc, vc, slots, Hkv, D, wl.num_blocks, dt)
@@ -91,7 +95,7 @@ def build(wl, steps: int = 0) -> OracleState:
 def advance(wl, st: OracleState, step: int):
     spec = wl.spec
     slots, cows = st.pool.seq_append_batch(st.seq_ids)
-    i8 = spec.cache == "i8"
+    i8 = spec.cache in ("i8", "fp8")
     if cows:
         if i8:
             oracle.copy_blocks_i8(st.k_cache, st.v_cache, st.k_scales, st.v_scales, np.array(cows),
@@ -101,9 +105,9 @@ def advance(wl, st: OracleState, step: int):
                                spec.head_dim, spec.dtype)
         st.cow_log.extend(("step", *c) for c in cows)
     if i8:
-        oracle.reshape_and_cache_i8(wl.step_k[step], wl.step_v[step], st.k_cache, st.v_cache,
-                                    st.k_scales, st.v_scales, slots, spec.num_kv_heads,
-                                    spec.head_dim, wl.num_blocks, spec.dtype)
+        put = oracle.reshape_and_cache_fp8 if spec.cache == "fp8" else oracle.reshape_and_cache_i8
+        put(wl.step_k[step], wl.step_v[step], st.k_cache, st.v_cache, st.k_scales, st.v_scales, slots,
+            spec.num_kv_heads, spec.head_dim, wl.num_blocks, spec.dtype)
     else:
         oracle.reshape_and_cache(wl.step_k[step], wl.step_v[step], st.k_cache, st.v_cache, slots,
                                  spec.num_kv_heads, spec.head_dim, wl.num_blocks, spec.dtype)
@@ -121,9 +125,9 @@ def decode(wl, st: OracleState, max_blocks: int, nthreads: int = 0, seq_subset=N
     q = wl.q
     if seq_subset is not None:
         tab, lens, q = tab[seq_subset], lens[seq_subset], np.ascontiguousarray(q[seq_subset])
-    if spec.cache == "i8":
+    if spec.cache in ("i8", "fp8"):
         return oracle.decode_i8(q, spec.dtype, st.k_cache, st.v_cache, st.k_scales, st.v_scales,
                                 tab, lens, spec.num_kv_heads, spec.fp32_scale(), nthreads=nthreads,
-                                window=window)
+                                window=window, fp8=spec.cache == "fp8")
     return oracle.decode(q, st.k_cache, st.v_cache, tab, lens, spec.num_kv_heads,
                          spec.fp32_scale(), spec.dtype, nthreads=nthreads, window=window)
