@@ -44,6 +44,15 @@
  *   V: (t, d) -> (m*64 + (t/4)*16 + d%16)*16 + ((d%64)/16)*4 + t%4,  m = d/64
  * (again one 16-byte lane load per operand fragment); scales are float32
  * arrays k_scales, v_scales [num_blocks][num_kv_heads][16].
+ *
+ * FP8 caches (PA_FP8): the same tiles and scales with OCP E4M3 codes (sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 subnormal,
+ * S.1111.111 NaN, largest finite 448) standing for value(c) * sc, with
+ * sc = max_d |x_d| / 448 and c_d the E4M3 value nearest to x_d / sc (float32
+ * division), ties to the even code, saturating at +-448 -- the int8 recipe
+ * above with FP8's range (the pages name an fp8 KV cache without a recipe).
+ * pa_copy_blocks_int8 and pa_swap_blocks_int8 move the codes and scales of
+ * either kind of byte cache.
  */
 #ifndef PA_H
 #define PA_H
@@ -66,9 +75,10 @@ typedef enum pa_status {
   PA_ERR_HIP = 5           /* a HIP runtime call failed (e.g. launch error) */
 } pa_status;
 
-/* PA_I8: a cache of int8 codes with one float32 scale per (token, KV head)
- * row (see "INT8 caches" below); never a q or output type. */
-typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_I8 = 3 } pa_dtype;
+/* PA_I8 / PA_FP8: a cache of int8 / E4M3 codes with one float32 scale per
+ * (token, KV head) row (see "INT8 caches" and "FP8 caches" above); never a q
+ * or output type. */
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_I8 = 3, PA_FP8 = 4 } pa_dtype;
 
 /* Which decode kernel runs.  AUTO picks the matrix-core kernel for fp16/bf16
  * caches and the vector-ALU kernel for fp32. */
@@ -170,12 +180,12 @@ typedef struct pa_decode_params {
   const void *k_new;
   const void *v_new;
   const int64_t *slot_mapping;
-  /* INT8 caches (kv_dtype = PA_I8) only, else ignored: the type of q (F16 or
-   * BF16; out_dtype is F32 or q_dtype) and the float32 scale arrays
-   * [num_blocks][num_kv_heads][16].  Decoding an INT8 cache needs the
-   * matrix-core kernel and automatic partitioning (the balanced split); the
-   * fused append is not available for it (append with
-   * pa_reshape_and_cache_int8 first). */
+  /* INT8 and FP8 caches (kv_dtype = PA_I8 or PA_FP8) only, else ignored: the
+   * type of q (F16 or BF16; out_dtype is F32 or q_dtype) and the float32
+   * scale arrays [num_blocks][num_kv_heads][16].  Decoding a byte cache needs
+   * the matrix-core kernel and automatic partitioning (the balanced split);
+   * the fused append is not available for it (append with
+   * pa_reshape_and_cache_int8 / _fp8 first). */
   pa_dtype q_dtype;
   const float *k_scales;
   const float *v_scales;
@@ -361,7 +371,15 @@ pa_status pa_swap_blocks_int8(const int8_t *src_k, const int8_t *src_v, const fl
                               int32_t dst_num_blocks, const int32_t *src_dst_pairs, int32_t num_pairs,
                               int32_t num_kv_heads, int32_t head_dim, void *stream);
 
-/* pa_copy_blocks for an INT8 cache: codes and scales of every head. */
+/* pa_reshape_and_cache_int8 for an FP8 (E4M3) cache: codes and scales are
+ * bit-exact to the recipe under "FP8 caches". */
+pa_status pa_reshape_and_cache_fp8(const void *k_new, const void *v_new, uint8_t *k_cache,
+                                   uint8_t *v_cache, float *k_scales, float *v_scales,
+                                   const int64_t *slot_mapping, int32_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                   pa_dtype src_dtype, void *stream);
+
+/* pa_copy_blocks for an INT8 or FP8 cache: codes and scales of every head. */
 pa_status pa_copy_blocks_int8(int8_t *k_cache, int8_t *v_cache, float *k_scales, float *v_scales,
                               const int32_t *src_dst_pairs, int32_t num_pairs, int32_t num_kv_heads,
                               int32_t head_dim, int32_t num_blocks, void *stream);

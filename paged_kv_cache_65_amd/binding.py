@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_OOM, PA_ERR_HIP = range(6)
-PA_F32, PA_F16, PA_BF16, PA_I8 = 0, 1, 2, 3
+PA_F32, PA_F16, PA_BF16, PA_I8, PA_FP8 = 0, 1, 2, 3, 4
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
 KERNELS = {"auto": PA_KERNEL_AUTO, "valu": PA_KERNEL_VALU, "mfma": PA_KERNEL_MFMA}
 BLOCK_SIZE = 16
@@ -85,6 +85,8 @@ def lib():
             "pa_reshape_and_cache_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                                          _I32, ctypes.c_int, _P]),
             "pa_copy_blocks_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P]),
+            "pa_reshape_and_cache_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                                        _I32, ctypes.c_int, _P]),
             "pa_swap_blocks": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I32, _P, _I32, _I32, _I32,
                                               ctypes.c_int, _P]),
             "pa_swap_blocks_int8": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _P, _P, _I32, _P,
@@ -130,7 +132,11 @@ def pa_version() -> str:
 # ---------------------------------------------------------------- device calls
 def _dtype_code(t) -> int:
     import torch
-    codes = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
+    # an FP8 (E4M3) cache holds its codes in uint8 (or float8_e4m3fn) tensors
+    codes = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.int8: PA_I8,
+             torch.uint8: PA_FP8}
+    if hasattr(torch, "float8_e4m3fn"):
+        codes[torch.float8_e4m3fn] = PA_FP8
     if t.dtype not in codes:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return codes[t.dtype]
@@ -293,6 +299,16 @@ def pa_reshape_and_cache_int8(k_new, v_new, k_cache, v_cache, k_scales, v_scales
     _check(lib().pa_reshape_and_cache_int8(_dev(k_new), _dev(v_new), _dev(k_cache), _dev(v_cache),
                                            _dev(k_scales), _dev(v_scales), _dev(slot_mapping), T,
                                            Hkv, D, nb, _dtype_code(k_new), _stream(stream)))
+
+
+def pa_reshape_and_cache_fp8(k_new, v_new, k_cache, v_cache, k_scales, v_scales, slot_mapping,
+                             stream=None):
+    """Quantize [T][Hkv][D] fp16/bf16 rows into an E4M3 cache (uint8 codes) and its scales."""
+    T, Hkv, D = k_new.shape
+    nb = k_cache.numel() // (Hkv * BLOCK_SIZE * D)
+    _check(lib().pa_reshape_and_cache_fp8(_dev(k_new), _dev(v_new), _dev(k_cache), _dev(v_cache),
+                                          _dev(k_scales), _dev(v_scales), _dev(slot_mapping), T,
+                                          Hkv, D, nb, _dtype_code(k_new), _stream(stream)))
 
 
 def pa_copy_blocks_int8(k_cache, v_cache, k_scales, v_scales, src_dst_pairs, num_kv_heads,

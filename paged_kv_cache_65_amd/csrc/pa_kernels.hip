@@ -549,11 +549,14 @@ __device__ void flush_parked(const DecodeArgs &a, const float *st, int64_t row0,
 //     -> A operand of the P.V tile n = 4x + k;
 //   scales: the four tokens 4c .. 4c+3 of the lane's score rows.
 // ============================================================================
-template <int QDT, int D>
+// Byte-code caches: FMT = PA_I8 (int8 codes) or PA_FP8 (OCP E4M3 codes),
+// one float32 scale per (token, KV head) row.
+template <int QDT, int D, int FMT = PA_I8>
 struct MfmaWaveI8 : MfmaWave<PA_F16, D> {
-  // fp16 matrix ops: a code c becomes an fp16 value exactly in three
-  // instructions per pair (pair16), and q (QDT) is carried in fp16 with a
-  // power-of-two prescale per (sequence, KV head) pair (load_q).
+  // fp16 matrix ops: a code becomes an fp16 value exactly (pair16: three
+  // instructions per pair for int8, one conversion for E4M3), and q (QDT) is
+  // carried in fp16 with a power-of-two prescale per (sequence, KV head) pair
+  // (load_q).
   using Base = MfmaWave<PA_F16, D>;
   using typename Base::v8;
   using Base::NC;
@@ -591,9 +594,15 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D> {
   // leaves int8(b).
   __device__ static uint32_t pair16(uint32_t w, int i) {
     using h2 = _Float16 __attribute__((ext_vector_type(2)));
-    const uint32_t biased = __builtin_amdgcn_perm(0u, w, i == 0 ? 0x0c010c00u : 0x0c030c02u) ^ 0x64806480u;
-    const h2 x = __builtin_bit_cast(h2, biased) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
-    return __builtin_bit_cast(uint32_t, x);
+    if constexpr (FMT == PA_FP8) {
+      // every finite E4M3 value is an fp16 value (3 mantissa bits, 2^-9 .. 448)
+      return i == 0 ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false))
+                    : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+    } else {
+      const uint32_t biased = __builtin_amdgcn_perm(0u, w, i == 0 ? 0x0c010c00u : 0x0c030c02u) ^ 0x64806480u;
+      const h2 x = __builtin_bit_cast(h2, biased) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
+      return __builtin_bit_cast(uint32_t, x);
+    }
   }
 
   float qscale;  // 2^-e undoes the prescale of q in the scores
@@ -680,6 +689,17 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D> {
     this->l += (p[0] + p[1]) + (p[2] + p[3]);
     u32x2_t ph, pl;
     Base::split(pw, ph, pl);
+    if constexpr (FMT == PA_FP8) {
+      // an unwritten or stale E4M3 slot may hold a NaN code: clear the V
+      // bytes of tokens outside the attended range (a word holds this
+      // lane's four tokens of one dim, one byte each)
+      if (vm != kAllTokens) {
+        const uint32_t bm = ((mine & 1u) ? 0x000000FFu : 0u) | ((mine & 2u) ? 0x0000FF00u : 0u) |
+                            ((mine & 4u) ? 0x00FF0000u : 0u) | ((mine & 8u) ? 0xFF000000u : 0u);
+#pragma unroll
+        for (int x = 0; x < NV; ++x) f.v[x] &= u32x4_t{bm, bm, bm, bm};
+      }
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const uint32_t w = f.v[n / 4][n % 4];
@@ -1790,12 +1810,35 @@ __global__ __launch_bounds__(256) void pa_reshape_and_cache_kernel(
   }
 }
 
-// ---------------------------------------------------------------- INT8 append
+// ---------------------------------------------------------------- INT8 / FP8 append
 // One wave per (token, KV head) row: max |x| over the row by a wave
-// reduction, scale = max / 127 and codes = x / scale truncated toward zero
-// (float32, correctly rounded division), codes scattered into the int8 tile
-// layout, the scale stored beside it.
-template <int SDT, int D>
+// reduction, scale = max / 127 (int8) or max / 448 (E4M3), codes from
+// x / scale (float32, correctly rounded division): truncated toward zero
+// (int8) or rounded to the nearest E4M3 value, ties to even, saturating at
+// +-448 (e4m3_code); codes scattered into the byte tile layout, the scale
+// stored beside it.
+
+// Nearest E4M3 code of x: below 2^-6 the step is 2^-9 (subnormals, and 2^-6
+// itself as code 8); above, 3 mantissa bits under the exponent of x.
+__device__ inline uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return 0x7Fu;
+  if (a >= 448.f) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.f);
+  int e;
+  (void)frexpf(a, &e);                       // a in [2^(e-1), 2^e)
+  const int E = e - 1;                       // -6 .. 8
+  int q = (int)rintf((ldexpf(a, -E) - 1.f) * 8.f);  // 0 .. 8, ties to even
+  int ef = E + 7;
+  if (q == 8) {
+    q = 0;
+    ++ef;
+  }
+  return sign | min((uint32_t)((ef << 3) | q), 0x7Eu);
+}
+
+template <int SDT, int D, int FMT>
 __device__ void quantize_row_i8(const uint16_t *x, int8_t *tile_codes, float *scale_out, int t, bool is_v,
                                 int lane) {
   constexpr int PER = D / 64;
@@ -1809,12 +1852,16 @@ __device__ void quantize_row_i8(const uint16_t *x, int8_t *tile_codes, float *sc
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-  const float scale = amax / 127.0f;
+  const float scale = amax / (FMT == PA_FP8 ? 448.0f : 127.0f);
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int d = lane * PER + e;
     const float qv = scale == 0.f ? 0.f : v[e] / scale;
-    const int code = qv == qv ? (int)qv : 0;  // conversion truncates toward zero
+    int code;
+    if constexpr (FMT == PA_FP8)
+      code = scale == 0.f ? 0 : (int)e4m3_code(qv);
+    else
+      code = qv == qv ? (int)qv : 0;  // conversion truncates toward zero
     int off;
     if (!is_v) {
       const int c = d / 64, w = d % 64;
@@ -1827,7 +1874,7 @@ __device__ void quantize_row_i8(const uint16_t *x, int8_t *tile_codes, float *sc
   if (lane == 0) *scale_out = scale;
 }
 
-template <int SDT, int D>
+template <int SDT, int D, int FMT>
 __global__ __launch_bounds__(256) void pa_reshape_and_cache_i8_kernel(
     const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new, int8_t *k_cache, int8_t *v_cache,
     float *k_scales, float *v_scales, const int64_t *__restrict__ slots, int32_t num_tokens,
@@ -1841,8 +1888,8 @@ __global__ __launch_bounds__(256) void pa_reshape_and_cache_i8_kernel(
   if (slot < 0 || slot >= num_slots) return;
   const int64_t tile = (slot / kBS) * num_kv_heads + g;
   const int t = (int)(slot % kBS);
-  quantize_row_i8<SDT, D>(k_new + row * D, k_cache + tile * kBS * D, k_scales + tile * kBS + t, t, false, lane);
-  quantize_row_i8<SDT, D>(v_new + row * D, v_cache + tile * kBS * D, v_scales + tile * kBS + t, t, true, lane);
+  quantize_row_i8<SDT, D, FMT>(k_new + row * D, k_cache + tile * kBS * D, k_scales + tile * kBS + t, t, false, lane);
+  quantize_row_i8<SDT, D, FMT>(v_new + row * D, v_cache + tile * kBS * D, v_scales + tile * kBS + t, t, true, lane);
 }
 
 // ---------------------------------------------------------------- block copy
@@ -1905,6 +1952,7 @@ __global__ __launch_bounds__(kSwapThreads) void pa_swap_blocks_kernel(
 // ============================================================================
 int elem_bytes(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
 bool valid_dtype(pa_dtype d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
+bool byte_cache(pa_dtype d) { return d == PA_I8 || d == PA_FP8; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 pa_status hip_check(hipError_t e, const char *what) {
@@ -1931,18 +1979,18 @@ pa_status validate(const pa_decode_params *p) {
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim must be 64 or 128");
   if (p->max_blocks_per_seq <= 0 || p->num_blocks <= 0 || p->max_context_len < 0)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: sizes must be positive");
-  if (!(valid_dtype(p->kv_dtype) || p->kv_dtype == PA_I8) || !valid_dtype(p->out_dtype))
+  if (!(valid_dtype(p->kv_dtype) || byte_cache(p->kv_dtype)) || !valid_dtype(p->out_dtype))
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: unknown dtype");
-  if (p->kv_dtype == PA_I8) {
+  if (byte_cache(p->kv_dtype)) {
     if (p->q_dtype != PA_F16 && p->q_dtype != PA_BF16)
-      return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: an INT8 cache needs q_dtype F16 or BF16");
+      return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: an INT8/FP8 cache needs q_dtype F16 or BF16");
     if (p->out_dtype != PA_F32 && p->out_dtype != p->q_dtype)
       return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype must be F32 or q_dtype");
     if (!p->k_scales || !p->v_scales || !aligned16(p->k_scales) || !aligned16(p->v_scales))
-      return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: an INT8 cache needs 16-byte aligned scale arrays");
+      return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: an INT8/FP8 cache needs 16-byte aligned scale arrays");
     if (p->kernel == PA_KERNEL_VALU || p->partition_tokens != 0 || p->k_new != nullptr)
       return pa::fail(PA_ERR_UNSUPPORTED,
-                      "pa_decode: an INT8 cache is decoded by the matrix-core kernel with automatic "
+                      "pa_decode: an INT8/FP8 cache is decoded by the matrix-core kernel with automatic "
                       "partitioning and no fused append");
   } else if (p->out_dtype != PA_F32 && p->out_dtype != p->kv_dtype) {
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype must be F32 or the cache type");
@@ -1970,9 +2018,9 @@ bool use_balanced(const pa_decode_params *p);
 pa_status validate_all(const pa_decode_params *p) {
   pa_status st = validate(p);
   if (st != PA_OK) return st;
-  if (p->kv_dtype == PA_I8 && !use_balanced(p))
+  if (byte_cache(p->kv_dtype) && !use_balanced(p))
     return pa::fail(PA_ERR_UNSUPPORTED,
-                    "pa_decode: an INT8 cache needs the balanced split (<= 1024 sequences, <= 32768 "
+                    "pa_decode: an INT8/FP8 cache needs the balanced split (<= 1024 sequences, <= 32768 "
                     "(sequence, KV head) pairs)");
   return PA_OK;
 }
@@ -2026,18 +2074,24 @@ const void *balanced_kernel(pa_dtype kv, pa_dtype qt, int D) {
     if (qt == PA_BF16) return D == 128 ? kfn<MfmaWaveI8<PA_BF16, 128>, 128>() : kfn<MfmaWaveI8<PA_BF16, 64>, 64>();
     return D == 128 ? kfn<MfmaWaveI8<PA_F16, 128>, 128>() : kfn<MfmaWaveI8<PA_F16, 64>, 64>();
   }
+  if (kv == PA_FP8) {
+    if (qt == PA_BF16)
+      return D == 128 ? kfn<MfmaWaveI8<PA_BF16, 128, PA_FP8>, 128>() : kfn<MfmaWaveI8<PA_BF16, 64, PA_FP8>, 64>();
+    return D == 128 ? kfn<MfmaWaveI8<PA_F16, 128, PA_FP8>, 128>() : kfn<MfmaWaveI8<PA_F16, 64, PA_FP8>, 64>();
+  }
   if (kv == PA_BF16) return D == 128 ? kfn<MfmaWave<PA_BF16, 128>, 128>() : kfn<MfmaWave<PA_BF16, 64>, 64>();
   return D == 128 ? kfn<MfmaWave<PA_F16, 128>, 128>() : kfn<MfmaWave<PA_F16, 64>, 64>();
 }
 
 int balanced_workgroups(pa_dtype kv, pa_dtype qt, int D, int G) {
-  static int cached[64][8][kGMax + 1] = {};
+  static int cached[64][12][kGMax + 1] = {};
   int dev = 0;
+  const bool bytes = byte_cache(kv);
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-    return (kv == PA_I8 ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU) * cu_count();
-  const int k = (kv == PA_I8 ? 4 : 0) + ((kv == PA_I8 ? qt : kv) == PA_BF16 ? 0 : 2) + (D == 128 ? 0 : 1);
+    return (bytes ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU) * cu_count();
+  const int k = (kv == PA_I8 ? 4 : kv == PA_FP8 ? 8 : 0) + ((bytes ? qt : kv) == PA_BF16 ? 0 : 2) + (D == 128 ? 0 : 1);
   if (!cached[dev][k][G]) {
-    const int want = kv == PA_I8 ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU;
+    const int want = bytes ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, balanced_kernel(kv, qt, D), kBThreads,
                                                      park_bytes(G, D)) != hipSuccess ||
@@ -2175,8 +2229,8 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
   a.v_cache = static_cast<const uint8_t *>(p->v_cache);
   a.block_tables = p->block_tables;
   a.context_lens = p->context_lens;
-  a.k_scales = p->kv_dtype == PA_I8 ? p->k_scales : nullptr;
-  a.v_scales = p->kv_dtype == PA_I8 ? p->v_scales : nullptr;
+  a.k_scales = byte_cache(p->kv_dtype) ? p->k_scales : nullptr;
+  a.v_scales = byte_cache(p->kv_dtype) ? p->v_scales : nullptr;
   a.k_new = static_cast<const uint8_t *>(p->k_new);
   a.v_new = static_cast<const uint8_t *>(p->v_new);
   a.slot_mapping = p->slot_mapping;
@@ -2333,37 +2387,62 @@ pa_status pa_reshape_and_cache(const void *k_new, const void *v_new, void *k_cac
   return hip_check(hipGetLastError(), "pa_reshape_and_cache launch");
 }
 
-pa_status pa_reshape_and_cache_int8(const void *k_new, const void *v_new, int8_t *k_cache, int8_t *v_cache,
-                                    float *k_scales, float *v_scales, const int64_t *slot_mapping,
-                                    int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-                                    int32_t num_blocks, pa_dtype src_dtype, void *stream) {
-  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0)
-    return pa::fail(PA_ERR_INVALID_ARG, "pa_reshape_and_cache_int8: bad sizes");
+}  // extern "C"
+
+namespace {
+
+template <int FMT>
+pa_status reshape_codes(const void *k_new, const void *v_new, void *k_cache, void *v_cache, float *k_scales,
+                        float *v_scales, const int64_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t num_blocks, pa_dtype src_dtype, void *stream, const char *who) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: bad sizes", who);
   if (head_dim != 64 && head_dim != 128)
-    return pa::fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache_int8: head_dim must be 64 or 128");
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128", who);
   if (src_dtype != PA_F16 && src_dtype != PA_BF16)
-    return pa::fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache_int8: rows must be F16 or BF16");
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: rows must be F16 or BF16", who);
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !k_cache || !v_cache || !k_scales || !v_scales || !slot_mapping)
-    return pa::fail(PA_ERR_INVALID_ARG, "pa_reshape_and_cache_int8: NULL device pointer");
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL device pointer", who);
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
       !aligned16(k_scales) || !aligned16(v_scales) || !aligned16(slot_mapping))
-    return pa::fail(PA_ERR_INVALID_ARG, "pa_reshape_and_cache_int8: device pointers must be 16-byte aligned");
+    return pa::fail(PA_ERR_INVALID_ARG, "%s: device pointers must be 16-byte aligned", who);
   const int64_t rows = (int64_t)num_tokens * num_kv_heads;
   const dim3 grid((unsigned)((rows + 3) / 4));
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const auto *kn = static_cast<const uint16_t *>(k_new);
   const auto *vn = static_cast<const uint16_t *>(v_new);
+  auto *kc = static_cast<int8_t *>(k_cache);
+  auto *vc = static_cast<int8_t *>(v_cache);
   const int64_t nslots = (int64_t)num_blocks * kBS;
   if (src_dtype == PA_BF16 && head_dim == 128)
-    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_BF16, 128>), grid, dim3(256), 0, hs, kn, vn, k_cache, v_cache, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
+    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_BF16, 128, FMT>), grid, dim3(256), 0, hs, kn, vn, kc, vc, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
   else if (src_dtype == PA_BF16)
-    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_BF16, 64>), grid, dim3(256), 0, hs, kn, vn, k_cache, v_cache, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
+    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_BF16, 64, FMT>), grid, dim3(256), 0, hs, kn, vn, kc, vc, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
   else if (head_dim == 128)
-    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_F16, 128>), grid, dim3(256), 0, hs, kn, vn, k_cache, v_cache, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
+    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_F16, 128, FMT>), grid, dim3(256), 0, hs, kn, vn, kc, vc, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
   else
-    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_F16, 64>), grid, dim3(256), 0, hs, kn, vn, k_cache, v_cache, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
-  return hip_check(hipGetLastError(), "pa_reshape_and_cache_int8 launch");
+    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_F16, 64, FMT>), grid, dim3(256), 0, hs, kn, vn, kc, vc, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
+  return hip_check(hipGetLastError(), who);
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_reshape_and_cache_int8(const void *k_new, const void *v_new, int8_t *k_cache, int8_t *v_cache,
+                                    float *k_scales, float *v_scales, const int64_t *slot_mapping,
+                                    int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t num_blocks, pa_dtype src_dtype, void *stream) {
+  return reshape_codes<PA_I8>(k_new, v_new, k_cache, v_cache, k_scales, v_scales, slot_mapping, num_tokens,
+                              num_kv_heads, head_dim, num_blocks, src_dtype, stream, "pa_reshape_and_cache_int8");
+}
+
+pa_status pa_reshape_and_cache_fp8(const void *k_new, const void *v_new, uint8_t *k_cache, uint8_t *v_cache,
+                                   float *k_scales, float *v_scales, const int64_t *slot_mapping,
+                                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t num_blocks, pa_dtype src_dtype, void *stream) {
+  return reshape_codes<PA_FP8>(k_new, v_new, k_cache, v_cache, k_scales, v_scales, slot_mapping, num_tokens,
+                               num_kv_heads, head_dim, num_blocks, src_dtype, stream, "pa_reshape_and_cache_fp8");
 }
 
 pa_status pa_copy_blocks_int8(int8_t *k_cache, int8_t *v_cache, float *k_scales, float *v_scales,

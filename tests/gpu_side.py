@@ -55,7 +55,7 @@ class GpuState:
 
 def _append_rows(st, k_rows, v_rows, slots, spec, cow_pairs):
     dev = st.k_cache.device
-    i8 = spec.cache == "i8"
+    i8 = spec.cache in ("i8", "fp8")
     if len(cow_pairs):
         pairs = torch.from_numpy(np.ascontiguousarray(cow_pairs, dtype=np.int32)).to(dev)
         if i8:
@@ -66,15 +66,19 @@ def _append_rows(st, k_rows, v_rows, slots, spec, cow_pairs):
     if len(slots):
         s = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).to(dev)
         kd, vd = to_device(k_rows, spec.dtype, dev), to_device(v_rows, spec.dtype, dev)
-        if i8:
+        if spec.cache == "fp8":
+            pa.pa_reshape_and_cache_fp8(kd, vd, st.k_cache, st.v_cache, st.k_scales, st.v_scales, s)
+        elif i8:
             pa.pa_reshape_and_cache_int8(kd, vd, st.k_cache, st.v_cache, st.k_scales, st.v_scales, s)
         else:
             pa.pa_reshape_and_cache(kd, vd, st.k_cache, st.v_cache, s)
 
 
-def i8_cache(num_blocks, num_kv_heads, head_dim, device="cuda"):
-    """(codes, scales) of an unwritten int8 pool: codes 0x7F, scales NaN."""
-    codes = torch.full((num_blocks * num_kv_heads * BS * head_dim,), 127, dtype=torch.int8, device=device)
+def i8_cache(num_blocks, num_kv_heads, head_dim, device="cuda", fp8=False):
+    """(codes, scales) of an unwritten int8 / E4M3 pool: codes 0x7F (a NaN code
+    for E4M3), scales NaN."""
+    codes = torch.full((num_blocks * num_kv_heads * BS * head_dim,), 127,
+                       dtype=torch.uint8 if fp8 else torch.int8, device=device)
     scales = torch.full((num_blocks * num_kv_heads * BS,), float("nan"), dtype=torch.float32, device=device)
     return codes, scales
 
@@ -82,9 +86,10 @@ def i8_cache(num_blocks, num_kv_heads, head_dim, device="cuda"):
 def build(wl, steps: int = 0, device="cuda") -> GpuState:
     spec = wl.spec
     pool = pa.BlockPool(wl.num_blocks, BS, wl.free_order)
-    if spec.cache == "i8":
-        kc, ks = i8_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, device)
-        vc, vs = i8_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, device)
+    if spec.cache in ("i8", "fp8"):
+        f8 = spec.cache == "fp8"
+        kc, ks = i8_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, device, fp8=f8)
+        vc, vs = i8_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, device, fp8=f8)
     else:
         kc = nan_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, spec.dtype, device)
         vc = nan_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, spec.dtype, device)
