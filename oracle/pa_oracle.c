@@ -459,21 +459,21 @@ double oracle_e4m3_value(int code) {
   return s ? -v : v;
 }
 
-/* Nearest finite E4M3 value by search over the 127 non-negative codes. */
+/* Nearest finite E4M3 value by search in the table of the 127 non-negative
+ * codes, whose values increase with the code: the last code not above |x|,
+ * then the nearer of it and the next one, ties to the even code. */
 int oracle_e4m3_encode(float x) {
   if (x != x) return 0x7F;
   int sign = signbit(x) ? 0x80 : 0;
   double a = fabs((double)x);
   if (a >= 448.0) return sign | 0x7E;
-  int best = 0;
-  double best_d = INFINITY;
-  for (int c = 0; c <= 0x7E; ++c) {
-    double d = fabs(oracle_e4m3_value(c) - a);
-    if (d < best_d || (d == best_d && (c & 1) == 0)) {
-      best = c;
-      best_d = d;
-    }
+  int lo = 0, hi = 0x7E; /* value(lo) <= a < value(hi) */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (oracle_e4m3_value(mid) <= a) lo = mid; else hi = mid;
   }
+  double dl = a - oracle_e4m3_value(lo), dh = oracle_e4m3_value(hi) - a;
+  int best = dl < dh ? lo : dh < dl ? hi : ((lo & 1) == 0 ? lo : hi);
   return sign | best;
 }
 
