@@ -180,12 +180,14 @@ def build_replica(pa, torch, wl, order, k_rows_d, v_rows_d, MB, S, dev):
     slots = torch.from_numpy(np.concatenate(slots_all)).to(dev)
     n_elems = nb * spec.num_kv_heads * 16 * spec.head_dim
     ks = vs = None
-    if spec.cache == "i8":
-        kc = torch.full((n_elems,), 127, dtype=torch.int8, device=dev)
-        vc = torch.full((n_elems,), 127, dtype=torch.int8, device=dev)
+    if spec.cache in ("i8", "fp8"):
+        code_t = torch.uint8 if spec.cache == "fp8" else torch.int8
+        kc = torch.full((n_elems,), 127, dtype=code_t, device=dev)
+        vc = torch.full((n_elems,), 127, dtype=code_t, device=dev)
         ks = torch.full((n_elems // spec.head_dim,), float("nan"), dtype=torch.float32, device=dev)
         vs = torch.full((n_elems // spec.head_dim,), float("nan"), dtype=torch.float32, device=dev)
-        pa.pa_reshape_and_cache_int8(k_rows_d, v_rows_d, kc, vc, ks, vs, slots)
+        quantize = pa.pa_reshape_and_cache_fp8 if spec.cache == "fp8" else pa.pa_reshape_and_cache_int8
+        quantize(k_rows_d, v_rows_d, kc, vc, ks, vs, slots)
     else:
         dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[spec.dtype]
         kc = torch.full((n_elems,), float("nan"), dtype=dt, device=dev)
@@ -258,7 +260,7 @@ def run_gpu(args, wl):
                                            sliding_window=spec.window)
         ws_need = max(ws_need, pa.pa_decode_workspace_bytes(rep.params))
         rep.params.max_context_len = rep.max_ctx
-        if args.append == "fused" and spec.cache != "i8":
+        if args.append == "fused" and spec.cache not in ("i8", "fp8"):
             rep.params.k_new = step_k_d.data_ptr()
             rep.params.v_new = step_v_d.data_ptr()
             rep.params.slot_mapping = slots_v.data_ptr()
@@ -318,8 +320,9 @@ def run_gpu(args, wl):
             ks=ctypes.c_void_p(rep.k_scales.data_ptr()) if rep.k_scales is not None else None,
             vs=ctypes.c_void_p(rep.v_scales.data_ptr()) if rep.v_scales is not None else None))
     pool_h = [rep.pool._h for rep in reps]
-    i8 = spec.cache == "i8"
-    fused = args.append == "fused" and not i8   # an INT8 cache appends with its own kernel
+    i8 = spec.cache in ("i8", "fp8")             # byte caches: codes + row scales
+    append_codes = L.pa_reshape_and_cache_fp8 if spec.cache == "fp8" else L.pa_reshape_and_cache_int8
+    fused = args.append == "fused" and not i8   # a byte cache appends with its own kernel
     k0, v0 = step_k_d.data_ptr(), step_v_d.data_ptr()
     torch.cuda.synchronize()
 
@@ -367,7 +370,7 @@ def run_gpu(args, wl):
             prm.v_new = v0 + i * row_bytes
             prm.slot_mapping = pp["slots_d"]
         elif i8:
-            pa._check(L.pa_reshape_and_cache_int8(ctypes.c_void_p(k0 + i * row_bytes),
+            pa._check(append_codes(ctypes.c_void_p(k0 + i * row_bytes),
                                                   ctypes.c_void_p(v0 + i * row_bytes), q["kc"], q["vc"],
                                                   q["ks"], q["vs"], ctypes.c_void_p(pp["slots_d"]), S, Hkv,
                                                   D, nb_rep, dt_code, cs))
@@ -440,17 +443,20 @@ def run_cpu_baseline(wl, seconds):
     spec = wl.spec
     Hkv, D, dt = spec.num_kv_heads, spec.head_dim, spec.dtype
     pool = PoolModel(wl.num_blocks, 16, wl.free_order)
-    i8 = spec.cache == "i8"
+    i8 = spec.cache in ("i8", "fp8")
+    fp8 = spec.cache == "fp8"
     if i8:
-        kc, ks = oracle.empty_cache_i8(wl.num_blocks, Hkv, D)
-        vc, vs = oracle.empty_cache_i8(wl.num_blocks, Hkv, D)
+        empty = oracle.empty_cache_fp8 if fp8 else oracle.empty_cache_i8
+        kc, ks = empty(wl.num_blocks, Hkv, D)
+        vc, vs = empty(wl.num_blocks, Hkv, D)
     else:
         kc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
         vc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
 
     def put(k, v, sl):
         if i8:
-            oracle.reshape_and_cache_i8(k, v, kc, vc, ks, vs, sl, Hkv, D, wl.num_blocks, dt)
+            (oracle.reshape_and_cache_fp8 if fp8 else oracle.reshape_and_cache_i8)(
+                k, v, kc, vc, ks, vs, sl, Hkv, D, wl.num_blocks, dt)
         else:
             oracle.reshape_and_cache(k, v, kc, vc, sl, Hkv, D, wl.num_blocks, dt)
     owner = -1
@@ -473,7 +479,7 @@ def run_cpu_baseline(wl, seconds):
     while True:
         if i8:
             _, used = oracle.decode_i8(wl.q, dt, kc, vc, ks, vs, tab, lens, Hkv, spec.fp32_scale(),
-                                       nthreads=0, return_threads=True, window=spec.window)
+                                       nthreads=0, return_threads=True, window=spec.window, fp8=fp8)
         else:
             _, used = oracle.decode(wl.q, kc, vc, tab, lens, Hkv, spec.fp32_scale(), dt,
                                     nthreads=0, return_threads=True, window=spec.window)
@@ -638,7 +644,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
@@ -684,7 +690,7 @@ def main():
     K = args.steps
     tok_s = spec.num_seqs * K / g["elapsed"]
     mean_alg = float(np.mean([a["total"] for a in g["alg"]]))
-    row_bytes = (spec.head_dim + accounting.I8_SCALE_BYTES) if spec.cache == "i8" else \
+    row_bytes = (spec.head_dim + accounting.I8_SCALE_BYTES) if spec.cache in ("i8", "fp8") else \
         spec.head_dim * accounting.ELEM_BYTES[spec.dtype]
     mean_kv_tokens = float(np.mean([a["kv_logical"] for a in g["alg"]])) / (2 * spec.num_kv_heads * row_bytes)
     part_s = float(g["part_ms"].mean()) / 1e3
@@ -716,16 +722,16 @@ def main():
         "config": {
             "workload": spec.name, "num_seqs": spec.num_seqs, "num_q_heads": spec.num_q_heads,
             "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim, "block_size": 16,
-            "kv_dtype": "int8 + f32 row scales" if spec.cache == "i8" else spec.dtype,
+            "kv_dtype": {"i8": "int8 + f32 row scales", "fp8": "fp8 e4m3 + f32 row scales"}.get(spec.cache, spec.dtype),
             "pool_blocks": int(wl.num_blocks),
             "sliding_window": int(spec.window),
             "mean_context": round(mean_kv_tokens / spec.num_seqs, 1),
             "partition_tokens": g["part_tokens"], "replicas": args.replicas,
             "kernel": args.kernel, "seed": spec.seed,
             "step": ("pool append + H2D slots/tables/lens + decode partitions (fused K/V append) + merge"
-                     if args.append == "fused" and spec.cache != "i8" else
-                     "pool append + H2D slots/tables/lens + reshape_and_cache_int8 + decode partitions + merge"
-                     if spec.cache == "i8" else
+                     if args.append == "fused" and spec.cache not in ("i8", "fp8") else
+                     f"pool append + H2D slots/tables/lens + reshape_and_cache_{'fp8' if spec.cache == 'fp8' else 'int8'}"
+                     " + decode partitions + merge" if spec.cache in ("i8", "fp8") else
                      "pool append + H2D slots/tables/lens + reshape_and_cache + decode partitions + merge"),
             "device": g["device"],
         },

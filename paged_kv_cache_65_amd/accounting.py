@@ -44,7 +44,7 @@ def decode_algorithmic_bytes(context_lens, num_q_heads, num_kv_heads, head_dim, 
 
     shared_tokens: tokens of a prefix whose blocks every sequence maps (counted
     once in 'kv_unique' and once per sequence in 'kv_logical').
-    cache: "i8" for an INT8 cache (codes + per-row scales); q and out stay in
+    cache: "i8" / "fp8" for an INT8 / E4M3 cache (codes + per-row scales); q and out stay in
     dtype / out_dtype.
     window: sliding window W (0 = none): only the attended rows and the table
     entries of their blocks count.
@@ -53,7 +53,7 @@ def decode_algorithmic_bytes(context_lens, num_q_heads, num_kv_heads, head_dim, 
     lens, blocks = attended(lens_all, window)
     eb = ELEM_BYTES[dtype]
     S = len(lens)
-    if cache == "i8":
+    if cache in ("i8", "fp8"):
         per_tok = 2 * num_kv_heads * (head_dim + I8_SCALE_BYTES)
     else:
         per_tok = kv_bytes_per_token(1, num_kv_heads, head_dim, eb)
@@ -77,5 +77,5 @@ def decode_flops(context_lens, num_q_heads, head_dim) -> int:
 def append_bytes(num_tokens, num_kv_heads, head_dim, dtype, cache: str = "") -> int:
     """Read new K/V rows + write them into the cache + the int64 slot mapping."""
     row = 2 * num_kv_heads * head_dim * ELEM_BYTES[dtype]
-    written = 2 * num_kv_heads * (head_dim + I8_SCALE_BYTES) if cache == "i8" else row
+    written = 2 * num_kv_heads * (head_dim + I8_SCALE_BYTES) if cache in ("i8", "fp8") else row
     return num_tokens * (row + written + 8)

@@ -67,8 +67,8 @@ class Spec:
 
 
 def named(n: int) -> Spec:
-    """The measured workloads (1-based; 6 is workload 3 over an INT8 cache; 7 is a
-    Mistral-7B-shaped batch under a 4096-token sliding window)."""
+    """The measured workloads (1-based; 6 and 8 are workload 3 over an INT8 and an
+    FP8 cache; 7 is a Mistral-7B-shaped batch under a 4096-token sliding window)."""
     if n == 1:
         return Spec("tiny-fp32-mha-d64", 1, "f32", "f32", 4, 4, 4, 64, 64,
                     lens=[1, 17, 33, 100], scale=1.0 / 8.0)
@@ -87,6 +87,9 @@ def named(n: int) -> Spec:
     if n == 6:  # workload 3 with an INT8 cache (rows quantized on append)
         return Spec("llama70b-gqa8-int8kv-b64-l128to4096", 3, "bf16", "bf16", 64, 64, 8, 128,
                     20000, len_range=(128, 4096), cache="i8")
+    if n == 8:  # workload 3 with an FP8 (E4M3) cache
+        return Spec("llama70b-gqa8-fp8kv-b64-l128to4096", 3, "bf16", "bf16", 64, 64, 8, 128,
+                    20000, len_range=(128, 4096), cache="fp8")
     if n == 7:  # GQA 32/8 heads, D = 128, contexts past the window
         return Spec("mistral7b-gqa4-bf16-b32-l4kto16k-sw4096", 7, "bf16", "bf16", 32, 32, 8, 128,
                     0, len_range=(4096, 16384), window=4096)
