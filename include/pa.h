@@ -50,7 +50,8 @@
  * S.1111.111 NaN, largest finite 448) standing for value(c) * sc, with
  * sc = max_d |x_d| / 448 and c_d the E4M3 value nearest to x_d / sc (float32
  * division), ties to the even code, saturating at +-448 -- the int8 recipe
- * above with FP8's range (the pages name an fp8 KV cache without a recipe).
+ * above with FP8's range ("Inference serving: the KV-cache machine", What
+ * insiders know, names an fp8 KV cache with per-head scales but no recipe).
  * pa_copy_blocks_int8 and pa_swap_blocks_int8 move the codes and scales of
  * either kind of byte cache.
  */

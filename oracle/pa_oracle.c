@@ -443,8 +443,9 @@ float oracle_quantize_row_i8(const void *x, int64_t first, int n, int src_dtype,
  * e = 15 with m = 7 is NaN (no infinities); largest finite 448 (0x7E).
  * Quantization, read from the int8 recipe of "LLM Inference Optimization:
  * KV-Cache, PagedAttention, and GPU Memory Efficiency" (Future
- * Optimizations) with FP8's range ("Modern AI Infrastructure ..." names an
- * fp8 KV cache): scale = max |x| / 448 in float32, code = the E4M3 value
+ * Optimizations) with FP8's range ("Inference serving: the KV-cache machine",
+ * What insiders know, names an fp8 KV cache with per-head scales but gives no
+ * recipe): scale = max |x| / 448 in float32, code = the E4M3 value
  * nearest to x / scale (float32 division), ties to the even code, values
  * beyond 448 saturate to +-448, NaN -> 0x7F; an all-zero row has scale 0.
  * ------------------------------------------------------------------------ */
