@@ -2643,7 +2643,7 @@ ExtendShape extend_shape(const pa_extend_params *p) {
 }
 
 size_t extend_ws_bytes(const pa_extend_params *p, const ExtendShape &e) {
-  if (e.np <= 1) return 0;
+  if (e.np <= 1 || p->num_seqs == 0 || p->num_query_rows == 0) return 0;  // nothing split, or nothing to do
   return (size_t)p->num_query_rows * p->num_q_heads * e.np * (p->head_dim + 2) * sizeof(float);
 }
 

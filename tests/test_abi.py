@@ -176,3 +176,103 @@ def test_int8_append_and_copy_reject_bad_arguments():
     assert L.pa_reshape_and_cache_int8(*args, 0, 8, 128, 10, pa.PA_BF16, None) == pa.PA_OK
     assert L.pa_copy_blocks_int8(None, None, None, None, None, 0, 8, 128, 10, None) == pa.PA_OK
     assert L.pa_copy_blocks_int8(None, None, None, None, None, 2, 8, 128, 10, None) == pa.PA_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- FP8 caches, window
+def test_fp8_cache_follows_the_byte_cache_rules():
+    f8 = dict(kv_dtype=pa.PA_FP8, q_dtype=pa.PA_BF16, out_dtype=pa.PA_F32,
+              k_scales=ctypes.c_void_p(112), v_scales=ctypes.c_void_p(128))
+    assert pa.pa_decode_partition_tokens(_params(**f8)) == 0
+    for over, status in ((dict(q_dtype=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),
+                         (dict(k_scales=None), pa.PA_ERR_INVALID_ARG),
+                         (dict(partition_tokens=64), pa.PA_ERR_UNSUPPORTED)):
+        p = _params(**{**f8, **over})
+        assert pa.lib().pa_decode(ctypes.byref(p), None, 0, None) == status
+    L = pa.lib()
+    args = (None, None, None, None, None, None, None)
+    assert L.pa_reshape_and_cache_fp8(*args, 4, 8, 128, 10, pa.PA_F32, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_reshape_and_cache_fp8(*args, 4, 8, 128, 10, pa.PA_BF16, None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_reshape_and_cache_fp8(*args, 0, 8, 128, 10, pa.PA_BF16, None) == pa.PA_OK
+
+
+def test_negative_sliding_window_is_rejected():
+    p = _params(sliding_window=-1)
+    assert pa.lib().pa_decode(ctypes.byref(p), None, 0, None) == pa.PA_ERR_INVALID_ARG
+    assert pa.pa_decode_workspace_bytes(p) == 0
+
+
+# ---------------------------------------------------------------- extend
+def _ext(**over):
+    p = pa.pa_extend_params(
+        ctypes.c_void_p(16), ctypes.c_void_p(32), ctypes.c_void_p(48), ctypes.c_void_p(64),
+        ctypes.c_void_p(80), ctypes.c_void_p(96), ctypes.c_void_p(112),
+        64, 256, 64, 8, 128, 256, 20000, 4096, 4, 0.088, pa.PA_BF16, pa.PA_BF16, 0, None, None)
+    for k, v in over.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("query_start", None, pa.PA_ERR_INVALID_ARG),
+    ("out", ctypes.c_void_p(17), pa.PA_ERR_INVALID_ARG),
+    ("kv_dtype", pa.PA_F32, pa.PA_ERR_UNSUPPORTED),
+    ("kv_dtype", pa.PA_I8, pa.PA_ERR_UNSUPPORTED),
+    ("num_q_heads", 8 * 17, pa.PA_ERR_UNSUPPORTED),
+    ("num_kv_heads", 7, pa.PA_ERR_INVALID_ARG),
+    ("head_dim", 96, pa.PA_ERR_UNSUPPORTED),
+    ("out_dtype", pa.PA_F16, pa.PA_ERR_UNSUPPORTED),
+    ("partition_tokens", 24, pa.PA_ERR_INVALID_ARG),
+    ("max_query_len", -1, pa.PA_ERR_INVALID_ARG),
+    ("num_query_rows", -1, pa.PA_ERR_INVALID_ARG),
+])
+def test_extend_rejects_bad_parameters_before_launch(field, value, status):
+    p = _ext(**{field: value})
+    assert pa.lib().pa_extend(ctypes.byref(p), None, 0, None) == status
+    assert pa.lib().pa_last_error().decode().startswith("pa_extend")
+    assert pa.pa_extend_workspace_bytes(p) == 0
+    assert pa.lib().pa_extend_partition_tokens(ctypes.byref(p)) == -status
+
+
+def test_extend_partition_and_workspace_arithmetic():
+    # 64 sequences x 8 KV heads x 1 query group (4 tokens of 8 heads fit 32 columns)
+    # already give two workgroups per CU: one partition, no workspace
+    p = _ext()
+    assert pa.pa_extend_partition_tokens(p) == 4096
+    assert pa.pa_extend_workspace_bytes(p) == 0
+    # one sequence: the context is split, partials need [T][Hq][P][D+2] floats
+    p = _ext(num_seqs=1, num_query_rows=4)
+    pt = pa.pa_extend_partition_tokens(p)
+    assert pt % 16 == 0 and 64 <= pt < 4096
+    np_ = -(-4096 // pt)
+    assert pa.pa_extend_workspace_bytes(p) == 4 * 64 * np_ * 130 * 4
+    assert pa.lib().pa_extend(ctypes.byref(p), None, 0, None) == pa.PA_ERR_WORKSPACE
+    p = _ext(partition_tokens=1024)
+    assert pa.pa_extend_partition_tokens(p) == 1024
+    assert pa.pa_extend_workspace_bytes(p) == 256 * 64 * 4 * 130 * 4
+
+
+def test_extend_without_rows_launches_nothing():
+    for over in (dict(num_seqs=0), dict(num_query_rows=0)):
+        p = _ext(**over)
+        assert pa.lib().pa_extend(ctypes.byref(p), None, 0, None) == pa.PA_OK
+
+
+# ---------------------------------------------------------------- swap copies
+def test_swap_blocks_reject_bad_arguments_before_touching_memory():
+    L = pa.lib()
+    nul = (None, None)
+    assert L.pa_swap_blocks(*nul, 10, *nul, 10, None, 0, 8, 128, pa.PA_BF16, None) == pa.PA_OK
+    assert L.pa_swap_blocks(*nul, 10, *nul, 10, None, 1, 8, 96, pa.PA_BF16, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_swap_blocks(*nul, 10, *nul, 10, None, 1, 8, 128, pa.PA_BF16, None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_swap_blocks(*nul, 10, *nul, 10, None, 70000, 8, 128, pa.PA_BF16, None) \
+        == pa.PA_ERR_INVALID_ARG
+    assert L.pa_swap_blocks(*nul, 10, *nul, 10, None, 1, 8, 128, pa.PA_I8, None) == pa.PA_ERR_INVALID_ARG
+    # pointers the runtime does not know (no device here, or pageable memory) are refused
+    buf = (ctypes.c_uint8 * 4096)()
+    addr = (ctypes.addressof(buf) + 15) // 16 * 16
+    pairs = (ctypes.c_int32 * 2)(0, 0)
+    a = ctypes.c_void_p(addr)
+    assert L.pa_swap_blocks(a, a, 1, a, a, 1, pairs, 1, 1, 64, pa.PA_BF16, None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_swap_blocks_int8(*nul, *nul, 10, *nul, *nul, 10, None, 0, 8, 128, None) == pa.PA_OK
+    assert L.pa_swap_blocks_int8(*nul, *nul, 10, *nul, *nul, 10, None, 1, 8, 128, None) \
+        == pa.PA_ERR_INVALID_ARG
