@@ -250,6 +250,8 @@ def run_gpu(args, wl):
         return (slot.desc[0:2 * S].view(torch.int64), slot.desc[lay["lens"]:lay["lens"] + S],
                 slot.desc[lay["tables"]:lay["tables"] + S * MB].view(S, MB))
 
+    # every sequence forks the prefix owner: its blocks lead every table
+    shared_prefix = spec.prefix_len // 16 if (spec.prefix_len and not args.no_shared_prefix) else 0
     for rep in reps:
         slots_v, lens_v, tab_v = views(slots[0])
         rep.out = torch.empty((S, Hq, D), dtype=out_dt, device=dev)
@@ -257,7 +259,8 @@ def run_gpu(args, wl):
                                            Hkv, rep.max_ctx + W + K, spec.fp32_scale(),
                                            args.partition_tokens, args.kernel,
                                            k_scales=rep.k_scales, v_scales=rep.v_scales,
-                                           sliding_window=spec.window)
+                                           sliding_window=spec.window,
+                                           shared_prefix_blocks=shared_prefix)
         ws_need = max(ws_need, pa.pa_decode_workspace_bytes(rep.params))
         rep.params.max_context_len = rep.max_ctx
         if args.append == "fused" and spec.cache not in ("i8", "fp8"):
@@ -656,6 +659,9 @@ def main():
     ap.add_argument("--event-markers", action="store_true",
                     help="record the timing and completion events as separate stream markers "
                          "(hipEventRecord) instead of on the kernel dispatches")
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="with a shared-prefix workload, stream the prefix blocks per sequence instead of "
+                         "computing their attention once (shared_prefix_blocks = 0)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -725,6 +731,7 @@ def main():
             "kv_dtype": {"i8": "int8 + f32 row scales", "fp8": "fp8 e4m3 + f32 row scales"}.get(spec.cache, spec.dtype),
             "pool_blocks": int(wl.num_blocks),
             "sliding_window": int(spec.window),
+            "shared_prefix_blocks": (spec.prefix_len // 16) if (spec.prefix_len and not args.no_shared_prefix) else 0,
             "mean_context": round(mean_kv_tokens / spec.num_seqs, 1),
             "partition_tokens": g["part_tokens"], "replicas": args.replicas,
             "kernel": args.kernel, "seed": spec.seed,

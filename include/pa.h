@@ -209,6 +209,19 @@ typedef struct pa_decode_params {
    * included).  Table entries of blocks wholly before position L-1-W are
    * never read (they may be -1 or stale); negative values are rejected. */
   int32_t sliding_window;
+  /* Shared prefix (0 = none): the first shared_prefix_blocks entries of every
+   * sequence's table are the same physical blocks (sequence 0's row is read
+   * for them; the other rows' entries there are not), as when every sequence
+   * forks one prefix owner ("Modern AI Infrastructure and Agentic System
+   * Design", section 9.1; "Inference serving: the KV-cache machine", Lab B).
+   * The attention over the prefix is then computed once for all sequences
+   * (a third kernel before the attention launch of pa_decode /
+   * pa_decode_partitions) and folded into each row; the result is the same
+   * attention.  Needs an fp16/bf16 cache, no sliding window and the balanced
+   * split; every context must reach past the prefix (L > 16 *
+   * shared_prefix_blocks, else that sequence's rows are NaN).  The workspace
+   * grows by num_seqs * num_q_heads * (head_dim + 2) floats. */
+  int32_t shared_prefix_blocks;
 } pa_decode_params;
 
 /* Partition size (tokens) pa_decode will use for these parameters, 0 for the

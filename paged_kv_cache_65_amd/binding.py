@@ -45,7 +45,8 @@ class pa_decode_params(ctypes.Structure):
                 ("out_dtype", ctypes.c_int), ("partition_tokens", _I32), ("kernel", ctypes.c_int),
                 ("k_new", _P), ("v_new", _P), ("slot_mapping", _P),
                 ("q_dtype", ctypes.c_int), ("k_scales", _P), ("v_scales", _P),
-                ("start_event", _P), ("stop_event", _P), ("sliding_window", _I32)]
+                ("start_event", _P), ("stop_event", _P), ("sliding_window", _I32),
+                ("shared_prefix_blocks", _I32)]
 
 
 class pa_extend_params(ctypes.Structure):
@@ -171,7 +172,7 @@ def _stream(stream):
 def make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
                        max_context_len, scale, partition_tokens=0, kernel="auto", k_new=None,
                        v_new=None, slot_mapping=None, k_scales=None, v_scales=None,
-                       start_event=None, stop_event=None, sliding_window=0):
+                       start_event=None, stop_event=None, sliding_window=0, shared_prefix_blocks=0):
     """k_scales / v_scales: the float32 scale arrays of an int8 cache (else None).
     start_event / stop_event: raw hipEvent_t handles (ints) or None.
     sliding_window: W > 0 attends positions L-1-W .. L-1 only; 0 = the whole context."""
@@ -183,7 +184,7 @@ def make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens, num
         int(max_context_len), float(scale), _dtype_code(k_cache), _dtype_code(out),
         int(partition_tokens), KERNELS[kernel], _dev(k_new), _dev(v_new), _dev(slot_mapping),
         _dtype_code(q), _dev(k_scales), _dev(v_scales), _event(start_event), _event(stop_event),
-        int(sliding_window))
+        int(sliding_window), int(shared_prefix_blocks))
 
 
 def _event(ev):
@@ -206,7 +207,7 @@ def pa_decode_partition_tokens(params: pa_decode_params) -> int:
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
               max_context_len, scale, partition_tokens=0, kernel="auto", workspace=None,
               stream=None, k_new=None, v_new=None, slot_mapping=None, k_scales=None,
-              v_scales=None, sliding_window=0):
+              v_scales=None, sliding_window=0, shared_prefix_blocks=0):
     """out <- paged decode attention (optionally appending k_new/v_new first).
     workspace: a uint8 device tensor of at least pa_decode_workspace_bytes()
     bytes (no initialization needed), or None to allocate one.  For an int8
@@ -215,7 +216,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads
     params = make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens,
                                 num_kv_heads, max_context_len, scale, partition_tokens, kernel,
                                 k_new, v_new, slot_mapping, k_scales, v_scales,
-                                sliding_window=sliding_window)
+                                sliding_window=sliding_window, shared_prefix_blocks=shared_prefix_blocks)
     need = pa_decode_workspace_bytes(params)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

@@ -165,6 +165,10 @@ struct DecodeArgs {
   int32_t num_seqs, num_q_heads, num_kv_heads, group, max_blocks, num_blocks, max_ctx, max_parts,
       part_tokens, out_dtype, num_workers, window;
   float scale_log2;
+  int32_t prefix_blocks;   // shared prefix: the first table entries, the same blocks for every sequence
+  int32_t park_slots;      // balanced split: LDS parking slots per wave (1 .. kParkSlotsMax)
+  float *ws_pfx_ml;        // shared prefix: [S][Hq][2] (m, l) of every row over the prefix
+  float *ws_pfx_acc;       //                [S][Hq][D]
 };
 
 __device__ inline bool ctx_valid(int L, const DecodeArgs &a) {
@@ -479,11 +483,28 @@ struct MfmaWave {
     const f32x4_t nan4 = {NAN, NAN, NAN, NAN};
     if (whole) {
       const int64_t o = (row0 + r) * D + 4 * tq;
+      float fa = 1.f, fp = 0.f, den = lt;
+      const float *px = nullptr;
+      if (a.prefix_blocks > 0) {  // fold the row's attention over the shared prefix
+        const float pm = a.ws_pfx_ml[(row0 + r) * 2], pl = a.ws_pfx_ml[(row0 + r) * 2 + 1];
+        const float Mx = fmaxf(m, pm);
+        fa = exp2f(m - Mx);
+        fp = exp2f(pm - Mx);
+        den = lt * fa + pl * fp;
+        px = a.ws_pfx_acc + o;
+        if (pm != pm) bad = true;
+      }
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         f32x4_t v;
+        if (px) {
+          const f32x4_t pv = *reinterpret_cast<const f32x4_t *>(px + 16 * n);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[n][e] / lt;
+          for (int e = 0; e < 4; ++e) v[e] = (acc[n][e] * fa + pv[e] * fp) / den;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[n][e] / lt;
+        }
         store_out4(a.out, o + 16 * n, bad ? nan4 : v, a.out_dtype);
       }
     } else {
@@ -522,9 +543,21 @@ __device__ void flush_parked(const DecodeArgs &a, const float *st, int64_t row0,
     f32x4_t v = *reinterpret_cast<const f32x4_t *>(st + e);
     if (whole) {
       const float lt = st[G * D + G + r];
+      bool b = bad;
+      if (a.prefix_blocks > 0) {  // fold the row's attention over the shared prefix
+        const float m = st[G * D + r];
+        const float pm = a.ws_pfx_ml[(row0 + r) * 2], pl = a.ws_pfx_ml[(row0 + r) * 2 + 1];
+        const float Mx = fmaxf(m, pm), fa = exp2f(m - Mx), fp = exp2f(pm - Mx);
+        const float den = lt * fa + pl * fp;
+        const f32x4_t pv = *reinterpret_cast<const f32x4_t *>(a.ws_pfx_acc + (row0 + r) * D + e % D);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = v[k] / lt;
-      store_out4(a.out, (row0 + r) * D + e % D, bad ? nan4 : v, a.out_dtype);
+        for (int k = 0; k < 4; ++k) v[k] = (v[k] * fa + pv[k] * fp) / den;
+        b |= pm != pm;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = v[k] / lt;
+      }
+      store_out4(a.out, (row0 + r) * D + e % D, b ? nan4 : v, a.out_dtype);
     } else {
       *reinterpret_cast<f32x4_t *>(a.ws_acc + prow0 * D + e) = bad ? nan4 : v;
     }
@@ -1071,15 +1104,28 @@ struct __align__(16) SmemBalanced {
   int32_t len[kSeqMax];                          // context length (-1 when invalid)
 };
 
-// Attended blocks of a context of L tokens (L = -1: invalid, none): from the
-// block holding the window's first position to the one holding position L-1.
-__device__ inline int attended_blocks(int L, int W) {
-  return L > 0 ? (L + kBS - 1) / kBS - window_first_token(L, W) / kBS : 0;
+// First table entry the balanced split streams for a context of L tokens:
+// the block holding the window's first position, or the first block after a
+// shared prefix (whose attention comes from the prefix kernel).
+__device__ inline int first_block(int L, const DecodeArgs &a) {
+  return a.prefix_blocks > 0 ? a.prefix_blocks : window_first_token(L, a.window) / kBS;
+}
+
+// Blocks the balanced split streams for a context of L tokens (L = -1:
+// invalid, none): from first_block to the one holding position L-1.
+__device__ inline int attended_blocks(int L, const DecodeArgs &a) {
+  return L > 0 ? (L + kBS - 1) / kBS - first_block(L, a) : 0;
 }
 
 // Floats of one wave's parking area: G rows of D, then m and l per row
 // (rounded to 16 bytes).
 __host__ __device__ constexpr int park_floats(int G, int D) { return (G * (D + 2) + 3) / 4 * 4; }
+// One parking slot: the state, then its output row, partial row (int64) and flags.
+__host__ __device__ constexpr int park_slot_floats(int G, int D) { return park_floats(G, D) + 8; }
+#ifndef PA_PARK_SLOTS_MAX
+#define PA_PARK_SLOTS_MAX 8
+#endif
+constexpr int kParkSlotsMax = PA_PARK_SLOTS_MAX;
 
 // Per-unit flags, one unit per lane.
 constexpr uint32_t kUValid = 0x1Fu;         // tokens of the block inside the context (1..16)
@@ -1126,7 +1172,7 @@ __device__ inline int pair_of_unit(const SmemBalanced &sm, int u, int Hkv, int S
 template <class W, int D>
 __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(DecodeArgs a) {
   __shared__ SmemBalanced sm;
-  extern __shared__ __align__(16) float park_lds[];  // kBWaves x park_floats(G, D)
+  extern __shared__ __align__(16) float park_lds[];  // kBWaves x park_slots x park_slot_floats(G, D)
   const int tid = threadIdx.x, lane = tid % 64;
   const int wu = __builtin_amdgcn_readfirstlane(tid / 64);
   const int S = a.num_seqs, Hkv = a.num_kv_heads, G = a.group;
@@ -1135,14 +1181,16 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
   // lane sums a run of ceil(S/64) sequences, then a scan across lanes).
   for (int s = tid; s < S; s += kBThreads) {
     const int L = a.context_lens[s];
-    sm.len[s] = ctx_valid(L, a) ? L : -1;  // -1: invalid (no blocks, NaN rows)
+    // -1: invalid (no blocks, NaN rows); with a shared prefix a context must
+    // reach past it
+    sm.len[s] = ctx_valid(L, a) && (a.prefix_blocks == 0 || L > a.prefix_blocks * kBS) ? L : -1;
   }
   __syncthreads();
   if (wu == 0) {
     const int per = (S + 63) / 64;
     const int s0 = min(S, lane * per), s1 = min(S, s0 + per);
     int sum = 0;
-    for (int s = s0; s < s1; ++s) sum += attended_blocks(sm.len[s], a.window);
+    for (int s = s0; s < s1; ++s) sum += attended_blocks(sm.len[s], a);
     int inc = sum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -1152,7 +1200,7 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
     int run = inc - sum;
     for (int s = s0; s < s1; ++s) {
       sm.pre[s] = run;
-      run += attended_blocks(sm.len[s], a.window);
+      run += attended_blocks(sm.len[s], a);
     }
     if (lane == 63) sm.pre[S] = inc;
   }
@@ -1183,7 +1231,7 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
     const int s = seq_of_block(sm, u / Hkv, S);
     const int nb = sm.pre[s + 1] - sm.pre[s];
     const int off = u - Hkv * sm.pre[s];
-    const int jb = window_first_token(sm.len[s], a.window) / kBS;
+    const int jb = first_block(sm.len[s], a);
     id_first = a.block_tables[(int64_t)s * a.max_blocks + jb + off % nb];
   }
 
@@ -1204,13 +1252,14 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
   typename W::Frag fr[NB];
   bool bad = false, whole = false;
   constexpr int EB = 2;
-  // A segment that ends before the wave's share does is parked in LDS and
-  // written when the share is done: stores count in the same counter as the
-  // ring's loads, so a store in mid-stream would make the next block wait
-  // for its acknowledgement.
-  float *park = park_lds + wu * park_floats(G, D);
-  bool parked = false, p_whole = false, p_bad = false;
-  int64_t p_row0 = 0, p_prow0 = 0;
+  // A segment that ends before the wave's share does is parked in LDS (up
+  // to park_slots of them, sized by the host to the LDS left) and written
+  // when the share is done: stores count in the same counter as the ring's
+  // loads, so a store in mid-stream would make the next block wait for its
+  // acknowledgement.
+  const int slot_f = park_slot_floats(G, D);
+  float *park = park_lds + wu * a.park_slots * slot_f;
+  int nparked = 0;
   for (int c0 = u0; c0 < u1;) {
     // ---- this chunk's units, one per lane
     int nc = min(64, u1 - c0);
@@ -1220,7 +1269,7 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
     const int off = u - Hkv * sm.pre[s];
     const int g = off / nb, j = off - g * nb;
     const int L = sm.len[s];
-    const int jb = window_first_token(L, a.window) / kBS;  // attended block j is table entry jb + j
+    const int jb = first_block(L, a);  // attended block j is table entry jb + j
     const bool pend = j == nb - 1;
     // Fused append: the unit holding position L-1 of a pair takes the new
     // token.  At most kAppendMax such units per chunk (the chunk ends early).
@@ -1339,15 +1388,18 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
                        sm.vnew[wu][k]);
           if (mt & kULast) {  // (a segment may go on into the next chunk)
             const bool wh = whole && (mt & kUPairEnd);
-            if (c0 + i == u1 - 1 || parked) {  // (one parking place: a third segment stores)
+            if (c0 + i == u1 - 1 || nparked == a.park_slots) {  // (all parking places taken: it stores)
               wave.store_segment(a, (int64_t)pq * G, (int64_t)(w + pq) * G, wh, bad, lane, G);
             } else {
-              wave.park_segment(park, lane, G);
-              parked = true;
-              p_whole = wh;
-              p_bad = bad;
-              p_row0 = (int64_t)pq * G;
-              p_prow0 = (int64_t)(w + pq) * G;
+              float *st = park + nparked * slot_f;
+              wave.park_segment(st, lane, G);
+              if (lane == 0) {
+                int64_t *meta_p = reinterpret_cast<int64_t *>(st + park_floats(G, D));
+                meta_p[0] = (int64_t)pq * G;
+                meta_p[1] = (int64_t)(w + pq) * G;
+                meta_p[2] = (wh ? 1 : 0) | (bad ? 2 : 0);
+              }
+              ++nparked;
             }
           }
         }
@@ -1364,7 +1416,12 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
     }
     c0 += nc;
   }
-  if (parked) flush_parked<D>(a, park, p_row0, p_prow0, p_whole, p_bad, lane, G);
+  for (int k = 0; k < nparked; ++k) {
+    const float *st = park + k * slot_f;
+    const int64_t *meta_p = reinterpret_cast<const int64_t *>(st + park_floats(G, D));
+    const int64_t fl = meta_p[2];
+    flush_parked<D>(a, st, meta_p[0], meta_p[1], (fl & 1) != 0, (fl & 2) != 0, lane, G);
+  }
 }
 
 // ---------------------------------------------------------------- merge kernel
@@ -1378,9 +1435,25 @@ constexpr int kMergeWaves = 4;
 // into one output row.
 template <int D>
 __device__ void merge_row(void *out, int out_dtype, int64_t row, const float *ml, int64_t ml_stride,
-                          const float *acc, int64_t acc_stride, int np, int lane) {
+                          const float *acc, int64_t acc_stride, int np, int lane, const float *xml = nullptr,
+                          const float *xacc = nullptr) {
+  // xml / xacc: one more partial (m, l) and acc row at its own place (a shared
+  // prefix), or null.
   constexpr int PER = D / 64;  // output dims per lane
   constexpr int kFew = 8;
+  float xm = -INFINITY, xl = 0.f, xa[PER];
+  if (xml) {
+    xm = xml[0];
+    xl = xml[1];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) xa[e] = xacc[lane * PER + e];
+  }
+  float M = xm;
+  bool nan = xm != xm;
+  float den = 0.f;
+  float num[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) num[e] = 0.f;
   if (np <= kFew) {
     // Every load first (one memory round trip), then the same arithmetic in
     // the same order as the general loop below.
@@ -1394,8 +1467,6 @@ __device__ void merge_row(void *out, int out_dtype, int64_t row, const float *ml
         for (int e = 0; e < PER; ++e) av[q][e] = acc[q * acc_stride + lane * PER + e];
       }
     }
-    float M = -INFINITY;
-    bool nan = false;
 #pragma unroll
     for (int q = 0; q < kFew; ++q) {
       if (q < np) {
@@ -1403,10 +1474,6 @@ __device__ void merge_row(void *out, int out_dtype, int64_t row, const float *ml
         M = fmaxf(M, mv[q]);
       }
     }
-    float den = 0.f;
-    float num[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] = 0.f;
 #pragma unroll
     for (int q = 0; q < kFew; ++q) {
       if (q < np) {
@@ -1416,28 +1483,25 @@ __device__ void merge_row(void *out, int out_dtype, int64_t row, const float *ml
         for (int e = 0; e < PER; ++e) num[e] += f * av[q][e];
       }
     }
-#pragma unroll
-    for (int e = 0; e < PER; ++e)
-      store_out(out, row * D + lane * PER + e, nan ? NAN : num[e] / den, out_dtype);
-    return;
-  }
-  float M = -INFINITY;
-  bool nan = false;
-  for (int q = 0; q < np; ++q) {
-    const float mq = ml[q * ml_stride];
-    nan |= mq != mq;
-    M = fmaxf(M, mq);
-  }
-  float den = 0.f;
-  float num[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) num[e] = 0.f;
+  } else {
+    for (int q = 0; q < np; ++q) {
+      const float mq = ml[q * ml_stride];
+      nan |= mq != mq;
+      M = fmaxf(M, mq);
+    }
 #pragma unroll 4
-  for (int q = 0; q < np; ++q) {
-    const float f = exp2f(ml[q * ml_stride] - M);
-    den += f * ml[q * ml_stride + 1];
+    for (int q = 0; q < np; ++q) {
+      const float f = exp2f(ml[q * ml_stride] - M);
+      den += f * ml[q * ml_stride + 1];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] += f * acc[q * acc_stride + lane * PER + e];
+      for (int e = 0; e < PER; ++e) num[e] += f * acc[q * acc_stride + lane * PER + e];
+    }
+  }
+  if (xml) {
+    const float f = exp2f(xm - M);
+    den += f * xl;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) num[e] += f * xa[e];
   }
 #pragma unroll
   for (int e = 0; e < PER; ++e)
@@ -1478,7 +1542,9 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_balanced_kernel(Dec
   const int w0 = us / C, w1 = (us + nb - 1) / C;
   if (w0 == w1) return;
   const int64_t prow = (int64_t)(w0 + s * Hkv + g) * G + r;
-  merge_row<D>(a.out, a.out_dtype, row, a.ws_ml + prow * 2, (int64_t)G * 2, a.ws_acc + prow * D, (int64_t)G * D, w1 - w0 + 1, lane);
+  const bool pfx = a.prefix_blocks > 0;
+  merge_row<D>(a.out, a.out_dtype, row, a.ws_ml + prow * 2, (int64_t)G * 2, a.ws_acc + prow * D, (int64_t)G * D,
+               w1 - w0 + 1, lane, pfx ? a.ws_pfx_ml + row * 2 : nullptr, pfx ? a.ws_pfx_acc + row * D : nullptr);
 }
 
 // ---------------------------------------------------------------- extend (multi-query)
@@ -1770,6 +1836,159 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_extend_merge_kernel(Exten
                a.ws_acc + row * a.max_parts * D, D, np, lane);
 }
 
+// ---------------------------------------------------------------- shared prefix
+// Every sequence's table starts with the same prefix_blocks blocks (a shared
+// prefix: "Modern AI Infrastructure and Agentic System Design", section 9.1,
+// many requests mapping the same prefix blocks; "Inference serving: the
+// KV-cache machine", Lab B, the system prompt paid once).  The attention of
+// every query row over the prefix is computed once per KV head instead of
+// once per sequence: the score tile's 16 columns are (sequence, head) pairs,
+// sequence-major (16/G sequences of the G heads), a wave holds kExtNctMax
+// tiles, the four waves of a workgroup take every fourth prefix block and
+// meet in LDS, and the (m, l, acc) of each row over the prefix goes to the
+// workspace; the balanced split then streams only the blocks after the
+// prefix and folds it in.
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void pa_prefix_kernel(DecodeArgs a) {
+  using M = MfmaWave<DT, D>;
+  using v8 = typename M::v8;
+  constexpr int NC = D / 32, NT = D / 16, NCT = kExtNctMax;
+  constexpr int NB = 2;
+  __shared__ SmemExtend<D, NCT> sm;
+  const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_q_heads;
+  const int g = blockIdx.x % Hkv;
+  const int sg = blockIdx.x / Hkv;
+  const int tid = threadIdx.x, lane = tid % 64, r = lane % 16, tq = lane / 16;
+  const int wu = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int tpt = 16 / G, spg = NCT * tpt;  // sequences per tile, per workgroup
+  const int s0 = sg * spg;
+  const int ns = min(spg, a.num_seqs - s0);
+  if (ns <= 0) return;
+  const int hd = g * G + r % G;
+  v8 qB[NCT][NC];
+  f32x4_t acc[NCT][NT];
+  float mm[NCT], ll[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int sk = (r < tpt * G) ? ct * tpt + r / G : 1 << 30;
+    const bool ok = sk < ns;
+    const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
+                                                            ((int64_t)(s0 + (ok ? sk : 0)) * Hq + hd) * D * 2);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4_t x = qrow[4 * c + tq];
+      if (!ok) x = u32x4_t{0, 0, 0, 0};
+      qB[ct][c] = __builtin_bit_cast(v8, x);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[ct][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    mm[ct] = -INFINITY;
+    ll[ct] = 0.f;
+  }
+  const int nblk = a.prefix_blocks;
+  const int64_t head_off = (int64_t)g * M::TILE;
+  const int64_t blk_stride = (int64_t)Hkv * M::TILE;
+  typename M::Frag fr[NB];
+  int bad = 0;
+  const int nmine = nblk > wu ? (nblk - wu + kWaves - 1) / kWaves : 0;
+  for (int c0 = 0; c0 < nmine; c0 += 64) {
+    const int nc = min(64, nmine - c0);
+    int ids = lane < nc ? a.block_tables[wu + (c0 + lane) * kWaves] : 0;  // sequence 0's row
+    const bool id_ok = (uint32_t)ids < (uint32_t)a.num_blocks;
+    if (__builtin_amdgcn_ballot_w64(!id_ok)) bad = 1;
+    ids = id_ok ? ids : 0;
+    auto refill = [&](typename M::Frag &f, int i) {
+      const bool real = i < nc;
+      const int64_t off = real ? (int64_t)__builtin_amdgcn_readlane(ids, min(i, nc - 1)) * blk_stride + head_off : 0;
+      M::load(f, a.k_cache + off, a.v_cache + off, real ? lane : 0);
+    };
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b) {
+      refill(fr[b], b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int j0 = 0; j0 < nc; j0 += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int i = j0 + b;
+        refill(fr[(b + NB - 1) % NB], i + NB - 1);
+        if (i < nc) {
+          typename M::Frag &f = fr[b];
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) sc = M::mma_qk(__builtin_bit_cast(v8, f.k[c]), qB[ct][c], sc);
+            float sv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sv[v] = sc[v] * a.scale_log2;
+            float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            mx = max_xor32(max_xor16(mx));
+            const bool bump = mx > mm[ct] + kLazyLog2;
+            if (__builtin_amdgcn_ballot_w64(bump)) {
+              const float m_new = bump ? mx : mm[ct];
+              const float alpha = mm[ct] == -INFINITY ? 0.f : exp2_neg(mm[ct] - m_new);
+              ll[ct] *= alpha;
+#pragma unroll
+              for (int t = 0; t < NT; ++t) acc[ct][t] *= alpha;
+              mm[ct] = m_new;
+            }
+            float pw[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) pw[v] = __builtin_amdgcn_exp2f(sv[v] - mm[ct]);
+            ll[ct] += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+            u32x2_t ph, pl2;
+            M::split(pw, ph, pl2);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              const u32x2_t a0 = u32x2_t{f.v[c][0], f.v[c][1]};
+              const u32x2_t a1 = u32x2_t{f.v[c][2], f.v[c][3]};
+              acc[ct][2 * c] = M::mma_pv(a0, ph, acc[ct][2 * c]);
+              acc[ct][2 * c + 1] = M::mma_pv(a1, ph, acc[ct][2 * c + 1]);
+              acc[ct][2 * c] = M::mma_pv(a0, pl2, acc[ct][2 * c]);
+              acc[ct][2 * c + 1] = M::mma_pv(a1, pl2, acc[ct][2 * c + 1]);
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const float lt = sum_xor32(sum_xor16(ll[ct]));
+    const int col = ct * 16 + r;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t *>(&sm.acc[wu][col][16 * t + 4 * tq]) = acc[ct][t];
+    if (tq == 0) {
+      sm.m[wu][col] = mm[ct];
+      sm.l[wu][col] = lt;
+    }
+  }
+  const bool any_bad = __syncthreads_or(bad);
+  for (int i = tid; i < ns * G * D; i += kThreads) {
+    const int sk = i / (G * D), h = (i / D) % G, d = i % D;
+    const int col = (sk / tpt) * 16 + (sk % tpt) * G + h;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, sm.m[w][col]);
+    float num = 0.f, den = 0.f;
+    if (Mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = exp2f(sm.m[w][col] - Mx);
+        num += f * sm.acc[w][col][d];
+        den += f * sm.l[w][col];
+      }
+    }
+    const int64_t row = (int64_t)(s0 + sk) * Hq + g * G + h;
+    a.ws_pfx_acc[row * D + d] = any_bad ? NAN : num;
+    if (d == 0) {
+      a.ws_pfx_ml[row * 2] = any_bad ? NAN : Mx;
+      a.ws_pfx_ml[row * 2 + 1] = den;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- KV append
 // One thread per (token, kv head, X-dim chunk): reads X elements (16 bytes)
 // of the new K and V rows and writes them at the slot's place in the tiles.
@@ -2009,6 +2228,14 @@ pa_status validate(const pa_decode_params *p) {
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: scale must be finite");
   if (p->sliding_window < 0)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: sliding_window must be >= 0 (0 = none)");
+  if (p->shared_prefix_blocks < 0 || p->shared_prefix_blocks > p->max_blocks_per_seq)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: shared_prefix_blocks must be in [0, max_blocks_per_seq]");
+  if (p->shared_prefix_blocks > 0 &&
+      ((p->kv_dtype != PA_F16 && p->kv_dtype != PA_BF16) || p->sliding_window != 0 ||
+       p->partition_tokens != 0 || p->kernel == PA_KERNEL_VALU))
+    return pa::fail(PA_ERR_UNSUPPORTED,
+                    "pa_decode: a shared prefix needs an fp16/bf16 cache, no sliding window and the "
+                    "matrix-core kernel with automatic partitioning");
   return PA_OK;
 }
 
@@ -2018,7 +2245,7 @@ bool use_balanced(const pa_decode_params *p);
 pa_status validate_all(const pa_decode_params *p) {
   pa_status st = validate(p);
   if (st != PA_OK) return st;
-  if (byte_cache(p->kv_dtype) && !use_balanced(p))
+  if ((byte_cache(p->kv_dtype) || p->shared_prefix_blocks > 0) && !use_balanced(p))
     return pa::fail(PA_ERR_UNSUPPORTED,
                     "pa_decode: an INT8/FP8 cache needs the balanced split (<= 1024 sequences, <= 32768 "
                     "(sequence, KV head) pairs)");
@@ -2063,7 +2290,42 @@ bool use_mfma(const pa_decode_params *p) {
 // Workgroups of the balanced grid: PA_BALANCED_WG_PER_CU per CU (checked
 // against the kernel's occupancy with its parking LDS for G query heads per
 // KV head where a device answers).
-size_t park_bytes(int G, int D) { return (size_t)kBWaves * park_floats(G, D) * sizeof(float); }
+// Parking slots per wave: as many as the LDS left beside the kernel's own
+// shared memory allows (per workgroup, with wg_per_cu workgroups on a CU),
+// at least 1, at most kParkSlotsMax.
+int park_slots(int G, int D, int wg_per_cu) {
+  static int lds_block[64] = {}, lds_cu[64] = {};
+  int dev = 0, per_block = 64 * 1024, per_cu = 64 * 1024;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    if (!lds_block[dev]) {
+      int b = 0, c = 0;
+      if (hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+          hipDeviceGetAttribute(&c, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+          b <= 0 || c <= 0) {
+        (void)hipGetLastError();
+        b = c = 64 * 1024;
+      }
+      lds_cu[dev] = c;
+      lds_block[dev] = b;
+    }
+    per_block = lds_block[dev];
+    per_cu = lds_cu[dev];
+  } else {
+    (void)hipGetLastError();
+  }
+  const int64_t budget = std::min<int64_t>(per_block, per_cu / std::max(wg_per_cu, 1)) -
+                         (int64_t)sizeof(SmemBalanced) - 2048;
+  const int64_t slot = (int64_t)kBWaves * park_slot_floats(G, D) * sizeof(float);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(kParkSlotsMax, budget / slot));
+}
+
+size_t park_bytes(int G, int D, int slots) {
+  return (size_t)kBWaves * slots * park_slot_floats(G, D) * sizeof(float);
+}
+
+int balanced_park_slots(pa_dtype kv, int G, int D) {
+  return park_slots(G, D, byte_cache(kv) ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU);
+}
 
 // The balanced kernel for a cache type, q type and head size.
 template <class W, int D>
@@ -2094,7 +2356,8 @@ int balanced_workgroups(pa_dtype kv, pa_dtype qt, int D, int G) {
     const int want = bytes ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, balanced_kernel(kv, qt, D), kBThreads,
-                                                     park_bytes(G, D)) != hipSuccess ||
+                                                     park_bytes(G, D, balanced_park_slots(kv, G, D))) !=
+            hipSuccess ||
         per_cu <= 0)
       per_cu = want;
     cached[dev][k][G] = std::min(per_cu, want) * cu_count();
@@ -2120,7 +2383,9 @@ size_t round16(size_t x) { return (x + 15) / 16 * 16; }
 
 // Balanced-split workspace: [S+1] int32 block offsets, then per slot
 // (NW + S*Hkv - 1 of them) G rows of (m, l) and G rows of D accumulators.
-size_t balanced_bytes(const pa_decode_params *p, size_t *ml_off, size_t *acc_off) {
+// Balanced workspace: block offsets, partial (m, l) and acc slots, then with
+// a shared prefix the rows' (m, l) and acc over it.
+size_t balanced_bytes(const pa_decode_params *p, size_t *ml_off, size_t *acc_off, size_t *pfx_off = nullptr) {
   const int64_t nw = (int64_t)kBWaves * balanced_workgroups(p);
   const int64_t slots = nw + (int64_t)p->num_seqs * p->num_kv_heads - 1;
   const int64_t G = p->num_q_heads / p->num_kv_heads;
@@ -2128,7 +2393,11 @@ size_t balanced_bytes(const pa_decode_params *p, size_t *ml_off, size_t *acc_off
   const size_t ml = round16((size_t)slots * G * 2 * 4);
   if (ml_off) *ml_off = pre;
   if (acc_off) *acc_off = pre + ml;
-  return pre + ml + (size_t)slots * G * p->head_dim * 4;
+  const size_t base = pre + ml + round16((size_t)slots * G * p->head_dim * 4);
+  if (pfx_off) *pfx_off = base;
+  if (p->shared_prefix_blocks <= 0) return base;
+  const size_t rows = (size_t)p->num_seqs * p->num_q_heads;
+  return base + round16(rows * 2 * 4) + rows * p->head_dim * 4;
 }
 
 size_t partial_bytes(const pa_decode_params *p, int32_t np) {
@@ -2239,13 +2508,25 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
   a.ws_acc = need ? static_cast<float *>(workspace) + rows * 2 : nullptr;
   a.ws_pre = nullptr;
   a.num_workers = 0;
+  a.prefix_blocks = p->shared_prefix_blocks;
+  a.park_slots = 1;
+  a.ws_pfx_ml = nullptr;
+  a.ws_pfx_acc = nullptr;
   if (bal) {
     size_t ml_off = 0, acc_off = 0;
     balanced_bytes(p, &ml_off, &acc_off);
+    size_t pfx_off = 0;
+    balanced_bytes(p, nullptr, nullptr, &pfx_off);
     a.ws_pre = static_cast<int32_t *>(workspace);
     a.ws_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + ml_off);
     a.ws_acc = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + acc_off);
+    if (p->shared_prefix_blocks > 0) {
+      const size_t rows = (size_t)p->num_seqs * p->num_q_heads;
+      a.ws_pfx_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pfx_off);
+      a.ws_pfx_acc = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pfx_off + round16(rows * 2 * 4));
+    }
     a.num_workers = kBWaves * balanced_workgroups(p);
+    a.park_slots = balanced_park_slots(p->kv_dtype, p->num_q_heads / p->num_kv_heads, p->head_dim);
   }
 
   a.num_seqs = p->num_seqs;
@@ -2267,10 +2548,27 @@ pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipS
                             const LaunchEvents &ev) {
   void *args[] = {const_cast<DecodeArgs *>(&a)};
   if (use_balanced(p)) {
+    LaunchEvents bev = ev;
+    if (a.prefix_blocks > 0) {  // every row's attention over the shared prefix first
+      const int spg = kExtNctMax * (16 / a.group);
+      const dim3 pgrid((unsigned)(p->num_kv_heads * ((p->num_seqs + spg - 1) / spg)));
+      const void *pfn = p->kv_dtype == PA_BF16
+                            ? (p->head_dim == 128 ? reinterpret_cast<const void *>(&pa_prefix_kernel<PA_BF16, 128>)
+                                                  : reinterpret_cast<const void *>(&pa_prefix_kernel<PA_BF16, 64>))
+                            : (p->head_dim == 128 ? reinterpret_cast<const void *>(&pa_prefix_kernel<PA_F16, 128>)
+                                                  : reinterpret_cast<const void *>(&pa_prefix_kernel<PA_F16, 64>));
+      LaunchEvents pev;
+      pev.start = ev.start;
+      bev.start = nullptr;
+      hipError_t e = launch_kernel(pfn, pgrid, dim3(kThreads), args, 0, hs, pev);
+      if (e != hipSuccess) return hip_check(e, "pa_decode prefix launch");
+      pa_status st = hip_check(hipGetLastError(), "pa_decode prefix launch");
+      if (st != PA_OK) return st;
+    }
     const dim3 grid((unsigned)(a.num_workers / kBWaves));
-    const size_t lds = park_bytes(a.group, p->head_dim);
+    const size_t lds = park_bytes(a.group, p->head_dim, a.park_slots);
     hipError_t e = launch_kernel(balanced_kernel(p->kv_dtype, p->q_dtype, p->head_dim), grid,
-                                 dim3(kBThreads), args, lds, hs, ev);
+                                 dim3(kBThreads), args, lds, hs, bev);
     if (e != hipSuccess) return hip_check(e, "pa_decode balanced launch");
     return hip_check(hipGetLastError(), "pa_decode balanced launch");
   }
