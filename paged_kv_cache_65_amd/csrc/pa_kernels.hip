@@ -280,6 +280,12 @@ __device__ inline void write_token_row(uint8_t *k_cache, uint8_t *v_cache, int64
 #ifndef PA_I8_WG_PER_CU
 #define PA_I8_WG_PER_CU 2
 #endif
+#ifndef PA_FP8_RING
+#define PA_FP8_RING PA_I8_RING
+#endif
+#ifndef PA_FP8_WG_PER_CU
+#define PA_FP8_WG_PER_CU PA_I8_WG_PER_CU
+#endif
 
 // ============================================================================
 // MFMA wave: fp16 / bf16 caches.
@@ -599,8 +605,8 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D> {
   static constexpr bool kAppend = false;   // append with pa_reshape_and_cache_int8 first
   // The code conversions add ~250 VALU instructions per block: more waves per
   // SIMD hide their latency, a shallower ring keeps them in registers.
-  static constexpr int kBalRing = PA_I8_RING;
-  static constexpr int kBalWgPerCu = PA_I8_WG_PER_CU;
+  static constexpr int kBalRing = FMT == PA_FP8 ? PA_FP8_RING : PA_I8_RING;
+  static constexpr int kBalWgPerCu = FMT == PA_FP8 ? PA_FP8_WG_PER_CU : PA_I8_WG_PER_CU;
 
   struct Frag {
     u32x4_t k[NV];
@@ -1848,13 +1854,30 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_extend_merge_kernel(Exten
 // meet in LDS, and the (m, l, acc) of each row over the prefix goes to the
 // workspace; the balanced split then streams only the blocks after the
 // prefix and folds it in.
+#ifndef PA_PREFIX_NCT
+#define PA_PREFIX_NCT 2
+#endif
+#ifndef PA_PREFIX_RING
+#define PA_PREFIX_RING 2
+#endif
+constexpr int kPfxNct = PA_PREFIX_NCT;  // score tiles per wave
+
+template <int D, int NCT>
+struct __align__(16) SmemPrefix {
+  float acc[kWaves][NCT * 16][D];
+  float m[kWaves][NCT * 16];
+  float l[kWaves][NCT * 16];
+  float fac[kWaves][NCT * 16];  // each wave's weight in the fold of a column
+  float mx[NCT * 16];
+  float den[NCT * 16];
+};
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void pa_prefix_kernel(DecodeArgs a) {
   using M = MfmaWave<DT, D>;
   using v8 = typename M::v8;
-  constexpr int NC = D / 32, NT = D / 16, NCT = kExtNctMax;
-  constexpr int NB = 2;
-  __shared__ SmemExtend<D, NCT> sm;
+  constexpr int NC = D / 32, NT = D / 16, NCT = kPfxNct;
+  constexpr int NB = PA_PREFIX_RING;
+  __shared__ SmemPrefix<D, NCT> sm;
   const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_q_heads;
   const int g = blockIdx.x % Hkv;
   const int sg = blockIdx.x / Hkv;
@@ -1965,26 +1988,36 @@ __global__ __launch_bounds__(kThreads) void pa_prefix_kernel(DecodeArgs a) {
     }
   }
   const bool any_bad = __syncthreads_or(bad);
-  for (int i = tid; i < ns * G * D; i += kThreads) {
-    const int sk = i / (G * D), h = (i / D) % G, d = i % D;
-    const int col = (sk / tpt) * 16 + (sk % tpt) * G + h;
+  // Fold the four waves' states: one weight per (wave, column) first, then
+  // four floats of a row per thread.
+  if (tid < NCT * 16) {
     float Mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, sm.m[w][col]);
-    float num = 0.f, den = 0.f;
-    if (Mx != -INFINITY) {
+    for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, sm.m[w][tid]);
+    float den = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = exp2f(sm.m[w][col] - Mx);
-        num += f * sm.acc[w][col][d];
-        den += f * sm.l[w][col];
-      }
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = Mx == -INFINITY ? 0.f : exp2f(sm.m[w][tid] - Mx);
+      sm.fac[w][tid] = f;
+      den += f * sm.l[w][tid];
     }
+    sm.mx[tid] = Mx;
+    sm.den[tid] = den;
+  }
+  __syncthreads();
+  constexpr int NQ = D / 4;
+  const f32x4_t nan4 = {NAN, NAN, NAN, NAN};
+  for (int i = tid; i < ns * G * NQ; i += kThreads) {
+    const int sk = i / (G * NQ), h = (i / NQ) % G, d4 = (i % NQ) * 4;
+    const int col = (sk / tpt) * 16 + (sk % tpt) * G + h;
+    f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) num += sm.fac[w][col] * *reinterpret_cast<const f32x4_t *>(&sm.acc[w][col][d4]);
     const int64_t row = (int64_t)(s0 + sk) * Hq + g * G + h;
-    a.ws_pfx_acc[row * D + d] = any_bad ? NAN : num;
-    if (d == 0) {
-      a.ws_pfx_ml[row * 2] = any_bad ? NAN : Mx;
-      a.ws_pfx_ml[row * 2 + 1] = den;
+    *reinterpret_cast<f32x4_t *>(a.ws_pfx_acc + row * D + d4) = any_bad ? nan4 : num;
+    if (d4 == 0) {
+      a.ws_pfx_ml[row * 2] = any_bad ? NAN : sm.mx[col];
+      a.ws_pfx_ml[row * 2 + 1] = sm.den[col];
     }
   }
 }
@@ -2290,6 +2323,11 @@ bool use_mfma(const pa_decode_params *p) {
 // Workgroups of the balanced grid: PA_BALANCED_WG_PER_CU per CU (checked
 // against the kernel's occupancy with its parking LDS for G query heads per
 // KV head where a device answers).
+// Workgroups per CU the balanced kernel aims for with this cache type.
+int balanced_wg_per_cu(pa_dtype kv) {
+  return kv == PA_FP8 ? PA_FP8_WG_PER_CU : kv == PA_I8 ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU;
+}
+
 // Parking slots per wave: as many as the LDS left beside the kernel's own
 // shared memory allows (per workgroup, with wg_per_cu workgroups on a CU),
 // at least 1, at most kParkSlotsMax.
@@ -2324,7 +2362,7 @@ size_t park_bytes(int G, int D, int slots) {
 }
 
 int balanced_park_slots(pa_dtype kv, int G, int D) {
-  return park_slots(G, D, byte_cache(kv) ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU);
+  return park_slots(G, D, balanced_wg_per_cu(kv));
 }
 
 // The balanced kernel for a cache type, q type and head size.
@@ -2350,10 +2388,10 @@ int balanced_workgroups(pa_dtype kv, pa_dtype qt, int D, int G) {
   int dev = 0;
   const bool bytes = byte_cache(kv);
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-    return (bytes ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU) * cu_count();
+    return balanced_wg_per_cu(kv) * cu_count();
   const int k = (kv == PA_I8 ? 4 : kv == PA_FP8 ? 8 : 0) + ((bytes ? qt : kv) == PA_BF16 ? 0 : 2) + (D == 128 ? 0 : 1);
   if (!cached[dev][k][G]) {
-    const int want = bytes ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU;
+    const int want = balanced_wg_per_cu(kv);
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, balanced_kernel(kv, qt, D), kBThreads,
                                                      park_bytes(G, D, balanced_park_slots(kv, G, D))) !=
@@ -2550,7 +2588,7 @@ pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipS
   if (use_balanced(p)) {
     LaunchEvents bev = ev;
     if (a.prefix_blocks > 0) {  // every row's attention over the shared prefix first
-      const int spg = kExtNctMax * (16 / a.group);
+      const int spg = kPfxNct * (16 / a.group);
       const dim3 pgrid((unsigned)(p->num_kv_heads * ((p->num_seqs + spg - 1) / spg)));
       const void *pfn = p->kv_dtype == PA_BF16
                             ? (p->head_dim == 128 ? reinterpret_cast<const void *>(&pa_prefix_kernel<PA_BF16, 128>)

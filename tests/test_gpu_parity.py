@@ -348,7 +348,7 @@ def test_split_launches_equal_pa_decode_bitwise():
 
 # ------------------------------------------------------------------ balanced split
 BALANCED_CASES = ["tiny_pairs", "one_long_context", "fewer_units_than_waves",
-                  "two_chunks_per_wave", "largest_batch"]
+                  "two_chunks_per_wave", "largest_batch", "more_pair_ends_than_parking_slots"]
 
 
 @pytest.mark.parametrize("case", BALANCED_CASES)
@@ -371,6 +371,10 @@ def test_balanced_split_length_mixes(case):
         spec = workloads.custom(seed=93, dtype="bf16", lens=(8192,) * 12 + (8000,),
                                 num_q_heads=32, num_kv_heads=32, head_dim=64)
         sample = [0, 5, 12]
+    elif case == "more_pair_ends_than_parking_slots":   # ~16 one-block pairs per wave
+        lens = rng.integers(1, 17, 1024)
+        spec = workloads.custom(seed=95, dtype="bf16", lens=tuple(int(x) for x in lens),
+                                num_q_heads=16, num_kv_heads=16, head_dim=128)
     else:                                 # 1024 sequences (the path's limit), some empty
         lens = rng.integers(0, 300, 1024)
         lens[::37] = 0
