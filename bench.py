@@ -18,8 +18,9 @@ placement) so the working set is several times the 256 MB Infinity Cache.
 Prints one JSON line.  value = decode tokens/s (one token per sequence per
 step) over the timed steps, wall clock between device synchronizations.
 roofline = the attention kernel (balanced split, or partitions when
-  --partition-tokens is set): algorithmic bytes per launch / its mean
-duration from HIP events recorded around it on its stream.
+  --partition-tokens is set; with a shared prefix, the prefix kernel and the
+  split together): algorithmic bytes per launch / its mean duration from HIP
+  events recorded around it on its stream.
 cpu_baseline = the fp64 CPU oracle on whole-batch passes of the same workload.
 """
 from __future__ import annotations
@@ -703,7 +704,10 @@ def main():
     achieved = mean_alg / part_s / 1e9
     step_bytes = mean_alg + g["append_bytes"]
     step_gbps = step_bytes * K / g["elapsed"] / 1e9
+    shared_prefix = (spec.prefix_len // 16) if (spec.prefix_len and not args.no_shared_prefix) else 0
     kernel_name = "pa_balanced_kernel" if g["part_tokens"] == 0 else "pa_partition_kernel"
+    if shared_prefix:   # the events span both launches: the prefix kernel, then the split
+        kernel_name = "pa_prefix_kernel+" + kernel_name
     traffic = read_traffic(kernel_name, spec.name)
     cpu = None
     if not args.no_cpu_baseline:
@@ -731,11 +735,13 @@ def main():
             "kv_dtype": {"i8": "int8 + f32 row scales", "fp8": "fp8 e4m3 + f32 row scales"}.get(spec.cache, spec.dtype),
             "pool_blocks": int(wl.num_blocks),
             "sliding_window": int(spec.window),
-            "shared_prefix_blocks": (spec.prefix_len // 16) if (spec.prefix_len and not args.no_shared_prefix) else 0,
+            "shared_prefix_blocks": shared_prefix,
             "mean_context": round(mean_kv_tokens / spec.num_seqs, 1),
             "partition_tokens": g["part_tokens"], "replicas": args.replicas,
             "kernel": args.kernel, "seed": spec.seed,
             "step": ("pool append + H2D slots/tables/lens + decode partitions (fused K/V append) + merge"
+                     .replace("decode partitions", "prefix attention + decode partitions" if shared_prefix
+                              else "decode partitions")
                      if args.append == "fused" and spec.cache not in ("i8", "fp8") else
                      f"pool append + H2D slots/tables/lens + reshape_and_cache_{'fp8' if spec.cache == 'fp8' else 'int8'}"
                      " + decode partitions + merge" if spec.cache in ("i8", "fp8") else

@@ -1246,9 +1246,19 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
   const int qbase = pair_of_unit(sm, wg0, Hkv, S);
   const int nq = min(pair_of_unit(sm, wg1 - 1, Hkv, S) - qbase + 1, kQLds / pair_bytes);
   {
+    // every load goes out before the first LDS write: one memory latency
+    constexpr int kQPer = kQLds / 16 / kBThreads;
+    static_assert(kQLds % (16 * kBThreads) == 0, "q staging: whole vectors per thread");
     const u32x4_t *src = reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
                                                            (int64_t)qbase * pair_bytes);
-    for (int i = tid; i < nq * pair_bytes / 16; i += kBThreads) reinterpret_cast<u32x4_t *>(sm.q)[i] = src[i];
+    const int nvec = nq * pair_bytes / 16;
+    u32x4_t qv[kQPer];
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k)
+      if (tid + k * kBThreads < nvec) qv[k] = src[tid + k * kBThreads];
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k)
+      if (tid + k * kBThreads < nvec) reinterpret_cast<u32x4_t *>(sm.q)[tid + k * kBThreads] = qv[k];
   }
   __syncthreads();
   if (u0 >= u1) return;
