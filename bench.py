@@ -674,9 +674,9 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); the decode path shards by sequence and KV head with no "
-              f"exchange, so run it once per GPU.", file=sys.stderr)
+        print(f"bench.py times one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the "
+              f"decode path shards by sequence and KV head with no exchange, so run it once per GPU.",
+              file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         run_copy_calibration(args.copy_calibration)

@@ -70,7 +70,7 @@ extern "C" {
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = 1,  /* a null pointer, a size or an id out of range */
-  PA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement */
+  PA_ERR_UNSUPPORTED = 2,  /* a valid request the library does not implement */
   PA_ERR_WORKSPACE = 3,    /* the decode workspace is missing or too small */
   PA_ERR_OOM = 4,          /* the block pool has too few free blocks */
   PA_ERR_HIP = 5           /* a HIP runtime call failed (e.g. launch error) */

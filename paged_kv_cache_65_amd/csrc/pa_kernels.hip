@@ -1626,12 +1626,24 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
   constexpr int NB = 2;  // blocks in flight per wave
   __shared__ SmemExtend<D, NCT> sm;
   const int Hkv = a.num_kv_heads, G = a.group;
+#ifndef PA_EXT_QG_SLOW
+  // Query groups of one (sequence, KV head, partition) are neighbours in the
+  // grid: they run together and read the same blocks, the later reads served
+  // from the Infinity Cache.
+  const int qg = blockIdx.x % a.qgroups;
+  int rest = blockIdx.x / a.qgroups;
+  const int g = rest % Hkv;
+  rest /= Hkv;
+  const int s = rest % a.num_seqs;
+  const int p = rest / a.num_seqs;
+#else
   const int g = blockIdx.x % Hkv;
   int rest = blockIdx.x / Hkv;
   const int s = rest % a.num_seqs;
   rest /= a.num_seqs;
   const int qg = rest % a.qgroups;
   const int p = rest / a.qgroups;
+#endif
   const int tid = threadIdx.x, lane = tid % 64, r = lane % 16, tq = lane / 16;
   const int wu = __builtin_amdgcn_readfirstlane(tid / 64);
   const int L = a.context_lens[s];
