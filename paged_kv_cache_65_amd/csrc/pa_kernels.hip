@@ -479,8 +479,9 @@ struct MfmaWave {
 
   // Balanced split: writes this wave's state for one (sequence, KV head)
   // pair whose query rows start at row0: the normalised output rows when the
-  // wave saw the whole pair, else an (m, l, acc) partial at partial row
-  // prow0.  `bad` turns them into NaN.
+  // wave saw the whole pair (never with a shared prefix: the merge folds the
+  // prefix in), else an (m, l, acc) partial at partial row prow0.  `bad`
+  // turns them into NaN.
   __device__ void store_segment(const DecodeArgs &a, int64_t row0, int64_t prow0, bool whole, bool bad,
                                 int lane, int G) const {
     const int r = lane % 16, tq = lane / 16;
@@ -489,28 +490,11 @@ struct MfmaWave {
     const f32x4_t nan4 = {NAN, NAN, NAN, NAN};
     if (whole) {
       const int64_t o = (row0 + r) * D + 4 * tq;
-      float fa = 1.f, fp = 0.f, den = lt;
-      const float *px = nullptr;
-      if (a.prefix_blocks > 0) {  // fold the row's attention over the shared prefix
-        const float pm = a.ws_pfx_ml[(row0 + r) * 2], pl = a.ws_pfx_ml[(row0 + r) * 2 + 1];
-        const float Mx = fmaxf(m, pm);
-        fa = exp2f(m - Mx);
-        fp = exp2f(pm - Mx);
-        den = lt * fa + pl * fp;
-        px = a.ws_pfx_acc + o;
-        if (pm != pm) bad = true;
-      }
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         f32x4_t v;
-        if (px) {
-          const f32x4_t pv = *reinterpret_cast<const f32x4_t *>(px + 16 * n);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (acc[n][e] * fa + pv[e] * fp) / den;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[n][e] / lt;
-        }
+        for (int e = 0; e < 4; ++e) v[e] = acc[n][e] / lt;
         store_out4(a.out, o + 16 * n, bad ? nan4 : v, a.out_dtype);
       }
     } else {
@@ -549,21 +533,9 @@ __device__ void flush_parked(const DecodeArgs &a, const float *st, int64_t row0,
     f32x4_t v = *reinterpret_cast<const f32x4_t *>(st + e);
     if (whole) {
       const float lt = st[G * D + G + r];
-      bool b = bad;
-      if (a.prefix_blocks > 0) {  // fold the row's attention over the shared prefix
-        const float m = st[G * D + r];
-        const float pm = a.ws_pfx_ml[(row0 + r) * 2], pl = a.ws_pfx_ml[(row0 + r) * 2 + 1];
-        const float Mx = fmaxf(m, pm), fa = exp2f(m - Mx), fp = exp2f(pm - Mx);
-        const float den = lt * fa + pl * fp;
-        const f32x4_t pv = *reinterpret_cast<const f32x4_t *>(a.ws_pfx_acc + (row0 + r) * D + e % D);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = (v[k] * fa + pv[k] * fp) / den;
-        b |= pm != pm;
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = v[k] / lt;
-      }
-      store_out4(a.out, (row0 + r) * D + e % D, b ? nan4 : v, a.out_dtype);
+      for (int k = 0; k < 4; ++k) v[k] = v[k] / lt;
+      store_out4(a.out, (row0 + r) * D + e % D, bad ? nan4 : v, a.out_dtype);
     } else {
       *reinterpret_cast<f32x4_t *>(a.ws_acc + prow0 * D + e) = bad ? nan4 : v;
     }
@@ -1403,7 +1375,10 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
           wave.compute(fr[b], token_mask(lo, (int)(mt & kUValid)), a.scale_log2, lane, nt, sm.knew[wu][k],
                        sm.vnew[wu][k]);
           if (mt & kULast) {  // (a segment may go on into the next chunk)
-            const bool wh = whole && (mt & kUPairEnd);
+            // With a shared prefix every pair leaves a partial and the merge
+            // folds the prefix in: a fold here would make each wave's last
+            // stores wait on loads of the prefix state, one after another.
+            const bool wh = whole && (mt & kUPairEnd) && a.prefix_blocks == 0;
             if (c0 + i == u1 - 1 || nparked == a.park_slots) {  // (all parking places taken: it stores)
               wave.store_segment(a, (int64_t)pq * G, (int64_t)(w + pq) * G, wh, bad, lane, G);
             } else {
@@ -1556,9 +1531,9 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_balanced_kernel(Dec
   const int C = (U + a.num_workers - 1) / a.num_workers;
   const int us = Hkv * pre_s + g * nb;
   const int w0 = us / C, w1 = (us + nb - 1) / C;
-  if (w0 == w1) return;
-  const int64_t prow = (int64_t)(w0 + s * Hkv + g) * G + r;
   const bool pfx = a.prefix_blocks > 0;
+  if (w0 == w1 && !pfx) return;  // a whole pair: written by the attention launch
+  const int64_t prow = (int64_t)(w0 + s * Hkv + g) * G + r;
   merge_row<D>(a.out, a.out_dtype, row, a.ws_ml + prow * 2, (int64_t)G * 2, a.ws_acc + prow * D, (int64_t)G * D,
                w1 - w0 + 1, lane, pfx ? a.ws_pfx_ml + row * 2 : nullptr, pfx ? a.ws_pfx_acc + row * D : nullptr);
 }
@@ -1875,7 +1850,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_extend_merge_kernel(Exten
 // tiles, the four waves of a workgroup take every fourth prefix block and
 // meet in LDS, and the (m, l, acc) of each row over the prefix goes to the
 // workspace; the balanced split then streams only the blocks after the
-// prefix and folds it in.
+// prefix, leaving a partial for every pair, and the merge folds the prefix
+// state in as one more partial.
 #ifndef PA_PREFIX_NCT
 #define PA_PREFIX_NCT 2
 #endif
