@@ -648,7 +648,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6, 7, 8])
+    ap.add_argument("--workload", type=int, default=3, choices=list(range(1, 11)))
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)

@@ -1475,17 +1475,39 @@ __device__ void merge_row(void *out, int out_dtype, int64_t row, const float *ml
       }
     }
   } else {
-    for (int q = 0; q < np; ++q) {
-      const float mq = ml[q * ml_stride];
-      nan |= mq != mq;
-      M = fmaxf(M, mq);
+    // Many partials: their (m, l) 64 at a time, one per lane, then the acc
+    // rows kFew at a time with every load of a batch issued first, so a
+    // row costs about np / kFew memory round trips instead of np.
+    for (int q0 = 0; q0 < np; q0 += 64) {
+      const bool on = q0 + lane < np;
+      const float mq = on ? ml[(int64_t)(q0 + lane) * ml_stride] : -INFINITY;
+      nan |= __builtin_amdgcn_ballot_w64(on && mq != mq) != 0;
+      M = fmaxf(M, max_xor32(max_xor16(row_max16(mq))));
     }
-#pragma unroll 4
-    for (int q = 0; q < np; ++q) {
-      const float f = exp2f(ml[q * ml_stride] - M);
-      den += f * ml[q * ml_stride + 1];
+    for (int q0 = 0; q0 < np; q0 += 64) {
+      const int nq = min(64, np - q0);
+      const bool on = lane < nq;
+      const float f = on ? exp2f(ml[(int64_t)(q0 + lane) * ml_stride] - M) : 0.f;
+      const float fl = on ? f * ml[(int64_t)(q0 + lane) * ml_stride + 1] : 0.f;
+      den += sum_xor32(sum_xor16(row_sum16(fl)));
+      for (int qb = 0; qb < nq; qb += kFew) {
+        // no branches between the loads (a batch past the end re-reads the
+        // last partial with weight 0), so they all go out before one wait
+        float av[kFew][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) num[e] += f * acc[q * acc_stride + lane * PER + e];
+        for (int k = 0; k < kFew; ++k) {
+          const int64_t qk = q0 + min(qb + k, nq - 1);
+#pragma unroll
+          for (int e = 0; e < PER; ++e) av[k][e] = acc[qk * acc_stride + lane * PER + e];
+        }
+#pragma unroll
+        for (int k = 0; k < kFew; ++k) {
+          const float fk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), min(qb + k, nq - 1)));
+          const float wk = qb + k < nq ? fk : 0.f;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) num[e] += wk * av[k][e];
+        }
+      }
     }
   }
   if (xml) {

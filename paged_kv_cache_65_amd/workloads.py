@@ -68,7 +68,9 @@ class Spec:
 
 def named(n: int) -> Spec:
     """The measured workloads (1-based; 6 and 8 are workload 3 over an INT8 and an
-    FP8 cache; 7 is a Mistral-7B-shaped batch under a 4096-token sliding window)."""
+    FP8 cache; 7 is a Mistral-7B-shaped batch under a 4096-token sliding window;
+    9 and 10 are one GPU's share of workloads 3 and 5 when they are sharded over
+    eight GPUs by KV head and by context)."""
     if n == 1:
         return Spec("tiny-fp32-mha-d64", 1, "f32", "f32", 4, 4, 4, 64, 64,
                     lens=[1, 17, 33, 100], scale=1.0 / 8.0)
@@ -93,6 +95,12 @@ def named(n: int) -> Spec:
     if n == 7:  # GQA 32/8 heads, D = 128, contexts past the window
         return Spec("mistral7b-gqa4-bf16-b32-l4kto16k-sw4096", 7, "bf16", "bf16", 32, 32, 8, 128,
                     0, len_range=(4096, 16384), window=4096)
+    if n == 9:  # one GPU's share of workload 3 under 8-way tensor parallelism: 1 KV head, 8 q heads
+        return Spec("llama70b-tp8share-gqa8-bf16-b64-l128to4096", 3, "bf16", "bf16", 64, 8, 1, 128,
+                    20000, len_range=(128, 4096))
+    if n == 10:  # one GPU's share of workload 5 under 8-way context parallelism: 4096 tokens each
+        return Spec("long-ctx-cp8share-gqa4-bf16-b4-l4096", 5, "bf16", "bf16", 4, 32, 8, 128,
+                    1024 + 64, lens=[4096] * 4)
     raise ValueError(f"no workload {n}")
 
 
