@@ -66,6 +66,8 @@ extern "C" {
 #endif
 
 #define PA_BLOCK_SIZE 16
+/* pa_decode_params.partition_tokens value that asks for the balanced split */
+#define PA_PARTITION_BALANCED (-1)
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -114,10 +116,10 @@ const char *pa_last_error(void);
  * log-sum-exp rescaling.  Two splits exist:
  *   - partitions: every context is cut into partition_tokens-token pieces,
  *     one workgroup per (piece, KV head, sequence);
- *   - balanced (automatic partitioning on the matrix-core path, at most 1024
- *     sequences and 2^15 (sequence, KV head) pairs): all (sequence, KV head,
- *     16-token block) units are cut into equal contiguous shares, one per
- *     wave of a grid that fills every CU once, whatever the length mix.
+ *   - balanced (the matrix-core path, at most 1024 sequences and 2^15
+ *     (sequence, KV head) pairs): all (sequence, KV head, 16-token block)
+ *     units are cut into equal contiguous shares, one per wave of a grid
+ *     that fills every CU once, whatever the length mix.
  * The result does not depend on the split beyond float32 rounding; it is
  * deterministic for a given device (the balanced shares depend on its CU
  * count).
@@ -133,10 +135,15 @@ const char *pa_last_error(void);
  *   max_context_len  host-known upper bound on every context_lens[s]; it sizes
  *                 the launch grid
  *   scale         usually 1/sqrt(head_dim)
- *   partition_tokens  0 = automatic (the balanced split where it applies,
- *                 else partitions of 1024, 512 or 256 tokens: the largest
- *                 that gives >= 8 workgroups per compute unit), else a
- *                 positive multiple of 16 (partitions)
+ *   partition_tokens  0 = automatic: the balanced split where it applies
+ *                 and the batch holds at least 48 units per wave at
+ *                 max_context_len (always for INT8/FP8 caches and a shared
+ *                 prefix); 512-token partitions for a smaller batch on the
+ *                 matrix-core path; else partitions of 1024, 512 or 256
+ *                 tokens, the largest that gives >= 8 workgroups per compute
+ *                 unit.  PA_PARTITION_BALANCED (-1) = the balanced split
+ *                 (an error where it cannot run).  A positive multiple of
+ *                 16 = partitions of that size.
  * Supported: head_dim in {64, 128}; num_q_heads % num_kv_heads == 0;
  *   G <= 16; fp16/bf16 with any kernel, fp32 with the VALU kernel.
  * Contract violations found on the device (a table entry outside

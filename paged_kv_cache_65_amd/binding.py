@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_OOM, PA_ERR_HIP = range(6)
 PA_F32, PA_F16, PA_BF16, PA_I8, PA_FP8 = 0, 1, 2, 3, 4
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
+PA_PARTITION_BALANCED = -1      # partition_tokens value: the balanced split
 KERNELS = {"auto": PA_KERNEL_AUTO, "valu": PA_KERNEL_VALU, "mfma": PA_KERNEL_MFMA}
 BLOCK_SIZE = 16
 

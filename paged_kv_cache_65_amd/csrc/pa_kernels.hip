@@ -2260,15 +2260,17 @@ pa_status validate(const pa_decode_params *p) {
       return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype must be F32 or q_dtype");
     if (!p->k_scales || !p->v_scales || !aligned16(p->k_scales) || !aligned16(p->v_scales))
       return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: an INT8/FP8 cache needs 16-byte aligned scale arrays");
-    if (p->kernel == PA_KERNEL_VALU || p->partition_tokens != 0 || p->k_new != nullptr)
+    if (p->kernel == PA_KERNEL_VALU || p->partition_tokens > 0 || p->k_new != nullptr)
       return pa::fail(PA_ERR_UNSUPPORTED,
                       "pa_decode: an INT8/FP8 cache is decoded by the matrix-core kernel with automatic "
                       "partitioning and no fused append");
   } else if (p->out_dtype != PA_F32 && p->out_dtype != p->kv_dtype) {
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype must be F32 or the cache type");
   }
-  if (p->partition_tokens < 0 || p->partition_tokens % kBS)
-    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: partition_tokens must be 0 or a positive multiple of 16");
+  if (p->partition_tokens < PA_PARTITION_BALANCED || (p->partition_tokens > 0 && p->partition_tokens % kBS))
+    return pa::fail(PA_ERR_INVALID_ARG,
+                    "pa_decode: partition_tokens must be 0 (automatic), PA_PARTITION_BALANCED (-1) or a "
+                    "positive multiple of 16");
   if (p->kernel != PA_KERNEL_AUTO && p->kernel != PA_KERNEL_VALU && p->kernel != PA_KERNEL_MFMA)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: unknown kernel");
   if (p->kernel == PA_KERNEL_MFMA && p->kv_dtype == PA_F32)
@@ -2285,7 +2287,7 @@ pa_status validate(const pa_decode_params *p) {
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: shared_prefix_blocks must be in [0, max_blocks_per_seq]");
   if (p->shared_prefix_blocks > 0 &&
       ((p->kv_dtype != PA_F16 && p->kv_dtype != PA_BF16) || p->sliding_window != 0 ||
-       p->partition_tokens != 0 || p->kernel == PA_KERNEL_VALU))
+       p->partition_tokens > 0 || p->kernel == PA_KERNEL_VALU))
     return pa::fail(PA_ERR_UNSUPPORTED,
                     "pa_decode: a shared prefix needs an fp16/bf16 cache, no sliding window and the "
                     "matrix-core kernel with automatic partitioning");
@@ -2298,10 +2300,11 @@ bool use_balanced(const pa_decode_params *p);
 pa_status validate_all(const pa_decode_params *p) {
   pa_status st = validate(p);
   if (st != PA_OK) return st;
-  if ((byte_cache(p->kv_dtype) || p->shared_prefix_blocks > 0) && !use_balanced(p))
+  if ((byte_cache(p->kv_dtype) || p->shared_prefix_blocks > 0 || p->partition_tokens == PA_PARTITION_BALANCED) &&
+      !use_balanced(p))
     return pa::fail(PA_ERR_UNSUPPORTED,
-                    "pa_decode: an INT8/FP8 cache needs the balanced split (<= 1024 sequences, <= 32768 "
-                    "(sequence, KV head) pairs)");
+                    "pa_decode: INT8/FP8 caches, a shared prefix and PA_PARTITION_BALANCED need the balanced "
+                    "split (the matrix-core kernel, <= 1024 sequences, <= 32768 (sequence, KV head) pairs)");
   return PA_OK;
 }
 
@@ -2321,9 +2324,14 @@ int cu_count() {
 // Automatic partition size: the largest of 1024 / 512 / 256 tokens whose grid
 // still has >= 8 workgroups per CU (shorter partitions balance better but add
 // merge work); a context that fits one such partition is not split.
+bool balanced_fits(const pa_decode_params *p);
+
 int32_t resolve_partition(const pa_decode_params *p) {
   if (p->partition_tokens > 0) return p->partition_tokens;
   const int32_t ctx = ((std::max(p->max_context_len, 1) + kBS - 1) / kBS) * kBS;
+  // a small batch on the matrix-core path (one the balanced split could run
+  // but leaves to partitions): 512-token partitions measured best
+  if (balanced_fits(p)) return std::min(ctx, 512);
   const int64_t pairs = (int64_t)p->num_seqs * p->num_kv_heads;
   const int64_t target = 8LL * cu_count();
   int32_t pt = 256;
@@ -2429,12 +2437,40 @@ int balanced_workgroups(const pa_decode_params *p) {
 
 // Automatic partitioning on the matrix-core path uses the balanced split
 // when the batch fits its LDS tables and its unit counts fit 32 bits.
-bool use_balanced(const pa_decode_params *p) {
-  if (p->partition_tokens != 0 || !use_mfma(p) || p->num_seqs < 1 || p->num_seqs > kSeqMax) return false;
+// Most units (sequence, KV head, attended block) the batch can hold.
+int64_t max_units(const pa_decode_params *p) {
+  int64_t blocks = (std::max(p->max_context_len, 0) + kBS - 1) / kBS;
+  if (p->sliding_window > 0)  // W + 1 attended tokens span at most this many blocks
+    blocks = std::min<int64_t>(blocks, (p->sliding_window + kBS) / kBS + 1);
+  return (int64_t)p->num_kv_heads * p->num_seqs * blocks;
+}
+
+// Below this many units per wave at the longest context, automatic
+// partitioning on a 16-bit cache uses partitions: wave shares that short
+// spend most of their time in the launch's fixed latency chain (lengths,
+// tables, first tiles) and leave many partials to merge, while a partition
+// grid keeps several waves per SIMD streaming.  Measured: 7B MHA (8 x 2048
+// tokens, ~36 units per wave) 46.6 us with 512-token partitions vs 50.1
+// balanced; the 8-way head and context shares of the 70B and long-context
+// batches (17 and 8 units per wave) 19.2 / 16.3 us vs 21.8 / 20.0; at 64
+// (sliding window) and 135 (70B batch) units per wave the balanced split is
+// as fast or faster.
+constexpr int64_t kBalancedMinUnitsPerWave = 48;
+
+// The balanced split can run this batch.
+bool balanced_fits(const pa_decode_params *p) {
+  if (p->partition_tokens > 0 || !use_mfma(p) || p->num_seqs < 1 || p->num_seqs > kSeqMax) return false;
   if ((int64_t)p->num_seqs * p->num_kv_heads > kPairMax) return false;
   if ((int64_t)p->num_blocks * p->num_kv_heads > UINT32_MAX) return false;
   const int64_t units = (int64_t)p->num_kv_heads * p->num_seqs * ((std::max(p->max_context_len, 0) + kBS - 1) / kBS);
   return units + (int64_t)kBWaves * balanced_workgroups(p) < INT32_MAX;
+}
+
+bool use_balanced(const pa_decode_params *p) {
+  if (!balanced_fits(p)) return false;
+  if (p->partition_tokens == PA_PARTITION_BALANCED || byte_cache(p->kv_dtype) || p->shared_prefix_blocks > 0)
+    return true;
+  return max_units(p) >= kBalancedMinUnitsPerWave * kBWaves * balanced_workgroups(p);
 }
 
 size_t round16(size_t x) { return (x + 15) / 16 * 16; }

@@ -95,6 +95,32 @@ def test_balanced_split_selection_and_workspace():
     assert pa.pa_decode_partition_tokens(_params(kv_dtype=pa.PA_F32, out_dtype=pa.PA_F32)) > 0
 
 
+def test_small_batches_take_partitions_unless_the_balanced_split_is_asked_for():
+    # fewer than 48 units per wave at the longest context (1024 waves without a
+    # GPU): 8 sequences x 32 KV heads x 128 blocks = 32768 < 49152
+    small = dict(num_seqs=8, num_q_heads=32, num_kv_heads=32, max_context_len=2048)
+    assert pa.pa_decode_partition_tokens(_params(**small)) == 512
+    assert pa.pa_decode_partition_tokens(_params(**{**small, "max_context_len": 300})) == 304
+    assert pa.pa_decode_partition_tokens(_params(**small, partition_tokens=pa.PA_PARTITION_BALANCED)) == 0
+    # 8 sequences x 32 heads x 192 blocks = 49152: the balanced split
+    assert pa.pa_decode_partition_tokens(_params(**{**small, "max_context_len": 3072})) == 0
+    # a sliding window bounds the units a pair can hold: 48 x 1024 units need
+    # 32 x 8 pairs of >= 192 blocks, more than a 1024-token window spans
+    assert pa.pa_decode_partition_tokens(_params(num_seqs=32, num_q_heads=32, num_kv_heads=8,
+                                                 max_context_len=16384, sliding_window=1024)) == 512
+    assert pa.pa_decode_partition_tokens(_params(num_seqs=32, num_q_heads=32, num_kv_heads=8,
+                                                 max_context_len=16384, sliding_window=4096)) == 0
+    # the balanced split cannot run an fp32 cache or > 1024 sequences: asking is an error
+    for bad, status in ((dict(kv_dtype=pa.PA_F32, out_dtype=pa.PA_F32, partition_tokens=pa.PA_PARTITION_BALANCED),
+                         pa.PA_ERR_UNSUPPORTED),
+                        (dict(num_seqs=1025, partition_tokens=pa.PA_PARTITION_BALANCED), pa.PA_ERR_UNSUPPORTED),
+                        (dict(partition_tokens=-2), pa.PA_ERR_INVALID_ARG)):
+        with pytest.raises(pa.PaError) as err:
+            pa.pa_decode_partition_tokens(_params(**bad))
+        assert err.value.status == status
+        assert pa.pa_decode_workspace_bytes(_params(**bad)) == 0
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 96, pa.PA_ERR_UNSUPPORTED),
     ("num_kv_heads", 7, pa.PA_ERR_INVALID_ARG),

@@ -73,8 +73,9 @@ def _params(spec, wl, gst, mb, out, pt, start=None, stop=None):
     return prm, (tab_d, lens_d, q)
 
 
-# 256: partitions + merge kernel; 0: balanced split + merge; 2048: one partition, no merge launch
-@pytest.mark.parametrize("pt", [256, 0, 2048])
+# 256: partitions + merge kernel; 0: automatic; -1: balanced split + merge; 2048: one
+# partition, no merge launch
+@pytest.mark.parametrize("pt", [256, 0, -1, 2048])
 def test_decode_with_events_is_bitwise_the_same(events, pt):
     spec, wl, gst, mb = _case()
     print(f"[case] events pt={pt}", flush=True)
@@ -92,7 +93,7 @@ def test_decode_with_events_is_bitwise_the_same(events, pt):
     assert 0.0 < t < 1000.0
 
 
-@pytest.mark.parametrize("pt", [256, 0, 2048])
+@pytest.mark.parametrize("pt", [256, 0, -1, 2048])
 def test_split_launches_with_events(events, pt):
     spec, wl, gst, mb = _case()
     print(f"[case] split events pt={pt}", flush=True)

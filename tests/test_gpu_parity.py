@@ -18,6 +18,7 @@ from paged_kv_cache_65_amd import binding as pa  # noqa: E402
 from paged_kv_cache_65_amd import workloads  # noqa: E402
 from tests import gpu_side, oracle_side  # noqa: E402
 
+BAL = pa.PA_PARTITION_BALANCED
 pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
 
@@ -149,7 +150,8 @@ def test_decode_sweep(dtype, D, Hq, Hkv):
     ref = oracle_side.decode(wl, ost, mb)
     kernels = ["valu"] if dtype == "f32" else ["valu", "mfma"]
     for kern in kernels:
-        for pt in (0, 16, 64, 512, 1024):
+        # 0: automatic (partitions at these sizes); -1: the balanced split
+        for pt in ((0, BAL, 16, 64, 512, 1024) if kern == "mfma" else (0, 16, 64, 512, 1024)):
             _say(f"  kernel={kern} partition_tokens={pt}")
             out = gpu_side.decode(wl, gst, mb, out_dtype="f32", kernel=kern, partition_tokens=pt)
             got = _f32(out)
@@ -252,7 +254,7 @@ def test_contract_violations_give_nan_rows_not_faults():
     lens_d = torch.from_numpy(l).cuda()
     q = gpu_side.to_device(wl.q, "bf16")
     for kern in ("valu", "mfma"):
-        for pt in (0, 16):
+        for pt in ((0, BAL, 16) if kern == "mfma" else (0, 16)):
             out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
             pa.pa_decode(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, 2, int(l.max()),
                          spec.fp32_scale(), partition_tokens=pt, kernel=kern)
@@ -306,6 +308,17 @@ def test_workload_4_shared_prefix_sampled():
     assert all(gst.pool.refcount(int(b)) == 257 for b in owner_blocks)
 
 
+def test_workload_9_tensor_parallel_share_sampled():
+    # one GPU's share of workload 3 under 8-way KV-head sharding: 1 KV head, 8 q heads,
+    # every pair cut into ~16 partials (the merge's many-partial path)
+    _named_case(9, sample=[0, 5, 33, 63], kernels=("auto", "valu"))
+
+
+def test_workload_10_context_parallel_share():
+    # one GPU's share of workload 5 under 8-way context sharding: 4 x 4096 tokens
+    _named_case(10, sample=[0, 3], kernels=("auto", "valu"))
+
+
 def test_workload_5_long_context_loop_sampled_steps():
     spec = workloads.named(5)
     wl = workloads.generate(spec)
@@ -333,7 +346,7 @@ def test_split_launches_equal_pa_decode_bitwise():
     wl = workloads.generate(spec)
     gst = gpu_side.build(wl)
     mb = oracle_side.max_blocks_for(wl)
-    for pt in (256, 0):
+    for pt in (256, 0, BAL):
         whole = gpu_side.decode(wl, gst, mb, out_dtype="f32", partition_tokens=pt)
         tab_d, lens_d, _, l = gpu_side.tables(gst, mb)
         q = gpu_side.to_device(wl.q, "bf16")
@@ -386,9 +399,9 @@ def test_balanced_split_length_mixes(case):
     tab_d, lens_d, _, lh = gpu_side.tables(gst, mb)
     q = gpu_side.to_device(wl.q, spec.dtype)
     prm = pa.make_decode_params(torch.empty(1, device="cuda"), q, gst.k_cache, gst.v_cache, tab_d,
-                                lens_d, spec.num_kv_heads, int(lh.max()), spec.fp32_scale(), 0, "mfma")
+                                lens_d, spec.num_kv_heads, int(lh.max()), spec.fp32_scale(), BAL, "mfma")
     assert pa.pa_decode_partition_tokens(prm) == 0          # the balanced split runs
-    out = gpu_side.decode(wl, gst, mb, out_dtype="f32", kernel="mfma", partition_tokens=0)
+    out = gpu_side.decode(wl, gst, mb, out_dtype="f32", kernel="mfma", partition_tokens=BAL)
     got = _f32(out) if sample is None else _f32(out)[sample]
     err = np.max(np.abs(got - ref))
     _say(f"  {case}: max_abs_err={err:.3e}")
@@ -398,7 +411,8 @@ def test_balanced_split_length_mixes(case):
 
 
 # ------------------------------------------------------------------ fused append
-@pytest.mark.parametrize("dtype,D,kern,pt", [("bf16", 128, "mfma", 0), ("bf16", 128, "mfma", 16),
+@pytest.mark.parametrize("dtype,D,kern,pt", [("bf16", 128, "mfma", 0), ("bf16", 128, "mfma", -1),
+                                             ("bf16", 128, "mfma", 16),
                                              ("f16", 64, "mfma", 64), ("bf16", 128, "valu", 0),
                                              ("f32", 64, "valu", 32)])
 def test_fused_append_equals_append_then_decode(dtype, D, kern, pt):
@@ -419,7 +433,7 @@ def test_balanced_fused_append_with_more_pair_ends_than_one_chunk_stages():
     spec = workloads.custom(seed=95, dtype="bf16", lens=lens, num_q_heads=16, num_kv_heads=16,
                             head_dim=64, decode_steps=2)
     wl, gst, ost = _both(spec, steps=0)
-    _fused_steps(wl, gst, ost, "mfma", 0)
+    _fused_steps(wl, gst, ost, "mfma", BAL)
 
 
 def _fused_steps(wl, gst, ost, kern, pt):
@@ -496,7 +510,7 @@ def test_one_workspace_serves_calls_of_any_shape():
         tab_d, lens_d, _, lh = gpu_side.tables(gst, mb)
         q = gpu_side.to_device(wl.q, dt)
         for kern in ("mfma", "valu"):
-            for pt in (0, 16, 64, 256):
+            for pt in ((0, BAL, 16, 64, 256) if kern == "mfma" else (0, 16, 64, 256)):
                 whole = torch.full(q.shape, -7.0, dtype=torch.float32, device="cuda")
                 split = torch.full(q.shape, -7.0, dtype=torch.float32, device="cuda")
                 prm = pa.make_decode_params(whole, q, gst.k_cache, gst.v_cache, tab_d, lens_d,

@@ -45,8 +45,9 @@ def _both(spec):
 
 
 @pytest.mark.parametrize("dtype,D,Hq,Hkv,kern,pt", [
-    ("bf16", 128, 16, 2, "auto", 0),      # balanced split
-    ("f16", 64, 8, 8, "auto", 0),         # balanced split, G = 1
+    ("bf16", 128, 16, 2, "auto", 0),      # automatic (partitions at this size)
+    ("bf16", 128, 16, 2, "auto", -1),     # balanced split
+    ("f16", 64, 8, 8, "auto", -1),        # balanced split, G = 1
     ("bf16", 128, 8, 1, "mfma", 16),      # partitions of one block
     ("bf16", 128, 8, 2, "mfma", 256),
     ("f32", 64, 4, 2, "auto", 64),        # VALU kernel (fp32 cache)
@@ -70,14 +71,14 @@ def test_window_covering_every_context_is_the_full_decode_bitwise():
                             head_dim=128)
     wl, gst, ost = _both(spec)
     mb = oracle_side.max_blocks_for(wl)
-    for pt in (0, 64):
+    for pt in (0, -1, 64):
         full = gpu_side.decode(wl, gst, mb, out_dtype="f32", partition_tokens=pt)
         for W in (max(LENS) - 1, 10 ** 6):
             assert torch.equal(gpu_side.decode(wl, gst, mb, out_dtype="f32", partition_tokens=pt, window=W),
                                full), (pt, W)
 
 
-@pytest.mark.parametrize("pt", [0, 16, 128])
+@pytest.mark.parametrize("pt", [0, -1, 16, 128])
 def test_table_entries_before_the_window_are_never_read(pt):
     # entries of blocks wholly before the window set to -1 or outside the pool:
     # a read would make the row NaN (bad id); the output must not change
@@ -110,7 +111,7 @@ def test_int8_cache_window_matches_oracle():
         assert np.max(np.abs(_f32(out) - ref)) <= 2e-3, W
 
 
-@pytest.mark.parametrize("pt", [0, 32])
+@pytest.mark.parametrize("pt", [0, -1, 32])
 def test_window_with_fused_append(pt):
     spec = workloads.custom(seed=84, dtype="bf16", lens=(5, 40, 16, 300, 33, 64), num_q_heads=8,
                             num_kv_heads=2, head_dim=128, decode_steps=20)
