@@ -2348,9 +2348,6 @@ bool use_mfma(const pa_decode_params *p) {
   return p->kernel == PA_KERNEL_MFMA || (p->kernel == PA_KERNEL_AUTO && p->kv_dtype != PA_F32);
 }
 
-// Workgroups of the balanced grid: PA_BALANCED_WG_PER_CU per CU (checked
-// against the kernel's occupancy with its parking LDS for G query heads per
-// KV head where a device answers).
 // Workgroups per CU the balanced kernel aims for with this cache type.
 int balanced_wg_per_cu(pa_dtype kv) {
   return kv == PA_FP8 ? PA_FP8_WG_PER_CU : kv == PA_I8 ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU;
@@ -2411,6 +2408,9 @@ const void *balanced_kernel(pa_dtype kv, pa_dtype qt, int D) {
   return D == 128 ? kfn<MfmaWave<PA_F16, 128>, 128>() : kfn<MfmaWave<PA_F16, 64>, 64>();
 }
 
+// Workgroups of the balanced grid: balanced_wg_per_cu per CU (checked
+// against the kernel's occupancy with its parking LDS for G query heads per
+// KV head where a device answers).
 int balanced_workgroups(pa_dtype kv, pa_dtype qt, int D, int G) {
   static int cached[64][12][kGMax + 1] = {};
   int dev = 0;
@@ -2476,9 +2476,8 @@ bool use_balanced(const pa_decode_params *p) {
 size_t round16(size_t x) { return (x + 15) / 16 * 16; }
 
 // Balanced-split workspace: [S+1] int32 block offsets, then per slot
-// (NW + S*Hkv - 1 of them) G rows of (m, l) and G rows of D accumulators.
-// Balanced workspace: block offsets, partial (m, l) and acc slots, then with
-// a shared prefix the rows' (m, l) and acc over it.
+// (NW + S*Hkv - 1 of them) G rows of (m, l) and G rows of D accumulators,
+// then with a shared prefix every row's (m, l) and acc over it.
 size_t balanced_bytes(const pa_decode_params *p, size_t *ml_off, size_t *acc_off, size_t *pfx_off = nullptr) {
   const int64_t nw = (int64_t)kBWaves * balanced_workgroups(p);
   const int64_t slots = nw + (int64_t)p->num_seqs * p->num_kv_heads - 1;
