@@ -1350,9 +1350,10 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
         const int i = i0 + b;
         refill(fr[(b + NB - 1) % NB], i + NB - 1);
         if (i < nc) {
-#ifndef PA_NO_PRIO
-          set_wave_priority((u1 - c0 - i) * 4 / (C + 1));
-#endif
+          // With several waves per SIMD (byte caches) the ones further along
+          // their share yield issue slots to the others; with one wave per
+          // SIMD (16-bit caches) it only cost time (1 % on workloads 3, 4, 7).
+          if constexpr (W::kBalWgPerCu > 1) set_wave_priority((u1 - c0 - i) * 4 / (C + 1));
           const uint32_t mt = __builtin_amdgcn_readlane(meta, i);
           const int pq = (int)(mt >> kUPairShift);
           if (mt & kUFirst) {
@@ -1623,7 +1624,6 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
   constexpr int NB = 2;  // blocks in flight per wave
   __shared__ SmemExtend<D, NCT> sm;
   const int Hkv = a.num_kv_heads, G = a.group;
-#ifndef PA_EXT_QG_SLOW
   // Query groups of one (sequence, KV head, partition) are neighbours in the
   // grid: they run together and read the same blocks, the later reads served
   // from the Infinity Cache.
@@ -1633,14 +1633,6 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
   rest /= Hkv;
   const int s = rest % a.num_seqs;
   const int p = rest / a.num_seqs;
-#else
-  const int g = blockIdx.x % Hkv;
-  int rest = blockIdx.x / Hkv;
-  const int s = rest % a.num_seqs;
-  rest /= a.num_seqs;
-  const int qg = rest % a.qgroups;
-  const int p = rest / a.qgroups;
-#endif
   const int tid = threadIdx.x, lane = tid % 64, r = lane % 16, tq = lane / 16;
   const int wu = __builtin_amdgcn_readfirstlane(tid / 64);
   const int L = a.context_lens[s];
