@@ -1,12 +1,21 @@
 /*
  * pa.h -- C ABI of libpa: paged decode attention on AMD MI355X (gfx950).
  *
- * The library exports three groups of calls:
- *   1. pa_decode            paged decode attention (one new query per sequence)
- *   2. pa_reshape_and_cache append new tokens' K/V into the block pool through
+ * The library exports these groups of calls:
+ *   1. pa_decode            paged decode attention (one new query per sequence;
+ *                           optional sliding window, shared prefix, fused
+ *                           append); pa_decode_partitions + pa_decode_merge
+ *                           run it as two launches
+ *   2. pa_extend            the same attention for several new tokens per
+ *                           sequence (chunked prefill, speculative verify)
+ *   3. pa_reshape_and_cache append new tokens' K/V into the block pool through
  *      pa_copy_blocks       a slot mapping; whole-block copies for copy-on-write
- *   3. pa_block_pool_* /    a host-side refcounted block pool that owns block
- *      pa_seq_*             tables, hands out slots and decides copy-on-write
+ *                           (_int8 / _fp8 variants quantize into byte caches)
+ *   4. pa_swap_blocks       block copies between a device cache and a pinned
+ *                           host pool (preemption)
+ *   5. pa_block_pool_* /    a host-side refcounted block pool that owns block
+ *      pa_seq_*             tables, hands out slots, decides copy-on-write and
+ *                           swaps sequences out and in
  *
  * Conventions (all calls):
  *   - Every call returns pa_status; nothing throws or aborts across the ABI.
