@@ -29,6 +29,12 @@
 //     LDS, cross-lane reductions by shuffles.
 // Scores are kept in the log2 domain (scale * log2(e) folded into one
 // multiply) so the exponentials are single v_exp_f32 instructions.
+//
+// Also here: MfmaWaveI8, the same matrix-core policy over INT8 / FP8 code
+// tiles with per-row scales; multi-query ("extend") attention; the kernel that
+// computes attention over a shared prefix once for every sequence; the
+// quantizing append; and block copies between a device cache and pinned host
+// memory (swap).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -1860,7 +1866,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_extend_merge_kernel(Exten
 // KV-cache machine", Lab B, the system prompt paid once).  The attention of
 // every query row over the prefix is computed once per KV head instead of
 // once per sequence: the score tile's 16 columns are (sequence, head) pairs,
-// sequence-major (16/G sequences of the G heads), a wave holds kExtNctMax
+// sequence-major (16/G sequences of the G heads), a wave holds kPfxNct
 // tiles, the four waves of a workgroup take every fourth prefix block and
 // meet in LDS, and the (m, l, acc) of each row over the prefix goes to the
 // workspace; the balanced split then streams only the blocks after the

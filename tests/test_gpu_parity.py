@@ -410,6 +410,30 @@ def test_balanced_split_length_mixes(case):
         assert np.all(got[np.asarray(wl.prompt_lens) == 0] == 0)
 
 
+def test_more_sequences_than_the_balanced_split_holds():
+    # 1500 sequences (the balanced split holds 1024): automatic partitioning
+    # takes the partition kernel; asking for the balanced split is an error
+    lens = tuple(int(x) for x in np.random.default_rng(96).integers(0, 120, 1500))
+    spec = workloads.custom(seed=96, dtype="f16", lens=lens, num_q_heads=16, num_kv_heads=4, head_dim=64)
+    wl, gst, ost = _both(spec)
+    mb = oracle_side.max_blocks_for(wl)
+    ref = oracle_side.decode(wl, ost, mb)
+    tab_d, lens_d, _, lh = gpu_side.tables(gst, mb)
+    q = gpu_side.to_device(wl.q, spec.dtype)
+    prm = pa.make_decode_params(torch.empty(1, device="cuda"), q, gst.k_cache, gst.v_cache, tab_d, lens_d,
+                                spec.num_kv_heads, int(lh.max()), spec.fp32_scale(), 0, "mfma")
+    assert pa.pa_decode_partition_tokens(prm) > 0
+    for kern in ("mfma", "valu"):
+        out = gpu_side.decode(wl, gst, mb, out_dtype="f32", kernel=kern, partition_tokens=0)
+        got = _f32(out)
+        err = np.max(np.abs(got - ref))
+        _say(f"  1500 sequences kernel={kern} max_abs_err={err:.3e}")
+        assert np.all(np.isfinite(got)) and err <= TOL["f16"], err
+        assert np.all(got[np.asarray(wl.prompt_lens) == 0] == 0)
+    with pytest.raises(pa.PaError):
+        gpu_side.decode(wl, gst, mb, out_dtype="f32", kernel="mfma", partition_tokens=BAL)
+
+
 # ------------------------------------------------------------------ fused append
 @pytest.mark.parametrize("dtype,D,kern,pt", [("bf16", 128, "mfma", 0), ("bf16", 128, "mfma", -1),
                                              ("bf16", 128, "mfma", 16),
