@@ -147,10 +147,14 @@ const char *pa_last_error(void);
  *   partition_tokens  0 = automatic: the balanced split where it applies
  *                 and the batch holds at least 48 units per wave at
  *                 max_context_len (always for INT8/FP8 caches and a shared
- *                 prefix); 512-token partitions for a smaller batch on the
- *                 matrix-core path; else partitions of 1024, 512 or 256
- *                 tokens, the largest that gives >= 8 workgroups per compute
- *                 unit.  PA_PARTITION_BALANCED (-1) = the balanced split
+ *                 prefix); for a smaller batch on the matrix-core path,
+ *                 partitions giving about one workgroup per compute unit
+ *                 (one per (sequence, KV head) pair, with no merge, once the
+ *                 pairs outnumber the compute units); else partitions of
+ *                 1024, 512 or 256 tokens, the largest that gives >= 8
+ *                 workgroups per compute unit.  Under a sliding window W the
+ *                 partitions cover the attended range, at most W + 16
+ *                 tokens.  PA_PARTITION_BALANCED (-1) = the balanced split
  *                 (an error where it cannot run).  A positive multiple of
  *                 16 = partitions of that size.
  * Supported: head_dim in {64, 128}; num_q_heads % num_kv_heads == 0;

@@ -98,16 +98,24 @@ def test_balanced_split_selection_and_workspace():
 def test_small_batches_take_partitions_unless_the_balanced_split_is_asked_for():
     # fewer than 48 units per wave at the longest context (1024 waves without a
     # GPU): 8 sequences x 32 KV heads x 128 blocks = 32768 < 49152
+    # ... about one workgroup per CU: with as many (sequence, KV head) pairs as
+    # CUs (256 without a GPU) each pair is one partition and nothing is merged
     small = dict(num_seqs=8, num_q_heads=32, num_kv_heads=32, max_context_len=2048)
-    assert pa.pa_decode_partition_tokens(_params(**small)) == 512
+    assert pa.pa_decode_partition_tokens(_params(**small)) == 2048
+    assert pa.pa_decode_workspace_bytes(_params(**small)) == 0
     assert pa.pa_decode_partition_tokens(_params(**{**small, "max_context_len": 300})) == 304
+    # 64 pairs: each range cut into 256 / 64 = 4 pieces, ceil(4304 / 4) = 1076 -> 1088
+    tp = dict(num_seqs=64, num_q_heads=8, num_kv_heads=1, max_context_len=4300)
+    assert pa.pa_decode_partition_tokens(_params(**tp)) == 1088
+    assert pa.pa_decode_workspace_bytes(_params(**tp)) == 64 * 8 * 4 * (128 + 2) * 4
     assert pa.pa_decode_partition_tokens(_params(**small, partition_tokens=pa.PA_PARTITION_BALANCED)) == 0
     # 8 sequences x 32 heads x 192 blocks = 49152: the balanced split
     assert pa.pa_decode_partition_tokens(_params(**{**small, "max_context_len": 3072})) == 0
     # a sliding window bounds the units a pair can hold: 48 x 1024 units need
     # 32 x 8 pairs of >= 192 blocks, more than a 1024-token window spans
-    assert pa.pa_decode_partition_tokens(_params(num_seqs=32, num_q_heads=32, num_kv_heads=8,
-                                                 max_context_len=16384, sliding_window=1024)) == 512
+    # (256 pairs: one partition over the window's W + 16 tokens, no merge)
+    win = _params(num_seqs=32, num_q_heads=32, num_kv_heads=8, max_context_len=16384, sliding_window=1024)
+    assert pa.pa_decode_partition_tokens(win) == 1040 and pa.pa_decode_workspace_bytes(win) == 0
     assert pa.pa_decode_partition_tokens(_params(num_seqs=32, num_q_heads=32, num_kv_heads=8,
                                                  max_context_len=16384, sliding_window=4096)) == 0
     # the balanced split cannot run an fp32 cache or > 1024 sequences: asking is an error
