@@ -25,7 +25,9 @@
  *     stream (hipStream_t passed as void*, NULL = the default stream).  They
  *     enqueue work asynchronously and never synchronize.  The library
  *     allocates no device memory: the decode workspace is caller-provided.
- *   - Every device pointer must be 16-byte aligned.
+ *   - Every device pointer must be 16-byte aligned; one for an array with no
+ *     elements (no sequences, no query rows, a table with no columns) may be
+ *     NULL.
  *   - Block size is fixed at PA_BLOCK_SIZE = 16 tokens.
  *
  * Cache layout (one layer).  k_cache and v_cache each hold num_blocks physical

@@ -2232,7 +2232,10 @@ pa_status hip_check(hipError_t e, const char *what) {
 
 pa_status validate(const pa_decode_params *p) {
   if (!p) return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: params is NULL");
-  if (!p->out || !p->q || !p->k_cache || !p->v_cache || !p->block_tables || !p->context_lens)
+  // An array with no elements (no sequences; no table columns) may be NULL.
+  const bool rows = p->num_seqs > 0, cols = rows && p->max_blocks_per_seq > 0;
+  if ((rows && (!p->out || !p->q || !p->context_lens)) || (cols && !p->block_tables) || !p->k_cache ||
+      !p->v_cache)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: NULL device pointer");
   if (!aligned16(p->out) || !aligned16(p->q) || !aligned16(p->k_cache) || !aligned16(p->v_cache) ||
       !aligned16(p->block_tables) || !aligned16(p->context_lens))
@@ -2247,8 +2250,9 @@ pa_status validate(const pa_decode_params *p) {
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: at most %d query heads per KV head", kGMax);
   if (p->head_dim != 64 && p->head_dim != 128)
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim must be 64 or 128");
-  if (p->max_blocks_per_seq <= 0 || p->num_blocks <= 0 || p->max_context_len < 0)
-    return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: sizes must be positive");
+  if (p->max_blocks_per_seq < 0 || p->num_blocks <= 0 || p->max_context_len < 0)
+    return pa::fail(PA_ERR_INVALID_ARG,
+                    "pa_decode: num_blocks must be positive, max_blocks_per_seq and max_context_len >= 0");
   if (!(valid_dtype(p->kv_dtype) || byte_cache(p->kv_dtype)) || !valid_dtype(p->out_dtype))
     return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: unknown dtype");
   if (byte_cache(p->kv_dtype)) {
@@ -2996,7 +3000,10 @@ struct ExtendShape {
 
 pa_status validate_extend(const pa_extend_params *p) {
   if (!p) return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: params is NULL");
-  if (!p->out || !p->q || !p->k_cache || !p->v_cache || !p->block_tables || !p->context_lens || !p->query_start)
+  // An array with no elements (no query rows; no sequences; no table columns) may be NULL.
+  const bool rows = p->num_query_rows > 0, seqs = p->num_seqs > 0, cols = seqs && p->max_blocks_per_seq > 0;
+  if ((rows && (!p->out || !p->q)) || (seqs && !p->context_lens) || (cols && !p->block_tables) ||
+      !p->query_start || !p->k_cache || !p->v_cache)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: NULL device pointer");
   if (!aligned16(p->out) || !aligned16(p->q) || !aligned16(p->k_cache) || !aligned16(p->v_cache) ||
       !aligned16(p->block_tables) || !aligned16(p->context_lens) || !aligned16(p->query_start))
@@ -3013,8 +3020,9 @@ pa_status validate_extend(const pa_extend_params *p) {
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_extend: the cache must be fp16 or bf16");
   if (p->out_dtype != PA_F32 && p->out_dtype != p->kv_dtype)
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_extend: out_dtype must be F32 or the cache type");
-  if (p->max_blocks_per_seq <= 0 || p->num_blocks <= 0 || p->max_context_len < 0 || p->max_query_len < 0)
-    return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: sizes must be positive");
+  if (p->max_blocks_per_seq < 0 || p->num_blocks <= 0 || p->max_context_len < 0 || p->max_query_len < 0)
+    return pa::fail(PA_ERR_INVALID_ARG,
+                    "pa_extend: num_blocks must be positive, the other sizes >= 0");
   if (p->partition_tokens < 0 || p->partition_tokens % kBS)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: partition_tokens must be 0 or a positive multiple of 16");
   if (!std::isfinite(p->scale)) return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: scale must be finite");

@@ -95,6 +95,21 @@ def test_balanced_split_selection_and_workspace():
     assert pa.pa_decode_partition_tokens(_params(kv_dtype=pa.PA_F32, out_dtype=pa.PA_F32)) > 0
 
 
+def test_arrays_without_elements_may_be_null():
+    # every context empty: a table with no columns needs no pointer
+    p = _params(num_seqs=2, max_blocks_per_seq=0, max_context_len=0, block_tables=None)
+    assert pa.pa_decode_partition_tokens(p) >= 0
+    # no sequences: out, q, lengths and tables need none either
+    p = _params(num_seqs=0, out=None, q=None, context_lens=None, block_tables=None)
+    assert pa.pa_decode_partition_tokens(p) >= 0
+    # but a table with columns does
+    with pytest.raises(pa.PaError) as err:
+        pa.pa_decode_partition_tokens(_params(block_tables=None))
+    assert err.value.status == pa.PA_ERR_INVALID_ARG
+    with pytest.raises(pa.PaError):
+        pa.pa_decode_partition_tokens(_params(max_blocks_per_seq=-1))
+
+
 def test_small_batches_take_partitions_unless_the_balanced_split_is_asked_for():
     # fewer than 48 units per wave at the longest context (1024 waves without a
     # GPU): 8 sequences x 32 KV heads x 128 blocks = 32768 < 49152
