@@ -131,8 +131,12 @@ def test_small_batches_take_partitions_unless_the_balanced_split_is_asked_for():
     # (256 pairs: one partition over the window's W + 16 tokens, no merge)
     win = _params(num_seqs=32, num_q_heads=32, num_kv_heads=8, max_context_len=16384, sliding_window=1024)
     assert pa.pa_decode_partition_tokens(win) == 1040 and pa.pa_decode_workspace_bytes(win) == 0
+    # with a pair for every CU a window makes one partition per pair (W + 16 tokens, no merge);
+    # fewer pairs with enough units keep the balanced split
     assert pa.pa_decode_partition_tokens(_params(num_seqs=32, num_q_heads=32, num_kv_heads=8,
-                                                 max_context_len=16384, sliding_window=4096)) == 0
+                                                 max_context_len=16384, sliding_window=4096)) == 4112
+    assert pa.pa_decode_partition_tokens(_params(num_seqs=64, num_q_heads=16, num_kv_heads=2,
+                                                 max_context_len=16384, sliding_window=8192)) == 0
     # the balanced split cannot run an fp32 cache or > 1024 sequences: asking is an error
     for bad, status in ((dict(kv_dtype=pa.PA_F32, out_dtype=pa.PA_F32, partition_tokens=pa.PA_PARTITION_BALANCED),
                          pa.PA_ERR_UNSUPPORTED),
