@@ -1214,16 +1214,59 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
   const int wg1 = min(U, wg0 + kBWaves * C);
   const int w = blockIdx.x * kBWaves + wu;
   const int u0 = w * C, u1 = min(U, u0 + C);
-  // The first chunk's block ids go out before the q staging below.
-  int id_first = 0;
-  if (u0 < u1 && lane < u1 - u0) {
-    const int u = u0 + lane;
-    const int s = seq_of_block(sm, u / Hkv, S);
-    const int nb = sm.pre[s + 1] - sm.pre[s];
-    const int off = u - Hkv * sm.pre[s];
-    const int jb = first_block(sm.len[s], a);
-    id_first = a.block_tables[(int64_t)s * a.max_blocks + jb + off % nb];
-  }
+  constexpr int EB = 2;
+  // A chunk's units, one per lane, with their loads issued: the block id and,
+  // for fused appends, the slots and new K / V rows of the units holding a
+  // pair's last position (at most kAppendMax per chunk: the chunk ends early).
+  struct ChunkHead {
+    int nc, s, g, j, L, nb, id;
+    uint64_t amask;
+    int64_t slot_l;
+    int pos[kAppendMax];
+    uint32_t kr[kAppendMax], vr[kAppendMax];
+  };
+  auto chunk_head = [&](int c0) {
+    ChunkHead h;
+    h.nc = min(64, u1 - c0);
+    const int u = min(c0 + lane, u1 - 1);
+    h.s = seq_of_block(sm, u / Hkv, S);
+    h.nb = sm.pre[h.s + 1] - sm.pre[h.s];
+    const int off = u - Hkv * sm.pre[h.s];
+    h.g = off / h.nb;
+    h.j = off - h.g * h.nb;
+    h.L = sm.len[h.s];
+    const int jb = first_block(h.L, a);  // attended block j is table entry jb + j
+    h.id = a.block_tables[(int64_t)h.s * a.max_blocks + jb + h.j];
+    h.amask = 0;
+    if (W::kAppend && a.k_new != nullptr) {
+      h.amask = __builtin_amdgcn_ballot_w64(lane < h.nc && h.j == h.nb - 1);
+      uint64_t rest = h.amask;
+#pragma unroll
+      for (int k = 0; k < kAppendMax; ++k) rest &= rest - 1;
+      if (rest) {
+        h.nc = __builtin_ctzll(rest);
+        h.amask &= (1ull << h.nc) - 1;
+      }
+    }
+    h.slot_l = ((h.amask >> lane) & 1) ? a.slot_mapping[h.s] : -1;
+    uint64_t mm = h.amask;
+#pragma unroll
+    for (int k = 0; k < kAppendMax; ++k) {
+      h.pos[k] = mm ? __builtin_ctzll(mm) : -1;
+      mm &= mm - 1;
+      h.kr[k] = h.vr[k] = 0;
+      if (h.pos[k] >= 0 && lane < D * EB / 4) {
+        const int sk = __builtin_amdgcn_readlane(h.s, h.pos[k]), gk = __builtin_amdgcn_readlane(h.g, h.pos[k]);
+        const int64_t row = ((int64_t)sk * Hkv + gk) * D * EB / 4;
+        h.kr[k] = reinterpret_cast<const uint32_t *>(a.k_new)[row + lane];
+        h.vr[k] = reinterpret_cast<const uint32_t *>(a.v_new)[row + lane];
+      }
+    }
+    return h;
+  };
+  // The first chunk's loads go out with the q staging below (one latency for both).
+  ChunkHead h;
+  if (u0 < u1) h = chunk_head(u0);
 
   // q rows of the pairs this workgroup touches (as many as fit), contiguous in q.
   const int pair_bytes = G * D * 2;
@@ -1251,7 +1294,6 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
   constexpr int NB = W::kBalRing;  // blocks held in registers per wave
   typename W::Frag fr[NB];
   bool bad = false, whole = false;
-  constexpr int EB = 2;
   // A segment that ends before the wave's share does is parked in LDS (up
   // to park_slots of them, sized by the host to the LDS left) and written
   // when the share is done: stores count in the same counter as the ring's
@@ -1262,62 +1304,27 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
   int nparked = 0;
   for (int c0 = u0; c0 < u1;) {
     // ---- this chunk's units, one per lane
-    int nc = min(64, u1 - c0);
-    const int u = min(c0 + lane, u1 - 1);
-    const int s = seq_of_block(sm, u / Hkv, S);
-    const int nb = sm.pre[s + 1] - sm.pre[s];
-    const int off = u - Hkv * sm.pre[s];
-    const int g = off / nb, j = off - g * nb;
-    const int L = sm.len[s];
-    const int jb = first_block(L, a);  // attended block j is table entry jb + j
-    const bool pend = j == nb - 1;
-    // Fused append: the unit holding position L-1 of a pair takes the new
-    // token.  At most kAppendMax such units per chunk (the chunk ends early).
-    uint64_t amask = 0;
-    if (W::kAppend && a.k_new != nullptr) {
-      amask = __builtin_amdgcn_ballot_w64(lane < nc && pend);
-      uint64_t rest = amask;
-#pragma unroll
-      for (int k = 0; k < kAppendMax; ++k) rest &= rest - 1;
-      if (rest) {
-        nc = __builtin_ctzll(rest);
-        amask &= (1ull << nc) - 1;
-      }
-    }
-    int id = c0 == u0 ? id_first : a.block_tables[(int64_t)s * a.max_blocks + jb + j];
-    id = lane < nc ? id : 0;
-    uint32_t meta = (uint32_t)(pend ? L - (jb + nb - 1) * kBS : kBS) | (j == 0 ? kUPairStart : 0u) |
-                    (pend ? kUPairEnd : 0u) | (u == u0 || j == 0 ? kUFirst : 0u) |
-                    (u == u1 - 1 || pend ? kULast : 0u);
+    if (c0 != u0) h = chunk_head(c0);
+    const int nc = h.nc, s = h.s, g = h.g, L = h.L;
+    const bool pend = h.j == h.nb - 1;
+    int id = lane < nc ? h.id : 0;
+    uint32_t meta = (uint32_t)(pend ? L - (first_block(L, a) + h.nb - 1) * kBS : kBS) |
+                    (h.j == 0 ? kUPairStart : 0u) | (pend ? kUPairEnd : 0u) |
+                    (c0 + lane == u0 || h.j == 0 ? kUFirst : 0u) |
+                    (c0 + lane == u1 - 1 || pend ? kULast : 0u);
     // Cache rows of this chunk's appended tokens, written after its stream
     // (the blocks' fragments take the token from LDS, so the store may come
     // later; stores issued before the ring's loads would make its first wait
     // cover their acknowledgement too).
     int n_app = 0;
     int app_blk[kAppendMax], app_tg[kAppendMax];
-    if (amask) {
-      const int64_t slot_l = ((amask >> lane) & 1) ? a.slot_mapping[s] : -1;
-      uint32_t kr[kAppendMax], vr[kAppendMax];
-      int pos[kAppendMax];
-      uint64_t mm = amask;
+    if (h.amask) {
 #pragma unroll
       for (int k = 0; k < kAppendMax; ++k) {
-        pos[k] = mm ? __builtin_ctzll(mm) : -1;
-        mm &= mm - 1;
-        kr[k] = vr[k] = 0;
-        if (pos[k] >= 0 && lane < D * EB / 4) {
-          const int sk = __builtin_amdgcn_readlane(s, pos[k]), gk = __builtin_amdgcn_readlane(g, pos[k]);
-          const int64_t row = ((int64_t)sk * Hkv + gk) * D * EB / 4;
-          kr[k] = reinterpret_cast<const uint32_t *>(a.k_new)[row + lane];
-          vr[k] = reinterpret_cast<const uint32_t *>(a.v_new)[row + lane];
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < kAppendMax; ++k) {
-        if (pos[k] < 0) break;
-        const int p = pos[k];
-        const uint32_t slo = __builtin_amdgcn_readlane((uint32_t)slot_l, p);
-        const uint32_t shi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)slot_l >> 32), p);
+        if (h.pos[k] < 0) break;
+        const int p = h.pos[k];
+        const uint32_t slo = __builtin_amdgcn_readlane((uint32_t)h.slot_l, p);
+        const uint32_t shi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)h.slot_l >> 32), p);
         const int64_t slot = (int64_t)(((uint64_t)shi << 32) | slo);
         if (slot < 0) continue;
         const int blk = __builtin_amdgcn_readlane(id, p);
@@ -1327,8 +1334,8 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
           continue;
         }
         if (lane < D * EB / 4) {
-          sm.knew[wu][k][lane] = kr[k];
-          sm.vnew[wu][k][lane] = vr[k];
+          sm.knew[wu][k][lane] = h.kr[k];
+          sm.vnew[wu][k][lane] = h.vr[k];
         }
         app_blk[n_app] = blk;
         app_tg[n_app] = (k << 24) | (t << 16) | __builtin_amdgcn_readlane(g, p);
