@@ -1272,23 +1272,34 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
   const int pair_bytes = G * D * 2;
   const int qbase = pair_of_unit(sm, wg0, Hkv, S);
   const int nq = min(pair_of_unit(sm, wg1 - 1, Hkv, S) - qbase + 1, kQLds / pair_bytes);
+  // Every q load goes out before the first LDS write: one memory latency.
+  constexpr int kQPer = kQLds / 16 / kBThreads;
+  static_assert(kQLds % (16 * kBThreads) == 0, "q staging: whole vectors per thread");
+  const int nvec = nq * pair_bytes / 16;
+  u32x4_t qv[kQPer];
   {
-    // every load goes out before the first LDS write: one memory latency
-    constexpr int kQPer = kQLds / 16 / kBThreads;
-    static_assert(kQLds % (16 * kBThreads) == 0, "q staging: whole vectors per thread");
     const u32x4_t *src = reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
                                                            (int64_t)qbase * pair_bytes);
-    const int nvec = nq * pair_bytes / 16;
-    u32x4_t qv[kQPer];
 #pragma unroll
     for (int k = 0; k < kQPer; ++k)
       if (tid + k * kBThreads < nvec) qv[k] = src[tid + k * kBThreads];
+  }
+  // A wave writes its q vectors to LDS once its first blocks are requested:
+  // the q loads are older than the ring's, so waiting for them leaves the
+  // ring in flight.  Every wave passes this barrier exactly once (an idle
+  // wave right away, any other in its first chunk); it orders LDS only.
+  auto q_to_lds = [&]() {
 #pragma unroll
     for (int k = 0; k < kQPer; ++k)
       if (tid + k * kBThreads < nvec) reinterpret_cast<u32x4_t *>(sm.q)[tid + k * kBThreads] = qv[k];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  if (u0 >= u1) {
+    q_to_lds();
+    return;
   }
-  __syncthreads();
-  if (u0 >= u1) return;
 
   W wave;
   constexpr int NB = W::kBalRing;  // blocks held in registers per wave
@@ -1363,6 +1374,7 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
       refill(fr[b], b);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (c0 == u0) q_to_lds();
     for (int i0 = 0; i0 < nc; i0 += NB) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
