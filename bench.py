@@ -264,7 +264,7 @@ def run_gpu(args, wl):
                                            shared_prefix_blocks=shared_prefix)
         ws_need = max(ws_need, pa.pa_decode_workspace_bytes(rep.params))
         rep.params.max_context_len = rep.max_ctx
-        if args.append == "fused" and spec.cache not in ("i8", "fp8"):
+        if args.append == "fused":
             rep.params.k_new = step_k_d.data_ptr()
             rep.params.v_new = step_v_d.data_ptr()
             rep.params.slot_mapping = slots_v.data_ptr()
@@ -328,7 +328,7 @@ def run_gpu(args, wl):
     pool_h = [rep.pool._h for rep in reps]
     i8 = spec.cache in ("i8", "fp8")             # byte caches: codes + row scales
     append_codes = L.pa_reshape_and_cache_fp8 if spec.cache == "fp8" else L.pa_reshape_and_cache_int8
-    fused = args.append == "fused" and not i8   # a byte cache appends with its own kernel
+    fused = args.append == "fused"              # byte caches: the new rows are quantized in the launch
     k0, v0 = step_k_d.data_ptr(), step_v_d.data_ptr()
     torch.cuda.synchronize()
 
@@ -652,6 +652,15 @@ def run_swap_bench(blocks, reps):
     print(json.dumps(rec), flush=True)
 
 
+def step_description(fused, cache, shared_prefix):
+    append = {"i8": "quantized int8 ", "fp8": "quantized fp8 "}.get(cache, "")
+    attend = "prefix attention + decode partitions" if shared_prefix else "decode partitions"
+    if fused:
+        return f"pool append + H2D slots/tables/lens + {attend} (fused {append}K/V append) + merge"
+    kern = {"i8": "reshape_and_cache_int8", "fp8": "reshape_and_cache_fp8"}.get(cache, "reshape_and_cache")
+    return f"pool append + H2D slots/tables/lens + {kern} + {attend} + merge"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -748,13 +757,7 @@ def main():
             "mean_context": round(mean_kv_tokens / spec.num_seqs, 1),
             "partition_tokens": g["part_tokens"], "replicas": args.replicas,
             "kernel": args.kernel, "seed": spec.seed,
-            "step": ("pool append + H2D slots/tables/lens + decode partitions (fused K/V append) + merge"
-                     .replace("decode partitions", "prefix attention + decode partitions" if shared_prefix
-                              else "decode partitions")
-                     if args.append == "fused" and spec.cache not in ("i8", "fp8") else
-                     f"pool append + H2D slots/tables/lens + reshape_and_cache_{'fp8' if spec.cache == 'fp8' else 'int8'}"
-                     " + decode partitions + merge" if spec.cache in ("i8", "fp8") else
-                     "pool append + H2D slots/tables/lens + reshape_and_cache + decode partitions + merge"),
+            "step": step_description(args.append == "fused", spec.cache, shared_prefix),
             "device": g["device"],
         },
         "roofline": {

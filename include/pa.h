@@ -193,22 +193,25 @@ typedef struct pa_decode_params {
   /* Optional fused append (all three set, or all NULL).  Equivalent to
    * pa_reshape_and_cache(k_new, v_new, ..., slot_mapping, num_seqs) followed
    * by the decode, for a decode step that appends one token per sequence:
-   *   k_new, v_new  [num_seqs][num_kv_heads][head_dim], kv_dtype
+   *   k_new, v_new  [num_seqs][num_kv_heads][head_dim], kv_dtype (q_dtype
+   *                 for an INT8/FP8 cache, below)
    *   slot_mapping  int64 [num_seqs]: the slot of position context_lens[s]-1,
    *                 i.e. block_tables[s][(L-1)/16]*16 + (L-1)%16, or negative
    *                 for no append.  Any other slot writes nothing and makes
    *                 that sequence's row NaN.
    * A block written this way must be private to its sequence (copy-on-write
-   * copies done beforehand with pa_copy_blocks). */
+   * copies done beforehand with pa_copy_blocks / pa_copy_blocks_int8). */
   const void *k_new;
   const void *v_new;
   const int64_t *slot_mapping;
   /* INT8 and FP8 caches (kv_dtype = PA_I8 or PA_FP8) only, else ignored: the
    * type of q (F16 or BF16; out_dtype is F32 or q_dtype) and the float32
    * scale arrays [num_blocks][num_kv_heads][16].  Decoding a byte cache needs
-   * the matrix-core kernel and automatic partitioning (the balanced split);
-   * the fused append is not available for it (append with
-   * pa_reshape_and_cache_int8 / _fp8 first). */
+   * the matrix-core kernel and automatic partitioning (the balanced split).
+   * With a byte cache the fused append's k_new / v_new rows are q_dtype
+   * (F16 or BF16) and are quantized exactly as pa_reshape_and_cache_int8 /
+   * _fp8 quantize them (codes and the scale written to the cache, the same
+   * values attended). */
   pa_dtype q_dtype;
   const float *k_scales;
   const float *v_scales;

@@ -379,6 +379,21 @@ struct MfmaWave {
     load(f, a.k_cache + tile * TILE, a.v_cache + tile * TILE, lane);
   }
 
+  // Fused append, balanced kernel: a new token's K and V rows (two 16-bit
+  // elements per lane, lanes < D/2) staged as they are, and later written to
+  // their slot.  Called by the whole wave.
+  __device__ static void stage_new(uint32_t *kdst, uint32_t *vdst, uint32_t kr, uint32_t vr, int lane) {
+    if (lane < D / 2) {
+      kdst[lane] = kr;
+      vdst[lane] = vr;
+    }
+  }
+  __device__ static void write_new(const DecodeArgs &a, int64_t blk, int t, int g, const uint32_t *knew,
+                                   const uint32_t *vnew, int lane) {
+    write_token_row<2, D>(const_cast<uint8_t *>(a.k_cache), const_cast<uint8_t *>(a.v_cache), blk, t, g,
+                          a.num_kv_heads, knew, vnew, lane);
+  }
+
   __device__ static f32x4_t mma_qk(const v8 &a, const v8 &b, f32x4_t c) {
     if constexpr (DT == PA_BF16)
       return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -555,6 +570,66 @@ __device__ void flush_parked(const DecodeArgs &a, const float *st, int64_t row0,
   }
 }
 
+// ---------------------------------------------------------------- INT8 / FP8 codes
+// One wave per (token, KV head) row: max |x| over the row by a wave
+// reduction, scale = max / 127 (int8) or max / 448 (E4M3), codes from
+// x / scale (float32, correctly rounded division): truncated toward zero
+// (int8) or rounded to the nearest E4M3 value, ties to even, saturating at
+// +-448 (e4m3_code); codes scattered into the byte tile layout, the scale
+// stored beside it.
+
+// Nearest E4M3 code of x: below 2^-6 the step is 2^-9 (subnormals, and 2^-6
+// itself as code 8); above, 3 mantissa bits under the exponent of x.
+__device__ inline uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return 0x7Fu;
+  if (a >= 448.f) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.f);
+  int e;
+  (void)frexpf(a, &e);                       // a in [2^(e-1), 2^e)
+  const int E = e - 1;                       // -6 .. 8
+  int q = (int)rintf((ldexpf(a, -E) - 1.f) * 8.f);  // 0 .. 8, ties to even
+  int ef = E + 7;
+  if (q == 8) {
+    q = 0;
+    ++ef;
+  }
+  return sign | min((uint32_t)((ef << 3) | q), 0x7Eu);
+}
+
+// A 16-bit row element (SDT = PA_BF16 or PA_F16 bits) as float32.
+template <int SDT>
+__device__ inline float half_value(uint32_t bits) {
+  return SDT == PA_BF16 ? __uint_as_float(bits << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+template <int FMT>
+__device__ inline float code_scale(float amax) {
+  return amax / (FMT == PA_FP8 ? 448.0f : 127.0f);
+}
+
+template <int FMT>
+__device__ inline int code_of(float v, float scale) {
+  const float qv = scale == 0.f ? 0.f : v / scale;
+  if constexpr (FMT == PA_FP8)
+    return scale == 0.f ? 0 : (int)e4m3_code(qv);
+  else
+    return qv == qv ? (int)qv : 0;  // conversion truncates toward zero
+}
+
+// Byte offsets of (token t, dim d) in a code tile: K as 16-byte vectors
+// (dim block c = d / 64, lane ((d % 32) / 8) * 16 + t; dims 8q .. 8q+7 of the
+// block, then 32 + 8q .. 32 + 8q + 7), V as 4 tokens x 4 dim quarters per
+// vector (lane (t / 4) * 16 + d % 16, byte ((d % 64) / 16) * 4 + t % 4).
+__device__ inline int k_code_off(int d, int t) {
+  const int c = d / 64, w = d % 64;
+  return (c * 64 + ((w % 32) / 8) * 16 + t) * 16 + (w / 32) * 8 + w % 8;
+}
+__device__ inline int v_code_off(int d, int t) {
+  return ((d / 64) * 64 + (t / 4) * 16 + d % 16) * 16 + ((d % 64) / 16) * 4 + t % 4;
+}
+
 // ============================================================================
 // MFMA wave over an INT8 cache (q in QDT = fp16 / bf16).
 //
@@ -583,7 +658,7 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D> {
   using Base::NT;
   static constexpr int NV = D / 64;        // 16-byte code vectors per lane and tile
   static constexpr int TILE = kBS * D;     // code bytes per (block, head) tile
-  static constexpr bool kAppend = false;   // append with pa_reshape_and_cache_int8 first
+  static constexpr bool kAppend = true;    // new rows (QDT) quantized as pa_reshape_and_cache_int8 / _fp8 do
   // The code conversions add ~250 VALU instructions per block: more waves per
   // SIMD hide their latency, a shallower ring keeps them in registers.
   static constexpr int kBalRing = FMT == PA_FP8 ? PA_FP8_RING : PA_I8_RING;
@@ -674,9 +749,81 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D> {
     }
   }
 
-  __device__ void compute(Frag &f, uint32_t vm, float scale_log2, int lane, int /*new_tok*/,
-                          const uint32_t *, const uint32_t *) {
+  // Fused append: a new row (QDT bits, two elements per lane, lanes < D/2)
+  // quantized as the append kernel does (the same scale and the same code per
+  // element), staged as D code bytes in dim order with the scale after them.
+  // Called by the whole wave (the row maximum is a wave reduction).
+  __device__ static void stage_row(uint32_t *dst, uint32_t bits, int lane) {
+    const bool mine = lane < D / 2;
+    const float x0 = mine ? half_value<QDT>(bits & 0xFFFFu) : 0.f;
+    const float x1 = mine ? half_value<QDT>(bits >> 16) : 0.f;
+    float amax = fmaxf(fmaxf(0.f, fabsf(x0)), fabsf(x1));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float scale = code_scale<FMT>(amax);
+    if (mine)
+      reinterpret_cast<uint16_t *>(dst)[lane] =
+          (uint16_t)((code_of<FMT>(x0, scale) & 0xFF) | ((code_of<FMT>(x1, scale) & 0xFF) << 8));
+    if (lane == 0) reinterpret_cast<float *>(dst)[D / 4] = scale;
+  }
+  __device__ static void stage_new(uint32_t *kdst, uint32_t *vdst, uint32_t kr, uint32_t vr, int lane) {
+    stage_row(kdst, kr, lane);
+    stage_row(vdst, vr, lane);
+  }
+  // Codes and scales of a staged token into its slot (tile layouts as in
+  // pa_reshape_and_cache_int8).
+  __device__ static void write_new(const DecodeArgs &a, int64_t blk, int t, int g, const uint32_t *knew,
+                                   const uint32_t *vnew, int lane) {
+    const int64_t tile = blk * a.num_kv_heads + g;
+    uint8_t *kc = const_cast<uint8_t *>(a.k_cache) + tile * TILE;
+    uint8_t *vc = const_cast<uint8_t *>(a.v_cache) + tile * TILE;
+    const uint8_t *kb = reinterpret_cast<const uint8_t *>(knew), *vb = reinterpret_cast<const uint8_t *>(vnew);
+    for (int d = lane; d < D; d += 64) {
+      kc[k_code_off(d, t)] = kb[d];
+      vc[v_code_off(d, t)] = vb[d];
+    }
+    if (lane == 0) {
+      const_cast<float *>(a.k_scales)[tile * kBS + t] = reinterpret_cast<const float *>(knew)[D / 4];
+      const_cast<float *>(a.v_scales)[tile * kBS + t] = reinterpret_cast<const float *>(vnew)[D / 4];
+    }
+  }
+  // Replaces token t's codes and scales in a tile's fragments with the staged
+  // row (register indices all compile-time constants).
+  __device__ static void patch_new(Frag &f, int t, int lane, const uint32_t *knew, const uint32_t *vnew) {
+    const int r = lane % 16, tq = lane / 16;
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {  // K vector x of lane (tq, t): dims 64x + 8tq .., 64x + 32 + 8tq ..
+      const uint32_t *lo = knew + (64 * x + 8 * tq) / 4;
+      const uint32_t *hi = knew + (64 * x + 32 + 8 * tq) / 4;
+      const u32x4_t kx = {lo[0], lo[1], hi[0], hi[1]};
+      f.k[x] = r == t ? kx : f.k[x];
+    }
+    const bool in_quad = tq == t / 4;
+    const int sh = 8 * (t % 4);
+    const uint32_t keep = ~(0xFFu << sh);
+    const uint8_t *vb = reinterpret_cast<const uint8_t *>(vnew);
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // byte 4j + i = (token 4tq + i, dim 64x + 16j + r)
+        const uint32_t c = vb[64 * x + 16 * j + r];
+        f.v[x][j] = in_quad ? ((f.v[x][j] & keep) | (c << sh)) : f.v[x][j];
+      }
+    }
+    const float ksc = reinterpret_cast<const float *>(knew)[D / 4];
+    const float vsc = reinterpret_cast<const float *>(vnew)[D / 4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool hit = in_quad && i == t % 4;
+      f.ks[i] = hit ? ksc : f.ks[i];
+      f.vs[i] = hit ? vsc : f.vs[i];
+    }
+  }
+
+  __device__ void compute(Frag &f, uint32_t vm, float scale_log2, int lane, int new_tok,
+                          const uint32_t *knew, const uint32_t *vnew) {
     const int tq = lane / 16;
+    if (new_tok >= 0) patch_new(f, new_tok, lane, knew, vnew);
     const uint32_t mine = vm >> (4 * tq);
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1344,10 +1491,7 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
           if (lane == p) meta |= kUBad;
           continue;
         }
-        if (lane < D * EB / 4) {
-          sm.knew[wu][k][lane] = h.kr[k];
-          sm.vnew[wu][k][lane] = h.vr[k];
-        }
+        W::stage_new(sm.knew[wu][k], sm.vnew[wu][k], h.kr[k], h.vr[k], lane);
         app_blk[n_app] = blk;
         app_tg[n_app] = (k << 24) | (t << 16) | __builtin_amdgcn_readlane(g, p);
         ++n_app;
@@ -1433,8 +1577,7 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
     for (int x = 0; x < kAppendMax; ++x) {
       if (x < n_app) {
         const int k = app_tg[x] >> 24, t = (app_tg[x] >> 16) & 0xFF, gx = app_tg[x] & 0xFFFF;
-        write_token_row<EB, D>(const_cast<uint8_t *>(a.k_cache), const_cast<uint8_t *>(a.v_cache), app_blk[x],
-                               t, gx, Hkv, sm.knew[wu][k], sm.vnew[wu][k], lane);
+        W::write_new(a, app_blk[x], t, gx, sm.knew[wu][k], sm.vnew[wu][k], lane);
       }
     }
     c0 += nc;
@@ -2106,33 +2249,7 @@ __global__ __launch_bounds__(256) void pa_reshape_and_cache_kernel(
 }
 
 // ---------------------------------------------------------------- INT8 / FP8 append
-// One wave per (token, KV head) row: max |x| over the row by a wave
-// reduction, scale = max / 127 (int8) or max / 448 (E4M3), codes from
-// x / scale (float32, correctly rounded division): truncated toward zero
-// (int8) or rounded to the nearest E4M3 value, ties to even, saturating at
-// +-448 (e4m3_code); codes scattered into the byte tile layout, the scale
-// stored beside it.
-
-// Nearest E4M3 code of x: below 2^-6 the step is 2^-9 (subnormals, and 2^-6
-// itself as code 8); above, 3 mantissa bits under the exponent of x.
-__device__ inline uint32_t e4m3_code(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fabsf(x);
-  if (a != a) return 0x7Fu;
-  if (a >= 448.f) return sign | 0x7Eu;
-  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.f);
-  int e;
-  (void)frexpf(a, &e);                       // a in [2^(e-1), 2^e)
-  const int E = e - 1;                       // -6 .. 8
-  int q = (int)rintf((ldexpf(a, -E) - 1.f) * 8.f);  // 0 .. 8, ties to even
-  int ef = E + 7;
-  if (q == 8) {
-    q = 0;
-    ++ef;
-  }
-  return sign | min((uint32_t)((ef << 3) | q), 0x7Eu);
-}
-
+// (quantizer helpers: with the byte-code wave policy above)
 template <int SDT, int D, int FMT>
 __device__ void quantize_row_i8(const uint16_t *x, int8_t *tile_codes, float *scale_out, int t, bool is_v,
                                 int lane) {
@@ -2141,30 +2258,16 @@ __device__ void quantize_row_i8(const uint16_t *x, int8_t *tile_codes, float *sc
   float amax = 0.f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const uint32_t bits = x[lane * PER + e];
-    v[e] = SDT == PA_BF16 ? __uint_as_float(bits << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+    v[e] = half_value<SDT>(x[lane * PER + e]);
     amax = fmaxf(amax, fabsf(v[e]));
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-  const float scale = amax / (FMT == PA_FP8 ? 448.0f : 127.0f);
+  const float scale = code_scale<FMT>(amax);
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int d = lane * PER + e;
-    const float qv = scale == 0.f ? 0.f : v[e] / scale;
-    int code;
-    if constexpr (FMT == PA_FP8)
-      code = scale == 0.f ? 0 : (int)e4m3_code(qv);
-    else
-      code = qv == qv ? (int)qv : 0;  // conversion truncates toward zero
-    int off;
-    if (!is_v) {
-      const int c = d / 64, w = d % 64;
-      off = (c * 64 + ((w % 32) / 8) * 16 + t) * 16 + (w / 32) * 8 + w % 8;
-    } else {
-      off = ((d / 64) * 64 + (t / 4) * 16 + d % 16) * 16 + ((d % 64) / 16) * 4 + t % 4;
-    }
-    tile_codes[off] = (int8_t)code;
+    tile_codes[is_v ? v_code_off(d, t) : k_code_off(d, t)] = (int8_t)code_of<FMT>(v[e], scale);
   }
   if (lane == 0) *scale_out = scale;
 }
@@ -2287,10 +2390,10 @@ pa_status validate(const pa_decode_params *p) {
       return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype must be F32 or q_dtype");
     if (!p->k_scales || !p->v_scales || !aligned16(p->k_scales) || !aligned16(p->v_scales))
       return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: an INT8/FP8 cache needs 16-byte aligned scale arrays");
-    if (p->kernel == PA_KERNEL_VALU || p->partition_tokens > 0 || p->k_new != nullptr)
+    if (p->kernel == PA_KERNEL_VALU || p->partition_tokens > 0)
       return pa::fail(PA_ERR_UNSUPPORTED,
                       "pa_decode: an INT8/FP8 cache is decoded by the matrix-core kernel with automatic "
-                      "partitioning and no fused append");
+                      "partitioning");
   } else if (p->out_dtype != PA_F32 && p->out_dtype != p->kv_dtype) {
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype must be F32 or the cache type");
   }

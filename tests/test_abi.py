@@ -211,13 +211,22 @@ def test_int8_cache_takes_the_balanced_split():
     (dict(partition_tokens=256), pa.PA_ERR_UNSUPPORTED),
     (dict(kernel=pa.PA_KERNEL_VALU), pa.PA_ERR_UNSUPPORTED),
     (dict(num_seqs=1025), pa.PA_ERR_UNSUPPORTED),
-    (dict(k_new=ctypes.c_void_p(16), v_new=ctypes.c_void_p(16), slot_mapping=ctypes.c_void_p(16)),
-     pa.PA_ERR_UNSUPPORTED),
+    (dict(k_new=ctypes.c_void_p(16)), pa.PA_ERR_INVALID_ARG),
+    (dict(k_new=ctypes.c_void_p(16), v_new=ctypes.c_void_p(16), slot_mapping=ctypes.c_void_p(16),
+          partition_tokens=256), pa.PA_ERR_UNSUPPORTED),
 ])
 def test_int8_decode_rejects_unsupported_requests(over, status):
     p = _i8(**over)
     assert pa.lib().pa_decode(ctypes.byref(p), None, 0, None) == status
     assert pa.pa_decode_workspace_bytes(p) == 0
+
+
+def test_byte_caches_take_the_fused_append_on_the_balanced_split():
+    for kv in (pa.PA_I8, pa.PA_FP8):
+        p = _i8(kv_dtype=kv, k_new=ctypes.c_void_p(16), v_new=ctypes.c_void_p(16),
+                slot_mapping=ctypes.c_void_p(16))
+        assert pa.pa_decode_partition_tokens(p) == 0
+        assert pa.pa_decode_workspace_bytes(p) > 0
 
 
 def test_int8_append_and_copy_reject_bad_arguments():

@@ -130,3 +130,88 @@ def test_int8_split_launches_equal_pa_decode_bitwise_and_bad_ids_give_nan():
                  spec.fp32_scale(), k_scales=gst.k_scales, v_scales=gst.v_scales)
     b = bad.cpu().numpy()
     assert np.all(np.isnan(b[1])) and np.array_equal(b[0], whole.cpu().numpy()[0])
+
+
+# ------------------------------------------------------------------ fused append
+@pytest.mark.parametrize("cache,dtype,D", [("i8", "bf16", 128), ("i8", "f16", 64), ("fp8", "bf16", 128),
+                                           ("fp8", "f16", 64)])
+def test_byte_cache_fused_append_equals_append_then_decode(cache, dtype, D):
+    """pa_decode with k_new / v_new on an INT8 or E4M3 cache: every step's rows
+    against the oracle (which appends with its own quantizer first), and after
+    the steps the codes and scales bit for bit against the oracle's caches.  A
+    child of sequence 0 shares its partly filled last block, so the first
+    step's append into sequence 0 needs a copy-on-write first."""
+    spec = workloads.custom(seed=147, dtype=dtype, lens=(5, 40, 16, 300, 33), num_q_heads=8,
+                            num_kv_heads=2, head_dim=D, prefix_len=20, decode_steps=18, cache=cache)
+    wl = workloads.generate(spec)
+    _say(f"[case] fused append cache={cache} q={dtype} D={D} steps={spec.decode_steps}")
+    gst, ost = gpu_side.build(wl), oracle_side.build(wl)
+    assert gst.pool.seq_fork(gst.seq_ids[0]) == ost.pool.seq_fork(ost.seq_ids[0])
+    mb = oracle_side.max_blocks_for(wl)
+    q = gpu_side.to_device(wl.q, dtype)
+    saw_cow = False
+    for step in range(spec.decode_steps):
+        slots, cows = gst.pool.seq_append_batch(gst.seq_ids)
+        if len(cows):
+            saw_cow = True
+            pa.pa_copy_blocks_int8(gst.k_cache, gst.v_cache, gst.k_scales, gst.v_scales,
+                                   torch.from_numpy(cows.copy()).cuda(), spec.num_kv_heads, D)
+        oracle_side.advance(wl, ost, step)
+        assert slots.tolist() == ost.step_slots[-1]
+        tab_d, lens_d, _, lh = gpu_side.tables(gst, mb)
+        out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        pa.pa_decode(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, spec.num_kv_heads, int(lh.max()),
+                     spec.fp32_scale(), k_scales=gst.k_scales, v_scales=gst.v_scales,
+                     k_new=gpu_side.to_device(wl.step_k[step], dtype),
+                     v_new=gpu_side.to_device(wl.step_v[step], dtype),
+                     slot_mapping=torch.from_numpy(slots.copy()).cuda())
+        ref = oracle_side.decode(wl, ost, mb)
+        err = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref)))
+        _say(f"  step {step} max_abs_err={err:.3e}")
+        assert err <= TOL, (step, err)
+    assert saw_cow
+    torch.cuda.synchronize()
+    for g, o in ((gst.k_cache, ost.k_cache), (gst.v_cache, ost.v_cache)):
+        assert np.array_equal(g.cpu().numpy().view(np.uint8), o.view(np.uint8))
+    for g, o in ((gst.k_scales, ost.k_scales), (gst.v_scales, ost.v_scales)):
+        assert np.array_equal(_bits(g), o.view(np.uint32))
+
+
+def test_byte_cache_fused_append_rejects_a_foreign_slot_and_many_pair_ends_per_chunk():
+    """One-block contexts put more appended tokens in a wave's share than one
+    chunk stages; a slot that is not the sequence's own makes its row NaN and
+    writes nothing."""
+    lens = tuple(int(x) for x in np.random.default_rng(149).integers(1, 15, 600))
+    spec = workloads.custom(seed=149, dtype="bf16", lens=lens, num_q_heads=16, num_kv_heads=8,
+                            head_dim=128, cache="i8", decode_steps=1)
+    wl = workloads.generate(spec)
+    _say(f"[case] fused append i8 S={len(lens)} one-block contexts, foreign slot")
+    gst, ost = gpu_side.build(wl), oracle_side.build(wl)
+    slots, cows = gst.pool.seq_append_batch(gst.seq_ids)
+    assert len(cows) == 0
+    oracle_side.advance(wl, ost, 0)
+    mb = oracle_side.max_blocks_for(wl)
+    tab_d, lens_d, _, lh = gpu_side.tables(gst, mb)
+    bad = slots.copy()
+    bad[7] = bad[6]                      # sequence 7 pointed at sequence 6's slot
+    q = gpu_side.to_device(wl.q, "bf16")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    pa.pa_decode(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, spec.num_kv_heads, int(lh.max()),
+                 spec.fp32_scale(), k_scales=gst.k_scales, v_scales=gst.v_scales,
+                 k_new=gpu_side.to_device(wl.step_k[0], "bf16"), v_new=gpu_side.to_device(wl.step_v[0], "bf16"),
+                 slot_mapping=torch.from_numpy(bad).cuda())
+    got = out.cpu().numpy().astype(np.float64)
+    ref = oracle_side.decode(wl, ost, mb)
+    ok = np.ones(len(lens), bool)
+    ok[7] = False
+    assert np.all(np.isnan(got[7]))
+    assert float(np.max(np.abs(got[ok] - ref[ok]))) <= TOL
+    torch.cuda.synchronize()
+    # the oracle wrote sequence 7's own token; the kernel did not: only that
+    # token's codes (K and V, every head) differ, and its scales
+    kd = np.nonzero(_bits(gst.k_cache) != ost.k_cache.view(np.uint8))[0]
+    s7 = int(slots[7])
+    blk, t = s7 // 16, s7 % 16
+    assert all((i // (16 * 128)) // 8 == blk for i in kd)
+    ks = np.nonzero(_bits(gst.k_scales) != ost.k_scales.view(np.uint32))[0]
+    assert set(int(i) for i in ks) <= {(blk * 8 + g) * 16 + t for g in range(8)}
