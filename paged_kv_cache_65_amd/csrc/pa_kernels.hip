@@ -752,23 +752,26 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D> {
   // Fused append: a new row (QDT bits, two elements per lane, lanes < D/2)
   // quantized as the append kernel does (the same scale and the same code per
   // element), staged as D code bytes in dim order with the scale after them.
-  // Called by the whole wave (the row maximum is a wave reduction).
-  __device__ static void stage_row(uint32_t *dst, uint32_t bits, int lane) {
-    const bool mine = lane < D / 2;
-    const float x0 = mine ? half_value<QDT>(bits & 0xFFFFu) : 0.f;
-    const float x1 = mine ? half_value<QDT>(bits >> 16) : 0.f;
-    float amax = fmaxf(fmaxf(0.f, fabsf(x0)), fabsf(x1));
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-    const float scale = code_scale<FMT>(amax);
-    if (mine)
+  // Called by the whole wave; the K and V row maxima are reduced together
+  // (DPP and lane swaps; a maximum does not depend on the order).
+  __device__ static void stage_row(uint32_t *dst, float x0, float x1, float scale, int lane) {
+    if (lane < D / 2)
       reinterpret_cast<uint16_t *>(dst)[lane] =
           (uint16_t)((code_of<FMT>(x0, scale) & 0xFF) | ((code_of<FMT>(x1, scale) & 0xFF) << 8));
     if (lane == 0) reinterpret_cast<float *>(dst)[D / 4] = scale;
   }
   __device__ static void stage_new(uint32_t *kdst, uint32_t *vdst, uint32_t kr, uint32_t vr, int lane) {
-    stage_row(kdst, kr, lane);
-    stage_row(vdst, vr, lane);
+    const bool mine = lane < D / 2;
+    const float k0 = mine ? half_value<QDT>(kr & 0xFFFFu) : 0.f, k1 = mine ? half_value<QDT>(kr >> 16) : 0.f;
+    const float v0 = mine ? half_value<QDT>(vr & 0xFFFFu) : 0.f, v1 = mine ? half_value<QDT>(vr >> 16) : 0.f;
+    float km = fmaxf(fmaxf(0.f, fabsf(k0)), fabsf(k1));
+    float vm = fmaxf(fmaxf(0.f, fabsf(v0)), fabsf(v1));
+    km = row_max16(km);
+    vm = row_max16(vm);
+    km = max_xor32(max_xor16(km));
+    vm = max_xor32(max_xor16(vm));
+    stage_row(kdst, k0, k1, code_scale<FMT>(km), lane);
+    stage_row(vdst, v0, v1, code_scale<FMT>(vm), lane);
   }
   // Codes and scales of a staged token into its slot (tile layouts as in
   // pa_reshape_and_cache_int8).
