@@ -93,3 +93,69 @@ def test_random_configuration_matches_oracle(case):
     assert err <= TOL, err
     empty = np.asarray(wl.prompt_lens) + c["prefix"] == 0
     assert np.all(got[empty] == 0)
+
+
+# ------------------------------------------------------------------ fused append
+NAPPEND = 24
+
+
+def _draw_append(case):
+    """A shape, length mix and cache type as above; the batch then takes two
+    decode steps with the append fused into pa_decode."""
+    c = _draw(7400 + case)
+    rng = np.random.default_rng(7600 + case)
+    c["cache"] = str(rng.choice(["", "i8", "fp8"]))
+    if c["cache"]:
+        c["prefix"] = 0
+        c["pt"] = int(rng.choice([0, pa.PA_PARTITION_BALANCED]))
+    return c
+
+
+@pytest.mark.parametrize("case", range(NAPPEND))
+def test_random_fused_append_steps_match_oracle(case):
+    from tests.test_gpu_parity import _assert_caches_equal
+    c = _draw_append(case)
+    _say(f"[case] random append {case}: D={c['D']} G={c['G']} Hkv={c['Hkv']} S={len(c['lens'])} "
+         f"cache={c['cache'] or c['dtype']} q={c['dtype']} window={c['window']} prefix={c['prefix']} "
+         f"pt={c['pt']} max_len={max(c['lens'])}")
+    spec = workloads.custom(seed=7700 + case, dtype=c["dtype"], lens=c["lens"], num_q_heads=c["G"] * c["Hkv"],
+                            num_kv_heads=c["Hkv"], head_dim=c["D"], prefix_len=c["prefix"], cache=c["cache"],
+                            decode_steps=2)
+    wl = workloads.generate(spec)
+    gst, ost = gpu_side.build(wl), oracle_side.build(wl)
+    byte = c["cache"] != ""
+    mb = oracle_side.max_blocks_for(wl)
+    q = gpu_side.to_device(wl.q, spec.dtype)
+    for step in range(spec.decode_steps):
+        slots, cows = gst.pool.seq_append_batch(gst.seq_ids)
+        if len(cows):
+            pairs = torch.from_numpy(cows.copy()).cuda()
+            if byte:
+                pa.pa_copy_blocks_int8(gst.k_cache, gst.v_cache, gst.k_scales, gst.v_scales, pairs,
+                                       spec.num_kv_heads, spec.head_dim)
+            else:
+                pa.pa_copy_blocks(gst.k_cache, gst.v_cache, pairs, spec.num_kv_heads, spec.head_dim)
+        oracle_side.advance(wl, ost, step)
+        assert slots.tolist() == ost.step_slots[-1]
+        tab_d, lens_d, _, lh = gpu_side.tables(gst, mb)
+        out = torch.full(q.shape, -9.0, dtype=torch.float32, device="cuda")
+        pa.pa_decode(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, spec.num_kv_heads, int(lh.max()),
+                     spec.fp32_scale(), partition_tokens=c["pt"], k_scales=gst.k_scales, v_scales=gst.v_scales,
+                     sliding_window=c["window"], shared_prefix_blocks=c["prefix"] // 16,
+                     k_new=gpu_side.to_device(wl.step_k[step], spec.dtype),
+                     v_new=gpu_side.to_device(wl.step_v[step], spec.dtype),
+                     slot_mapping=torch.from_numpy(slots.copy()).cuda())
+        ref = oracle_side.decode(wl, ost, mb, window=c["window"])
+        got = out.cpu().numpy().astype(np.float64)
+        err = float(np.max(np.abs(got - ref)))
+        _say(f"  step {step} max_abs_err={err:.3e}")
+        assert np.all(np.isfinite(got))
+        assert err <= TOL, (step, err)
+    torch.cuda.synchronize()
+    if byte:
+        for g, o in ((gst.k_cache, ost.k_cache), (gst.v_cache, ost.v_cache)):
+            assert np.array_equal(g.cpu().numpy().view(np.uint8), o.view(np.uint8))
+        for g, o in ((gst.k_scales, ost.k_scales), (gst.v_scales, ost.v_scales)):
+            assert np.array_equal(g.cpu().numpy().view(np.uint32), o.view(np.uint32))
+    else:
+        _assert_caches_equal(gst, ost, spec.dtype)
