@@ -46,3 +46,12 @@ def test_a_record_of_other_kernel_source_is_not_reported(tmp_path, monkeypatch):
         monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
         got = bench.read_traffic(KERNEL, WORKLOAD)
         assert (got is None) == expect_none, (tag, got)
+
+
+def test_step_description_names_the_append_each_cache_takes():
+    assert bench.step_description(True, "", 0).endswith("decode partitions (fused K/V append) + merge")
+    assert "fused quantized int8 K/V append" in bench.step_description(True, "i8", 0)
+    assert "fused quantized fp8 K/V append" in bench.step_description(True, "fp8", 0)
+    assert "prefix attention + decode partitions" in bench.step_description(True, "", 32)
+    assert "reshape_and_cache_fp8 + decode partitions" in bench.step_description(False, "fp8", 0)
+    assert "reshape_and_cache + decode partitions" in bench.step_description(False, "", 0)
