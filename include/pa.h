@@ -45,10 +45,10 @@
  *
  * INT8 caches.  Row (token t, KV head g) of K (and of V) is stored as
  * head_dim int8 codes c and one float32 scale sc, standing for the values
- * c * sc.  Quantization ("LLM Inference Optimization: KV-Cache,
- * PagedAttention, and GPU Memory Efficiency", section "Future
- * Optimizations"): sc = max_d |x_d| / 127 and c_d = x_d / sc truncated
- * toward zero, both in float32 (an all-zero row has sc = 0, codes 0).  Code
+ * c * sc.  Quantization ("KV Cache Explained Like You're an LLM Engineer",
+ * section "Future Optimizations", subsection "KV Cache Quantization"):
+ * sc = max_d |x_d| / 127 and c_d = x_d / sc truncated toward zero, both in
+ * float32 (an all-zero row has sc = 0, codes 0).  Code
  * tiles are 16*head_dim bytes at byte (b*num_kv_heads + g)*16*head_dim:
  *   K: (t, d) -> (c*64 + q*16 + t)*16 + h*8 + e,  with c = d/64, w = d%64,
  *               h = w/32, q = (w%32)/8, e = w%8
@@ -227,9 +227,9 @@ typedef struct pa_decode_params {
    * the call's work.  The events are not read back by the library. */
   void *start_event;
   void *stop_event;
-  /* Sliding window ("LLM Inference Optimization: KV-Cache, PagedAttention,
-   * and GPU Memory Efficiency", Future Optimizations: token i attends to
-   * [i-W, i]).  0 = none.  W > 0: the query of sequence s, at position
+  /* Sliding window ("KV Cache Explained Like You're an LLM Engineer", section
+   * "Future Optimizations", subsection "Sliding Window Attention": token i
+   * attends to [i-W, i]).  0 = none.  W > 0: the query of sequence s, at position
    * L-1, attends to positions max(0, L-1-W) .. L-1 (W+1 tokens, both ends
    * included).  Table entries of blocks wholly before position L-1-W are
    * never read (they may be -1 or stale); negative values are rejected. */

@@ -213,9 +213,9 @@ static double value_at(const orc_src *s, int i, int d) {
 /* First position a decode query attends to.  The query is the newest token,
  * position i = L-1.  Without a window (window <= 0) it sees every position;
  * with a sliding window W it sees positions i-W .. i (clipped at 0): the
- * interval "[i-W, i]" of "LLM Inference Optimization: KV-Cache,
- * PagedAttention, and GPU Memory Efficiency", section "Future Optimizations"
- * (sliding window attention), read with both ends included. */
+ * interval "[i-W, i]" of "KV Cache Explained Like You're an LLM Engineer",
+ * section "Future Optimizations" (subsection "Sliding Window Attention"),
+ * read with both ends included. */
 static int first_attended(int L, int window) {
   if (window <= 0 || L - 1 - window <= 0) return 0;
   return L - 1 - window;
@@ -384,10 +384,10 @@ void oracle_bruteforce_contiguous(double *out, const void *q, const void *k_seq,
 /* ===========================================================================
  * INT8 KV cache with one scale per (token, KV head) row.
  *
- * Quantization follows "LLM Inference Optimization: KV-Cache, PagedAttention,
- * and GPU Memory Efficiency", section "Future Optimizations" (KV cache
- * quantization): scale = max |x| over the row's last dimension / 127,
- * code = (x / scale) converted to int8, dequantized value = code * scale.
+ * Quantization follows "KV Cache Explained Like You're an LLM Engineer",
+ * section "Future Optimizations" (subsection "KV Cache Quantization"):
+ * scale = max |x| over the row's last dimension / 127, code = (x / scale)
+ * converted to int8, dequantized value = code * scale.
  * Readings: the arithmetic is float32 (the row's 16-bit values are widened
  * exactly; the division is IEEE single precision, correctly rounded); the
  * conversion to int8 truncates toward zero, as a float-to-integer cast does;

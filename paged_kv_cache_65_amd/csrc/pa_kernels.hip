@@ -181,10 +181,11 @@ __device__ inline bool ctx_valid(int L, const DecodeArgs &a) {
   return L >= 0 && L <= a.max_ctx && (int64_t)L <= (int64_t)a.max_blocks * kBS;
 }
 
-// Sliding window ("LLM Inference Optimization: KV-Cache, PagedAttention, and
-// GPU Memory Efficiency", Future Optimizations): the query at position L-1
-// sees positions L-1-W .. L-1 (clipped at 0); W <= 0: no window.  Blocks
-// before the one holding the first such position are never touched.
+// Sliding window ("KV Cache Explained Like You're an LLM Engineer", section
+// "Future Optimizations", subsection "Sliding Window Attention"): the query
+// at position L-1 sees positions L-1-W .. L-1 (clipped at 0); W <= 0: no
+// window.  Blocks before the one holding the first such position are never
+// touched.
 __device__ inline int window_first_token(int L, int W) { return (W > 0 && L - 1 - W > 0) ? L - 1 - W : 0; }
 
 constexpr uint32_t kAllTokens = 0xFFFFu;

@@ -1,8 +1,8 @@
 """Pins for the oracle's INT8 cache (no GPU).
 
 Quantization is checked against values worked by hand from the definition
-("LLM Inference Optimization: KV-Cache, PagedAttention, and GPU Memory
-Efficiency", section "Future Optimizations": scale = max|x| / 127, code = the
+("KV Cache Explained Like You're an LLM Engineer", section "Future
+Optimizations", subsection "KV Cache Quantization": scale = max|x| / 127, code = the
 quotient converted to int8, value = code * scale); the paged append + decode
 chain is checked against numpy float64 attention over rows quantized one at a
 time, which never touches the tile layout.

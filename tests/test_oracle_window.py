@@ -1,7 +1,7 @@
 """Pins for the oracle's sliding-window decode (no GPU).
 
-Reading ("LLM Inference Optimization: KV-Cache, PagedAttention, and GPU Memory
-Efficiency", section "Future Optimizations", sliding window attention): the
+Reading ("KV Cache Explained Like You're an LLM Engineer", section "Future
+Optimizations", subsection "Sliding Window Attention"): the
 decode query is the newest token, position i = L-1, and with window W it
 attends to the interval [i-W, i] with both ends included (W+1 positions,
 clipped at 0).  W = 0 means no window.
