@@ -79,6 +79,8 @@ extern "C" {
 #define PA_BLOCK_SIZE 16
 /* pa_decode_params.partition_tokens value that asks for the balanced split */
 #define PA_PARTITION_BALANCED (-1)
+/* Size of the per-device workspace pa_decode_noalloc uses (64 MiB) */
+#define PA_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -283,6 +285,21 @@ pa_status pa_decode_partitions(const pa_decode_params *p, void *workspace,
                                size_t workspace_bytes, void *stream);
 pa_status pa_decode_merge(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/* pa_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a fixed array inside the library
+ * of PA_NOALLOC_WORKSPACE_BYTES bytes (64 MiB), one copy per
+ * device, held from the first call on a device until the process ends; the
+ * call itself allocates nothing.  A call whose pa_decode_workspace_bytes()
+ * exceeds that size returns PA_ERR_WORKSPACE and launches nothing.  Every
+ * call on one device shares that device's array: calls that overlap on the
+ * device (on different streams, or from several host threads without stream
+ * order between them) race on it and give undefined results.  The output is
+ * the same, bit for bit, as pa_decode's for the same parameters.  The first
+ * call on a device looks up the array's address there (that device must be
+ * current); other errors as pa_decode. */
+pa_status pa_decode_noalloc(const pa_decode_params *p, void *stream);
 
 /* ------------------------------------------------------------------------
  * KV append through a slot mapping.

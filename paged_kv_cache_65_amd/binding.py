@@ -21,6 +21,7 @@ PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
 PA_PARTITION_BALANCED = -1      # partition_tokens value: the balanced split
 KERNELS = {"auto": PA_KERNEL_AUTO, "valu": PA_KERNEL_VALU, "mfma": PA_KERNEL_MFMA}
 BLOCK_SIZE = 16
+PA_NOALLOC_WORKSPACE_BYTES = 64 << 20   # the per-device workspace of pa_decode_noalloc
 
 _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _PI32 = ctypes.POINTER(ctypes.c_int32)
@@ -78,6 +79,7 @@ def lib():
             "pa_decode": (ctypes.c_int, [ctypes.POINTER(pa_decode_params), _P, _SZ, _P]),
             "pa_decode_partitions": (ctypes.c_int, [ctypes.POINTER(pa_decode_params), _P, _SZ, _P]),
             "pa_decode_merge": (ctypes.c_int, [ctypes.POINTER(pa_decode_params), _P, _SZ, _P]),
+            "pa_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(pa_decode_params), _P]),
             "pa_extend_partition_tokens": (_I32, [ctypes.POINTER(pa_extend_params)]),
             "pa_extend_workspace_bytes": (_SZ, [ctypes.POINTER(pa_extend_params)]),
             "pa_extend": (ctypes.c_int, [ctypes.POINTER(pa_extend_params), _P, _SZ, _P]),
@@ -224,6 +226,19 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads
     ws_ptr = _dev(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().pa_decode(ctypes.byref(params), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
+                      max_context_len, scale, partition_tokens=0, kernel="auto", stream=None,
+                      k_new=None, v_new=None, slot_mapping=None, k_scales=None, v_scales=None,
+                      sliding_window=0, shared_prefix_blocks=0):
+    """pa_decode with the library's own per-device workspace: allocates nothing."""
+    params = make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens,
+                                num_kv_heads, max_context_len, scale, partition_tokens, kernel,
+                                k_new, v_new, slot_mapping, k_scales, v_scales,
+                                sliding_window=sliding_window, shared_prefix_blocks=shared_prefix_blocks)
+    _check(lib().pa_decode_noalloc(ctypes.byref(params), _stream(stream)))
     return out
 
 

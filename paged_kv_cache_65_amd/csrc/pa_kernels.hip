@@ -41,6 +41,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "pa.h"
@@ -2894,6 +2895,65 @@ pa_status pa_decode_merge(const pa_decode_params *p, void *workspace, size_t wor
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (p->num_seqs == 0) return record_events(events_of(p), hs, "pa_decode_merge events");
   return launch_merge(p, a, hs, events_of(p));
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------- allocation-free decode
+// Decode workspace for callers that cannot allocate device memory: a fixed
+// array in the code object, one copy per device the library runs on, held
+// until the process ends.  Every pa_decode_noalloc call on a device shares
+// that device's copy.
+constexpr size_t kScratchBytes = PA_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device with that device current (the array's name in host code is only a
+// stand-in for the symbol).
+pa_status scratch_address(void **out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_check(e, "pa_decode_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode_noalloc: device %d beyond the first %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_check(e, "pa_decode_noalloc: hipGetSymbolAddress");
+    if (!ptr || !aligned16(ptr)) return pa::fail(PA_ERR_HIP, "pa_decode_noalloc: bad scratch address");
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_noalloc(const pa_decode_params *p, void *stream) {
+  const pa_status st = validate_all(p);
+  if (st != PA_OK) return st;
+  const size_t need = pa_decode_workspace_bytes(p);
+  if (need > kScratchBytes)
+    return pa::fail(PA_ERR_WORKSPACE,
+                    "pa_decode_noalloc: the call needs %zu bytes of workspace, more than the %zu the library "
+                    "holds per device (use pa_decode with a workspace)",
+                    need, kScratchBytes);
+  void *ws = nullptr;
+  if (need > 0) {
+    const pa_status sa = scratch_address(&ws);
+    if (sa != PA_OK) return sa;
+  }
+  // The workspace needs no initialization: every slot a launch reads was
+  // written earlier in the same call.
+  return pa_decode(p, ws, need > 0 ? kScratchBytes : 0, stream);
 }
 
 pa_status pa_reshape_and_cache(const void *k_new, const void *v_new, void *k_cache, void *v_cache,

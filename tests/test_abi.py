@@ -169,6 +169,17 @@ def test_decode_requires_the_workspace():
     assert pa.lib().pa_decode(ctypes.byref(p), None, 0, None) == pa.PA_ERR_WORKSPACE
 
 
+def test_noalloc_decode_validates_and_refuses_more_than_its_array_before_any_device_call():
+    # invalid parameters: the same checks as pa_decode
+    p = _params(partition_tokens=24)
+    assert pa.lib().pa_decode_noalloc(ctypes.byref(p), None) == pa.PA_ERR_INVALID_ARG
+    # 1024 sequences x 64 query heads x 64 partitions x (128 + 2) floats >> 64 MiB
+    p = _params(kernel=pa.PA_KERNEL_VALU, num_seqs=1024, partition_tokens=64)
+    assert pa.pa_decode_workspace_bytes(p) > pa.PA_NOALLOC_WORKSPACE_BYTES
+    assert pa.lib().pa_decode_noalloc(ctypes.byref(p), None) == pa.PA_ERR_WORKSPACE
+    assert "pa_decode_noalloc" in pa.lib().pa_last_error().decode()
+
+
 def test_fused_append_fields_go_together():
     p = _params(k_new=ctypes.c_void_p(16))
     assert pa.lib().pa_decode(ctypes.byref(p), None, 0, None) == pa.PA_ERR_INVALID_ARG

@@ -1,0 +1,112 @@
+"""pa_decode_noalloc (the library's own per-device workspace) against pa_decode
+(a caller workspace) through the C ABI: the same kernels on the same inputs,
+so the outputs must agree bit for bit; the first output is also held to the
+oracle's bar (2e-3 max-abs for bf16 caches).
+
+Two calls in a row on one device share the library's array; the second is
+smaller than the first, so a result that depended on what the first call left
+in the array would show.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from paged_kv_cache_65_amd import binding as pa  # noqa: E402
+from paged_kv_cache_65_amd import workloads  # noqa: E402
+from tests import gpu_side, oracle_side  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(oracle_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.lib()
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _setup(spec, steps=0):
+    wl = workloads.generate(spec)
+    _say(f"[case] {spec.name} seed={spec.seed} S={spec.num_seqs} Hq={spec.num_q_heads} "
+         f"Hkv={spec.num_kv_heads} D={spec.head_dim} cache={spec.cache or spec.dtype}")
+    gst = gpu_side.build(wl, steps)
+    return wl, gst
+
+
+def _run_both(wl, gst, mb, seqs, pt):
+    """pa_decode and pa_decode_noalloc on the sequences `seqs` (a prefix of the batch)."""
+    spec = wl.spec
+    dev = gst.k_cache.device
+    tab_d, lens_d, _, lens_h = gpu_side.tables(gst, mb, dev)
+    tab_d, lens_d = tab_d[:seqs].contiguous(), lens_d[:seqs].contiguous()
+    q = gpu_side.to_device(wl.q[:seqs], spec.dtype, dev)
+    max_ctx = int(lens_h[:seqs].max())
+    outs = []
+    for fn in (pa.pa_decode, pa.pa_decode_noalloc):
+        out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=dev)
+        fn(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, spec.num_kv_heads, max_ctx,
+           spec.fp32_scale(), partition_tokens=pt, k_scales=gst.k_scales, v_scales=gst.v_scales)
+        outs.append(out)
+    torch.cuda.synchronize()
+    ref, mine = (o.cpu().numpy() for o in outs)
+    return ref, mine
+
+
+CASES = [
+    # (cache, pt of the first call, pt of the second call)
+    ("", pa.PA_PARTITION_BALANCED, pa.PA_PARTITION_BALANCED),
+    ("", 64, pa.PA_PARTITION_BALANCED),
+    ("i8", 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_noalloc_equals_pa_decode_on_two_calls_in_a_row(case):
+    cache, pt1, pt2 = CASES[case]
+    lens = [int(x) for x in np.random.default_rng(90 + case).integers(1, 1500, size=24)]
+    spec = workloads.custom(name=f"noalloc-{case}", seed=90 + case, dtype="bf16", out_dtype="f32",
+                            lens=lens, num_q_heads=16, num_kv_heads=2, head_dim=128, cache=cache)
+    wl, gst = _setup(spec)
+    ost = oracle_side.build(wl)
+    mb = oracle_side.max_blocks_for(wl)
+    # first call: the whole batch
+    ref, mine = _run_both(wl, gst, mb, spec.num_seqs, pt1)
+    _say(f"[noalloc] call 1: {spec.num_seqs} seqs pt={pt1}")
+    assert np.array_equal(ref.view(np.uint32), mine.view(np.uint32))
+    orc = oracle_side.decode(wl, ost, mb)
+    err = float(np.max(np.abs(mine.astype(np.float64) - orc)))
+    assert err <= 2e-3, err
+    # second call right after it: fewer sequences, the array still holds call 1's data
+    ref2, mine2 = _run_both(wl, gst, mb, 7, pt2)
+    _say(f"[noalloc] call 2: 7 seqs pt={pt2}")
+    assert np.array_equal(ref2.view(np.uint32), mine2.view(np.uint32))
+    assert np.all(np.isfinite(mine2))
+
+
+def test_noalloc_rejects_a_call_beyond_its_array_and_launches_nothing():
+    spec = workloads.custom(name="noalloc-big", seed=95, dtype="bf16", out_dtype="f32",
+                            lens=[40] * 4, num_q_heads=16, num_kv_heads=2, head_dim=128)
+    wl, gst = _setup(spec)
+    mb = oracle_side.max_blocks_for(wl)
+    dev = gst.k_cache.device
+    tab_d, lens_d, _, _ = gpu_side.tables(gst, mb, dev)
+    q = gpu_side.to_device(wl.q, spec.dtype, dev)
+    out = torch.full(q.shape, 7.0, dtype=torch.float32, device=dev)
+    # a host bound of 2^22 tokens in 16-token partitions asks for far more than 64 MiB
+    params = pa.make_decode_params(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, spec.num_kv_heads,
+                                   1 << 22, spec.fp32_scale(), partition_tokens=16)
+    assert pa.pa_decode_workspace_bytes(params) > pa.PA_NOALLOC_WORKSPACE_BYTES
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode_noalloc(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, spec.num_kv_heads,
+                             1 << 22, spec.fp32_scale(), partition_tokens=16)
+    assert e.value.status == pa.PA_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert bool(torch.all(out == 7.0))
