@@ -162,7 +162,12 @@ const char *pa_last_error(void);
  *                 (an error where it cannot run).  A positive multiple of
  *                 16 = partitions of that size.
  * Supported: head_dim in {64, 128}; num_q_heads % num_kv_heads == 0;
- *   G <= 16; fp16/bf16 with any kernel, fp32 with the VALU kernel.
+ *   G <= 64 (up to multi-query attention, every query head on one KV head:
+ *   "Inference serving: the KV-cache machine", section "The KV cache:
+ *   attention's memory bill, derived"); fp16/bf16 with any kernel, fp32
+ *   with the VALU kernel.  The matrix-core kernels read every K/V block once
+ *   for all G heads (ceil(G/16) score tiles per block); the VALU kernel takes
+ *   a group of more than 16 heads as 16-head chunks, one workgroup each.
  * Contract violations found on the device (a table entry outside
  * [0, num_blocks), or L outside [0, min(max_context_len,
  * 16*max_blocks_per_seq)]) are never dereferenced: that sequence's output row
@@ -358,7 +363,7 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst_pa
  *   query_start int32 [num_seqs + 1], ascending, query_start[0] = 0 and
  *               query_start[num_seqs] = num_query_rows (device)
  *   max_query_len >= every n_s, max_context_len >= every L (host bounds)
- * fp16 / bf16 caches, head_dim 64 or 128, up to 16 query heads per KV head.
+ * fp16 / bf16 caches, head_dim 64 or 128, up to 64 query heads per KV head.
  * A sequence with n_s > L, L outside [0, max_context_len] or beyond its
  * table row, or n_s > max_query_len, or a table entry outside the pool, gets
  * NaN rows (never dereferenced); a sequence whose rows fall outside

@@ -52,7 +52,8 @@ namespace {
 constexpr int kBS = 16;        // tokens per block
 constexpr int kWaves = 4;      // waves per partition workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kGMax = 16;      // query heads per KV head (MFMA column tile)
+constexpr int kTileCols = 16;  // query heads per MFMA column tile
+constexpr int kGMax = 64;      // query heads per KV head (up to four column tiles)
 constexpr int kDMax = 128;
 constexpr float kLazyLog2 = 8.0f;  // MFMA path: softmax weights stay below 2^8
 
@@ -194,17 +195,18 @@ constexpr uint32_t kAllTokens = 0xFFFFu;
 // Tokens lo .. hi-1 of a block (0 <= lo < hi <= 16) as a bit mask.
 __device__ inline uint32_t token_mask(int lo, int hi) { return ((1u << hi) - 1u) & ~((1u << lo) - 1u); }
 
-// Per-wave online-softmax states meet here at the end of a partition.
+// Per-wave online-softmax states meet here at the end of a partition, one
+// column tile (16 heads) at a time.
 struct __align__(16) SmemBase {
-  float acc[kWaves][kGMax][kDMax];
-  float m[kWaves][kGMax];
-  float l[kWaves][kGMax];
+  float acc[kWaves][kTileCols][kDMax];
+  float m[kWaves][kTileCols];
+  float l[kWaves][kTileCols];
   uint32_t knew[kDMax];  // fused append: the new token's K and V rows (raw bits, up to 512 B)
   uint32_t vnew[kDMax];
 };
 struct __align__(16) SmemValu : SmemBase {
-  float qs[kGMax][kDMax];        // q of the group in float32
-  float ps[kWaves][kGMax][kBS];  // softmax weights of the current block
+  float qs[kTileCols][kDMax];        // q of the workgroup's heads in float32
+  float ps[kWaves][kTileCols][kBS];  // softmax weights of the current block
 };
 
 // ---------------------------------------------------------------- fused append
@@ -301,17 +303,23 @@ __device__ inline void write_token_row(uint8_t *k_cache, uint8_t *v_cache, int64
 // Lane l, with r = l % 16 and tq = l / 16:
 //   K fragment c (c < D/32): the 16 bytes at tile + 1024c + 16l = token r,
 //     dims 32c + 8tq .. +7  -> A operand of mfma_f32_16x16x32 (row = token).
-//   q fragment c: head r of the group (zero when r >= G), same dims -> B operand.
-//   score tile: sc[v] = s(token 4tq+v, head r).
+//   q fragment [ct][c]: head 16ct + r of the group (zero past G), same dims
+//     -> B operand of column tile ct.
+//   score tile ct: sc[v] = s(token 4tq+v, head 16ct + r).
 //   V fragment m (m < D/32): 16 bytes at tile + 1024m + 16l = tokens
 //     4tq..4tq+3 of dim 32m+r (first 8 bytes) and of dim 32m+16+r (last 8)
 //     -> A operands of mfma_f32_16x16x16 for output tiles n = 2m, 2m+1
 //     (row = dim, contraction = token).
-//   P operand = the lane's own 4 weights (tokens 4tq..4tq+3, head r).
-//   acc[n][v] = O(head r, dim 16n + 4tq + v).
+//   P operand = the lane's own 4 weights (tokens 4tq..4tq+3, head 16ct + r).
+//   acc[ct][n][v] = O(head 16ct + r, dim 16n + 4tq + v).
+// NCT = ceil(G / 16) column tiles: a group of more than 16 query heads (up
+// to all 64 heads on one shared KV head, multi-query attention) takes
+// several 16-head tiles, each with its own softmax state, and every K and V
+// fragment in registers feeds all of them, so a block is still read once.
 // ============================================================================
-template <int DT, int D>
+template <int DT, int D, int NCT_ = 1>
 struct MfmaWave {
+  static constexpr int NCT = NCT_;   // 16-head column tiles
   static constexpr int NC = D / 32;  // 16-byte fragments per tile
   static constexpr int NT = D / 16;  // output tiles
   static constexpr int TILE = kBS * D * 2;
@@ -322,6 +330,9 @@ struct MfmaWave {
   // the matrix ops, the next loading) at twelve waves per CU measured 1-3%
   // faster than three, at 137 instead of 165 VGPRs (D = 128).
   static constexpr int kRing = PA_MFMA_RING;
+  // Partition workgroups per CU: each more column tile holds another set of
+  // q fragments and accumulators in registers.
+  static constexpr int kPartWgPerCu = NCT == 1 ? 3 : NCT == 2 ? 2 : 1;
   using v8 = typename std::conditional<DT == PA_BF16, bf16x8_t, f16x8_t>::type;
 
   struct Frag {
@@ -331,17 +342,18 @@ struct MfmaWave {
 
   using Smem = SmemBase;
 
-  v8 qB[NC];
-  f32x4_t acc[NT];
-  float m, l;
-
-  __device__ void stage(const DecodeArgs &, Smem &, int, int, int) {}
+  v8 qB[NCT][NC];
+  f32x4_t acc[NCT][NT];
+  float m[NCT], l[NCT];
 
   __device__ void reset() {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m = -INFINITY;
-    l = 0.f;
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[ct][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m[ct] = -INFINITY;
+      l[ct] = 0.f;
+    }
   }
 
   // q fragments from the group's G rows of D 16-bit values (rows >= G are 0).
@@ -349,16 +361,21 @@ struct MfmaWave {
   template <class P>
   __device__ void load_q(const P *rows, int G, int lane) {
     const int r = lane % 16, tq = lane / 16;
-    const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(rows) + (r < G ? r : 0) * (D / 8);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      u32x4_t x = qrow[4 * c + tq];
-      if (r >= G) x = u32x4_t{0, 0, 0, 0};
-      qB[c] = __builtin_bit_cast(v8, x);
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int h = 16 * ct + r;
+      const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(rows) + (h < G ? h : 0) * (D / 8);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        u32x4_t x = qrow[4 * c + tq];
+        if (h >= G) x = u32x4_t{0, 0, 0, 0};
+        qB[ct][c] = __builtin_bit_cast(v8, x);
+      }
     }
   }
 
-  __device__ void init(const DecodeArgs &a, const Smem &, int s, int g, int lane) {
+  // q rows of KV head g of sequence s.
+  __device__ void init(const DecodeArgs &a, int s, int g, int lane) {
     const int G = a.group;
     load_q(static_cast<const uint8_t *>(a.q) + ((int64_t)s * a.num_q_heads + g * G) * D * 2, G, lane);
     reset();
@@ -374,8 +391,10 @@ struct MfmaWave {
   }
 
   static constexpr bool kAppend = true;  // supports the fused append
-  static constexpr int kBalRing = PA_BALANCED_RING;          // balanced kernel: blocks in flight per wave
-  static constexpr int kBalWgPerCu = PA_BALANCED_WG_PER_CU;  // balanced kernel: workgroups per CU
+  // Balanced kernel: blocks in flight per wave (each more column tile takes
+  // registers from the ring) and workgroups per CU.
+  static constexpr int kBalRing = NCT == 1 ? PA_BALANCED_RING : NCT == 2 ? 3 : 2;
+  static constexpr int kBalWgPerCu = PA_BALANCED_WG_PER_CU;
   // Tile index = block * Hkv + head.
   __device__ static void load_tile(Frag &f, const DecodeArgs &a, int64_t tile, int lane) {
     load(f, a.k_cache + tile * TILE, a.v_cache + tile * TILE, lane);
@@ -431,6 +450,28 @@ struct MfmaWave {
     lo = u32x2_t{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
   }
 
+  // Online-softmax step of column tile ct for the block's scores s[] (log2
+  // units, masked tokens -inf): lazy reference max, weights, running sum.
+  // The state is rescaled only when a head's block max exceeds its
+  // reference by more than kLazyLog2, so weights stay below 2^kLazyLog2 and
+  // most blocks skip the rescale (a wave-uniform branch).
+  __device__ void softmax_step(int ct, const float s[4], float p[4]) {
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = max_xor32(max_xor16(mx));
+    const bool bump = mx > m[ct] + kLazyLog2;
+    if (__builtin_amdgcn_ballot_w64(bump)) {
+      const float m_new = bump ? mx : m[ct];
+      const float alpha = exp2_neg(m[ct] - m_new);
+      l[ct] *= alpha;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
+      m[ct] = m_new;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) p[v] = __builtin_amdgcn_exp2f(s[v] - m[ct]);
+    l[ct] += (p[0] + p[1]) + (p[2] + p[3]);
+  }
+
   // One block; bit t of `vm` set = token t of the block is attended (inside
   // the context and the window); new_tok >= 0: that token's K/V come from
   // the staged new row.
@@ -447,58 +488,49 @@ struct MfmaWave {
 #pragma unroll
       for (int c = 0; c < NC; ++c) f.v[c] &= u32x4_t{lo, hi, lo, hi};
     }
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sc = mma_qk(__builtin_bit_cast(v8, f.k[c]), qB[c], sc);
-    float s[4];
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s[v] = sc[v] * scale_log2;
-    if (vm != kAllTokens) {
+      for (int c = 0; c < NC; ++c) sc = mma_qk(__builtin_bit_cast(v8, f.k[c]), qB[ct][c], sc);
+      float s[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) s[v] = ((mine >> v) & 1u) ? s[v] : -INFINITY;
-    }
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = max_xor32(max_xor16(mx));
-    // Lazy reference max: the state is rescaled only when a head's block max
-    // exceeds its reference by more than kLazyLog2, so weights stay below
-    // 2^kLazyLog2 and most blocks skip the rescale (a wave-uniform branch).
-    const bool bump = mx > m + kLazyLog2;
-    if (__builtin_amdgcn_ballot_w64(bump)) {
-      const float m_new = bump ? mx : m;
-      const float alpha = exp2_neg(m - m_new);
-      l *= alpha;
+      for (int v = 0; v < 4; ++v) s[v] = sc[v] * scale_log2;
+      if (vm != kAllTokens) {
 #pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
-      m = m_new;
-    }
-    float p[4];
+        for (int v = 0; v < 4; ++v) s[v] = ((mine >> v) & 1u) ? s[v] : -INFINITY;
+      }
+      float p[4];
+      softmax_step(ct, s, p);
+      u32x2_t ph, pl;
+      split(p, ph, pl);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) p[v] = __builtin_amdgcn_exp2f(s[v] - m);
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-    u32x2_t ph, pl;
-    split(p, ph, pl);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const u32x2_t a0 = u32x2_t{f.v[c][0], f.v[c][1]};
-      const u32x2_t a1 = u32x2_t{f.v[c][2], f.v[c][3]};
-      acc[2 * c] = mma_pv(a0, ph, acc[2 * c]);
-      acc[2 * c + 1] = mma_pv(a1, ph, acc[2 * c + 1]);
-      acc[2 * c] = mma_pv(a0, pl, acc[2 * c]);
-      acc[2 * c + 1] = mma_pv(a1, pl, acc[2 * c + 1]);
+      for (int c = 0; c < NC; ++c) {
+        const u32x2_t a0 = u32x2_t{f.v[c][0], f.v[c][1]};
+        const u32x2_t a1 = u32x2_t{f.v[c][2], f.v[c][3]};
+        acc[ct][2 * c] = mma_pv(a0, ph, acc[ct][2 * c]);
+        acc[ct][2 * c + 1] = mma_pv(a1, ph, acc[ct][2 * c + 1]);
+        acc[ct][2 * c] = mma_pv(a0, pl, acc[ct][2 * c]);
+        acc[ct][2 * c + 1] = mma_pv(a1, pl, acc[ct][2 * c + 1]);
+      }
     }
   }
 
-  // Publishes this wave's state for the group's heads into LDS.
-  __device__ void finish(Smem &sm, int w, int lane, int G) {
+  // Publishes this wave's state for column tile ct (heads 16ct .. 16ct+15 of
+  // the group, those below G) into LDS rows 0 .. 15.
+  __device__ void finish(Smem &sm, int w, int lane, int G, int ct) {
     const int r = lane % 16, tq = lane / 16;
-    const float lt = sum_xor32(sum_xor16(l));
-    if (r < G) {
 #pragma unroll
-      for (int n = 0; n < NT; ++n)
-        *reinterpret_cast<f32x4_t *>(&sm.acc[w][r][16 * n + 4 * tq]) = acc[n];
-      if (tq == 0) {
-        sm.m[w][r] = m;
-        sm.l[w][r] = lt;
+    for (int c = 0; c < NCT; ++c) {
+      if (c != ct) continue;  // register indices stay compile-time constants
+      const float lt = sum_xor32(sum_xor16(l[c]));
+      if (16 * c + r < G) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4_t *>(&sm.acc[w][r][16 * n + 4 * tq]) = acc[c][n];
+        if (tq == 0) {
+          sm.m[w][r] = m[c];
+          sm.l[w][r] = lt;
+        }
       }
     }
   }
@@ -511,25 +543,29 @@ struct MfmaWave {
   __device__ void store_segment(const DecodeArgs &a, int64_t row0, int64_t prow0, bool whole, bool bad,
                                 int lane, int G) const {
     const int r = lane % 16, tq = lane / 16;
-    const float lt = sum_xor32(sum_xor16(l));
-    if (r >= G) return;
     const f32x4_t nan4 = {NAN, NAN, NAN, NAN};
-    if (whole) {
-      const int64_t o = (row0 + r) * D + 4 * tq;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        f32x4_t v;
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float lt = sum_xor32(sum_xor16(l[ct]));
+      const int h = 16 * ct + r;
+      if (h >= G) continue;
+      if (whole) {
+        const int64_t o = (row0 + h) * D + 4 * tq;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[n][e] / lt;
-        store_out4(a.out, o + 16 * n, bad ? nan4 : v, a.out_dtype);
-      }
-    } else {
-      float *pacc = a.ws_acc + (prow0 + r) * D + 4 * tq;
+        for (int n = 0; n < NT; ++n) {
+          f32x4_t v;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4_t *>(pacc + 16 * n) = bad ? nan4 : acc[n];
-      if (tq == 0) {
-        a.ws_ml[(prow0 + r) * 2] = bad ? NAN : m;
-        a.ws_ml[(prow0 + r) * 2 + 1] = lt;
+          for (int e = 0; e < 4; ++e) v[e] = acc[ct][n][e] / lt;
+          store_out4(a.out, o + 16 * n, bad ? nan4 : v, a.out_dtype);
+        }
+      } else {
+        float *pacc = a.ws_acc + (prow0 + h) * D + 4 * tq;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4_t *>(pacc + 16 * n) = bad ? nan4 : acc[ct][n];
+        if (tq == 0) {
+          a.ws_ml[(prow0 + h) * 2] = bad ? NAN : m[ct];
+          a.ws_ml[(prow0 + h) * 2 + 1] = lt;
+        }
       }
     }
   }
@@ -538,13 +574,17 @@ struct MfmaWave {
   // m[G], l[G]); flush_parked() writes it out later.
   __device__ void park_segment(float *st, int lane, int G) const {
     const int r = lane % 16, tq = lane / 16;
-    const float lt = sum_xor32(sum_xor16(l));
-    if (r >= G) return;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4_t *>(st + r * D + 16 * n + 4 * tq) = acc[n];
-    if (tq == 0) {
-      st[G * D + r] = m;
-      st[G * D + G + r] = lt;
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float lt = sum_xor32(sum_xor16(l[ct]));
+      const int h = 16 * ct + r;
+      if (h >= G) continue;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4_t *>(st + h * D + 16 * n + 4 * tq) = acc[ct][n];
+      if (tq == 0) {
+        st[G * D + h] = m[ct];
+        st[G * D + G + h] = lt;
+      }
     }
   }
 };
@@ -645,29 +685,34 @@ __device__ inline int v_code_off(int d, int t) {
 //   V code vector x: tokens 4c .. 4c+3 of dims 64x + 16k + r, bytes 4k .. 4k+3
 //     -> A operand of the P.V tile n = 4x + k;
 //   scales: the four tokens 4c .. 4c+3 of the lane's score rows.
+// Several column tiles (G > 16) share the block's codes: they are converted
+// once per block and feed every tile.
 // ============================================================================
 // Byte-code caches: FMT = PA_I8 (int8 codes) or PA_FP8 (OCP E4M3 codes),
 // one float32 scale per (token, KV head) row.
-template <int QDT, int D, int FMT = PA_I8>
-struct MfmaWaveI8 : MfmaWave<PA_F16, D> {
+template <int QDT, int D, int FMT = PA_I8, int NCT_ = 1>
+struct MfmaWaveI8 : MfmaWave<PA_F16, D, NCT_> {
   // fp16 matrix ops: a code becomes an fp16 value exactly (pair16: three
   // instructions per pair for int8, one conversion for E4M3), and q (QDT) is
   // carried in fp16 with a power-of-two prescale per (sequence, KV head) pair
   // (load_q).
-  using Base = MfmaWave<PA_F16, D>;
+  using Base = MfmaWave<PA_F16, D, NCT_>;
   using typename Base::v8;
   using Base::NC;
+  using Base::NCT;
   using Base::NT;
   static constexpr int NV = D / 64;        // 16-byte code vectors per lane and tile
   static constexpr int TILE = kBS * D;     // code bytes per (block, head) tile
   static constexpr bool kAppend = true;    // new rows (QDT) quantized as pa_reshape_and_cache_int8 / _fp8 do
   // The code conversions add ~250 VALU instructions per block: more waves per
-  // SIMD hide their latency, a shallower ring keeps them in registers.
-  static constexpr int kBalRing = FMT == PA_FP8 ? PA_FP8_RING : PA_I8_RING;
+  // SIMD hide their latency, a shallower ring keeps them in registers.  With
+  // several column tiles the q fragments and accumulators no longer fit two
+  // waves per SIMD: one wave per SIMD with a deeper ring instead.
+  static constexpr int kBalRing = NCT > 1 ? 3 : FMT == PA_FP8 ? PA_FP8_RING : PA_I8_RING;
   // Partition kernel: a code tile is half a 16-bit tile, so three blocks per
   // wave hold as many bytes in flight as 1.5 16-bit blocks.
   static constexpr int kRing = 3;
-  static constexpr int kBalWgPerCu = FMT == PA_FP8 ? PA_FP8_WG_PER_CU : PA_I8_WG_PER_CU;
+  static constexpr int kBalWgPerCu = NCT > 1 ? 1 : FMT == PA_FP8 ? PA_FP8_WG_PER_CU : PA_I8_WG_PER_CU;
 
   struct Frag {
     u32x4_t k[NV];
@@ -707,28 +752,33 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D> {
 
   float qscale;  // 2^-e undoes the prescale of q in the scores
 
+  // Element e (0..7) of 8 packed QDT values as float32.
+  __device__ static float qval(const u32x4_t &w, int e) {
+    const uint32_t h = (w[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+    if constexpr (QDT == PA_BF16)
+      return __uint_as_float(h << 16);
+    else
+      return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  }
+
   // q rows (QDT) -> fp16 fragments scaled by 2^e, e chosen per wave so the
   // largest |q| of the G rows lands in [2^14, 2^15): a bf16 or fp16 value is
   // then exact in fp16 unless it is below 2^-28 of that largest one.
   template <class P>
   __device__ void load_q(const P *rows, int G, int lane) {
     const int r = lane % 16, tq = lane / 16;
-    const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(rows) + (r < G ? r : 0) * (D / 8);
-    float x[NC][8];
+    u32x4_t w[NCT][NC];
     float mx = 0.f;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const u32x4_t w = qrow[4 * c + tq];
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int h = 16 * ct + r;
+      const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(rows) + (h < G ? h : 0) * (D / 8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t h = (w[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-        float v;
-        if constexpr (QDT == PA_BF16)
-          v = __uint_as_float(h << 16);
-        else
-          v = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-        x[c][e] = r < G ? v : 0.f;
-        mx = fmaxf(mx, fabsf(x[c][e]));
+      for (int c = 0; c < NC; ++c) {
+        w[ct][c] = qrow[4 * c + tq];
+        if (h >= G) w[ct][c] = u32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qval(w[ct][c], e)));
       }
     }
     mx = max_xor32(max_xor16(row_max16(mx)));
@@ -741,13 +791,16 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D> {
     const float up = ldexpf(1.f, ex);
     qscale = ldexpf(1.f, -ex);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      uint32_t h[4];
+    for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        h[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(x[c][2 * e] * up)) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(x[c][2 * e + 1] * up)) << 16);
-      this->qB[c] = __builtin_bit_cast(v8, u32x4_t{h[0], h[1], h[2], h[3]});
+      for (int c = 0; c < NC; ++c) {
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          h[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(qval(w[ct][c], 2 * e) * up)) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(qval(w[ct][c], 2 * e + 1) * up)) << 16);
+        this->qB[ct][c] = __builtin_bit_cast(v8, u32x4_t{h[0], h[1], h[2], h[3]});
+      }
     }
   }
 
@@ -830,40 +883,13 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D> {
     const int tq = lane / 16;
     if (new_tok >= 0) patch_new(f, new_tok, lane, knew, vnew);
     const uint32_t mine = vm >> (4 * tq);
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    // K codes as fp16 A operands, once for every column tile
+    v8 kb[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const uint32_t w0 = f.k[c / 2][(c % 2) * 2], w1 = f.k[c / 2][(c % 2) * 2 + 1];
-      const u32x4_t ab = {pair16(w0, 0), pair16(w0, 2), pair16(w1, 0), pair16(w1, 2)};
-      sc = Base::mma_qk(__builtin_bit_cast(v8, ab), this->qB[c], sc);
+      kb[c] = __builtin_bit_cast(v8, u32x4_t{pair16(w0, 0), pair16(w0, 2), pair16(w1, 0), pair16(w1, 2)});
     }
-    float s[4];
-    const float sl = scale_log2 * qscale;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) s[v] = sc[v] * f.ks[v] * sl;
-    // tokens outside the attended range: scores masked (their scales may be anything)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) s[v] = ((mine >> v) & 1u) ? s[v] : -INFINITY;
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = max_xor32(max_xor16(mx));
-    const bool bump = mx > this->m + kLazyLog2;
-    if (__builtin_amdgcn_ballot_w64(bump)) {
-      const float m_new = bump ? mx : this->m;
-      const float alpha = exp2_neg(this->m - m_new);
-      this->l *= alpha;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) this->acc[n] *= alpha;
-      this->m = m_new;
-    }
-    float p[4], pw[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      p[v] = __builtin_amdgcn_exp2f(s[v] - this->m);
-      pw[v] = ((mine >> v) & 1u) ? p[v] * f.vs[v] : 0.f;
-    }
-    this->l += (p[0] + p[1]) + (p[2] + p[3]);
-    u32x2_t ph, pl;
-    Base::split(pw, ph, pl);
     if constexpr (FMT == PA_FP8) {
       // an unwritten or stale E4M3 slot may hold a NaN code: clear the V
       // bytes of tokens outside the attended range (a word holds this
@@ -875,18 +901,39 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D> {
         for (int x = 0; x < NV; ++x) f.v[x] &= u32x4_t{bm, bm, bm, bm};
       }
     }
+    const float sl = scale_log2 * qscale;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const uint32_t w = f.v[n / 4][n % 4];
-      const u32x2_t av = {pair16(w, 0), pair16(w, 2)};
-      this->acc[n] = Base::mma_pv(av, ph, this->acc[n]);
-      this->acc[n] = Base::mma_pv(av, pl, this->acc[n]);
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sc = Base::mma_qk(kb[c], this->qB[ct][c], sc);
+      float s[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s[v] = sc[v] * f.ks[v] * sl;
+      // tokens outside the attended range: scores masked (their scales may be anything)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s[v] = ((mine >> v) & 1u) ? s[v] : -INFINITY;
+      float p[4], pw[4];
+      this->softmax_step(ct, s, p);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) pw[v] = ((mine >> v) & 1u) ? p[v] * f.vs[v] : 0.f;
+      u32x2_t ph, pl;
+      Base::split(pw, ph, pl);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const uint32_t w = f.v[n / 4][n % 4];
+        const u32x2_t av = {pair16(w, 0), pair16(w, 2)};
+        this->acc[ct][n] = Base::mma_pv(av, ph, this->acc[ct][n]);
+        this->acc[ct][n] = Base::mma_pv(av, pl, this->acc[ct][n]);
+      }
     }
   }
 };
 
 // ============================================================================
-// Vector-ALU wave: any cache type, GM = compile-time bound on the group size.
+// Vector-ALU wave: any cache type, GM = compile-time bound on the heads one
+// workgroup takes (at most 16: a group of more than 16 query heads is split
+// into 16-head chunks, one workgroup each, that read the same blocks).
 //
 // With X = 16 / element bytes and NC = D*bytes/1024 sixteen-byte fragments:
 //   K fragment c of lane l holds token r = l % 16, dims X*(4c + tq) .. +X-1;
@@ -913,11 +960,11 @@ struct ValuWave {
   float acc[GM][VD];  // partial over this lane's 4-token quad
   float m[GM], l[GM];
 
-  __device__ void stage(const DecodeArgs &a, Smem &sm, int s, int g, int tid) {
-    const int G = a.group;
+  // q rows h0 .. h0+G-1 of sequence s (G <= 16) into LDS as float32.
+  __device__ void stage(const DecodeArgs &a, Smem &sm, int s, int h0, int G, int tid) {
     const uint8_t *qb = static_cast<const uint8_t *>(a.q);
     for (int i = tid; i < G * D; i += kThreads) {
-      const int64_t e = ((int64_t)s * a.num_q_heads + g * G) * D + i;
+      const int64_t e = ((int64_t)s * a.num_q_heads + h0) * D + i;
       uint32_t bits;
       if constexpr (EB == 4)
         bits = reinterpret_cast<const uint32_t *>(qb)[e];
@@ -927,7 +974,7 @@ struct ValuWave {
     }
   }
 
-  __device__ void init(const DecodeArgs &, const Smem &, int, int, int) {
+  __device__ void reset() {
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
       m[h] = -INFINITY;
@@ -1053,20 +1100,46 @@ __device__ void write_partial_nan(const DecodeArgs &a, int s, int h0, int G, int
   }
 }
 
-// MFMA path: three 4-wave workgroups per CU (3 waves per SIMD, <= 168 VGPRs).
+// Partition workgroups per CU: the matrix-core wave's choice (three for one
+// column tile: 3 waves per SIMD, <= 168 VGPRs); one for the vector-ALU wave.
+template <class W, bool kMfma>
+constexpr int partition_wg_per_cu() {
+  if constexpr (kMfma)
+    return W::kPartWgPerCu;
+  else
+    return 1;
+}
+
+// Column tiles of the wave's state (the vector-ALU wave holds one group of
+// at most 16 heads).
+template <class W, bool kMfma>
+constexpr int wave_tiles() {
+  if constexpr (kMfma)
+    return W::NCT;
+  else
+    return 1;
+}
+
 template <class W, int D, bool kMfma>
-__global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, (partition_wg_per_cu<W, kMfma>())) void pa_partition_kernel(DecodeArgs a) {
   __shared__ typename W::Smem sm;
   // 1-D grid, KV head fastest, then sequence, then partition.  Workgroups are
   // dealt round-robin to the 8 XCDs by linear id, so this order spreads every
   // sequence's (unequal) partitions evenly over the XCDs; with the partition
   // index fastest, partition p of every sequence would land on the same XCD.
-  const int g = blockIdx.x % a.num_kv_heads;
-  const int s = (blockIdx.x / a.num_kv_heads) % a.num_seqs;
-  const int p = blockIdx.x / (a.num_kv_heads * a.num_seqs);
-  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
+  // The vector-ALU wave takes at most 16 heads: a larger group is split into
+  // 16-head chunks, the fastest grid index (they read the same blocks at
+  // about the same time).
   const int G = a.group;
-  const int h0 = g * G;
+  const int nch = kMfma ? 1 : (G + kTileCols - 1) / kTileCols;
+  const int hc = kMfma ? 0 : (int)(blockIdx.x % nch);
+  const int id = kMfma ? (int)blockIdx.x : (int)(blockIdx.x / nch);
+  const int g = id % a.num_kv_heads;
+  const int s = (id / a.num_kv_heads) % a.num_seqs;
+  const int p = id / (a.num_kv_heads * a.num_seqs);
+  const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
+  const int h0 = g * G + hc * kTileCols;        // first query head of this workgroup
+  const int Gc = min(G - hc * kTileCols, kMfma ? G : kTileCols);  // and how many
   const int wu = __builtin_amdgcn_readfirstlane(w);
   // Loads that do not depend on the context length go out together with it:
   // the q fragments, and this wave's first 64 block ids (speculative: only
@@ -1078,13 +1151,16 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
   const int32_t *trow = a.block_tables + (int64_t)s * a.max_blocks + blk0;
   int ids_first = (int64_t)blk0 + wu + lane * kWaves < a.max_blocks ? trow[wu + lane * kWaves] : 0;
   W wave;
-  wave.init(a, sm, s, g, lane);
+  if constexpr (kMfma)
+    wave.init(a, s, g, lane);
+  else
+    wave.reset();
   if (!ctx_valid(L, a)) {
-    if (p == 0) write_rows<D>(a, s, h0, G, NAN);
+    if (p == 0) write_rows<D>(a, s, h0, Gc, NAN);
     return;
   }
   if (L == 0) {
-    if (p == 0) write_rows<D>(a, s, h0, G, 0.f);
+    if (p == 0) write_rows<D>(a, s, h0, Gc, 0.f);
     return;
   }
   const int first = window_first_token(L, a.window);
@@ -1102,15 +1178,18 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
   const int last_valid = tok1 - (blk0 + nblk - 1) * kBS;
   const int first_lo = p == 0 ? first - jb * kBS : 0;  // masked tokens of the partition's block 0
 
-  wave.stage(a, sm, s, g, tid);
-  if constexpr (!kMfma) __syncthreads();  // q staged in LDS
+  if constexpr (!kMfma) {
+    wave.stage(a, sm, s, h0, Gc, tid);
+    __syncthreads();  // q staged in LDS
+  }
   int bad = 0;  // a block id outside the pool was seen (never dereferenced)
   // Fused append (one new token per sequence, at position L-1, in the last
   // block of the last partition): the wave that computes that block checks
   // the slot against the table, stages the token's K/V rows for head g in
-  // LDS, stores them into the slot, and later takes the token from LDS.  A
-  // slot that is not position L-1's slot marks the sequence bad: nothing is
-  // written and the row is NaN.  Only that wave is involved (no barrier).
+  // LDS, stores them into the slot (only the first head chunk's workgroup),
+  // and later takes the token from LDS.  A slot that is not position L-1's
+  // slot marks the sequence bad: nothing is written and the row is NaN.
+  // Only that wave is involved (no barrier).
   int new_tok = -1;
   if (a.k_new != nullptr && p == nparts - 1 && wu == (nblk - 1) % kWaves) {
     const int64_t slot = a.slot_mapping[s];
@@ -1127,8 +1206,9 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
           sm.vnew[i] = reinterpret_cast<const uint32_t *>(a.v_new + row)[i];
         }
         new_tok = pos % kBS;
-        write_token_row<EB, D>(const_cast<uint8_t *>(a.k_cache), const_cast<uint8_t *>(a.v_cache),
-                               blk, new_tok, g, a.num_kv_heads, sm.knew, sm.vnew, lane);
+        if (hc == 0)
+          write_token_row<EB, D>(const_cast<uint8_t *>(a.k_cache), const_cast<uint8_t *>(a.v_cache),
+                                 blk, new_tok, g, a.num_kv_heads, sm.knew, sm.vnew, lane);
       }
     }
   }
@@ -1176,21 +1256,33 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
           if constexpr (kMfma)
             wave.compute(fr[b], vm, a.scale_log2, lane, nt, sm.knew, sm.vnew);
           else
-            wave.compute(fr[b], vm, a.scale_log2, lane, nt, sm, w, G);
+            wave.compute(fr[b], vm, a.scale_log2, lane, nt, sm, w, Gc);
         }
       }
     }
   }
-  wave.finish(sm, w, lane, G);
-  if (__syncthreads_or(bad)) {
-    if (nparts == 1) {
-      write_rows<D>(a, s, h0, G, NAN);
-      return;
+  // Fold the four wave states, one column tile (16 heads) at a time:
+  // M = max m_w, out = sum 2^(m_w-M) acc_w / sum 2^(m_w-M) l_w.
+  constexpr int kTiles = wave_tiles<W, kMfma>();
+#pragma unroll
+  for (int ct = 0; ct < kTiles; ++ct) {
+    if constexpr (kMfma)
+      wave.finish(sm, w, lane, Gc, ct);
+    else
+      wave.finish(sm, w, lane, Gc);
+    if (ct == 0) {
+      if (__syncthreads_or(bad)) {
+        if (nparts == 1)
+          write_rows<D>(a, s, h0, Gc, NAN);
+        else
+          write_partial_nan<D>(a, s, h0, Gc, p);
+        return;
+      }
+    } else {
+      __syncthreads();
     }
-    write_partial_nan<D>(a, s, h0, G, p);
-  } else {
-    // Fold the four wave states: M = max m_w, out = sum 2^(m_w-M) acc_w / sum 2^(m_w-M) l_w.
-    for (int i = tid; i < G * D; i += kThreads) {
+    const int hb = ct * kTileCols, nh = min(kTileCols, Gc - hb);  // heads of this tile
+    for (int i = tid; i < nh * D; i += kThreads) {
       const int h = i / D, d = i % D;
       float M = -INFINITY;
 #pragma unroll
@@ -1202,7 +1294,7 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
         num += f * sm.acc[ww][h][d];
         den += f * sm.l[ww][h];
       }
-      const int64_t row = (int64_t)s * a.num_q_heads + h0 + h;
+      const int64_t row = (int64_t)s * a.num_q_heads + h0 + hb + h;
       if (nparts == 1) {
         store_out(a.out, row * D + d, num / den, a.out_dtype);
       } else {
@@ -1214,6 +1306,7 @@ __global__ __launch_bounds__(kThreads, kMfma ? 3 : 1) void pa_partition_kernel(D
         }
       }
     }
+    if (ct + 1 < kTiles) __syncthreads();  // the next tile reuses the LDS rows
   }
 }
 
@@ -1747,7 +1840,9 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_balanced_kernel(Dec
 // machine").  The score tile's 16 columns are (query token, head) pairs,
 // token-major: a tile holds tpt = 16/G tokens of the group's G heads, a wave
 // holds NCT tiles (tpg = NCT*tpt tokens: a "query group"), each column with
-// its own online-softmax state and causal limit.  Workgroup = (KV head g,
+// its own online-softmax state and causal limit.  With G > 16 a tile holds
+// 16 heads of one token and a query group NCT*16 of that token's heads
+// (hparts query groups per token).  Workgroup = (KV head g,
 // sequence s, query group, partition of the blocks the group needs); its
 // four waves take every fourth block, their states meet in LDS, and the
 // group writes final rows or (m, l, acc) partials for the merge.
@@ -1762,7 +1857,7 @@ struct ExtendArgs {
   float *ws_ml;                   // [T][Hq][max_parts][2]
   float *ws_acc;                  // [T][Hq][max_parts][D]
   int32_t num_seqs, num_q_heads, num_kv_heads, group, max_blocks, num_blocks, max_ctx, max_q,
-      num_rows, max_parts, part_tokens, out_dtype, qgroups, tpt, tpg;
+      num_rows, max_parts, part_tokens, out_dtype, qgroups, tpt, tpg, hparts;
   float scale_log2;
 };
 
@@ -1807,6 +1902,7 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
   // grid: they run together and read the same blocks, the later reads served
   // from the Infinity Cache.
   const int qg = blockIdx.x % a.qgroups;
+  const int tg = qg / a.hparts, hp = qg % a.hparts;  // token group, head part
   int rest = blockIdx.x / a.qgroups;
   const int g = rest % Hkv;
   rest /= Hkv;
@@ -1817,18 +1913,22 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
   const int L = a.context_lens[s];
   const int q0 = a.query_start[s];
   const int n = a.query_start[s + 1] - q0;
-  const int i0 = qg * a.tpg;
+  const int i0 = tg * a.tpg;
   if (!extend_rows_valid(q0, n, a) || i0 >= n) return;  // no such query group
   const int ni = min(a.tpg, n - i0);
   const int Hq = a.num_q_heads;
-  // this lane's column in tile ct: token tk(ct), head r % G
-  auto col_token = [&](int ct) { return (r < a.tpt * G) ? ct * a.tpt + r / G : 1 << 30; };
-  const int hd = g * G + r % G;
+  // column (ct, lane row rr): token i0 + col_token of the group's head col_head
+  const bool wide = G > kTileCols;
+  auto col_token = [&](int ct, int rr) { return wide ? 0 : (rr < a.tpt * G ? ct * a.tpt + rr / G : 1 << 30); };
+  auto col_head = [&](int ct, int rr) { return wide ? (hp * NCT + ct) * kTileCols + rr : rr % G; };
+  auto col_ok = [&](int ct, int rr) { return col_token(ct, rr) < ni && col_head(ct, rr) < G; };
   if (!extend_seq_valid(L, n, a)) {
     if (p == 0)
-      for (int i = tid; i < ni * G * D; i += kThreads) {
-        const int tk = i / (G * D), h = (i / D) % G, d = i % D;
-        store_out(a.out, ((int64_t)(q0 + i0 + tk) * Hq + g * G + h) * D + d, NAN, a.out_dtype);
+      for (int i = tid; i < NCT * kTileCols * D; i += kThreads) {
+        const int col = i / D, d = i % D, ct = col / kTileCols, rr = col % kTileCols;
+        if (col_ok(ct, rr))
+          store_out(a.out, ((int64_t)(q0 + i0 + col_token(ct, rr)) * Hq + g * G + col_head(ct, rr)) * D + d, NAN,
+                    a.out_dtype);
       }
     return;
   }
@@ -1849,11 +1949,11 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
   float mm[NCT], ll[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    const int tk = col_token(ct);
-    const bool ok = tk < ni;
+    const bool ok = col_ok(ct, r);
+    const int tk = ok ? col_token(ct, r) : 0, hd = g * G + (ok ? col_head(ct, r) : 0);
     lim[ct] = ok ? pf + tk : -1;
     const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
-                                                            ((int64_t)(q0 + i0 + (ok ? tk : 0)) * Hq + hd) * D * 2);
+                                                            ((int64_t)(q0 + i0 + tk) * Hq + hd) * D * 2);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       u32x4_t x = qrow[4 * c + tq];
@@ -1868,7 +1968,7 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
   // the first position any column of tile ct may not see (wave-uniform)
   int tile_min[NCT];
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) tile_min[ct] = pf + ct * a.tpt;
+  for (int ct = 0; ct < NCT; ++ct) tile_min[ct] = pf + (wide ? 0 : ct * a.tpt);
 
   const int64_t head_off = (int64_t)g * M::TILE;
   const int64_t blk_stride = (int64_t)Hkv * M::TILE;
@@ -1964,9 +2064,10 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
     }
   }
   if (__syncthreads_or(bad)) {
-    for (int i = tid; i < ni * G * D; i += kThreads) {
-      const int tk = i / (G * D), h = (i / D) % G, d = i % D;
-      const int64_t row = (int64_t)(q0 + i0 + tk) * Hq + g * G + h;
+    for (int i = tid; i < NCT * kTileCols * D; i += kThreads) {
+      const int col = i / D, d = i % D, ct = col / kTileCols, rr = col % kTileCols;
+      if (!col_ok(ct, rr)) continue;
+      const int64_t row = (int64_t)(q0 + i0 + col_token(ct, rr)) * Hq + g * G + col_head(ct, rr);
       if (nparts == 1) {
         store_out(a.out, row * D + d, NAN, a.out_dtype);
       } else {
@@ -1982,9 +2083,9 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
   }
   // fold the four waves; a wave (or the whole group) that saw no position of
   // a column leaves m = -inf, l = 0 for it
-  for (int i = tid; i < ni * G * D; i += kThreads) {
-    const int tk = i / (G * D), h = (i / D) % G, d = i % D;
-    const int col = (tk / a.tpt) * 16 + (tk % a.tpt) * G + h;
+  for (int i = tid; i < NCT * kTileCols * D; i += kThreads) {
+    const int col = i / D, d = i % D, ct = col / kTileCols, rr = col % kTileCols;
+    if (!col_ok(ct, rr)) continue;
     float Mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, sm.m[w][col]);
@@ -1997,7 +2098,7 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
         den += f * sm.l[w][col];
       }
     }
-    const int64_t row = (int64_t)(q0 + i0 + tk) * Hq + g * G + h;
+    const int64_t row = (int64_t)(q0 + i0 + col_token(ct, rr)) * Hq + g * G + col_head(ct, rr);
     if (nparts == 1) {
       store_out(a.out, row * D + d, num / den, a.out_dtype);
     } else {
@@ -2039,8 +2140,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_extend_merge_kernel(Exten
 // KV-cache machine", Lab B, the system prompt paid once).  The attention of
 // every query row over the prefix is computed once per KV head instead of
 // once per sequence: the score tile's 16 columns are (sequence, head) pairs,
-// sequence-major (16/G sequences of the G heads), a wave holds kPfxNct
-// tiles, the four waves of a workgroup take every fourth prefix block and
+// sequence-major (16/G sequences of the G heads; with G > 16, 16 heads of
+// one sequence), a wave holds kPfxNct tiles, the four waves of a workgroup take every fourth prefix block and
 // meet in LDS, and the (m, l, acc) of each row over the prefix goes to the
 // workspace; the balanced split then streams only the blocks after the
 // prefix, leaving a partial for every pair, and the merge folds the prefix
@@ -2074,20 +2175,29 @@ __global__ __launch_bounds__(kThreads) void pa_prefix_kernel(DecodeArgs a) {
   const int sg = blockIdx.x / Hkv;
   const int tid = threadIdx.x, lane = tid % 64, r = lane % 16, tq = lane / 16;
   const int wu = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int tpt = 16 / G, spg = NCT * tpt;  // sequences per tile, per workgroup
-  const int s0 = sg * spg;
+  // Columns: with G <= 16 a tile holds tpt = 16/G whole sequences; with
+  // G > 16 a tile holds 16 heads of one sequence and a workgroup's NCT tiles
+  // cover NCT*16 of its heads (hparts workgroups per sequence).
+  const bool wide = G > kTileCols;
+  const int tpt = wide ? 1 : kTileCols / G;
+  const int hparts = wide ? (G + NCT * kTileCols - 1) / (NCT * kTileCols) : 1;
+  const int spg = wide ? 1 : NCT * tpt;  // sequences per workgroup
+  const int s0 = (sg / hparts) * spg, hp = sg % hparts;
   const int ns = min(spg, a.num_seqs - s0);
   if (ns <= 0) return;
-  const int hd = g * G + r % G;
+  // column (ct, lane row r): sequence s0 + col_seq, head col_head of the group
+  auto col_seq = [&](int ct, int rr) { return wide ? 0 : (rr < tpt * G ? ct * tpt + rr / G : 1 << 30); };
+  auto col_head = [&](int ct, int rr) { return wide ? (hp * NCT + ct) * kTileCols + rr : rr % G; };
+  auto col_ok = [&](int ct, int rr) { return col_seq(ct, rr) < ns && col_head(ct, rr) < G; };
   v8 qB[NCT][NC];
   f32x4_t acc[NCT][NT];
   float mm[NCT], ll[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    const int sk = (r < tpt * G) ? ct * tpt + r / G : 1 << 30;
-    const bool ok = sk < ns;
+    const bool ok = col_ok(ct, r);
+    const int sk = ok ? col_seq(ct, r) : 0, hd = g * G + (ok ? col_head(ct, r) : 0);
     const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
-                                                            ((int64_t)(s0 + (ok ? sk : 0)) * Hq + hd) * D * 2);
+                                                            ((int64_t)(s0 + sk) * Hq + hd) * D * 2);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       u32x4_t x = qrow[4 * c + tq];
@@ -2198,9 +2308,10 @@ __global__ __launch_bounds__(kThreads) void pa_prefix_kernel(DecodeArgs a) {
   __syncthreads();
   constexpr int NQ = D / 4;
   const f32x4_t nan4 = {NAN, NAN, NAN, NAN};
-  for (int i = tid; i < ns * G * NQ; i += kThreads) {
-    const int sk = i / (G * NQ), h = (i / NQ) % G, d4 = (i % NQ) * 4;
-    const int col = (sk / tpt) * 16 + (sk % tpt) * G + h;
+  for (int i = tid; i < NCT * kTileCols * NQ; i += kThreads) {
+    const int col = i / NQ, d4 = (i % NQ) * 4;
+    if (!col_ok(col / kTileCols, col % kTileCols)) continue;
+    const int sk = col_seq(col / kTileCols, col % kTileCols), h = col_head(col / kTileCols, col % kTileCols);
     f32x4_t num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) num += sm.fac[w][col] * *reinterpret_cast<const f32x4_t *>(&sm.acc[w][col][d4]);
@@ -2493,14 +2604,30 @@ bool use_mfma(const pa_decode_params *p) {
   return p->kernel == PA_KERNEL_MFMA || (p->kernel == PA_KERNEL_AUTO && p->kv_dtype != PA_F32);
 }
 
-// Workgroups per CU the balanced kernel aims for with this cache type.
-int balanced_wg_per_cu(pa_dtype kv) {
-  return kv == PA_FP8 ? PA_FP8_WG_PER_CU : kv == PA_I8 ? PA_I8_WG_PER_CU : PA_BALANCED_WG_PER_CU;
+// Partition workgroups per (partition, KV head, sequence): the vector-ALU
+// kernel takes at most 16 heads per workgroup, the matrix-core kernel all G.
+int head_chunks(const pa_decode_params *p) {
+  const int G = p->num_q_heads / p->num_kv_heads;
+  return use_mfma(p) ? 1 : (G + kTileCols - 1) / kTileCols;
 }
+
+// Shared-prefix workgroups per KV head for S sequences of G query heads:
+// kPfxNct score tiles each, a tile holding 16/G whole sequences (G <= 16) or
+// 16 heads of one sequence.
+int prefix_workgroups(int S, int G) {
+  if (G > kTileCols) return S * ((G + kPfxNct * kTileCols - 1) / (kPfxNct * kTileCols));
+  const int spg = kPfxNct * (kTileCols / G);
+  return (S + spg - 1) / spg;
+}
+
+// Matrix-core column tiles for G query heads per KV head: ceil(G / 16),
+// rounded up to 1, 2 or 4 (the instantiated kernels).
+int nct_of(int G) { return G <= kTileCols ? 1 : G <= 2 * kTileCols ? 2 : 4; }
 
 // Parking slots per wave: as many as the LDS left beside the kernel's own
 // shared memory allows (per workgroup, with wg_per_cu workgroups on a CU),
-// at least 1, at most kParkSlotsMax.
+// at most kParkSlotsMax; none when a slot does not fit (every segment then
+// stores as it ends).
 int park_slots(int G, int D, int wg_per_cu) {
   static int lds_block[64] = {}, lds_cu[64] = {};
   int dev = 0, per_block = 64 * 1024, per_cu = 64 * 1024;
@@ -2524,50 +2651,70 @@ int park_slots(int G, int D, int wg_per_cu) {
   const int64_t budget = std::min<int64_t>(per_block, per_cu / std::max(wg_per_cu, 1)) -
                          (int64_t)sizeof(SmemBalanced) - 2048;
   const int64_t slot = (int64_t)kBWaves * park_slot_floats(G, D) * sizeof(float);
-  return (int)std::max<int64_t>(1, std::min<int64_t>(kParkSlotsMax, budget / slot));
+  return (int)std::max<int64_t>(0, std::min<int64_t>(kParkSlotsMax, budget / slot));
 }
 
 size_t park_bytes(int G, int D, int slots) {
   return (size_t)kBWaves * slots * park_slot_floats(G, D) * sizeof(float);
 }
 
-int balanced_park_slots(pa_dtype kv, int G, int D) {
-  return park_slots(G, D, balanced_wg_per_cu(kv));
+// The balanced kernel for a cache type, q type, head size and group size,
+// with the workgroups per CU it is built for.
+struct BalancedKernel {
+  const void *fn;
+  int wg_per_cu;
+};
+
+template <class W, int D>
+BalancedKernel kinfo() {
+  return {reinterpret_cast<const void *>(&pa_balanced_kernel<W, D>), W::kBalWgPerCu};
 }
 
-// The balanced kernel for a cache type, q type and head size.
-template <class W, int D>
-const void *kfn() { return reinterpret_cast<const void *>(&pa_balanced_kernel<W, D>); }
-
-const void *balanced_kernel(pa_dtype kv, pa_dtype qt, int D) {
+template <int NCT>
+BalancedKernel balanced_kernel_nct(pa_dtype kv, pa_dtype qt, int D) {
   if (kv == PA_I8) {
-    if (qt == PA_BF16) return D == 128 ? kfn<MfmaWaveI8<PA_BF16, 128>, 128>() : kfn<MfmaWaveI8<PA_BF16, 64>, 64>();
-    return D == 128 ? kfn<MfmaWaveI8<PA_F16, 128>, 128>() : kfn<MfmaWaveI8<PA_F16, 64>, 64>();
+    if (qt == PA_BF16)
+      return D == 128 ? kinfo<MfmaWaveI8<PA_BF16, 128, PA_I8, NCT>, 128>() : kinfo<MfmaWaveI8<PA_BF16, 64, PA_I8, NCT>, 64>();
+    return D == 128 ? kinfo<MfmaWaveI8<PA_F16, 128, PA_I8, NCT>, 128>() : kinfo<MfmaWaveI8<PA_F16, 64, PA_I8, NCT>, 64>();
   }
   if (kv == PA_FP8) {
     if (qt == PA_BF16)
-      return D == 128 ? kfn<MfmaWaveI8<PA_BF16, 128, PA_FP8>, 128>() : kfn<MfmaWaveI8<PA_BF16, 64, PA_FP8>, 64>();
-    return D == 128 ? kfn<MfmaWaveI8<PA_F16, 128, PA_FP8>, 128>() : kfn<MfmaWaveI8<PA_F16, 64, PA_FP8>, 64>();
+      return D == 128 ? kinfo<MfmaWaveI8<PA_BF16, 128, PA_FP8, NCT>, 128>()
+                      : kinfo<MfmaWaveI8<PA_BF16, 64, PA_FP8, NCT>, 64>();
+    return D == 128 ? kinfo<MfmaWaveI8<PA_F16, 128, PA_FP8, NCT>, 128>() : kinfo<MfmaWaveI8<PA_F16, 64, PA_FP8, NCT>, 64>();
   }
-  if (kv == PA_BF16) return D == 128 ? kfn<MfmaWave<PA_BF16, 128>, 128>() : kfn<MfmaWave<PA_BF16, 64>, 64>();
-  return D == 128 ? kfn<MfmaWave<PA_F16, 128>, 128>() : kfn<MfmaWave<PA_F16, 64>, 64>();
+  if (kv == PA_BF16)
+    return D == 128 ? kinfo<MfmaWave<PA_BF16, 128, NCT>, 128>() : kinfo<MfmaWave<PA_BF16, 64, NCT>, 64>();
+  return D == 128 ? kinfo<MfmaWave<PA_F16, 128, NCT>, 128>() : kinfo<MfmaWave<PA_F16, 64, NCT>, 64>();
 }
 
-// Workgroups of the balanced grid: balanced_wg_per_cu per CU (checked
-// against the kernel's occupancy with its parking LDS for G query heads per
-// KV head where a device answers).
+BalancedKernel balanced_kernel(pa_dtype kv, pa_dtype qt, int D, int G) {
+  switch (nct_of(G)) {
+    case 1: return balanced_kernel_nct<1>(kv, qt, D);
+    case 2: return balanced_kernel_nct<2>(kv, qt, D);
+    default: return balanced_kernel_nct<4>(kv, qt, D);
+  }
+}
+
+int balanced_park_slots(pa_dtype kv, pa_dtype qt, int G, int D) {
+  return park_slots(G, D, balanced_kernel(kv, qt, D, G).wg_per_cu);
+}
+
+// Workgroups of the balanced grid: the kernel's workgroups per CU (checked
+// against its occupancy with its parking LDS for G query heads per KV head
+// where a device answers).
 int balanced_workgroups(pa_dtype kv, pa_dtype qt, int D, int G) {
   static int cached[64][12][kGMax + 1] = {};
   int dev = 0;
   const bool bytes = byte_cache(kv);
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-    return balanced_wg_per_cu(kv) * cu_count();
+  const BalancedKernel bk = balanced_kernel(kv, qt, D, G);
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return bk.wg_per_cu * cu_count();
   const int k = (kv == PA_I8 ? 4 : kv == PA_FP8 ? 8 : 0) + ((bytes ? qt : kv) == PA_BF16 ? 0 : 2) + (D == 128 ? 0 : 1);
   if (!cached[dev][k][G]) {
-    const int want = balanced_wg_per_cu(kv);
+    const int want = bk.wg_per_cu;
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, balanced_kernel(kv, qt, D), kBThreads,
-                                                     park_bytes(G, D, balanced_park_slots(kv, G, D))) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bk.fn, kBThreads,
+                                                     park_bytes(G, D, balanced_park_slots(kv, qt, G, D))) !=
             hipSuccess ||
         per_cu <= 0)
       per_cu = want;
@@ -2690,11 +2837,18 @@ const void *valu_kernel(int G) {
   return reinterpret_cast<const void *>(&pa_partition_kernel<ValuWave<DT, D, 16>, D, false>);
 }
 
+template <int DT, int D>
+const void *mfma_partition_kernel(int G) {
+  switch (nct_of(G)) {
+    case 1: return reinterpret_cast<const void *>(&pa_partition_kernel<MfmaWave<DT, D, 1>, D, true>);
+    case 2: return reinterpret_cast<const void *>(&pa_partition_kernel<MfmaWave<DT, D, 2>, D, true>);
+    default: return reinterpret_cast<const void *>(&pa_partition_kernel<MfmaWave<DT, D, 4>, D, true>);
+  }
+}
+
 template <int D>
 const void *partition_kernel(pa_dtype dt, bool mfma, int G) {
-  if (mfma)
-    return dt == PA_BF16 ? reinterpret_cast<const void *>(&pa_partition_kernel<MfmaWave<PA_BF16, D>, D, true>)
-                         : reinterpret_cast<const void *>(&pa_partition_kernel<MfmaWave<PA_F16, D>, D, true>);
+  if (mfma) return dt == PA_BF16 ? mfma_partition_kernel<PA_BF16, D>(G) : mfma_partition_kernel<PA_F16, D>(G);
   if (dt == PA_BF16) return valu_kernel<PA_BF16, D>(G);
   if (dt == PA_F16) return valu_kernel<PA_F16, D>(G);
   return valu_kernel<PA_F32, D>(G);
@@ -2732,7 +2886,7 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
   const bool bal = use_balanced(p);
   const int32_t pt = bal ? 0 : resolve_partition(p);
   const int32_t np = bal ? 1 : num_partitions(p, pt);
-  if ((int64_t)np * p->num_kv_heads * p->num_seqs > INT32_MAX)
+  if ((int64_t)np * p->num_kv_heads * p->num_seqs * head_chunks(p) > INT32_MAX)
     return pa::fail(PA_ERR_UNSUPPORTED, "%s: more than 2^31-1 workgroups (raise partition_tokens)", who);
   const size_t need = pa_decode_workspace_bytes(p);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
@@ -2772,7 +2926,7 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
       a.ws_pfx_acc = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pfx_off + round16(rows * 2 * 4));
     }
     a.num_workers = kBWaves * balanced_workgroups(p);
-    a.park_slots = balanced_park_slots(p->kv_dtype, p->num_q_heads / p->num_kv_heads, p->head_dim);
+    a.park_slots = balanced_park_slots(p->kv_dtype, p->q_dtype, p->num_q_heads / p->num_kv_heads, p->head_dim);
   }
 
   a.num_seqs = p->num_seqs;
@@ -2796,8 +2950,7 @@ pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipS
   if (use_balanced(p)) {
     LaunchEvents bev = ev;
     if (a.prefix_blocks > 0) {  // every row's attention over the shared prefix first
-      const int spg = kPfxNct * (16 / a.group);
-      const dim3 pgrid((unsigned)(p->num_kv_heads * ((p->num_seqs + spg - 1) / spg)));
+      const dim3 pgrid((unsigned)(p->num_kv_heads * prefix_workgroups(p->num_seqs, a.group)));
       const void *pfn = p->kv_dtype == PA_BF16
                             ? (p->head_dim == 128 ? reinterpret_cast<const void *>(&pa_prefix_kernel<PA_BF16, 128>)
                                                   : reinterpret_cast<const void *>(&pa_prefix_kernel<PA_BF16, 64>))
@@ -2813,13 +2966,13 @@ pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipS
     }
     const dim3 grid((unsigned)(a.num_workers / kBWaves));
     const size_t lds = park_bytes(a.group, p->head_dim, a.park_slots);
-    hipError_t e = launch_kernel(balanced_kernel(p->kv_dtype, p->q_dtype, p->head_dim), grid,
+    hipError_t e = launch_kernel(balanced_kernel(p->kv_dtype, p->q_dtype, p->head_dim, a.group).fn, grid,
                                  dim3(kBThreads), args, lds, hs, bev);
     if (e != hipSuccess) return hip_check(e, "pa_decode balanced launch");
     return hip_check(hipGetLastError(), "pa_decode balanced launch");
   }
   const bool mfma = use_mfma(p);
-  const dim3 grid((unsigned)((int64_t)a.max_parts * p->num_kv_heads * p->num_seqs));
+  const dim3 grid((unsigned)((int64_t)a.max_parts * p->num_kv_heads * p->num_seqs * head_chunks(p)));
   const void *fn = p->head_dim == 128 ? partition_kernel<128>(p->kv_dtype, mfma, a.group)
                                       : partition_kernel<64>(p->kv_dtype, mfma, a.group);
   hipError_t e = launch_kernel(fn, grid, dim3(kThreads), args, 0, hs, ev);
@@ -3191,7 +3344,7 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst_pa
 namespace {
 
 struct ExtendShape {
-  int nct, tpt, tpg, qgroups, pt, np;
+  int nct, tpt, tpg, hparts, qgroups, pt, np;
 };
 
 pa_status validate_extend(const pa_extend_params *p) {
@@ -3208,8 +3361,8 @@ pa_status validate_extend(const pa_extend_params *p) {
     return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: num_seqs must be in [0, 65535], num_query_rows >= 0");
   if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads || p->num_kv_heads > 65535)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_extend: num_q_heads must be a positive multiple of num_kv_heads");
-  if (p->num_q_heads / p->num_kv_heads > 16)
-    return pa::fail(PA_ERR_UNSUPPORTED, "pa_extend: at most 16 query heads per KV head");
+  if (p->num_q_heads / p->num_kv_heads > kGMax)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_extend: at most %d query heads per KV head", kGMax);
   if (p->head_dim != 64 && p->head_dim != 128)
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_extend: head_dim must be 64 or 128");
   if (p->kv_dtype != PA_F16 && p->kv_dtype != PA_BF16)
@@ -3229,10 +3382,18 @@ ExtendShape extend_shape(const pa_extend_params *p) {
   ExtendShape e;
   const int G = p->num_q_heads / p->num_kv_heads;
   const int mq = std::max(p->max_query_len, 1);
-  e.tpt = 16 / G;
-  e.nct = (int64_t)mq * G > 16 ? kExtNctMax : 1;
-  e.tpg = e.nct * e.tpt;
-  e.qgroups = (mq + e.tpg - 1) / e.tpg;
+  if (G > kTileCols) {  // a token's heads span tiles: NCT * 16 heads of one token per query group
+    e.tpt = 1;
+    e.nct = kExtNctMax;
+    e.tpg = 1;
+    e.hparts = (G + e.nct * kTileCols - 1) / (e.nct * kTileCols);
+  } else {
+    e.tpt = kTileCols / G;
+    e.nct = (int64_t)mq * G > kTileCols ? kExtNctMax : 1;
+    e.tpg = e.nct * e.tpt;
+    e.hparts = 1;
+  }
+  e.qgroups = (mq + e.tpg - 1) / e.tpg * e.hparts;
   const int ctx = ((std::max(p->max_context_len, 1) + kBS - 1) / kBS) * kBS;
   if (p->partition_tokens > 0) {
     e.pt = p->partition_tokens;
@@ -3319,6 +3480,7 @@ pa_status pa_extend(const pa_extend_params *p, void *workspace, size_t workspace
   a.qgroups = e.qgroups;
   a.tpt = e.tpt;
   a.tpg = e.tpg;
+  a.hparts = e.hparts;
   a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
   const bool merge = e.np > 1;
   LaunchEvents first, second;

@@ -70,7 +70,8 @@ def named(n: int) -> Spec:
     """The measured workloads (1-based; 6 and 8 are workload 3 over an INT8 and an
     FP8 cache; 7 is a Mistral-7B-shaped batch under a 4096-token sliding window;
     9 and 10 are one GPU's share of workloads 3 and 5 when they are sharded over
-    eight GPUs by KV head and by context)."""
+    eight GPUs by KV head and by context; 11 is multi-query attention, 32 query
+    heads on one shared KV head)."""
     if n == 1:
         return Spec("tiny-fp32-mha-d64", 1, "f32", "f32", 4, 4, 4, 64, 64,
                     lens=[1, 17, 33, 100], scale=1.0 / 8.0)
@@ -101,6 +102,9 @@ def named(n: int) -> Spec:
     if n == 10:  # one GPU's share of workload 5 under 8-way context parallelism: 4096 tokens each
         return Spec("long-ctx-cp8share-gqa4-bf16-b4-l4096", 5, "bf16", "bf16", 4, 32, 8, 128,
                     1024 + 64, lens=[4096] * 4)
+    if n == 11:  # multi-query attention: the Llama-3-8B shape with one KV head shared by all 32 q heads
+        return Spec("llama3-8b-mqa32-bf16-b256-l128to4096", 11, "bf16", "bf16", 256, 32, 1, 128,
+                    0, len_range=(128, 4096))
     raise ValueError(f"no workload {n}")
 
 

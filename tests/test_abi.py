@@ -151,7 +151,7 @@ def test_small_batches_take_partitions_unless_the_balanced_split_is_asked_for():
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 96, pa.PA_ERR_UNSUPPORTED),
     ("num_kv_heads", 7, pa.PA_ERR_INVALID_ARG),
-    ("num_q_heads", 256, pa.PA_ERR_UNSUPPORTED),
+    ("num_q_heads", 8 * 65, pa.PA_ERR_UNSUPPORTED),
     ("partition_tokens", 24, pa.PA_ERR_INVALID_ARG),
     ("out_dtype", pa.PA_F16, pa.PA_ERR_UNSUPPORTED),
     ("q", ctypes.c_void_p(33), pa.PA_ERR_INVALID_ARG),
@@ -290,7 +290,7 @@ def _ext(**over):
     ("out", ctypes.c_void_p(17), pa.PA_ERR_INVALID_ARG),
     ("kv_dtype", pa.PA_F32, pa.PA_ERR_UNSUPPORTED),
     ("kv_dtype", pa.PA_I8, pa.PA_ERR_UNSUPPORTED),
-    ("num_q_heads", 8 * 17, pa.PA_ERR_UNSUPPORTED),
+    ("num_q_heads", 8 * 65, pa.PA_ERR_UNSUPPORTED),
     ("num_kv_heads", 7, pa.PA_ERR_INVALID_ARG),
     ("head_dim", 96, pa.PA_ERR_UNSUPPORTED),
     ("out_dtype", pa.PA_F16, pa.PA_ERR_UNSUPPORTED),
