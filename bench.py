@@ -17,11 +17,21 @@ placement) so the working set is several times the 256 MB Infinity Cache.
 
 Prints one JSON line.  value = decode tokens/s (one token per sequence per
 step) over the timed steps, wall clock between device synchronizations.
-roofline = the attention kernel (balanced split, or partitions when
-  --partition-tokens is set; with a shared prefix, the prefix kernel and the
-  split together): algorithmic bytes per launch / its mean duration from HIP
-  events recorded around it on its stream.
-cpu_baseline = the fp64 CPU oracle on whole-batch passes of the same workload.
+roofline = the decode: the attention launch (balanced split or partitions;
+  with a shared prefix, the prefix kernel and the split together) and the
+  merge launch, from the first dispatch's start to the merge's end, taken
+  with HIP events on the dispatches of at least 10 timed steps: algorithmic
+  bytes per step / that duration.  roofline.kernel_only is the attention
+  launch alone.  max_abs_err compares sampled rows of the last timed step's
+  output with the fp64 oracle, which rebuilds those sequences from the
+  workload's rows.
+cpu_baseline = the fp64 CPU oracle on whole-batch passes of the same workload
+  (OpenMP), plus a single-threaded figure on a sample of its sequences.
+
+A workload that is a decode loop (workload 5: 4 x 32768 tokens, 128 steps,
+512-token partitions) runs exactly its steps on one pool (its 537 MB per step
+is twice the Infinity Cache), after --warmup decode launches without appends,
+and adds the whole loop's tokens/s and GB/s.
 """
 from __future__ import annotations
 
@@ -57,7 +67,9 @@ def kernel_source_hash() -> str:
 
 def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` on `workload` from committed rocprofv3
-    counter runs, or None when the kernel source changed since they were taken."""
+    counter runs, or None when the kernel source changed since they were taken.
+    With the counter run's own algorithmic bytes per launch in the record, the
+    result is a dict {"hbm": bytes, "algorithmic": bytes}; else just the bytes."""
     path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -69,9 +81,35 @@ def read_traffic(kernel: str, workload: str):
     if kv.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     try:
-        return float(kv["hbm_bytes_per_dispatch"])
+        hbm = float(kv["hbm_bytes_per_dispatch"])
     except (KeyError, ValueError):
         return None
+    try:
+        return {"hbm": hbm, "algorithmic": float(kv["algorithmic_bytes_per_dispatch"])}
+    except (KeyError, ValueError):
+        return hbm
+
+
+def traffic_bytes(rec):
+    return None if rec is None else (rec["hbm"] if isinstance(rec, dict) else rec)
+
+
+def timing_stats(ms) -> dict:
+    """mean, median, p10 and p90 in microseconds of launch durations in ms."""
+    us = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"mean_us": round(float(us.mean()), 2), "median_us": round(float(np.median(us)), 2),
+            "p10_us": round(float(np.percentile(us, 10)), 2), "p90_us": round(float(np.percentile(us, 90)), 2),
+            "timed_launches": int(us.size)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ---------------------------------------------------------------- GPU side
@@ -201,14 +239,17 @@ def build_replica(pa, torch, wl, order, k_rows_d, v_rows_d, MB, S, dev):
     return rep
 
 
-def run_gpu(args, wl):
+def run_gpu(args, wl, loop=False):
+    """loop: the workload is a decode loop -- the --warmup launches decode the
+    prompt state without appending, then exactly --steps steps append and attend."""
     import torch
     from paged_kv_cache_65_amd import binding as pa
     L = pa.lib()
     spec = wl.spec
     dev = torch.device("cuda:0")
     S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
-    W, K, R = args.warmup, args.steps, args.replicas
+    K, R = args.steps, args.replicas
+    W = 0 if loop else args.warmup          # warmup steps of the step loop (they append too)
     MB = int(-(-(int(wl.prompt_lens.max()) + W + K) // 16))
     dt_code = {"f32": pa.PA_F32, "f16": pa.PA_F16, "bf16": pa.PA_BF16}[spec.dtype]
 
@@ -295,7 +336,9 @@ def run_gpu(args, wl):
     ncow_c = ctypes.c_int32()
     row_bytes = S * Hkv * D * step_k_d.element_size()
     nb_rep = nb_pool
-    every = max(1, args.time_every)
+    # events ride on the dispatches of every `every`-th step: at least 10 timed
+    # launches whatever --steps is (each event costs a few us of stream time)
+    every = args.time_every if args.time_every > 0 else max(1, min(10, K // 10))
     markers = args.event_markers
     n_timed = (K + every - 1) // every
     ev_a = [hip.event(timing=True) for _ in range(n_timed)]
@@ -410,16 +453,26 @@ def run_gpu(args, wl):
             prm.start_event = None
             prm.stop_event = ev_c[timed_idx] if timed_idx >= 0 else done
             pa._check(L.pa_decode_merge(ctypes.byref(prm), ws_ptr, ws_bytes, cs))
-        if timed_idx >= 0:
-            lens_log.append(pp["lens_np"].copy())
+        lens_log.append((timed_idx >= 0, pp["lens_np"].copy()))
 
+    if loop and args.warmup > 0:
+        # decode launches on the prompt state (no append), for warm code and caches
+        for rep in reps:
+            tab, lens = rep.pool.seq_export(rep.seq_ids, MB)
+            tab_d, lens_d = torch.from_numpy(tab).to(dev), torch.from_numpy(lens).to(dev)
+            for _ in range(args.warmup):
+                pa.pa_decode(rep.out, q_d, rep.k_cache, rep.v_cache, tab_d, lens_d, Hkv, int(lens.max()),
+                             spec.fp32_scale(), partition_tokens=args.partition_tokens, kernel=args.kernel,
+                             k_scales=rep.k_scales, v_scales=rep.v_scales, sliding_window=spec.window,
+                             shared_prefix_blocks=shared_prefix)
+        torch.cuda.synchronize()
     total = W + K
     prepare(0)
     for i in range(W):
         launch(i, -1)
         prepare(i + 1)
     hip.sync_device()
-    log(f"warmup done ({W} steps); timing {K} steps")
+    log(f"warmup done ({args.warmup} {'decode launches' if loop else 'steps'}); timing {K} steps")
     waited[0] = 0.0
     t0 = time.perf_counter()
     host = 0.0
@@ -436,42 +489,98 @@ def run_gpu(args, wl):
     elapsed = t1 - t0
     part_ms = np.array([hip.elapsed_ms(ev_a[k], ev_b[k]) for k in range(n_timed)])
     decode_ms = None if markers else np.array([hip.elapsed_ms(ev_a[k], ev_c[k]) for k in range(n_timed)])
-    alg_bytes = [accounting.decode_algorithmic_bytes(l, Hq, Hkv, D, spec.dtype, spec.out_dtype, cache=spec.cache,
-                                                     shared_tokens=spec.prefix_len, window=spec.window)
-                 for l in lens_log]
-    log(f"timed {K} steps in {elapsed * 1e3:.2f} ms; partition kernel mean {part_ms.mean() * 1e3:.1f} us")
+
+    def alg_of(lens):
+        return accounting.decode_algorithmic_bytes(lens, Hq, Hkv, D, spec.dtype, spec.out_dtype, cache=spec.cache,
+                                                   shared_tokens=spec.prefix_len, window=spec.window)
+    alg_bytes = [alg_of(l) for timed, l in lens_log if timed]
+    alg_timed_steps = [alg_of(l) for timed, l in lens_log[W:]]   # every step of the timed region
+    log(f"timed {K} steps in {elapsed * 1e3:.2f} ms; attention launch mean {part_ms.mean() * 1e3:.1f} us")
+    # the last step's output (its replica's out was last written by it) and the
+    # steps whose rows that replica's sequences appended, for the oracle check
+    last = total - 1
+    last_out = reps[last % R].out.float().cpu().numpy()
     return {
-        "elapsed": elapsed, "part_ms": part_ms, "decode_ms": decode_ms, "alg": alg_bytes, "part_tokens": part_tokens,
+        "elapsed": elapsed, "part_ms": part_ms, "decode_ms": decode_ms, "alg": alg_bytes,
+        "alg_all": alg_timed_steps, "part_tokens": part_tokens,
         "max_blocks": MB, "S": S,
         "append_bytes": accounting.append_bytes(S, Hkv, D, spec.dtype, spec.cache),
         "device": torch.cuda.get_device_name(0),
+        "last_out": last_out, "last_steps": list(range(last % R, last + 1, R)), "every": every,
     }
 
 
 # ---------------------------------------------------------------- CPU oracle leg
+class OracleCaches:
+    """The oracle's K/V pool of a workload's cache type (16-bit, INT8 or FP8)."""
+
+    def __init__(self, spec, num_blocks):
+        import oracle
+        self.o, self.spec, self.nb = oracle, spec, num_blocks
+        Hkv, D, dt = spec.num_kv_heads, spec.head_dim, spec.dtype
+        self.i8, self.fp8 = spec.cache in ("i8", "fp8"), spec.cache == "fp8"
+        if self.i8:
+            empty = oracle.empty_cache_fp8 if self.fp8 else oracle.empty_cache_i8
+            self.kc, self.ks = empty(num_blocks, Hkv, D)
+            self.vc, self.vs = empty(num_blocks, Hkv, D)
+        else:
+            self.kc = oracle.empty_cache(num_blocks, Hkv, D, dt)
+            self.vc = oracle.empty_cache(num_blocks, Hkv, D, dt)
+
+    def put(self, k, v, slots):
+        o, sp = self.o, self.spec
+        if self.i8:
+            (o.reshape_and_cache_fp8 if self.fp8 else o.reshape_and_cache_i8)(
+                k, v, self.kc, self.vc, self.ks, self.vs, slots, sp.num_kv_heads, sp.head_dim, self.nb, sp.dtype)
+        else:
+            o.reshape_and_cache(k, v, self.kc, self.vc, slots, sp.num_kv_heads, sp.head_dim, self.nb, sp.dtype)
+
+    def decode(self, q, tab, lens, nthreads=0):
+        """(fp64 output, threads used)."""
+        o, sp = self.o, self.spec
+        if self.i8:
+            return o.decode_i8(q, sp.dtype, self.kc, self.vc, self.ks, self.vs, tab, lens, sp.num_kv_heads,
+                               sp.fp32_scale(), nthreads=nthreads, return_threads=True, window=sp.window,
+                               fp8=self.fp8)
+        return o.decode(q, self.kc, self.vc, tab, lens, sp.num_kv_heads, sp.fp32_scale(), sp.dtype,
+                        nthreads=nthreads, return_threads=True, window=sp.window)
+
+
+def oracle_sample(wl, seqs, step_ids):
+    """The fp64 oracle's output rows of sequences `seqs` after the decode steps
+    `step_ids` appended their rows: each sequence is rebuilt alone from the
+    workload's rows (prompt, then one row per step) in an oracle pool and
+    decoded by the oracle's table walk."""
+    import oracle
+    from oracle.pool_model import PoolModel
+    oracle.build()
+    spec = wl.spec
+    outs = []
+    for s in seqs:
+        k = np.concatenate([wl.seq_rows(s, "k")] + [wl.step_k[j, s][None] for j in step_ids])
+        v = np.concatenate([wl.seq_rows(s, "v")] + [wl.step_v[j, s][None] for j in step_ids])
+        n = len(k)
+        mb = -(-n // 16)
+        pool = PoolModel(mb + 1, 16, np.arange(mb + 1, dtype=np.int32))
+        sid = pool.seq_create()
+        slots, _ = pool.seq_append(sid, n)
+        caches = OracleCaches(spec, mb + 1)
+        caches.put(np.ascontiguousarray(k), np.ascontiguousarray(v), slots)
+        tab, lens = pool.export([sid], mb)
+        out, _ = caches.decode(np.ascontiguousarray(wl.q[s:s + 1]), np.array(tab, np.int32).reshape(1, mb),
+                               np.array(lens, np.int32))
+        outs.append(out[0])
+    return np.stack(outs)
+
+
 def run_cpu_baseline(wl, seconds):
     import oracle
     from oracle.pool_model import PoolModel
     oracle.build()
     spec = wl.spec
-    Hkv, D, dt = spec.num_kv_heads, spec.head_dim, spec.dtype
     pool = PoolModel(wl.num_blocks, 16, wl.free_order)
-    i8 = spec.cache in ("i8", "fp8")
-    fp8 = spec.cache == "fp8"
-    if i8:
-        empty = oracle.empty_cache_fp8 if fp8 else oracle.empty_cache_i8
-        kc, ks = empty(wl.num_blocks, Hkv, D)
-        vc, vs = empty(wl.num_blocks, Hkv, D)
-    else:
-        kc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
-        vc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
-
-    def put(k, v, sl):
-        if i8:
-            (oracle.reshape_and_cache_fp8 if fp8 else oracle.reshape_and_cache_i8)(
-                k, v, kc, vc, ks, vs, sl, Hkv, D, wl.num_blocks, dt)
-        else:
-            oracle.reshape_and_cache(k, v, kc, vc, sl, Hkv, D, wl.num_blocks, dt)
+    caches = OracleCaches(spec, wl.num_blocks)
+    put = caches.put
     owner = -1
     if spec.prefix_len:
         owner = pool.seq_create()
@@ -490,15 +599,22 @@ def run_cpu_baseline(wl, seconds):
     passes, used = 0, 0
     t0 = time.perf_counter()
     while True:
-        if i8:
-            _, used = oracle.decode_i8(wl.q, dt, kc, vc, ks, vs, tab, lens, Hkv, spec.fp32_scale(),
-                                       nthreads=0, return_threads=True, window=spec.window, fp8=fp8)
-        else:
-            _, used = oracle.decode(wl.q, kc, vc, tab, lens, Hkv, spec.fp32_scale(), dt,
-                                    nthreads=0, return_threads=True, window=spec.window)
+        _, used = caches.decode(wl.q, tab, lens)
         passes += 1
         el = time.perf_counter() - t0
         if el >= seconds:
+            break
+    # one thread: the leading sequences holding about an eighth of the batch's tokens
+    m = int(np.searchsorted(np.cumsum(lens), max(1, int(lens.sum()) // 8))) + 1
+    m = min(max(m, 1), spec.num_seqs)
+    q1 = np.ascontiguousarray(wl.q[:m])
+    passes1 = 0
+    t1 = time.perf_counter()
+    while True:
+        caches.decode(q1, tab[:m], lens[:m], nthreads=1)
+        passes1 += 1
+        el1 = time.perf_counter() - t1
+        if el1 >= seconds / 2:
             break
     return {
         "value": round(spec.num_seqs * passes / el, 3), "unit": "tokens/s", "cores": int(used),
@@ -506,6 +622,10 @@ def run_cpu_baseline(wl, seconds):
         "sample": f"{passes} whole-batch fp64 decode passes of the same workload "
                   f"({spec.num_seqs} sequences, prompt contexts, sum L={int(lens.sum())}) "
                   f"in {el:.1f} s, OpenMP over (sequence, head)",
+        "single_thread": {"value": round(m * passes1 / el1, 3), "unit": "tokens/s", "cores": 1,
+                          "sample": f"{passes1} passes over sequences 0-{m - 1} (sum L={int(lens[:m].sum())}) "
+                                    f"in {el1:.1f} s on one thread"},
+        "cpu_model": cpu_model(),
     }
 
 
@@ -664,17 +784,20 @@ def step_description(fused, cache, shared_prefix):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 200; a decode-loop workload: its own step count)")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=3, choices=list(range(1, 11)))
-    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, choices=list(range(1, 12)))
+    ap.add_argument("--replicas", type=int, default=None,
+                    help="independent pools in rotation (default 3; a decode-loop workload: 1)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
-    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--partition-tokens", type=int, default=None,
+                    help="0 = automatic, -1 = balanced split, else a multiple of 16 (default: the workload's)")
     ap.add_argument("--append", default="fused", choices=["fused", "separate"],
                     help="append the step's K/V inside the decode launch, or with pa_reshape_and_cache")
-    ap.add_argument("--time-every", type=int, default=10, metavar="N",
-                    help="bracket every N-th attention launch with timing events (the event markers "
-                         "themselves cost stream time)")
+    ap.add_argument("--time-every", type=int, default=0, metavar="N",
+                    help="bracket every N-th step's launches with timing events (default: often enough "
+                         "for at least 10 timed launches; the events themselves cost stream time)")
     ap.add_argument("--event-markers", action="store_true",
                     help="record the timing and completion events as separate stream markers "
                          "(hipEventRecord) instead of on the kernel dispatches")
@@ -703,7 +826,14 @@ def main():
         run_swap_bench(args.swap, 10)
         return
     base = workloads.named(args.workload)
-    spec = dataclasses.replace(base, decode_steps=args.warmup + args.steps)
+    loop = base.decode_steps > 0 and not args.extend   # a decode loop: its own steps, one pool
+    if args.steps is None:
+        args.steps = base.decode_steps if loop else 200
+    if args.replicas is None:
+        args.replicas = 1 if loop else 3
+    if args.partition_tokens is None:
+        args.partition_tokens = base.partition_tokens
+    spec = dataclasses.replace(base, decode_steps=args.steps if loop else args.warmup + args.steps)
     t = time.perf_counter()
     wl = workloads.generate(spec)
     log(f"workload {spec.name} generated in {time.perf_counter() - t:.1f} s "
@@ -711,22 +841,56 @@ def main():
     if args.extend:
         run_extend_bench(args, wl, args.extend)
         return
-    g = run_gpu(args, wl)
+    g = run_gpu(args, wl, loop=loop)
     K = args.steps
     tok_s = spec.num_seqs * K / g["elapsed"]
     mean_alg = float(np.mean([a["total"] for a in g["alg"]]))
     row_bytes = (spec.head_dim + accounting.I8_SCALE_BYTES) if spec.cache in ("i8", "fp8") else \
         spec.head_dim * accounting.ELEM_BYTES[spec.dtype]
     mean_kv_tokens = float(np.mean([a["kv_logical"] for a in g["alg"]])) / (2 * spec.num_kv_heads * row_bytes)
-    part_s = float(g["part_ms"].mean()) / 1e3
-    achieved = mean_alg / part_s / 1e9
+    part = timing_stats(g["part_ms"])
     step_bytes = mean_alg + g["append_bytes"]
     step_gbps = step_bytes * K / g["elapsed"] / 1e9
     shared_prefix = (spec.prefix_len // 16) if (spec.prefix_len and not args.no_shared_prefix) else 0
-    kernel_name = "pa_balanced_kernel" if g["part_tokens"] == 0 else "pa_partition_kernel"
+    balanced = g["part_tokens"] == 0
+    kernel_name = "pa_balanced_kernel" if balanced else "pa_partition_kernel"
     if shared_prefix:   # the events span both launches: the prefix kernel, then the split
         kernel_name = "pa_prefix_kernel+" + kernel_name
-    traffic = read_traffic(kernel_name, spec.name)
+    merge_name = "pa_merge_balanced_kernel" if balanced else "pa_merge_kernel"
+    t_attn = read_traffic(kernel_name, spec.name)
+    t_merge = read_traffic(merge_name, spec.name)
+
+    def gbps(nbytes, us):
+        return round(nbytes / (us * 1e-6) / 1e9, 1)
+
+    kernel_only = {"kernel": kernel_name, **part, "achieved": gbps(mean_alg, part["mean_us"]),
+                   "frac": round(gbps(mean_alg, part["mean_us"]) / HBM_PEAK_GBPS, 4),
+                   "traffic": traffic_bytes(t_attn)}
+    if isinstance(t_attn, dict):
+        kernel_only["traffic_ratio"] = round(t_attn["hbm"] / t_attn["algorithmic"], 4)
+    if g["decode_ms"] is not None:
+        dec = timing_stats(g["decode_ms"])
+        # the merge launches only when some context was split; its traffic joins the attention's
+        decode_traffic = None
+        if t_attn is not None and t_merge is not None:
+            decode_traffic = traffic_bytes(t_attn) + traffic_bytes(t_merge)
+        roofline = {"kernel": f"{kernel_name}+{merge_name} (decode: attention and merge launches)",
+                    "bound": "hbm", "achieved": gbps(mean_alg, dec["mean_us"]), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(gbps(mean_alg, dec["mean_us"]) / HBM_PEAK_GBPS, 4),
+                    "traffic": decode_traffic, "algorithmic_bytes_per_launch": round(mean_alg),
+                    "mean_launch_us": dec["mean_us"], **{k: v for k, v in dec.items() if k != "mean_us"},
+                    "kernel_only": kernel_only}
+        if isinstance(t_attn, dict) and isinstance(t_merge, dict):
+            roofline["traffic_ratio"] = round(decode_traffic / t_attn["algorithmic"], 4)
+    else:                # marker events: the attention launch alone
+        roofline = {**kernel_only, "bound": "hbm", "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "algorithmic_bytes_per_launch": round(mean_alg), "mean_launch_us": part["mean_us"]}
+    # parity of a timed step: sampled rows of the last step's output against the oracle
+    S = spec.num_seqs
+    sample = sorted({0, S // 3, (2 * S) // 3, S - 1})
+    log(f"oracle check: sequences {sample} of step {args.warmup + K - 1 if not loop else K - 1}")
+    ref = oracle_sample(wl, sample, g["last_steps"])
+    err = float(np.max(np.abs(g["last_out"][sample].astype(np.float64) - ref)))
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle")
@@ -747,6 +911,9 @@ def main():
         "achieved_GBps": round(step_gbps, 1),
         "hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
         "kv_tokens_per_s": round(mean_kv_tokens * K / g["elapsed"], 1),
+        "max_abs_err": err,
+        "max_abs_err_rows": f"sequences {sample} of the last timed step, all heads, {spec.out_dtype} output "
+                            f"vs the fp64 oracle",
         "config": {
             "workload": spec.name, "num_seqs": spec.num_seqs, "num_q_heads": spec.num_q_heads,
             "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim, "block_size": 16,
@@ -756,28 +923,19 @@ def main():
             "shared_prefix_blocks": shared_prefix,
             "mean_context": round(mean_kv_tokens / spec.num_seqs, 1),
             "partition_tokens": g["part_tokens"], "replicas": args.replicas,
-            "kernel": args.kernel, "seed": spec.seed,
+            "kernel": args.kernel, "seed": spec.seed, "timed_every": g["every"],
             "step": step_description(args.append == "fused", spec.cache, shared_prefix),
             "device": g["device"],
         },
-        "roofline": {
-            "kernel": kernel_name,
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": round(mean_alg),
-            "mean_launch_us": round(part_s * 1e6, 2),
-        },
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    if g["decode_ms"] is not None:   # attention and merge launches together, same events
-        dec_s = float(g["decode_ms"].mean()) / 1e3
-        rec["decode_attention_plus_merge"] = {
-            "mean_us": round(dec_s * 1e6, 2), "achieved": round(mean_alg / dec_s / 1e9, 1), "unit": "GB/s",
-            "frac": round(mean_alg / dec_s / 1e9 / HBM_PEAK_GBPS, 4)}
+    if loop:   # the whole decode loop: every step's tokens and bytes over the loop's wall time
+        loop_bytes = float(sum(a["total"] for a in g["alg_all"])) + g["append_bytes"] * K
+        rec["loop"] = {"steps": K, "decode_tokens": S * K, "total_ms": round(g["elapsed"] * 1e3, 3),
+                       "tokens_per_s": round(tok_s, 1), "per_step_us": round(g["elapsed"] / K * 1e6, 2),
+                       "GBps": round(loop_bytes / g["elapsed"] / 1e9, 1),
+                       "algorithmic_bytes": round(loop_bytes)}
     print(json.dumps(rec), flush=True)
 
 

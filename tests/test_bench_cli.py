@@ -55,3 +55,32 @@ def test_step_description_names_the_append_each_cache_takes():
     assert "prefix attention + decode partitions" in bench.step_description(True, "", 32)
     assert "reshape_and_cache_fp8 + decode partitions" in bench.step_description(False, "fp8", 0)
     assert "reshape_and_cache + decode partitions" in bench.step_description(False, "", 0)
+
+
+def test_timing_stats_reports_mean_median_and_percentiles():
+    st = bench.timing_stats([0.001 * k for k in range(1, 101)])   # 1 .. 100 us
+    assert st["timed_launches"] == 100
+    assert abs(st["mean_us"] - 50.5) < 1e-9 and abs(st["median_us"] - 50.5) < 1e-9
+    assert abs(st["p10_us"] - 10.9) < 1e-6 and abs(st["p90_us"] - 90.1) < 1e-6
+
+
+def test_oracle_sample_rebuilds_the_rows_a_replica_attends():
+    """bench's parity check rebuilds sampled sequences from the workload's rows
+    (prompt, then the rows of the steps that replica appended); with every step
+    it must equal the oracle's decode of the whole pool after those steps, bit
+    for bit (the fp64 table walk does not depend on block placement)."""
+    import numpy as np
+    from paged_kv_cache_65_amd import workloads
+    from tests import oracle_side
+    for cache in ("", "i8"):
+        spec = workloads.custom(seed=81, dtype="bf16", lens=(3, 40, 17, 100), num_q_heads=8, num_kv_heads=2,
+                                head_dim=64, decode_steps=5, prefix_len=16, cache=cache)
+        wl = workloads.generate(spec)
+        ost = oracle_side.build(wl, steps=5)
+        mb = oracle_side.max_blocks_for(wl)
+        full = oracle_side.decode(wl, ost, mb)
+        got = bench.oracle_sample(wl, [0, 2, 3], list(range(5)))
+        assert np.array_equal(got, full[[0, 2, 3]]), cache
+        # a replica that took every other step attends to those rows only
+        part = bench.oracle_sample(wl, [1], [1, 3])
+        assert not np.array_equal(part[0], full[1])
