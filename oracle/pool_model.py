@@ -166,10 +166,21 @@ class PoolModel:
         Returns (slots, cows) with cows a list of (src, dst) in sequence order."""
         if len(set(sids)) != len(sids):
             raise PoolError("duplicate sequence in batch")
+        # blocks taken in batch order: a shared, partly filled last block is
+        # copied and loses one holder, so the last of its holders in the batch
+        # writes in place
         need = 0
+        holders = {}
         for sid in sids:
-            self._resident(sid)
-            need += self._blocks_needed(sid, 1)
+            table, ntok, _ = self._resident(sid)
+            if ntok % self.block_size == 0:
+                need += 1
+            else:
+                last = table[-1]
+                holders.setdefault(last, self.refcount[last])
+                if holders[last] > 1:
+                    need += 1
+                    holders[last] -= 1
         if need > len(self.free):
             raise OutOfBlocks("pool exhausted")
         slots, cows = [], []

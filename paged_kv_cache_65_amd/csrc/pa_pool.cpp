@@ -13,6 +13,7 @@
 // sequence's private suffix and later refills it with fresh blocks.
 #include <cstdint>
 #include <cstring>
+#include <unordered_map>
 #include <vector>
 
 #include "pa.h"
@@ -210,6 +211,11 @@ pa_status pa_seq_append_batch(pa_block_pool *pool, const int32_t *seq_ids, int32
     return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append_batch: NULL argument");
   if (n < 0) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append_batch: negative n");
   std::vector<char> seen(pool->seqs.size(), 0);
+  // Blocks the batch takes, counted as the appends below will take them: a
+  // partly filled last block shared with others is copied, and its refcount
+  // drops, so when every holder is in the batch the last one in batch order
+  // finds itself alone and writes in place.
+  std::unordered_map<int32_t, int32_t> shared_left;  // block -> refcount as the batch goes
   int64_t need = 0;
   for (int32_t i = 0; i < n; ++i) {
     int32_t sid = seq_ids[i];
@@ -219,9 +225,20 @@ pa_status pa_seq_append_batch(pa_block_pool *pool, const int32_t *seq_ids, int32
       return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append_batch: sequence %d is swapped out", sid);
     if (seen[sid]) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append_batch: duplicate sequence %d", sid);
     seen[sid] = 1;
-    if (pool->seqs[sid].tokens >= (int64_t)INT32_MAX)
+    const auto &sq = pool->seqs[sid];
+    if (sq.tokens >= (int64_t)INT32_MAX)
       return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append_batch: sequence %d is full", sid);
-    need += pool->blocks_needed(pool->seqs[sid], 1);
+    if (sq.tokens % PA_BLOCK_SIZE == 0) {
+      need += 1;  // a fresh block
+    } else {
+      const int32_t last = sq.table.back();
+      auto it = shared_left.find(last);
+      if (it == shared_left.end()) it = shared_left.emplace(last, pool->refcount[last]).first;
+      if (it->second > 1) {  // copy-on-write into a fresh block, one holder fewer
+        need += 1;
+        --it->second;
+      }
+    }
   }
   if (need > (int64_t)pool->free_stack.size())
     return pa::fail(PA_ERR_OOM, "pa_seq_append_batch: pool exhausted");

@@ -204,3 +204,18 @@ def test_random_scripts_with_swaps_match_the_model(seed):
                 pool.seq_append(sid, 1)
             assert pool.seq_num_tokens(sid) == model.seq_num_tokens(sid)
         _same(model, pool, live)
+
+
+def test_batch_with_every_holder_of_a_shared_block_matches_the_model():
+    """Parent and fork appended together on a pool with one free block: one
+    copy, the second holder writes in place (native pool = model, bit for bit)."""
+    order = np.array([2, 1, 0], dtype=np.int32)
+    model, pool = PoolModel(3, 16, order), pa.BlockPool(3, 16, order)
+    for m in (model, pool):
+        p = m.seq_create()
+        m.seq_append(p, 20)
+        m.seq_fork(p)
+    s1, c1 = model.seq_append_batch([0, 1])
+    s2, c2 = pool.seq_append_batch([0, 1])
+    assert s1 == s2.tolist() and [list(c) for c in c1] == c2.tolist() == [[1, 2]]
+    _same(model, pool, [0, 1])

@@ -234,3 +234,31 @@ def test_swap_out_keeps_a_shared_last_block():
     assert pool.seq_swap_out(a) == [] and pool.seq_swapped_blocks(a) == 0
     assert pool.seq_table(a) == pool.seq_table(b) and pool.refcount[5] == 2
     assert pool.seq_swap_in(a) == [] and pool.seq_swapped_blocks(a) == -1
+
+
+def test_a_batch_of_every_holder_of_a_shared_block_fits_a_tight_pool():
+    """Worked by hand: a parent with 20 tokens (a full block and one with 4
+    tokens) and its fork share both blocks; one block is free.  Appending one
+    token to both copies the shared partly filled block once: the first in the
+    batch takes the free block, and the second, now its only holder, writes
+    in place.  The batch fits; so would the same appends one after another."""
+    for first_parent in (True, False):
+        pool = PoolModel(3, 16, [2, 1, 0])            # pops 0, 1, 2
+        p = pool.seq_create()
+        pool.seq_append(p, 20)
+        assert pool.seq_table(p) == [0, 1]
+        c = pool.seq_fork(p)
+        assert pool.refcount[1] == 2 and pool.num_free() == 1
+        batch = [p, c] if first_parent else [c, p]
+        slots, cows = pool.seq_append_batch(batch)
+        assert cows == [(1, 2)]
+        copier, stayer = batch
+        assert pool.seq_table(copier) == [0, 2] and pool.seq_table(stayer) == [0, 1]
+        assert slots == [2 * 16 + 4, 1 * 16 + 4]
+        assert pool.refcount[1] == 1 and pool.refcount[2] == 1 and pool.num_free() == 0
+        # a third sequence needing a block of its own does not fit: nothing changes
+        snap = (list(pool.free), list(pool.refcount), pool.seq_table(p), pool.seq_table(c))
+        q = pool.seq_create()
+        with pytest.raises(OutOfBlocks):
+            pool.seq_append_batch([p, c, q])
+        assert snap == (list(pool.free), list(pool.refcount), pool.seq_table(p), pool.seq_table(c))
