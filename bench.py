@@ -495,6 +495,9 @@ def run_gpu(args, wl, loop=False):
                                                    shared_tokens=spec.prefix_len, window=spec.window)
     alg_bytes = [alg_of(l) for timed, l in lens_log if timed]
     alg_timed_steps = [alg_of(l) for timed, l in lens_log[W:]]   # every step of the timed region
+    # per attention launch over every step, warmup included: what a counter run sees
+    log(f"algorithmic bytes per attention launch over all {len(lens_log)} steps: "
+        f"{np.mean([alg_of(l)['total'] for _, l in lens_log]):.0f}")
     log(f"timed {K} steps in {elapsed * 1e3:.2f} ms; attention launch mean {part_ms.mean() * 1e3:.1f} us")
     # the last step's output (its replica's out was last written by it) and the
     # steps whose rows that replica's sequences appended, for the oracle check

@@ -1861,7 +1861,9 @@ struct ExtendArgs {
   float scale_log2;
 };
 
-constexpr int kExtNctMax = 2;
+// Score tiles per extend wave: 1, 2 or 4 (four tiles hold 64 (token, head)
+// columns: k = 8 drafted tokens at G = 8 read the context once).
+constexpr int kExtNctMax = 4;
 
 template <int D, int NCT>
 struct __align__(16) SmemExtend {
@@ -3384,12 +3386,13 @@ ExtendShape extend_shape(const pa_extend_params *p) {
   const int mq = std::max(p->max_query_len, 1);
   if (G > kTileCols) {  // a token's heads span tiles: NCT * 16 heads of one token per query group
     e.tpt = 1;
-    e.nct = kExtNctMax;
+    e.nct = 2;
     e.tpg = 1;
     e.hparts = (G + e.nct * kTileCols - 1) / (e.nct * kTileCols);
   } else {
     e.tpt = kTileCols / G;
-    e.nct = (int64_t)mq * G > kTileCols ? kExtNctMax : 1;
+    const int64_t cols = (int64_t)mq * G;  // columns one sequence's new tokens need
+    e.nct = cols > 2 * kTileCols ? kExtNctMax : cols > kTileCols ? 2 : 1;
     e.tpg = e.nct * e.tpt;
     e.hparts = 1;
   }
@@ -3415,13 +3418,18 @@ size_t extend_ws_bytes(const pa_extend_params *p, const ExtendShape &e) {
   return (size_t)p->num_query_rows * p->num_q_heads * e.np * (p->head_dim + 2) * sizeof(float);
 }
 
+template <int DT, int D>
+const void *extend_kernel_nct(int nct) {
+  switch (nct) {
+    case 1: return reinterpret_cast<const void *>(&pa_extend_kernel<DT, D, 1>);
+    case 2: return reinterpret_cast<const void *>(&pa_extend_kernel<DT, D, 2>);
+    default: return reinterpret_cast<const void *>(&pa_extend_kernel<DT, D, kExtNctMax>);
+  }
+}
+
 template <int D>
 const void *extend_kernel(pa_dtype dt, int nct) {
-  if (dt == PA_BF16)
-    return nct == 1 ? reinterpret_cast<const void *>(&pa_extend_kernel<PA_BF16, D, 1>)
-                    : reinterpret_cast<const void *>(&pa_extend_kernel<PA_BF16, D, kExtNctMax>);
-  return nct == 1 ? reinterpret_cast<const void *>(&pa_extend_kernel<PA_F16, D, 1>)
-                  : reinterpret_cast<const void *>(&pa_extend_kernel<PA_F16, D, kExtNctMax>);
+  return dt == PA_BF16 ? extend_kernel_nct<PA_BF16, D>(nct) : extend_kernel_nct<PA_F16, D>(nct);
 }
 
 }  // namespace
