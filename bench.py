@@ -857,10 +857,10 @@ def main():
     shared_prefix = (spec.prefix_len // 16) if (spec.prefix_len and not args.no_shared_prefix) else 0
     balanced = g["part_tokens"] == 0
     kernel_name = "pa_balanced_kernel" if balanced else "pa_partition_kernel"
-    if shared_prefix:   # the events span both launches: the prefix kernel, then the split
-        kernel_name = "pa_prefix_kernel+" + kernel_name
+    if shared_prefix:   # the prefix kernel runs beside the split on a second stream
+        kernel_name = kernel_name + " (pa_prefix_kernel beside it)"
     merge_name = "pa_merge_balanced_kernel" if balanced else "pa_merge_kernel"
-    t_attn = read_traffic(kernel_name, spec.name)
+    t_attn = read_traffic(kernel_name.split(" ")[0], spec.name)
     t_merge = read_traffic(merge_name, spec.name)
 
     def gbps(nbytes, us):

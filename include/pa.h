@@ -247,9 +247,10 @@ typedef struct pa_decode_params {
    * forks one prefix owner ("Modern AI Infrastructure and Agentic System
    * Design", section 9.1; "Inference serving: the KV-cache machine", Lab B).
    * The attention over the prefix is then computed once for all sequences
-   * (a third kernel before the attention launch of pa_decode /
-   * pa_decode_partitions) and folded into each row; the result is the same
-   * attention.  Needs an fp16/bf16 cache, no sliding window and the balanced
+   * (a third kernel, on a second stream the library owns, beside the
+   * attention launch of pa_decode / pa_decode_partitions; the caller's
+   * stream waits for it right after that launch) and folded into each row;
+   * the result is the same attention.  Needs an fp16/bf16 cache, no sliding window and the balanced
    * split; every context must reach past the prefix (L > 16 *
    * shared_prefix_blocks, else that sequence's rows are NaN).  The workspace
    * grows by num_seqs * num_q_heads * (head_dim + 2) floats. */

@@ -2630,7 +2630,7 @@ int nct_of(int G) { return G <= kTileCols ? 1 : G <= 2 * kTileCols ? 2 : 4; }
 // shared memory allows (per workgroup, with wg_per_cu workgroups on a CU),
 // at most kParkSlotsMax; none when a slot does not fit (every segment then
 // stores as it ends).
-int park_slots(int G, int D, int wg_per_cu) {
+int park_slots(int G, int D, int wg_per_cu, int64_t reserve = 0) {
   static int lds_block[64] = {}, lds_cu[64] = {};
   int dev = 0, per_block = 64 * 1024, per_cu = 64 * 1024;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
@@ -2650,7 +2650,7 @@ int park_slots(int G, int D, int wg_per_cu) {
   } else {
     (void)hipGetLastError();
   }
-  const int64_t budget = std::min<int64_t>(per_block, per_cu / std::max(wg_per_cu, 1)) -
+  const int64_t budget = std::min<int64_t>(per_block, per_cu / std::max(wg_per_cu, 1) - reserve) -
                          (int64_t)sizeof(SmemBalanced) - 2048;
   const int64_t slot = (int64_t)kBWaves * park_slot_floats(G, D) * sizeof(float);
   return (int)std::max<int64_t>(0, std::min<int64_t>(kParkSlotsMax, budget / slot));
@@ -2698,8 +2698,15 @@ BalancedKernel balanced_kernel(pa_dtype kv, pa_dtype qt, int D, int G) {
   }
 }
 
-int balanced_park_slots(pa_dtype kv, pa_dtype qt, int G, int D) {
-  return park_slots(G, D, balanced_kernel(kv, qt, D, G).wg_per_cu);
+// LDS of one shared-prefix workgroup, which runs beside the balanced split.
+int64_t prefix_lds(int D) {
+  return D == 128 ? (int64_t)sizeof(SmemPrefix<128, kPfxNct>) : (int64_t)sizeof(SmemPrefix<64, kPfxNct>);
+}
+
+// Parking slots of the balanced kernel; with a shared prefix, room is left
+// on each CU for one prefix workgroup.
+int balanced_park_slots(pa_dtype kv, pa_dtype qt, int G, int D, bool prefix = false) {
+  return park_slots(G, D, balanced_kernel(kv, qt, D, G).wg_per_cu, prefix ? prefix_lds(D) : 0);
 }
 
 // Workgroups of the balanced grid: the kernel's workgroups per CU (checked
@@ -2928,7 +2935,8 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
       a.ws_pfx_acc = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pfx_off + round16(rows * 2 * 4));
     }
     a.num_workers = kBWaves * balanced_workgroups(p);
-    a.park_slots = balanced_park_slots(p->kv_dtype, p->q_dtype, p->num_q_heads / p->num_kv_heads, p->head_dim);
+    a.park_slots = balanced_park_slots(p->kv_dtype, p->q_dtype, p->num_q_heads / p->num_kv_heads, p->head_dim,
+                                       p->shared_prefix_blocks > 0);
   }
 
   a.num_seqs = p->num_seqs;
@@ -2946,32 +2954,86 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
   return PA_OK;
 }
 
+// A second stream of default priority per device, on which the shared-prefix
+// kernel runs beside the balanced split, with the events that fork it from
+// and join it back into the caller's stream.  The mutex keeps one call's
+// fork, launches and join together when several host threads decode on
+// one device.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+
+pa_status side_stream(SideStream **out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static SideStream side[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_check(e, "pa_decode side stream: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: device %d beyond the first %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  SideStream &ss = side[dev];
+  if (!ss.stream) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess)
+      return hip_check(e, "pa_decode side stream: hipStreamCreateWithFlags");
+    if ((e = hipEventCreateWithFlags(&f, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&j, hipEventDisableTiming)) != hipSuccess) {
+      if (f) (void)hipEventDestroy(f);
+      (void)hipStreamDestroy(st);
+      return hip_check(e, "pa_decode side stream: hipEventCreateWithFlags");
+    }
+    ss.stream = st;
+    ss.fork = f;
+    ss.join = j;
+  }
+  *out = &ss;
+  return PA_OK;
+}
+
+const void *prefix_kernel(pa_dtype kv, int D) {
+  return kv == PA_BF16 ? (D == 128 ? reinterpret_cast<const void *>(&pa_prefix_kernel<PA_BF16, 128>)
+                                   : reinterpret_cast<const void *>(&pa_prefix_kernel<PA_BF16, 64>))
+                       : (D == 128 ? reinterpret_cast<const void *>(&pa_prefix_kernel<PA_F16, 128>)
+                                   : reinterpret_cast<const void *>(&pa_prefix_kernel<PA_F16, 64>));
+}
+
 pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipStream_t hs,
                             const LaunchEvents &ev) {
   void *args[] = {const_cast<DecodeArgs *>(&a)};
   if (use_balanced(p)) {
-    LaunchEvents bev = ev;
-    if (a.prefix_blocks > 0) {  // every row's attention over the shared prefix first
-      const dim3 pgrid((unsigned)(p->num_kv_heads * prefix_workgroups(p->num_seqs, a.group)));
-      const void *pfn = p->kv_dtype == PA_BF16
-                            ? (p->head_dim == 128 ? reinterpret_cast<const void *>(&pa_prefix_kernel<PA_BF16, 128>)
-                                                  : reinterpret_cast<const void *>(&pa_prefix_kernel<PA_BF16, 64>))
-                            : (p->head_dim == 128 ? reinterpret_cast<const void *>(&pa_prefix_kernel<PA_F16, 128>)
-                                                  : reinterpret_cast<const void *>(&pa_prefix_kernel<PA_F16, 64>));
-      LaunchEvents pev;
-      pev.start = ev.start;
-      bev.start = nullptr;
-      hipError_t e = launch_kernel(pfn, pgrid, dim3(kThreads), args, 0, hs, pev);
-      if (e != hipSuccess) return hip_check(e, "pa_decode prefix launch");
-      pa_status st = hip_check(hipGetLastError(), "pa_decode prefix launch");
-      if (st != PA_OK) return st;
-    }
     const dim3 grid((unsigned)(a.num_workers / kBWaves));
     const size_t lds = park_bytes(a.group, p->head_dim, a.park_slots);
-    hipError_t e = launch_kernel(balanced_kernel(p->kv_dtype, p->q_dtype, p->head_dim, a.group).fn, grid,
-                                 dim3(kBThreads), args, lds, hs, bev);
+    const void *bfn = balanced_kernel(p->kv_dtype, p->q_dtype, p->head_dim, a.group).fn;
+    if (a.prefix_blocks == 0) {
+      hipError_t e = launch_kernel(bfn, grid, dim3(kBThreads), args, lds, hs, ev);
+      if (e != hipSuccess) return hip_check(e, "pa_decode balanced launch");
+      return hip_check(hipGetLastError(), "pa_decode balanced launch");
+    }
+    // Shared prefix: every row's attention over the prefix, on the side
+    // stream, runs beside the split (one prefix workgroup fits on each CU
+    // next to the split's); the caller's stream waits for it after the
+    // split, before anything that reads the workspace.
+    SideStream *ss = nullptr;
+    pa_status st = side_stream(&ss);
+    if (st != PA_OK) return st;
+    std::lock_guard<std::mutex> lock(ss->mu);
+    hipError_t e = hipEventRecord(ss->fork, hs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
+    if (e != hipSuccess) return hip_check(e, "pa_decode prefix fork");
+    const dim3 pgrid((unsigned)(p->num_kv_heads * prefix_workgroups(p->num_seqs, a.group)));
+    e = hipLaunchKernel(prefix_kernel(p->kv_dtype, p->head_dim), pgrid, dim3(kThreads), args, 0, ss->stream);
+    if (e != hipSuccess) return hip_check(e, "pa_decode prefix launch");
+    if ((st = hip_check(hipGetLastError(), "pa_decode prefix launch")) != PA_OK) return st;
+    if ((e = hipEventRecord(ss->join, ss->stream)) != hipSuccess) return hip_check(e, "pa_decode prefix join");
+    e = launch_kernel(bfn, grid, dim3(kBThreads), args, lds, hs, ev);
     if (e != hipSuccess) return hip_check(e, "pa_decode balanced launch");
-    return hip_check(hipGetLastError(), "pa_decode balanced launch");
+    if ((st = hip_check(hipGetLastError(), "pa_decode balanced launch")) != PA_OK) return st;
+    return hip_check(hipStreamWaitEvent(hs, ss->join, 0), "pa_decode prefix join");
   }
   const bool mfma = use_mfma(p);
   const dim3 grid((unsigned)((int64_t)a.max_parts * p->num_kv_heads * p->num_seqs * head_chunks(p)));
