@@ -302,7 +302,9 @@ pa_status pa_decode_merge(const pa_decode_params *p, void *workspace, size_t wor
  * call on one device shares that device's array: calls that overlap on the
  * device (on different streams, or from several host threads without stream
  * order between them) race on it and give undefined results.  The output is
- * the same, bit for bit, as pa_decode's for the same parameters.  The first
+ * the same, bit for bit, as pa_decode's for the same parameters (with a
+ * shared prefix its kernel runs before the split on the caller's stream, not
+ * beside it on a stream of the library's).  The first
  * call on a device looks up the array's address there (that device must be
  * current); other errors as pa_decode. */
 pa_status pa_decode_noalloc(const pa_decode_params *p, void *stream);

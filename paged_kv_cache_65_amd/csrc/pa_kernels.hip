@@ -3002,14 +3002,23 @@ const void *prefix_kernel(pa_dtype kv, int D) {
                                    : reinterpret_cast<const void *>(&pa_prefix_kernel<PA_F16, 64>));
 }
 
+// side_stream_ok = false: a shared prefix's kernel runs before the split on
+// the caller's stream (no stream of the library's own is created or used).
 pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipStream_t hs,
-                            const LaunchEvents &ev) {
+                            const LaunchEvents &ev, bool side_stream_ok = true) {
   void *args[] = {const_cast<DecodeArgs *>(&a)};
   if (use_balanced(p)) {
     const dim3 grid((unsigned)(a.num_workers / kBWaves));
     const size_t lds = park_bytes(a.group, p->head_dim, a.park_slots);
     const void *bfn = balanced_kernel(p->kv_dtype, p->q_dtype, p->head_dim, a.group).fn;
-    if (a.prefix_blocks == 0) {
+    const dim3 pgrid((unsigned)(p->num_kv_heads * prefix_workgroups(p->num_seqs, a.group)));
+    if (a.prefix_blocks == 0 || !side_stream_ok) {
+      if (a.prefix_blocks > 0) {
+        hipError_t e = hipLaunchKernel(prefix_kernel(p->kv_dtype, p->head_dim), pgrid, dim3(kThreads), args, 0, hs);
+        if (e != hipSuccess) return hip_check(e, "pa_decode prefix launch");
+        pa_status st = hip_check(hipGetLastError(), "pa_decode prefix launch");
+        if (st != PA_OK) return st;
+      }
       hipError_t e = launch_kernel(bfn, grid, dim3(kBThreads), args, lds, hs, ev);
       if (e != hipSuccess) return hip_check(e, "pa_decode balanced launch");
       return hip_check(hipGetLastError(), "pa_decode balanced launch");
@@ -3025,7 +3034,6 @@ pa_status launch_partitions(const pa_decode_params *p, const DecodeArgs &a, hipS
     hipError_t e = hipEventRecord(ss->fork, hs);
     if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
     if (e != hipSuccess) return hip_check(e, "pa_decode prefix fork");
-    const dim3 pgrid((unsigned)(p->num_kv_heads * prefix_workgroups(p->num_seqs, a.group)));
     e = hipLaunchKernel(prefix_kernel(p->kv_dtype, p->head_dim), pgrid, dim3(kThreads), args, 0, ss->stream);
     if (e != hipSuccess) return hip_check(e, "pa_decode prefix launch");
     if ((st = hip_check(hipGetLastError(), "pa_decode prefix launch")) != PA_OK) return st;
@@ -3074,14 +3082,11 @@ LaunchEvents events_of(const pa_decode_params *p) {
   return ev;
 }
 
-}  // namespace
-
-extern "C" {
-
-pa_status pa_decode(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
-                    void *stream) {
+// The attention launch(es) and the merge of one decode call.
+pa_status decode_call(const pa_decode_params *p, void *workspace, size_t workspace_bytes, void *stream,
+                      bool side_stream_ok, const char *who) {
   DecodeArgs a;
-  pa_status st = prepare(p, workspace, workspace_bytes, "pa_decode", a);
+  pa_status st = prepare(p, workspace, workspace_bytes, who, a);
   if (st != PA_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const LaunchEvents ev = events_of(p);
@@ -3090,8 +3095,17 @@ pa_status pa_decode(const pa_decode_params *p, void *workspace, size_t workspace
   LaunchEvents first, second;
   first.start = ev.start;
   (merge ? second : first).stop = ev.stop;
-  if ((st = launch_partitions(p, a, hs, first)) != PA_OK) return st;
+  if ((st = launch_partitions(p, a, hs, first, side_stream_ok)) != PA_OK) return st;
   return merge ? launch_merge(p, a, hs, second) : PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  return decode_call(p, workspace, workspace_bytes, stream, true, "pa_decode");
 }
 
 pa_status pa_decode_partitions(const pa_decode_params *p, void *workspace, size_t workspace_bytes,
@@ -3169,8 +3183,9 @@ pa_status pa_decode_noalloc(const pa_decode_params *p, void *stream) {
     if (sa != PA_OK) return sa;
   }
   // The workspace needs no initialization: every slot a launch reads was
-  // written earlier in the same call.
-  return pa_decode(p, ws, need > 0 ? kScratchBytes : 0, stream);
+  // written earlier in the same call.  A shared prefix's kernel runs before
+  // the split on the caller's stream (no stream of the library's own).
+  return decode_call(p, ws, need > 0 ? kScratchBytes : 0, stream, false, "pa_decode_noalloc");
 }
 
 pa_status pa_reshape_and_cache(const void *k_new, const void *v_new, void *k_cache, void *v_cache,

@@ -41,7 +41,7 @@ def _setup(spec, steps=0):
     return wl, gst
 
 
-def _run_both(wl, gst, mb, seqs, pt):
+def _run_both(wl, gst, mb, seqs, pt, prefix_blocks=0):
     """pa_decode and pa_decode_noalloc on the sequences `seqs` (a prefix of the batch)."""
     spec = wl.spec
     dev = gst.k_cache.device
@@ -53,7 +53,8 @@ def _run_both(wl, gst, mb, seqs, pt):
     for fn in (pa.pa_decode, pa.pa_decode_noalloc):
         out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=dev)
         fn(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, spec.num_kv_heads, max_ctx,
-           spec.fp32_scale(), partition_tokens=pt, k_scales=gst.k_scales, v_scales=gst.v_scales)
+           spec.fp32_scale(), partition_tokens=pt, k_scales=gst.k_scales, v_scales=gst.v_scales,
+           shared_prefix_blocks=prefix_blocks)
         outs.append(out)
     torch.cuda.synchronize()
     ref, mine = (o.cpu().numpy() for o in outs)
@@ -110,3 +111,21 @@ def test_noalloc_rejects_a_call_beyond_its_array_and_launches_nothing():
     assert e.value.status == pa.PA_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool(torch.all(out == 7.0))
+
+
+def test_noalloc_with_a_shared_prefix_equals_pa_decode():
+    # pa_decode runs the prefix kernel beside the split on a second stream,
+    # pa_decode_noalloc before it on the caller's: the same kernels, the same bits
+    lens = [int(x) for x in np.random.default_rng(96).integers(1, 900, size=20)]
+    spec = workloads.custom(name="noalloc-prefix", seed=96, dtype="bf16", out_dtype="f32", lens=lens,
+                            num_q_heads=16, num_kv_heads=4, head_dim=128, prefix_len=64)
+    wl, gst = _setup(spec)
+    ost = oracle_side.build(wl)
+    mb = oracle_side.max_blocks_for(wl)
+    for seqs in (spec.num_seqs, 5):
+        ref, mine = _run_both(wl, gst, mb, seqs, 0, prefix_blocks=4)
+        _say(f"[noalloc] prefix: {seqs} seqs")
+        assert np.array_equal(ref.view(np.uint32), mine.view(np.uint32))
+    orc = oracle_side.decode(wl, ost, mb)
+    err = float(np.max(np.abs(mine.astype(np.float64) - orc[:5])))
+    assert err <= 2e-3, err
