@@ -524,8 +524,7 @@ class OracleCaches:
         self.i8, self.fp8 = spec.cache in ("i8", "fp8"), spec.cache == "fp8"
         if self.i8:
             empty = oracle.empty_cache_fp8 if self.fp8 else oracle.empty_cache_i8
-            self.kc, self.ks = empty(num_blocks, Hkv, D)
-            self.vc, self.vs = empty(num_blocks, Hkv, D)
+            self.kc, self.vc = empty(num_blocks, Hkv, D), empty(num_blocks, Hkv, D)
         else:
             self.kc = oracle.empty_cache(num_blocks, Hkv, D, dt)
             self.vc = oracle.empty_cache(num_blocks, Hkv, D, dt)
@@ -534,7 +533,7 @@ class OracleCaches:
         o, sp = self.o, self.spec
         if self.i8:
             (o.reshape_and_cache_fp8 if self.fp8 else o.reshape_and_cache_i8)(
-                k, v, self.kc, self.vc, self.ks, self.vs, slots, sp.num_kv_heads, sp.head_dim, self.nb, sp.dtype)
+                k, v, self.kc, self.vc, slots, sp.num_kv_heads, sp.head_dim, self.nb, sp.dtype)
         else:
             o.reshape_and_cache(k, v, self.kc, self.vc, slots, sp.num_kv_heads, sp.head_dim, self.nb, sp.dtype)
 
@@ -542,9 +541,8 @@ class OracleCaches:
         """(fp64 output, threads used)."""
         o, sp = self.o, self.spec
         if self.i8:
-            return o.decode_i8(q, sp.dtype, self.kc, self.vc, self.ks, self.vs, tab, lens, sp.num_kv_heads,
-                               sp.fp32_scale(), nthreads=nthreads, return_threads=True, window=sp.window,
-                               fp8=self.fp8)
+            return o.decode_i8(q, sp.dtype, self.kc, self.vc, tab, lens, sp.num_kv_heads, sp.fp32_scale(),
+                               nthreads=nthreads, return_threads=True, window=sp.window, fp8=self.fp8)
         return o.decode(q, self.kc, self.vc, tab, lens, sp.num_kv_heads, sp.fp32_scale(), sp.dtype,
                         nthreads=nthreads, return_threads=True, window=sp.window)
 

@@ -11,9 +11,10 @@ Contents
     whole-block copies.  Passages followed are cited in that file.
   * ``pool_model.py``: an independent pure-Python model of the refcounted
     block pool (allocation, fork, append with copy-on-write, free).
-  * INT8 caches: codes (``np.int8``) in their own tile layout plus one fp32
-    scale per (token, KV head) row; quantized on append, attended over the
-    dequantized rows (``*_i8`` functions).
+  * INT8 / FP8 caches: one byte array per K and V whose tiles hold the codes
+    (``np.int8`` / ``np.uint8``) of 16 tokens of one (block, KV head) followed
+    by their 16 float32 row scales; quantized on append, attended over the
+    dequantized rows (``*_i8`` / ``*_fp8`` functions).
 
 Data convention for the wrappers: cache-typed arrays are numpy arrays of
 ``np.float32`` (fp32), ``np.float16`` (fp16) or ``np.uint16`` holding raw
@@ -74,13 +75,14 @@ def _load():
         lib.oracle_v_offset_i8.argtypes = [_I64, _I, _I, _I, _I, _I]
         lib.oracle_quantize_row_i8.restype = ctypes.c_float
         lib.oracle_quantize_row_i8.argtypes = [_P, _I64, _I, _I, _P]
+        lib.oracle_scale_offset_i8.restype = _I64
+        lib.oracle_scale_offset_i8.argtypes = [_I64, _I, _I, _I, _I]
         lib.oracle_reshape_and_cache_i8.restype = _I
-        lib.oracle_reshape_and_cache_i8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
-                                                    _I64, _I]
+        lib.oracle_reshape_and_cache_i8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I64, _I]
         lib.oracle_copy_blocks_i8.restype = None
-        lib.oracle_copy_blocks_i8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I]
+        lib.oracle_copy_blocks_i8.argtypes = [_P, _P, _P, _I, _I, _I]
         lib.oracle_decode_codes.restype = _I
-        lib.oracle_decode_codes.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+        lib.oracle_decode_codes.argtypes = [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I,
                                             _I, ctypes.c_float, _I, _I, _I]
         lib.oracle_e4m3_value.restype = ctypes.c_double
         lib.oracle_e4m3_value.argtypes = [_I]
@@ -89,8 +91,7 @@ def _load():
         lib.oracle_quantize_row_fp8.restype = ctypes.c_float
         lib.oracle_quantize_row_fp8.argtypes = [_P, _I64, _I, _I, _P]
         lib.oracle_reshape_and_cache_fp8.restype = _I
-        lib.oracle_reshape_and_cache_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
-                                                     _I64, _I]
+        lib.oracle_reshape_and_cache_fp8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I64, _I]
         lib.oracle_extend.restype = _I
         lib.oracle_extend.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                       ctypes.c_float, _I, _I]
@@ -227,6 +228,21 @@ def v_offset_i8(block, head, tok, dim, num_kv_heads, head_dim):
     return _load().oracle_v_offset_i8(block, head, tok, dim, num_kv_heads, head_dim)
 
 
+def scale_offset_i8(block, head, tok, num_kv_heads, head_dim):
+    """Byte offset of the float32 scale of row (block, head, tok) in a K or V cache."""
+    return _load().oracle_scale_offset_i8(block, head, tok, num_kv_heads, head_dim)
+
+
+def read_scale(cache, block, head, tok, num_kv_heads, head_dim) -> np.float32:
+    o = scale_offset_i8(block, head, tok, num_kv_heads, head_dim)
+    return cache[o:o + 4].view(np.float32)[0]
+
+
+def cache_bytes_i8(num_blocks, num_kv_heads, head_dim) -> int:
+    """Bytes of one K or V byte cache: 16 rows of head_dim codes + 4 scale bytes per tile."""
+    return num_blocks * num_kv_heads * 16 * (head_dim + 4)
+
+
 def quantize_row_i8(row: np.ndarray, dtype: str):
     """(codes int8 [n], scale float32) of one row in the given type."""
     row = _check(np.asarray(row), dtype)
@@ -235,34 +251,41 @@ def quantize_row_i8(row: np.ndarray, dtype: str):
     return codes, np.float32(sc)
 
 
+def _empty_codes(num_blocks, num_kv_heads, head_dim, np_type):
+    """An unwritten byte cache: codes 0x7F, every scale NaN."""
+    tiles = np.full((num_blocks * num_kv_heads, 16 * (head_dim + 4)), 0x7F, dtype=np.uint8)
+    tiles[:, 16 * head_dim:].view(np.float32)[:] = np.nan
+    return tiles.reshape(-1).view(np_type)
+
+
 def empty_cache_i8(num_blocks, num_kv_heads, head_dim):
-    """(codes, scales) of an unwritten int8 pool: codes 0x7F, scales NaN."""
-    codes = np.full(num_blocks * num_kv_heads * 16 * head_dim, 127, dtype=np.int8)
-    scales = np.full(num_blocks * num_kv_heads * 16, np.nan, dtype=np.float32)
-    return codes, scales
+    """One unwritten int8 cache (K or V): codes 0x7F, scales NaN."""
+    return _empty_codes(num_blocks, num_kv_heads, head_dim, np.int8)
 
 
-def reshape_and_cache_i8(k_new, v_new, k_cache, v_cache, k_scales, v_scales, slot_mapping,
-                         num_kv_heads, head_dim, num_blocks, src_dtype):
+def reshape_and_cache_i8(k_new, v_new, k_cache, v_cache, slot_mapping, num_kv_heads, head_dim,
+                         num_blocks, src_dtype):
     """Quantize [T][Hkv][D] rows into the int8 caches in place; returns #out-of-range slots."""
     k_new = _check(k_new, src_dtype)
     v_new = _check(v_new, src_dtype)
     slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
-    for a, t in ((k_cache, np.int8), (v_cache, np.int8), (k_scales, np.float32), (v_scales, np.float32)):
-        assert a.dtype == t and a.flags["C_CONTIGUOUS"]
+    for a in (k_cache, v_cache):
+        assert a.dtype == np.int8 and a.flags["C_CONTIGUOUS"]
+        assert a.size == cache_bytes_i8(num_blocks, num_kv_heads, head_dim)
     return _load().oracle_reshape_and_cache_i8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
-                                               _ptr(k_scales), _ptr(v_scales), _ptr(slots), len(slots),
-                                               num_kv_heads, head_dim, num_blocks, _DTYPES[src_dtype])
+                                               _ptr(slots), len(slots), num_kv_heads, head_dim, num_blocks,
+                                               _DTYPES[src_dtype])
 
 
-def copy_blocks_i8(k_cache, v_cache, k_scales, v_scales, pairs, num_kv_heads, head_dim):
+def copy_blocks_i8(k_cache, v_cache, pairs, num_kv_heads, head_dim):
+    """Whole-block copies of a byte cache (int8 or E4M3): codes and scales of every head."""
     pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
-    _load().oracle_copy_blocks_i8(_ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
-                                  _ptr(pairs), len(pairs), num_kv_heads, head_dim)
+    _load().oracle_copy_blocks_i8(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), len(pairs), num_kv_heads,
+                                  head_dim)
 
 
-def decode_i8(q, q_dtype, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens,
-              num_kv_heads, scale, nthreads=0, return_threads=False, window=0, fp8=False):
+def decode_i8(q, q_dtype, k_cache, v_cache, block_tables, context_lens, num_kv_heads, scale, nthreads=0,
+              return_threads=False, window=0, fp8=False):
     """fp64 paged decode over an int8 cache (an E4M3 one with fp8=True; codes as
     uint8); q is [S][Hq][D] in q_dtype."""
     q = _check(q, q_dtype)
@@ -271,9 +294,8 @@ def decode_i8(q, q_dtype, k_cache, v_cache, k_scales, v_scales, block_tables, co
     lens = np.ascontiguousarray(context_lens, dtype=np.int32)
     out = np.empty((S, Hq, D), dtype=np.float64)
     used = _load().oracle_decode_codes(_ptr(out), _ptr(q), _DTYPES[q_dtype], _ptr(k_cache), _ptr(v_cache),
-                                       _ptr(k_scales), _ptr(v_scales), _ptr(tables), _ptr(lens), S, Hq,
-                                       num_kv_heads, D, tables.shape[1], float(scale), int(window),
-                                       int(fp8), nthreads)
+                                       _ptr(tables), _ptr(lens), S, Hq, num_kv_heads, D, tables.shape[1],
+                                       float(scale), int(window), int(fp8), nthreads)
     return (out, used) if return_threads else out
 
 
@@ -295,20 +317,19 @@ def quantize_row_fp8(row: np.ndarray, dtype: str):
 
 
 def empty_cache_fp8(num_blocks, num_kv_heads, head_dim):
-    """(codes, scales) of an unwritten FP8 pool: NaN codes 0x7F, NaN scales."""
-    codes = np.full(num_blocks * num_kv_heads * 16 * head_dim, 0x7F, dtype=np.uint8)
-    scales = np.full(num_blocks * num_kv_heads * 16, np.nan, dtype=np.float32)
-    return codes, scales
+    """One unwritten FP8 cache (K or V): NaN codes 0x7F, NaN scales."""
+    return _empty_codes(num_blocks, num_kv_heads, head_dim, np.uint8)
 
 
-def reshape_and_cache_fp8(k_new, v_new, k_cache, v_cache, k_scales, v_scales, slot_mapping,
-                          num_kv_heads, head_dim, num_blocks, src_dtype):
+def reshape_and_cache_fp8(k_new, v_new, k_cache, v_cache, slot_mapping, num_kv_heads, head_dim,
+                          num_blocks, src_dtype):
     """Quantize [T][Hkv][D] rows into the FP8 caches in place; returns #out-of-range slots."""
     k_new = _check(k_new, src_dtype)
     v_new = _check(v_new, src_dtype)
     slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
-    for a, t in ((k_cache, np.uint8), (v_cache, np.uint8), (k_scales, np.float32), (v_scales, np.float32)):
-        assert a.dtype == t and a.flags["C_CONTIGUOUS"]
+    for a in (k_cache, v_cache):
+        assert a.dtype == np.uint8 and a.flags["C_CONTIGUOUS"]
+        assert a.size == cache_bytes_i8(num_blocks, num_kv_heads, head_dim)
     return _load().oracle_reshape_and_cache_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
-                                                _ptr(k_scales), _ptr(v_scales), _ptr(slots), len(slots),
-                                                num_kv_heads, head_dim, num_blocks, _DTYPES[src_dtype])
+                                                _ptr(slots), len(slots), num_kv_heads, head_dim, num_blocks,
+                                                _DTYPES[src_dtype])

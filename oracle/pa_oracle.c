@@ -395,27 +395,45 @@ void oracle_bruteforce_contiguous(double *out, const void *q, const void *k_seq,
  * machine" ("What insiders know") names per-head / per-channel scales as what
  * keeps outlier heads accurate; here every (token, head) row has its own.
  *
- * Layout contract (byte offsets inside a tile of 16 tokens x D dims; tile
- * (b, g) starts at byte (b*Hkv + g)*16*D; scales at float index
- * (b*Hkv + g)*16 + t in separate k_scales / v_scales arrays):
- *   K: element (t, d): c = d/64, w = d%64, h = w/32, q = (w%32)/8, e = w%8
+ * Layout contract (byte offsets into the K or V cache array).  A tile holds
+ * the 16 tokens x D codes of one (block b, KV head g) followed by their 16
+ * float32 row scales: 16*(D+4) bytes, starting at byte (b*Hkv + g)*16*(D+4).
+ * Inside the tile:
+ *   K code (t, d): c = d/64, w = d%64, h = w/32, q = (w%32)/8, e = w%8
  *      -> byte (c*64 + q*16 + t)*16 + h*8 + e
- *   V: element (t, d): m = d/64, k = (d%64)/16, r = d%16
+ *   V code (t, d): m = d/64, k = (d%64)/16, r = d%16
  *      -> byte (m*64 + (t/4)*16 + r)*16 + k*4 + t%4
+ *   scale of token t -> bytes 16*D + 4t .. 16*D + 4t + 3 (float32, host
+ *      byte order)
  * ------------------------------------------------------------------------ */
+static int64_t tile_i8(int64_t block, int head, int num_kv_heads, int head_dim) {
+  return (block * num_kv_heads + head) * (int64_t)ORC_BS * (head_dim + 4);
+}
+
 int64_t oracle_k_offset_i8(int64_t block, int head, int tok, int dim, int num_kv_heads,
                            int head_dim) {
-  int64_t tile = (block * num_kv_heads + head) * (int64_t)ORC_BS * head_dim;
   int c = dim / 64, w = dim % 64, h = w / 32, q = (w % 32) / 8, e = w % 8;
-  return tile + (int64_t)(c * 64 + q * 16 + tok) * 16 + h * 8 + e;
+  return tile_i8(block, head, num_kv_heads, head_dim) + (int64_t)(c * 64 + q * 16 + tok) * 16 + h * 8 + e;
 }
 
 int64_t oracle_v_offset_i8(int64_t block, int head, int tok, int dim, int num_kv_heads,
                            int head_dim) {
-  int64_t tile = (block * num_kv_heads + head) * (int64_t)ORC_BS * head_dim;
   int m = dim / 64, k = (dim % 64) / 16, r = dim % 16;
-  return tile + (int64_t)(m * 64 + (tok / 4) * 16 + r) * 16 + k * 4 + tok % 4;
+  return tile_i8(block, head, num_kv_heads, head_dim) + (int64_t)(m * 64 + (tok / 4) * 16 + r) * 16 + k * 4 +
+         tok % 4;
 }
+
+int64_t oracle_scale_offset_i8(int64_t block, int head, int tok, int num_kv_heads, int head_dim) {
+  return tile_i8(block, head, num_kv_heads, head_dim) + (int64_t)ORC_BS * head_dim + 4 * tok;
+}
+
+static float load_scale(const void *cache, int64_t off) {
+  float v;
+  memcpy(&v, (const uint8_t *)cache + off, sizeof v);
+  return v;
+}
+
+static void store_scale(void *cache, int64_t off, float v) { memcpy((uint8_t *)cache + off, &v, sizeof v); }
 
 /* Quantizes n elements of a row (src_dtype F16/BF16/F32) into int8 codes and
  * returns the row's scale. */
@@ -441,9 +459,9 @@ float oracle_quantize_row_i8(const void *x, int64_t first, int n, int src_dtype,
  * FP8 (OCP E4M3) codes, same tiles and per-row scales as the int8 cache.
  * A code is s eeee mmm: exponent bias 7; e = 0 is subnormal (m * 2^-9);
  * e = 15 with m = 7 is NaN (no infinities); largest finite 448 (0x7E).
- * Quantization, read from the int8 recipe of "LLM Inference Optimization:
- * KV-Cache, PagedAttention, and GPU Memory Efficiency" (Future
- * Optimizations) with FP8's range ("Inference serving: the KV-cache machine",
+ * Quantization, read from the int8 recipe of "KV Cache Explained Like You're
+ * an LLM Engineer" (Future Optimizations, KV Cache Quantization) with FP8's
+ * range ("Inference serving: the KV-cache machine",
  * What insiders know, names an fp8 KV cache with per-head scales but gives no
  * recipe): scale = max |x| / 448 in float32, code = the E4M3 value
  * nearest to x / scale (float32 division), ties to the even code, values
@@ -497,9 +515,8 @@ float oracle_quantize_row_fp8(const void *x, int64_t first, int n, int src_dtype
 }
 
 int oracle_reshape_and_cache_fp8(const void *k_new, const void *v_new, uint8_t *k_cache,
-                                 uint8_t *v_cache, float *k_scales, float *v_scales,
-                                 const int64_t *slot_mapping, int num_tokens, int num_kv_heads,
-                                 int head_dim, int64_t num_blocks, int src_dtype) {
+                                 uint8_t *v_cache, const int64_t *slot_mapping, int num_tokens,
+                                 int num_kv_heads, int head_dim, int64_t num_blocks, int src_dtype) {
   int bad = 0;
   uint8_t *codes = (uint8_t *)malloc((size_t)head_dim);
   for (int n = 0; n < num_tokens; ++n) {
@@ -510,11 +527,11 @@ int oracle_reshape_and_cache_fp8(const void *k_new, const void *v_new, uint8_t *
     int t = (int)(s % ORC_BS);
     for (int g = 0; g < num_kv_heads; ++g) {
       int64_t row = ((int64_t)n * num_kv_heads + g) * head_dim;
-      int64_t sidx = (blk * num_kv_heads + g) * ORC_BS + t;
-      k_scales[sidx] = oracle_quantize_row_fp8(k_new, row, head_dim, src_dtype, codes);
+      int64_t soff = oracle_scale_offset_i8(blk, g, t, num_kv_heads, head_dim);
+      store_scale(k_cache, soff, oracle_quantize_row_fp8(k_new, row, head_dim, src_dtype, codes));
       for (int d = 0; d < head_dim; ++d)
         k_cache[oracle_k_offset_i8(blk, g, t, d, num_kv_heads, head_dim)] = codes[d];
-      v_scales[sidx] = oracle_quantize_row_fp8(v_new, row, head_dim, src_dtype, codes);
+      store_scale(v_cache, soff, oracle_quantize_row_fp8(v_new, row, head_dim, src_dtype, codes));
       for (int d = 0; d < head_dim; ++d)
         v_cache[oracle_v_offset_i8(blk, g, t, d, num_kv_heads, head_dim)] = codes[d];
     }
@@ -524,11 +541,10 @@ int oracle_reshape_and_cache_fp8(const void *k_new, const void *v_new, uint8_t *
 }
 
 /* Append with quantization: like oracle_reshape_and_cache, into int8 tiles
- * plus per-row scales.  Returns the number of out-of-range slots. */
+ * with their per-row scales.  Returns the number of out-of-range slots. */
 int oracle_reshape_and_cache_i8(const void *k_new, const void *v_new, int8_t *k_cache,
-                                int8_t *v_cache, float *k_scales, float *v_scales,
-                                const int64_t *slot_mapping, int num_tokens, int num_kv_heads,
-                                int head_dim, int64_t num_blocks, int src_dtype) {
+                                int8_t *v_cache, const int64_t *slot_mapping, int num_tokens,
+                                int num_kv_heads, int head_dim, int64_t num_blocks, int src_dtype) {
   int bad = 0;
   int8_t *codes = (int8_t *)malloc((size_t)head_dim);
   for (int n = 0; n < num_tokens; ++n) {
@@ -539,11 +555,11 @@ int oracle_reshape_and_cache_i8(const void *k_new, const void *v_new, int8_t *k_
     int t = (int)(s % ORC_BS);
     for (int g = 0; g < num_kv_heads; ++g) {
       int64_t row = ((int64_t)n * num_kv_heads + g) * head_dim;
-      int64_t sidx = (blk * num_kv_heads + g) * ORC_BS + t;
-      k_scales[sidx] = oracle_quantize_row_i8(k_new, row, head_dim, src_dtype, codes);
+      int64_t soff = oracle_scale_offset_i8(blk, g, t, num_kv_heads, head_dim);
+      store_scale(k_cache, soff, oracle_quantize_row_i8(k_new, row, head_dim, src_dtype, codes));
       for (int d = 0; d < head_dim; ++d)
         k_cache[oracle_k_offset_i8(blk, g, t, d, num_kv_heads, head_dim)] = codes[d];
-      v_scales[sidx] = oracle_quantize_row_i8(v_new, row, head_dim, src_dtype, codes);
+      store_scale(v_cache, soff, oracle_quantize_row_i8(v_new, row, head_dim, src_dtype, codes));
       for (int d = 0; d < head_dim; ++d)
         v_cache[oracle_v_offset_i8(blk, g, t, d, num_kv_heads, head_dim)] = codes[d];
     }
@@ -552,17 +568,15 @@ int oracle_reshape_and_cache_i8(const void *k_new, const void *v_new, int8_t *k_
   return bad;
 }
 
-/* Whole-block copy of an int8 cache: codes and scales of every head. */
-void oracle_copy_blocks_i8(int8_t *k_cache, int8_t *v_cache, float *k_scales, float *v_scales,
-                           const int32_t *pairs, int num_pairs, int num_kv_heads, int head_dim) {
-  size_t code_bytes = (size_t)num_kv_heads * ORC_BS * head_dim;
-  size_t scale_count = (size_t)num_kv_heads * ORC_BS;
+/* Whole-block copy of an int8 / E4M3 cache: the tiles (codes and scales) of
+ * every head. */
+void oracle_copy_blocks_i8(int8_t *k_cache, int8_t *v_cache, const int32_t *pairs, int num_pairs,
+                           int num_kv_heads, int head_dim) {
+  size_t block_bytes = (size_t)num_kv_heads * ORC_BS * (head_dim + 4);
   for (int p = 0; p < num_pairs; ++p) {
     size_t src = (size_t)pairs[2 * p], dst = (size_t)pairs[2 * p + 1];
-    memmove(k_cache + dst * code_bytes, k_cache + src * code_bytes, code_bytes);
-    memmove(v_cache + dst * code_bytes, v_cache + src * code_bytes, code_bytes);
-    memmove(k_scales + dst * scale_count, k_scales + src * scale_count, scale_count * sizeof(float));
-    memmove(v_scales + dst * scale_count, v_scales + src * scale_count, scale_count * sizeof(float));
+    memmove(k_cache + dst * block_bytes, k_cache + src * block_bytes, block_bytes);
+    memmove(v_cache + dst * block_bytes, v_cache + src * block_bytes, block_bytes);
   }
 }
 
@@ -570,7 +584,6 @@ void oracle_copy_blocks_i8(int8_t *k_cache, int8_t *v_cache, float *k_scales, fl
  * dequantized rows code * scale (exact in double); q is F16 or BF16. */
 typedef struct {
   const int8_t *k_cache, *v_cache;
-  const float *k_scales, *v_scales;
   const int32_t *table;
   int num_kv_heads, head_dim, kv_head;
   int fp8; /* codes are E4M3 (else int8) */
@@ -592,7 +605,7 @@ static void attend_one_i8(double *out, const double *q, const orc_src_i8 *s, int
   for (int i = i0; i < L; ++i) {
     int64_t blk = s->table[i / ORC_BS];
     int t = i % ORC_BS;
-    double ks = (double)s->k_scales[(blk * s->num_kv_heads + s->kv_head) * ORC_BS + t];
+    double ks = (double)load_scale(s->k_cache, oracle_scale_offset_i8(blk, s->kv_head, t, s->num_kv_heads, D));
     double dot = 0.0;
     for (int d = 0; d < D; ++d)
       dot += q[d] * (code_value(s, s->k_cache[oracle_k_offset_i8(blk, s->kv_head, t, d, s->num_kv_heads, D)]) * ks);
@@ -609,7 +622,7 @@ static void attend_one_i8(double *out, const double *q, const orc_src_i8 *s, int
     for (int i = i0; i < L; ++i) {
       int64_t blk = s->table[i / ORC_BS];
       int t = i % ORC_BS;
-      double vs = (double)s->v_scales[(blk * s->num_kv_heads + s->kv_head) * ORC_BS + t];
+      double vs = (double)load_scale(s->v_cache, oracle_scale_offset_i8(blk, s->kv_head, t, s->num_kv_heads, D));
       acc += sigma[i] * (code_value(s, s->v_cache[oracle_v_offset_i8(blk, s->kv_head, t, d, s->num_kv_heads, D)]) * vs);
     }
     out[d] = acc / Z;
@@ -618,8 +631,7 @@ static void attend_one_i8(double *out, const double *q, const orc_src_i8 *s, int
 
 /* Decode over an int8 (fp8 = 0) or E4M3 (fp8 = 1) cache. */
 int oracle_decode_codes(double *out, const void *q, int q_dtype, const int8_t *k_cache,
-                        const int8_t *v_cache, const float *k_scales, const float *v_scales,
-                        const int32_t *tables, const int32_t *lens, int num_seqs, int num_q_heads,
+                        const int8_t *v_cache, const int32_t *tables, const int32_t *lens, int num_seqs, int num_q_heads,
                         int num_kv_heads, int head_dim, int max_blocks, float scale, int window,
                         int fp8, int nthreads) {
   int G = num_q_heads / num_kv_heads;
@@ -642,7 +654,7 @@ int oracle_decode_codes(double *out, const void *q, int q_dtype, const int8_t *k
     for (int sh = 0; sh < num_seqs * num_q_heads; ++sh) {
       int s = sh / num_q_heads, h = sh % num_q_heads;
       for (int d = 0; d < head_dim; ++d) qd[d] = load_elem(q, (int64_t)sh * head_dim + d, q_dtype);
-      orc_src_i8 src = {k_cache, v_cache, k_scales, v_scales, tables + (int64_t)s * max_blocks,
+      orc_src_i8 src = {k_cache, v_cache, tables + (int64_t)s * max_blocks,
                         num_kv_heads, head_dim, h / G, fp8};
       attend_one_i8(out + (int64_t)sh * head_dim, qd, &src, lens[s], window, (double)scale, sigma);
     }

@@ -30,8 +30,6 @@ class OracleState:
     prefix_slots: list
     step_slots: list            # per step, slots in sequence order
     cow_log: list               # (phase, src, dst)
-    k_scales: np.ndarray = None  # int8 caches: per-row scales
-    v_scales: np.ndarray = None
 
 
 def max_blocks_for(wl, steps=None) -> int:
@@ -47,24 +45,22 @@ def build(wl, steps: int = 0) -> OracleState:
     fp8 = spec.cache == "fp8"
     if i8:
         empty = oracle.empty_cache_fp8 if fp8 else oracle.empty_cache_i8
-        kc, ks = empty(wl.num_blocks, Hkv, D)
-        vc, vs = empty(wl.num_blocks, Hkv, D)
+        kc, vc = empty(wl.num_blocks, Hkv, D), empty(wl.num_blocks, Hkv, D)
     else:
         kc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
         vc = oracle.empty_cache(wl.num_blocks, Hkv, D, dt)
-        ks = vs = None
 
     def put(k, v, slots):
         if fp8:
-            oracle.reshape_and_cache_fp8(k, v, kc, vc, ks, vs, slots, Hkv, D, wl.num_blocks, dt)
+            oracle.reshape_and_cache_fp8(k, v, kc, vc, slots, Hkv, D, wl.num_blocks, dt)
         elif i8:
-            oracle.reshape_and_cache_i8(k, v, kc, vc, ks, vs, slots, Hkv, D, wl.num_blocks, dt)
+            oracle.reshape_and_cache_i8(k, v, kc, vc, slots, Hkv, D, wl.num_blocks, dt)
         else:
             oracle.reshape_and_cache(k, v, kc, vc, slots, Hkv, D, wl.num_blocks, dt)
 
     def copy(pairs):
         if i8:
-            oracle.copy_blocks_i8(kc, vc, ks, vs, pairs, Hkv, D)
+            oracle.copy_blocks_i8(kc, vc, pairs, Hkv, D)
         else:
             oracle.copy_blocks(kc, vc, pairs, Hkv, D, dt)
     cow_log = []
@@ -86,7 +82,7 @@ def build(wl, steps: int = 0) -> OracleState:
             cow_log.append(("prompt", *cow))
         put(wl.k_tokens[lo:hi], wl.v_tokens[lo:hi], slots)
         prompt_slots.append(slots)
-    st = OracleState(pool, seq_ids, owner, kc, vc, prompt_slots, prefix_slots, [], cow_log, ks, vs)
+    st = OracleState(pool, seq_ids, owner, kc, vc, prompt_slots, prefix_slots, [], cow_log)
     for step in range(steps):
         advance(wl, st, step)
     return st
@@ -98,16 +94,15 @@ def advance(wl, st: OracleState, step: int):
     i8 = spec.cache in ("i8", "fp8")
     if cows:
         if i8:
-            oracle.copy_blocks_i8(st.k_cache, st.v_cache, st.k_scales, st.v_scales, np.array(cows),
-                                  spec.num_kv_heads, spec.head_dim)
+            oracle.copy_blocks_i8(st.k_cache, st.v_cache, np.array(cows), spec.num_kv_heads, spec.head_dim)
         else:
             oracle.copy_blocks(st.k_cache, st.v_cache, np.array(cows), spec.num_kv_heads,
                                spec.head_dim, spec.dtype)
         st.cow_log.extend(("step", *c) for c in cows)
     if i8:
         put = oracle.reshape_and_cache_fp8 if spec.cache == "fp8" else oracle.reshape_and_cache_i8
-        put(wl.step_k[step], wl.step_v[step], st.k_cache, st.v_cache, st.k_scales, st.v_scales, slots,
-            spec.num_kv_heads, spec.head_dim, wl.num_blocks, spec.dtype)
+        put(wl.step_k[step], wl.step_v[step], st.k_cache, st.v_cache, slots, spec.num_kv_heads, spec.head_dim,
+            wl.num_blocks, spec.dtype)
     else:
         oracle.reshape_and_cache(wl.step_k[step], wl.step_v[step], st.k_cache, st.v_cache, slots,
                                  spec.num_kv_heads, spec.head_dim, wl.num_blocks, spec.dtype)
@@ -126,8 +121,7 @@ def decode(wl, st: OracleState, max_blocks: int, nthreads: int = 0, seq_subset=N
     if seq_subset is not None:
         tab, lens, q = tab[seq_subset], lens[seq_subset], np.ascontiguousarray(q[seq_subset])
     if spec.cache in ("i8", "fp8"):
-        return oracle.decode_i8(q, spec.dtype, st.k_cache, st.v_cache, st.k_scales, st.v_scales,
-                                tab, lens, spec.num_kv_heads, spec.fp32_scale(), nthreads=nthreads,
-                                window=window, fp8=spec.cache == "fp8")
+        return oracle.decode_i8(q, spec.dtype, st.k_cache, st.v_cache, tab, lens, spec.num_kv_heads,
+                                spec.fp32_scale(), nthreads=nthreads, window=window, fp8=spec.cache == "fp8")
     return oracle.decode(q, st.k_cache, st.v_cache, tab, lens, spec.num_kv_heads,
                          spec.fp32_scale(), spec.dtype, nthreads=nthreads, window=window)

@@ -69,16 +69,24 @@ def test_i8_layout_hand_computed_offsets():
     assert oracle.k_offset_i8(0, 0, 15, 127, 1, 128) == 127 * 16 + 15
     # V (t=5, d=37), D=128: m=0, k=2, r=5, t/4=1, t%4=1 -> (0 + 16 + 5)*16 + 8 + 1
     assert oracle.v_offset_i8(0, 0, 5, 37, 1, 128) == 21 * 16 + 9
-    # tile (b=2, g=1) of Hkv=3, D=64 starts at (2*3 + 1)*16*64
-    assert oracle.k_offset_i8(2, 1, 0, 0, 3, 64) == 7 * 1024
-    assert oracle.v_offset_i8(2, 1, 0, 0, 3, 64) == 7 * 1024
+    # a tile is 16 rows of D codes followed by their 16 float32 scales: 16*(D+4)
+    # bytes; tile (b=2, g=1) of Hkv=3, D=64 starts at (2*3 + 1)*16*68 = 7616
+    assert oracle.k_offset_i8(2, 1, 0, 0, 3, 64) == 7616
+    assert oracle.v_offset_i8(2, 1, 0, 0, 3, 64) == 7616
+    # scales after the codes: token 5 of tile 0, D=128 -> 16*128 + 4*5
+    assert oracle.scale_offset_i8(0, 0, 5, 1, 128) == 2068
+    # token 15 of tile (2, 1), Hkv=3, D=64 -> 7616 + 16*64 + 60
+    assert oracle.scale_offset_i8(2, 1, 15, 3, 64) == 8700
+    assert oracle.cache_bytes_i8(5, 3, 64) == 5 * 3 * 1088
 
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_i8_layout_is_a_bijection_per_tile(D):
+    # codes of either tile kind and the 16 four-byte scales fill the tile exactly once
+    scales = [oracle.scale_offset_i8(0, 0, t, 1, D) + i for t in range(16) for i in range(4)]
     for off in (oracle.k_offset_i8, oracle.v_offset_i8):
-        seen = sorted(off(0, 0, t, d, 1, D) for t in range(16) for d in range(D))
-        assert seen == list(range(16 * D))
+        seen = sorted([off(0, 0, t, d, 1, D) for t in range(16) for d in range(D)] + scales)
+        assert seen == list(range(16 * (D + 4)))
 
 
 # ---------------------------------------------------------------- append + decode
@@ -88,8 +96,7 @@ def _pool_case(seed, lens, Hq, Hkv, D, q_dtype):
     perm = rng.permutation(nb).astype(np.int32)
     mb = max(1, max(-(-l // 16) for l in lens))
     tables = np.full((len(lens), mb), -1, dtype=np.int32)
-    kc, ks = oracle.empty_cache_i8(nb, Hkv, D)
-    vc, vs = oracle.empty_cache_i8(nb, Hkv, D)
+    kc, vc = oracle.empty_cache_i8(nb, Hkv, D), oracle.empty_cache_i8(nb, Hkv, D)
     rows_k, rows_v = [], []
     nxt = 0
     for s, L in enumerate(lens):
@@ -99,19 +106,19 @@ def _pool_case(seed, lens, Hq, Hkv, D, q_dtype):
         k = workloads.round_to(rng.standard_normal((L, Hkv, D)).astype(np.float32) * rng.uniform(0.5, 3), q_dtype)
         v = workloads.round_to(rng.standard_normal((L, Hkv, D)).astype(np.float32), q_dtype)
         slots = np.array([tables[s, i // 16] * 16 + i % 16 for i in range(L)], dtype=np.int64)
-        assert oracle.reshape_and_cache_i8(k, v, kc, vc, ks, vs, slots, Hkv, D, nb, q_dtype) == 0
+        assert oracle.reshape_and_cache_i8(k, v, kc, vc, slots, Hkv, D, nb, q_dtype) == 0
         rows_k.append(k)
         rows_v.append(v)
     q = workloads.round_to(rng.standard_normal((len(lens), Hq, D)).astype(np.float32), q_dtype)
-    return q, kc, vc, ks, vs, tables, np.array(lens, dtype=np.int32), rows_k, rows_v
+    return q, kc, vc, tables, np.array(lens, dtype=np.int32), rows_k, rows_v
 
 
 @pytest.mark.parametrize("q_dtype,Hq,Hkv,D", [("bf16", 8, 2, 128), ("f16", 4, 4, 64), ("bf16", 16, 1, 64)])
 def test_decode_i8_matches_numpy_over_rows_quantized_one_by_one(q_dtype, Hq, Hkv, D):
     lens = [1, 17, 40, 0, 33]
-    q, kc, vc, ks, vs, tables, L, rows_k, rows_v = _pool_case(11 + D, lens, Hq, Hkv, D, q_dtype)
+    q, kc, vc, tables, L, rows_k, rows_v = _pool_case(11 + D, lens, Hq, Hkv, D, q_dtype)
     scale = 1.0 / np.sqrt(D)
-    got = oracle.decode_i8(q, q_dtype, kc, vc, ks, vs, tables, L, Hkv, scale)
+    got = oracle.decode_i8(q, q_dtype, kc, vc, tables, L, Hkv, scale)
     G = Hq // Hkv
     q64 = oracle.to_float64(q, q_dtype)
     for s, n in enumerate(lens):
@@ -137,33 +144,42 @@ def test_decode_i8_matches_numpy_over_rows_quantized_one_by_one(q_dtype, Hq, Hkv
     assert np.array_equal(got[0, 0], c.astype(np.float64) * float(sc))
 
 
+def _codes(cache, nb, Hkv, D):
+    """The code bytes of every tile (rows of 16*D), scales left out."""
+    return cache.reshape(nb * Hkv, 16 * (D + 4))[:, :16 * D]
+
+
+def _scales(cache, nb, Hkv, D):
+    """The float32 row scales of every tile ([nb*Hkv][16])."""
+    return np.ascontiguousarray(cache.reshape(nb * Hkv, 16 * (D + 4))[:, 16 * D:]).view(np.float32)
+
+
 def test_reshape_and_cache_i8_writes_only_mapped_rows_and_skips_bad_slots():
     nb, Hkv, D = 4, 2, 64
-    kc, ks = oracle.empty_cache_i8(nb, Hkv, D)
-    vc, vs = oracle.empty_cache_i8(nb, Hkv, D)
+    kc, vc = oracle.empty_cache_i8(nb, Hkv, D), oracle.empty_cache_i8(nb, Hkv, D)
     rng = np.random.default_rng(3)
     k = _bf16(rng.standard_normal((3, Hkv, D)))
     v = _bf16(rng.standard_normal((3, Hkv, D)))
     slots = np.array([5, -1, 16 * nb], dtype=np.int64)
-    assert oracle.reshape_and_cache_i8(k, v, kc, vc, ks, vs, slots, Hkv, D, nb, "bf16") == 1
+    assert oracle.reshape_and_cache_i8(k, v, kc, vc, slots, Hkv, D, nb, "bf16") == 1
     for g in range(Hkv):
         c, sc = oracle.quantize_row_i8(k[0, g], "bf16")
-        assert ks[(0 * Hkv + g) * 16 + 5] == sc
+        assert oracle.read_scale(kc, 0, g, 5, Hkv, D) == sc
+        assert _scales(kc, nb, Hkv, D)[g, 5] == sc            # tile (block 0, head g), token 5
         assert [kc[oracle.k_offset_i8(0, g, 5, d, Hkv, D)] for d in range(D)] == c.tolist()
-    assert np.isnan(ks).sum() == nb * Hkv * 16 - Hkv and np.isnan(vs).sum() == nb * Hkv * 16 - Hkv
-    assert (kc != 127).sum() <= Hkv * D
+    for cache in (kc, vc):
+        assert np.isnan(_scales(cache, nb, Hkv, D)).sum() == nb * Hkv * 16 - Hkv
+        assert (_codes(cache, nb, Hkv, D) != 127).sum() <= Hkv * D
 
 
 def test_copy_blocks_i8_moves_codes_and_scales():
     nb, Hkv, D = 5, 2, 64
     rng = np.random.default_rng(4)
-    kc = rng.integers(-127, 128, nb * Hkv * 16 * D).astype(np.int8)
-    vc = rng.integers(-127, 128, nb * Hkv * 16 * D).astype(np.int8)
-    ks = rng.random(nb * Hkv * 16).astype(np.float32)
-    vs = rng.random(nb * Hkv * 16).astype(np.float32)
-    k0, v0, ks0, vs0 = kc.copy(), vc.copy(), ks.copy(), vs.copy()
-    oracle.copy_blocks_i8(kc, vc, ks, vs, [[1, 3], [4, 0]], Hkv, D)
-    B, SB = Hkv * 16 * D, Hkv * 16
+    n = oracle.cache_bytes_i8(nb, Hkv, D)
+    kc = rng.integers(-127, 128, n).astype(np.int8)
+    vc = rng.integers(-127, 128, n).astype(np.int8)
+    k0, v0 = kc.copy(), vc.copy()
+    oracle.copy_blocks_i8(kc, vc, [[1, 3], [4, 0]], Hkv, D)
+    B = Hkv * 16 * (D + 4)                      # a block: every head's codes and scales
     assert np.array_equal(kc[3 * B:4 * B], k0[1 * B:2 * B]) and np.array_equal(vc[0:B], v0[4 * B:5 * B])
-    assert np.array_equal(ks[3 * SB:4 * SB], ks0[SB:2 * SB]) and np.array_equal(vs[0:SB], vs0[4 * SB:5 * SB])
     assert np.array_equal(kc[2 * B:3 * B], k0[2 * B:3 * B])
