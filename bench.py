@@ -218,15 +218,18 @@ def build_replica(pa, torch, wl, order, k_rows_d, v_rows_d, MB, S, dev):
         slots_all.append(s_)
     slots = torch.from_numpy(np.concatenate(slots_all)).to(dev)
     n_elems = nb * spec.num_kv_heads * 16 * spec.head_dim
-    ks = vs = None
     if spec.cache in ("i8", "fp8"):
+        # byte caches: every tile holds its 16 rows' codes (0x7F unwritten), then their scales (NaN)
         code_t = torch.uint8 if spec.cache == "fp8" else torch.int8
-        kc = torch.full((n_elems,), 127, dtype=code_t, device=dev)
-        vc = torch.full((n_elems,), 127, dtype=code_t, device=dev)
-        ks = torch.full((n_elems // spec.head_dim,), float("nan"), dtype=torch.float32, device=dev)
-        vs = torch.full((n_elems // spec.head_dim,), float("nan"), dtype=torch.float32, device=dev)
+        D = spec.head_dim
+        caches = []
+        for _ in range(2):
+            c = torch.full((nb * spec.num_kv_heads * 16 * (D + 4),), 127, dtype=code_t, device=dev)
+            c.view(-1, 16 * (D + 4))[:, 16 * D:].view(torch.float32).fill_(float("nan"))
+            caches.append(c)
+        kc, vc = caches
         quantize = pa.pa_reshape_and_cache_fp8 if spec.cache == "fp8" else pa.pa_reshape_and_cache_int8
-        quantize(k_rows_d, v_rows_d, kc, vc, ks, vs, slots)
+        quantize(k_rows_d, v_rows_d, kc, vc, slots)
     else:
         dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[spec.dtype]
         kc = torch.full((n_elems,), float("nan"), dtype=dt, device=dev)
@@ -234,9 +237,7 @@ def build_replica(pa, torch, wl, order, k_rows_d, v_rows_d, MB, S, dev):
         pa.pa_reshape_and_cache(k_rows_d, v_rows_d, kc, vc, slots)
     ids = np.array(ids, dtype=np.int32)
     tab, lens = pool.seq_export(ids, MB)
-    rep = Replica(pool, ids, kc, vc, None, None, int(lens.max()), lens.copy())
-    rep.k_scales, rep.v_scales = ks, vs
-    return rep
+    return Replica(pool, ids, kc, vc, None, None, int(lens.max()), lens.copy())
 
 
 def run_gpu(args, wl, loop=False):
@@ -300,7 +301,6 @@ def run_gpu(args, wl, loop=False):
         rep.params = pa.make_decode_params(rep.out, q_d, rep.k_cache, rep.v_cache, tab_v, lens_v,
                                            Hkv, rep.max_ctx + W + K, spec.fp32_scale(),
                                            args.partition_tokens, args.kernel,
-                                           k_scales=rep.k_scales, v_scales=rep.v_scales,
                                            sliding_window=spec.window,
                                            shared_prefix_blocks=shared_prefix)
         ws_need = max(ws_need, pa.pa_decode_workspace_bytes(rep.params))
@@ -365,9 +365,7 @@ def run_gpu(args, wl, loop=False):
     rp = []
     for rep in reps:
         rp.append(dict(
-            kc=ctypes.c_void_p(rep.k_cache.data_ptr()), vc=ctypes.c_void_p(rep.v_cache.data_ptr()),
-            ks=ctypes.c_void_p(rep.k_scales.data_ptr()) if rep.k_scales is not None else None,
-            vs=ctypes.c_void_p(rep.v_scales.data_ptr()) if rep.v_scales is not None else None))
+            kc=ctypes.c_void_p(rep.k_cache.data_ptr()), vc=ctypes.c_void_p(rep.v_cache.data_ptr())))
     pool_h = [rep.pool._h for rep in reps]
     i8 = spec.cache in ("i8", "fp8")             # byte caches: codes + row scales
     append_codes = L.pa_reshape_and_cache_fp8 if spec.cache == "fp8" else L.pa_reshape_and_cache_int8
@@ -411,8 +409,7 @@ def run_gpu(args, wl, loop=False):
         prm.max_context_len = rep.max_ctx
         if ncow[j]:
             if i8:
-                pa._check(L.pa_copy_blocks_int8(q["kc"], q["vc"], q["ks"], q["vs"], pp["cows_d"],
-                                                ncow[j], Hkv, D, nb_rep, cs))
+                pa._check(L.pa_copy_blocks_int8(q["kc"], q["vc"], pp["cows_d"], ncow[j], Hkv, D, nb_rep, cs))
             else:
                 pa._check(L.pa_copy_blocks(q["kc"], q["vc"], pp["cows_d"], ncow[j], Hkv, D,
                                            nb_rep, dt_code, cs))
@@ -421,10 +418,9 @@ def run_gpu(args, wl, loop=False):
             prm.v_new = v0 + i * row_bytes
             prm.slot_mapping = pp["slots_d"]
         elif i8:
-            pa._check(append_codes(ctypes.c_void_p(k0 + i * row_bytes),
-                                                  ctypes.c_void_p(v0 + i * row_bytes), q["kc"], q["vc"],
-                                                  q["ks"], q["vs"], ctypes.c_void_p(pp["slots_d"]), S, Hkv,
-                                                  D, nb_rep, dt_code, cs))
+            pa._check(append_codes(ctypes.c_void_p(k0 + i * row_bytes), ctypes.c_void_p(v0 + i * row_bytes),
+                                   q["kc"], q["vc"], ctypes.c_void_p(pp["slots_d"]), S, Hkv, D, nb_rep, dt_code,
+                                   cs))
         else:
             pa._check(L.pa_reshape_and_cache(ctypes.c_void_p(k0 + i * row_bytes),
                                              ctypes.c_void_p(v0 + i * row_bytes), q["kc"], q["vc"],
@@ -463,7 +459,7 @@ def run_gpu(args, wl, loop=False):
             for _ in range(args.warmup):
                 pa.pa_decode(rep.out, q_d, rep.k_cache, rep.v_cache, tab_d, lens_d, Hkv, int(lens.max()),
                              spec.fp32_scale(), partition_tokens=args.partition_tokens, kernel=args.kernel,
-                             k_scales=rep.k_scales, v_scales=rep.v_scales, sliding_window=spec.window,
+                             sliding_window=spec.window,
                              shared_prefix_blocks=shared_prefix)
         torch.cuda.synchronize()
     total = W + K

@@ -48,13 +48,16 @@
  * c * sc.  Quantization ("KV Cache Explained Like You're an LLM Engineer",
  * section "Future Optimizations", subsection "KV Cache Quantization"):
  * sc = max_d |x_d| / 127 and c_d = x_d / sc truncated toward zero, both in
- * float32 (an all-zero row has sc = 0, codes 0).  Code
- * tiles are 16*head_dim bytes at byte (b*num_kv_heads + g)*16*head_dim:
- *   K: (t, d) -> (c*64 + q*16 + t)*16 + h*8 + e,  with c = d/64, w = d%64,
- *               h = w/32, q = (w%32)/8, e = w%8
- *   V: (t, d) -> (m*64 + (t/4)*16 + d%16)*16 + ((d%64)/16)*4 + t%4,  m = d/64
- * (again one 16-byte lane load per operand fragment); scales are float32
- * arrays k_scales, v_scales [num_blocks][num_kv_heads][16].
+ * float32 (an all-zero row has sc = 0, codes 0).  A byte cache (K or V) is
+ * one array of tiles of 16*(head_dim + 4) bytes, tile (b, g) at byte
+ * (b*num_kv_heads + g)*16*(head_dim + 4): the 16 rows' codes, then their 16
+ * float32 scales, so one (block, head) is one contiguous run.  In a tile:
+ *   K code (t, d) -> (c*64 + q*16 + t)*16 + h*8 + e,  with c = d/64, w = d%64,
+ *                    h = w/32, q = (w%32)/8, e = w%8
+ *   V code (t, d) -> (m*64 + (t/4)*16 + d%16)*16 + ((d%64)/16)*4 + t%4,
+ *                    m = d/64
+ *   scale of t   -> bytes 16*head_dim + 4t .. +3 (float32)
+ * (again one 16-byte lane load per operand fragment).
  *
  * FP8 caches (PA_FP8): the same tiles and scales with OCP E4M3 codes (sign,
  * 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 subnormal,
@@ -63,8 +66,8 @@
  * division), ties to the even code, saturating at +-448 -- the int8 recipe
  * above with FP8's range ("Inference serving: the KV-cache machine", What
  * insiders know, names an fp8 KV cache with per-head scales but no recipe).
- * pa_copy_blocks_int8 and pa_swap_blocks_int8 move the codes and scales of
- * either kind of byte cache.
+ * pa_copy_blocks_int8 and pa_swap_blocks_int8 move the tiles (codes and
+ * scales) of either kind of byte cache.
  */
 #ifndef PA_H
 #define PA_H
@@ -212,16 +215,14 @@ typedef struct pa_decode_params {
   const void *v_new;
   const int64_t *slot_mapping;
   /* INT8 and FP8 caches (kv_dtype = PA_I8 or PA_FP8) only, else ignored: the
-   * type of q (F16 or BF16; out_dtype is F32 or q_dtype) and the float32
-   * scale arrays [num_blocks][num_kv_heads][16].  Decoding a byte cache needs
-   * the matrix-core kernel and automatic partitioning (the balanced split).
-   * With a byte cache the fused append's k_new / v_new rows are q_dtype
-   * (F16 or BF16) and are quantized exactly as pa_reshape_and_cache_int8 /
-   * _fp8 quantize them (codes and the scale written to the cache, the same
-   * values attended). */
+   * type of q (F16 or BF16; out_dtype is F32 or q_dtype).  k_cache / v_cache
+   * are then byte caches (codes and row scales in their tiles, above).
+   * Decoding a byte cache needs the matrix-core kernel and automatic
+   * partitioning (the balanced split).  With a byte cache the fused append's
+   * k_new / v_new rows are q_dtype (F16 or BF16) and are quantized exactly as
+   * pa_reshape_and_cache_int8 / _fp8 quantize them (codes and the scale
+   * written to the cache, the same values attended). */
   pa_dtype q_dtype;
-  const float *k_scales;
-  const float *v_scales;
   /* Optional hipEvent_t handles (NULL = none), created by the caller.  They
    * are recorded from the kernel dispatches' own start and end times
    * (hipExtLaunchKernel), so timing a launch adds no marker to the stream:
@@ -329,11 +330,10 @@ pa_status pa_reshape_and_cache(const void *k_new, const void *v_new, void *k_cac
 
 /* pa_reshape_and_cache into an INT8 cache: each (token, KV head) row of
  * k_new / v_new (src_dtype F16 or BF16) is quantized as described under
- * "INT8 caches" and stored with its scale.  Codes and scales are bit-exact
- * with that definition (float32 division, correctly rounded). */
+ * "INT8 caches" and stored with its scale in its tile.  Codes and scales are
+ * bit-exact with that definition (float32 division, correctly rounded). */
 pa_status pa_reshape_and_cache_int8(const void *k_new, const void *v_new, int8_t *k_cache,
-                                    int8_t *v_cache, float *k_scales, float *v_scales,
-                                    const int64_t *slot_mapping, int32_t num_tokens,
+                                    int8_t *v_cache, const int64_t *slot_mapping, int32_t num_tokens,
                                     int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                                     pa_dtype src_dtype, void *stream);
 
@@ -428,25 +428,25 @@ pa_status pa_swap_blocks(const void *src_k, const void *src_v, int32_t src_num_b
                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
                          void *stream);
 
-/* pa_swap_blocks for INT8 caches: codes and the per-row scales of every head. */
-pa_status pa_swap_blocks_int8(const int8_t *src_k, const int8_t *src_v, const float *src_k_scales,
-                              const float *src_v_scales, int32_t src_num_blocks, int8_t *dst_k,
-                              int8_t *dst_v, float *dst_k_scales, float *dst_v_scales,
-                              int32_t dst_num_blocks, const int32_t *src_dst_pairs, int32_t num_pairs,
-                              int32_t num_kv_heads, int32_t head_dim, void *stream);
+/* pa_swap_blocks for INT8 and FP8 caches: the tiles (codes and row scales)
+ * of every head. */
+pa_status pa_swap_blocks_int8(const int8_t *src_k, const int8_t *src_v, int32_t src_num_blocks,
+                              int8_t *dst_k, int8_t *dst_v, int32_t dst_num_blocks,
+                              const int32_t *src_dst_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                              int32_t head_dim, void *stream);
 
 /* pa_reshape_and_cache_int8 for an FP8 (E4M3) cache: codes and scales are
  * bit-exact to the recipe under "FP8 caches". */
 pa_status pa_reshape_and_cache_fp8(const void *k_new, const void *v_new, uint8_t *k_cache,
-                                   uint8_t *v_cache, float *k_scales, float *v_scales,
-                                   const int64_t *slot_mapping, int32_t num_tokens,
+                                   uint8_t *v_cache, const int64_t *slot_mapping, int32_t num_tokens,
                                    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                                    pa_dtype src_dtype, void *stream);
 
-/* pa_copy_blocks for an INT8 or FP8 cache: codes and scales of every head. */
-pa_status pa_copy_blocks_int8(int8_t *k_cache, int8_t *v_cache, float *k_scales, float *v_scales,
-                              const int32_t *src_dst_pairs, int32_t num_pairs, int32_t num_kv_heads,
-                              int32_t head_dim, int32_t num_blocks, void *stream);
+/* pa_copy_blocks for an INT8 or FP8 cache: the tiles (codes and scales) of
+ * every head. */
+pa_status pa_copy_blocks_int8(int8_t *k_cache, int8_t *v_cache, const int32_t *src_dst_pairs,
+                              int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t num_blocks, void *stream);
 
 /* ------------------------------------------------------------------------
  * Host-side block pool.  Blocks are allocated on demand and returned when

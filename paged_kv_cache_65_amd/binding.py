@@ -46,7 +46,7 @@ class pa_decode_params(ctypes.Structure):
                 ("max_context_len", _I32), ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int),
                 ("out_dtype", ctypes.c_int), ("partition_tokens", _I32), ("kernel", ctypes.c_int),
                 ("k_new", _P), ("v_new", _P), ("slot_mapping", _P),
-                ("q_dtype", ctypes.c_int), ("k_scales", _P), ("v_scales", _P),
+                ("q_dtype", ctypes.c_int),
                 ("start_event", _P), ("stop_event", _P), ("sliding_window", _I32),
                 ("shared_prefix_blocks", _I32)]
 
@@ -86,15 +86,14 @@ def lib():
             "pa_reshape_and_cache": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                                     ctypes.c_int, _P]),
             "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, ctypes.c_int, _P]),
-            "pa_reshape_and_cache_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
-                                                         _I32, ctypes.c_int, _P]),
-            "pa_copy_blocks_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P]),
-            "pa_reshape_and_cache_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
-                                                        _I32, ctypes.c_int, _P]),
+            "pa_reshape_and_cache_int8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                                         ctypes.c_int, _P]),
+            "pa_copy_blocks_int8": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P]),
+            "pa_reshape_and_cache_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                                        ctypes.c_int, _P]),
             "pa_swap_blocks": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I32, _P, _I32, _I32, _I32,
                                               ctypes.c_int, _P]),
-            "pa_swap_blocks_int8": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _P, _P, _I32, _P,
-                                                   _I32, _I32, _I32, _P]),
+            "pa_swap_blocks_int8": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I32, _P, _I32, _I32, _I32, _P]),
             "pa_seq_swap_out": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32]),
             "pa_seq_swap_in": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32]),
             "pa_seq_swapped_blocks": (_I32, [_P, _I32]),
@@ -172,21 +171,26 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def block_elems(cache, num_kv_heads, head_dim) -> int:
+    """Elements of one block of a cache tensor: a byte cache (int8 / uint8 /
+    float8 codes) holds its 16 row scales in every tile (16*(D+4) bytes)."""
+    return num_kv_heads * BLOCK_SIZE * (head_dim + 4 if cache.element_size() == 1 else head_dim)
+
+
 def make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
                        max_context_len, scale, partition_tokens=0, kernel="auto", k_new=None,
-                       v_new=None, slot_mapping=None, k_scales=None, v_scales=None,
-                       start_event=None, stop_event=None, sliding_window=0, shared_prefix_blocks=0):
-    """k_scales / v_scales: the float32 scale arrays of an int8 cache (else None).
-    start_event / stop_event: raw hipEvent_t handles (ints) or None.
+                       v_new=None, slot_mapping=None, start_event=None, stop_event=None,
+                       sliding_window=0, shared_prefix_blocks=0):
+    """start_event / stop_event: raw hipEvent_t handles (ints) or None.
     sliding_window: W > 0 attends positions L-1-W .. L-1 only; 0 = the whole context."""
     S, Hq, D = q.shape
-    nb = k_cache.numel() // (num_kv_heads * BLOCK_SIZE * D)
+    nb = k_cache.numel() // block_elems(k_cache, num_kv_heads, D)
     return pa_decode_params(
         _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), _dev(context_lens),
         S, Hq, num_kv_heads, D, block_tables.shape[1] if block_tables.dim() == 2 else 0, nb,
         int(max_context_len), float(scale), _dtype_code(k_cache), _dtype_code(out),
         int(partition_tokens), KERNELS[kernel], _dev(k_new), _dev(v_new), _dev(slot_mapping),
-        _dtype_code(q), _dev(k_scales), _dev(v_scales), _event(start_event), _event(stop_event),
+        _dtype_code(q), _event(start_event), _event(stop_event),
         int(sliding_window), int(shared_prefix_blocks))
 
 
@@ -209,17 +213,17 @@ def pa_decode_partition_tokens(params: pa_decode_params) -> int:
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
               max_context_len, scale, partition_tokens=0, kernel="auto", workspace=None,
-              stream=None, k_new=None, v_new=None, slot_mapping=None, k_scales=None,
-              v_scales=None, sliding_window=0, shared_prefix_blocks=0):
+              stream=None, k_new=None, v_new=None, slot_mapping=None, sliding_window=0,
+              shared_prefix_blocks=0):
     """out <- paged decode attention (optionally appending k_new/v_new first).
     workspace: a uint8 device tensor of at least pa_decode_workspace_bytes()
     bytes (no initialization needed), or None to allocate one.  For an int8
-    cache pass its k_scales / v_scales."""
+    cache (codes and scales in its tiles) q gives the q type."""
     import torch
     params = make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens,
                                 num_kv_heads, max_context_len, scale, partition_tokens, kernel,
-                                k_new, v_new, slot_mapping, k_scales, v_scales,
-                                sliding_window=sliding_window, shared_prefix_blocks=shared_prefix_blocks)
+                                k_new, v_new, slot_mapping, sliding_window=sliding_window,
+                                shared_prefix_blocks=shared_prefix_blocks)
     need = pa_decode_workspace_bytes(params)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -231,13 +235,12 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads
 
 def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
                       max_context_len, scale, partition_tokens=0, kernel="auto", stream=None,
-                      k_new=None, v_new=None, slot_mapping=None, k_scales=None, v_scales=None,
-                      sliding_window=0, shared_prefix_blocks=0):
+                      k_new=None, v_new=None, slot_mapping=None, sliding_window=0, shared_prefix_blocks=0):
     """pa_decode with the library's own per-device workspace: allocates nothing."""
     params = make_decode_params(out, q, k_cache, v_cache, block_tables, context_lens,
                                 num_kv_heads, max_context_len, scale, partition_tokens, kernel,
-                                k_new, v_new, slot_mapping, k_scales, v_scales,
-                                sliding_window=sliding_window, shared_prefix_blocks=shared_prefix_blocks)
+                                k_new, v_new, slot_mapping, sliding_window=sliding_window,
+                                shared_prefix_blocks=shared_prefix_blocks)
     _check(lib().pa_decode_noalloc(ctypes.byref(params), _stream(stream)))
     return out
 
@@ -308,33 +311,29 @@ def pa_reshape_and_cache(k_new, v_new, k_cache, v_cache, slot_mapping, stream=No
                                       _stream(stream)))
 
 
-def pa_reshape_and_cache_int8(k_new, v_new, k_cache, v_cache, k_scales, v_scales, slot_mapping,
-                              stream=None):
-    """Quantize [T][Hkv][D] fp16/bf16 rows into an int8 cache and its scales."""
+def pa_reshape_and_cache_int8(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
+    """Quantize [T][Hkv][D] fp16/bf16 rows into an int8 cache (codes and scales in its tiles)."""
     T, Hkv, D = k_new.shape
-    nb = k_cache.numel() // (Hkv * BLOCK_SIZE * D)
+    nb = k_cache.numel() // block_elems(k_cache, Hkv, D)
     _check(lib().pa_reshape_and_cache_int8(_dev(k_new), _dev(v_new), _dev(k_cache), _dev(v_cache),
-                                           _dev(k_scales), _dev(v_scales), _dev(slot_mapping), T,
-                                           Hkv, D, nb, _dtype_code(k_new), _stream(stream)))
+                                           _dev(slot_mapping), T, Hkv, D, nb, _dtype_code(k_new),
+                                           _stream(stream)))
 
 
-def pa_reshape_and_cache_fp8(k_new, v_new, k_cache, v_cache, k_scales, v_scales, slot_mapping,
-                             stream=None):
-    """Quantize [T][Hkv][D] fp16/bf16 rows into an E4M3 cache (uint8 codes) and its scales."""
+def pa_reshape_and_cache_fp8(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
+    """Quantize [T][Hkv][D] fp16/bf16 rows into an E4M3 cache (uint8 codes and scales in its tiles)."""
     T, Hkv, D = k_new.shape
-    nb = k_cache.numel() // (Hkv * BLOCK_SIZE * D)
+    nb = k_cache.numel() // block_elems(k_cache, Hkv, D)
     _check(lib().pa_reshape_and_cache_fp8(_dev(k_new), _dev(v_new), _dev(k_cache), _dev(v_cache),
-                                          _dev(k_scales), _dev(v_scales), _dev(slot_mapping), T,
-                                          Hkv, D, nb, _dtype_code(k_new), _stream(stream)))
+                                          _dev(slot_mapping), T, Hkv, D, nb, _dtype_code(k_new),
+                                          _stream(stream)))
 
 
-def pa_copy_blocks_int8(k_cache, v_cache, k_scales, v_scales, src_dst_pairs, num_kv_heads,
-                        head_dim, stream=None):
+def pa_copy_blocks_int8(k_cache, v_cache, src_dst_pairs, num_kv_heads, head_dim, stream=None):
     n = src_dst_pairs.numel() // 2
-    nb = k_cache.numel() // (num_kv_heads * BLOCK_SIZE * head_dim)
-    _check(lib().pa_copy_blocks_int8(_dev(k_cache), _dev(v_cache), _dev(k_scales), _dev(v_scales),
-                                     _dev(src_dst_pairs), n, num_kv_heads, head_dim, nb,
-                                     _stream(stream)))
+    nb = k_cache.numel() // block_elems(k_cache, num_kv_heads, head_dim)
+    _check(lib().pa_copy_blocks_int8(_dev(k_cache), _dev(v_cache), _dev(src_dst_pairs), n, num_kv_heads,
+                                     head_dim, nb, _stream(stream)))
 
 
 def pa_swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs, num_kv_heads, head_dim, stream=None):
@@ -348,14 +347,14 @@ def pa_swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs, num_kv_heads, head
                                 _dtype_code(src_k), _stream(stream)))
 
 
-def pa_swap_blocks_int8(src_k, src_v, src_ks, src_vs, dst_k, dst_v, dst_ks, dst_vs, src_dst_pairs,
-                        num_kv_heads, head_dim, stream=None):
+def pa_swap_blocks_int8(src_k, src_v, dst_k, dst_v, src_dst_pairs, num_kv_heads, head_dim, stream=None):
+    """Block copies between two byte caches (codes and scales in their tiles)."""
     n = src_dst_pairs.numel() // 2
-    per = num_kv_heads * BLOCK_SIZE * head_dim
+    per = block_elems(src_k, num_kv_heads, head_dim)
     g = _gpu_addressable
-    _check(lib().pa_swap_blocks_int8(g(src_k), g(src_v), g(src_ks), g(src_vs), src_k.numel() // per,
-                                     g(dst_k), g(dst_v), g(dst_ks), g(dst_vs), dst_k.numel() // per,
-                                     g(src_dst_pairs), n, num_kv_heads, head_dim, _stream(stream)))
+    _check(lib().pa_swap_blocks_int8(g(src_k), g(src_v), src_k.numel() // per, g(dst_k), g(dst_v),
+                                     dst_k.numel() // per, g(src_dst_pairs), n, num_kv_heads, head_dim,
+                                     _stream(stream)))
 
 
 def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, num_kv_heads, head_dim, stream=None):

@@ -164,8 +164,6 @@ struct DecodeArgs {
   const int32_t *context_lens;
   float *ws_ml;   // [S][Hq][max_parts][2]  (m in log2 units, l)
   float *ws_acc;  // [S][Hq][max_parts][D]  unnormalised weighted V sums
-  const float *k_scales;         // INT8 caches: [NB][Hkv][16] per-row scales
-  const float *v_scales;
   const uint8_t *k_new;          // fused append: [S][Hkv][D] rows of the step's token, or null
   const uint8_t *v_new;
   const int64_t *slot_mapping;   // fused append: [S] slot of position L-1 (negative = no append)
@@ -702,7 +700,7 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D, NCT_> {
   using Base::NCT;
   using Base::NT;
   static constexpr int NV = D / 64;        // 16-byte code vectors per lane and tile
-  static constexpr int TILE = kBS * D;     // code bytes per (block, head) tile
+  static constexpr int TILE = kBS * (D + 4);  // bytes per (block, head) tile: codes, then 16 row scales
   static constexpr bool kAppend = true;    // new rows (QDT) quantized as pa_reshape_and_cache_int8 / _fp8 do
   // The code conversions add ~250 VALU instructions per block: more waves per
   // SIMD hide their latency, a shallower ring keeps them in registers.  With
@@ -727,8 +725,9 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D, NCT_> {
     for (int x = 0; x < NV; ++x) f.k[x] = __builtin_nontemporal_load(&kp[x * 64 + lane]);
 #pragma unroll
     for (int x = 0; x < NV; ++x) f.v[x] = __builtin_nontemporal_load(&vp[x * 64 + lane]);
-    const f32x4_t *ksp = reinterpret_cast<const f32x4_t *>(a.k_scales + tile * kBS);
-    const f32x4_t *vsp = reinterpret_cast<const f32x4_t *>(a.v_scales + tile * kBS);
+    // the tile's 16 row scales follow its codes (lane l takes those of its tokens 4(l/16) ..)
+    const f32x4_t *ksp = reinterpret_cast<const f32x4_t *>(a.k_cache + tile * TILE + kBS * D);
+    const f32x4_t *vsp = reinterpret_cast<const f32x4_t *>(a.v_cache + tile * TILE + kBS * D);
     f.ks = __builtin_nontemporal_load(&ksp[lane / 16]);
     f.vs = __builtin_nontemporal_load(&vsp[lane / 16]);
   }
@@ -841,8 +840,8 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D, NCT_> {
       vc[v_code_off(d, t)] = vb[d];
     }
     if (lane == 0) {
-      const_cast<float *>(a.k_scales)[tile * kBS + t] = reinterpret_cast<const float *>(knew)[D / 4];
-      const_cast<float *>(a.v_scales)[tile * kBS + t] = reinterpret_cast<const float *>(vnew)[D / 4];
+      reinterpret_cast<float *>(kc + kBS * D)[t] = reinterpret_cast<const float *>(knew)[D / 4];
+      reinterpret_cast<float *>(vc + kBS * D)[t] = reinterpret_cast<const float *>(vnew)[D / 4];
     }
   }
   // Replaces token t's codes and scales in a tile's fragments with the staged
@@ -2368,9 +2367,10 @@ __global__ __launch_bounds__(256) void pa_reshape_and_cache_kernel(
 
 // ---------------------------------------------------------------- INT8 / FP8 append
 // (quantizer helpers: with the byte-code wave policy above)
+// One row into its tile: the codes at their places, the scale after the
+// tile's codes (byte 16*D + 4t).
 template <int SDT, int D, int FMT>
-__device__ void quantize_row_i8(const uint16_t *x, int8_t *tile_codes, float *scale_out, int t, bool is_v,
-                                int lane) {
+__device__ void quantize_row_i8(const uint16_t *x, int8_t *tile, int t, bool is_v, int lane) {
   constexpr int PER = D / 64;
   float v[PER];
   float amax = 0.f;
@@ -2385,16 +2385,15 @@ __device__ void quantize_row_i8(const uint16_t *x, int8_t *tile_codes, float *sc
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int d = lane * PER + e;
-    tile_codes[is_v ? v_code_off(d, t) : k_code_off(d, t)] = (int8_t)code_of<FMT>(v[e], scale);
+    tile[is_v ? v_code_off(d, t) : k_code_off(d, t)] = (int8_t)code_of<FMT>(v[e], scale);
   }
-  if (lane == 0) *scale_out = scale;
+  if (lane == 0) reinterpret_cast<float *>(tile + kBS * D)[t] = scale;
 }
 
 template <int SDT, int D, int FMT>
 __global__ __launch_bounds__(256) void pa_reshape_and_cache_i8_kernel(
     const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new, int8_t *k_cache, int8_t *v_cache,
-    float *k_scales, float *v_scales, const int64_t *__restrict__ slots, int32_t num_tokens,
-    int32_t num_kv_heads, int64_t num_slots) {
+    const int64_t *__restrict__ slots, int32_t num_tokens, int32_t num_kv_heads, int64_t num_slots) {
   const int lane = threadIdx.x % 64;
   const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // token * Hkv + head
   if (row >= (int64_t)num_tokens * num_kv_heads) return;
@@ -2404,8 +2403,9 @@ __global__ __launch_bounds__(256) void pa_reshape_and_cache_i8_kernel(
   if (slot < 0 || slot >= num_slots) return;
   const int64_t tile = (slot / kBS) * num_kv_heads + g;
   const int t = (int)(slot % kBS);
-  quantize_row_i8<SDT, D, FMT>(k_new + row * D, k_cache + tile * kBS * D, k_scales + tile * kBS + t, t, false, lane);
-  quantize_row_i8<SDT, D, FMT>(v_new + row * D, v_cache + tile * kBS * D, v_scales + tile * kBS + t, t, true, lane);
+  constexpr int64_t kTileBytes = kBS * (D + 4);  // codes, then the 16 row scales
+  quantize_row_i8<SDT, D, FMT>(k_new + row * D, k_cache + tile * kTileBytes, t, false, lane);
+  quantize_row_i8<SDT, D, FMT>(v_new + row * D, v_cache + tile * kTileBytes, t, true, lane);
 }
 
 // ---------------------------------------------------------------- block copy
@@ -2506,8 +2506,6 @@ pa_status validate(const pa_decode_params *p) {
       return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: an INT8/FP8 cache needs q_dtype F16 or BF16");
     if (p->out_dtype != PA_F32 && p->out_dtype != p->q_dtype)
       return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype must be F32 or q_dtype");
-    if (!p->k_scales || !p->v_scales || !aligned16(p->k_scales) || !aligned16(p->v_scales))
-      return pa::fail(PA_ERR_INVALID_ARG, "pa_decode: an INT8/FP8 cache needs 16-byte aligned scale arrays");
     if (p->kernel == PA_KERNEL_VALU || p->partition_tokens > 0)
       return pa::fail(PA_ERR_UNSUPPORTED,
                       "pa_decode: an INT8/FP8 cache is decoded by the matrix-core kernel with automatic "
@@ -2907,8 +2905,6 @@ pa_status prepare(const pa_decode_params *p, void *workspace, size_t workspace_b
   a.v_cache = static_cast<const uint8_t *>(p->v_cache);
   a.block_tables = p->block_tables;
   a.context_lens = p->context_lens;
-  a.k_scales = byte_cache(p->kv_dtype) ? p->k_scales : nullptr;
-  a.v_scales = byte_cache(p->kv_dtype) ? p->v_scales : nullptr;
   a.k_new = static_cast<const uint8_t *>(p->k_new);
   a.v_new = static_cast<const uint8_t *>(p->v_new);
   a.slot_mapping = p->slot_mapping;
@@ -3227,19 +3223,19 @@ pa_status pa_reshape_and_cache(const void *k_new, const void *v_new, void *k_cac
 namespace {
 
 template <int FMT>
-pa_status reshape_codes(const void *k_new, const void *v_new, void *k_cache, void *v_cache, float *k_scales,
-                        float *v_scales, const int64_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
-                        int32_t head_dim, int32_t num_blocks, pa_dtype src_dtype, void *stream, const char *who) {
+pa_status reshape_codes(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                        const int64_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t num_blocks, pa_dtype src_dtype, void *stream, const char *who) {
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return pa::fail(PA_ERR_INVALID_ARG, "%s: bad sizes", who);
   if (head_dim != 64 && head_dim != 128)
     return pa::fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128", who);
   if (src_dtype != PA_F16 && src_dtype != PA_BF16)
     return pa::fail(PA_ERR_UNSUPPORTED, "%s: rows must be F16 or BF16", who);
   if (num_tokens == 0) return PA_OK;
-  if (!k_new || !v_new || !k_cache || !v_cache || !k_scales || !v_scales || !slot_mapping)
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)
     return pa::fail(PA_ERR_INVALID_ARG, "%s: NULL device pointer", who);
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned16(k_scales) || !aligned16(v_scales) || !aligned16(slot_mapping))
+      !aligned16(slot_mapping))
     return pa::fail(PA_ERR_INVALID_ARG, "%s: device pointers must be 16-byte aligned", who);
   const int64_t rows = (int64_t)num_tokens * num_kv_heads;
   const dim3 grid((unsigned)((rows + 3) / 4));
@@ -3250,13 +3246,13 @@ pa_status reshape_codes(const void *k_new, const void *v_new, void *k_cache, voi
   auto *vc = static_cast<int8_t *>(v_cache);
   const int64_t nslots = (int64_t)num_blocks * kBS;
   if (src_dtype == PA_BF16 && head_dim == 128)
-    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_BF16, 128, FMT>), grid, dim3(256), 0, hs, kn, vn, kc, vc, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
+    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_BF16, 128, FMT>), grid, dim3(256), 0, hs, kn, vn, kc, vc, slot_mapping, num_tokens, num_kv_heads, nslots);
   else if (src_dtype == PA_BF16)
-    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_BF16, 64, FMT>), grid, dim3(256), 0, hs, kn, vn, kc, vc, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
+    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_BF16, 64, FMT>), grid, dim3(256), 0, hs, kn, vn, kc, vc, slot_mapping, num_tokens, num_kv_heads, nslots);
   else if (head_dim == 128)
-    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_F16, 128, FMT>), grid, dim3(256), 0, hs, kn, vn, kc, vc, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
+    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_F16, 128, FMT>), grid, dim3(256), 0, hs, kn, vn, kc, vc, slot_mapping, num_tokens, num_kv_heads, nslots);
   else
-    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_F16, 64, FMT>), grid, dim3(256), 0, hs, kn, vn, kc, vc, k_scales, v_scales, slot_mapping, num_tokens, num_kv_heads, nslots);
+    hipLaunchKernelGGL((pa_reshape_and_cache_i8_kernel<PA_F16, 64, FMT>), grid, dim3(256), 0, hs, kn, vn, kc, vc, slot_mapping, num_tokens, num_kv_heads, nslots);
   return hip_check(hipGetLastError(), who);
 }
 
@@ -3265,41 +3261,34 @@ pa_status reshape_codes(const void *k_new, const void *v_new, void *k_cache, voi
 extern "C" {
 
 pa_status pa_reshape_and_cache_int8(const void *k_new, const void *v_new, int8_t *k_cache, int8_t *v_cache,
-                                    float *k_scales, float *v_scales, const int64_t *slot_mapping,
-                                    int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-                                    int32_t num_blocks, pa_dtype src_dtype, void *stream) {
-  return reshape_codes<PA_I8>(k_new, v_new, k_cache, v_cache, k_scales, v_scales, slot_mapping, num_tokens,
-                              num_kv_heads, head_dim, num_blocks, src_dtype, stream, "pa_reshape_and_cache_int8");
+                                    const int64_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t num_blocks, pa_dtype src_dtype, void *stream) {
+  return reshape_codes<PA_I8>(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                              num_blocks, src_dtype, stream, "pa_reshape_and_cache_int8");
 }
 
 pa_status pa_reshape_and_cache_fp8(const void *k_new, const void *v_new, uint8_t *k_cache, uint8_t *v_cache,
-                                   float *k_scales, float *v_scales, const int64_t *slot_mapping,
-                                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-                                   int32_t num_blocks, pa_dtype src_dtype, void *stream) {
-  return reshape_codes<PA_FP8>(k_new, v_new, k_cache, v_cache, k_scales, v_scales, slot_mapping, num_tokens,
-                               num_kv_heads, head_dim, num_blocks, src_dtype, stream, "pa_reshape_and_cache_fp8");
+                                   const int64_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t num_blocks, pa_dtype src_dtype, void *stream) {
+  return reshape_codes<PA_FP8>(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                               num_blocks, src_dtype, stream, "pa_reshape_and_cache_fp8");
 }
 
-pa_status pa_copy_blocks_int8(int8_t *k_cache, int8_t *v_cache, float *k_scales, float *v_scales,
-                              const int32_t *src_dst_pairs, int32_t num_pairs, int32_t num_kv_heads,
-                              int32_t head_dim, int32_t num_blocks, void *stream) {
+pa_status pa_copy_blocks_int8(int8_t *k_cache, int8_t *v_cache, const int32_t *src_dst_pairs, int32_t num_pairs,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, void *stream) {
   if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_copy_blocks_int8: bad sizes");
   if (head_dim != 64 && head_dim != 128)
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks_int8: head_dim must be 64 or 128");
   if (num_pairs == 0) return PA_OK;
-  if (!k_cache || !v_cache || !k_scales || !v_scales || !src_dst_pairs)
+  if (!k_cache || !v_cache || !src_dst_pairs)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_copy_blocks_int8: NULL device pointer");
-  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_scales) || !aligned16(v_scales))
+  if (!aligned16(k_cache) || !aligned16(v_cache))
     return pa::fail(PA_ERR_INVALID_ARG, "pa_copy_blocks_int8: caches must be 16-byte aligned");
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  // codes, then scales: each a [num_blocks] array of equal-size blocks
-  hipLaunchKernelGGL(pa_copy_blocks_kernel, dim3(num_pairs), dim3(256), 0, hs, reinterpret_cast<uint8_t *>(k_cache),
-                     reinterpret_cast<uint8_t *>(v_cache), src_dst_pairs, (int64_t)num_kv_heads * kBS * head_dim,
-                     num_blocks);
-  hipLaunchKernelGGL(pa_copy_blocks_kernel, dim3(num_pairs), dim3(256), 0, hs, reinterpret_cast<uint8_t *>(k_scales),
-                     reinterpret_cast<uint8_t *>(v_scales), src_dst_pairs,
-                     (int64_t)num_kv_heads * kBS * (int64_t)sizeof(float), num_blocks);
+  // a block: every head's tile of codes and row scales
+  hipLaunchKernelGGL(pa_copy_blocks_kernel, dim3(num_pairs), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     reinterpret_cast<uint8_t *>(k_cache), reinterpret_cast<uint8_t *>(v_cache), src_dst_pairs,
+                     (int64_t)num_kv_heads * kBS * (head_dim + 4), num_blocks);
   return hip_check(hipGetLastError(), "pa_copy_blocks_int8 launch");
 }
 
@@ -3378,23 +3367,18 @@ pa_status pa_swap_blocks(const void *src_k, const void *src_v, int32_t src_num_b
                      static_cast<hipStream_t>(stream), "pa_swap_blocks launch");
 }
 
-pa_status pa_swap_blocks_int8(const int8_t *src_k, const int8_t *src_v, const float *src_k_scales,
-                              const float *src_v_scales, int32_t src_num_blocks, int8_t *dst_k, int8_t *dst_v,
-                              float *dst_k_scales, float *dst_v_scales, int32_t dst_num_blocks,
-                              const int32_t *src_dst_pairs, int32_t num_pairs, int32_t num_kv_heads,
-                              int32_t head_dim, void *stream) {
-  const void *ptrs[] = {src_k, src_v, src_k_scales, src_v_scales, dst_k, dst_v, dst_k_scales, dst_v_scales};
+pa_status pa_swap_blocks_int8(const int8_t *src_k, const int8_t *src_v, int32_t src_num_blocks, int8_t *dst_k,
+                              int8_t *dst_v, int32_t dst_num_blocks, const int32_t *src_dst_pairs, int32_t num_pairs,
+                              int32_t num_kv_heads, int32_t head_dim, void *stream) {
+  const void *ptrs[] = {src_k, src_v, dst_k, dst_v};
   const int32_t *pairs = src_dst_pairs;
-  pa_status st = check_swap_args(num_pairs, num_kv_heads, head_dim, src_num_blocks, dst_num_blocks, ptrs, 8,
+  pa_status st = check_swap_args(num_pairs, num_kv_heads, head_dim, src_num_blocks, dst_num_blocks, ptrs, 4,
                                  &pairs, "pa_swap_blocks_int8");
   if (st != PA_OK || num_pairs == 0) return st;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  auto w = [&](int i) { return const_cast<void *>(ptrs[i]); };
-  st = launch_swap(ptrs[0], ptrs[1], src_num_blocks, w(4), w(5), dst_num_blocks, pairs, num_pairs,
-                   (int64_t)num_kv_heads * kBS * head_dim, hs, "pa_swap_blocks_int8 launch");
-  if (st != PA_OK) return st;
-  return launch_swap(ptrs[2], ptrs[3], src_num_blocks, w(6), w(7), dst_num_blocks, pairs, num_pairs,
-                     (int64_t)num_kv_heads * kBS * (int64_t)sizeof(float), hs, "pa_swap_blocks_int8 launch");
+  // a block: every head's tile of codes and row scales
+  return launch_swap(ptrs[0], ptrs[1], src_num_blocks, const_cast<void *>(ptrs[2]), const_cast<void *>(ptrs[3]),
+                     dst_num_blocks, pairs, num_pairs, (int64_t)num_kv_heads * kBS * (head_dim + 4),
+                     static_cast<hipStream_t>(stream), "pa_swap_blocks_int8 launch");
 }
 
 pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_dst_pairs, int32_t num_pairs,

@@ -49,8 +49,6 @@ class GpuState:
     prefix_slots: list
     step_slots: list
     cow_log: list
-    k_scales: torch.Tensor = None   # int8 caches: per-row scales
-    v_scales: torch.Tensor = None
 
 
 def _append_rows(st, k_rows, v_rows, slots, spec, cow_pairs):
@@ -59,7 +57,7 @@ def _append_rows(st, k_rows, v_rows, slots, spec, cow_pairs):
     if len(cow_pairs):
         pairs = torch.from_numpy(np.ascontiguousarray(cow_pairs, dtype=np.int32)).to(dev)
         if i8:
-            pa.pa_copy_blocks_int8(st.k_cache, st.v_cache, st.k_scales, st.v_scales, pairs,
+            pa.pa_copy_blocks_int8(st.k_cache, st.v_cache, pairs,
                                    spec.num_kv_heads, spec.head_dim)
         else:
             pa.pa_copy_blocks(st.k_cache, st.v_cache, pairs, spec.num_kv_heads, spec.head_dim)
@@ -67,20 +65,20 @@ def _append_rows(st, k_rows, v_rows, slots, spec, cow_pairs):
         s = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).to(dev)
         kd, vd = to_device(k_rows, spec.dtype, dev), to_device(v_rows, spec.dtype, dev)
         if spec.cache == "fp8":
-            pa.pa_reshape_and_cache_fp8(kd, vd, st.k_cache, st.v_cache, st.k_scales, st.v_scales, s)
+            pa.pa_reshape_and_cache_fp8(kd, vd, st.k_cache, st.v_cache, s)
         elif i8:
-            pa.pa_reshape_and_cache_int8(kd, vd, st.k_cache, st.v_cache, st.k_scales, st.v_scales, s)
+            pa.pa_reshape_and_cache_int8(kd, vd, st.k_cache, st.v_cache, s)
         else:
             pa.pa_reshape_and_cache(kd, vd, st.k_cache, st.v_cache, s)
 
 
 def i8_cache(num_blocks, num_kv_heads, head_dim, device="cuda", fp8=False):
-    """(codes, scales) of an unwritten int8 / E4M3 pool: codes 0x7F (a NaN code
-    for E4M3), scales NaN."""
-    codes = torch.full((num_blocks * num_kv_heads * BS * head_dim,), 127,
-                       dtype=torch.uint8 if fp8 else torch.int8, device=device)
-    scales = torch.full((num_blocks * num_kv_heads * BS,), float("nan"), dtype=torch.float32, device=device)
-    return codes, scales
+    """An unwritten int8 / E4M3 cache (K or V) in the library's tile layout:
+    every tile's codes 0x7F (a NaN code for E4M3), then its 16 scales NaN."""
+    tiles = np.full((num_blocks * num_kv_heads, BS * (head_dim + 4)), 0x7F, dtype=np.uint8)
+    tiles[:, BS * head_dim:].view(np.float32)[:] = np.nan
+    flat = tiles.reshape(-1)
+    return torch.from_numpy(flat if fp8 else flat.view(np.int8)).to(device)
 
 
 def build(wl, steps: int = 0, device="cuda") -> GpuState:
@@ -88,13 +86,12 @@ def build(wl, steps: int = 0, device="cuda") -> GpuState:
     pool = pa.BlockPool(wl.num_blocks, BS, wl.free_order)
     if spec.cache in ("i8", "fp8"):
         f8 = spec.cache == "fp8"
-        kc, ks = i8_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, device, fp8=f8)
-        vc, vs = i8_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, device, fp8=f8)
+        kc = i8_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, device, fp8=f8)
+        vc = i8_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, device, fp8=f8)
     else:
         kc = nan_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, spec.dtype, device)
         vc = nan_cache(wl.num_blocks, spec.num_kv_heads, spec.head_dim, spec.dtype, device)
-        ks = vs = None
-    st = GpuState(pool, [], -1, kc, vc, [], [], [], [], ks, vs)
+    st = GpuState(pool, [], -1, kc, vc, [], [], [], [])
     if spec.prefix_len:
         st.owner = pool.seq_create()
         slots, cow = pool.seq_append(st.owner, spec.prefix_len)
@@ -142,6 +139,5 @@ def decode(wl, st: GpuState, max_blocks: int, out_dtype=None, kernel="auto", par
     pt = spec.partition_tokens if partition_tokens is None else partition_tokens
     max_ctx = int(lens_h.max()) if len(lens_h) else 0
     pa.pa_decode(out, qd, st.k_cache, st.v_cache, tab_d, lens_d, spec.num_kv_heads, max_ctx,
-                 spec.fp32_scale(), partition_tokens=pt, kernel=kernel, k_scales=st.k_scales,
-                 v_scales=st.v_scales, sliding_window=window)
+                 spec.fp32_scale(), partition_tokens=pt, kernel=kernel, sliding_window=window)
     return out

@@ -203,8 +203,7 @@ def test_append_and_copy_reject_bad_sizes():
 
 
 def _i8(**over):
-    base = dict(kv_dtype=pa.PA_I8, q_dtype=pa.PA_BF16, out_dtype=pa.PA_F32,
-                k_scales=ctypes.c_void_p(112), v_scales=ctypes.c_void_p(128))
+    base = dict(kv_dtype=pa.PA_I8, q_dtype=pa.PA_BF16, out_dtype=pa.PA_F32)
     base.update(over)
     return _params(**base)
 
@@ -217,8 +216,6 @@ def test_int8_cache_takes_the_balanced_split():
 @pytest.mark.parametrize("over,status", [
     (dict(q_dtype=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),
     (dict(out_dtype=pa.PA_F16), pa.PA_ERR_UNSUPPORTED),
-    (dict(k_scales=None), pa.PA_ERR_INVALID_ARG),
-    (dict(v_scales=ctypes.c_void_p(129)), pa.PA_ERR_INVALID_ARG),
     (dict(partition_tokens=256), pa.PA_ERR_UNSUPPORTED),
     (dict(kernel=pa.PA_KERNEL_VALU), pa.PA_ERR_UNSUPPORTED),
     (dict(num_seqs=1025), pa.PA_ERR_UNSUPPORTED),
@@ -242,27 +239,25 @@ def test_byte_caches_take_the_fused_append_on_the_balanced_split():
 
 def test_int8_append_and_copy_reject_bad_arguments():
     L = pa.lib()
-    args = (None, None, None, None, None, None, None)
+    args = (None, None, None, None, None)       # rows, caches (codes and scales in their tiles), slots
     assert L.pa_reshape_and_cache_int8(*args, 4, 8, 128, 10, pa.PA_F32, None) == pa.PA_ERR_UNSUPPORTED
     assert L.pa_reshape_and_cache_int8(*args, 4, 8, 96, 10, pa.PA_BF16, None) == pa.PA_ERR_UNSUPPORTED
     assert L.pa_reshape_and_cache_int8(*args, 4, 8, 128, 10, pa.PA_BF16, None) == pa.PA_ERR_INVALID_ARG
     assert L.pa_reshape_and_cache_int8(*args, 0, 8, 128, 10, pa.PA_BF16, None) == pa.PA_OK
-    assert L.pa_copy_blocks_int8(None, None, None, None, None, 0, 8, 128, 10, None) == pa.PA_OK
-    assert L.pa_copy_blocks_int8(None, None, None, None, None, 2, 8, 128, 10, None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_copy_blocks_int8(None, None, None, 0, 8, 128, 10, None) == pa.PA_OK
+    assert L.pa_copy_blocks_int8(None, None, None, 2, 8, 128, 10, None) == pa.PA_ERR_INVALID_ARG
 
 
 # ---------------------------------------------------------------- FP8 caches, window
 def test_fp8_cache_follows_the_byte_cache_rules():
-    f8 = dict(kv_dtype=pa.PA_FP8, q_dtype=pa.PA_BF16, out_dtype=pa.PA_F32,
-              k_scales=ctypes.c_void_p(112), v_scales=ctypes.c_void_p(128))
+    f8 = dict(kv_dtype=pa.PA_FP8, q_dtype=pa.PA_BF16, out_dtype=pa.PA_F32)
     assert pa.pa_decode_partition_tokens(_params(**f8)) == 0
     for over, status in ((dict(q_dtype=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),
-                         (dict(k_scales=None), pa.PA_ERR_INVALID_ARG),
                          (dict(partition_tokens=64), pa.PA_ERR_UNSUPPORTED)):
         p = _params(**{**f8, **over})
         assert pa.lib().pa_decode(ctypes.byref(p), None, 0, None) == status
     L = pa.lib()
-    args = (None, None, None, None, None, None, None)
+    args = (None, None, None, None, None)
     assert L.pa_reshape_and_cache_fp8(*args, 4, 8, 128, 10, pa.PA_F32, None) == pa.PA_ERR_UNSUPPORTED
     assert L.pa_reshape_and_cache_fp8(*args, 4, 8, 128, 10, pa.PA_BF16, None) == pa.PA_ERR_INVALID_ARG
     assert L.pa_reshape_and_cache_fp8(*args, 0, 8, 128, 10, pa.PA_BF16, None) == pa.PA_OK
@@ -346,6 +341,5 @@ def test_swap_blocks_reject_bad_arguments_before_touching_memory():
     pairs = (ctypes.c_int32 * 2)(0, 0)
     a = ctypes.c_void_p(addr)
     assert L.pa_swap_blocks(a, a, 1, a, a, 1, pairs, 1, 1, 64, pa.PA_BF16, None) == pa.PA_ERR_INVALID_ARG
-    assert L.pa_swap_blocks_int8(*nul, *nul, 10, *nul, *nul, 10, None, 0, 8, 128, None) == pa.PA_OK
-    assert L.pa_swap_blocks_int8(*nul, *nul, 10, *nul, *nul, 10, None, 1, 8, 128, None) \
-        == pa.PA_ERR_INVALID_ARG
+    assert L.pa_swap_blocks_int8(*nul, 10, *nul, 10, None, 0, 8, 128, None) == pa.PA_OK
+    assert L.pa_swap_blocks_int8(*nul, 10, *nul, 10, None, 1, 8, 128, None) == pa.PA_ERR_INVALID_ARG

@@ -84,8 +84,8 @@ def test_random_configuration_matches_oracle(case):
     q = gpu_side.to_device(wl.q, spec.dtype)
     out = torch.full(q.shape, -9.0, dtype=torch.float32, device="cuda")
     pa.pa_decode(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, spec.num_kv_heads, int(lh.max()),
-                 spec.fp32_scale(), partition_tokens=c["pt"], k_scales=gst.k_scales, v_scales=gst.v_scales,
-                 sliding_window=c["window"], shared_prefix_blocks=c["prefix"] // 16)
+                 spec.fp32_scale(), partition_tokens=c["pt"], sliding_window=c["window"],
+                 shared_prefix_blocks=c["prefix"] // 16)
     got = out.cpu().numpy().astype(np.float64)
     err = float(np.max(np.abs(got - ref))) if got.size else 0.0
     _say(f"  max_abs_err={err:.3e}")
@@ -131,8 +131,7 @@ def test_random_fused_append_steps_match_oracle(case):
         if len(cows):
             pairs = torch.from_numpy(cows.copy()).cuda()
             if byte:
-                pa.pa_copy_blocks_int8(gst.k_cache, gst.v_cache, gst.k_scales, gst.v_scales, pairs,
-                                       spec.num_kv_heads, spec.head_dim)
+                pa.pa_copy_blocks_int8(gst.k_cache, gst.v_cache, pairs, spec.num_kv_heads, spec.head_dim)
             else:
                 pa.pa_copy_blocks(gst.k_cache, gst.v_cache, pairs, spec.num_kv_heads, spec.head_dim)
         oracle_side.advance(wl, ost, step)
@@ -140,8 +139,8 @@ def test_random_fused_append_steps_match_oracle(case):
         tab_d, lens_d, _, lh = gpu_side.tables(gst, mb)
         out = torch.full(q.shape, -9.0, dtype=torch.float32, device="cuda")
         pa.pa_decode(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, spec.num_kv_heads, int(lh.max()),
-                     spec.fp32_scale(), partition_tokens=c["pt"], k_scales=gst.k_scales, v_scales=gst.v_scales,
-                     sliding_window=c["window"], shared_prefix_blocks=c["prefix"] // 16,
+                     spec.fp32_scale(), partition_tokens=c["pt"], sliding_window=c["window"],
+                     shared_prefix_blocks=c["prefix"] // 16,
                      k_new=gpu_side.to_device(wl.step_k[step], spec.dtype),
                      v_new=gpu_side.to_device(wl.step_v[step], spec.dtype),
                      slot_mapping=torch.from_numpy(slots.copy()).cuda())
@@ -155,7 +154,5 @@ def test_random_fused_append_steps_match_oracle(case):
     if byte:
         for g, o in ((gst.k_cache, ost.k_cache), (gst.v_cache, ost.v_cache)):
             assert np.array_equal(g.cpu().numpy().view(np.uint8), o.view(np.uint8))
-        for g, o in ((gst.k_scales, ost.k_scales), (gst.v_scales, ost.v_scales)):
-            assert np.array_equal(g.cpu().numpy().view(np.uint32), o.view(np.uint32))
     else:
         _assert_caches_equal(gst, ost, spec.dtype)

@@ -53,8 +53,7 @@ def _run_both(wl, gst, mb, seqs, pt, prefix_blocks=0):
     for fn in (pa.pa_decode, pa.pa_decode_noalloc):
         out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=dev)
         fn(out, q, gst.k_cache, gst.v_cache, tab_d, lens_d, spec.num_kv_heads, max_ctx,
-           spec.fp32_scale(), partition_tokens=pt, k_scales=gst.k_scales, v_scales=gst.v_scales,
-           shared_prefix_blocks=prefix_blocks)
+           spec.fp32_scale(), partition_tokens=pt, shared_prefix_blocks=prefix_blocks)
         outs.append(out)
     torch.cuda.synchronize()
     ref, mine = (o.cpu().numpy() for o in outs)
