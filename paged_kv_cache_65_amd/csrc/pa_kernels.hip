@@ -743,7 +743,9 @@ struct MfmaWaveI8 : MfmaWave<PA_F16, D, NCT_> {
       return i == 0 ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false))
                     : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
     } else {
-      const uint32_t biased = __builtin_amdgcn_perm(0u, w, i == 0 ? 0x0c010c00u : 0x0c030c02u) ^ 0x64806480u;
+      // (one XOR flips the top bits of all four bytes; the permute then puts
+      // two of them under 0x64 high bytes)
+      const uint32_t biased = __builtin_amdgcn_perm(0x64646464u, w ^ 0x80808080u, i == 0 ? 0x04010400u : 0x04030402u);
       const h2 x = __builtin_bit_cast(h2, biased) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
       return __builtin_bit_cast(uint32_t, x);
     }
