@@ -13,9 +13,8 @@ Contents
     block pool (allocation, fork, append with copy-on-write, free).
   * INT8 / FP8 caches: one byte array per K and V whose tiles hold the codes
     (``np.int8`` / ``np.uint8``) of 16 tokens of one (block, KV head) followed
-    by their 16 float32 row scales, padded to a multiple of 128 bytes;
-    quantized on append, attended over the dequantized rows (``*_i8`` /
-    ``*_fp8`` functions).
+    by their 16 float32 row scales; quantized on append, attended over the
+    dequantized rows (``*_i8`` / ``*_fp8`` functions).
 
 Data convention for the wrappers: cache-typed arrays are numpy arrays of
 ``np.float32`` (fp32), ``np.float16`` (fp16) or ``np.uint16`` holding raw
@@ -78,8 +77,6 @@ def _load():
         lib.oracle_quantize_row_i8.argtypes = [_P, _I64, _I, _I, _P]
         lib.oracle_scale_offset_i8.restype = _I64
         lib.oracle_scale_offset_i8.argtypes = [_I64, _I, _I, _I, _I]
-        lib.oracle_tile_bytes_i8.restype = _I64
-        lib.oracle_tile_bytes_i8.argtypes = [_I]
         lib.oracle_reshape_and_cache_i8.restype = _I
         lib.oracle_reshape_and_cache_i8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I64, _I]
         lib.oracle_copy_blocks_i8.restype = None
@@ -241,15 +238,9 @@ def read_scale(cache, block, head, tok, num_kv_heads, head_dim) -> np.float32:
     return cache[o:o + 4].view(np.float32)[0]
 
 
-def tile_bytes_i8(head_dim) -> int:
-    """Bytes of one (block, KV head) tile of a byte cache: 16 rows of head_dim
-    codes and 4 scale bytes each, padded to a multiple of 128 bytes."""
-    return int(_load().oracle_tile_bytes_i8(head_dim))
-
-
 def cache_bytes_i8(num_blocks, num_kv_heads, head_dim) -> int:
-    """Bytes of one K or V byte cache."""
-    return num_blocks * num_kv_heads * tile_bytes_i8(head_dim)
+    """Bytes of one K or V byte cache: 16 rows of head_dim codes + 4 scale bytes per tile."""
+    return num_blocks * num_kv_heads * 16 * (head_dim + 4)
 
 
 def quantize_row_i8(row: np.ndarray, dtype: str):
@@ -262,8 +253,8 @@ def quantize_row_i8(row: np.ndarray, dtype: str):
 
 def _empty_codes(num_blocks, num_kv_heads, head_dim, np_type):
     """An unwritten byte cache: codes 0x7F, every scale NaN."""
-    tiles = np.full((num_blocks * num_kv_heads, tile_bytes_i8(head_dim)), 0x7F, dtype=np.uint8)
-    tiles[:, 16 * head_dim:16 * (head_dim + 4)].view(np.float32)[:] = np.nan
+    tiles = np.full((num_blocks * num_kv_heads, 16 * (head_dim + 4)), 0x7F, dtype=np.uint8)
+    tiles[:, 16 * head_dim:].view(np.float32)[:] = np.nan
     return tiles.reshape(-1).view(np_type)
 
 

@@ -397,9 +397,8 @@ void oracle_bruteforce_contiguous(double *out, const void *q, const void *k_seq,
  *
  * Layout contract (byte offsets into the K or V cache array).  A tile holds
  * the 16 tokens x D codes of one (block b, KV head g) followed by their 16
- * float32 row scales, 16*(D+4) bytes, then padding up to the next multiple
- * of 128 bytes: T = 128*ceil(16*(D+4)/128) bytes (2176 at D = 128, 1152 at
- * D = 64), tile (b, g) starting at byte (b*Hkv + g)*T.  Inside the tile:
+ * float32 row scales: 16*(D+4) bytes, starting at byte (b*Hkv + g)*16*(D+4).
+ * Inside the tile:
  *   K code (t, d): c = d/64, w = d%64, h = w/32, q = (w%32)/8, e = w%8
  *      -> byte (c*64 + q*16 + t)*16 + h*8 + e
  *   V code (t, d): m = d/64, k = (d%64)/16, r = d%16
@@ -407,13 +406,8 @@ void oracle_bruteforce_contiguous(double *out, const void *q, const void *k_seq,
  *   scale of token t -> bytes 16*D + 4t .. 16*D + 4t + 3 (float32, host
  *      byte order)
  * ------------------------------------------------------------------------ */
-int64_t oracle_tile_bytes_i8(int head_dim) {
-  const int64_t used = (int64_t)ORC_BS * (head_dim + 4);
-  return (used + 127) / 128 * 128;
-}
-
 static int64_t tile_i8(int64_t block, int head, int num_kv_heads, int head_dim) {
-  return (block * num_kv_heads + head) * oracle_tile_bytes_i8(head_dim);
+  return (block * num_kv_heads + head) * (int64_t)ORC_BS * (head_dim + 4);
 }
 
 int64_t oracle_k_offset_i8(int64_t block, int head, int tok, int dim, int num_kv_heads,
@@ -574,11 +568,11 @@ int oracle_reshape_and_cache_i8(const void *k_new, const void *v_new, int8_t *k_
   return bad;
 }
 
-/* Whole-block copy of an int8 / E4M3 cache: the tiles (codes, scales and
- * padding) of every head. */
+/* Whole-block copy of an int8 / E4M3 cache: the tiles (codes and scales) of
+ * every head. */
 void oracle_copy_blocks_i8(int8_t *k_cache, int8_t *v_cache, const int32_t *pairs, int num_pairs,
                            int num_kv_heads, int head_dim) {
-  size_t block_bytes = (size_t)num_kv_heads * (size_t)oracle_tile_bytes_i8(head_dim);
+  size_t block_bytes = (size_t)num_kv_heads * ORC_BS * (head_dim + 4);
   for (int p = 0; p < num_pairs; ++p) {
     size_t src = (size_t)pairs[2 * p], dst = (size_t)pairs[2 * p + 1];
     memmove(k_cache + dst * block_bytes, k_cache + src * block_bytes, block_bytes);

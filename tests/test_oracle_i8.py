@@ -69,32 +69,24 @@ def test_i8_layout_hand_computed_offsets():
     assert oracle.k_offset_i8(0, 0, 15, 127, 1, 128) == 127 * 16 + 15
     # V (t=5, d=37), D=128: m=0, k=2, r=5, t/4=1, t%4=1 -> (0 + 16 + 5)*16 + 8 + 1
     assert oracle.v_offset_i8(0, 0, 5, 37, 1, 128) == 21 * 16 + 9
-    # a tile is 16 rows of D codes followed by their 16 float32 scales, 16*(D+4)
-    # bytes, padded to a multiple of 128: 16*68 = 1088 -> 1152 at D = 64,
-    # 16*132 = 2112 -> 2176 at D = 128
-    assert oracle.tile_bytes_i8(64) == 1152 and oracle.tile_bytes_i8(128) == 2176
-    # tile (b=2, g=1) of Hkv=3, D=64 starts at (2*3 + 1)*1152 = 8064
-    assert oracle.k_offset_i8(2, 1, 0, 0, 3, 64) == 8064
-    assert oracle.v_offset_i8(2, 1, 0, 0, 3, 64) == 8064
-    # tile (b=1, g=0) of Hkv=2, D=128 starts at 2*2176 = 4352; K (t=15, d=127) -> 4352 + 127*16 + 15
-    assert oracle.k_offset_i8(1, 0, 15, 127, 2, 128) == 4352 + 2047
+    # a tile is 16 rows of D codes followed by their 16 float32 scales: 16*(D+4)
+    # bytes; tile (b=2, g=1) of Hkv=3, D=64 starts at (2*3 + 1)*16*68 = 7616
+    assert oracle.k_offset_i8(2, 1, 0, 0, 3, 64) == 7616
+    assert oracle.v_offset_i8(2, 1, 0, 0, 3, 64) == 7616
     # scales after the codes: token 5 of tile 0, D=128 -> 16*128 + 4*5
     assert oracle.scale_offset_i8(0, 0, 5, 1, 128) == 2068
-    # token 15 of tile (2, 1), Hkv=3, D=64 -> 8064 + 16*64 + 60
-    assert oracle.scale_offset_i8(2, 1, 15, 3, 64) == 9148
-    assert oracle.cache_bytes_i8(5, 3, 64) == 5 * 3 * 1152
+    # token 15 of tile (2, 1), Hkv=3, D=64 -> 7616 + 16*64 + 60
+    assert oracle.scale_offset_i8(2, 1, 15, 3, 64) == 8700
+    assert oracle.cache_bytes_i8(5, 3, 64) == 5 * 3 * 1088
 
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_i8_layout_is_a_bijection_per_tile(D):
-    # codes of either tile kind and the 16 four-byte scales fill the tile's
-    # first 16*(D+4) bytes exactly once; the rest of it is padding, and the
-    # next tile starts on a 128-byte boundary
+    # codes of either tile kind and the 16 four-byte scales fill the tile exactly once
     scales = [oracle.scale_offset_i8(0, 0, t, 1, D) + i for t in range(16) for i in range(4)]
     for off in (oracle.k_offset_i8, oracle.v_offset_i8):
         seen = sorted([off(0, 0, t, d, 1, D) for t in range(16) for d in range(D)] + scales)
         assert seen == list(range(16 * (D + 4)))
-        assert off(0, 1, 0, 0, 2, D) == oracle.tile_bytes_i8(D) and oracle.tile_bytes_i8(D) % 128 == 0
 
 
 # ---------------------------------------------------------------- append + decode
@@ -153,14 +145,13 @@ def test_decode_i8_matches_numpy_over_rows_quantized_one_by_one(q_dtype, Hq, Hkv
 
 
 def _codes(cache, nb, Hkv, D):
-    """The code bytes of every tile (rows of 16*D), scales and padding left out."""
-    return cache.reshape(nb * Hkv, oracle.tile_bytes_i8(D))[:, :16 * D]
+    """The code bytes of every tile (rows of 16*D), scales left out."""
+    return cache.reshape(nb * Hkv, 16 * (D + 4))[:, :16 * D]
 
 
 def _scales(cache, nb, Hkv, D):
     """The float32 row scales of every tile ([nb*Hkv][16])."""
-    return np.ascontiguousarray(cache.reshape(nb * Hkv, oracle.tile_bytes_i8(D))[:, 16 * D:16 * (D + 4)]).view(
-        np.float32)
+    return np.ascontiguousarray(cache.reshape(nb * Hkv, 16 * (D + 4))[:, 16 * D:]).view(np.float32)
 
 
 def test_reshape_and_cache_i8_writes_only_mapped_rows_and_skips_bad_slots():
@@ -189,6 +180,6 @@ def test_copy_blocks_i8_moves_codes_and_scales():
     vc = rng.integers(-127, 128, n).astype(np.int8)
     k0, v0 = kc.copy(), vc.copy()
     oracle.copy_blocks_i8(kc, vc, [[1, 3], [4, 0]], Hkv, D)
-    B = Hkv * oracle.tile_bytes_i8(D)           # a block: every head's tile (codes, scales, padding)
+    B = Hkv * 16 * (D + 4)                      # a block: every head's codes and scales
     assert np.array_equal(kc[3 * B:4 * B], k0[1 * B:2 * B]) and np.array_equal(vc[0:B], v0[4 * B:5 * B])
     assert np.array_equal(kc[2 * B:3 * B], k0[2 * B:3 * B])
