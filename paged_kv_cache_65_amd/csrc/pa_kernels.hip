@@ -1865,6 +1865,8 @@ struct ExtendArgs {
 // Score tiles per extend wave: 1, 2 or 4 (four tiles hold 64 (token, head)
 // columns: k = 8 drafted tokens at G = 8 read the context once).
 constexpr int kExtNctMax = 4;
+// Batches of up to this many sequences are dispatched longest context first.
+constexpr int kExtRankMax = 256;
 
 template <int D, int NCT>
 struct __align__(16) SmemExtend {
@@ -1909,9 +1911,33 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
   int rest = blockIdx.x / a.qgroups;
   const int g = rest % Hkv;
   rest /= Hkv;
-  const int s = rest % a.num_seqs;
+  int s = rest % a.num_seqs;
   const int p = rest / a.num_seqs;
   const int tid = threadIdx.x, lane = tid % 64, r = lane % 16, tq = lane / 16;
+  if (a.num_seqs > 1 && a.num_seqs <= kExtRankMax) {
+    // Longest contexts first: workgroups start in index order, so the long
+    // (sequence, KV head) pairs take the first round of CUs and the short
+    // ones fill the CUs that free up (in sequence order a CU that drew two
+    // long pairs ended last).  Slot s of the grid takes the sequence of rank
+    // s (longer first, then lower index); which workgroup computes a row
+    // does not change its result.
+    __shared__ int32_t rank_len[kExtRankMax];
+    __shared__ int32_t rank_pick;
+    const int S = a.num_seqs;
+    for (int i = tid; i < S; i += kThreads) rank_len[i] = a.context_lens[i];
+    __syncthreads();
+    for (int i = tid; i < S; i += kThreads) {
+      const int Li = rank_len[i];
+      int rk = 0;
+      for (int j = 0; j < S; ++j) {
+        const int Lj = rank_len[j];
+        rk += (Lj > Li || (Lj == Li && j < i)) ? 1 : 0;
+      }
+      if (rk == s) rank_pick = i;
+    }
+    __syncthreads();
+    s = rank_pick;
+  }
   const int wu = __builtin_amdgcn_readfirstlane(tid / 64);
   const int L = a.context_lens[s];
   const int q0 = a.query_start[s];
