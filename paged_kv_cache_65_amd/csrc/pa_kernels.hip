@@ -1868,12 +1868,21 @@ constexpr int kExtNctMax = 4;
 // Batches of up to this many sequences are dispatched longest context first.
 constexpr int kExtRankMax = 256;
 
+// With four tiles (64 columns) a wave's q fragments live in LDS, not in
+// registers, and the four waves' states meet one 16-column tile at a time:
+// two workgroups then fit a CU (registers and LDS), where one did, and a
+// wave's chain of matrix ops and softmax overlaps another wave's.
 template <int D, int NCT>
 struct __align__(16) SmemExtend {
-  float acc[kWaves][NCT * 16][D];
-  float m[kWaves][NCT * 16];
-  float l[kWaves][NCT * 16];
+  static constexpr bool kTiled = NCT >= 4;
+  static constexpr int kCols = kTiled ? kTileCols : NCT * kTileCols;  // columns folded at a time
+  float acc[kWaves][kCols][D];
+  float m[kWaves][kCols];
+  float l[kWaves][kCols];
+  u32x4_t q[kTiled ? NCT : 1][kTiled ? D / 32 : 1][64];  // q fragment [tile][c] of each lane
 };
+template <int NCT>
+constexpr int extend_wg_per_cu() { return NCT >= 4 ? 2 : 1; }
 
 // Sequence whose query rows hold row t (query_start ascending).
 __device__ inline int seq_of_row(const int32_t *qs, int S, int t) {
@@ -1896,7 +1905,7 @@ __device__ inline bool extend_seq_valid(int L, int n, const ExtendArgs &a) {
 }
 
 template <int DT, int D, int NCT>
-__global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
+__global__ __launch_bounds__(kThreads, (extend_wg_per_cu<NCT>())) void pa_extend_kernel(ExtendArgs a) {
   using M = MfmaWave<DT, D>;
   using v8 = typename M::v8;
   constexpr int NC = D / 32, NT = D / 16;
@@ -1983,17 +1992,23 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
     lim[ct] = ok ? pf + tk : -1;
     const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
                                                             ((int64_t)(q0 + i0 + tk) * Hq + hd) * D * 2);
+    if (!SmemExtend<D, NCT>::kTiled || wu == 0) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      u32x4_t x = qrow[4 * c + tq];
-      if (!ok) x = u32x4_t{0, 0, 0, 0};
-      qB[ct][c] = __builtin_bit_cast(v8, x);
+      for (int c = 0; c < NC; ++c) {
+        u32x4_t x = qrow[4 * c + tq];
+        if (!ok) x = u32x4_t{0, 0, 0, 0};
+        if constexpr (SmemExtend<D, NCT>::kTiled)
+          sm.q[ct][c][lane] = x;  // the four waves' columns are the same: one copy
+        else
+          qB[ct][c] = __builtin_bit_cast(v8, x);
+      }
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[ct][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     mm[ct] = -INFINITY;
     ll[ct] = 0.f;
   }
+  if constexpr (SmemExtend<D, NCT>::kTiled) __syncthreads();
   // the first position any column of tile ct may not see (wave-uniform)
   int tile_min[NCT];
 #pragma unroll
@@ -2037,11 +2052,22 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) f.v[c] &= u32x4_t{lo, hi, lo, hi};
           }
+          // q fragments from LDS (four tiles) are read again for every block:
+          // an opaque zero in the index keeps the compiler from hoisting the
+          // reads out of the loop into registers
+          int qz = 0;
+          if constexpr (SmemExtend<D, NCT>::kTiled) asm volatile("v_mov_b32 %0, 0" : "=v"(qz));
+          auto q_frag = [&](int ct, int c) -> v8 {
+            if constexpr (SmemExtend<D, NCT>::kTiled)
+              return __builtin_bit_cast(v8, sm.q[ct][c][lane + qz]);
+            else
+              return qB[ct][c];
+          };
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) {
             f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < NC; ++c) sc = M::mma_qk(__builtin_bit_cast(v8, f.k[c]), qB[ct][c], sc);
+            for (int c = 0; c < NC; ++c) sc = M::mma_qk(__builtin_bit_cast(v8, f.k[c]), q_frag(ct, c), sc);
             float sv[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) sv[v] = sc[v] * a.scale_log2;
@@ -2080,18 +2106,6 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
       }
     }
   }
-  // wave states -> LDS
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const float lt = sum_xor32(sum_xor16(ll[ct]));
-    const int col = ct * 16 + r;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t *>(&sm.acc[wu][col][16 * t + 4 * tq]) = acc[ct][t];
-    if (tq == 0) {
-      sm.m[wu][col] = mm[ct];
-      sm.l[wu][col] = lt;
-    }
-  }
   if (__syncthreads_or(bad)) {
     for (int i = tid; i < NCT * kTileCols * D; i += kThreads) {
       const int col = i / D, d = i % D, ct = col / kTileCols, rr = col % kTileCols;
@@ -2110,32 +2124,53 @@ __global__ __launch_bounds__(kThreads) void pa_extend_kernel(ExtendArgs a) {
     }
     return;
   }
-  // fold the four waves; a wave (or the whole group) that saw no position of
-  // a column leaves m = -inf, l = 0 for it
-  for (int i = tid; i < NCT * kTileCols * D; i += kThreads) {
-    const int col = i / D, d = i % D, ct = col / kTileCols, rr = col % kTileCols;
-    if (!col_ok(ct, rr)) continue;
-    float Mx = -INFINITY;
+  // wave states -> LDS, then fold the four waves (all columns at once, or
+  // one 16-column tile at a time with four tiles); a wave (or the whole
+  // group) that saw no position of a column leaves m = -inf, l = 0 for it
+  constexpr int FG = SmemExtend<D, NCT>::kTiled ? NCT : 1;  // fold rounds
+  constexpr int FC = SmemExtend<D, NCT>::kCols;             // columns per round
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, sm.m[w][col]);
-    float num = 0.f, den = 0.f;
-    if (Mx != -INFINITY) {
+  for (int fg = 0; fg < FG; ++fg) {
+    if (fg > 0) __syncthreads();  // the previous round has read the buffer
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = exp2f(sm.m[w][col] - Mx);  // 0 for m = -inf
-        num += f * sm.acc[w][col][d];
-        den += f * sm.l[w][col];
+    for (int ct = 0; ct < NCT; ++ct) {
+      if (FG > 1 && ct != fg) continue;
+      const float lt = sum_xor32(sum_xor16(ll[ct]));
+      const int col = (FG > 1 ? 0 : ct * kTileCols) + r;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t *>(&sm.acc[wu][col][16 * t + 4 * tq]) = acc[ct][t];
+      if (tq == 0) {
+        sm.m[wu][col] = mm[ct];
+        sm.l[wu][col] = lt;
       }
     }
-    const int64_t row = (int64_t)(q0 + i0 + col_token(ct, rr)) * Hq + g * G + col_head(ct, rr);
-    if (nparts == 1) {
-      store_out(a.out, row * D + d, num / den, a.out_dtype);
-    } else {
-      const int64_t prow = row * a.max_parts + p;
-      a.ws_acc[prow * D + d] = num;
-      if (d == 0) {
-        a.ws_ml[prow * 2] = Mx;
-        a.ws_ml[prow * 2 + 1] = den;
+    __syncthreads();
+    for (int i = tid; i < FC * D; i += kThreads) {
+      const int cl = i / D, d = i % D, colg = fg * FC + cl;
+      const int ct = colg / kTileCols, rr = colg % kTileCols;
+      if (!col_ok(ct, rr)) continue;
+      float Mx = -INFINITY;
+  #pragma unroll
+      for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, sm.m[w][cl]);
+      float num = 0.f, den = 0.f;
+      if (Mx != -INFINITY) {
+  #pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float f = exp2f(sm.m[w][cl] - Mx);  // 0 for m = -inf
+          num += f * sm.acc[w][cl][d];
+          den += f * sm.l[w][cl];
+        }
+      }
+      const int64_t row = (int64_t)(q0 + i0 + col_token(ct, rr)) * Hq + g * G + col_head(ct, rr);
+      if (nparts == 1) {
+        store_out(a.out, row * D + d, num / den, a.out_dtype);
+      } else {
+        const int64_t prow = row * a.max_parts + p;
+        a.ws_acc[prow * D + d] = num;
+        if (d == 0) {
+          a.ws_ml[prow * 2] = Mx;
+          a.ws_ml[prow * 2 + 1] = den;
+        }
       }
     }
   }
