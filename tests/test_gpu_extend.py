@@ -114,13 +114,15 @@ def test_sequences_without_new_tokens_and_contract_violations():
         assert np.all(np.isnan(o[3:])) and np.max(np.abs(o[0:3] - ref[0:3])) <= 2e-3
 
 
-def test_speculative_verify_on_the_70b_shape_sampled():
+@pytest.mark.parametrize("k", [4, 8])
+def test_speculative_verify_on_the_70b_shape_sampled(k):
     # workload-3 shapes (64 sequences, 64 / 8 heads, D = 128, L ~ U[128, 4096]) with k = 4
+    # (two score tiles per wave) and k = 8 (four tiles: q in LDS, one tile folded at a time;
+    # the sequences taken longest context first)
     spec = workloads.named(3)
     wl = workloads.generate(spec)
     gst, ost = gpu_side.build(wl), oracle_side.build(wl)
     mb = oracle_side.max_blocks_for(wl)
-    k = 4
     news = (k,) * spec.num_seqs
     qs = np.arange(0, k * spec.num_seqs + 1, k, dtype=np.int32)
     q = workloads.round_to(np.random.default_rng(52).standard_normal((k * spec.num_seqs, 64, 128),
@@ -134,5 +136,20 @@ def test_speculative_verify_on_the_70b_shape_sampled():
                         np.ascontiguousarray(tab[sample]), np.ascontiguousarray(l[sample]), sub_qs, 8,
                         spec.fp32_scale(), "bf16")
     err = np.max(np.abs(out[rows] - ref))
-    _say(f"  70B verify k=4 sampled max_abs_err={err:.3e}")
+    _say(f"  70B verify k={k} sampled max_abs_err={err:.3e}")
+    assert err <= 2e-3
+
+
+def test_more_than_256_sequences_keep_their_grid_order():
+    # above 256 sequences the extend grid is not reordered by context length;
+    # every row still matches the oracle
+    rng = np.random.default_rng(57)
+    lens = tuple(int(x) for x in rng.integers(8, 120, 300))
+    news = tuple(int(x) for x in rng.integers(0, 4, 300))
+    spec, wl, gst, ost, mb, qs, q = _case(57, "bf16", lens, news, 8, 2, 64)
+    out = _run(spec, gst, mb, qs, q, news).cpu().numpy()
+    tab, l = oracle_side.tables(ost, mb)
+    ref = oracle.extend(q, ost.k_cache, ost.v_cache, tab, l, qs, 2, spec.fp32_scale(), "bf16")
+    err = np.max(np.abs(out - ref))
+    _say(f"  300 sequences, k in 0..3: max_abs_err={err:.3e}")
     assert err <= 2e-3
