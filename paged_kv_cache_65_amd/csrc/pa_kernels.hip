@@ -63,6 +63,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -109,6 +110,13 @@ __device__ inline void store_out4(void *out, int64_t idx, f32x4_t v, int out_dty
     for (int e = 0; e < 4; ++e) h[e] = out_dtype == PA_F16 ? f32_to_f16_bits(v[e]) : f32_to_bf16_bits(v[e]);
     *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(out) + idx) = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
   }
+}
+
+// Four consecutive floats of a partial row: the partial accumulators follow
+// the (m, l) pairs in the workspace, so they are 8-byte aligned.
+__device__ inline void store_partial4(float *dst, f32x4_t v) {
+  reinterpret_cast<f32x2_t *>(dst)[0] = f32x2_t{v[0], v[1]};
+  reinterpret_cast<f32x2_t *>(dst)[1] = f32x2_t{v[2], v[3]};
 }
 
 __device__ inline float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
@@ -193,12 +201,20 @@ constexpr uint32_t kAllTokens = 0xFFFFu;
 // Tokens lo .. hi-1 of a block (0 <= lo < hi <= 16) as a bit mask.
 __device__ inline uint32_t token_mask(int lo, int hi) { return ((1u << hi) - 1u) & ~((1u << lo) - 1u); }
 
+// Floats of padding after each row of a fold buffer: a wave writes its
+// accumulators as 16-byte pieces of 16 rows at once, and rows a multiple of
+// 128 bytes apart would put all 16 in the same LDS banks.
+constexpr int kAccPad = 4;
+
 // Per-wave online-softmax states meet here at the end of a partition, one
 // column tile (16 heads) at a time.
 struct __align__(16) SmemBase {
-  float acc[kWaves][kTileCols][kDMax];
+  float acc[kWaves][kTileCols][kDMax + kAccPad];
   float m[kWaves][kTileCols];
   float l[kWaves][kTileCols];
+  float fac[kWaves][kTileCols];  // each wave's weight in the fold of a head
+  float mx[kTileCols];
+  float den[kTileCols];
   uint32_t knew[kDMax];  // fused append: the new token's K and V rows (raw bits, up to 512 B)
   uint32_t vnew[kDMax];
 };
@@ -1283,27 +1299,42 @@ __global__ __launch_bounds__(kThreads, (partition_wg_per_cu<W, kMfma>())) void p
       __syncthreads();
     }
     const int hb = ct * kTileCols, nh = min(kTileCols, Gc - hb);  // heads of this tile
-    for (int i = tid; i < nh * D; i += kThreads) {
-      const int h = i / D, d = i % D;
+    // One weight per (wave, head) and the head's denominator first, then
+    // four dims of a row per thread.
+    if (tid < nh) {
       float M = -INFINITY;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][h]);
-      float num = 0.f, den = 0.f;
+      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][tid]);
+      float den = 0.f;
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
-        const float f = exp2f(sm.m[ww][h] - M);  // 0 for a wave that saw no block
-        num += f * sm.acc[ww][h][d];
-        den += f * sm.l[ww][h];
+        const float f = exp2f(sm.m[ww][tid] - M);  // 0 for a wave that saw no block
+        sm.fac[ww][tid] = f;
+        den += f * sm.l[ww][tid];
       }
+      sm.mx[tid] = M;
+      sm.den[tid] = den;
+    }
+    __syncthreads();
+    constexpr int NQ = D / 4;
+    for (int i = tid; i < nh * NQ; i += kThreads) {
+      const int h = i / NQ, d4 = (i % NQ) * 4;
+      f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) num += sm.fac[ww][h] * *reinterpret_cast<const f32x4_t *>(&sm.acc[ww][h][d4]);
       const int64_t row = (int64_t)s * a.num_q_heads + h0 + hb + h;
       if (nparts == 1) {
-        store_out(a.out, row * D + d, num / den, a.out_dtype);
+        const float den = sm.den[h];
+        f32x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = num[e] / den;
+        store_out4(a.out, row * D + d4, v, a.out_dtype);
       } else {
         const int64_t prow = row * a.max_parts + p;
-        a.ws_acc[prow * D + d] = num;
-        if (d == 0) {
-          a.ws_ml[prow * 2] = M;
-          a.ws_ml[prow * 2 + 1] = den;
+        store_partial4(a.ws_acc + prow * D + d4, num);
+        if (d4 == 0) {
+          a.ws_ml[prow * 2] = sm.mx[h];
+          a.ws_ml[prow * 2 + 1] = sm.den[h];
         }
       }
     }
@@ -1872,15 +1903,26 @@ constexpr int kExtRankMax = 256;
 // registers, and the four waves' states meet one 16-column tile at a time:
 // two workgroups then fit a CU (registers and LDS), where one did, and a
 // wave's chain of matrix ops and softmax overlaps another wave's.
+// Waves per extend workgroup: eight with four tiles (one workgroup per CU,
+// two waves per SIMD), so a long context is streamed by eight waves; four
+// otherwise.
+template <int NCT>
+constexpr int extend_waves() { return NCT >= 4 ? 8 : 4; }
+
 template <int D, int NCT>
 struct __align__(16) SmemExtend {
+  static constexpr int EW = extend_waves<NCT>();
   static constexpr bool kTiled = NCT >= 4;
   static constexpr int kCols = kTiled ? kTileCols : NCT * kTileCols;  // columns folded at a time
-  float acc[kWaves][kCols][D];
-  float m[kWaves][kCols];
-  float l[kWaves][kCols];
+  float acc[EW][kCols][D + kAccPad];
+  float m[EW][kCols];
+  float l[EW][kCols];
+  float fac[EW][kCols];  // each wave's weight in the fold of a column
+  float mx[kCols];
+  float den[kCols];
   u32x4_t q[kTiled ? NCT : 1][kTiled ? D / 32 : 1][64];  // q fragment [tile][c] of each lane
 };
+// Minimum waves per SIMD the register budget is set for.
 template <int NCT>
 constexpr int extend_wg_per_cu() { return NCT >= 4 ? 2 : 1; }
 
@@ -1905,7 +1947,8 @@ __device__ inline bool extend_seq_valid(int L, int n, const ExtendArgs &a) {
 }
 
 template <int DT, int D, int NCT>
-__global__ __launch_bounds__(kThreads, (extend_wg_per_cu<NCT>())) void pa_extend_kernel(ExtendArgs a) {
+__global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())) void pa_extend_kernel(ExtendArgs a) {
+  constexpr int EW = extend_waves<NCT>(), ET = EW * 64;
   using M = MfmaWave<DT, D>;
   using v8 = typename M::v8;
   constexpr int NC = D / 32, NT = D / 16;
@@ -1933,9 +1976,9 @@ __global__ __launch_bounds__(kThreads, (extend_wg_per_cu<NCT>())) void pa_extend
     __shared__ int32_t rank_len[kExtRankMax];
     __shared__ int32_t rank_pick;
     const int S = a.num_seqs;
-    for (int i = tid; i < S; i += kThreads) rank_len[i] = a.context_lens[i];
+    for (int i = tid; i < S; i += ET) rank_len[i] = a.context_lens[i];
     __syncthreads();
-    for (int i = tid; i < S; i += kThreads) {
+    for (int i = tid; i < S; i += ET) {
       const int Li = rank_len[i];
       int rk = 0;
       for (int j = 0; j < S; ++j) {
@@ -1962,7 +2005,7 @@ __global__ __launch_bounds__(kThreads, (extend_wg_per_cu<NCT>())) void pa_extend
   auto col_ok = [&](int ct, int rr) { return col_token(ct, rr) < ni && col_head(ct, rr) < G; };
   if (!extend_seq_valid(L, n, a)) {
     if (p == 0)
-      for (int i = tid; i < NCT * kTileCols * D; i += kThreads) {
+      for (int i = tid; i < NCT * kTileCols * D; i += ET) {
         const int col = i / D, d = i % D, ct = col / kTileCols, rr = col % kTileCols;
         if (col_ok(ct, rr))
           store_out(a.out, ((int64_t)(q0 + i0 + col_token(ct, rr)) * Hq + g * G + col_head(ct, rr)) * D + d, NAN,
@@ -2018,10 +2061,10 @@ __global__ __launch_bounds__(kThreads, (extend_wg_per_cu<NCT>())) void pa_extend
   const int64_t blk_stride = (int64_t)Hkv * M::TILE;
   typename M::Frag fr[NB];
   int bad = 0;
-  const int nmine = nblk > wu ? (nblk - wu + kWaves - 1) / kWaves : 0;
+  const int nmine = nblk > wu ? (nblk - wu + EW - 1) / EW : 0;
   for (int c0 = 0; c0 < nmine; c0 += 64) {
     const int nc = min(64, nmine - c0);
-    int ids = lane < nc ? trow[wu + (c0 + lane) * kWaves] : 0;
+    int ids = lane < nc ? trow[wu + (c0 + lane) * EW] : 0;
     const bool id_ok = (uint32_t)ids < (uint32_t)a.num_blocks;
     if (__builtin_amdgcn_ballot_w64(!id_ok)) bad = 1;
     ids = id_ok ? ids : 0;
@@ -2042,7 +2085,7 @@ __global__ __launch_bounds__(kThreads, (extend_wg_per_cu<NCT>())) void pa_extend
         refill(fr[(b + NB - 1) % NB], i + NB - 1);
         if (i < nc) {
           typename M::Frag &f = fr[b];
-          const int b0 = (blk0 + wu + (c0 + i) * kWaves) * kBS;  // position of the block's token 0
+          const int b0 = (blk0 + wu + (c0 + i) * EW) * kBS;  // position of the block's token 0
           if (b0 + kBS > L) {
             // slots at and past L may hold anything: zero their V elements
             const int lo_ok = L - b0;  // tokens 0 .. lo_ok-1 exist
@@ -2107,7 +2150,7 @@ __global__ __launch_bounds__(kThreads, (extend_wg_per_cu<NCT>())) void pa_extend
     }
   }
   if (__syncthreads_or(bad)) {
-    for (int i = tid; i < NCT * kTileCols * D; i += kThreads) {
+    for (int i = tid; i < NCT * kTileCols * D; i += ET) {
       const int col = i / D, d = i % D, ct = col / kTileCols, rr = col % kTileCols;
       if (!col_ok(ct, rr)) continue;
       const int64_t row = (int64_t)(q0 + i0 + col_token(ct, rr)) * Hq + g * G + col_head(ct, rr);
@@ -2145,31 +2188,44 @@ __global__ __launch_bounds__(kThreads, (extend_wg_per_cu<NCT>())) void pa_extend
       }
     }
     __syncthreads();
-    for (int i = tid; i < FC * D; i += kThreads) {
-      const int cl = i / D, d = i % D, colg = fg * FC + cl;
+    // one weight per (wave, column) and the column's denominator first,
+    // then four dims of a row per thread
+    if (tid < FC) {
+      float Mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < EW; ++w) Mx = fmaxf(Mx, sm.m[w][tid]);
+      float den = 0.f;
+#pragma unroll
+      for (int w = 0; w < EW; ++w) {
+        const float f = Mx == -INFINITY ? 0.f : exp2f(sm.m[w][tid] - Mx);  // 0 for m = -inf
+        sm.fac[w][tid] = f;
+        den += f * sm.l[w][tid];
+      }
+      sm.mx[tid] = Mx;
+      sm.den[tid] = den;
+    }
+    __syncthreads();
+    constexpr int NQ = D / 4;
+    for (int i = tid; i < FC * NQ; i += ET) {
+      const int cl = i / NQ, d4 = (i % NQ) * 4, colg = fg * FC + cl;
       const int ct = colg / kTileCols, rr = colg % kTileCols;
       if (!col_ok(ct, rr)) continue;
-      float Mx = -INFINITY;
-  #pragma unroll
-      for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, sm.m[w][cl]);
-      float num = 0.f, den = 0.f;
-      if (Mx != -INFINITY) {
-  #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float f = exp2f(sm.m[w][cl] - Mx);  // 0 for m = -inf
-          num += f * sm.acc[w][cl][d];
-          den += f * sm.l[w][cl];
-        }
-      }
+      f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < EW; ++w) num += sm.fac[w][cl] * *reinterpret_cast<const f32x4_t *>(&sm.acc[w][cl][d4]);
       const int64_t row = (int64_t)(q0 + i0 + col_token(ct, rr)) * Hq + g * G + col_head(ct, rr);
       if (nparts == 1) {
-        store_out(a.out, row * D + d, num / den, a.out_dtype);
+        const float den = sm.den[cl];
+        f32x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = num[e] / den;
+        store_out4(a.out, row * D + d4, v, a.out_dtype);
       } else {
         const int64_t prow = row * a.max_parts + p;
-        a.ws_acc[prow * D + d] = num;
-        if (d == 0) {
-          a.ws_ml[prow * 2] = Mx;
-          a.ws_ml[prow * 2 + 1] = den;
+        store_partial4(a.ws_acc + prow * D + d4, num);
+        if (d4 == 0) {
+          a.ws_ml[prow * 2] = sm.mx[cl];
+          a.ws_ml[prow * 2 + 1] = sm.den[cl];
         }
       }
     }
@@ -2220,7 +2276,7 @@ constexpr int kPfxNct = PA_PREFIX_NCT;  // score tiles per wave
 
 template <int D, int NCT>
 struct __align__(16) SmemPrefix {
-  float acc[kWaves][NCT * 16][D];
+  float acc[kWaves][NCT * 16][D + kAccPad];
   float m[kWaves][NCT * 16];
   float l[kWaves][NCT * 16];
   float fac[kWaves][NCT * 16];  // each wave's weight in the fold of a column
@@ -3525,9 +3581,10 @@ ExtendShape extend_shape(const pa_extend_params *p) {
   if (p->partition_tokens > 0) {
     e.pt = p->partition_tokens;
   } else {
-    // enough workgroups for about two per CU, partitions of at least 64 tokens
+    // enough workgroups for about two per CU (one per CU with four tiles:
+    // eight-wave workgroups), partitions of at least 64 tokens
     const int64_t base = (int64_t)std::max(p->num_seqs, 1) * p->num_kv_heads * e.qgroups;
-    const int64_t want = 2LL * cu_count();
+    const int64_t want = (e.nct >= kExtNctMax ? 1LL : 2LL) * cu_count();
     const int64_t parts = base >= want ? 1 : (want + base - 1) / base;
     int64_t pt = (ctx + parts - 1) / parts;
     pt = std::max<int64_t>(64, (pt + kBS - 1) / kBS * kBS);
@@ -3620,7 +3677,8 @@ pa_status pa_extend(const pa_extend_params *p, void *workspace, size_t workspace
   (merge ? second : first).stop = ev.stop;
   void *args[] = {&a};
   const void *fn = p->head_dim == 128 ? extend_kernel<128>(p->kv_dtype, e.nct) : extend_kernel<64>(p->kv_dtype, e.nct);
-  hipError_t err = launch_kernel(fn, dim3((unsigned)grid), dim3(kThreads), args, 0, hs, first);
+  const int threads = 64 * (e.nct >= kExtNctMax ? extend_waves<kExtNctMax>() : extend_waves<1>());
+  hipError_t err = launch_kernel(fn, dim3((unsigned)grid), dim3(threads), args, 0, hs, first);
   if (err != hipSuccess) return hip_check(err, "pa_extend launch");
   if ((st = hip_check(hipGetLastError(), "pa_extend launch")) != PA_OK || !merge) return st;
   const int64_t rows = (int64_t)p->num_query_rows * p->num_q_heads;
