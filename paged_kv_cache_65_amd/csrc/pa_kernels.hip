@@ -121,6 +121,14 @@ __device__ inline void store_partial4(float *dst, f32x4_t v) {
 
 __device__ inline float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Workgroup barrier that orders LDS only: a wave's global stores in flight
+// need not be acknowledged first (each output element has one writer).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Cross-lane combines that stay in the vector ALU (no LDS round trip).
 // permlane16_swap / permlane32_swap of a value with itself leave, in the two
 // results, the lane's own value and the value of the lane 16 (resp. 32)
@@ -584,9 +592,11 @@ struct MfmaWave {
     }
   }
 
-  // Balanced split: parks the state in LDS instead (acc rows [G][D], then
-  // m[G], l[G]); flush_parked() writes it out later.
+  // Balanced split: parks the state in LDS instead (acc rows [G][D] with
+  // kAccPad floats after each, then m[G], l[G]); flush_parked() writes it
+  // out later.
   __device__ void park_segment(float *st, int lane, int G) const {
+    constexpr int RS = D + kAccPad;
     const int r = lane % 16, tq = lane / 16;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -594,10 +604,10 @@ struct MfmaWave {
       const int h = 16 * ct + r;
       if (h >= G) continue;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4_t *>(st + h * D + 16 * n + 4 * tq) = acc[ct][n];
+      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4_t *>(st + h * RS + 16 * n + 4 * tq) = acc[ct][n];
       if (tq == 0) {
-        st[G * D + h] = m[ct];
-        st[G * D + G + h] = lt;
+        st[G * RS + h] = m[ct];
+        st[G * RS + G + h] = lt;
       }
     }
   }
@@ -608,11 +618,12 @@ template <int D>
 __device__ void flush_parked(const DecodeArgs &a, const float *st, int64_t row0, int64_t prow0, bool whole,
                              bool bad, int lane, int G) {
   const f32x4_t nan4 = {NAN, NAN, NAN, NAN};
+  constexpr int RS = D + kAccPad;
   for (int e = lane * 4; e < G * D; e += 256) {
     const int r = e / D;
-    f32x4_t v = *reinterpret_cast<const f32x4_t *>(st + e);
+    f32x4_t v = *reinterpret_cast<const f32x4_t *>(st + r * RS + e % D);
     if (whole) {
-      const float lt = st[G * D + G + r];
+      const float lt = st[G * RS + G + r];
 #pragma unroll
       for (int k = 0; k < 4; ++k) v[k] = v[k] / lt;
       store_out4(a.out, (row0 + r) * D + e % D, bad ? nan4 : v, a.out_dtype);
@@ -621,8 +632,8 @@ __device__ void flush_parked(const DecodeArgs &a, const float *st, int64_t row0,
     }
   }
   if (!whole && lane < G) {
-    a.ws_ml[(prow0 + lane) * 2] = bad ? NAN : st[G * D + lane];
-    a.ws_ml[(prow0 + lane) * 2 + 1] = st[G * D + G + lane];
+    a.ws_ml[(prow0 + lane) * 2] = bad ? NAN : st[G * RS + lane];
+    a.ws_ml[(prow0 + lane) * 2 + 1] = st[G * RS + G + lane];
   }
 }
 
@@ -1296,7 +1307,7 @@ __global__ __launch_bounds__(kThreads, (partition_wg_per_cu<W, kMfma>())) void p
         return;
       }
     } else {
-      __syncthreads();
+      lds_barrier();
     }
     const int hb = ct * kTileCols, nh = min(kTileCols, Gc - hb);  // heads of this tile
     // One weight per (wave, head) and the head's denominator first, then
@@ -1315,7 +1326,7 @@ __global__ __launch_bounds__(kThreads, (partition_wg_per_cu<W, kMfma>())) void p
       sm.mx[tid] = M;
       sm.den[tid] = den;
     }
-    __syncthreads();
+    lds_barrier();
     constexpr int NQ = D / 4;
     for (int i = tid; i < nh * NQ; i += kThreads) {
       const int h = i / NQ, d4 = (i % NQ) * 4;
@@ -1338,7 +1349,7 @@ __global__ __launch_bounds__(kThreads, (partition_wg_per_cu<W, kMfma>())) void p
         }
       }
     }
-    if (ct + 1 < kTiles) __syncthreads();  // the next tile reuses the LDS rows
+    if (ct + 1 < kTiles) lds_barrier();  // the next tile reuses the LDS rows
   }
 }
 
@@ -1386,7 +1397,7 @@ __device__ inline int attended_blocks(int L, const DecodeArgs &a) {
 
 // Floats of one wave's parking area: G rows of D, then m and l per row
 // (rounded to 16 bytes).
-__host__ __device__ constexpr int park_floats(int G, int D) { return (G * (D + 2) + 3) / 4 * 4; }
+__host__ __device__ constexpr int park_floats(int G, int D) { return (G * (D + kAccPad + 2) + 3) / 4 * 4; }
 // One parking slot: the state, then its output row, partial row (int64) and flags.
 __host__ __device__ constexpr int park_slot_floats(int G, int D) { return park_floats(G, D) + 8; }
 #ifndef PA_PARK_SLOTS_MAX
@@ -1899,27 +1910,24 @@ constexpr int kExtNctMax = 4;
 // Batches of up to this many sequences are dispatched longest context first.
 constexpr int kExtRankMax = 256;
 
-// With four tiles (64 columns) a wave's q fragments live in LDS, not in
-// registers, and the four waves' states meet one 16-column tile at a time:
-// two workgroups then fit a CU (registers and LDS), where one did, and a
-// wave's chain of matrix ops and softmax overlaps another wave's.
 // Waves per extend workgroup: eight with four tiles (one workgroup per CU,
 // two waves per SIMD), so a long context is streamed by eight waves; four
 // otherwise.
 template <int NCT>
 constexpr int extend_waves() { return NCT >= 4 ? 8 : 4; }
 
+// With four tiles (64 columns) a wave's q fragments live in LDS, not in
+// registers (one copy per workgroup: its waves hold the same columns), and
+// the waves' states meet a part of the columns at a time (32 at D = 128, in
+// the LDS one workgroup per CU leaves; 16 at D = 64).
 template <int D, int NCT>
 struct __align__(16) SmemExtend {
   static constexpr int EW = extend_waves<NCT>();
   static constexpr bool kTiled = NCT >= 4;
-  static constexpr int kCols = kTiled ? kTileCols : NCT * kTileCols;  // columns folded at a time
+  static constexpr int kCols = kTiled ? (D >= 128 ? 2 : 1) * kTileCols : NCT * kTileCols;  // folded at a time
   float acc[EW][kCols][D + kAccPad];
   float m[EW][kCols];
   float l[EW][kCols];
-  float fac[EW][kCols];  // each wave's weight in the fold of a column
-  float mx[kCols];
-  float den[kCols];
   u32x4_t q[kTiled ? NCT : 1][kTiled ? D / 32 : 1][64];  // q fragment [tile][c] of each lane
 };
 // Minimum waves per SIMD the register budget is set for.
@@ -1955,12 +1963,13 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
   constexpr int NB = 2;  // blocks in flight per wave
   __shared__ SmemExtend<D, NCT> sm;
   const int Hkv = a.num_kv_heads, G = a.group;
-  // Query groups of one (sequence, KV head, partition) are neighbours in the
-  // grid: they run together and read the same blocks, the later reads served
-  // from the Infinity Cache.
-  const int qg = blockIdx.x % a.qgroups;
+  // The query groups of one (sequence, KV head, partition) take grid slots 8
+  // apart: workgroups are dealt to the 8 XCDs in turn, so they run together
+  // on one XCD and the later groups' block reads are served from its L2.
+  const int qg = (int)(blockIdx.x / 8) % a.qgroups;
   const int tg = qg / a.hparts, hp = qg % a.hparts;  // token group, head part
-  int rest = blockIdx.x / a.qgroups;
+  int rest = (int)(blockIdx.x / 8 / a.qgroups) * 8 + (int)(blockIdx.x % 8);
+  if (rest >= (int64_t)Hkv * a.num_seqs * a.max_parts) return;  // padding of the last 8 slots
   const int g = rest % Hkv;
   rest /= Hkv;
   int s = rest % a.num_seqs;
@@ -2024,6 +2033,12 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
   const int32_t *trow = a.block_tables + (int64_t)s * a.max_blocks + blk0;
 
   // q fragments and causal limits of this lane's columns
+  auto q_row = [&](int ct) {
+    const bool ok = col_ok(ct, r);
+    const int tk = ok ? col_token(ct, r) : 0, hd = g * G + (ok ? col_head(ct, r) : 0);
+    return reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
+                                             ((int64_t)(q0 + i0 + tk) * Hq + hd) * D * 2);
+  };
   v8 qB[NCT][NC];
   int lim[NCT];
   f32x4_t acc[NCT][NT];
@@ -2031,27 +2046,31 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     const bool ok = col_ok(ct, r);
-    const int tk = ok ? col_token(ct, r) : 0, hd = g * G + (ok ? col_head(ct, r) : 0);
-    lim[ct] = ok ? pf + tk : -1;
-    const u32x4_t *qrow = reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
-                                                            ((int64_t)(q0 + i0 + tk) * Hq + hd) * D * 2);
-    if (!SmemExtend<D, NCT>::kTiled || wu == 0) {
+    lim[ct] = ok ? pf + col_token(ct, r) : -1;
+    if constexpr (!SmemExtend<D, NCT>::kTiled) {
+      const u32x4_t *qrow = q_row(ct);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        u32x4_t x = qrow[4 * c + tq];
-        if (!ok) x = u32x4_t{0, 0, 0, 0};
-        if constexpr (SmemExtend<D, NCT>::kTiled)
-          sm.q[ct][c][lane] = x;  // the four waves' columns are the same: one copy
-        else
-          qB[ct][c] = __builtin_bit_cast(v8, x);
-      }
+      for (int c = 0; c < NC; ++c) qB[ct][c] = __builtin_bit_cast(v8, ok ? qrow[4 * c + tq] : u32x4_t{0, 0, 0, 0});
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[ct][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     mm[ct] = -INFINITY;
     ll[ct] = 0.f;
   }
-  if constexpr (SmemExtend<D, NCT>::kTiled) __syncthreads();
+  // Four tiles: the waves stage the q fragments in LDS together (fragment
+  // f = ct * NC + c by wave f mod EW), each once its first blocks are
+  // requested, so the two memory latencies overlap.  Every wave passes the
+  // barrier exactly once.
+  auto stage_q = [&]() {
+    if constexpr (SmemExtend<D, NCT>::kTiled) {
+      for (int fi = wu; fi < NCT * NC; fi += EW) {
+        const int ct = fi / NC, c = fi % NC;
+        const u32x4_t x = col_ok(ct, r) ? q_row(ct)[4 * c + tq] : u32x4_t{0, 0, 0, 0};
+        sm.q[ct][c][lane] = x;
+      }
+      lds_barrier();
+    }
+  };
   // the first position any column of tile ct may not see (wave-uniform)
   int tile_min[NCT];
 #pragma unroll
@@ -2062,6 +2081,7 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
   typename M::Frag fr[NB];
   int bad = 0;
   const int nmine = nblk > wu ? (nblk - wu + EW - 1) / EW : 0;
+  if (nmine == 0) stage_q();
   for (int c0 = 0; c0 < nmine; c0 += 64) {
     const int nc = min(64, nmine - c0);
     int ids = lane < nc ? trow[wu + (c0 + lane) * EW] : 0;
@@ -2078,6 +2098,7 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
       refill(fr[b], b);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (c0 == 0) stage_q();
     for (int j0 = 0; j0 < nc; j0 += NB) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
@@ -2167,19 +2188,20 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
     }
     return;
   }
-  // wave states -> LDS, then fold the four waves (all columns at once, or
-  // one 16-column tile at a time with four tiles); a wave (or the whole
-  // group) that saw no position of a column leaves m = -inf, l = 0 for it
-  constexpr int FG = SmemExtend<D, NCT>::kTiled ? NCT : 1;  // fold rounds
-  constexpr int FC = SmemExtend<D, NCT>::kCols;             // columns per round
+  // wave states -> LDS, then fold the waves, FC columns at a time; a wave
+  // (or the whole group) that saw no position of a column leaves m = -inf,
+  // l = 0 for it
+  constexpr int FC = SmemExtend<D, NCT>::kCols;  // columns per round
+  constexpr int FT = FC / kTileCols;             // tiles per round
+  constexpr int FG = NCT / FT;                   // fold rounds
 #pragma unroll
   for (int fg = 0; fg < FG; ++fg) {
-    if (fg > 0) __syncthreads();  // the previous round has read the buffer
+    if (fg > 0) lds_barrier();  // the previous round has read the buffer
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      if (FG > 1 && ct != fg) continue;
+      if (ct / FT != fg) continue;
       const float lt = sum_xor32(sum_xor16(ll[ct]));
-      const int col = (FG > 1 ? 0 : ct * kTileCols) + r;
+      const int col = (ct % FT) * kTileCols + r;
 #pragma unroll
       for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t *>(&sm.acc[wu][col][16 * t + 4 * tq]) = acc[ct][t];
       if (tq == 0) {
@@ -2187,35 +2209,27 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
         sm.l[wu][col] = lt;
       }
     }
-    __syncthreads();
-    // one weight per (wave, column) and the column's denominator first,
-    // then four dims of a row per thread
-    if (tid < FC) {
-      float Mx = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < EW; ++w) Mx = fmaxf(Mx, sm.m[w][tid]);
-      float den = 0.f;
-#pragma unroll
-      for (int w = 0; w < EW; ++w) {
-        const float f = Mx == -INFINITY ? 0.f : exp2f(sm.m[w][tid] - Mx);  // 0 for m = -inf
-        sm.fac[w][tid] = f;
-        den += f * sm.l[w][tid];
-      }
-      sm.mx[tid] = Mx;
-      sm.den[tid] = den;
-    }
-    __syncthreads();
+    lds_barrier();
+    // four dims of a row per thread, with the column's wave weights
+    // 2^(m_w - M) and denominator computed by each thread
     constexpr int NQ = D / 4;
     for (int i = tid; i < FC * NQ; i += ET) {
       const int cl = i / NQ, d4 = (i % NQ) * 4, colg = fg * FC + cl;
       const int ct = colg / kTileCols, rr = colg % kTileCols;
       if (!col_ok(ct, rr)) continue;
-      f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+      float Mx = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < EW; ++w) num += sm.fac[w][cl] * *reinterpret_cast<const f32x4_t *>(&sm.acc[w][cl][d4]);
+      for (int w = 0; w < EW; ++w) Mx = fmaxf(Mx, sm.m[w][cl]);
+      f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+      float den = 0.f;
+#pragma unroll
+      for (int w = 0; w < EW; ++w) {
+        const float f = Mx == -INFINITY ? 0.f : exp2f(sm.m[w][cl] - Mx);  // 0 for m = -inf
+        num += f * *reinterpret_cast<const f32x4_t *>(&sm.acc[w][cl][d4]);
+        den += f * sm.l[w][cl];
+      }
       const int64_t row = (int64_t)(q0 + i0 + col_token(ct, rr)) * Hq + g * G + col_head(ct, rr);
       if (nparts == 1) {
-        const float den = sm.den[cl];
         f32x4_t v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = num[e] / den;
@@ -2224,8 +2238,8 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
         const int64_t prow = row * a.max_parts + p;
         store_partial4(a.ws_acc + prow * D + d4, num);
         if (d4 == 0) {
-          a.ws_ml[prow * 2] = sm.mx[cl];
-          a.ws_ml[prow * 2 + 1] = sm.den[cl];
+          a.ws_ml[prow * 2] = Mx;
+          a.ws_ml[prow * 2 + 1] = den;
         }
       }
     }
@@ -2425,7 +2439,7 @@ __global__ __launch_bounds__(kThreads) void pa_prefix_kernel(DecodeArgs a) {
     sm.mx[tid] = Mx;
     sm.den[tid] = den;
   }
-  __syncthreads();
+  lds_barrier();
   constexpr int NQ = D / 4;
   const f32x4_t nan4 = {NAN, NAN, NAN, NAN};
   for (int i = tid; i < NCT * kTileCols * NQ; i += kThreads) {
@@ -3636,7 +3650,8 @@ pa_status pa_extend(const pa_extend_params *p, void *workspace, size_t workspace
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return pa::fail(PA_ERR_WORKSPACE, "pa_extend: workspace of %zu bytes (16-byte aligned) required, got %zu",
                     need, workspace ? workspace_bytes : (size_t)0);
-  const int64_t grid = (int64_t)p->num_kv_heads * p->num_seqs * e.qgroups * e.np;
+  // (KV head, sequence, partition) triples in runs of 8, each run once per query group
+  const int64_t grid = ((int64_t)p->num_kv_heads * p->num_seqs * e.np + 7) / 8 * 8 * e.qgroups;
   if (grid > INT32_MAX)
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_extend: more than 2^31-1 workgroups (raise partition_tokens)");
   hipStream_t hs = static_cast<hipStream_t>(stream);
