@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -2054,7 +2055,10 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[ct][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    mm[ct] = -INFINITY;
+    // no score yet: the lowest finite value, so that a block with every
+    // score of the column masked (-inf) gives weights 2^(-inf) = 0 and the
+    // first finite score always raises the reference
+    mm[ct] = -FLT_MAX;
     ll[ct] = 0.f;
   }
   // Four tiles: the waves stage the q fragments in LDS together (fragment
@@ -2144,7 +2148,7 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
             const bool bump = mx > mm[ct] + kLazyLog2;
             if (__builtin_amdgcn_ballot_w64(bump)) {
               const float m_new = bump ? mx : mm[ct];
-              const float alpha = mm[ct] == -INFINITY ? 0.f : exp2_neg(mm[ct] - m_new);
+              const float alpha = exp2_neg(mm[ct] - m_new);  // 0 from -FLT_MAX
               ll[ct] *= alpha;
 #pragma unroll
               for (int t = 0; t < NT; ++t) acc[ct][t] *= alpha;
@@ -2152,7 +2156,7 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
             }
             float pw[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) pw[v] = sv[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[v] - mm[ct]);
+            for (int v = 0; v < 4; ++v) pw[v] = __builtin_amdgcn_exp2f(sv[v] - mm[ct]);
             ll[ct] += (pw[0] + pw[1]) + (pw[2] + pw[3]);
             u32x2_t ph, pl2;
             M::split(pw, ph, pl2);
@@ -2189,8 +2193,8 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
     return;
   }
   // wave states -> LDS, then fold the waves, FC columns at a time; a wave
-  // (or the whole group) that saw no position of a column leaves m = -inf,
-  // l = 0 for it
+  // (or the whole group) that saw no position of a column leaves
+  // m = -FLT_MAX, l = 0 for it (weight 0 beside any wave that did)
   constexpr int FC = SmemExtend<D, NCT>::kCols;  // columns per round
   constexpr int FT = FC / kTileCols;             // tiles per round
   constexpr int FG = NCT / FT;                   // fold rounds
@@ -2224,7 +2228,7 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
       float den = 0.f;
 #pragma unroll
       for (int w = 0; w < EW; ++w) {
-        const float f = Mx == -INFINITY ? 0.f : exp2f(sm.m[w][cl] - Mx);  // 0 for m = -inf
+        const float f = exp2f(sm.m[w][cl] - Mx);  // 0 for m = -FLT_MAX beside a real one
         num += f * *reinterpret_cast<const f32x4_t *>(&sm.acc[w][cl][d4]);
         den += f * sm.l[w][cl];
       }
