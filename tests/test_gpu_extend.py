@@ -114,11 +114,12 @@ def test_sequences_without_new_tokens_and_contract_violations():
         assert np.all(np.isnan(o[3:])) and np.max(np.abs(o[0:3] - ref[0:3])) <= 2e-3
 
 
-@pytest.mark.parametrize("k", [4, 8])
+@pytest.mark.parametrize("k", [4, 8, 16])
 def test_speculative_verify_on_the_70b_shape_sampled(k):
     # workload-3 shapes (64 sequences, 64 / 8 heads, D = 128, L ~ U[128, 4096]) with k = 4
-    # (two score tiles per wave) and k = 8 (four tiles: q in LDS, one tile folded at a time;
-    # the sequences taken longest context first)
+    # (two score tiles per wave), k = 8 (four tiles: q in LDS, eight-wave workgroups, 32
+    # columns folded at a time; the sequences taken longest context first) and k = 16 (two
+    # query groups per (sequence, KV head), their workgroups 8 grid slots apart)
     spec = workloads.named(3)
     wl = workloads.generate(spec)
     gst, ost = gpu_side.build(wl), oracle_side.build(wl)
