@@ -627,6 +627,97 @@ def run_cpu_baseline(wl, seconds):
 
 
 # ---------------------------------------------------------------- copy calibration
+def summarize_waves(rec):
+    """Per-launch summary of the traced build's wave records (uint64 [n][8]: entry,
+    inputs ready, first block, stream end, exit, XCD, blocks, written), times in
+    microseconds from the first wave's entry."""
+    rec = rec[rec[:, 7] == 1].astype(np.int64)
+    base = rec[:, 0].min()
+    us = lambda c: (rec[:, c] - base) / 100.0   # 100 MHz real-time counter
+    t0, t1, t2, t3, t4 = (us(c) for c in range(5))
+    work = rec[:, 6] > 0
+    med = lambda x: round(float(np.median(x)), 2)
+    pct = lambda x, q: round(float(np.percentile(x, q)), 2)
+    xcd = [med(t3[work & (rec[:, 5] == x)]) if np.any(work & (rec[:, 5] == x)) else None for x in range(8)]
+    return {"waves": int(len(rec)), "working_waves": int(work.sum()), "span_us": round(float(t4.max()), 2),
+            "entry_us": {"median": med(t0), "max": round(float(t0.max()), 2)},
+            "inputs_ready_us": {"median": med(t1), "p90": pct(t1, 90)},
+            "first_block_us": {"median": med(t2[work]), "p90": pct(t2[work], 90)},
+            "stream_end_us": {"median": med(t3[work]), "p10": pct(t3[work], 10), "p90": pct(t3[work], 90),
+                              "max": round(float(t3[work].max()), 2)},
+            "exit_us": {"median": med(t4[work]), "max": round(float(t4.max()), 2)},
+            "blocks_per_wave": {"median": med(rec[work, 6]), "max": int(rec[work, 6].max())},
+            "stream_end_median_us_by_xcd": xcd}
+
+
+def run_wave_trace(args, wl):
+    """--wave-trace: per-wave timeline of the attention launch of the workload
+    (the decode without a fused append, or pa_extend with --extend K), from the
+    traced build libpa_trace.so; one JSON line with a summary per launch."""
+    import torch
+    from paged_kv_cache_65_amd import binding as pa
+    from paged_kv_cache_65_amd import build as pa_build
+    if not os.path.exists(pa_build.TRACE_LIB):
+        sys.exit("bench.py --wave-trace needs the traced build: python -m paged_kv_cache_65_amd.build --trace")
+    pa.use_library(pa_build.TRACE_LIB)
+    L = pa.lib()
+    L.pa_trace_read.argtypes, L.pa_trace_read.restype = [ctypes.c_void_p, ctypes.c_size_t], ctypes.c_int
+    L.pa_trace_clear.argtypes, L.pa_trace_clear.restype = [], ctypes.c_int
+    L.pa_trace_bytes.argtypes, L.pa_trace_bytes.restype = [], ctypes.c_size_t
+    spec = wl.spec
+    dev = torch.device("cuda:0")
+    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    MB = int(-(-int(wl.prompt_lens.max()) // 16))
+
+    def to_dev(a):
+        if spec.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    k_rows = np.concatenate([wl.prefix_k, wl.k_tokens]) if spec.prefix_len else wl.k_tokens
+    v_rows = np.concatenate([wl.prefix_v, wl.v_tokens]) if spec.prefix_len else wl.v_tokens
+    rep = build_replica(pa, torch, wl, wl.free_order, to_dev(k_rows), to_dev(v_rows), MB, S, dev)
+    tab, lens = rep.pool.seq_export(rep.seq_ids, MB)
+    tab_d, lens_d = torch.from_numpy(tab).to(dev), torch.from_numpy(lens).to(dev)
+    out_dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[spec.out_dtype]
+    k = args.extend
+    if k:
+        q = to_dev(workloads.round_to(np.random.default_rng(spec.seed + 77).standard_normal(
+            (S * k, Hq, D), dtype=np.float32), spec.dtype))
+        qs = torch.arange(0, S * k + 1, k, dtype=torch.int32, device=dev)
+        out = torch.empty((S * k, Hq, D), dtype=q.dtype, device=dev)
+
+        def call():
+            pa.pa_extend(out, q, rep.k_cache, rep.v_cache, tab_d, lens_d, qs, Hkv, int(lens.max()), k,
+                         spec.fp32_scale(), partition_tokens=args.partition_tokens or 0)
+        kernel, what = "pa_extend_kernel", f"pa_extend, {k} new tokens per sequence"
+    else:
+        q = to_dev(wl.q)
+        out = torch.empty((S, Hq, D), dtype=out_dt, device=dev)
+        sp = (spec.prefix_len // 16) if spec.prefix_len else 0
+
+        def call():
+            pa.pa_decode(out, q, rep.k_cache, rep.v_cache, tab_d, lens_d, Hkv, int(lens.max()),
+                         spec.fp32_scale(), partition_tokens=-1, sliding_window=spec.window,
+                         shared_prefix_blocks=sp)
+        kernel, what = "pa_balanced_kernel", "pa_decode (balanced split, no fused append)"
+    buf = np.zeros(L.pa_trace_bytes() // 8, dtype=np.uint64)
+    launches = []
+    for r in range(max(1, args.steps or 3)):
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        assert L.pa_trace_clear() == 0
+        call()
+        torch.cuda.synchronize()
+        assert L.pa_trace_read(buf.ctypes.data, buf.nbytes) == 0
+        launches.append(summarize_waves(buf.reshape(-1, 8)))
+        log(f"traced launch {r}: span {launches[-1]['span_us']} us")
+    print(json.dumps({"wave_trace": kernel, "launch": what, "workload": spec.name,
+                      "clock": "s_memrealtime, 100 MHz, from the first wave's entry", "launches": launches}),
+          flush=True)
+
+
 def run_copy_calibration(nbytes):
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -807,6 +898,9 @@ def main():
                     help="only run a plain device copy of BYTES (counter calibration)")
     ap.add_argument("--extend", type=int, default=0, metavar="K",
                     help="only measure multi-query attention with K new tokens per sequence of the workload")
+    ap.add_argument("--wave-trace", action="store_true",
+                    help="only print the per-wave timeline of --steps traced attention launches (default 3), "
+                         "from the traced build (python -m paged_kv_cache_65_amd.build --trace)")
     ap.add_argument("--swap", type=int, default=0, metavar="BLOCKS",
                     help="only measure swap-out / swap-in of BLOCKS scattered cache blocks")
     args = ap.parse_args()
@@ -825,7 +919,7 @@ def main():
     base = workloads.named(args.workload)
     loop = base.decode_steps > 0 and not args.extend   # a decode loop: its own steps, one pool
     if args.steps is None:
-        args.steps = base.decode_steps if loop else 200
+        args.steps = 3 if args.wave_trace else base.decode_steps if loop else 200
     if args.replicas is None:
         args.replicas = 1 if loop else 3
     if args.partition_tokens is None:
@@ -835,6 +929,9 @@ def main():
     wl = workloads.generate(spec)
     log(f"workload {spec.name} generated in {time.perf_counter() - t:.1f} s "
         f"(sum of prompt lengths {int(wl.prompt_lens.sum())})")
+    if args.wave_trace:
+        run_wave_trace(args, wl)
+        return
     if args.extend:
         run_extend_bench(args, wl, args.extend)
         return

@@ -64,6 +64,15 @@ class pa_extend_params(ctypes.Structure):
 _lib = None
 
 
+def use_library(path: str) -> None:
+    """Loads the library from `path` instead of libpa.so (the traced build,
+    libpa_trace.so, for a per-wave timeline); call before anything else here."""
+    global LIB_PATH
+    if _lib is not None:
+        raise RuntimeError("the library is already loaded")
+    LIB_PATH = path
+
+
 def lib():
     """Loads libpa.so once; raises if it is not built."""
     global _lib

@@ -12,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
+TRACE_LIB = os.path.join(HERE, "libpa_trace.so")  # diagnostic build with per-wave timestamps
 SOURCES = ["pa_kernels.hip", "pa_pool.cpp", "pa_error.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -27,10 +28,13 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+def build(verbose: bool = False, extra_flags=(), trace: bool = False) -> str:
+    """Builds libpa.so; with trace=True the diagnostic libpa_trace.so instead
+    (-DPA_TRACE: the balanced and extend kernels record per-wave timestamps)."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra_flags, *srcs, "-o", tmp]
+    out = TRACE_LIB if trace else LIB
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(["-DPA_TRACE"] if trace else []), *extra_flags, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -40,9 +44,9 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if errs.strip() and verbose:
         print(errs, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, trace="--trace" in sys.argv[1:]))

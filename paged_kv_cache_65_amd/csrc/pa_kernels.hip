@@ -130,6 +130,43 @@ __device__ inline void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Per-wave timeline of the balanced and extend kernels, in a traced build
+// only (compiled with -DPA_TRACE; the library's own build has none of it):
+// each wave stamps the real-time counter (100 MHz) at entry, when its
+// inputs are ready (lengths scanned / contexts ranked), at its first block,
+// when its stream ends and at its exit, and records its XCD and the blocks it
+// streamed; pa_trace_read copies the records of the last launch back.
+#ifdef PA_TRACE
+constexpr int kTraceWaves = 65536;
+__device__ uint64_t pa_trace_buf[kTraceWaves * 8];
+struct WaveTrace {
+  uint64_t t[4] = {0, 0, 0, 0};
+  __device__ void stamp(int k) { t[k] = __builtin_amdgcn_s_memrealtime(); }
+  __device__ void first() {
+    if (t[2] == 0) stamp(2);
+  }
+  __device__ void write(int64_t wave, int lane, uint64_t units) {
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    if (lane == 0 && wave >= 0 && wave < kTraceWaves) {
+      uint64_t *p = pa_trace_buf + wave * 8;
+      for (int k = 0; k < 4; ++k) p[k] = t[k];
+      p[4] = t_end;
+      p[5] = xcc;
+      p[6] = units;
+      p[7] = 1;
+    }
+  }
+};
+#else
+struct WaveTrace {
+  __device__ void stamp(int) {}
+  __device__ void first() {}
+  __device__ void write(int64_t, int, uint64_t) {}
+};
+#endif
+
 // Cross-lane combines that stay in the vector ALU (no LDS round trip).
 // permlane16_swap / permlane32_swap of a value with itself leave, in the two
 // results, the lane's own value and the value of the lane 16 (resp. 32)
@@ -1450,6 +1487,8 @@ __device__ inline int pair_of_unit(const SmemBalanced &sm, int u, int Hkv, int S
 
 template <class W, int D>
 __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(DecodeArgs a) {
+  WaveTrace tr;
+  tr.stamp(0);
   __shared__ SmemBalanced sm;
   extern __shared__ __align__(16) float park_lds[];  // kBWaves x park_slots x park_slot_floats(G, D)
   const int tid = threadIdx.x, lane = tid % 64;
@@ -1484,6 +1523,7 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
     if (lane == 63) sm.pre[S] = inc;
   }
   __syncthreads();
+  tr.stamp(1);
   const int U = Hkv * sm.pre[S];
   const int NW = a.num_workers;
   const int C = (U + NW - 1) / NW;
@@ -1587,6 +1627,7 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
   };
   if (u0 >= u1) {
     q_to_lds();
+    tr.write(w, lane, 0);
     return;
   }
 
@@ -1690,6 +1731,7 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
           // The window's first block masks the tokens before its first position.
           const int lo = (a.window > 0 && (mt & kUPairStart))
                              ? window_first_token(sm.len[pq / Hkv], a.window) % kBS : 0;
+          tr.first();
           wave.compute(fr[b], token_mask(lo, (int)(mt & kUValid)), a.scale_log2, lane, nt, sm.knew[wu][k],
                        sm.vnew[wu][k]);
           if (mt & kULast) {  // (a segment may go on into the next chunk)
@@ -1724,12 +1766,14 @@ __global__ __launch_bounds__(kBThreads, W::kBalWgPerCu) void pa_balanced_kernel(
     }
     c0 += nc;
   }
+  tr.stamp(3);
   for (int k = 0; k < nparked; ++k) {
     const float *st = park + k * slot_f;
     const int64_t *meta_p = reinterpret_cast<const int64_t *>(st + park_floats(G, D));
     const int64_t fl = meta_p[2];
     flush_parked<D>(a, st, meta_p[0], meta_p[1], (fl & 1) != 0, (fl & 2) != 0, lane, G);
   }
+  tr.write(w, lane, (uint64_t)(u1 - u0));
 }
 
 // ---------------------------------------------------------------- merge kernel
@@ -1958,6 +2002,8 @@ __device__ inline bool extend_seq_valid(int L, int n, const ExtendArgs &a) {
 template <int DT, int D, int NCT>
 __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())) void pa_extend_kernel(ExtendArgs a) {
   constexpr int EW = extend_waves<NCT>(), ET = EW * 64;
+  WaveTrace tr;
+  tr.stamp(0);
   using M = MfmaWave<DT, D>;
   using v8 = typename M::v8;
   constexpr int NC = D / 32, NT = D / 16;
@@ -2000,6 +2046,7 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
     __syncthreads();
     s = rank_pick;
   }
+  tr.stamp(1);
   const int wu = __builtin_amdgcn_readfirstlane(tid / 64);
   const int L = a.context_lens[s];
   const int q0 = a.query_start[s];
@@ -2109,6 +2156,7 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
         const int i = j0 + b;
         refill(fr[(b + NB - 1) % NB], i + NB - 1);
         if (i < nc) {
+          tr.first();
           typename M::Frag &f = fr[b];
           const int b0 = (blk0 + wu + (c0 + i) * EW) * kBS;  // position of the block's token 0
           if (b0 + kBS > L) {
@@ -2174,6 +2222,7 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
       }
     }
   }
+  tr.stamp(3);
   if (__syncthreads_or(bad)) {
     for (int i = tid; i < NCT * kTileCols * D; i += ET) {
       const int col = i / D, d = i % D, ct = col / kTileCols, rr = col % kTileCols;
@@ -2248,6 +2297,7 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
       }
     }
   }
+  tr.write((int64_t)blockIdx.x * EW + wu, lane, (uint64_t)nmine);
 }
 
 // One wave per (query row, head) whose group was split: folds its partials.
@@ -3632,6 +3682,23 @@ const void *extend_kernel(pa_dtype dt, int nct) {
 }
 
 }  // namespace
+
+#ifdef PA_TRACE
+extern "C" {
+// Traced build: copies the wave records of the last traced launch (8 uint64
+// per wave: entry, inputs ready, first block, stream end, exit, XCD, blocks,
+// written flag) to host memory; pa_trace_clear zeroes them.  Synchronous.
+int pa_trace_read(void *host, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(pa_trace_buf), std::min(bytes, sizeof(pa_trace_buf)), 0,
+                                  hipMemcpyDeviceToHost);
+}
+int pa_trace_clear() {
+  static uint64_t zeros[kTraceWaves * 8];
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(pa_trace_buf), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice);
+}
+size_t pa_trace_bytes() { return sizeof(pa_trace_buf); }
+}  // extern "C"
+#endif
 
 extern "C" {
 

@@ -84,3 +84,22 @@ def test_oracle_sample_rebuilds_the_rows_a_replica_attends():
         # a replica that took every other step attends to those rows only
         part = bench.oracle_sample(wl, [1], [1, 3])
         assert not np.array_equal(part[0], full[1])
+
+
+def test_wave_trace_summary_reads_the_records():
+    # records as the traced build writes them: entry, inputs ready, first block,
+    # stream end, exit (100 MHz ticks), XCD, blocks, written flag
+    import numpy as np
+    rec = np.zeros((6, 8), dtype=np.uint64)
+    for w in range(4):
+        rec[w] = [1000 + w, 1100 + w, 1500 + w, 9000 + 100 * w, 9050 + 100 * w, w % 2, 10, 1]
+    rec[4] = [1200, 1300, 0, 0, 1400, 1, 0, 1]     # a wave without units
+    # rec[5] never written (flag 0): ignored
+    s = bench.summarize_waves(rec)
+    assert s["waves"] == 5 and s["working_waves"] == 4
+    assert s["span_us"] == (9350 - 1000) / 100.0
+    assert abs(s["first_block_us"]["median"] - 5.015) <= 0.006   # (rounded to 0.01 us)
+    assert s["stream_end_us"]["max"] == (9300 - 1000) / 100.0
+    assert s["stream_end_median_us_by_xcd"][0] == (9100 - 1000) / 100.0   # waves 0 and 2
+    assert s["stream_end_median_us_by_xcd"][1] == (9200 - 1000) / 100.0   # waves 1 and 3
+    assert s["stream_end_median_us_by_xcd"][2] is None
