@@ -1932,8 +1932,9 @@ __global__ __launch_bounds__(kMergeWaves * 64) void pa_merge_balanced_kernel(Dec
 // 16 heads of one token and a query group NCT*16 of that token's heads
 // (hparts query groups per token).  Workgroup = (KV head g,
 // sequence s, query group, partition of the blocks the group needs); its
-// four waves take every fourth block, their states meet in LDS, and the
-// group writes final rows or (m, l, acc) partials for the merge.
+// EW waves (four, or eight with four tiles) take every EW-th block, their
+// states meet in LDS, and the group writes final rows or (m, l, acc)
+// partials for the merge.
 struct ExtendArgs {
   void *out;                      // [T][Hq][D]
   const void *q;                  // [T][Hq][D]
