@@ -730,6 +730,34 @@ def run_copy_calibration(nbytes):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
+def run_read_ceiling(nbytes, reps=20):
+    """--read-ceiling: what plain library kernels reach on this GPU's HBM, as a
+    reference beside the 8 TB/s peak: a full reduction reading nbytes (torch.sum
+    over float32, result 4 bytes) and a device copy of nbytes / 2 (read + write),
+    each timed with events over `reps` launches."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    src = torch.ones(nbytes // 8, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, moved in (("sum_read", lambda: torch.sum(x), nbytes),
+                            ("copy_read_write", lambda: dst.copy_(src), nbytes)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for i in range(reps):
+            ev[2 * i].record()
+            fn()
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        ms = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)])
+        out[name] = {"bytes": moved, "median_us": round(float(np.median(ms)) * 1e3, 2),
+                     "GBps": round(moved / (float(np.median(ms)) / 1e3) / 1e9, 1),
+                     "frac_of_8TBps": round(moved / (float(np.median(ms)) / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    print(json.dumps({"read_ceiling": out, "device": torch.cuda.get_device_name(0)}), flush=True)
+
+
 def run_extend_bench(args, wl, k):
     """Speculative verification on the workload: the last k cached tokens of every
     sequence are the drafted ones, each attending causally (pa_extend), over R
@@ -898,6 +926,8 @@ def main():
                     help="only run a plain device copy of BYTES (counter calibration)")
     ap.add_argument("--extend", type=int, default=0, metavar="K",
                     help="only measure multi-query attention with K new tokens per sequence of the workload")
+    ap.add_argument("--read-ceiling", type=int, default=0, metavar="BYTES",
+                    help="only time plain library kernels over BYTES of HBM (a reduction and a copy)")
     ap.add_argument("--wave-trace", action="store_true",
                     help="only print the per-wave timeline of --steps traced attention launches (default 3), "
                          "from the traced build (python -m paged_kv_cache_65_amd.build --trace)")
@@ -912,6 +942,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         run_copy_calibration(args.copy_calibration)
+        return
+    if args.read_ceiling:
+        run_read_ceiling(args.read_ceiling)
         return
     if args.swap:
         run_swap_bench(args.swap, 10)
