@@ -718,6 +718,64 @@ def run_wave_trace(args, wl):
           flush=True)
 
 
+def run_read_probe(args, wl, reps=20):
+    """--read-probe: the read rate of the balanced split's access pattern with none
+    of its math (the traced build's pa_read_probe) over the workload's cache: every
+    (sequence, KV head, block) unit's K and V tiles once, in the split's order."""
+    import torch
+    from paged_kv_cache_65_amd import binding as pa
+    from paged_kv_cache_65_amd import build as pa_build
+    if not os.path.exists(pa_build.TRACE_LIB):
+        sys.exit("bench.py --read-probe needs the traced build: python -m paged_kv_cache_65_amd.build --trace")
+    spec = wl.spec
+    if spec.head_dim != 128 or spec.dtype == "f32" or spec.cache in ("i8", "fp8"):
+        sys.exit("bench.py --read-probe reads 4 KiB tiles: a D = 128 16-bit cache")
+    pa.use_library(pa_build.TRACE_LIB)
+    L = pa.lib()
+    L.pa_read_probe.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t] + \
+        [ctypes.c_void_p] * 3
+    L.pa_read_probe.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    S, Hkv = spec.num_seqs, spec.num_kv_heads
+    MB = int(-(-int(wl.prompt_lens.max()) // 16))
+
+    def to_dev(a):
+        if spec.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    rep = build_replica(pa, torch, wl, wl.free_order, to_dev(wl.k_tokens), to_dev(wl.v_tokens), MB, S, dev)
+    tab, lens = rep.pool.seq_export(rep.seq_ids, MB)
+    units = []   # (sequence, KV head, block) order: tile index block * Hkv + head
+    for s in range(S):
+        blocks = tab[s, :-(-int(lens[s]) // 16)].astype(np.int64)
+        units += [blocks * Hkv + g for g in range(Hkv)]
+    tiles = np.concatenate(units).astype(np.int32)
+    tiles_d = torch.from_numpy(tiles).to(dev)
+    n = int(tiles.size)
+    sink = torch.zeros(4 * 1024, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    hip = Hip()
+    ev = [(hip.event(timing=True), hip.event(timing=True)) for _ in range(reps)]
+    args_of = lambda e0, e1: (ctypes.c_void_p(rep.k_cache.data_ptr()), ctypes.c_void_p(rep.v_cache.data_ptr()),
+                              ctypes.c_void_p(tiles_d.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
+                              sink.numel(), e0, e1, stream)
+    for _ in range(5):
+        pa._check(L.pa_read_probe(*args_of(None, None)))
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        pa._check(L.pa_read_probe(*args_of(e0, e1)))
+    torch.cuda.synchronize()
+    us = np.array([hip.elapsed_ms(e0, e1) for e0, e1 in ev]) * 1e3
+    nbytes = n * 2 * 4096
+    print(json.dumps({"read_probe": "pa_read_probe (balanced split access pattern, no math)", "workload": spec.name,
+                      "units": n, "bytes": nbytes, "launches": reps,
+                      "median_us": round(float(np.median(us)), 2), "p10_us": round(float(np.percentile(us, 10)), 2),
+                      "p90_us": round(float(np.percentile(us, 90)), 2),
+                      "GBps": round(nbytes / float(np.median(us)) / 1e3, 1),
+                      "frac_of_8TBps": round(nbytes / float(np.median(us)) / 1e3 / HBM_PEAK_GBPS, 4)}), flush=True)
+
+
 def run_copy_calibration(nbytes):
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -928,6 +986,9 @@ def main():
                     help="only measure multi-query attention with K new tokens per sequence of the workload")
     ap.add_argument("--read-ceiling", type=int, default=0, metavar="BYTES",
                     help="only time plain library kernels over BYTES of HBM (a reduction and a copy)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only time the traced build's read probe over the workload's cache (its K / V tiles "
+                         "in the balanced split's order, no math)")
     ap.add_argument("--wave-trace", action="store_true",
                     help="only print the per-wave timeline of --steps traced attention launches (default 3), "
                          "from the traced build (python -m paged_kv_cache_65_amd.build --trace)")
@@ -964,6 +1025,9 @@ def main():
         f"(sum of prompt lengths {int(wl.prompt_lens.sum())})")
     if args.wave_trace:
         run_wave_trace(args, wl)
+        return
+    if args.read_probe:
+        run_read_probe(args, wl)
         return
     if args.extend:
         run_extend_bench(args, wl, args.extend)

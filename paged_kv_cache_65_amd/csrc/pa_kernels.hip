@@ -3682,6 +3682,54 @@ const void *extend_kernel(pa_dtype dt, int nct) {
   return dt == PA_BF16 ? extend_kernel_nct<PA_BF16, D>(nct) : extend_kernel_nct<PA_F16, D>(nct);
 }
 
+#ifdef PA_TRACE
+// Read probe (traced build only): the balanced split's access pattern with
+// none of its math.  A persistent grid of four-wave workgroups (one per CU)
+// cuts a list of tile indices (block * num_kv_heads + head) into equal
+// contiguous shares; each wave reads its units' K and V tiles (4 KiB each)
+// through a 4-deep register ring of 16-byte non-temporal loads per lane and
+// folds the data with XOR into one word, written per wave so that no load is
+// dropped.  It shows what read rate that pattern reaches on the device.
+__global__ __launch_bounds__(256, 1) void pa_read_probe_kernel(const uint8_t *k_cache, const uint8_t *v_cache,
+                                                                const int32_t *tiles, int32_t n, uint32_t *sink) {
+  constexpr int R = 4, NF = 4;  // ring depth; 1 KiB fragments per 4 KiB tile
+  const int lane = threadIdx.x % 64;
+  const int w = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int NW = gridDim.x * 4;
+  const int C = (n + NW - 1) / NW, u0 = min(n, w * C), u1 = min(n, u0 + C);
+  u32x4_t acc = {0, 0, 0, 0};
+  for (int c0 = u0; c0 < u1; c0 += 64) {
+    const int nc = min(64, u1 - c0);
+    const int my = lane < nc ? tiles[c0 + lane] : 0;
+    u32x4_t fr[R][2 * NF];
+    auto load = [&](u32x4_t (&f)[2 * NF], int i) {
+      const int64_t off = (int64_t)__builtin_amdgcn_readlane(my, min(i, nc - 1)) * 4096;
+      const u32x4_t *kp = reinterpret_cast<const u32x4_t *>(k_cache + off);
+      const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(v_cache + off);
+#pragma unroll
+      for (int c = 0; c < NF; ++c) f[c] = __builtin_nontemporal_load(&kp[c * 64 + lane]);
+#pragma unroll
+      for (int c = 0; c < NF; ++c) f[NF + c] = __builtin_nontemporal_load(&vp[c * 64 + lane]);
+    };
+#pragma unroll
+    for (int b = 0; b < R - 1; ++b) load(fr[b], b);
+    for (int i0 = 0; i0 < nc; i0 += R) {
+#pragma unroll
+      for (int b = 0; b < R; ++b) {
+        const int i = i0 + b;
+        load(fr[(b + R - 1) % R], i + R - 1);  // (past the end: the last tile again)
+        if (i < nc) {
+#pragma unroll
+          for (int c = 0; c < 2 * NF; ++c) acc ^= fr[b][c];
+        }
+      }
+    }
+  }
+  const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (lane == 0) sink[w] = x;
+}
+#endif
+
 }  // namespace
 
 #ifdef PA_TRACE
@@ -3698,6 +3746,27 @@ int pa_trace_clear() {
   return (int)hipMemcpyToSymbol(HIP_SYMBOL(pa_trace_buf), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice);
 }
 size_t pa_trace_bytes() { return sizeof(pa_trace_buf); }
+
+// Read probe over n units of the tile list `tiles` (device, int32 tile
+// indices of 4 KiB K and V tiles: a D = 128 16-bit cache), one workgroup per
+// CU; sink (device) takes one word per wave (4 per CU).  Events as in
+// pa_decode_params.  Returns a pa_status.
+int pa_read_probe(const void *k_cache, const void *v_cache, const int32_t *tiles, int32_t n, uint32_t *sink,
+                  size_t sink_words, void *start_event, void *stop_event, void *stream) {
+  const int grid = cu_count();
+  if (!k_cache || !v_cache || !tiles || !sink || n <= 0 || sink_words < (size_t)grid * 4)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_read_probe: null pointer, n <= 0 or a sink of fewer than %d words",
+                    grid * 4);
+  LaunchEvents ev;
+  ev.start = static_cast<hipEvent_t>(start_event);
+  ev.stop = static_cast<hipEvent_t>(stop_event);
+  const uint8_t *k = static_cast<const uint8_t *>(k_cache), *v = static_cast<const uint8_t *>(v_cache);
+  void *args[] = {&k, &v, &tiles, &n, &sink};
+  const hipError_t err = launch_kernel(reinterpret_cast<const void *>(&pa_read_probe_kernel), dim3(grid),
+                                       dim3(256), args, 0, static_cast<hipStream_t>(stream), ev);
+  if (err != hipSuccess) return hip_check(err, "pa_read_probe launch");
+  return hip_check(hipGetLastError(), "pa_read_probe launch");
+}
 }  // extern "C"
 #endif
 
