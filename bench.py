@@ -702,6 +702,8 @@ def run_wave_trace(args, wl):
                          shared_prefix_blocks=sp)
         kernel, what = "pa_balanced_kernel", "pa_decode (balanced split, no fused append)"
     buf = np.zeros(L.pa_trace_bytes() // 8, dtype=np.uint64)
+    if k:
+        warm_past_transient(lambda i: call(), args.warmup)
     launches = []
     for r in range(max(1, args.steps or 3)):
         for _ in range(args.warmup):
@@ -716,6 +718,26 @@ def run_wave_trace(args, wl):
     print(json.dumps({"wave_trace": kernel, "launch": what, "workload": spec.name,
                       "clock": "s_memrealtime, 100 MHz, from the first wave's entry", "launches": launches}),
           flush=True)
+
+
+def run_extend_ramp(args, L, params, ws_ptr, ws_bytes, stream, hip, spec, k, n=1000):
+    """--extend K --ramp: per-call times of n pa_extend calls started from an idle
+    GPU (one second of sleep first), as means over windows of call indices."""
+    from paged_kv_cache_65_amd import binding as pa
+    ev_a = [hip.event(timing=True) for _ in range(n)]
+    ev_b = [hip.event(timing=True) for _ in range(n)]
+    time.sleep(1.0)
+    for i in range(n):
+        prm = params[i % len(params)]
+        prm.start_event, prm.stop_event = ev_a[i], ev_b[i]
+        pa._check(L.pa_extend(ctypes.byref(prm), ws_ptr, ws_bytes, stream))
+        prm.start_event = prm.stop_event = None
+    hip.sync_event(ev_b[-1])
+    t = np.array([hip.elapsed_ms(ev_a[i], ev_b[i]) * 1e3 for i in range(n)])
+    edges = [0, 5, 15, 35, 60, 100, 200, 400, 700, n]
+    print(json.dumps({"ramp": "pa_extend per-call time from idle", "workload": spec.name, "draft_tokens": k,
+                      "calls": n, "windows": [{"calls": [a, b], "mean_us": round(float(t[a:b].mean()), 2)}
+                                             for a, b in zip(edges[:-1], edges[1:])]}), flush=True)
 
 
 def run_read_probe(args, wl, reps=20):
@@ -816,6 +838,28 @@ def run_read_ceiling(nbytes, reps=20):
     print(json.dumps({"read_ceiling": out, "device": torch.cuda.get_device_name(0)}), flush=True)
 
 
+# pa_extend launches with several query tiles per wave (k >= 8 at G = 8) keep the
+# matrix cores busy enough that, from idle, the GPU's clock management settles
+# only after a transient: per-call times over a long run of calls (--ramp) go
+# 110 -> 135 -> 105 us at k = 8 over the first ~200 calls (~25 ms), while the
+# decode and k = 1 launches are flat from the start.  Their timing warms up past it.
+EXTEND_WARMUP_S = 0.1
+
+
+def warm_past_transient(call, min_calls, seconds=EXTEND_WARMUP_S, sync=None):
+    """Runs call(i) for i = 0, 1, ... until at least min_calls calls and `seconds`
+    of wall time (synchronized every 20 calls) have passed; returns the count."""
+    import torch
+    t0, i = time.perf_counter(), 0
+    while i < min_calls or time.perf_counter() - t0 < seconds:
+        call(i)
+        i += 1
+        if i % 20 == 0:
+            (sync or torch.cuda.synchronize)()
+    (sync or torch.cuda.synchronize)()
+    return i
+
+
 def run_extend_bench(args, wl, k):
     """Speculative verification on the workload: the last k cached tokens of every
     sequence are the drafted ones, each attending causally (pa_extend), over R
@@ -862,9 +906,10 @@ def run_extend_bench(args, wl, k):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     ev_a = [hip.event(timing=True) for _ in range(K)]
     ev_b = [hip.event(timing=True) for _ in range(K)]
-    for i in range(W):
-        pa._check(L.pa_extend(ctypes.byref(params[i % R]), ws_ptr, ws_bytes, stream))
-    torch.cuda.synchronize()
+    if args.ramp:
+        run_extend_ramp(args, L, params, ws_ptr, ws_bytes, stream, hip, wl.spec, k)
+        return
+    W = warm_past_transient(lambda i: pa._check(L.pa_extend(ctypes.byref(params[i % R]), ws_ptr, ws_bytes, stream)), W)
     t0 = time.perf_counter()
     for i in range(K):
         prm = params[i % R]
@@ -883,7 +928,7 @@ def run_extend_bench(args, wl, k):
     rec = {"metric": "speculative-verify attention tokens/s (k drafted tokens per sequence, pa_extend)",
            "value": round(T * K / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
            "ms_per_step": round(elapsed / K * 1e3, 5), "higher_is_better": True, "dtype": spec.dtype,
-           "data": "synthetic",
+           "data": "synthetic", "warmup_note": f"{W} calls, at least {EXTEND_WARMUP_S} s (clock transient)",
            "config": {"workload": spec.name, "draft_tokens": k, "query_rows": T,
                       "partition_tokens": pa.pa_extend_partition_tokens(params[0]), "replicas": R,
                       "device": torch.cuda.get_device_name(0)},
@@ -984,6 +1029,8 @@ def main():
                     help="only run a plain device copy of BYTES (counter calibration)")
     ap.add_argument("--extend", type=int, default=0, metavar="K",
                     help="only measure multi-query attention with K new tokens per sequence of the workload")
+    ap.add_argument("--ramp", action="store_true",
+                    help="with --extend: only print per-call times of 1000 calls started from an idle GPU")
     ap.add_argument("--read-ceiling", type=int, default=0, metavar="BYTES",
                     help="only time plain library kernels over BYTES of HBM (a reduction and a copy)")
     ap.add_argument("--read-probe", action="store_true",

@@ -62,6 +62,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -491,23 +493,28 @@ struct MfmaWave {
                                                    __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
   }
 
-  // Splits p into hi + lo 16-bit values (hi = round(p), lo = round(p - hi)).
+  // Two floats rounded to nearest even and packed into one word (the first
+  // in the low half): one v_cvt_pk_{bf16,f16}_f32.
+  __device__ static uint32_t pack2(float a, float b) {
+    if constexpr (DT == PA_BF16)
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+    else
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+  }
+  // The two 16-bit values of a packed word, widened back to float.
+  __device__ static f32x2_t unpack2(uint32_t w) {
+    if constexpr (DT == PA_BF16)
+      return f32x2_t{__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)};
+    else
+      return __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
+  }
+  // Splits p into hi + lo 16-bit values (hi = round(p), lo = round(p - hi)),
+  // two values per conversion.
   __device__ static void split(const float p[4], u32x2_t &hi, u32x2_t &lo) {
-    uint32_t h[4], w[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      if constexpr (DT == PA_BF16) {
-        __bf16 x = (__bf16)p[v];
-        h[v] = __builtin_bit_cast(uint16_t, x);
-        w[v] = __builtin_bit_cast(uint16_t, (__bf16)(p[v] - (float)x));
-      } else {
-        _Float16 x = (_Float16)p[v];
-        h[v] = __builtin_bit_cast(uint16_t, x);
-        w[v] = __builtin_bit_cast(uint16_t, (_Float16)(p[v] - (float)x));
-      }
-    }
-    hi = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-    lo = u32x2_t{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+    const uint32_t h01 = pack2(p[0], p[1]), h23 = pack2(p[2], p[3]);
+    const f32x2_t b01 = unpack2(h01), b23 = unpack2(h23);
+    hi = u32x2_t{h01, h23};
+    lo = u32x2_t{pack2(p[0] - b01.x, p[1] - b01.y), pack2(p[2] - b23.x, p[3] - b23.y)};
   }
 
   // Online-softmax step of column tile ct for the block's scores s[] (log2
@@ -2158,6 +2165,12 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
         refill(fr[(b + NB - 1) % NB], i + NB - 1);
         if (i < nc) {
           tr.first();
+          // Eight waves share each SIMD two by two and the sequencer favours
+          // the older one (waves 0-3 streamed about 1.25x faster than 4-7 in
+          // per-wave timestamps, and every workgroup waited for its last
+          // four): a wave yields issue priority as it works through its
+          // share, so the pair ends together.
+          if constexpr (EW == 8) set_wave_priority((nmine - c0 - i) * 4 / (nmine + 1));
           typename M::Frag &f = fr[b];
           const int b0 = (blk0 + wu + (c0 + i) * EW) * kBS;  // position of the block's token 0
           if (b0 + kBS > L) {

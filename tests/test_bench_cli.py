@@ -103,3 +103,13 @@ def test_wave_trace_summary_reads_the_records():
     assert s["stream_end_median_us_by_xcd"][0] == (9100 - 1000) / 100.0   # waves 0 and 2
     assert s["stream_end_median_us_by_xcd"][1] == (9200 - 1000) / 100.0   # waves 1 and 3
     assert s["stream_end_median_us_by_xcd"][2] is None
+
+
+def test_warmup_runs_for_both_the_calls_and_the_time_asked():
+    calls, syncs = [], []
+    n = bench.warm_past_transient(calls.append, 7, seconds=0.05, sync=lambda: syncs.append(1))
+    assert n == len(calls) >= 7 and calls == list(range(n))
+    assert syncs  # the GPU is synchronized, so the time is GPU time, not queueing
+    t = bench.time.perf_counter()
+    assert bench.warm_past_transient(lambda i: None, 1000, seconds=0.0, sync=lambda: None) == 1000
+    assert bench.time.perf_counter() - t < 5
