@@ -734,10 +734,65 @@ def run_extend_ramp(args, L, params, ws_ptr, ws_bytes, stream, hip, spec, k, n=1
         prm.start_event = prm.stop_event = None
     hip.sync_event(ev_b[-1])
     t = np.array([hip.elapsed_ms(ev_a[i], ev_b[i]) * 1e3 for i in range(n)])
-    edges = [0, 5, 15, 35, 60, 100, 200, 400, 700, n]
     print(json.dumps({"ramp": "pa_extend per-call time from idle", "workload": spec.name, "draft_tokens": k,
-                      "calls": n, "windows": [{"calls": [a, b], "mean_us": round(float(t[a:b].mean()), 2)}
-                                             for a, b in zip(edges[:-1], edges[1:])]}), flush=True)
+                      "calls": n, "windows": ramp_windows(t)}), flush=True)
+
+
+def ramp_windows(t):
+    edges = [0, 5, 15, 35, 60, 100, 200, 400, 700, len(t)]
+    return [{"calls": [a, b], "mean_us": round(float(t[a:b].mean()), 2)} for a, b in zip(edges[:-1], edges[1:])]
+
+
+def run_decode_ramp(args, wl, n=1000):
+    """--ramp without --extend: per-call times of n pa_decode calls (balanced split
+    and merge, no append; three replicas in turn) started from an idle GPU, with
+    timing events recorded between the calls."""
+    import torch
+    from paged_kv_cache_65_amd import binding as pa
+    spec = wl.spec
+    dev = torch.device("cuda:0")
+    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    MB = int(-(-int(wl.prompt_lens.max()) // 16))
+
+    def to_dev(a):
+        if spec.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    k_rows = np.concatenate([wl.prefix_k, wl.k_tokens]) if spec.prefix_len else wl.k_tokens
+    v_rows = np.concatenate([wl.prefix_v, wl.v_tokens]) if spec.prefix_len else wl.v_tokens
+    k_rows, v_rows = to_dev(k_rows), to_dev(v_rows)
+    reps = []
+    for r in range(3):
+        order = wl.free_order if r == 0 else \
+            np.random.default_rng(spec.seed * 1000 + r).permutation(wl.num_blocks).astype(np.int32)
+        rep = build_replica(pa, torch, wl, order, k_rows, v_rows, MB, S, dev)
+        tab, lens = rep.pool.seq_export(rep.seq_ids, MB)
+        reps.append((rep, torch.from_numpy(tab).to(dev), torch.from_numpy(lens).to(dev), int(lens.max())))
+    del k_rows, v_rows
+    q = to_dev(wl.q)
+    out = torch.empty((S, Hq, D), dtype={"f32": torch.float32, "f16": torch.float16,
+                                         "bf16": torch.bfloat16}[spec.out_dtype], device=dev)
+    sp = (spec.prefix_len // 16) if spec.prefix_len else 0
+    need = max(pa.pa_decode_workspace_bytes(pa.make_decode_params(
+        out, q, rep.k_cache, rep.v_cache, tab_d, lens_d, Hkv, mx, spec.fp32_scale(), args.partition_tokens, "auto",
+        None, None, None, sliding_window=spec.window, shared_prefix_blocks=sp)) for rep, tab_d, lens_d, mx in reps)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    torch.cuda.synchronize()
+    time.sleep(1.0)
+    for i in range(n):
+        rep, tab_d, lens_d, mx = reps[i % 3]
+        ev_a[i].record()
+        pa.pa_decode(out, q, rep.k_cache, rep.v_cache, tab_d, lens_d, Hkv, mx, spec.fp32_scale(),
+                     partition_tokens=args.partition_tokens, sliding_window=spec.window, shared_prefix_blocks=sp,
+                     workspace=ws)
+        ev_b[i].record()
+    torch.cuda.synchronize()
+    t = np.array([ev_a[i].elapsed_time(ev_b[i]) * 1e3 for i in range(n)])
+    print(json.dumps({"ramp": "pa_decode per-call time from idle", "workload": spec.name, "calls": n,
+                      "windows": ramp_windows(t)}), flush=True)
 
 
 def run_read_probe(args, wl, reps=20):
@@ -1030,7 +1085,8 @@ def main():
     ap.add_argument("--extend", type=int, default=0, metavar="K",
                     help="only measure multi-query attention with K new tokens per sequence of the workload")
     ap.add_argument("--ramp", action="store_true",
-                    help="with --extend: only print per-call times of 1000 calls started from an idle GPU")
+                    help="only print per-call times of 1000 attention calls (pa_decode, or pa_extend with "
+                         "--extend) started from an idle GPU")
     ap.add_argument("--read-ceiling", type=int, default=0, metavar="BYTES",
                     help="only time plain library kernels over BYTES of HBM (a reduction and a copy)")
     ap.add_argument("--read-probe", action="store_true",
@@ -1075,6 +1131,9 @@ def main():
         return
     if args.read_probe:
         run_read_probe(args, wl)
+        return
+    if args.ramp and not args.extend:
+        run_decode_ramp(args, wl)
         return
     if args.extend:
         run_extend_bench(args, wl, args.extend)
