@@ -2030,35 +2030,65 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
   int s = rest % a.num_seqs;
   const int p = rest / a.num_seqs;
   const int tid = threadIdx.x, lane = tid % 64, r = lane % 16, tq = lane / 16;
+  const int wu = __builtin_amdgcn_readfirstlane(tid / 64);
+  int L, q0, n;
   if (a.num_seqs > 1 && a.num_seqs <= kExtRankMax) {
     // Longest contexts first: workgroups start in index order, so the long
     // (sequence, KV head) pairs take the first round of CUs and the short
     // ones fill the CUs that free up (in sequence order a CU that drew two
     // long pairs ended last).  Slot s of the grid takes the sequence of rank
     // s (longer first, then lower index); which workgroup computes a row
-    // does not change its result.
+    // does not change its result.  The S x S comparisons are spread over
+    // the whole workgroup (tps threads per sequence, each a slice of the
+    // others, counted with LDS adds), and the thread that finds rank s
+    // passes its sequence's length and query rows on through LDS, so no
+    // dependent load of them follows.
     __shared__ int32_t rank_len[kExtRankMax];
-    __shared__ int32_t rank_pick;
+    __shared__ int32_t rank_cnt[kExtRankMax];
+    __shared__ int32_t rank_qs[kExtRankMax + 1];
+    __shared__ int32_t rank_pick[4];
     const int S = a.num_seqs;
-    for (int i = tid; i < S; i += ET) rank_len[i] = a.context_lens[i];
+    int sp = 1;
+    while (sp < S) sp *= 2;
+    const int tps = max(1, min(ET / sp, sp)), per = sp / tps;  // threads per sequence, comparisons per thread
+    for (int i = tid; i <= S; i += ET) {
+      if (i < S) {
+        rank_len[i] = a.context_lens[i];
+        rank_cnt[i] = 0;
+      }
+      rank_qs[i] = a.query_start[i];
+    }
     __syncthreads();
-    for (int i = tid; i < S; i += ET) {
+    for (int t = tid; t < sp * tps; t += ET) {
+      const int i = t / tps, j0 = (t % tps) * per;
+      if (i >= S) continue;
       const int Li = rank_len[i];
       int rk = 0;
-      for (int j = 0; j < S; ++j) {
+      for (int j = j0; j < min(S, j0 + per); ++j) {
         const int Lj = rank_len[j];
         rk += (Lj > Li || (Lj == Li && j < i)) ? 1 : 0;
       }
-      if (rk == s) rank_pick = i;
+      if (rk) atomicAdd(&rank_cnt[i], rk);
     }
     __syncthreads();
-    s = rank_pick;
+    for (int i = tid; i < S; i += ET)
+      if (rank_cnt[i] == s) {
+        rank_pick[0] = i;
+        rank_pick[1] = rank_len[i];
+        rank_pick[2] = rank_qs[i];
+        rank_pick[3] = rank_qs[i + 1];
+      }
+    __syncthreads();
+    s = rank_pick[0];
+    L = rank_pick[1];
+    q0 = rank_pick[2];
+    n = rank_pick[3] - q0;
+  } else {
+    L = a.context_lens[s];
+    q0 = a.query_start[s];
+    n = a.query_start[s + 1] - q0;
   }
   tr.stamp(1);
-  const int wu = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int L = a.context_lens[s];
-  const int q0 = a.query_start[s];
-  const int n = a.query_start[s + 1] - q0;
   const int i0 = tg * a.tpg;
   if (!extend_rows_valid(q0, n, a) || i0 >= n) return;  // no such query group
   const int ni = min(a.tpg, n - i0);
@@ -2117,15 +2147,24 @@ __global__ __launch_bounds__(extend_waves<NCT>() * 64, (extend_wg_per_cu<NCT>())
     ll[ct] = 0.f;
   }
   // Four tiles: the waves stage the q fragments in LDS together (fragment
-  // f = ct * NC + c by wave f mod EW), each once its first blocks are
-  // requested, so the two memory latencies overlap.  Every wave passes the
-  // barrier exactly once.
+  // f = ct * NC + c by wave f mod EW); a wave loads its share beside its
+  // block ids (one memory latency for both) and writes it once its first
+  // blocks are requested.  Every wave passes the barrier exactly once.
+  constexpr int QF = (NCT * NC + EW - 1) / EW;  // fragments a wave stages
+  u32x4_t qst[QF];
+  if constexpr (SmemExtend<D, NCT>::kTiled) {
+#pragma unroll
+    for (int k = 0; k < QF; ++k) {
+      const int fi = wu + k * EW, ct = fi / NC, c = fi % NC;
+      qst[k] = fi < NCT * NC && col_ok(ct, r) ? q_row(ct)[4 * c + tq] : u32x4_t{0, 0, 0, 0};
+    }
+  }
   auto stage_q = [&]() {
     if constexpr (SmemExtend<D, NCT>::kTiled) {
-      for (int fi = wu; fi < NCT * NC; fi += EW) {
-        const int ct = fi / NC, c = fi % NC;
-        const u32x4_t x = col_ok(ct, r) ? q_row(ct)[4 * c + tq] : u32x4_t{0, 0, 0, 0};
-        sm.q[ct][c][lane] = x;
+#pragma unroll
+      for (int k = 0; k < QF; ++k) {
+        const int fi = wu + k * EW;
+        if (fi < NCT * NC) sm.q[fi / NC][fi % NC][lane] = qst[k];
       }
       lds_barrier();
     }
