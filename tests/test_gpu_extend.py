@@ -154,3 +154,21 @@ def test_more_than_256_sequences_keep_their_grid_order():
     err = np.max(np.abs(out - ref))
     _say(f"  300 sequences, k in 0..3: max_abs_err={err:.3e}")
     assert err <= 2e-3
+
+
+@pytest.mark.parametrize("S,k", [(256, 8), (131, 2), (65, 16)])
+def test_ranked_grids_up_to_256_sequences(S, k):
+    # the longest-first ranking at every size it covers (its S x S comparisons
+    # split over the workgroup: 2, 1 and 4 threads per sequence here), with
+    # many equal lengths (ties broken by index), on the four-tile eight-wave
+    # path (k = 8, 16 at G = 8) and the one-tile path (k = 2)
+    rng = np.random.default_rng(58 + S)
+    lens = tuple(int(x) for x in rng.integers(k, k + 40, S))
+    news = (k,) * S
+    spec, wl, gst, ost, mb, qs, q = _case(58 + S, "bf16", lens, news, 16, 2, 64)
+    out = _run(spec, gst, mb, qs, q, news).cpu().numpy()
+    tab, l = oracle_side.tables(ost, mb)
+    ref = oracle.extend(q, ost.k_cache, ost.v_cache, tab, l, qs, 2, spec.fp32_scale(), "bf16")
+    err = np.max(np.abs(out - ref))
+    _say(f"  {S} sequences, k={k}: max_abs_err={err:.3e}")
+    assert err <= 2e-3
