@@ -1464,9 +1464,10 @@ constexpr int kUPairShift = 17;             // (s, g) pair index s*Hkv + g (15 b
 constexpr int kPairMax = 1 << 15;
 
 // Instruction-issue priority of this wave (0..3).  The sequencer favours
-// older waves; a wave of the balanced split lowers its priority as it works
-// through its share, so waves that started later (or were starved) catch up
-// and all shares end together.
+// older waves; a wave of the balanced split (byte caches) or of an
+// eight-wave extend workgroup lowers its priority as it works through its
+// share, so waves that started later (or were starved) catch up and all
+// shares end together.
 __device__ inline void set_wave_priority(int level) {
   switch (level) {
     case 0: __builtin_amdgcn_s_setprio(0); break;
